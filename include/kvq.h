@@ -1,0 +1,191 @@
+/*
+ * kvq.h -- C ABI of libkvq.so: Block-GTQ key-cache quantization and packed-cache
+ * decode attention for AMD Instinct MI355X (gfx950).
+ *
+ * The method is the one on the page "RoPE-Aware Bit Allocation for KV-Cache
+ * Quantization" (abstract): under RoPE a cached key's contribution to a later
+ * logit splits into 2-D frequency blocks; per layer and KV head a label-free
+ * energy is scored per block; integer bit widths are handed out greedily by
+ * marginal gain on top of a TQ-MSE scalar quantizer; a packed cache is then read
+ * by a decode-attention path.  The concrete numeric reading (per-token L2 norm,
+ * per-block scale, Gaussian Lloyd-Max codebooks, packed layout v1) is fixed by the
+ * comments below.
+ *
+ * Conventions for every call:
+ *  - All buffers are owned by the caller; pointers marked "device" are device
+ *    memory on the current HIP device.  The library allocates no device memory
+ *    and keeps no pointer after returning.
+ *  - `stream` is a hipStream_t (NULL = default stream).  Calls enqueue work and
+ *    return without synchronising; asynchronous faults surface at the caller's
+ *    next synchronisation.
+ *  - Arguments are validated on the host BEFORE any HIP call; on failure nothing
+ *    is launched or written and a negative kvq_status is returned.
+ *  - Element strides are in elements (binary16), not bytes.
+ *  - No call aborts, exits or throws.  Calls on different streams may run
+ *    concurrently; calls that write the same buffer must be ordered by the caller.
+ */
+#ifndef KVQ_H
+#define KVQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+#define KVQ_LAYOUT_VERSION 1
+#define KVQ_TILE_TOKENS 64
+
+typedef enum {
+    KVQ_OK = 0,
+    KVQ_ERR_ARG = -1,        /* null pointer, bad enum, n < 0 */
+    KVQ_ERR_SHAPE = -2,      /* unsupported head_dim, n_kv_heads, GQA ratio */
+    KVQ_ERR_BUDGET = -3,     /* budget outside [0, 8*d/2] and != 16*d/2; UNIFORM not divisible; v_bits invalid */
+    KVQ_ERR_ALIGN = -4,      /* pointer or row stride not 16-byte aligned */
+    KVQ_ERR_CAPACITY = -5,   /* capacity not a multiple of 64, or max_len/max_new beyond it */
+    KVQ_ERR_WORKSPACE = -6,  /* workspace too small */
+    KVQ_ERR_HIP = -7,        /* a HIP launch failed */
+    KVQ_ERR_VERSION = -8     /* layout_version != KVQ_LAYOUT_VERSION */
+} kvq_status;
+
+/* RoPE block map (which two coordinates form 2-D frequency block i) */
+#define KVQ_PAIR_HALF 0          /* block i = (i, i + d/2): rotate-half convention (default) */
+#define KVQ_PAIR_INTERLEAVED 1   /* block i = (2i, 2i + 1) */
+
+/* allocation modes */
+#define KVQ_GREEDY 0             /* Block-GTQ greedy marginal-gain allocation */
+#define KVQ_UNIFORM 1            /* every block budget/(d/2) bits (values, uniform baseline) */
+
+/* decode kernel choice for kvq_packed_decode_attn_ex */
+#define KVQ_DECODE_AUTO 0
+#define KVQ_DECODE_GENERIC 1     /* any widths incl. 16-bit passthrough, GQA ratio <= 16 */
+#define KVQ_DECODE_MFMA 2        /* widths 0..8, v_bits 1..8, GQA ratio <= 8 */
+
+typedef struct {
+    int32_t layout_version;  /* KVQ_LAYOUT_VERSION */
+    int32_t head_dim;        /* d: 128 for quantize/attention; even, 2..128 for energy/allocation */
+    int32_t n_kv_heads;      /* KV heads of one layer, >= 1 */
+    int32_t rope_pairing;    /* KVQ_PAIR_HALF or KVQ_PAIR_INTERLEAVED */
+    int32_t k_budget;        /* sum of the d/2 key block widths: 0..8*(d/2), or exactly 16*(d/2) (passthrough) */
+    int32_t v_bits;          /* uniform value width: 1..8, or 16 (passthrough) */
+    int64_t capacity_tokens; /* token slots per sequence and layer; multiple of 64 */
+} kvq_geom;
+
+/* Packed layout v1 (per sequence and layer):  [n_kv_heads][capacity/64 tiles][tile].
+ * Tile of 64 token slots:
+ *   K section: 64 records of SK = 16*ceil(2*k_budget/128) bytes.  Record p holds slot
+ *              p's key codes as an LSB-first bitstream (bit b of the stream is bit
+ *              b%8 of byte b/8) in "K order": blocks sorted by width descending
+ *              (ties: lower block index first), each block contributing coordinate
+ *              p(i) then q(i), width-0 blocks omitted; a field is w bits (16 bits =
+ *              raw binary16 for passthrough).
+ *   V section: d runs of 8*v_bits bytes; run c holds slot p's value code of
+ *              coordinate c at bits [p*v_bits, (p+1)*v_bits).
+ *   64 binary32 key scales, then 64 binary32 value scales (per-token L2 norms).
+ * Unused slots are zero; the cache must be zero-initialised before first use. */
+
+int32_t kvq_version(void);                        /* KVQ_LAYOUT_VERSION */
+const char *kvq_status_string(int32_t status);    /* static string, never NULL */
+
+/* Bytes of one tile, of one sequence's region for one layer, or a negative
+ * kvq_status if the geometry is invalid. */
+int64_t kvq_tile_bytes(const kvq_geom *g);
+int64_t kvq_cache_bytes(const kvq_geom *g);
+
+/* Host copy of the built-in codebook for width w (1..8): 2^w binary16 levels
+ * (ascending), 2^w binary32 thresholds (entry 0 unused; entry j is the midpoint of
+ * levels j-1 and j), and the 8 binary32 distortion drops dD[b] = D(b) - D(b+1) of
+ * Gaussian Lloyd-Max quantization (D(0) = 1) used as greedy gains.  Any output
+ * pointer may be NULL.  No GPU access. */
+int32_t kvq_get_codebook(int32_t w, uint16_t *levels_fp16, float *thresholds, float *gain_dd);
+
+/* a1 -- Block energy.  The page ("RoPE-Aware Bit Allocation...", abstract) scores
+ * each RoPE block of each KV head with a label-free energy.  Reading: the exact sum
+ * over the given tokens of k_{p(i)}^2 + k_{q(i)}^2.  Every binary16 square is a
+ * multiple of 2^-48, so the sum is kept exactly as an unsigned 128-bit count of
+ * 2^-48 units; results are independent of order, tiling and launch shape.
+ *   x       : device binary16, element (t, h, c) at x[t*stride_tok + h*stride_head + c],
+ *             t < n_tok, h < n_kv_heads, c < head_dim (c contiguous)
+ *   energy  : device uint64 [n_kv_heads][head_dim/2][2] = (low, high) limbs;
+ *             ACCUMULATED INTO (zero it for a fresh sum; call repeatedly to add tokens)
+ * Requirements: head_dim even, 2..128; n_tok >= 0; x and energy 16-byte aligned
+ * and stride_tok, stride_head multiples of 8 when head_dim is a multiple of 8. */
+int32_t kvq_block_energy(const kvq_geom *g, const void *x, int64_t n_tok, int64_t stride_tok,
+                         int64_t stride_head, uint64_t *energy, void *stream);
+
+/* a2 -- Bit allocation (page abstract: greedy integer widths by marginal gain under
+ * a fixed budget, per layer and KV head).  Per unit (row of `energy`):
+ *   E_i = RN64(energy_i * 2^-48) (correctly rounded from the exact integer);
+ *   GREEDY: from b = 0, `budget` times give one bit to the block maximising
+ *           RN64(E_i * dD[b_i]) among blocks with b_i < 8; ties -> lowest index;
+ *   UNIFORM: b_i = budget/(d/2) (budget must be divisible);
+ *   budget == 16*(d/2): every block 16 (raw passthrough), either mode;
+ *   sigma_i = RN32(sqrt(E_i / (2*E_tot))), E_tot = RN64(sum_i energy_i * 2^-48); 0 if E_tot = 0.
+ *   energy : device uint64 [n_units][head_dim/2][2]
+ *   bits   : device uint8  [n_units][head_dim/2]
+ *   sigma  : device float  [n_units][head_dim/2]
+ * Uses g->head_dim only.  Requirements: budget in [0, 8*(d/2)] or == 16*(d/2). */
+int32_t kvq_allocate_bits(const kvq_geom *g, const uint64_t *energy, int32_t n_units, int32_t budget,
+                          int32_t mode, uint8_t *bits, float *sigma, void *stream);
+
+/* a3 -- Quantize and pack (page abstract: TQ-MSE codes at the allocated widths,
+ * stored in a packed cache).  For sequence s (< n_seq) the n_new[s] token rows
+ * src_row0[s] .. src_row0[s]+n_new[s]-1 of k and v are written to slots
+ * first_slot[s] .. of the region cache + seq_byte_off[s].  Per token and head:
+ *   s_t = sqrtf(pairwise binary32 tree of the squared coordinates, coordinate order);
+ *   code_c = #{ j in 1..2^w-1 : x_c >= RN32(s_t * RN32(sigma_i * thr_w[j])) } for
+ *            width w = 1..8 (w = 16: raw binary16 bits; w = 0: nothing stored).
+ * Keys use k_bits/k_sigma; values use width v_bits and v_sigma.
+ *   k, v        : device binary16 rows, element (r, h, c) at base[r*stride_tok + h*stride_head + c]
+ *   first_slot, src_row0, seq_byte_off : device int64 [n_seq];  n_new : device int32 [n_seq]
+ *   k_bits      : device uint8 [n_kv_heads][64];  k_sigma, v_sigma : device float [n_kv_heads][64]
+ *   cache       : device, zero-initialised, regions of kvq_cache_bytes(g) bytes
+ * Appends OR codes into partially filled tiles; sequences must not share regions.
+ * Device-side entries with first_slot < 0, n_new < 0, n_new > max_new or
+ * first_slot + n_new > capacity_tokens are skipped (nothing written for them).
+ * Requirements: head_dim 128; 0 <= max_new <= capacity; alignment 16 B. */
+int32_t kvq_quantize_pack(const kvq_geom *g, const void *k, const void *v, int64_t stride_tok,
+                          int64_t stride_head, int32_t n_seq, const int64_t *first_slot,
+                          const int32_t *n_new, const int64_t *src_row0, int32_t max_new,
+                          const uint8_t *k_bits, const float *k_sigma, const float *v_sigma,
+                          uint8_t *cache, const int64_t *seq_byte_off, void *stream);
+
+/* a4 + a5 -- Packed-cache GQA decode attention (page abstract: packed-cache
+ * serving path).  For sequence s and query head h (KV head h / (n_q_heads/n_kv_heads)):
+ *   out[s][h] = sum_t p_t vhat_t,  p = softmax_t(softmax_scale * q[s][h] . khat_t),
+ * over slots t < seq_len[s], with khat = s_t * sigma_i * level_w[code] (raw value at
+ * width 16, 0 at width 0) and vhat likewise.  The token axis is split into chunks
+ * whose partial (max, sum, output) are merged by a log-sum-exp combine.  Empty
+ * sequences give 0.
+ *   q        : device binary16 [n_seq][n_q_heads][128] (post-RoPE), contiguous
+ *   seq_len  : device int32 [n_seq] (clamped to [0, max_len])
+ *   out      : device float [n_seq][n_q_heads][128]
+ *   workspace: device scratch of at least kvq_decode_workspace_bytes(...) bytes
+ * Requirements: head_dim 128; n_q_heads multiple of n_kv_heads with ratio <= 16;
+ * 0 <= max_len <= capacity; alignment 16 B. */
+int32_t kvq_packed_decode_attn(const kvq_geom *g, int32_t n_q_heads, const void *q, const uint8_t *cache,
+                               const int64_t *seq_byte_off, const int32_t *seq_len, int32_t n_seq,
+                               int64_t max_len, const uint8_t *k_bits, const float *k_sigma,
+                               const float *v_sigma, float softmax_scale, float *out, void *workspace,
+                               size_t workspace_bytes, void *stream);
+
+/* Same, choosing the kernel (KVQ_DECODE_*) and the number of 64-token tiles per
+ * split chunk (0 = automatic).  Returns KVQ_ERR_SHAPE if the chosen kernel cannot
+ * serve the geometry. */
+int32_t kvq_packed_decode_attn_ex(const kvq_geom *g, int32_t n_q_heads, const void *q, const uint8_t *cache,
+                                  const int64_t *seq_byte_off, const int32_t *seq_len, int32_t n_seq,
+                                  int64_t max_len, const uint8_t *k_bits, const float *k_sigma,
+                                  const float *v_sigma, float softmax_scale, float *out, void *workspace,
+                                  size_t workspace_bytes, int32_t kernel, int32_t tiles_per_split,
+                                  void *stream);
+
+/* Workspace bytes needed by kvq_packed_decode_attn(_ex) (negative status if invalid). */
+int64_t kvq_decode_workspace_bytes(const kvq_geom *g, int32_t n_q_heads, int32_t n_seq, int64_t max_len);
+int64_t kvq_decode_workspace_bytes_ex(const kvq_geom *g, int32_t n_q_heads, int32_t n_seq, int64_t max_len,
+                                      int32_t kernel, int32_t tiles_per_split);
+
+#ifdef __cplusplus
+}
+#endif
+#endif /* KVQ_H */

@@ -1,0 +1,207 @@
+// kvq_api.hip -- the extern "C" boundary of libkvq.so (declared in include/kvq.h).
+// Every argument is checked on the host before the first HIP call, so a rejected
+// call launches nothing and writes nothing.
+#include <stdio.h>
+#include <stdlib.h>
+#include <string.h>
+
+#include "kvq_internal.h"
+
+namespace {
+
+using namespace kvq;
+
+const uint16_t h_levels[510] = {KVQ_LEVELS_FP16_LIST};
+const float h_thresholds[510] = {KVQ_THRESHOLDS_LIST};
+const float h_gain_dd[8] = {KVQ_GAIN_DD_LIST};
+
+bool debug_on() {
+    static const bool on = getenv("KVQ_DEBUG") != nullptr;
+    return on;
+}
+
+int32_t fail(int32_t st, const char* fn, const char* why) {
+    if (debug_on()) fprintf(stderr, "kvq: %s rejected: %s (%s)\n", fn, why, kvq_status_string(st));
+    return st;
+}
+
+bool aligned(const void* p, uintptr_t a) { return ((uintptr_t)p & (a - 1)) == 0; }
+
+// head_dim rule: exact128 for quantize/attention, any even 2..128 for energy/allocation
+int32_t check_geom(const kvq_geom* g, bool exact128, const char* fn) {
+    if (!g) return fail(KVQ_ERR_ARG, fn, "null geometry");
+    if (g->layout_version != KVQ_LAYOUT_VERSION) return fail(KVQ_ERR_VERSION, fn, "layout_version");
+    const int d = g->head_dim;
+    if (exact128 ? d != kHeadDim : (d < 2 || d > kHeadDim || (d & 1))) return fail(KVQ_ERR_SHAPE, fn, "head_dim");
+    if (g->n_kv_heads < 1 || g->n_kv_heads > 65535) return fail(KVQ_ERR_SHAPE, fn, "n_kv_heads");
+    if (g->rope_pairing != KVQ_PAIR_HALF && g->rope_pairing != KVQ_PAIR_INTERLEAVED)
+        return fail(KVQ_ERR_ARG, fn, "rope_pairing");
+    const int nb = d / 2;
+    if (!((g->k_budget >= 0 && g->k_budget <= 8 * nb) || g->k_budget == 16 * nb))
+        return fail(KVQ_ERR_BUDGET, fn, "k_budget");
+    if (!((g->v_bits >= 1 && g->v_bits <= 8) || g->v_bits == 16)) return fail(KVQ_ERR_BUDGET, fn, "v_bits");
+    if (g->capacity_tokens < 0 || g->capacity_tokens % kTile) return fail(KVQ_ERR_CAPACITY, fn, "capacity_tokens");
+    return KVQ_OK;
+}
+
+int32_t hip_status(hipError_t e, const char* fn) {
+    if (e == hipSuccess) return KVQ_OK;
+    if (debug_on()) fprintf(stderr, "kvq: %s: HIP error %s\n", fn, hipGetErrorString(e));
+    return KVQ_ERR_HIP;
+}
+
+}  // namespace
+
+extern "C" {
+
+int32_t kvq_version(void) { return KVQ_LAYOUT_VERSION; }
+
+const char* kvq_status_string(int32_t status) {
+    switch (status) {
+        case KVQ_OK: return "ok";
+        case KVQ_ERR_ARG: return "invalid argument";
+        case KVQ_ERR_SHAPE: return "unsupported shape";
+        case KVQ_ERR_BUDGET: return "invalid bit budget";
+        case KVQ_ERR_ALIGN: return "misaligned pointer or stride";
+        case KVQ_ERR_CAPACITY: return "capacity exceeded or not a multiple of 64";
+        case KVQ_ERR_WORKSPACE: return "workspace too small";
+        case KVQ_ERR_HIP: return "HIP launch failed";
+        case KVQ_ERR_VERSION: return "unsupported layout version";
+        default: return "unknown status";
+    }
+}
+
+int64_t kvq_tile_bytes(const kvq_geom* g) {
+    const int32_t st = check_geom(g, true, "kvq_tile_bytes");
+    if (st) return st;
+    return tile_bytes(g->head_dim, g->k_budget, g->v_bits);
+}
+
+int64_t kvq_cache_bytes(const kvq_geom* g) {
+    const int32_t st = check_geom(g, true, "kvq_cache_bytes");
+    if (st) return st;
+    return (int64_t)g->n_kv_heads * (g->capacity_tokens / kTile) * tile_bytes(g->head_dim, g->k_budget, g->v_bits);
+}
+
+int32_t kvq_get_codebook(int32_t w, uint16_t* levels_fp16, float* thresholds, float* gain_dd) {
+    if (w < 1 || w > 8) return fail(KVQ_ERR_ARG, "kvq_get_codebook", "width");
+    const int off = KVQ_CB_OFF(w), n = 1 << w;
+    if (levels_fp16) memcpy(levels_fp16, h_levels + off, sizeof(uint16_t) * n);
+    if (thresholds) memcpy(thresholds, h_thresholds + off, sizeof(float) * n);
+    if (gain_dd) memcpy(gain_dd, h_gain_dd, sizeof(float) * 8);
+    return KVQ_OK;
+}
+
+int32_t kvq_block_energy(const kvq_geom* g, const void* x, int64_t n_tok, int64_t stride_tok, int64_t stride_head,
+                         uint64_t* energy, void* stream) {
+    const char* fn = "kvq_block_energy";
+    int32_t st = check_geom(g, false, fn);
+    if (st) return st;
+    if (n_tok < 0) return fail(KVQ_ERR_ARG, fn, "n_tok < 0");
+    if (!energy || (n_tok > 0 && !x)) return fail(KVQ_ERR_ARG, fn, "null pointer");
+    if (stride_tok < 0 || stride_head < 0) return fail(KVQ_ERR_ARG, fn, "negative stride");
+    if (!aligned(x, 4) || (stride_tok & 1) || (stride_head & 1) || !aligned(energy, 16))
+        return fail(KVQ_ERR_ALIGN, fn, "x 4-byte / strides even / energy 16-byte");
+    if (n_tok == 0) return KVQ_OK;
+    return hip_status(launch_block_energy((const uint16_t*)x, n_tok, stride_tok, stride_head, g->n_kv_heads,
+                                          g->head_dim, g->rope_pairing, energy, (hipStream_t)stream),
+                      fn);
+}
+
+int32_t kvq_allocate_bits(const kvq_geom* g, const uint64_t* energy, int32_t n_units, int32_t budget, int32_t mode,
+                          uint8_t* bits, float* sigma, void* stream) {
+    const char* fn = "kvq_allocate_bits";
+    int32_t st = check_geom(g, false, fn);
+    if (st) return st;
+    const int nb = g->head_dim / 2;
+    if (n_units < 0) return fail(KVQ_ERR_ARG, fn, "n_units < 0");
+    if (mode != KVQ_GREEDY && mode != KVQ_UNIFORM) return fail(KVQ_ERR_ARG, fn, "mode");
+    if (!((budget >= 0 && budget <= 8 * nb) || budget == 16 * nb)) return fail(KVQ_ERR_BUDGET, fn, "budget");
+    if (mode == KVQ_UNIFORM && budget != 16 * nb && budget % nb) return fail(KVQ_ERR_BUDGET, fn, "uniform budget");
+    if (n_units > 0 && (!energy || !bits || !sigma)) return fail(KVQ_ERR_ARG, fn, "null pointer");
+    if (!aligned(energy, 16) || !aligned(sigma, 4)) return fail(KVQ_ERR_ALIGN, fn, "energy 16-byte / sigma 4-byte");
+    if (n_units == 0) return KVQ_OK;
+    return hip_status(launch_allocate(energy, n_units, nb, budget, mode, bits, sigma, (hipStream_t)stream), fn);
+}
+
+int32_t kvq_quantize_pack(const kvq_geom* g, const void* k, const void* v, int64_t stride_tok, int64_t stride_head,
+                          int32_t n_seq, const int64_t* first_slot, const int32_t* n_new, const int64_t* src_row0,
+                          int32_t max_new, const uint8_t* k_bits, const float* k_sigma, const float* v_sigma,
+                          uint8_t* cache, const int64_t* seq_byte_off, void* stream) {
+    const char* fn = "kvq_quantize_pack";
+    int32_t st = check_geom(g, true, fn);
+    if (st) return st;
+    if (n_seq < 0 || max_new < 0) return fail(KVQ_ERR_ARG, fn, "negative count");
+    if (n_seq > 65535) return fail(KVQ_ERR_SHAPE, fn, "n_seq");
+    if (max_new > g->capacity_tokens) return fail(KVQ_ERR_CAPACITY, fn, "max_new > capacity");
+    if (stride_tok < 0 || stride_head < 0) return fail(KVQ_ERR_ARG, fn, "negative stride");
+    if (n_seq == 0 || max_new == 0) return KVQ_OK;
+    if (!k || !v || !first_slot || !n_new || !src_row0 || !k_bits || !k_sigma || !v_sigma || !cache || !seq_byte_off)
+        return fail(KVQ_ERR_ARG, fn, "null pointer");
+    if (!aligned(k, 4) || !aligned(v, 4) || (stride_tok & 1) || (stride_head & 1) || !aligned(cache, 16) ||
+        !aligned(first_slot, 8) || !aligned(src_row0, 8) || !aligned(seq_byte_off, 8) || !aligned(n_new, 4) ||
+        !aligned(k_sigma, 4) || !aligned(v_sigma, 4))
+        return fail(KVQ_ERR_ALIGN, fn, "alignment");
+    return hip_status(launch_quantize_pack(*g, (const uint16_t*)k, (const uint16_t*)v, stride_tok, stride_head, n_seq,
+                                           first_slot, n_new, src_row0, max_new, k_bits, k_sigma, v_sigma, cache,
+                                           seq_byte_off, (hipStream_t)stream),
+                      fn);
+}
+
+int64_t kvq_decode_workspace_bytes_ex(const kvq_geom* g, int32_t n_q_heads, int32_t n_seq, int64_t max_len,
+                                      int32_t kernel, int32_t tiles_per_split) {
+    const char* fn = "kvq_decode_workspace_bytes";
+    int32_t st = check_geom(g, true, fn);
+    if (st) return st;
+    if (n_q_heads < 1 || n_q_heads % g->n_kv_heads) return fail(KVQ_ERR_SHAPE, fn, "n_q_heads");
+    if (n_seq < 0 || max_len < 0) return fail(KVQ_ERR_ARG, fn, "negative count");
+    if (max_len > g->capacity_tokens) return fail(KVQ_ERR_CAPACITY, fn, "max_len > capacity");
+    DecodePlan plan;
+    st = plan_decode(*g, n_q_heads, n_seq, max_len, kernel, tiles_per_split, &plan);
+    if (st) return fail(st, fn, "no kernel for this geometry");
+    return plan.workspace;
+}
+
+int64_t kvq_decode_workspace_bytes(const kvq_geom* g, int32_t n_q_heads, int32_t n_seq, int64_t max_len) {
+    return kvq_decode_workspace_bytes_ex(g, n_q_heads, n_seq, max_len, KVQ_DECODE_AUTO, 0);
+}
+
+int32_t kvq_packed_decode_attn_ex(const kvq_geom* g, int32_t n_q_heads, const void* q, const uint8_t* cache,
+                                  const int64_t* seq_byte_off, const int32_t* seq_len, int32_t n_seq, int64_t max_len,
+                                  const uint8_t* k_bits, const float* k_sigma, const float* v_sigma,
+                                  float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
+                                  int32_t kernel, int32_t tiles_per_split, void* stream) {
+    const char* fn = "kvq_packed_decode_attn";
+    int32_t st = check_geom(g, true, fn);
+    if (st) return st;
+    if (n_q_heads < 1 || n_q_heads % g->n_kv_heads) return fail(KVQ_ERR_SHAPE, fn, "n_q_heads");
+    if (n_seq < 0 || max_len < 0 || tiles_per_split < 0) return fail(KVQ_ERR_ARG, fn, "negative count");
+    if ((int64_t)n_seq * n_q_heads > 2147483647LL) return fail(KVQ_ERR_SHAPE, fn, "n_seq * n_q_heads");
+    if (n_seq > 65535) return fail(KVQ_ERR_SHAPE, fn, "n_seq");
+    if (max_len > g->capacity_tokens) return fail(KVQ_ERR_CAPACITY, fn, "max_len > capacity");
+    DecodePlan plan;
+    st = plan_decode(*g, n_q_heads, n_seq, max_len, kernel, tiles_per_split, &plan);
+    if (st) return fail(st, fn, "no kernel for this geometry");
+    if (n_seq == 0) return KVQ_OK;
+    if (!q || !cache || !seq_byte_off || !seq_len || !k_bits || !k_sigma || !v_sigma || !out || !workspace)
+        return fail(KVQ_ERR_ARG, fn, "null pointer");
+    if (!aligned(q, 16) || !aligned(cache, 16) || !aligned(out, 16) || !aligned(workspace, 16) ||
+        !aligned(seq_byte_off, 8) || !aligned(seq_len, 4) || !aligned(k_sigma, 4) || !aligned(v_sigma, 4))
+        return fail(KVQ_ERR_ALIGN, fn, "alignment");
+    if ((int64_t)workspace_bytes < plan.workspace) return fail(KVQ_ERR_WORKSPACE, fn, "workspace_bytes");
+    return hip_status(launch_decode(*g, plan, n_q_heads, (const uint16_t*)q, cache, seq_byte_off, seq_len, n_seq,
+                                    max_len, k_bits, k_sigma, v_sigma, softmax_scale, out, (float*)workspace,
+                                    (hipStream_t)stream),
+                      fn);
+}
+
+int32_t kvq_packed_decode_attn(const kvq_geom* g, int32_t n_q_heads, const void* q, const uint8_t* cache,
+                               const int64_t* seq_byte_off, const int32_t* seq_len, int32_t n_seq, int64_t max_len,
+                               const uint8_t* k_bits, const float* k_sigma, const float* v_sigma, float softmax_scale,
+                               float* out, void* workspace, size_t workspace_bytes, void* stream) {
+    return kvq_packed_decode_attn_ex(g, n_q_heads, q, cache, seq_byte_off, seq_len, n_seq, max_len, k_bits, k_sigma,
+                                     v_sigma, softmax_scale, out, workspace, workspace_bytes, KVQ_DECODE_AUTO, 0,
+                                     stream);
+}
+
+}  // extern "C"

@@ -1,0 +1,246 @@
+// kvq_decode.hip -- packed-cache GQA decode attention, split over the token axis,
+// plus the log-sum-exp merge of the split partials.  The page "RoPE-Aware Bit
+// Allocation for KV-Cache Quantization" (abstract) describes a packed-cache
+// serving path that reads the compressed cache at decode time; this file holds
+// the generic (VALU + LDS) kernel that serves every width, including 16-bit
+// passthrough, and the merge shared with the matrix-core kernel.
+//
+// Partials: workspace[((s*n_q + hq)*n_split + split)*(d+2) + {0: m, 1: l, 2+c: o_c}],
+// with m in log2 units (logits are pre-multiplied by log2 e) and o unnormalised.
+#include <math.h>
+
+#include "kvq_internal.h"
+
+namespace kvq {
+
+constexpr int kGenericMaxGroup = 16;
+constexpr bool kMfmaKernel = false;
+
+// bits [pos, pos + w) of a little-endian bitstream at base (w <= 16); reads only
+// the (aligned) dwords that hold the field
+__device__ __forceinline__ uint32_t read_field(const uint8_t* base, int pos, int w) {
+    const uint32_t* dw = (const uint32_t*)base;
+    const int k = pos >> 5, sh = pos & 31;
+    uint32_t v = dw[k] >> sh;
+    if (sh + w > 32) v |= dw[k + 1] << (32 - sh);
+    return v & ((1u << w) - 1u);
+}
+
+__device__ __forceinline__ float level(uint32_t code, int w) {
+    if (w == 16) return h2f(code);
+    return h2f(c_levels[min(KVQ_CB_OFF(w) + (int)code, 509)]);
+}
+
+// grid: (n_split, n_kv, n_seq); block: 256 threads
+__global__ __launch_bounds__(256) void decode_generic_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, const int64_t* __restrict__ seq_byte_off,
+    const int32_t* __restrict__ seq_len, int64_t max_len, int64_t capacity, const uint8_t* __restrict__ k_bits,
+    const float* __restrict__ k_sigma, const float* __restrict__ v_sigma, float scale_log2, int n_q, int g,
+    int pairing, int k_budget, int v_bits, int tiles_per_split, int n_split, float* __restrict__ ws) {
+    const int split = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
+    const int tid = threadIdx.x;
+    const int64_t len = min(max((int64_t)seq_len[s], (int64_t)0), max_len);
+    const int64_t n_tiles_seq = (len + kTile - 1) / kTile;
+    const int64_t t0 = (int64_t)split * tiles_per_split;
+    const int64_t t1 = min(t0 + tiles_per_split, n_tiles_seq);
+    const int D2 = kHeadDim + 2;
+
+    __shared__ float s_x[kTile][kHeadDim + 1];  // dequantized K, then V, of the current tile
+    __shared__ float s_q[kGenericMaxGroup][kHeadDim];
+    __shared__ float s_p[kGenericMaxGroup][kTile];
+    __shared__ float s_m[kGenericMaxGroup], s_l[kGenericMaxGroup], s_a[kGenericMaxGroup];
+    __shared__ float s_ksig[kHeadDim], s_vsig[kHeadDim];
+    __shared__ uint8_t s_bw[kMaxBlocks];
+    __shared__ uint8_t s_fc[kHeadDim], s_fw[kHeadDim];
+    __shared__ uint16_t s_fo[kHeadDim];
+    __shared__ int s_nf;
+
+    // per-(KV head) tables: block scales per coordinate and the K order
+    if (tid < kMaxBlocks) {
+        const int i = tid;
+        const int p = pairing == KVQ_PAIR_HALF ? i : 2 * i;
+        const int qq = pairing == KVQ_PAIR_HALF ? i + kMaxBlocks : 2 * i + 1;
+        s_bw[i] = k_bits[kvh * kMaxBlocks + i];
+        s_ksig[p] = s_ksig[qq] = k_sigma[kvh * kMaxBlocks + i];
+        s_vsig[p] = s_vsig[qq] = v_sigma[kvh * kMaxBlocks + i];
+    }
+    for (int idx = tid; idx < g * kHeadDim; idx += 256) {
+        const int j = idx / kHeadDim, c = idx - j * kHeadDim;
+        s_q[j][c] = h2f(q[((int64_t)s * n_q + kvh * g + j) * kHeadDim + c]);
+    }
+    if (tid < g) { s_m[tid] = -INFINITY; s_l[tid] = 0.f; }
+    __syncthreads();
+    if (tid < kMaxBlocks) {
+        const int i = tid, w = s_bw[i];
+        int rank = 0, off = 0;
+        for (int j = 0; j < kMaxBlocks; ++j) {
+            const int wj = s_bw[j];
+            if (wj > w || (wj == w && j < i)) { ++rank; off += 2 * wj; }
+        }
+        if (w > 0) {
+            const int p = pairing == KVQ_PAIR_HALF ? i : 2 * i;
+            const int qq = pairing == KVQ_PAIR_HALF ? i + kMaxBlocks : 2 * i + 1;
+            s_fc[2 * rank] = (uint8_t)p; s_fo[2 * rank] = (uint16_t)off; s_fw[2 * rank] = (uint8_t)w;
+            s_fc[2 * rank + 1] = (uint8_t)qq; s_fo[2 * rank + 1] = (uint16_t)(off + w); s_fw[2 * rank + 1] = (uint8_t)w;
+        }
+        const unsigned long long nz = __ballot(w > 0);
+        if (i == 0) s_nf = 2 * __popcll(nz);
+    }
+    __syncthreads();
+    const int nf = s_nf;
+
+    const int64_t SK = k_record_bytes(k_budget);
+    const int64_t TB = tile_bytes(kHeadDim, k_budget, v_bits);
+    const uint8_t* head = cache + seq_byte_off[s] + (int64_t)kvh * (capacity / kTile) * TB;
+    const int per = (g * kHeadDim + 255) / 256;  // (head, coordinate) outputs per thread
+    float o[kGenericMaxGroup * kHeadDim / 256];
+    for (int r = 0; r < per; ++r) o[r] = 0.f;
+
+    for (int64_t tau = t0; tau < t1; ++tau) {
+        const uint8_t* tile = head + tau * TB;
+        const float* scl = (const float*)(tile + kTile * SK + kHeadDim * 8 * v_bits);
+        const int nvalid = (int)min((int64_t)kTile, len - tau * kTile);
+        // dequantize K (width-0 coordinates are 0)
+        for (int idx = tid; idx < kTile * (kHeadDim + 1); idx += 256) (&s_x[0][0])[idx] = 0.f;
+        __syncthreads();
+        for (int idx = tid; idx < kTile * nf; idx += 256) {
+            const int p = idx / nf, f = idx - p * nf;
+            const int w = s_fw[f], c = s_fc[f];
+            const uint32_t code = read_field(tile + p * SK, s_fo[f], w);
+            const float lv = level(code, w);
+            s_x[p][c] = w == 16 ? lv : scl[p] * s_ksig[c] * lv;
+        }
+        __syncthreads();
+        // logits (log2 units); padding slots of a ragged last tile are masked
+        for (int idx = tid; idx < g * kTile; idx += 256) {
+            const int j = idx / kTile, p = idx - j * kTile;
+            float z = 0.f;
+            for (int c = 0; c < kHeadDim; ++c) z += s_q[j][c] * s_x[p][c];
+            s_p[j][p] = p < nvalid ? z * scale_log2 : -INFINITY;
+        }
+        __syncthreads();
+        // online softmax, one thread per head
+        if (tid < g) {
+            const int j = tid;
+            float mt = -INFINITY;
+            for (int p = 0; p < kTile; ++p) mt = fmaxf(mt, s_p[j][p]);
+            const float mn = fmaxf(s_m[j], mt);
+            const float a = exp2f(s_m[j] - mn);
+            float l = 0.f;
+            for (int p = 0; p < kTile; ++p) {
+                const float e = exp2f(s_p[j][p] - mn);
+                s_p[j][p] = e;
+                l += e;
+            }
+            s_l[j] = s_l[j] * a + l;
+            s_m[j] = mn;
+            s_a[j] = a;
+        }
+        __syncthreads();
+        // dequantize V
+        for (int idx = tid; idx < kTile * kHeadDim; idx += 256) {
+            const int c = idx / kTile, p = idx - c * kTile;
+            const uint32_t code = read_field(tile + kTile * SK + c * 8 * v_bits, p * v_bits, v_bits);
+            const float lv = level(code, v_bits);
+            s_x[p][c] = v_bits == 16 ? lv : scl[kTile + p] * s_vsig[c] * lv;
+        }
+        __syncthreads();
+        for (int r = 0; r < per; ++r) {
+            const int idx = tid + 256 * r;
+            if (idx >= g * kHeadDim) break;
+            const int j = idx / kHeadDim, c = idx - j * kHeadDim;
+            float acc = o[r] * s_a[j];
+            for (int p = 0; p < kTile; ++p) acc += s_p[j][p] * s_x[p][c];
+            o[r] = acc;
+        }
+        __syncthreads();
+    }
+    // partials (an empty chunk writes m = -inf, l = 0, o = 0)
+    for (int r = 0; r < per; ++r) {
+        const int idx = tid + 256 * r;
+        if (idx >= g * kHeadDim) break;
+        const int j = idx / kHeadDim, c = idx - j * kHeadDim;
+        float* part = ws + (((int64_t)s * n_q + kvh * g + j) * n_split + split) * D2;
+        part[2 + c] = o[r];
+        if (c == 0) { part[0] = s_m[j]; part[1] = s_l[j]; }
+    }
+}
+
+// grid: n_seq * n_q; block: 128 threads (one per output coordinate)
+__global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ ws, int n_split,
+                                                   float* __restrict__ out) {
+    const int64_t row = blockIdx.x;
+    const int c = threadIdx.x;
+    const float* part = ws + row * n_split * (kHeadDim + 2);
+    float m = -INFINITY;
+    for (int sp = 0; sp < n_split; ++sp) m = fmaxf(m, part[sp * (kHeadDim + 2)]);
+    float l = 0.f, acc = 0.f;
+    if (m != -INFINITY) {
+        for (int sp = 0; sp < n_split; ++sp) {
+            const float* p = part + sp * (kHeadDim + 2);
+            const float a = exp2f(p[0] - m);
+            l += a * p[1];
+            acc += a * p[2 + c];
+        }
+    }
+    out[row * kHeadDim + c] = l > 0.f ? acc / l : 0.f;
+}
+
+hipError_t launch_decode_mfma(const kvq_geom& g, const DecodePlan& plan, int n_q_heads, const uint16_t* q,
+                              const uint8_t* cache, const int64_t* seq_byte_off, const int32_t* seq_len, int n_seq,
+                              int64_t max_len, const uint8_t* k_bits, const float* k_sigma, const float* v_sigma,
+                              float scale_log2, float* workspace, hipStream_t st);
+
+int plan_decode(const kvq_geom& g, int n_q_heads, int n_seq, int64_t max_len, int kernel, int tiles_per_split,
+                DecodePlan* plan) {
+    const int grp = n_q_heads / g.n_kv_heads;
+    const bool mfma_ok = kMfmaKernel && g.k_budget <= 8 * kMaxBlocks && g.v_bits <= 8 && grp <= 8;
+    if (kernel == KVQ_DECODE_AUTO) kernel = mfma_ok ? KVQ_DECODE_MFMA : KVQ_DECODE_GENERIC;
+    if (kernel == KVQ_DECODE_MFMA && !mfma_ok) return KVQ_ERR_SHAPE;
+    if (kernel == KVQ_DECODE_GENERIC && grp > kGenericMaxGroup) return KVQ_ERR_SHAPE;
+    if (kernel != KVQ_DECODE_MFMA && kernel != KVQ_DECODE_GENERIC) return KVQ_ERR_ARG;
+    const int64_t n_tiles = (max_len + kTile - 1) / kTile;
+    int64_t T = tiles_per_split;
+    if (T <= 0) {
+        // enough chunks to give every CU several workgroups, but chunks of at least
+        // 4 tiles (MFMA) so the merge traffic stays small against the cache bytes
+        const int64_t units = (int64_t)n_seq * g.n_kv_heads;
+        const int64_t target = kernel == KVQ_DECODE_MFMA ? 1024 : 512;
+        int64_t want = (target + units - 1) / (units > 0 ? units : 1);
+        if (want < 1) want = 1;
+        T = (n_tiles + want - 1) / want;
+        const int64_t minT = kernel == KVQ_DECODE_MFMA ? 4 : 1;
+        if (T < minT) T = minT;
+    }
+    int64_t ns = n_tiles > 0 ? (n_tiles + T - 1) / T : 1;
+    if (ns > 65535) return KVQ_ERR_CAPACITY;
+    plan->kernel = kernel;
+    plan->tiles_per_split = (int)T;
+    plan->n_split = (int)ns;
+    plan->workspace = (int64_t)n_seq * n_q_heads * ns * (kHeadDim + 2) * 4;
+    return 0;
+}
+
+hipError_t launch_decode(const kvq_geom& g, const DecodePlan& plan, int n_q_heads, const uint16_t* q,
+                         const uint8_t* cache, const int64_t* seq_byte_off, const int32_t* seq_len, int n_seq,
+                         int64_t max_len, const uint8_t* k_bits, const float* k_sigma, const float* v_sigma,
+                         float softmax_scale, float* out, float* workspace, hipStream_t st) {
+    const float scale_log2 = softmax_scale * kLog2e;
+    const int grp = n_q_heads / g.n_kv_heads;
+    if (plan.kernel == KVQ_DECODE_MFMA) {
+        hipError_t e = launch_decode_mfma(g, plan, n_q_heads, q, cache, seq_byte_off, seq_len, n_seq, max_len,
+                                          k_bits, k_sigma, v_sigma, scale_log2, workspace, st);
+        if (e != hipSuccess) return e;
+    } else {
+        dim3 grid(plan.n_split, g.n_kv_heads, n_seq);
+        hipLaunchKernelGGL(decode_generic_kernel, grid, dim3(256), 0, st, q, cache, seq_byte_off, seq_len, max_len,
+                           g.capacity_tokens, k_bits, k_sigma, v_sigma, scale_log2, n_q_heads, grp, g.rope_pairing,
+                           g.k_budget, g.v_bits, plan.tiles_per_split, plan.n_split, workspace);
+        hipError_t e = hipGetLastError();
+        if (e != hipSuccess) return e;
+    }
+    hipLaunchKernelGGL(merge_kernel, dim3(n_seq * n_q_heads), dim3(128), 0, st, workspace, plan.n_split, out);
+    return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,181 @@
+// kvq_energy_alloc.hip -- block energy (exact 128-bit integer reduction) and
+// greedy bit allocation, for "RoPE-Aware Bit Allocation for KV-Cache
+// Quantization" (abstract: per layer and KV head, a label-free energy score per
+// RoPE block, then integer widths handed out greedily by marginal gain).
+#include "kvq_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace kvq {
+
+// ---------------------------------------------------------------------------
+// Block energy
+// ---------------------------------------------------------------------------
+// A binary16 pattern with exponent field e and fraction m is M * 2^(e-25) with
+// M = 1024 + m (e >= 1), or m * 2^-24 (e = 0).  Its square is M^2 << (2e - 2)
+// units of 2^-48 (M^2 << 0 for e = 0): an integer below 2^82, accumulated in a
+// 128-bit (lo, hi) pair.
+__device__ __forceinline__ void acc_square(uint32_t h, uint64_t& lo, uint64_t& hi) {
+    const uint32_t e = (h >> 10) & 31u, m = h & 1023u;
+    const uint64_t M = e ? (1024u | m) : m;
+    const uint32_t sh = e ? 2u * e - 2u : 0u;
+    const uint64_t sq = M * M;
+    const uint64_t l = sq << sh;
+    const uint64_t u = sh > 42u ? (sq >> (64u - sh)) : 0ull;
+    lo += l;
+    hi += u + (lo < l ? 1ull : 0ull);
+}
+
+// 128-bit add of (alo, ahi) into a (lo, hi) pair in global memory with two 64-bit
+// atomics: the carry out of the low word is forwarded to the high word, so the
+// final value is exact whatever the interleaving.
+__device__ __forceinline__ void atomic_add_u128(uint64_t* p, uint64_t alo, uint64_t ahi) {
+    const uint64_t old = atomicAdd((unsigned long long*)p, (unsigned long long)alo);
+    const uint64_t carry = (old + alo < old) ? 1ull : 0ull;
+    if (ahi + carry) atomicAdd((unsigned long long*)(p + 1), (unsigned long long)(ahi + carry));
+}
+
+// grid: (n_heads, row blocks); block: 256 threads = 4 row lanes x 64 coordinate pairs.
+// Thread (r, j) accumulates coordinates 2j, 2j+1 of rows r, r+4, ... of its row range.
+__global__ __launch_bounds__(256) void block_energy_kernel(const uint16_t* __restrict__ x, int64_t n_tok,
+                                                          int64_t stride_tok, int64_t stride_head, int d,
+                                                          int pairing, int64_t rows_per_block,
+                                                          uint64_t* __restrict__ energy) {
+    const int h = blockIdx.x;
+    const int j = threadIdx.x & 63;
+    const int r = threadIdx.x >> 6;
+    const int npairs = d >> 1;
+    const int64_t row0 = (int64_t)blockIdx.y * rows_per_block;
+    const int64_t row1 = min(row0 + rows_per_block, n_tok);
+    uint64_t lo0 = 0, hi0 = 0, lo1 = 0, hi1 = 0;
+    if (j < npairs) {
+        const uint16_t* base = x + (int64_t)h * stride_head + 2 * j;
+        int64_t t = row0 + r;
+        // four independent rows in flight per iteration
+        for (; t + 12 < row1; t += 16) {
+            uint32_t w0 = *(const uint32_t*)(base + t * stride_tok);
+            uint32_t w1 = *(const uint32_t*)(base + (t + 4) * stride_tok);
+            uint32_t w2 = *(const uint32_t*)(base + (t + 8) * stride_tok);
+            uint32_t w3 = *(const uint32_t*)(base + (t + 12) * stride_tok);
+            acc_square(w0 & 0xffffu, lo0, hi0); acc_square(w0 >> 16, lo1, hi1);
+            acc_square(w1 & 0xffffu, lo0, hi0); acc_square(w1 >> 16, lo1, hi1);
+            acc_square(w2 & 0xffffu, lo0, hi0); acc_square(w2 >> 16, lo1, hi1);
+            acc_square(w3 & 0xffffu, lo0, hi0); acc_square(w3 >> 16, lo1, hi1);
+        }
+        for (; t < row1; t += 4) {
+            uint32_t w0 = *(const uint32_t*)(base + t * stride_tok);
+            acc_square(w0 & 0xffffu, lo0, hi0); acc_square(w0 >> 16, lo1, hi1);
+        }
+    }
+    // reduce the 4 row lanes per coordinate, then pair coordinates into blocks
+    __shared__ uint64_t s_lo[4][128], s_hi[4][128];
+    s_lo[r][2 * j] = lo0; s_hi[r][2 * j] = hi0;
+    s_lo[r][2 * j + 1] = lo1; s_hi[r][2 * j + 1] = hi1;
+    __syncthreads();
+    uint64_t clo = 0, chi = 0;
+    if (threadIdx.x < 128) {
+        const int c = threadIdx.x;
+        clo = s_lo[0][c];
+        chi = s_hi[0][c];
+        for (int q = 1; q < 4; ++q) {
+            clo += s_lo[q][c];
+            chi += s_hi[q][c] + (clo < s_lo[q][c] ? 1ull : 0ull);
+        }
+    }
+    __syncthreads();
+    if (threadIdx.x < 128) {
+        s_lo[0][threadIdx.x] = clo;
+        s_hi[0][threadIdx.x] = chi;
+    }
+    __syncthreads();
+    if ((int)threadIdx.x < npairs) {
+        const int i = threadIdx.x;
+        const int p = pairing == KVQ_PAIR_HALF ? i : 2 * i;
+        const int q = pairing == KVQ_PAIR_HALF ? i + npairs : 2 * i + 1;
+        uint64_t lo = s_lo[0][p], hi = s_hi[0][p];
+        lo += s_lo[0][q];
+        hi += s_hi[0][q] + (lo < s_lo[0][q] ? 1ull : 0ull);
+        if (lo | hi) atomic_add_u128(energy + ((int64_t)h * npairs + i) * 2, lo, hi);
+    }
+}
+
+hipError_t launch_block_energy(const uint16_t* x, int64_t n_tok, int64_t stride_tok, int64_t stride_head,
+                               int n_heads, int d, int pairing, uint64_t* energy, hipStream_t st) {
+    // about 2048 workgroups in total, at least 64 rows each
+    int64_t blocks_per_head = (2048 + n_heads - 1) / n_heads;
+    int64_t rows = (n_tok + blocks_per_head - 1) / blocks_per_head;
+    if (rows < 64) rows = 64;
+    rows = (rows + 15) / 16 * 16;
+    const int64_t nby = (n_tok + rows - 1) / rows;
+    dim3 grid(n_heads, (unsigned)nby);
+    hipLaunchKernelGGL(block_energy_kernel, grid, dim3(256), 0, st, x, n_tok, stride_tok, stride_head, d, pairing,
+                       rows, energy);
+    return hipGetLastError();
+}
+
+// ---------------------------------------------------------------------------
+// Allocation
+// ---------------------------------------------------------------------------
+// unsigned 128-bit integer -> double, round to nearest even
+__device__ __forceinline__ double u128_to_f64(uint64_t lo, uint64_t hi) {
+    if (hi == 0 && lo < (1ull << 53)) return (double)lo;  // exact
+    const int top = hi ? 127 - __clzll(hi) : 63 - __clzll(lo);
+    const int drop = top - 52;  // 1..75 bits below the kept 53
+    uint64_t keep;
+    if (drop >= 64) keep = hi >> (drop - 64);
+    else keep = (hi << (64 - drop)) | (lo >> drop);
+    const int rb = drop - 1;  // round bit position
+    const uint64_t round_bit = rb >= 64 ? (hi >> (rb - 64)) & 1ull : (lo >> rb) & 1ull;
+    bool sticky;
+    if (rb >= 64) sticky = lo != 0 || (rb > 64 && (hi & ((1ull << (rb - 64)) - 1ull)) != 0);
+    else sticky = rb > 0 && (lo & ((1ull << rb) - 1ull)) != 0;
+    if (round_bit && (sticky || (keep & 1ull))) keep += 1;
+    return ldexp((double)keep, drop);
+}
+
+// one wave per unit; lane i = block i
+__global__ __launch_bounds__(64) void allocate_kernel(const uint64_t* __restrict__ energy, int nb, int budget,
+                                                     int mode, uint8_t* __restrict__ bits,
+                                                     float* __restrict__ sigma) {
+    const int u = blockIdx.x, i = threadIdx.x;
+    const bool act = i < nb;
+    const uint64_t lo = act ? energy[((int64_t)u * nb + i) * 2] : 0ull;
+    const uint64_t hi = act ? energy[((int64_t)u * nb + i) * 2 + 1] : 0ull;
+    const double E = ldexp(u128_to_f64(lo, hi), -48);
+    uint64_t tlo = lo, thi = hi;
+    for (int off = 32; off >= 1; off >>= 1) {
+        const uint64_t olo = __shfl_xor(tlo, off), ohi = __shfl_xor(thi, off);
+        tlo += olo;
+        thi += ohi + (tlo < olo ? 1ull : 0ull);
+    }
+    const double Etot = ldexp(u128_to_f64(tlo, thi), -48);
+    int b = 0;
+    if (budget == 16 * nb) {
+        b = 16;
+    } else if (mode == KVQ_UNIFORM) {
+        b = budget / nb;
+    } else {
+        for (int step = 0; step < budget; ++step) {
+            double g = (act && b < 8) ? E * (double)c_gain_dd[b] : -1.0;
+            int idx = i;
+            for (int off = 32; off >= 1; off >>= 1) {
+                const double og = __shfl_xor(g, off);
+                const int oi = __shfl_xor(idx, off);
+                if (og > g || (og == g && oi < idx)) { g = og; idx = oi; }
+            }
+            if (idx == i) ++b;
+        }
+    }
+    if (act) {
+        bits[(int64_t)u * nb + i] = (uint8_t)b;
+        sigma[(int64_t)u * nb + i] = Etot > 0.0 ? (float)sqrt(E / (2.0 * Etot)) : 0.0f;
+    }
+}
+
+hipError_t launch_allocate(const uint64_t* energy, int n_units, int nb, int budget, int mode, uint8_t* bits,
+                           float* sigma, hipStream_t st) {
+    hipLaunchKernelGGL(allocate_kernel, dim3(n_units), dim3(64), 0, st, energy, nb, budget, mode, bits, sigma);
+    return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,58 @@
+// kvq_internal.h -- device helpers, constant tables and launch wrappers shared by
+// the HIP translation units of libkvq.so (gfx950 / CDNA4, wave64).
+#pragma once
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/kvq.h"
+#include "kvq_codebooks.inc"
+
+namespace kvq {
+
+constexpr int kTile = 64;       // token slots per tile
+constexpr int kHeadDim = 128;   // head_dim served by quantize/attention
+constexpr int kMaxBlocks = 64;  // d/2 for d = 128
+constexpr float kLog2e = 1.4426950408889634f;
+
+// Codebook tables in constant memory (one copy per translation unit); width w
+// occupies entries [KVQ_CB_OFF(w), KVQ_CB_OFF(w) + 2^w).
+static __constant__ unsigned short c_levels[510] = {KVQ_LEVELS_FP16_LIST};
+static __constant__ float c_thresholds[510] = {KVQ_THRESHOLDS_LIST};
+static __constant__ float c_gain_dd[8] = {KVQ_GAIN_DD_LIST};
+
+// binary16 bit pattern -> float (exact)
+__device__ __forceinline__ float h2f(uint32_t bits16) {
+    return (float)__builtin_bit_cast(_Float16, (uint16_t)bits16);
+}
+
+// ---- layout ----
+__host__ __device__ inline int64_t k_record_bytes(int k_budget) { return 16 * ((2 * (int64_t)k_budget + 127) / 128); }
+__host__ __device__ inline int64_t tile_bytes(int d, int k_budget, int v_bits) {
+    return kTile * k_record_bytes(k_budget) + (int64_t)d * 8 * v_bits + 2 * kTile * 4;
+}
+
+// ---- launch wrappers (host side, one per kernel family) ----
+hipError_t launch_block_energy(const uint16_t* x, int64_t n_tok, int64_t stride_tok, int64_t stride_head,
+                               int n_heads, int d, int pairing, uint64_t* energy, hipStream_t st);
+hipError_t launch_allocate(const uint64_t* energy, int n_units, int nb, int budget, int mode, uint8_t* bits,
+                           float* sigma, hipStream_t st);
+hipError_t launch_quantize_pack(const kvq_geom& g, const uint16_t* k, const uint16_t* v, int64_t stride_tok,
+                                int64_t stride_head, int n_seq, const int64_t* first_slot, const int32_t* n_new,
+                                const int64_t* src_row0, int max_new, const uint8_t* k_bits, const float* k_sigma,
+                                const float* v_sigma, uint8_t* cache, const int64_t* seq_byte_off, hipStream_t st);
+
+struct DecodePlan {
+    int kernel;           // KVQ_DECODE_GENERIC or KVQ_DECODE_MFMA
+    int tiles_per_split;  // 64-token tiles per chunk
+    int n_split;          // chunks per (sequence, KV head)
+    int64_t workspace;    // bytes
+};
+// Returns 0 and fills the plan, or a negative kvq_status.
+int plan_decode(const kvq_geom& g, int n_q_heads, int n_seq, int64_t max_len, int kernel, int tiles_per_split,
+                DecodePlan* plan);
+hipError_t launch_decode(const kvq_geom& g, const DecodePlan& plan, int n_q_heads, const uint16_t* q,
+                         const uint8_t* cache, const int64_t* seq_byte_off, const int32_t* seq_len, int n_seq,
+                         int64_t max_len, const uint8_t* k_bits, const float* k_sigma, const float* v_sigma,
+                         float softmax_scale, float* out, float* workspace, hipStream_t st);
+
+}  // namespace kvq

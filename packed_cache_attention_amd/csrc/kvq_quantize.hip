@@ -1,0 +1,194 @@
+// kvq_quantize.hip -- per-token norm, Lloyd-Max codes at the allocated widths and
+// bit packing into 64-slot tiles (packed layout v1), for "RoPE-Aware Bit
+// Allocation for KV-Cache Quantization" (abstract: TQ-MSE codes at the widths the
+// Block-GTQ allocator assigns, kept in a packed cache).
+//
+// One workgroup owns one (sequence, KV head, tile): it is the only writer of that
+// tile during the call, so partially filled tiles are updated with plain
+// read-modify-write.  Phase 1: each wave takes tokens; lane l holds coordinates
+// 2l, 2l+1, forms the squared-norm tree with xor-butterflies (level 1 is the
+// lane's own pair, level k the butterfly with mask 2^(k-2)), and finds each code
+// by binary search over the monotone threshold products.  Phase 2: the tile's K
+// records, V runs and scales are assembled dword by dword from the codes in LDS.
+#include "kvq_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace kvq {
+
+// code = #{ j in 1..2^w-1 : x >= RN32(s * RN32(sig * thr_w[j])) }; the products are
+// non-decreasing in j, so the count is found by binary lifting.
+__device__ __forceinline__ uint32_t code_of(float x, int w, float sig, float s) {
+    const float* thr = c_thresholds + KVQ_CB_OFF(w);
+    uint32_t code = 0;
+    for (int bit = 1 << (w - 1); bit >= 1; bit >>= 1) {
+        const uint32_t cand = code + bit;
+        const float a = sig * thr[cand];
+        const float b = s * a;
+        if (x >= b) code = cand;
+    }
+    return code;
+}
+
+__device__ __forceinline__ uint32_t encode(uint32_t bits16, int w, float sig, float s) {
+    if (w == 0) return 0;
+    if (w == 16) return bits16;
+    return code_of(h2f(bits16), w, sig, s);
+}
+
+// balanced pairwise binary32 tree over the 128 squares (lane l: coordinates 2l, 2l+1)
+__device__ __forceinline__ float token_norm(uint32_t pair) {
+    const float a = h2f(pair & 0xffffu), b = h2f(pair >> 16);
+    float t = a * a + b * b;  // both squares exact in binary32
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) t = t + __shfl_xor(t, m);
+    return sqrtf(t);  // correctly rounded on gfx950
+}
+
+__global__ __launch_bounds__(256) void quantize_pack_kernel(
+    const uint16_t* __restrict__ kx, const uint16_t* __restrict__ vx, int64_t stride_tok, int64_t stride_head,
+    const int64_t* __restrict__ first_slot, const int32_t* __restrict__ n_new, const int64_t* __restrict__ src_row0,
+    int max_new, int64_t capacity, const uint8_t* __restrict__ k_bits, const float* __restrict__ k_sigma,
+    const float* __restrict__ v_sigma, uint8_t* __restrict__ cache, const int64_t* __restrict__ seq_byte_off,
+    int pairing, int k_budget, int v_bits) {
+    const int s = blockIdx.z, h = blockIdx.y;
+    const int64_t first = first_slot[s];
+    const int n = n_new[s];
+    if (first < 0 || n <= 0 || n > max_new || first + n > capacity) return;
+    const int64_t tau = first / kTile + blockIdx.x;
+    const int64_t tile0 = tau * kTile;
+    const int64_t lo_slot = max(first, tile0), hi_slot = min(first + (int64_t)n, tile0 + kTile);
+    if (lo_slot >= hi_slot) return;
+
+    const int64_t SK = k_record_bytes(k_budget);
+    const int64_t TB = tile_bytes(kHeadDim, k_budget, v_bits);
+    const int64_t n_tiles = capacity / kTile;
+    uint8_t* tile = cache + seq_byte_off[s] + ((int64_t)h * n_tiles + tau) * TB;
+
+    __shared__ uint16_t s_kc[kTile][kHeadDim];
+    __shared__ uint16_t s_vc[kTile][kHeadDim];
+    __shared__ float s_ks[kTile], s_vs[kTile];
+    __shared__ uint8_t s_w[kHeadDim];          // key width per coordinate
+    __shared__ float s_ksig[kHeadDim], s_vsig[kHeadDim];
+    __shared__ uint8_t s_bw[kMaxBlocks];       // key width per block
+    __shared__ uint8_t s_fc[kHeadDim];         // K order: coordinate of field f
+    __shared__ uint16_t s_fo[kHeadDim];        // bit offset of field f in the record
+    __shared__ uint8_t s_fw[kHeadDim];         // width of field f
+    __shared__ uint8_t s_first[64];            // first field touching record dword k
+    __shared__ int s_nf;
+
+    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+
+    // ---- phase 0: per-head tables and the K order ----
+    if (tid < kMaxBlocks) {
+        const int i = tid;
+        const int w = k_bits[h * kMaxBlocks + i];
+        const int p = pairing == KVQ_PAIR_HALF ? i : 2 * i;
+        const int q = pairing == KVQ_PAIR_HALF ? i + kMaxBlocks : 2 * i + 1;
+        s_bw[i] = (uint8_t)w;
+        s_w[p] = s_w[q] = (uint8_t)w;
+        s_ksig[p] = s_ksig[q] = k_sigma[h * kMaxBlocks + i];
+        s_vsig[p] = s_vsig[q] = v_sigma[h * kMaxBlocks + i];
+    }
+    __syncthreads();
+    if (tid < kMaxBlocks) {
+        const int i = tid, w = s_bw[i];
+        int rank = 0, off = 0;
+        for (int j = 0; j < kMaxBlocks; ++j) {
+            const int wj = s_bw[j];
+            if (wj > w || (wj == w && j < i)) { ++rank; off += 2 * wj; }
+        }
+        // blocks of width 0 sort last and hold no field
+        if (w > 0) {
+            const int p = pairing == KVQ_PAIR_HALF ? i : 2 * i;
+            const int q = pairing == KVQ_PAIR_HALF ? i + kMaxBlocks : 2 * i + 1;
+            s_fc[2 * rank] = (uint8_t)p; s_fo[2 * rank] = (uint16_t)off; s_fw[2 * rank] = (uint8_t)w;
+            s_fc[2 * rank + 1] = (uint8_t)q; s_fo[2 * rank + 1] = (uint16_t)(off + w); s_fw[2 * rank + 1] = (uint8_t)w;
+        }
+        const unsigned long long nz = __ballot(w > 0);
+        if (i == 0) {
+            const int nf = 2 * __popcll(nz);
+            s_nf = nf;
+        }
+    }
+    __syncthreads();
+    const int nf = s_nf;
+    if (tid < (int)(SK / 4)) {
+        int f = 0;
+        while (f < nf && s_fo[f] + s_fw[f] <= 32 * tid) ++f;
+        s_first[tid] = (uint8_t)f;
+    }
+
+    // ---- phase 1: codes ----
+    for (int64_t slot = lo_slot + wave; slot < hi_slot; slot += 4) {
+        const int p = (int)(slot - tile0);
+        const int64_t row = src_row0[s] + (slot - first);
+        const uint32_t kp = *(const uint32_t*)(kx + row * stride_tok + (int64_t)h * stride_head + 2 * lane);
+        const uint32_t vp = *(const uint32_t*)(vx + row * stride_tok + (int64_t)h * stride_head + 2 * lane);
+        const float sk = token_norm(kp), sv = token_norm(vp);
+        const int c0 = 2 * lane, c1 = 2 * lane + 1;
+        s_kc[p][c0] = (uint16_t)encode(kp & 0xffffu, s_w[c0], s_ksig[c0], sk);
+        s_kc[p][c1] = (uint16_t)encode(kp >> 16, s_w[c1], s_ksig[c1], sk);
+        s_vc[p][c0] = (uint16_t)encode(vp & 0xffffu, v_bits, s_vsig[c0], sv);
+        s_vc[p][c1] = (uint16_t)encode(vp >> 16, v_bits, s_vsig[c1], sv);
+        if (lane == 0) { s_ks[p] = sk; s_vs[p] = sv; }
+    }
+    __syncthreads();
+
+    // ---- phase 2: assemble the tile ----
+    const int lo_p = (int)(lo_slot - tile0), hi_p = (int)(hi_slot - tile0);
+    const bool whole = lo_p == 0 && hi_p == kTile;
+    // K records (each belongs to one slot: plain stores)
+    const int skd = (int)(SK / 4);
+    uint32_t* krec = (uint32_t*)tile;
+    for (int idx = tid; idx < kTile * skd; idx += 256) {
+        const int p = idx / skd, k = idx - p * skd;
+        if (p < lo_p || p >= hi_p) continue;
+        uint32_t val = 0;
+        const int lo_bit = 32 * k;
+        for (int f = s_first[k]; f < nf && s_fo[f] < lo_bit + 32; ++f) {
+            const uint32_t code = s_kc[p][s_fc[f]];
+            const int sh = (int)s_fo[f] - lo_bit;
+            val |= sh >= 0 ? (code << sh) : (code >> (-sh));
+        }
+        krec[idx] = val;
+    }
+    // V runs (shared by slots: read-modify-write unless the whole tile is new)
+    const int vd = 2 * v_bits;
+    uint32_t* vrun = (uint32_t*)(tile + kTile * SK);
+    for (int idx = tid; idx < kHeadDim * vd; idx += 256) {
+        const int c = idx / vd, k = idx - c * vd;
+        const int lo_bit = 32 * k;
+        const int pa = max(lo_bit / v_bits, lo_p);
+        const int pb = min((lo_bit + 31) / v_bits, hi_p - 1);
+        uint32_t val = 0;
+        for (int p = pa; p <= pb; ++p) {
+            const uint32_t code = s_vc[p][c];
+            const int sh = p * v_bits - lo_bit;
+            val |= sh >= 0 ? (code << sh) : (code >> (-sh));
+        }
+        if (whole) vrun[idx] = val;
+        else if (pa <= pb) vrun[idx] |= val;
+    }
+    // scales
+    float* scl = (float*)(tile + kTile * SK + kHeadDim * 8 * v_bits);
+    if (tid >= lo_p && tid < hi_p) {
+        scl[tid] = s_ks[tid];
+        scl[kTile + tid] = s_vs[tid];
+    }
+}
+
+hipError_t launch_quantize_pack(const kvq_geom& g, const uint16_t* k, const uint16_t* v, int64_t stride_tok,
+                                int64_t stride_head, int n_seq, const int64_t* first_slot, const int32_t* n_new,
+                                const int64_t* src_row0, int max_new, const uint8_t* k_bits, const float* k_sigma,
+                                const float* v_sigma, uint8_t* cache, const int64_t* seq_byte_off, hipStream_t st) {
+    // a run of max_new slots starting anywhere touches at most ceil(max_new/64) + 1 tiles
+    const int tiles = (max_new + kTile - 1) / kTile + 1;
+    dim3 grid(tiles, g.n_kv_heads, n_seq);
+    hipLaunchKernelGGL(quantize_pack_kernel, grid, dim3(256), 0, st, k, v, stride_tok, stride_head, first_slot,
+                       n_new, src_row0, max_new, g.capacity_tokens, k_bits, k_sigma, v_sigma, cache, seq_byte_off,
+                       g.rope_pairing, g.k_budget, g.v_bits);
+    return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -1,0 +1,102 @@
+"""Host-side checks of libkvq.so: it loads, exports every symbol include/kvq.h
+declares, carries the same codebook the oracle derives independently, sizes the
+layout as specified, and rejects invalid calls on the host before any GPU work
+(these calls never reach HIP, so they run without a GPU)."""
+import ctypes as C
+import os
+import re
+
+import numpy as np
+import pytest
+
+import oracle
+from packed_cache_attention_amd import kvq
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+
+
+def test_exports_match_header():
+    hdr = open(os.path.join(ROOT, "include", "kvq.h")).read()
+    declared = set(re.findall(r"^\s*(?:int32_t|int64_t|const char \*)\s*(kvq_\w+)\(", hdr, re.M))
+    assert declared == set(kvq.EXPORTS)
+    L = kvq.lib()
+    for name in declared:
+        assert hasattr(L, name), name
+    assert L.kvq_version() == 1
+
+
+@pytest.mark.parametrize("w", range(1, 9))
+def test_codebook_matches_oracle(w):
+    lev, thr, dd = kvq.get_codebook(w)
+    cb = oracle.codebook(w)
+    np.testing.assert_array_equal(lev, cb["levels_fp16"])
+    np.testing.assert_array_equal(thr, cb["thresholds"])
+    np.testing.assert_array_equal(dd, oracle.tables()["dD"])
+
+
+@pytest.mark.parametrize("kb,vb", [(192, 3), (128, 2), (192, 2), (1024, 16), (0, 1), (300, 8), (7, 5)])
+def test_layout_sizes(kb, vb):
+    g = kvq.geom(3, kb, vb, 640)
+    assert kvq.tile_bytes(g) == oracle.tile_bytes(128, kb, vb)
+    assert kvq.cache_bytes(g) == 3 * 10 * oracle.tile_bytes(128, kb, vb)
+
+
+def test_workspace_bytes_and_plan():
+    g = kvq.geom(2, 192, 3, 131072)
+    ws = kvq.decode_workspace_bytes(g, 16, 1, 131072)
+    assert ws > 0 and ws % 4 == 0
+    ws2 = kvq.decode_workspace_bytes(g, 16, 1, 131072, kvq.DECODE_GENERIC, 8)
+    assert ws2 == 1 * 16 * (2048 // 8) * 130 * 4
+    assert kvq.decode_workspace_bytes(g, 16, 1, 0) >= 0
+
+
+def _st(r):
+    return int(r)
+
+
+FAKE = 1 << 20  # a non-null, 16-byte aligned address that is never dereferenced
+
+
+def test_host_validation_rejects_before_gpu():
+    L = kvq.lib()
+    good = kvq.geom(2, 192, 3, 1024)
+    st = L.kvq_block_energy(None, FAKE, 10, 256, 128, FAKE, None)
+    assert st == -1
+    bad = kvq.geom(2, 192, 3, 1024)
+    bad.layout_version = 2
+    assert L.kvq_block_energy(C.byref(bad), FAKE, 10, 256, 128, FAKE, None) == -8
+    bad = kvq.geom(2, 192, 3, 1024, head_dim=7)
+    assert L.kvq_block_energy(C.byref(bad), FAKE, 10, 256, 128, FAKE, None) == -2
+    bad = kvq.geom(2, 600, 3, 1024)
+    assert L.kvq_block_energy(C.byref(bad), FAKE, 10, 256, 128, FAKE, None) == -3
+    bad = kvq.geom(2, 192, 9, 1024)
+    assert L.kvq_block_energy(C.byref(bad), FAKE, 10, 256, 128, FAKE, None) == -3
+    bad = kvq.geom(2, 192, 3, 1000)
+    assert L.kvq_block_energy(C.byref(bad), FAKE, 10, 256, 128, FAKE, None) == -5
+    # misaligned input / odd stride / null energy / negative count
+    assert L.kvq_block_energy(C.byref(good), FAKE + 2, 10, 256, 128, FAKE, None) == -4
+    assert L.kvq_block_energy(C.byref(good), FAKE, 10, 255, 128, FAKE, None) == -4
+    assert L.kvq_block_energy(C.byref(good), FAKE, 10, 256, 128, None, None) == -1
+    assert L.kvq_block_energy(C.byref(good), FAKE, -1, 256, 128, FAKE, None) == -1
+    assert L.kvq_block_energy(C.byref(good), FAKE, 0, 256, 128, FAKE, None) == 0  # nothing to do
+    # allocation: budgets and modes
+    for budget, mode, want in ((513, 0, -3), (-1, 0, -3), (100, 1, -3), (192, 2, -1), (1024, 1, 0)):
+        r = L.kvq_allocate_bits(C.byref(good), FAKE, 0 if want == 0 else 4, budget, mode, FAKE, FAKE, None)
+        assert r == want, (budget, mode, r)
+    # quantize: head_dim must be 128; capacity
+    g64 = kvq.geom(2, 64, 3, 1024, head_dim=64)
+    args = (FAKE, FAKE, 256, 128, 1, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert L.kvq_quantize_pack(C.byref(g64), *args) == -2
+    args_cap = (FAKE, FAKE, 256, 128, 1, FAKE, FAKE, FAKE, 2048, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert L.kvq_quantize_pack(C.byref(good), *args_cap) == -5
+    args_al = (FAKE + 2, FAKE, 255, 128, 1, FAKE, FAKE, FAKE, 4, FAKE, FAKE, FAKE, FAKE, FAKE, None)
+    assert L.kvq_quantize_pack(C.byref(good), *args_al) == -4
+    # decode: GQA ratio, capacity, workspace, alignment
+    d_args = lambda nq, max_len, ws, q=FAKE: (C.byref(good), nq, q, FAKE, FAKE, FAKE, 1, max_len, FAKE, FAKE, FAKE,
+                                              0.1, FAKE, FAKE, ws, 0, 0, None)
+    assert L.kvq_packed_decode_attn_ex(*d_args(3, 512, 1 << 30)) == -2
+    assert L.kvq_packed_decode_attn_ex(*d_args(64, 512, 1 << 30)) == -2  # ratio 32 > 16
+    assert L.kvq_packed_decode_attn_ex(*d_args(16, 2048, 1 << 30)) == -5
+    assert L.kvq_packed_decode_attn_ex(*d_args(16, 512, 16)) == -6
+    assert L.kvq_packed_decode_attn_ex(*d_args(16, 512, 1 << 30, q=FAKE + 8)) == -4
+    assert kvq.status_string(-6) == "workspace too small"

@@ -1,0 +1,199 @@
+"""GPU parity: the HIP library against the CPU oracle on the same seeded inputs.
+
+Energies, widths, scales and packed bytes must match bit for bit; decode
+attention must agree per (sequence, query head) within 2e-3 of max|o_ref|.
+Shapes span several tiles, ragged tails, empty and one-token sequences, all
+budget kinds (K3V3, K2V2, K3V2, K-only V16, K16V16 passthrough, odd budgets),
+both RoPE pairings, batches and appends.
+"""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from packed_cache_attention_amd import kvq, synth
+
+from pipeline import check_attention, energy_u64, gpu_energy, run_batch, say
+
+pytestmark = pytest.mark.gpu
+
+rng = np.random.default_rng(2024)
+
+
+def _rand(n, H, d=128, scale=1.0, seed=0):
+    g = torch.Generator().manual_seed(seed)
+    return (torch.randn(n, H, d, generator=g, dtype=torch.float64) * scale).to(torch.float16)
+
+
+def _heads(wl, n, seed=0, seq=0, layer=0):
+    return synth.gen_layer(wl, seq, layer, n_tok=n, seed=seed)
+
+
+# ----------------------------------------------------------------- energy + allocation
+
+@pytest.mark.parametrize("d", [2, 4, 6, 8, 16, 64, 128])
+@pytest.mark.parametrize("pairing", [0, 1])
+def test_energy_and_allocation_bit_exact(d, pairing):
+    say("energy/alloc d=%d pairing=%d" % (d, pairing))
+    H = 3
+    x = _rand(257, H, d, scale=20.0, seed=d)
+    flat = x.view(-1)
+    # special values: subnormals, zeros, extremes
+    idx = torch.from_numpy(rng.choice(flat.numel(), 12, replace=False))
+    flat[idx] = torch.tensor([6e-8, -6e-8, 0.0, -0.0, 65504, -65504, 1e-5, -3e-6, 2.0, -1.0, 1e-7, 300],
+                             dtype=torch.float16)
+    nb = d // 2
+    g = kvq.geom(H, nb * 3 if nb * 3 <= 8 * nb else 0, 3, 0, head_dim=d, rope_pairing=pairing)
+    e = gpu_energy(g, [x[:100], x[100:]])
+    oe = oracle.block_energy(x.numpy(), pairing)
+    np.testing.assert_array_equal(energy_u64(e), oe)
+    budgets = sorted(set([0, 1, nb, 3 * nb, 8 * nb, 16 * nb] + list(rng.integers(0, 8 * nb + 1, 6))))
+    for budget in budgets:
+        for mode in (kvq.GREEDY, kvq.UNIFORM):
+            if mode == kvq.UNIFORM and budget % nb and budget != 16 * nb:
+                continue
+            bits = torch.empty(H, nb, dtype=torch.uint8, device="cuda")
+            sig = torch.empty(H, nb, dtype=torch.float32, device="cuda")
+            kvq.allocate_bits(g, e, int(budget), mode, bits, sig)
+            ob, os_ = oracle.allocate(oe, int(budget), mode)
+            np.testing.assert_array_equal(bits.cpu().numpy(), ob, err_msg="budget %d mode %d" % (budget, mode))
+            np.testing.assert_array_equal(sig.cpu().numpy().view(np.uint32), os_.view(np.uint32))
+
+
+def test_energy_accumulates_exactly_with_strides():
+    say("energy strided")
+    H, d = 4, 128
+    big = _rand(300, H + 2, d + 8, seed=5)  # padded rows and heads: strides != dense
+    x = big[:, 1:H + 1, :d]
+    g = kvq.geom(H, 192, 3, 0)
+    e = torch.zeros(H, 64, 2, dtype=torch.int64, device="cuda")
+    xd = big.cuda()[:, 1:H + 1, :d]
+    kvq.block_energy(g, xd, e)
+    kvq.block_energy(g, xd, e)  # accumulate twice
+    oe = oracle.block_energy(np.ascontiguousarray(x.numpy()))
+    oracle.block_energy(np.ascontiguousarray(x.numpy()), energy=oe)
+    np.testing.assert_array_equal(energy_u64(e), oe)
+
+
+# ----------------------------------------------------------------- full pipeline
+
+CASES = [
+    # name, H_kv, group, n tokens, capacity, k_budget, v_bits, pairing
+    ("k3v3-1tile", 1, 1, 64, 64, 192, 3, 0),
+    ("k3v3-ragged", 2, 8, 150, 192, 192, 3, 0),
+    ("k2v2-ragged", 2, 4, 321, 384, 128, 2, 0),
+    ("k3v2-gqa7", 2, 7, 200, 256, 192, 2, 0),
+    ("kodd-v5", 1, 3, 77, 128, 131, 5, 0),
+    ("k8v8-max", 1, 2, 130, 192, 512, 8, 0),
+    ("k0v1", 1, 2, 65, 128, 0, 1, 0),
+    ("konly-v16", 2, 2, 100, 128, 192, 16, 0),
+    ("k16v16-pass", 1, 4, 90, 128, 1024, 16, 0),
+    ("interleaved", 2, 2, 140, 192, 160, 4, 1),
+    ("gqa16", 1, 16, 70, 128, 192, 3, 0),
+]
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_pipeline_matches_oracle(case):
+    name, H, grp, n, cap, kb, vb, pairing = case
+    say("pipeline %s" % name)
+    wl = synth.Workload(name, 1, H * grp, H, 1e6, (n,), kb, vb, "decay")
+    K, V, q = _heads(wl, n, seed=7)
+    if pairing == 1:  # the generator rotates half-split planes; any fp16 keys are valid input
+        K = K[:, :, torch.randperm(128, generator=torch.Generator().manual_seed(3))].contiguous()
+    run_batch([(K, V, q)], kb, vb, cap, pairing=pairing)
+
+
+def test_passthrough_attention_is_exact_softmax():
+    """K16V16: decode attention equals fp64 softmax attention of the fp16 cache."""
+    say("passthrough exact")
+    H, grp, n = 2, 3, 150
+    K, V = _rand(n, H, seed=11), _rand(n, H, seed=12)
+    q = _rand(H * grp, 1, seed=13)[:, 0, :]
+    r = run_batch([(K, V, q)], 1024, 16, 192, oracle_attn=False)
+    for h in range(H * grp):
+        k = K[:, h // grp].double().numpy()
+        v = V[:, h // grp].double().numpy()
+        z = k @ q[h].double().numpy() / np.sqrt(128)
+        p = np.exp(z - z.max())
+        ref = (p / p.sum()) @ v
+        check_attention(r["out"][0, h][None], ref[None])
+
+
+def test_c1_configuration():
+    wl = synth.WORKLOADS["c1"]
+    say("c1 %s" % wl.name)
+    K, V, q = synth.gen_layer(wl, 0, 0)
+    run_batch([(K, V, q)], wl.k_budget, wl.v_bits, 1024)
+
+
+def test_batch_ragged_lengths():
+    """A batch of sequences of different lengths (one allocation shared per head)."""
+    say("batch ragged")
+    wl = synth.Workload("batch", 1, 14, 2, 1e6, (0,), 192, 2, "decay")
+    lens = [1, 63, 64, 65, 200, 0, 129]
+    seqs = []
+    for s, n in enumerate(lens):
+        K, V, q = synth.gen_layer(wl.with_lens(lens), s, 0, n_tok=n, seed=3)
+        seqs.append((K, V, q))
+    r = run_batch(seqs, 192, 2, 256)
+    assert np.all(r["out"][5] == 0)  # empty sequence -> zeros
+
+
+def test_appends_equal_bulk_and_decode_after_append():
+    """Bulk quantization, then token-by-token and chunked appends at ragged slots,
+    give the same bytes as the oracle's bulk quantization of all tokens."""
+    say("appends")
+    wl = synth.Workload("app", 1, 8, 2, 1e6, (0,), 192, 3, "decay")
+    n0, n1 = 70, 60
+    K, V, q = synth.gen_layer(wl.with_lens([n0 + n1]), 0, 0, n_tok=n0 + n1, seed=9)
+    r = run_batch([(K[:n0], V[:n0], q)], 192, 3, 256, check_attn=False)
+    g, cache, off = r["g"], r["cache"], r["off"]
+    Kd, Vd = K.cuda(), V.cuda()
+    slot = n0
+    chunks = [1, 1, 5, 17, 1, 35]
+    for c in chunks:
+        first = torch.tensor([slot], dtype=torch.int64, device="cuda")
+        nn = torch.tensor([c], dtype=torch.int32, device="cuda")
+        src = torch.tensor([slot], dtype=torch.int64, device="cuda")
+        kvq.quantize_pack(g, Kd, Vd, first, nn, src, c, r["kbits"], r["ksig"], r["vsig"], cache, off)
+        slot += c
+    assert slot == n0 + n1
+    oc = np.zeros_like(r["oc"])
+    oracle.quantize_pack(r["ogeom"], oc, K.numpy(), V.numpy(), 0, r["ob"], r["osig"], r["ovsig"])
+    np.testing.assert_array_equal(cache.cpu().numpy(), oc)
+    # invalid device-side entries are skipped (slot beyond capacity)
+    first = torch.tensor([250], dtype=torch.int64, device="cuda")
+    nn = torch.tensor([10], dtype=torch.int32, device="cuda")
+    kvq.quantize_pack(g, Kd, Vd, first, nn, first, 10, r["kbits"], r["ksig"], r["vsig"], cache, off)
+    np.testing.assert_array_equal(cache.cpu().numpy(), oc)
+    # decode over the appended cache
+    seq_len = torch.tensor([n0 + n1], dtype=torch.int32, device="cuda")
+    ws = torch.empty(kvq.decode_workspace_bytes(g, 8, 1, 256) // 4, dtype=torch.float32, device="cuda")
+    out = torch.empty(1, 8, 128, dtype=torch.float32, device="cuda")
+    kvq.packed_decode_attn(g, q[None].cuda().contiguous(), cache, off, seq_len, 256, r["kbits"], r["ksig"],
+                           r["vsig"], out, ws)
+    ref = oracle.decode_attention(r["ogeom"], oc, q.numpy(), n0 + n1, r["ob"], r["osig"], r["ovsig"])
+    check_attention(out.cpu().numpy()[0], ref)
+
+
+@pytest.mark.parametrize("kernel", [kvq.DECODE_GENERIC, kvq.DECODE_AUTO])
+def test_split_count_invariance(kernel):
+    """Any split of the token axis gives the same output up to fp32 re-association (1e-5 of max|o|)."""
+    say("split invariance kernel=%d" % kernel)
+    wl = synth.Workload("split", 1, 8, 1, 1e6, (0,), 192, 3, "decay")
+    n = 1000
+    K, V, q = synth.gen_layer(wl.with_lens([n]), 0, 0, n_tok=n, seed=4)
+    r = run_batch([(K, V, q)], 192, 3, 1024, kernel=kernel, tiles=1)
+    base = r["out"]
+    for tiles in (2, 3, 16):
+        r2 = run_batch([(K, V, q)], 192, 3, 1024, kernel=kernel, tiles=tiles, oracle_attn=False)
+        np.testing.assert_allclose(r2["out"], base, rtol=0, atol=1e-5 * np.abs(base).max())
+
+
+def test_c2_full_size():
+    """Llama-3.1-8B-shaped layer: 32 q / 8 KV heads, 32K tokens, K2V2 -- every stage."""
+    wl = synth.WORKLOADS["c2"]
+    say("c2 full %s" % wl.name)
+    K, V, q = synth.gen_layer(wl, 0, 0)
+    run_batch([(K, V, q)], wl.k_budget, wl.v_bits, 32768)
