@@ -1,0 +1,357 @@
+#!/usr/bin/env python3
+"""Benchmark of the packed-cache hot path on one MI355X.
+
+Workload (default): Qwen2.5-3B-shaped decode -- 36 layers, 16 query heads, 2 KV
+heads, head_dim 128, one sequence of 131072 cached tokens, K3V3 Block-GTQ cache,
+synthetic seeded inputs (packed_cache_attention_amd.synth).
+
+Phases, all on the GPU through the C ABI (libkvq.so):
+  prefill  (untimed setup, measured separately): per layer, exact block energies
+           of K and V, greedy K / uniform V allocation, bulk quantize+pack.
+  step     (the timed unit): per layer, append the new token's K/V
+           (kvq_quantize_pack), split-K decode attention over the packed cache
+           (kvq_decode_partials) and the log-sum-exp merge (kvq_merge_partials).
+           The 36-layer step is captured once in a HIP graph and replayed.
+
+value = algorithmic bytes of one step (packed cache read by attention + queries
++ outputs + appended token) / measured step time, in GB/s.  The dominant kernel's
+duration is measured with HIP events around each split-phase launch on the stream
+it runs on.  A CPU baseline runs the oracle (test infrastructure) on a bounded
+sample of the same workload.
+"""
+from __future__ import annotations
+
+import argparse
+import hashlib
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBPS = 8000.0
+METRIC = "packed-cache decode-attn GB/s (% HBM peak) + quantize tokens/s, 128K K3V3"
+TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
+
+
+def log(msg):
+    print("[bench] " + msg, file=sys.stderr, flush=True)
+
+
+def kernel_source_hash(kernel: str) -> str:
+    name = "kvq_decode_mfma.hip" if kernel == "mfma" else "kvq_decode.hip"
+    with open(os.path.join(ROOT, "packed_cache_attention_amd", "csrc", name), "rb") as f:
+        return hashlib.sha256(f.read()).hexdigest()[:16]
+
+
+def main():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=50)
+    ap.add_argument("--warmup", type=int, default=5)
+    ap.add_argument("--workload", default="c3", choices=["c2", "c3", "c4", "c5"])
+    ap.add_argument("--kernel", default="auto", choices=["auto", "generic", "mfma"])
+    ap.add_argument("--tiles-per-split", type=int, default=0)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--no-graph", action="store_true", help="time eager launches instead of a graph replay")
+    ap.add_argument("--copy-probe-mib", type=int, default=0,
+                    help="also run a plain device copy of this many MiB (counter calibration)")
+    ap.add_argument("--seed", type=int, default=0)
+    args = ap.parse_args()
+
+    world = int(os.environ.get("WORLD_SIZE", "1"))
+    if args.gpus != 1 or world != 1:
+        print("bench.py measures one GPU only: the hot path is data-parallel per (sequence, layer, KV head) "
+              "and this build runs no multi-GPU configuration (see the sharding design notes). "
+              "Run with --gpus 1.", file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+    from packed_cache_attention_amd import kvq, synth
+
+    if not torch.cuda.is_available():
+        print("bench.py needs a GPU", file=sys.stderr)
+        sys.exit(1)
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    kern = {"auto": kvq.DECODE_AUTO, "generic": kvq.DECODE_GENERIC, "mfma": kvq.DECODE_MFMA}[args.kernel]
+
+    wl = synth.WORKLOADS[args.workload]
+    L, Hq, H, d = wl.n_layers, wl.n_q_heads, wl.n_kv_heads, wl.head_dim
+    lens = list(wl.seq_lens)
+    S = len(lens)
+    # every step appends one token: eager warm-up, graph warm-up, timed steps, kernel-timing steps
+    extra = 2 * max(1, args.warmup) + args.steps + min(args.steps, 10) + 4
+    cap = synth.ceil_to(max(lens) + extra, 64)
+    g = kvq.geom(H, wl.k_budget, wl.v_bits, cap)
+    region = kvq.cache_bytes(g)
+    tile = kvq.tile_bytes(g)
+    bytes_per_token_head = tile // 64
+    log("workload %s: %d layers, %d q / %d kv heads, %d seq(s), lengths %s, K budget %d, V %d bits; "
+        "capacity %d, %.1f MB packed per layer" % (wl.name, L, Hq, H, S, lens[:4], wl.k_budget, wl.v_bits, cap,
+                                                    S * region / 1e6))
+
+    # ------------------------------------------------------------ inputs (resident in HBM)
+    t0 = time.perf_counter()
+    rows = sum(lens)
+    Kall = torch.empty(L, rows, H, d, dtype=torch.float16, device=dev)
+    Vall = torch.empty_like(Kall)
+    Qall = torch.empty(L, S, Hq, d, dtype=torch.float16, device=dev)
+    row0 = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    for l in range(L):
+        for s in range(S):
+            k, v, q = synth.gen_layer(wl, s, l, seed=args.seed, device=dev)
+            Kall[l, row0[s]:row0[s] + lens[s]] = k
+            Vall[l, row0[s]:row0[s] + lens[s]] = v
+            Qall[l, s] = q
+    # the decode step's new token per (layer, sequence)
+    Knew = torch.empty(L, S, H, d, dtype=torch.float16, device=dev)
+    Vnew = torch.empty_like(Knew)
+    for l in range(L):
+        for s in range(S):
+            k, v, q = synth.gen_new_token(wl, s, l, lens[s], 0, seed=args.seed, device=dev)
+            Knew[l, s], Vnew[l, s] = k, v
+            Qall[l, s] = q
+    torch.cuda.synchronize()
+    log("generated inputs in %.1f s (%.2f GB fp16 K/V)" % (time.perf_counter() - t0, 2 * Kall.numel() * 2 / 1e9))
+
+    # ------------------------------------------------------------ prefill: energy, allocation, bulk quantize
+    cache = torch.zeros(L, S * region, dtype=torch.uint8, device=dev)
+    eK = torch.zeros(L, H, d // 2, 2, dtype=torch.int64, device=dev)
+    eV = torch.zeros_like(eK)
+    kbits = torch.empty(L, H, d // 2, dtype=torch.uint8, device=dev)
+    ksig = torch.empty(L, H, d // 2, dtype=torch.float32, device=dev)
+    vbits = torch.empty_like(kbits)
+    vsig = torch.empty_like(ksig)
+    off = torch.arange(S, dtype=torch.int64, device=dev) * region
+    first0 = torch.zeros(S, dtype=torch.int64, device=dev)
+    nnew0 = torch.tensor(lens, dtype=torch.int32, device=dev)
+    src0 = torch.tensor(row0, dtype=torch.int64, device=dev)
+    v_budget = wl.v_bits * (d // 2)
+
+    def prefill(ev=None):
+        eK.zero_()
+        eV.zero_()
+        for l in range(L):
+            if ev: ev["e0"][l].record()
+            for s in range(S):
+                xs = slice(int(row0[s]), int(row0[s]) + lens[s])
+                kvq.block_energy(g, Kall[l, xs], eK[l])
+                kvq.block_energy(g, Vall[l, xs], eV[l])
+            if ev: ev["a0"][l].record()
+            kvq.allocate_bits(g, eK[l], wl.k_budget, kvq.GREEDY, kbits[l], ksig[l])
+            kvq.allocate_bits(g, eV[l], v_budget, kvq.UNIFORM, vbits[l], vsig[l])
+            if ev: ev["q0"][l].record()
+            kvq.quantize_pack(g, Kall[l], Vall[l], first0, nnew0, src0, max(lens), kbits[l], ksig[l], vsig[l],
+                              cache[l], off)
+            if ev: ev["q1"][l].record()
+
+    prefill()
+    torch.cuda.synchronize()
+    reps = 3
+    evs = [{k: [torch.cuda.Event(enable_timing=True) for _ in range(L)] for k in ("e0", "a0", "q0", "q1")}
+           for _ in range(reps)]
+    tp0 = torch.cuda.Event(enable_timing=True)
+    tp1 = torch.cuda.Event(enable_timing=True)
+    tp0.record()
+    for r in range(reps):
+        prefill(evs[r])
+    tp1.record()
+    torch.cuda.synchronize()
+    t_energy = np.mean([sum(e["e0"][l].elapsed_time(e["a0"][l]) for l in range(L)) for e in evs]) / 1e3
+    t_alloc = np.mean([sum(e["a0"][l].elapsed_time(e["q0"][l]) for l in range(L)) for e in evs]) / 1e3
+    t_quant = np.mean([sum(e["q0"][l].elapsed_time(e["q1"][l]) for l in range(L)) for e in evs]) / 1e3
+    t_prefill = tp0.elapsed_time(tp1) / 1e3 / reps
+    tok_heads = rows * H * L
+    quant_bytes = tok_heads * (2 * d * 2 + bytes_per_token_head)
+    energy_bytes = tok_heads * 2 * d * 2
+    log("prefill: energy %.3f ms (%.0f GB/s), alloc %.3f ms, quantize %.3f ms (%.0f GB/s, %.3g tokens/s)"
+        % (t_energy * 1e3, energy_bytes / t_energy / 1e9, t_alloc * 1e3, t_quant * 1e3,
+           quant_bytes / t_quant / 1e9, rows / t_quant))
+
+    # ------------------------------------------------------------ decode step
+    cur = torch.tensor(lens, dtype=torch.int64, device=dev)          # slot of the next token
+    seq_len = (cur + 1).to(torch.int32)                               # attended tokens incl. the new one
+    src_new = torch.arange(S, dtype=torch.int64, device=dev)
+    ones32 = torch.ones(S, dtype=torch.int32, device=dev)
+    max_len = cap
+    plan = kvq.decode_plan(g, Hq, S, max_len, kern, args.tiles_per_split)
+    n_split = plan["n_split"]
+    partials = torch.empty(L, S, Hq, n_split, d + 2, dtype=torch.float32, device=dev)
+    out = torch.empty(L, S, Hq, d, dtype=torch.float32, device=dev)
+    log("decode plan: %s" % plan)
+
+    def step(ev=None):
+        for l in range(L):
+            kvq.quantize_pack(g, Knew[l], Vnew[l], cur, ones32, src_new, 1, kbits[l], ksig[l], vsig[l], cache[l], off)
+            if ev: ev[0][l].record()
+            kvq.decode_partials(g, Qall[l], cache[l], off, seq_len, max_len, kbits[l], ksig[l], vsig[l],
+                                partials[l], kernel=kern, tiles_per_split=args.tiles_per_split)
+            if ev: ev[1][l].record()
+            kvq.merge_partials(S, Hq, n_split, partials[l], out[l])
+        cur.add_(1)
+        seq_len.add_(1)
+
+    def seq_bytes():
+        # algorithmic bytes of one step at the current lengths (cache read + q + out + append)
+        ln = seq_len.cpu().numpy().astype(np.int64)
+        attn = int(ln.sum()) * H * bytes_per_token_head + S * Hq * d * (2 + 4)
+        app = S * H * (2 * d * 2 + bytes_per_token_head)
+        return L * attn, L * app
+
+    # warm-up (eager) then capture
+    for _ in range(max(1, args.warmup)):
+        step()
+    torch.cuda.synchronize()
+    graph = None
+    if not args.no_graph:
+        s_cap = torch.cuda.Stream()
+        s_cap.wait_stream(torch.cuda.current_stream())
+        graph = torch.cuda.CUDAGraph()
+        with torch.cuda.stream(s_cap):
+            with torch.cuda.graph(graph, stream=s_cap):
+                step()
+        torch.cuda.current_stream().wait_stream(s_cap)
+        torch.cuda.synchronize()
+        for _ in range(args.warmup):
+            graph.replay()
+        torch.cuda.synchronize()
+    attn_b0, app_b0 = seq_bytes()
+    # timed region: exactly `steps` steps, synchronised on both sides
+    torch.cuda.synchronize()
+    e0 = torch.cuda.Event(enable_timing=True)
+    e1 = torch.cuda.Event(enable_timing=True)
+    w0 = time.perf_counter()
+    e0.record()
+    for _ in range(args.steps):
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
+    e1.record()
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - w0
+    ms_step = e0.elapsed_time(e1) / args.steps
+    attn_b1, app_b1 = seq_bytes()
+    step_bytes = 0.5 * (attn_b0 + attn_b1) + app_b0
+    value = step_bytes / (ms_step / 1e3) / 1e9
+    log("timed %d steps: %.4f ms/step (wall %.4f ms/step), %.1f GB/s = %.1f%% of HBM peak"
+        % (args.steps, ms_step, wall * 1e3 / args.steps, value, 100 * value / HBM_PEAK_GBPS))
+
+    # ------------------------------------------------------------ dominant kernel: events around each launch
+    # The GPU is first held by a spin so the host enqueues the whole step ahead of it;
+    # the event pairs then bracket back-to-back work with no host gaps.
+    ksteps = min(args.steps, 10)
+    durs = []
+    for _ in range(ksteps):
+        ev = ([torch.cuda.Event(enable_timing=True) for _ in range(L)],
+              [torch.cuda.Event(enable_timing=True) for _ in range(L)])
+        torch.cuda._sleep(20_000_000)
+        step(ev)
+        torch.cuda.synchronize()
+        durs += [ev[0][l].elapsed_time(ev[1][l]) / 1e3 for l in range(L)]
+    kdur = float(np.mean(durs))
+    ln = seq_len.cpu().numpy().astype(np.int64) - 1 - np.arange(ksteps).mean()
+    launch_bytes = float(ln.sum()) * H * bytes_per_token_head
+    achieved = launch_bytes / kdur / 1e9
+    kernel_name = "decode_mfma_kernel" if plan["kernel"] == kvq.DECODE_MFMA else "decode_generic_kernel"
+    log("%s: %.2f us/launch avg over %d launches, %.1f GB/s algorithmic (%.1f%% of peak)"
+        % (kernel_name, kdur * 1e6, len(durs), achieved, 100 * achieved / HBM_PEAK_GBPS))
+
+    traffic = None
+    src_hash = kernel_source_hash("mfma" if kernel_name == "decode_mfma_kernel" else "generic")
+    if os.path.exists(TRAFFIC_FILE):
+        try:
+            tf = json.load(open(TRAFFIC_FILE))
+            ent = tf.get(wl.name, {})
+            if ent.get("kernel") == kernel_name and ent.get("source_sha256_16") == src_hash:
+                traffic = ent.get("hbm_bytes_per_launch")
+        except Exception:
+            traffic = None
+
+    if args.copy_probe_mib:
+        n = args.copy_probe_mib * (1 << 20) // 4
+        a = torch.empty(n, dtype=torch.float32, device=dev).normal_()
+        b = torch.empty_like(a)
+        for _ in range(3):
+            b.copy_(a)
+        torch.cuda.synchronize()
+        log("copy probe: %d MiB copied 3x" % args.copy_probe_mib)
+
+    # ------------------------------------------------------------ CPU baseline: the oracle on a bounded sample
+    cpu = None
+    if not args.no_cpu_baseline:
+        cpu = cpu_baseline(wl, Kall, Vall, Qall, lens, row0, bytes_per_token_head)
+
+    result = {
+        "metric": METRIC,
+        "value": round(value, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_step, 5),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "f16xf16->f32 (mfma)" if kernel_name == "decode_mfma_kernel" else "f32",
+        "data": "synthetic",
+        "config": {"workload": wl.name, "layers": L, "q_heads": Hq, "kv_heads": H, "head_dim": d,
+                   "batch": S, "context": lens if S > 1 else lens[0], "k_budget": wl.k_budget,
+                   "v_bits": wl.v_bits, "capacity": cap, "graph": graph is not None,
+                   "split_chunks": n_split, "kernel": kernel_name},
+        "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
+        "step_bytes": int(step_bytes),
+        "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "quantize_tokens_per_s": round(rows / t_quant, 1),
+        "prefill": {"energy_ms": round(t_energy * 1e3, 4), "energy_GBps": round(energy_bytes / t_energy / 1e9, 1),
+                    "allocate_ms": round(t_alloc * 1e3, 4), "quantize_ms": round(t_quant * 1e3, 4),
+                    "quantize_GBps": round(quant_bytes / t_quant / 1e9, 1), "total_ms": round(t_prefill * 1e3, 4),
+                    "tokens": rows, "token_heads": tok_heads},
+        "roofline": {"kernel": kernel_name, "bound": "hbm", "achieved": round(achieved, 2),
+                     "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(achieved / HBM_PEAK_GBPS, 4),
+                     "traffic": traffic, "avg_launch_us": round(kdur * 1e6, 3),
+                     "algorithmic_bytes_per_launch": int(launch_bytes),
+                     "bytes_per_token_head": bytes_per_token_head},
+        "cpu_baseline": cpu,
+    }
+    print(json.dumps(result), flush=True)
+
+
+def cpu_baseline(wl, Kall, Vall, Qall, lens, row0, bytes_per_token_head):
+    """Oracle (CPU, fp64) on a bounded sample: layer 0 of sequence 0, all KV heads,
+    a token window sized to keep the run around 10-20 s; reports the packed bytes
+    its decode attention processes per second."""
+    import numpy as np
+    import oracle
+    n_threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or min(16, os.cpu_count() or 1)
+    os.environ["OMP_NUM_THREADS"] = str(n_threads)
+    n = min(lens[0], 32768)
+    H = wl.n_kv_heads
+    K = Kall[0, int(row0[0]):int(row0[0]) + n].cpu().numpy()
+    V = Vall[0, int(row0[0]):int(row0[0]) + n].cpu().numpy()
+    q = Qall[0, 0].cpu().numpy()
+    t0 = time.perf_counter()
+    eK = oracle.block_energy(K)
+    eV = oracle.block_energy(V)
+    kb, ks = oracle.allocate(eK, wl.k_budget)
+    _, vs = oracle.allocate(eV, wl.v_bits * 64, oracle.UNIFORM)
+    geom = oracle.Geometry(H, wl.k_budget, wl.v_bits, ((n + 63) // 64) * 64)
+    region = np.zeros(geom.seq_bytes, np.uint8)
+    oracle.quantize_pack(geom, region, K, V, 0, kb, ks, vs)
+    t1 = time.perf_counter()
+    oracle.decode_attention(geom, region, q, n, kb, ks, vs)
+    t2 = time.perf_counter()
+    attn_bytes = n * H * bytes_per_token_head
+    return {"value": round(attn_bytes / (t2 - t1) / 1e9, 5), "unit": "GB/s", "cores": n_threads, "kind": "oracle",
+            "sample": "layer 0, %d KV heads x %d tokens, %d query heads (decode attention, fp64, %.2f s); "
+                      "oracle energy+allocation+quantize of the same sample took %.2f s (%.0f tokens/s)"
+                      % (H, n, wl.n_q_heads, t2 - t1, t1 - t0, n / (t1 - t0)),
+            "quantize_tokens_per_s": round(n / (t1 - t0), 1)}
+
+
+if __name__ == "__main__":
+    main()

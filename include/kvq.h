@@ -42,7 +42,7 @@ typedef enum {
     KVQ_ERR_ARG = -1,        /* null pointer, bad enum, n < 0 */
     KVQ_ERR_SHAPE = -2,      /* unsupported head_dim, n_kv_heads, GQA ratio */
     KVQ_ERR_BUDGET = -3,     /* budget outside [0, 8*d/2] and != 16*d/2; UNIFORM not divisible; v_bits invalid */
-    KVQ_ERR_ALIGN = -4,      /* pointer or row stride not 16-byte aligned */
+    KVQ_ERR_ALIGN = -4,      /* pointer or stride below the alignment a call requires */
     KVQ_ERR_CAPACITY = -5,   /* capacity not a multiple of 64, or max_len/max_new beyond it */
     KVQ_ERR_WORKSPACE = -6,  /* workspace too small */
     KVQ_ERR_HIP = -7,        /* a HIP launch failed */
@@ -109,8 +109,8 @@ int32_t kvq_get_codebook(int32_t w, uint16_t *levels_fp16, float *thresholds, fl
  *             t < n_tok, h < n_kv_heads, c < head_dim (c contiguous)
  *   energy  : device uint64 [n_kv_heads][head_dim/2][2] = (low, high) limbs;
  *             ACCUMULATED INTO (zero it for a fresh sum; call repeatedly to add tokens)
- * Requirements: head_dim even, 2..128; n_tok >= 0; x and energy 16-byte aligned
- * and stride_tok, stride_head multiples of 8 when head_dim is a multiple of 8. */
+ * Requirements: head_dim even, 2..128; n_tok >= 0; x 4-byte aligned with even
+ * strides; energy 16-byte aligned.  The whole geometry must be valid. */
 int32_t kvq_block_energy(const kvq_geom *g, const void *x, int64_t n_tok, int64_t stride_tok,
                          int64_t stride_head, uint64_t *energy, void *stream);
 
@@ -125,7 +125,8 @@ int32_t kvq_block_energy(const kvq_geom *g, const void *x, int64_t n_tok, int64_
  *   energy : device uint64 [n_units][head_dim/2][2]
  *   bits   : device uint8  [n_units][head_dim/2]
  *   sigma  : device float  [n_units][head_dim/2]
- * Uses g->head_dim only.  Requirements: budget in [0, 8*(d/2)] or == 16*(d/2). */
+ * The call uses g->head_dim (the whole geometry must be valid).  Requirements:
+ * budget in [0, 8*(d/2)] or == 16*(d/2); energy 16-byte aligned. */
 int32_t kvq_allocate_bits(const kvq_geom *g, const uint64_t *energy, int32_t n_units, int32_t budget,
                           int32_t mode, uint8_t *bits, float *sigma, void *stream);
 
@@ -144,7 +145,8 @@ int32_t kvq_allocate_bits(const kvq_geom *g, const uint64_t *energy, int32_t n_u
  * Appends OR codes into partially filled tiles; sequences must not share regions.
  * Device-side entries with first_slot < 0, n_new < 0, n_new > max_new or
  * first_slot + n_new > capacity_tokens are skipped (nothing written for them).
- * Requirements: head_dim 128; 0 <= max_new <= capacity; alignment 16 B. */
+ * Requirements: head_dim 128; 0 <= max_new <= capacity; k, v 4-byte aligned with
+ * even strides; cache 16-byte aligned; metadata naturally aligned. */
 int32_t kvq_quantize_pack(const kvq_geom *g, const void *k, const void *v, int64_t stride_tok,
                           int64_t stride_head, int32_t n_seq, const int64_t *first_slot,
                           const int32_t *n_new, const int64_t *src_row0, int32_t max_new,
@@ -162,8 +164,9 @@ int32_t kvq_quantize_pack(const kvq_geom *g, const void *k, const void *v, int64
  *   seq_len  : device int32 [n_seq] (clamped to [0, max_len])
  *   out      : device float [n_seq][n_q_heads][128]
  *   workspace: device scratch of at least kvq_decode_workspace_bytes(...) bytes
- * Requirements: head_dim 128; n_q_heads multiple of n_kv_heads with ratio <= 16;
- * 0 <= max_len <= capacity; alignment 16 B. */
+ * Requirements: head_dim 128; n_q_heads multiple of n_kv_heads with ratio <= 16
+ * (<= 8 for KVQ_DECODE_MFMA); 0 <= max_len <= capacity; q, cache, out and
+ * workspace 16-byte aligned. */
 int32_t kvq_packed_decode_attn(const kvq_geom *g, int32_t n_q_heads, const void *q, const uint8_t *cache,
                                const int64_t *seq_byte_off, const int32_t *seq_len, int32_t n_seq,
                                int64_t max_len, const uint8_t *k_bits, const float *k_sigma,
@@ -179,6 +182,37 @@ int32_t kvq_packed_decode_attn_ex(const kvq_geom *g, int32_t n_q_heads, const vo
                                   const float *v_sigma, float softmax_scale, float *out, void *workspace,
                                   size_t workspace_bytes, int32_t kernel, int32_t tiles_per_split,
                                   void *stream);
+
+/* The two phases of kvq_packed_decode_attn_ex, for callers that merge partials
+ * themselves (e.g. partials gathered from several devices that each hold a token
+ * range) or time the phases apart.
+ *
+ * kvq_decode_partials writes, for every (sequence s, query head h, chunk k < n_split),
+ * 130 floats at partials[((s*n_q_heads + h)*n_split + k)*130]:
+ *   [0] m = max over the chunk's tokens of softmax_scale * q.khat * log2(e)  (-inf if empty)
+ *   [1] l = sum_t 2^(z_t - m)
+ *   [2..129] o_c = sum_t 2^(z_t - m) vhat_{t,c}          (unnormalised)
+ * n_split is kvq_decode_n_split(...) for the same arguments; partials_bytes must be
+ * at least kvq_decode_workspace_bytes_ex(...). */
+int32_t kvq_decode_partials(const kvq_geom *g, int32_t n_q_heads, const void *q, const uint8_t *cache,
+                            const int64_t *seq_byte_off, const int32_t *seq_len, int32_t n_seq, int64_t max_len,
+                            const uint8_t *k_bits, const float *k_sigma, const float *v_sigma, float softmax_scale,
+                            float *partials, size_t partials_bytes, int32_t kernel, int32_t tiles_per_split,
+                            void *stream);
+/* Log-sum-exp merge of n_split partials per (sequence, head) in the format above:
+ * out[s][h][c] = sum_k 2^(m_k - M) o_k,c / sum_k 2^(m_k - M) l_k, M = max_k m_k; rows
+ * with no tokens give 0.  out: device float [n_seq][n_q_heads][128]. */
+int32_t kvq_merge_partials(int32_t n_seq, int32_t n_q_heads, int32_t n_split, const float *partials, float *out,
+                           void *stream);
+/* The decode plan for these arguments: chosen kernel (KVQ_DECODE_GENERIC or
+ * KVQ_DECODE_MFMA), tiles per chunk, chunks per sequence, workspace bytes.  Any
+ * output pointer may be NULL.  Host only. */
+int32_t kvq_decode_plan(const kvq_geom *g, int32_t n_q_heads, int32_t n_seq, int64_t max_len, int32_t kernel,
+                        int32_t tiles_per_split, int32_t *kernel_out, int32_t *tiles_out, int32_t *n_split_out,
+                        int64_t *workspace_out);
+/* Number of chunks the decode kernels split each sequence into (negative status if invalid). */
+int32_t kvq_decode_n_split(const kvq_geom *g, int32_t n_q_heads, int32_t n_seq, int64_t max_len, int32_t kernel,
+                           int32_t tiles_per_split);
 
 /* Workspace bytes needed by kvq_packed_decode_attn(_ex) (negative status if invalid). */
 int64_t kvq_decode_workspace_bytes(const kvq_geom *g, int32_t n_q_heads, int32_t n_seq, int64_t max_len);

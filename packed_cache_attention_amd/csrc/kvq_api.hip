@@ -166,12 +166,12 @@ int64_t kvq_decode_workspace_bytes(const kvq_geom* g, int32_t n_q_heads, int32_t
     return kvq_decode_workspace_bytes_ex(g, n_q_heads, n_seq, max_len, KVQ_DECODE_AUTO, 0);
 }
 
-int32_t kvq_packed_decode_attn_ex(const kvq_geom* g, int32_t n_q_heads, const void* q, const uint8_t* cache,
-                                  const int64_t* seq_byte_off, const int32_t* seq_len, int32_t n_seq, int64_t max_len,
-                                  const uint8_t* k_bits, const float* k_sigma, const float* v_sigma,
-                                  float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
-                                  int32_t kernel, int32_t tiles_per_split, void* stream) {
-    const char* fn = "kvq_packed_decode_attn";
+namespace {
+// shared validation of the decode calls; fills the plan
+int32_t check_decode(const kvq_geom* g, int32_t n_q_heads, const void* q, const uint8_t* cache,
+                     const int64_t* seq_byte_off, const int32_t* seq_len, int32_t n_seq, int64_t max_len,
+                     const uint8_t* k_bits, const float* k_sigma, const float* v_sigma, const void* ws,
+                     size_t ws_bytes, int32_t kernel, int32_t tiles_per_split, DecodePlan* plan, const char* fn) {
     int32_t st = check_geom(g, true, fn);
     if (st) return st;
     if (n_q_heads < 1 || n_q_heads % g->n_kv_heads) return fail(KVQ_ERR_SHAPE, fn, "n_q_heads");
@@ -179,19 +179,96 @@ int32_t kvq_packed_decode_attn_ex(const kvq_geom* g, int32_t n_q_heads, const vo
     if ((int64_t)n_seq * n_q_heads > 2147483647LL) return fail(KVQ_ERR_SHAPE, fn, "n_seq * n_q_heads");
     if (n_seq > 65535) return fail(KVQ_ERR_SHAPE, fn, "n_seq");
     if (max_len > g->capacity_tokens) return fail(KVQ_ERR_CAPACITY, fn, "max_len > capacity");
+    st = plan_decode(*g, n_q_heads, n_seq, max_len, kernel, tiles_per_split, plan);
+    if (st) return fail(st, fn, "no kernel for this geometry");
+    if (n_seq == 0) return KVQ_OK;
+    if (!q || !cache || !seq_byte_off || !seq_len || !k_bits || !k_sigma || !v_sigma || !ws)
+        return fail(KVQ_ERR_ARG, fn, "null pointer");
+    if (!aligned(q, 16) || !aligned(cache, 16) || !aligned(ws, 16) || !aligned(seq_byte_off, 8) ||
+        !aligned(seq_len, 4) || !aligned(k_sigma, 4) || !aligned(v_sigma, 4))
+        return fail(KVQ_ERR_ALIGN, fn, "alignment");
+    if ((int64_t)ws_bytes < plan->workspace) return fail(KVQ_ERR_WORKSPACE, fn, "workspace/partials bytes");
+    return KVQ_OK;
+}
+}  // namespace
+
+int32_t kvq_decode_plan(const kvq_geom* g, int32_t n_q_heads, int32_t n_seq, int64_t max_len, int32_t kernel,
+                        int32_t tiles_per_split, int32_t* kernel_out, int32_t* tiles_out, int32_t* n_split_out,
+                        int64_t* workspace_out) {
+    const char* fn = "kvq_decode_plan";
+    int32_t st = check_geom(g, true, fn);
+    if (st) return st;
+    if (n_q_heads < 1 || n_q_heads % g->n_kv_heads) return fail(KVQ_ERR_SHAPE, fn, "n_q_heads");
+    if (n_seq < 0 || max_len < 0 || tiles_per_split < 0) return fail(KVQ_ERR_ARG, fn, "negative count");
+    if (max_len > g->capacity_tokens) return fail(KVQ_ERR_CAPACITY, fn, "max_len > capacity");
     DecodePlan plan;
     st = plan_decode(*g, n_q_heads, n_seq, max_len, kernel, tiles_per_split, &plan);
     if (st) return fail(st, fn, "no kernel for this geometry");
-    if (n_seq == 0) return KVQ_OK;
-    if (!q || !cache || !seq_byte_off || !seq_len || !k_bits || !k_sigma || !v_sigma || !out || !workspace)
-        return fail(KVQ_ERR_ARG, fn, "null pointer");
-    if (!aligned(q, 16) || !aligned(cache, 16) || !aligned(out, 16) || !aligned(workspace, 16) ||
-        !aligned(seq_byte_off, 8) || !aligned(seq_len, 4) || !aligned(k_sigma, 4) || !aligned(v_sigma, 4))
-        return fail(KVQ_ERR_ALIGN, fn, "alignment");
-    if ((int64_t)workspace_bytes < plan.workspace) return fail(KVQ_ERR_WORKSPACE, fn, "workspace_bytes");
-    return hip_status(launch_decode(*g, plan, n_q_heads, (const uint16_t*)q, cache, seq_byte_off, seq_len, n_seq,
-                                    max_len, k_bits, k_sigma, v_sigma, softmax_scale, out, (float*)workspace,
-                                    (hipStream_t)stream),
+    if (kernel_out) *kernel_out = plan.kernel;
+    if (tiles_out) *tiles_out = plan.tiles_per_split;
+    if (n_split_out) *n_split_out = plan.n_split;
+    if (workspace_out) *workspace_out = plan.workspace;
+    return KVQ_OK;
+}
+
+int32_t kvq_decode_n_split(const kvq_geom* g, int32_t n_q_heads, int32_t n_seq, int64_t max_len, int32_t kernel,
+                           int32_t tiles_per_split) {
+    const char* fn = "kvq_decode_n_split";
+    int32_t st = check_geom(g, true, fn);
+    if (st) return st;
+    if (n_q_heads < 1 || n_q_heads % g->n_kv_heads) return fail(KVQ_ERR_SHAPE, fn, "n_q_heads");
+    if (n_seq < 0 || max_len < 0 || tiles_per_split < 0) return fail(KVQ_ERR_ARG, fn, "negative count");
+    if (max_len > g->capacity_tokens) return fail(KVQ_ERR_CAPACITY, fn, "max_len > capacity");
+    DecodePlan plan;
+    st = plan_decode(*g, n_q_heads, n_seq, max_len, kernel, tiles_per_split, &plan);
+    if (st) return fail(st, fn, "no kernel for this geometry");
+    return plan.n_split;
+}
+
+int32_t kvq_decode_partials(const kvq_geom* g, int32_t n_q_heads, const void* q, const uint8_t* cache,
+                            const int64_t* seq_byte_off, const int32_t* seq_len, int32_t n_seq, int64_t max_len,
+                            const uint8_t* k_bits, const float* k_sigma, const float* v_sigma, float softmax_scale,
+                            float* partials, size_t partials_bytes, int32_t kernel, int32_t tiles_per_split,
+                            void* stream) {
+    const char* fn = "kvq_decode_partials";
+    DecodePlan plan;
+    int32_t st = check_decode(g, n_q_heads, q, cache, seq_byte_off, seq_len, n_seq, max_len, k_bits, k_sigma, v_sigma,
+                              partials, partials_bytes, kernel, tiles_per_split, &plan, fn);
+    if (st || n_seq == 0) return st;
+    return hip_status(launch_decode_partials(*g, plan, n_q_heads, (const uint16_t*)q, cache, seq_byte_off, seq_len,
+                                             n_seq, max_len, k_bits, k_sigma, v_sigma, softmax_scale, partials,
+                                             (hipStream_t)stream),
+                      fn);
+}
+
+int32_t kvq_merge_partials(int32_t n_seq, int32_t n_q_heads, int32_t n_split, const float* partials, float* out,
+                           void* stream) {
+    const char* fn = "kvq_merge_partials";
+    if (n_seq < 0 || n_q_heads < 0 || n_split < 1) return fail(KVQ_ERR_ARG, fn, "counts");
+    if ((int64_t)n_seq * n_q_heads > 2147483647LL) return fail(KVQ_ERR_SHAPE, fn, "n_seq * n_q_heads");
+    if (n_seq == 0 || n_q_heads == 0) return KVQ_OK;
+    if (!partials || !out) return fail(KVQ_ERR_ARG, fn, "null pointer");
+    if (!aligned(partials, 16) || !aligned(out, 16)) return fail(KVQ_ERR_ALIGN, fn, "alignment");
+    return hip_status(launch_merge(n_seq * n_q_heads, n_split, partials, out, (hipStream_t)stream), fn);
+}
+
+int32_t kvq_packed_decode_attn_ex(const kvq_geom* g, int32_t n_q_heads, const void* q, const uint8_t* cache,
+                                  const int64_t* seq_byte_off, const int32_t* seq_len, int32_t n_seq, int64_t max_len,
+                                  const uint8_t* k_bits, const float* k_sigma, const float* v_sigma,
+                                  float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
+                                  int32_t kernel, int32_t tiles_per_split, void* stream) {
+    const char* fn = "kvq_packed_decode_attn";
+    DecodePlan plan;
+    int32_t st = check_decode(g, n_q_heads, q, cache, seq_byte_off, seq_len, n_seq, max_len, k_bits, k_sigma, v_sigma,
+                              workspace, workspace_bytes, kernel, tiles_per_split, &plan, fn);
+    if (st || n_seq == 0) return st;
+    if (!out) return fail(KVQ_ERR_ARG, fn, "null pointer");
+    if (!aligned(out, 16)) return fail(KVQ_ERR_ALIGN, fn, "alignment");
+    hipError_t e = launch_decode_partials(*g, plan, n_q_heads, (const uint16_t*)q, cache, seq_byte_off, seq_len,
+                                          n_seq, max_len, k_bits, k_sigma, v_sigma, softmax_scale, (float*)workspace,
+                                          (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, fn);
+    return hip_status(launch_merge(n_seq * n_q_heads, plan.n_split, (const float*)workspace, out, (hipStream_t)stream),
                       fn);
 }
 

@@ -14,7 +14,7 @@
 namespace kvq {
 
 constexpr int kGenericMaxGroup = 16;
-constexpr bool kMfmaKernel = false;
+constexpr bool kMfmaKernel = true;
 
 // bits [pos, pos + w) of a little-endian bitstream at base (w <= 16); reads only
 // the (aligned) dwords that hold the field
@@ -205,7 +205,7 @@ int plan_decode(const kvq_geom& g, int n_q_heads, int n_seq, int64_t max_len, in
         // enough chunks to give every CU several workgroups, but chunks of at least
         // 4 tiles (MFMA) so the merge traffic stays small against the cache bytes
         const int64_t units = (int64_t)n_seq * g.n_kv_heads;
-        const int64_t target = kernel == KVQ_DECODE_MFMA ? 1024 : 512;
+        const int64_t target = 512;
         int64_t want = (target + units - 1) / (units > 0 ? units : 1);
         if (want < 1) want = 1;
         T = (n_tiles + want - 1) / want;
@@ -221,25 +221,24 @@ int plan_decode(const kvq_geom& g, int n_q_heads, int n_seq, int64_t max_len, in
     return 0;
 }
 
-hipError_t launch_decode(const kvq_geom& g, const DecodePlan& plan, int n_q_heads, const uint16_t* q,
-                         const uint8_t* cache, const int64_t* seq_byte_off, const int32_t* seq_len, int n_seq,
-                         int64_t max_len, const uint8_t* k_bits, const float* k_sigma, const float* v_sigma,
-                         float softmax_scale, float* out, float* workspace, hipStream_t st) {
+hipError_t launch_decode_partials(const kvq_geom& g, const DecodePlan& plan, int n_q_heads, const uint16_t* q,
+                                  const uint8_t* cache, const int64_t* seq_byte_off, const int32_t* seq_len,
+                                  int n_seq, int64_t max_len, const uint8_t* k_bits, const float* k_sigma,
+                                  const float* v_sigma, float softmax_scale, float* partials, hipStream_t st) {
     const float scale_log2 = softmax_scale * kLog2e;
     const int grp = n_q_heads / g.n_kv_heads;
-    if (plan.kernel == KVQ_DECODE_MFMA) {
-        hipError_t e = launch_decode_mfma(g, plan, n_q_heads, q, cache, seq_byte_off, seq_len, n_seq, max_len,
-                                          k_bits, k_sigma, v_sigma, scale_log2, workspace, st);
-        if (e != hipSuccess) return e;
-    } else {
-        dim3 grid(plan.n_split, g.n_kv_heads, n_seq);
-        hipLaunchKernelGGL(decode_generic_kernel, grid, dim3(256), 0, st, q, cache, seq_byte_off, seq_len, max_len,
-                           g.capacity_tokens, k_bits, k_sigma, v_sigma, scale_log2, n_q_heads, grp, g.rope_pairing,
-                           g.k_budget, g.v_bits, plan.tiles_per_split, plan.n_split, workspace);
-        hipError_t e = hipGetLastError();
-        if (e != hipSuccess) return e;
-    }
-    hipLaunchKernelGGL(merge_kernel, dim3(n_seq * n_q_heads), dim3(128), 0, st, workspace, plan.n_split, out);
+    if (plan.kernel == KVQ_DECODE_MFMA)
+        return launch_decode_mfma(g, plan, n_q_heads, q, cache, seq_byte_off, seq_len, n_seq, max_len, k_bits,
+                                  k_sigma, v_sigma, scale_log2, partials, st);
+    dim3 grid(plan.n_split, g.n_kv_heads, n_seq);
+    hipLaunchKernelGGL(decode_generic_kernel, grid, dim3(256), 0, st, q, cache, seq_byte_off, seq_len, max_len,
+                       g.capacity_tokens, k_bits, k_sigma, v_sigma, scale_log2, n_q_heads, grp, g.rope_pairing,
+                       g.k_budget, g.v_bits, plan.tiles_per_split, plan.n_split, partials);
+    return hipGetLastError();
+}
+
+hipError_t launch_merge(int n_rows, int n_split, const float* partials, float* out, hipStream_t st) {
+    hipLaunchKernelGGL(merge_kernel, dim3(n_rows), dim3(128), 0, st, partials, n_split, out);
     return hipGetLastError();
 }
 

@@ -50,9 +50,10 @@ struct DecodePlan {
 // Returns 0 and fills the plan, or a negative kvq_status.
 int plan_decode(const kvq_geom& g, int n_q_heads, int n_seq, int64_t max_len, int kernel, int tiles_per_split,
                 DecodePlan* plan);
-hipError_t launch_decode(const kvq_geom& g, const DecodePlan& plan, int n_q_heads, const uint16_t* q,
-                         const uint8_t* cache, const int64_t* seq_byte_off, const int32_t* seq_len, int n_seq,
-                         int64_t max_len, const uint8_t* k_bits, const float* k_sigma, const float* v_sigma,
-                         float softmax_scale, float* out, float* workspace, hipStream_t st);
+hipError_t launch_decode_partials(const kvq_geom& g, const DecodePlan& plan, int n_q_heads, const uint16_t* q,
+                                  const uint8_t* cache, const int64_t* seq_byte_off, const int32_t* seq_len,
+                                  int n_seq, int64_t max_len, const uint8_t* k_bits, const float* k_sigma,
+                                  const float* v_sigma, float softmax_scale, float* partials, hipStream_t st);
+hipError_t launch_merge(int n_rows, int n_split, const float* partials, float* out, hipStream_t st);
 
 }  // namespace kvq

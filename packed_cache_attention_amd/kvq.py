@@ -71,6 +71,14 @@ def lib() -> C.CDLL:
     L.kvq_packed_decode_attn.restype = I32
     L.kvq_packed_decode_attn_ex.argtypes = [G, I32, P, P, P, P, I32, I64, P, P, P, F32, P, P, SZ, I32, I32, P]
     L.kvq_packed_decode_attn_ex.restype = I32
+    L.kvq_decode_partials.argtypes = [G, I32, P, P, P, P, I32, I64, P, P, P, F32, P, SZ, I32, I32, P]
+    L.kvq_decode_partials.restype = I32
+    L.kvq_merge_partials.argtypes = [I32, I32, I32, P, P, P]
+    L.kvq_merge_partials.restype = I32
+    L.kvq_decode_n_split.argtypes = [G, I32, I32, I64, I32, I32]
+    L.kvq_decode_n_split.restype = I32
+    L.kvq_decode_plan.argtypes = [G, I32, I32, I64, I32, I32, P, P, P, P]
+    L.kvq_decode_plan.restype = I32
     if L.kvq_version() != LAYOUT_VERSION:
         raise RuntimeError("libkvq.so layout version mismatch")
     return L
@@ -78,7 +86,8 @@ def lib() -> C.CDLL:
 
 EXPORTS = ["kvq_version", "kvq_status_string", "kvq_tile_bytes", "kvq_cache_bytes", "kvq_get_codebook",
            "kvq_block_energy", "kvq_allocate_bits", "kvq_quantize_pack", "kvq_decode_workspace_bytes",
-           "kvq_decode_workspace_bytes_ex", "kvq_packed_decode_attn", "kvq_packed_decode_attn_ex"]
+           "kvq_decode_workspace_bytes_ex", "kvq_packed_decode_attn", "kvq_packed_decode_attn_ex",
+           "kvq_decode_partials", "kvq_merge_partials", "kvq_decode_n_split", "kvq_decode_plan"]
 
 
 def status_string(st: int) -> str:
@@ -196,3 +205,41 @@ def packed_decode_attn(g: Geom, q: torch.Tensor, cache: torch.Tensor, seq_byte_o
         C.byref(g), n_q, _ptr(q), _ptr(cache), _ptr(seq_byte_off), _ptr(seq_len), n_seq, max_len, _ptr(k_bits),
         _ptr(k_sigma), _ptr(v_sigma), float(softmax_scale), _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), kernel, tiles_per_split, _stream(stream)))
+
+
+def decode_n_split(g: Geom, n_q_heads: int, n_seq: int, max_len: int, kernel: int = DECODE_AUTO,
+                   tiles_per_split: int = 0) -> int:
+    r = lib().kvq_decode_n_split(C.byref(g), n_q_heads, n_seq, max_len, kernel, tiles_per_split)
+    if r < 0:
+        raise KvqError("kvq_decode_n_split", r)
+    return r
+
+
+def decode_partials(g: Geom, q: torch.Tensor, cache: torch.Tensor, seq_byte_off: torch.Tensor, seq_len: torch.Tensor,
+                    max_len: int, k_bits: torch.Tensor, k_sigma: torch.Tensor, v_sigma: torch.Tensor,
+                    partials: torch.Tensor, softmax_scale: float | None = None, kernel: int = DECODE_AUTO,
+                    tiles_per_split: int = 0, stream=None):
+    """Split phase only: partials [n_seq, n_q, n_split, 130] fp32 (m in log2 units, l, unnormalised o)."""
+    assert q.dtype == torch.float16 and q.is_contiguous() and partials.dtype == torch.float32
+    n_seq, n_q = q.shape[0], q.shape[1]
+    if softmax_scale is None:
+        softmax_scale = g.head_dim ** -0.5
+    _check("kvq_decode_partials", lib().kvq_decode_partials(
+        C.byref(g), n_q, _ptr(q), _ptr(cache), _ptr(seq_byte_off), _ptr(seq_len), n_seq, max_len, _ptr(k_bits),
+        _ptr(k_sigma), _ptr(v_sigma), float(softmax_scale), _ptr(partials), partials.numel() * 4, kernel,
+        tiles_per_split, _stream(stream)))
+
+
+def merge_partials(n_seq: int, n_q: int, n_split: int, partials: torch.Tensor, out: torch.Tensor, stream=None):
+    assert partials.dtype == torch.float32 and out.dtype == torch.float32 and out.is_contiguous()
+    _check("kvq_merge_partials", lib().kvq_merge_partials(n_seq, n_q, n_split, _ptr(partials), _ptr(out),
+                                                          _stream(stream)))
+
+
+def decode_plan(g: Geom, n_q_heads: int, n_seq: int, max_len: int, kernel: int = DECODE_AUTO,
+                tiles_per_split: int = 0) -> dict:
+    k, t, n = C.c_int32(), C.c_int32(), C.c_int32()
+    w = C.c_int64()
+    _check("kvq_decode_plan", lib().kvq_decode_plan(C.byref(g), n_q_heads, n_seq, max_len, kernel, tiles_per_split,
+                                                     C.byref(k), C.byref(t), C.byref(n), C.byref(w)))
+    return {"kernel": k.value, "tiles_per_split": t.value, "n_split": n.value, "workspace": w.value}

@@ -93,15 +93,16 @@ CASES = [
 ]
 
 
+@pytest.mark.parametrize("kernel", [kvq.DECODE_AUTO, kvq.DECODE_GENERIC], ids=["auto", "generic"])
 @pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
-def test_pipeline_matches_oracle(case):
+def test_pipeline_matches_oracle(case, kernel):
     name, H, grp, n, cap, kb, vb, pairing = case
-    say("pipeline %s" % name)
+    say("pipeline %s kernel=%d" % (name, kernel))
     wl = synth.Workload(name, 1, H * grp, H, 1e6, (n,), kb, vb, "decay")
     K, V, q = _heads(wl, n, seed=7)
     if pairing == 1:  # the generator rotates half-split planes; any fp16 keys are valid input
         K = K[:, :, torch.randperm(128, generator=torch.Generator().manual_seed(3))].contiguous()
-    run_batch([(K, V, q)], kb, vb, cap, pairing=pairing)
+    run_batch([(K, V, q)], kb, vb, cap, pairing=pairing, kernel=kernel)
 
 
 def test_passthrough_attention_is_exact_softmax():
@@ -177,7 +178,7 @@ def test_appends_equal_bulk_and_decode_after_append():
     check_attention(out.cpu().numpy()[0], ref)
 
 
-@pytest.mark.parametrize("kernel", [kvq.DECODE_GENERIC, kvq.DECODE_AUTO])
+@pytest.mark.parametrize("kernel", [kvq.DECODE_GENERIC, kvq.DECODE_MFMA])
 def test_split_count_invariance(kernel):
     """Any split of the token axis gives the same output up to fp32 re-association (1e-5 of max|o|)."""
     say("split invariance kernel=%d" % kernel)
@@ -186,14 +187,15 @@ def test_split_count_invariance(kernel):
     K, V, q = synth.gen_layer(wl.with_lens([n]), 0, 0, n_tok=n, seed=4)
     r = run_batch([(K, V, q)], 192, 3, 1024, kernel=kernel, tiles=1)
     base = r["out"]
-    for tiles in (2, 3, 16):
+    for tiles in (2, 3, 5, 16):
         r2 = run_batch([(K, V, q)], 192, 3, 1024, kernel=kernel, tiles=tiles, oracle_attn=False)
         np.testing.assert_allclose(r2["out"], base, rtol=0, atol=1e-5 * np.abs(base).max())
 
 
-def test_c2_full_size():
+@pytest.mark.parametrize("kernel", [kvq.DECODE_MFMA, kvq.DECODE_GENERIC])
+def test_c2_full_size(kernel):
     """Llama-3.1-8B-shaped layer: 32 q / 8 KV heads, 32K tokens, K2V2 -- every stage."""
     wl = synth.WORKLOADS["c2"]
-    say("c2 full %s" % wl.name)
+    say("c2 full %s kernel=%d" % (wl.name, kernel))
     K, V, q = synth.gen_layer(wl, 0, 0)
-    run_batch([(K, V, q)], wl.k_budget, wl.v_bits, 32768)
+    run_batch([(K, V, q)], wl.k_budget, wl.v_bits, 32768, kernel=kernel)
