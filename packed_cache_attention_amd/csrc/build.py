@@ -15,7 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 PKG = os.path.dirname(HERE)
 OUT = os.path.join(PKG, "libkvq.so")
 BUILD = os.path.join(PKG, "_build")
-SOURCES = ["kvq_api.hip", "kvq_energy_alloc.hip", "kvq_quantize.hip", "kvq_decode.hip", "kvq_decode_mfma.hip"]
+SOURCES = ["kvq_api.hip", "kvq_energy_alloc.hip", "kvq_quantize.hip", "kvq_decode.hip", "kvq_decode_mfma.hip"] + \
+    ["kvq_decode_mfma_v%d.hip" % v for v in range(1, 9)]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          # packed FP32 instructions are kept out of every kernel
@@ -48,7 +49,7 @@ def _compile(src):
 
 def build(verbose=False):
     os.makedirs(BUILD, exist_ok=True)
-    with cf.ThreadPoolExecutor(max_workers=min(8, len(SOURCES))) as ex:
+    with cf.ThreadPoolExecutor(max_workers=min(int(os.environ.get("MAX_JOBS", "8")), len(SOURCES))) as ex:
         results = list(ex.map(_compile, SOURCES))
     for obj, err in results:
         if verbose and err.strip():

@@ -194,7 +194,8 @@ hipError_t launch_decode_mfma(const kvq_geom& g, const DecodePlan& plan, int n_q
 int plan_decode(const kvq_geom& g, int n_q_heads, int n_seq, int64_t max_len, int kernel, int tiles_per_split,
                 DecodePlan* plan) {
     const int grp = n_q_heads / g.n_kv_heads;
-    const bool mfma_ok = kMfmaKernel && g.k_budget <= 8 * kMaxBlocks && g.v_bits <= 8 && grp <= 8;
+    // the matrix-core kernel keeps a K record (<= 64 bytes: k_budget <= 256) in registers
+    const bool mfma_ok = kMfmaKernel && g.k_budget <= 4 * kMaxBlocks && g.v_bits <= 8 && grp <= 8;
     if (kernel == KVQ_DECODE_AUTO) kernel = mfma_ok ? KVQ_DECODE_MFMA : KVQ_DECODE_GENERIC;
     if (kernel == KVQ_DECODE_MFMA && !mfma_ok) return KVQ_ERR_SHAPE;
     if (kernel == KVQ_DECODE_GENERIC && grp > kGenericMaxGroup) return KVQ_ERR_SHAPE;

@@ -1,0 +1,8 @@
+// kvq_decode_mfma_v7.hip -- matrix-core decode kernels for 7-bit values.
+#include "kvq_decode_mfma.h"
+
+namespace kvq {
+template hipError_t launch_mfma_v<7>(const kvq_geom&, const DecodePlan&, int, const uint16_t*, const uint8_t*,
+                                     const int64_t*, const int32_t*, int, int64_t, const uint8_t*, const float*,
+                                     const float*, float, float*, hipStream_t);
+}  // namespace kvq
