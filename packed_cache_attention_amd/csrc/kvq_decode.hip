@@ -166,24 +166,49 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
     }
 }
 
-// grid: n_seq * n_q; block: 128 threads (one per output coordinate)
-__global__ __launch_bounds__(128) void merge_kernel(const float* __restrict__ ws, int n_split,
+// grid: n_seq * n_q rows; block: 256 threads = 2 split halves x 128 coordinates
+__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ws, int n_split,
                                                    float* __restrict__ out) {
     const int64_t row = blockIdx.x;
-    const int c = threadIdx.x;
-    const float* part = ws + row * n_split * (kHeadDim + 2);
+    const int tid = threadIdx.x, c = tid & 127, half = tid >> 7;
+    constexpr int D2 = kHeadDim + 2;
+    const float* part = ws + row * n_split * D2;
+    __shared__ float s_red[8];
+    __shared__ float s_o[kHeadDim], s_l;
     float m = -INFINITY;
-    for (int sp = 0; sp < n_split; ++sp) m = fmaxf(m, part[sp * (kHeadDim + 2)]);
+    for (int sp = tid; sp < n_split; sp += 256) m = fmaxf(m, part[(int64_t)sp * D2]);
+    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
+    if ((tid & 63) == 0) s_red[tid >> 6] = m;
+    __syncthreads();
+    const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
     float l = 0.f, acc = 0.f;
-    if (m != -INFINITY) {
-        for (int sp = 0; sp < n_split; ++sp) {
-            const float* p = part + sp * (kHeadDim + 2);
-            const float a = exp2f(p[0] - m);
-            l += a * p[1];
-            acc += a * p[2 + c];
+    if (M != -INFINITY) {
+        int sp = half;
+        for (; sp + 6 < n_split; sp += 8) {
+            const float* p0 = part + (int64_t)sp * D2;
+            const float* p1 = p0 + 2 * D2;
+            const float* p2 = p0 + 4 * D2;
+            const float* p3 = p0 + 6 * D2;
+            const float a0 = exp2f(p0[0] - M), a1 = exp2f(p1[0] - M), a2 = exp2f(p2[0] - M), a3 = exp2f(p3[0] - M);
+            l += a0 * p0[1] + a1 * p1[1] + a2 * p2[1] + a3 * p3[1];
+            acc += a0 * p0[2 + c] + a1 * p1[2 + c] + a2 * p2[2 + c] + a3 * p3[2 + c];
+        }
+        for (; sp < n_split; sp += 2) {
+            const float* p0 = part + (int64_t)sp * D2;
+            const float a0 = exp2f(p0[0] - M);
+            l += a0 * p0[1];
+            acc += a0 * p0[2 + c];
         }
     }
-    out[row * kHeadDim + c] = l > 0.f ? acc / l : 0.f;
+    if (half == 1) {
+        s_o[c] = acc;
+        if (c == 0) s_l = l;
+    }
+    __syncthreads();
+    if (half == 0) {
+        const float lt = l + s_l;
+        out[row * kHeadDim + c] = lt > 0.f ? (acc + s_o[c]) / lt : 0.f;
+    }
 }
 
 hipError_t launch_decode_mfma(const kvq_geom& g, const DecodePlan& plan, int n_q_heads, const uint16_t* q,
@@ -239,7 +264,7 @@ hipError_t launch_decode_partials(const kvq_geom& g, const DecodePlan& plan, int
 }
 
 hipError_t launch_merge(int n_rows, int n_split, const float* partials, float* out, hipStream_t st) {
-    hipLaunchKernelGGL(merge_kernel, dim3(n_rows), dim3(128), 0, st, partials, n_split, out);
+    hipLaunchKernelGGL(merge_kernel, dim3(n_rows), dim3(256), 0, st, partials, n_split, out);
     return hipGetLastError();
 }
 

@@ -3,28 +3,35 @@
 // Allocation for KV-Cache Quantization" (abstract).
 //
 // Per 64-slot tile, one wave computes
-//   z_t = s_t * sum_c (q_c sigma_c scale log2e) level[code_{t,c}]      (QK)
-//   o  += sum_t p_t s^V_t level[vcode_{t,c}]   (times sigma^V_c at the end)  (PV)
+//   z_t = s_t * sum_c (q_c sigma_c scale log2e) level[code_{t,c}]               (QK)
+//   o  += sum_t 2^(z_t - m) s^V_t level[vcode_{t,c}]   (times sigma^V_c at the end)  (PV)
 // with the levels (exact binary16) as matrix operands and the fp32 factors
-// q.sigma and p.s^V split into binary16 hi + lo parts, so the products keep
-// about 22 bits.
+// q.sigma and p.s^V split into binary16 hi + lo parts, so products keep ~22 bits.
 //
 // QK uses v_mfma_f32_32x32x16_f16 with a block-diagonal B operand: lane l decodes
-// one token (slot sigma(l)), and all 64 lanes decode the SAME 8 K-order
+// one token (slot qslot(l)), and all 64 lanes decode the SAME 8 K-order
 // coordinates per instruction (K widths are per (layer, head), so field offsets
 // and widths are wave-uniform).  Lanes 0-31 feed token set 0 into k-slots 0-7 and
 // lanes 32-63 feed token set 1 into k-slots 8-15; B columns 0-15 read only k-slots
-// 0-7 and columns 16-31 only k-slots 8-15, each column being (hi|lo, head).  The
-// 32x32 accumulator then holds, in lane l, 16 logits of column l%32 for slots
+// 0-7 and columns 16-31 only k-slots 8-15, each column being (hi|lo, head).  Since
+// the K order sorts blocks by width, the coordinates are taken one width class at
+// a time, 8 fields per instruction with compile-time offsets (the last unit of a
+// class is padded with zero q in the operand, never in the cache).
+//
+// The 32x32 accumulator then holds, in lane l, 16 logits of column l%32 for slots
 // 16*(l/16) + i, i = 0..15 -- exactly the A-operand layout of the PV product
-// v_mfma_f32_16x16x32_f16 (row = l%16 = (hi|lo, head), k = 8*(l/16) + j), so
+// v_mfma_f32_16x16x32_f16 (row = l%16 = (hi|lo, head), k = 8*(l/16) + j), so the
 // softmax weights never leave registers.  The PV B operand of lane l is 16
-// consecutive slots of one coordinate, i.e. one contiguous 16*v-bit piece of a V
-// run.  Codes become binary16 levels through LDS tables: two codes per lookup
-// (one dword = two levels) for widths <= 4, one code per lookup for widths 5..8.
+// consecutive slots of one coordinate, one contiguous 16*v-bit piece of a V run.
+// Codes become binary16 levels through LDS tables: two codes per lookup (a dword
+// of two levels) for widths <= 5, one code per lookup for widths 6..8.
+//
+// The running max is a lazy reference: it only moves (and the accumulators are
+// only rescaled) when a head's tile max exceeds it by more than 8 (log2 units),
+// so p <= 2^8.  Each wave loads tile n+1 while it computes tile n.
+#pragma once
 #include <math.h>
 
-#pragma once
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -33,16 +40,38 @@ typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
 
-constexpr int kMaxUnits = 24;          // 128 coordinates in 8-wide units, plus one partial unit per class
+constexpr int kMaxUnits = 24;  // 128 coordinates in 8-wide units, plus one partial unit per width class
 constexpr int kWaves = 4;
-constexpr float kPrescale = 256.f;     // keeps q.sigma well inside the binary16 range
+constexpr float kRescaleSlack = 8.f;
 
-// pair tables (widths 1..4): entry a | b << w -> half2(level_w[a], level_w[b])
-__host__ __device__ constexpr int pair_off(int w) { return w == 1 ? 0 : w == 2 ? 4 : w == 3 ? 20 : 84; }
-constexpr int kPairEntries = 340;
-// single tables (widths 5..8)
-__host__ __device__ constexpr int single_off(int w) { return w == 5 ? 0 : w == 6 ? 32 : w == 7 ? 96 : 224; }
-constexpr int kSingleEntries = 480;
+// level tables: pairs (widths 1..5): entry a | b << w -> half2(level_w[a], level_w[b]);
+// singles (widths 6..8)
+constexpr int kPairMax = 5;
+__host__ __device__ constexpr int pair_off(int w) { return w == 1 ? 0 : w == 2 ? 4 : w == 3 ? 20 : w == 4 ? 84 : 340; }
+constexpr int kPairEntries = 1364;
+__host__ __device__ constexpr int single_off(int w) { return w == 6 ? 0 : w == 7 ? 64 : 192; }
+constexpr int kSingleEntries = 448;
+
+struct alignas(16) LevelTables {
+    uint32_t pair[kPairEntries];
+    uint16_t single[kSingleEntries];
+};
+static_assert(sizeof(LevelTables) % 16 == 0, "tables are copied to LDS in 16-byte pieces");
+
+constexpr uint16_t kLevelsInit[510] = {KVQ_LEVELS_FP16_LIST};
+constexpr LevelTables make_level_tables() {
+    LevelTables t{};
+    for (int w = 1; w <= kPairMax; ++w)
+        for (int e = 0; e < (1 << (2 * w)); ++e) {
+            const int a = e & ((1 << w) - 1), b = e >> w;
+            t.pair[pair_off(w) + e] =
+                (uint32_t)kLevelsInit[KVQ_CB_OFF(w) + a] | ((uint32_t)kLevelsInit[KVQ_CB_OFF(w) + b] << 16);
+        }
+    for (int w = kPairMax + 1; w <= 8; ++w)
+        for (int e = 0; e < (1 << w); ++e) t.single[single_off(w) + e] = kLevelsInit[KVQ_CB_OFF(w) + e];
+    return t;
+}
+static __device__ const LevelTables g_level_tables = make_level_tables();
 
 union H8 {
     half8 h;
@@ -54,15 +83,8 @@ __device__ __forceinline__ uint32_t alignbit(uint32_t hi, uint32_t lo, uint32_t 
     return __builtin_amdgcn_alignbit(hi, lo, s);
 }
 
-// bits [r, r + n) (n <= 16) of the 64-bit value hi:lo
-__device__ __forceinline__ uint32_t field64(uint32_t lo, uint32_t hi, int r, int n) {
-    const uint32_t x = r >= 32 ? (hi >> (r - 32)) : alignbit(hi, lo, (uint32_t)r);
-    return x & ((1u << n) - 1u);
-}
-
 struct MfmaSmem {
-    uint32_t pair[kPairEntries];
-    uint16_t single[kSingleEntries];
+    LevelTables tab;
     // binary16 hi/lo of q.sigma.scale by padded position: width class w occupies whole
     // 8-position units (its last unit zero-padded), classes in descending width
     alignas(16) uint16_t qsplit[2][8][8 * kMaxUnits];
@@ -72,13 +94,13 @@ struct MfmaSmem {
     alignas(16) float alpha[kWaves][8];
     float wm[kWaves][8], wl[kWaves][8];
     float wo[kWaves][8][kHeadDim];
-    int nf;
 };
 
 __device__ __forceinline__ float dpp_ror8(float x) {
     // row_ror:8 within each row of 16 lanes: lane l receives lane l ^ 8
     return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
 }
+
 // permlane{16,32}_swap(x, x) returns the even rows (halves) of x in its first result
 // and the odd ones in its second: lane l sees x at l & ~16 (~32) and at l | 16 (| 32).
 // The two results are copied into named integers before any bit cast (a bit cast
@@ -103,17 +125,47 @@ __device__ __forceinline__ float xor32_max(float x) { float a, b; pair32(x, a, b
 __device__ __forceinline__ float xor16_sum(float x) { float a, b; pair16(x, a, b); return a + b; }
 __device__ __forceinline__ float xor32_sum(float x) { float a, b; pair32(x, a, b); return a + b; }
 
-// Two equal-width fields at compile-time bit offset REL of the 64-bit window hi:lo,
-// returned as two binary16 levels in one dword.
+// byte offset 4 * (bits [r, r + n) of x), for a table of dwords
+template <int R, int N>
+__device__ __forceinline__ uint32_t field_x4(uint32_t x) {
+    constexpr uint32_t m = ((1u << N) - 1u) << 2;
+    if (R >= 2) return (x >> (R - 2)) & m;
+    return (x << (2 - R)) & m;
+}
+// byte offset 2 * (bits [r, r + n) of x), for a table of halves
+template <int R, int N>
+__device__ __forceinline__ uint32_t field_x2(uint32_t x) {
+    constexpr uint32_t m = ((1u << N) - 1u) << 1;
+    if (R >= 1) return (x >> (R - 1)) & m;
+    return (x << 1) & m;
+}
+__device__ __forceinline__ uint32_t lds_u32(const void* base, uint32_t byte_off) {
+    return *(const uint32_t*)((const char*)base + byte_off);
+}
+__device__ __forceinline__ uint32_t lds_u16(const void* base, uint32_t byte_off) {
+    return *(const uint16_t*)((const char*)base + byte_off);
+}
+
+// Two equal-width fields at bit offset REL of the 64-bit window hi:lo, returned
+// as two binary16 levels in one dword.
 template <int W, int REL>
-__device__ __forceinline__ uint32_t decode_pair(const MfmaSmem& sm, uint32_t lo, uint32_t hi) {
-    uint32_t x;
-    if (REL >= 32) x = hi >> (REL - 32);
-    else if (REL + 2 * W <= 32) x = lo >> REL;
-    else x = alignbit(hi, lo, REL);
-    if (W <= 4) return sm.pair[pair_off(W) + (x & ((1u << (2 * W)) - 1u))];
-    constexpr uint32_t m = (1u << W) - 1u;
-    return (uint32_t)sm.single[single_off(W) + (x & m)] | ((uint32_t)sm.single[single_off(W) + ((x >> W) & m)] << 16);
+__device__ __forceinline__ uint32_t decode_pair(const LevelTables& t, uint32_t lo, uint32_t hi) {
+    if (W <= kPairMax) {
+        const uint32_t* base = t.pair + pair_off(W);
+        if (REL >= 32) return lds_u32(base, field_x4<(REL >= 32 ? REL - 32 : 0), 2 * W>(hi));
+        if (REL + 2 * W <= 32) return lds_u32(base, field_x4<(REL < 32 ? REL : 0), 2 * W>(lo));
+        return lds_u32(base, field_x4<0, 2 * W>(alignbit(hi, lo, REL)));
+    } else {
+        const uint16_t* base = t.single + single_off(W);
+        uint32_t xa, xb;
+        if (REL >= 32) { xa = hi >> (REL - 32); }
+        else if (REL + W <= 32) { xa = lo >> REL; }
+        else { xa = alignbit(hi, lo, REL); }
+        if (REL + W >= 32) { xb = hi >> (REL + W - 32); }
+        else if (REL + 2 * W <= 32) { xb = lo >> (REL + W); }
+        else { xb = alignbit(hi, lo, REL + W); }
+        return lds_u16(base, field_x2<0, W>(xa)) | (lds_u16(base, field_x2<0, W>(xb)) << 16);
+    }
 }
 
 // QK over the units of one width class: window of 8 fields -> A operand, q split -> B
@@ -124,13 +176,14 @@ __device__ __forceinline__ void qk_class(const MfmaSmem& sm, const uint32_t (&re
         const int st = start + j * 8 * W;
         const int d = min(st >> 5, RD > 0 ? RD - 1 : 0);
         const uint32_t sh = (uint32_t)(st & 31);
-        const uint32_t d0 = rec[d], d1 = rec[d + 1], d2 = rec[d + 2];
-        const uint32_t lo = alignbit(d1, d0, sh), hi = alignbit(d2, d1, sh);
+        const uint32_t d0 = rec[d], d1 = rec[d + 1];
+        const uint32_t lo = alignbit(d1, d0, sh);
+        const uint32_t hi = W <= 4 ? 0u : alignbit(rec[d + 2], d1, sh);
         H8 a;
-        a.u[0] = decode_pair<W, 0>(sm, lo, hi);
-        a.u[1] = decode_pair<W, 2 * W>(sm, lo, hi);
-        a.u[2] = decode_pair<W, 4 * W>(sm, lo, hi);
-        a.u[3] = decode_pair<W, 6 * W>(sm, lo, hi);
+        a.u[0] = decode_pair<W, 0>(sm.tab, lo, hi);
+        a.u[1] = decode_pair<W, 2 * W>(sm.tab, lo, hi);
+        a.u[2] = decode_pair<W, 4 * W>(sm.tab, lo, hi);
+        a.u[3] = decode_pair<W, 6 * W>(sm.tab, lo, hi);
         H8 b;
         const uint4 q4 = *(const uint4*)(bdiag ? qb_src + 8 * (ubase + j) : sm.qzero);
         b.u[0] = q4.x; b.u[1] = q4.y; b.u[2] = q4.z; b.u[3] = q4.w;
@@ -138,67 +191,151 @@ __device__ __forceinline__ void qk_class(const MfmaSmem& sm, const uint32_t (&re
     }
 }
 
+// PV B operand (16 consecutive slots of one coordinate) from the lane's raw words
+template <int V>
+__device__ __forceinline__ void decode_v(const LevelTables& t, const uint32_t* raw, uint32_t sh, H8& b0, H8& b1) {
+    constexpr int NW = (16 * V + 31) / 32;
+    uint32_t nw[NW + 1];
+#pragma unroll
+    for (int k = 0; k < NW; ++k) nw[k] = alignbit(raw[k + 1], raw[k], sh);
+    nw[NW] = 0;
+#pragma unroll
+    for (int pr = 0; pr < 8; ++pr) {
+        const int bit = 2 * V * pr;
+        const int k = bit >> 5, r = bit & 31;
+        uint32_t val;
+        if (V <= kPairMax) {
+            const uint32_t* base = t.pair + pair_off(V);
+            const uint32_t src = (r + 2 * V <= 32) ? (nw[k] >> r) : alignbit(nw[k + 1], nw[k], r);
+            val = lds_u32(base, (src << 2) & (((1u << (2 * V)) - 1u) << 2));
+        } else {
+            const uint16_t* base = t.single + single_off(V);
+            const int bit2 = bit + V, k2 = bit2 >> 5, r2 = bit2 & 31;
+            const uint32_t sa = (r + V <= 32) ? (nw[k] >> r) : alignbit(nw[k + 1], nw[k], r);
+            const uint32_t sb = (r2 + V <= 32) ? (nw[k2] >> r2) : alignbit(nw[k2 + 1], nw[k2], r2);
+            val = lds_u16(base, (sa << 1) & (((1u << V) - 1u) << 1)) |
+                  (lds_u16(base, (sb << 1) & (((1u << V) - 1u) << 1)) << 16);
+        }
+        if (pr < 4) b0.u[pr] = val; else b1.u[pr - 4] = val;
+    }
+}
+
+// s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt << 4 | lgkmcnt << 8 | vmcnt[5:4] << 14)
+constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0)
+constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
+
+typedef __attribute__((address_space(3))) uint8_t lds_u8;
+
+// 16 bytes per lane from global memory straight into LDS at lds_base + 16 * lane
+// (global_load_lds_dwordx4; M0 holds the wave-uniform LDS base).  Written as asm so
+// that the compiler does not order every later LDS read behind it: the caller
+// waits for it explicitly (vmcnt) before reading the buffer, and issues it only
+// after its own reads of that buffer have returned (lgkmcnt).
+#pragma clang diagnostic push
+#pragma clang diagnostic ignored "-Winline-asm"  // M0 is reserved, and this asm does overwrite it
+__device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
+    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                 :
+                 : "v"(gptr), "s"(lds_base)
+                 : "memory", "m0");
+}
+#pragma clang diagnostic pop
+
 template <int V, int RD>
-__global__ __launch_bounds__(256) void decode_mfma_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, const int64_t* __restrict__ seq_byte_off,
     const int32_t* __restrict__ seq_len, int64_t max_len, int64_t capacity, const uint8_t* __restrict__ k_bits,
     const float* __restrict__ k_sigma, const float* __restrict__ v_sigma, float scale_log2, int n_q, int g,
     int pairing, int k_budget, int tiles_per_split, int n_split, float* __restrict__ ws) {
+    constexpr int NW = (16 * V + 31) / 32;  // words of one lane's V piece
+    constexpr int SK = 4 * RD;
+    constexpr int TB = kTile * SK + kHeadDim * 8 * V + 2 * kTile * 4;
     __shared__ MfmaSmem sm;
+    __shared__ __attribute__((aligned(16))) uint8_t tbuf_all[kWaves * TB];  // one tile buffer per wave
+    constexpr int KCH = RD / 4;              // 16-byte chunks per K record
+    constexpr int RCH = (TB - kTile * SK) / 16;  // chunks of the V section and scales
     const int split = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     const int64_t len = min(max((int64_t)seq_len[s], (int64_t)0), max_len);
     const int64_t n_tiles_seq = (len + kTile - 1) / kTile;
     const int64_t t0 = (int64_t)split * tiles_per_split;
     const int64_t t1 = min(t0 + tiles_per_split, n_tiles_seq);
 
+    // lane roles
+    const int col = lane & 31;
+    const bool bdiag = (col >> 4) == (lane >> 5);
+    const int m = lane & 31;
+    const int qslot = 16 * (2 * ((m >> 2) & 1) + (lane >> 5)) + 4 * (m >> 3) + (m & 3);  // QK token
+    const int grp = lane >> 4;       // PV k group: slots 16*grp .. 16*grp+15
+    const int row = lane & 15;       // PV row = (hi|lo) * 8 + head
+    const bool lo_row = row >= 8;
+
+    const uint8_t* head_base = cache + seq_byte_off[s] + (int64_t)kvh * (capacity / kTile) * TB;
+    uint8_t* tbuf = tbuf_all + wave * TB;
+    const uint32_t tbuf_lds = (uint32_t)(uintptr_t)(lds_u8*)tbuf;
+
+    // Tile DMA into this wave's buffer.  K record chunks are stored chunk-major
+    // (chunk k of record r at 16*(64*k + r)), the rest of the tile linearly after them.
+    auto dma_tile = [&](int64_t tau) {
+        const uint8_t* tile = head_base + tau * TB;
+#pragma unroll
+        for (int k = 0; k < KCH; ++k)
+            dma16(tile + lane * SK + 16 * k, tbuf_lds + 1024 * k);
+#pragma unroll
+        for (int j = 0; j < (RCH + 63) / 64; ++j) {
+            const int ch = 64 * j + lane;
+            if (64 * j + 63 < RCH || ch < RCH)
+                dma16(tile + kTile * SK + 16 * ch, tbuf_lds + kTile * SK + 1024 * j);
+        }
+    };
+    int64_t tau = t0 + wave;
+    if (tau < t1) dma_tile(tau);  // independent of the per-head tables: goes out first
+
     // ------------------------------------------------------------------ prologue
-    for (int i = tid; i < kPairEntries; i += 256) {
-        const int w = i < 4 ? 1 : i < 20 ? 2 : i < 84 ? 3 : 4;
-        const int e = i - pair_off(w);
-        const int a = e & ((1 << w) - 1), b = e >> w;
-        sm.pair[i] = (uint32_t)c_levels[KVQ_CB_OFF(w) + a] | ((uint32_t)c_levels[KVQ_CB_OFF(w) + b] << 16);
+    {
+        const uint4* src = (const uint4*)&g_level_tables;
+        uint4* dst = (uint4*)&sm.tab;
+        for (int i = tid; i < (int)(sizeof(LevelTables) / 16); i += 256) dst[i] = src[i];
+        uint4* qz = (uint4*)&sm.qsplit[0][0][0];
+        for (int i = tid; i < (int)(sizeof(sm.qsplit) / 16); i += 256) qz[i] = uint4{0, 0, 0, 0};
+        if (tid == 0) *(uint4*)sm.qzero = uint4{0, 0, 0, 0};
+        for (int c = tid; c < kHeadDim; c += 256) {
+            const int i = pairing == KVQ_PAIR_HALF ? (c & (kMaxBlocks - 1)) : (c >> 1);
+            sm.vsig[c] = v_sigma[kvh * kMaxBlocks + i];
+        }
     }
-    for (int i = tid; i < kSingleEntries; i += 256) {
-        const int w = i < 32 ? 5 : i < 96 ? 6 : i < 224 ? 7 : 8;
-        sm.single[i] = c_levels[KVQ_CB_OFF(w) + i - single_off(w)];
-    }
-    for (int c = tid; c < kHeadDim; c += 256) {
-        const int i = pairing == KVQ_PAIR_HALF ? (c & (kMaxBlocks - 1)) : (c >> 1);
-        sm.vsig[c] = v_sigma[kvh * kMaxBlocks + i];
-    }
-    for (int i = tid; i < 2 * 8 * 8 * kMaxUnits; i += 256) (&sm.qsplit[0][0][0])[i] = 0;
-    if (tid < 8) sm.qzero[tid] = 0;
-    __syncthreads();
-    if (wave == 0) {
-        // width classes in descending order; a block's fields sit at its rank within its class
-        const int i = lane;
-        const int my_w = k_bits[kvh * kMaxBlocks + i];
-        const float my_ksig = k_sigma[kvh * kMaxBlocks + i];
-        const unsigned long long below = (1ull << i) - 1ull;
-        int start = 0, ubase = 0, my_pos = 0;
+    // width classes (descending): every wave ranks the blocks; a block's two fields sit
+    // at its rank within its class.  Wave w fills the q split of heads w, w+4.
+    const int my_w = k_bits[kvh * kMaxBlocks + lane];
+    const float my_ksig = k_sigma[kvh * kMaxBlocks + lane];
+    int my_pos = 0;
+    {
+        const unsigned long long below = (1ull << lane) - 1ull;
+        int start = 0, ubase = 0;
 #pragma unroll
         for (int w = 8; w >= 1; --w) {
             const unsigned long long mk = __ballot(my_w == w);
             const int nfw = 2 * __popcll(mk), units = (nfw + 7) >> 3;
-            if (i == 0) { sm.cls_start[w] = start; sm.cls_units[w] = units; sm.cls_ubase[w] = ubase; }
+            if (tid == 0) { sm.cls_start[w] = start; sm.cls_units[w] = units; sm.cls_ubase[w] = ubase; }
             if (my_w == w) my_pos = 8 * ubase + 2 * __popcll(mk & below);
             start += nfw * w;
             ubase += units;
         }
-        if (my_w > 0) {
-            const int p = pairing == KVQ_PAIR_HALF ? i : 2 * i;
-            const int qq = pairing == KVQ_PAIR_HALF ? i + kMaxBlocks : 2 * i + 1;
-            for (int hh = 0; hh < g; ++hh) {
-                const uint16_t* qrow = q + ((int64_t)s * n_q + kvh * g + hh) * kHeadDim;
+    }
+    __syncthreads();  // zeroed q split before it is filled
+    if (my_w > 0) {
+        const int p = pairing == KVQ_PAIR_HALF ? lane : 2 * lane;
+        const int qq = pairing == KVQ_PAIR_HALF ? lane + kMaxBlocks : 2 * lane + 1;
+        for (int hh = wave; hh < g; hh += kWaves) {
+            const uint16_t* qrow = q + ((int64_t)s * n_q + kvh * g + hh) * kHeadDim;
+            const uint32_t qa = qrow[p], qb2 = qrow[qq];
 #pragma unroll
-                for (int e = 0; e < 2; ++e) {
-                    const float v = h2f(qrow[e ? qq : p]) * my_ksig * scale_log2 * kPrescale;
-                    const _Float16 hi = (_Float16)v;
-                    const _Float16 lo = (_Float16)(v - (float)hi);
-                    sm.qsplit[0][hh][my_pos + e] = __builtin_bit_cast(uint16_t, hi);
-                    sm.qsplit[1][hh][my_pos + e] = __builtin_bit_cast(uint16_t, lo);
-                }
+            for (int e = 0; e < 2; ++e) {
+                const float v = h2f(e ? qb2 : qa) * my_ksig * scale_log2;
+                const _Float16 hi = (_Float16)v;
+                const _Float16 lo = (_Float16)(v - (float)hi);
+                sm.qsplit[0][hh][my_pos + e] = __builtin_bit_cast(uint16_t, hi);
+                sm.qsplit[1][hh][my_pos + e] = __builtin_bit_cast(uint16_t, lo);
             }
         }
     }
@@ -210,57 +347,49 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
         cunits[w] = __builtin_amdgcn_readfirstlane(sm.cls_units[w]);
         cubase[w] = __builtin_amdgcn_readfirstlane(sm.cls_ubase[w]);
     }
-
-    const int col = lane & 31;
-    const bool bdiag = (col >> 4) == (lane >> 5);
-    const uint16_t* qb_src = bdiag ? &sm.qsplit[(col >> 3) & 1][col & 7][0] : nullptr;
-    // slot decoded by this lane for QK: token set lane/32, row m = lane%32
-    const int m = lane & 31;
-    const int qslot = 16 * (2 * ((m >> 2) & 1) + (lane >> 5)) + 4 * (m >> 3) + (m & 3);
-    const int grp = lane >> 4;       // PV k group: slots 16*grp .. 16*grp+15
-    const int row = lane & 15;       // PV row = (hi|lo) * 8 + head
-    const bool lo_row = row >= 8;
-
-    const int64_t SK = 4 * RD;
-    const int64_t TB = tile_bytes(kHeadDim, k_budget, V);
-    const uint8_t* head_base = cache + seq_byte_off[s] + (int64_t)kvh * (capacity / kTile) * TB;
-    constexpr int NW = (16 * V + 31) / 32;  // words of one lane's V piece
+    const uint16_t* qb_src = &sm.qsplit[(col >> 3) & 1][col & 7][0];
 
     floatx4 o[8];
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) o[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
-    float mrun = -INFINITY, lrun = 0.f;
+    float mref = -INFINITY, lrun = 0.f;
 
     // ------------------------------------------------------------------ tiles
-    for (int64_t tau = t0 + wave; tau < t1; tau += kWaves) {
-        const uint8_t* tile = head_base + tau * TB;
+    for (; tau < t1; tau += kWaves) {
         const int nvalid = (int)min((int64_t)kTile, len - tau * kTile);
-        const float* scl = (const float*)(tile + kTile * SK + kHeadDim * 8 * V);
-        const uint8_t* vsec = tile + kTile * SK;
-        // ---- issue every load of the tile first
+        // this tile has landed in the wave's buffer: move what this lane needs to registers
+        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        __builtin_amdgcn_wave_barrier();
         uint32_t rec[RD + 2];
 #pragma unroll
-        for (int k = 0; k < RD / 4; ++k) {
-            const uint4 v4 = *(const uint4*)(tile + qslot * SK + 16 * k);
+        for (int k = 0; k < KCH; ++k) {
+            const uint4 v4 = *(const uint4*)(tbuf + 16 * (64 * k + qslot));
             rec[4 * k] = v4.x; rec[4 * k + 1] = v4.y; rec[4 * k + 2] = v4.z; rec[4 * k + 3] = v4.w;
         }
-        rec[RD] = 0; rec[RD + 1] = 0;
+        rec[RD] = 0;
+        rec[RD + 1] = 0;
+        const uint8_t* vsec = tbuf + kTile * SK;
         uint32_t vraw[8][NW + 1];
-        uint32_t vsh[8];
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
             const int byte0 = (16 * ct + row) * 8 * V + 2 * V * grp;
             const uint32_t* w = (const uint32_t*)(vsec + (byte0 & ~3));
-            vsh[ct] = (uint32_t)(byte0 & 3) * 8;
 #pragma unroll
             for (int k = 0; k <= NW; ++k) vraw[ct][k] = w[k];
         }
-        float4 skv[4], svv[4];
+        const float* scl = (const float*)(vsec + kHeadDim * 8 * V);
+        float sk[16], sv[16];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
-            skv[i] = *(const float4*)(scl + 16 * grp + 4 * i);
-            svv[i] = *(const float4*)(scl + kTile + 16 * grp + 4 * i);
+            const float4 a = *(const float4*)(scl + 16 * grp + 4 * i);
+            const float4 b = *(const float4*)(scl + kTile + 16 * grp + 4 * i);
+            sk[4 * i] = a.x; sk[4 * i + 1] = a.y; sk[4 * i + 2] = a.z; sk[4 * i + 3] = a.w;
+            sv[4 * i] = b.x; sv[4 * i + 1] = b.y; sv[4 * i + 2] = b.z; sv[4 * i + 3] = b.w;
         }
+        // the buffer is free once these reads have returned: fetch the next tile into it
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_wave_barrier();
+        if (tau + kWaves < t1) dma_tile(tau + kWaves);
         // ---- QK: this lane's token, 8 fields of one width class per instruction
         floatx16 acc = {};
         qk_class<8, RD>(sm, rec, cstart[8], cunits[8], cubase[8], qb_src, bdiag, acc);
@@ -271,44 +400,29 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
         qk_class<3, RD>(sm, rec, cstart[3], cunits[3], cubase[3], qb_src, bdiag, acc);
         qk_class<2, RD>(sm, rec, cstart[2], cunits[2], cubase[2], qb_src, bdiag, acc);
         qk_class<1, RD>(sm, rec, cstart[1], cunits[1], cubase[1], qb_src, bdiag, acc);
-        // ---- logits: hi + lo columns (lane l and l^8), token scale, ragged-tail mask
+        // ---- logits: hi + lo columns (lanes l and l^8), token scale, ragged-tail mask
         float z[16];
-        const float sk[16] = {skv[0].x, skv[0].y, skv[0].z, skv[0].w, skv[1].x, skv[1].y, skv[1].z, skv[1].w,
-                              skv[2].x, skv[2].y, skv[2].z, skv[2].w, skv[3].x, skv[3].y, skv[3].z, skv[3].w};
-        const float sv[16] = {svv[0].x, svv[0].y, svv[0].z, svv[0].w, svv[1].x, svv[1].y, svv[1].z, svv[1].w,
-                              svv[2].x, svv[2].y, svv[2].z, svv[2].w, svv[3].x, svv[3].y, svv[3].z, svv[3].w};
 #pragma unroll
-        for (int i = 0; i < 16; ++i) z[i] = (acc[i] + dpp_ror8(acc[i])) * sk[i] * (1.f / kPrescale);
-        if (nvalid < kTile) {
+        for (int i = 0; i < 16; ++i) z[i] = (acc[i] + dpp_ror8(acc[i])) * sk[i];
+        if (__builtin_expect(nvalid < kTile, 0)) {
 #pragma unroll
             for (int i = 0; i < 16; ++i)
                 if (16 * grp + i >= nvalid) z[i] = -INFINITY;
         }
-        // ---- online softmax: a head's 64 logits sit in the lanes with equal lane%16
+        // ---- softmax weights against the lazy reference max
         float tm = z[0];
 #pragma unroll
         for (int i = 1; i < 16; ++i) tm = fmaxf(tm, z[i]);
         tm = xor32_max(xor16_max(tm));
-        const float mnew = fmaxf(mrun, tm);
-        const float alpha = exp2f(mrun - mnew);
-        mrun = mnew;
-        float psum = 0.f;
-        H8 pa[2];
-#pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float p = exp2f(z[i] - mnew);
-            psum += p;
-            const float pv = p * sv[i];
-            const _Float16 ph = (_Float16)pv;
-            const _Float16 pl = (_Float16)(pv - (float)ph);
-            pa[i >> 3].s[i & 7] = __builtin_bit_cast(uint16_t, lo_row ? pl : ph);
-        }
-        lrun = lrun * alpha + psum;
-        // rescale the PV accumulator rows (row 4*(lane/16) + j holds head (row & 7))
-        if (__ballot(alpha != 1.f)) {
+        if (__ballot(tm > mref + kRescaleSlack)) {
+            const float mnew = fmaxf(mref, tm);
+            const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
+            mref = mnew;
+            lrun *= alpha;
             if (lane < 8) sm.alpha[wave][lane] = alpha;
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
             __builtin_amdgcn_wave_barrier();
+            // PV accumulator row 4*(lane/16) + j holds head (row & 7)
             const float4 al = *(const float4*)&sm.alpha[wave][4 * (grp & 1)];
 #pragma unroll
             for (int ct = 0; ct < 8; ++ct) {
@@ -316,33 +430,24 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
             }
             __builtin_amdgcn_wave_barrier();
         }
+        float psum = 0.f;
+        H8 pa[2];
+#pragma unroll
+        for (int i = 0; i < 16; ++i) {
+            const float p = __builtin_amdgcn_exp2f(z[i] - mref);
+            psum += p;
+            const float pv = p * sv[i];
+            const _Float16 ph = (_Float16)pv;
+            const _Float16 pl = (_Float16)(pv - (float)ph);
+            pa[i >> 3].s[i & 7] = __builtin_bit_cast(uint16_t, lo_row ? pl : ph);
+        }
+        lrun += psum;
         // ---- PV: B operand = 16 consecutive slots of coordinate 16*ct + lane%16
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
-            uint32_t nw[NW + 1];
-#pragma unroll
-            for (int k = 0; k < NW; ++k) nw[k] = alignbit(vraw[ct][k + 1], vraw[ct][k], vsh[ct]);
-            nw[NW] = 0;
+            const uint32_t sh = (uint32_t)(((16 * ct + row) * 8 * V + 2 * V * grp) & 3) * 8;
             H8 b0, b1;
-#pragma unroll
-            for (int pr = 0; pr < 8; ++pr) {
-                const int bit = 2 * V * pr;
-                const int k = bit >> 5, r = bit & 31;
-                uint32_t val;
-                if (V <= 4) {
-                    const uint32_t idx = (r + 2 * V <= 32) ? ((nw[k] >> r) & ((1u << (2 * V)) - 1u))
-                                                          : (alignbit(nw[k + 1], nw[k], r) & ((1u << (2 * V)) - 1u));
-                    val = sm.pair[pair_off(V) + idx];
-                } else {
-                    const int bit2 = bit + V, k2 = bit2 >> 5, r2 = bit2 & 31;
-                    const uint32_t ca = (r + V <= 32) ? ((nw[k] >> r) & ((1u << V) - 1u))
-                                                      : (alignbit(nw[k + 1], nw[k], r) & ((1u << V) - 1u));
-                    const uint32_t cb = (r2 + V <= 32) ? ((nw[k2] >> r2) & ((1u << V) - 1u))
-                                                       : (alignbit(nw[k2 + 1], nw[k2], r2) & ((1u << V) - 1u));
-                    val = (uint32_t)sm.single[single_off(V) + ca] | ((uint32_t)sm.single[single_off(V) + cb] << 16);
-                }
-                if (pr < 4) b0.u[pr] = val; else b1.u[pr - 4] = val;
-            }
+            decode_v<V>(sm.tab, vraw[ct], sh, b0, b1);
             o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[0].h, b0.h, o[ct], 0, 0, 0);
             o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[1].h, b1.h, o[ct], 0, 0, 0);
         }
@@ -356,7 +461,7 @@ __global__ __launch_bounds__(256) void decode_mfma_kernel(
     for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
         for (int j = 0; j < 4; ++j) o[ct][j] = xor32_sum(o[ct][j]);
-    if (lane < 8) { sm.wm[wave][lane] = mrun; sm.wl[wave][lane] = lsum; }
+    if (lane < 8) { sm.wm[wave][lane] = mref; sm.wl[wave][lane] = lsum; }
     if (lane < 32) {
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct)

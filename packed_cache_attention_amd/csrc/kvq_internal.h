@@ -4,7 +4,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
-#include "../../include/kvq.h"
+#include "kvq.h"
 #include "kvq_codebooks.inc"
 
 namespace kvq {

@@ -18,8 +18,8 @@ namespace kvq {
 
 // code = #{ j in 1..2^w-1 : x >= RN32(s * RN32(sig * thr_w[j])) }; the products are
 // non-decreasing in j, so the count is found by binary lifting.
-__device__ __forceinline__ uint32_t code_of(float x, int w, float sig, float s) {
-    const float* thr = c_thresholds + KVQ_CB_OFF(w);
+__device__ __forceinline__ uint32_t code_of(const float* thr_all, float x, int w, float sig, float s) {
+    const float* thr = thr_all + KVQ_CB_OFF(w);
     uint32_t code = 0;
     for (int bit = 1 << (w - 1); bit >= 1; bit >>= 1) {
         const uint32_t cand = code + bit;
@@ -30,10 +30,10 @@ __device__ __forceinline__ uint32_t code_of(float x, int w, float sig, float s) 
     return code;
 }
 
-__device__ __forceinline__ uint32_t encode(uint32_t bits16, int w, float sig, float s) {
+__device__ __forceinline__ uint32_t encode(const float* thr_all, uint32_t bits16, int w, float sig, float s) {
     if (w == 0) return 0;
     if (w == 16) return bits16;
-    return code_of(h2f(bits16), w, sig, s);
+    return code_of(thr_all, h2f(bits16), w, sig, s);
 }
 
 // balanced pairwise binary32 tree over the 128 squares (lane l: coordinates 2l, 2l+1)
@@ -70,46 +70,40 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
     __shared__ float s_ks[kTile], s_vs[kTile];
     __shared__ uint8_t s_w[kHeadDim];          // key width per coordinate
     __shared__ float s_ksig[kHeadDim], s_vsig[kHeadDim];
-    __shared__ uint8_t s_bw[kMaxBlocks];       // key width per block
     __shared__ uint8_t s_fc[kHeadDim];         // K order: coordinate of field f
     __shared__ uint16_t s_fo[kHeadDim];        // bit offset of field f in the record
     __shared__ uint8_t s_fw[kHeadDim];         // width of field f
     __shared__ uint8_t s_first[64];            // first field touching record dword k
     __shared__ int s_nf;
+    __shared__ float s_thr[510];               // the codebook thresholds, staged once
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
     // ---- phase 0: per-head tables and the K order ----
+    for (int i = tid; i < 510; i += 256) s_thr[i] = c_thresholds[i];
     if (tid < kMaxBlocks) {
+        // rank blocks by (width desc, index asc) with wave ballots; offsets are prefix
+        // sums of 2*width in that order
         const int i = tid;
         const int w = k_bits[h * kMaxBlocks + i];
         const int p = pairing == KVQ_PAIR_HALF ? i : 2 * i;
         const int q = pairing == KVQ_PAIR_HALF ? i + kMaxBlocks : 2 * i + 1;
-        s_bw[i] = (uint8_t)w;
         s_w[p] = s_w[q] = (uint8_t)w;
         s_ksig[p] = s_ksig[q] = k_sigma[h * kMaxBlocks + i];
         s_vsig[p] = s_vsig[q] = v_sigma[h * kMaxBlocks + i];
-    }
-    __syncthreads();
-    if (tid < kMaxBlocks) {
-        const int i = tid, w = s_bw[i];
+        const unsigned long long below = (1ull << i) - 1ull;
         int rank = 0, off = 0;
-        for (int j = 0; j < kMaxBlocks; ++j) {
-            const int wj = s_bw[j];
-            if (wj > w || (wj == w && j < i)) { ++rank; off += 2 * wj; }
+        for (int wc = 16; wc >= 1; --wc) {
+            const unsigned long long mk = __ballot(w == wc);
+            if (wc > w) { rank += __popcll(mk); off += 2 * wc * __popcll(mk); }
+            if (wc == w) { rank += __popcll(mk & below); off += 2 * wc * __popcll(mk & below); }
         }
-        // blocks of width 0 sort last and hold no field
         if (w > 0) {
-            const int p = pairing == KVQ_PAIR_HALF ? i : 2 * i;
-            const int q = pairing == KVQ_PAIR_HALF ? i + kMaxBlocks : 2 * i + 1;
             s_fc[2 * rank] = (uint8_t)p; s_fo[2 * rank] = (uint16_t)off; s_fw[2 * rank] = (uint8_t)w;
             s_fc[2 * rank + 1] = (uint8_t)q; s_fo[2 * rank + 1] = (uint16_t)(off + w); s_fw[2 * rank + 1] = (uint8_t)w;
         }
         const unsigned long long nz = __ballot(w > 0);
-        if (i == 0) {
-            const int nf = 2 * __popcll(nz);
-            s_nf = nf;
-        }
+        if (i == 0) s_nf = 2 * __popcll(nz);
     }
     __syncthreads();
     const int nf = s_nf;
@@ -127,10 +121,10 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
         const uint32_t vp = *(const uint32_t*)(vx + row * stride_tok + (int64_t)h * stride_head + 2 * lane);
         const float sk = token_norm(kp), sv = token_norm(vp);
         const int c0 = 2 * lane, c1 = 2 * lane + 1;
-        s_kc[p][c0] = (uint16_t)encode(kp & 0xffffu, s_w[c0], s_ksig[c0], sk);
-        s_kc[p][c1] = (uint16_t)encode(kp >> 16, s_w[c1], s_ksig[c1], sk);
-        s_vc[p][c0] = (uint16_t)encode(vp & 0xffffu, v_bits, s_vsig[c0], sv);
-        s_vc[p][c1] = (uint16_t)encode(vp >> 16, v_bits, s_vsig[c1], sv);
+        s_kc[p][c0] = (uint16_t)encode(s_thr, kp & 0xffffu, s_w[c0], s_ksig[c0], sk);
+        s_kc[p][c1] = (uint16_t)encode(s_thr, kp >> 16, s_w[c1], s_ksig[c1], sk);
+        s_vc[p][c0] = (uint16_t)encode(s_thr, vp & 0xffffu, v_bits, s_vsig[c0], sv);
+        s_vc[p][c1] = (uint16_t)encode(s_thr, vp >> 16, v_bits, s_vsig[c1], sv);
         if (lane == 0) { s_ks[p] = sk; s_vs[p] = sv; }
     }
     __syncthreads();
