@@ -167,47 +167,62 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
 }
 
 // grid: n_seq * n_q rows; block: 256 threads = 2 split halves x 128 coordinates
-__global__ __launch_bounds__(256) void merge_kernel(const float* __restrict__ ws, int n_split,
-                                                   float* __restrict__ out) {
+// Split merge: out = sum_j 2^(m_j - M) o_j / sum_j 2^(m_j - M) l_j.  A workgroup
+// takes 32 coordinates of one row; its 32 split groups stride over the splits with
+// their own running maximum, eight splits' loads in flight at a time, and are
+// combined through LDS at the end.
+constexpr int kMergeCols = 32, kMergeGroups = 32, kMergeUnroll = 8;
+
+__global__ __launch_bounds__(kMergeCols * kMergeGroups) void merge_kernel(const float* __restrict__ ws, int n_split,
+                                                                           float* __restrict__ out) {
     const int64_t row = blockIdx.x;
-    const int tid = threadIdx.x, c = tid & 127, half = tid >> 7;
+    const int tid = threadIdx.x, sg = tid / kMergeCols, c = blockIdx.y * kMergeCols + tid % kMergeCols;
     constexpr int D2 = kHeadDim + 2;
     const float* part = ws + row * n_split * D2;
-    __shared__ float s_red[8];
-    __shared__ float s_o[kHeadDim], s_l;
-    float m = -INFINITY;
-    for (int sp = tid; sp < n_split; sp += 256) m = fmaxf(m, part[(int64_t)sp * D2]);
-    for (int off = 32; off >= 1; off >>= 1) m = fmaxf(m, __shfl_xor(m, off));
-    if ((tid & 63) == 0) s_red[tid >> 6] = m;
-    __syncthreads();
-    const float M = fmaxf(fmaxf(s_red[0], s_red[1]), fmaxf(s_red[2], s_red[3]));
-    float l = 0.f, acc = 0.f;
-    if (M != -INFINITY) {
-        int sp = half;
-        for (; sp + 6 < n_split; sp += 8) {
-            const float* p0 = part + (int64_t)sp * D2;
-            const float* p1 = p0 + 2 * D2;
-            const float* p2 = p0 + 4 * D2;
-            const float* p3 = p0 + 6 * D2;
-            const float a0 = exp2f(p0[0] - M), a1 = exp2f(p1[0] - M), a2 = exp2f(p2[0] - M), a3 = exp2f(p3[0] - M);
-            l += a0 * p0[1] + a1 * p1[1] + a2 * p2[1] + a3 * p3[1];
-            acc += a0 * p0[2 + c] + a1 * p1[2 + c] + a2 * p2[2 + c] + a3 * p3[2 + c];
+    float M = -INFINITY, L = 0.f, A = 0.f;
+    for (int sp0 = sg; sp0 < n_split; sp0 += kMergeGroups * kMergeUnroll) {
+        float m[kMergeUnroll], l[kMergeUnroll], o[kMergeUnroll];
+#pragma unroll
+        for (int u = 0; u < kMergeUnroll; ++u) {
+            const int sp = sp0 + u * kMergeGroups;
+            const float* p = part + (int64_t)min(sp, n_split - 1) * D2;
+            m[u] = sp < n_split ? p[0] : -INFINITY;
+            l[u] = p[1];
+            o[u] = p[2 + c];
         }
-        for (; sp < n_split; sp += 2) {
-            const float* p0 = part + (int64_t)sp * D2;
-            const float a0 = exp2f(p0[0] - M);
-            l += a0 * p0[1];
-            acc += a0 * p0[2 + c];
+        float mx = M;
+#pragma unroll
+        for (int u = 0; u < kMergeUnroll; ++u) mx = fmaxf(mx, m[u]);
+        if (mx == -INFINITY) continue;  // nothing attended yet in these splits
+        const float r = exp2f(M - mx);
+        L *= r;
+        A *= r;
+#pragma unroll
+        for (int u = 0; u < kMergeUnroll; ++u) {
+            const float a = exp2f(m[u] - mx);
+            L += a * l[u];
+            A += a * o[u];
         }
+        M = mx;
     }
-    if (half == 1) {
-        s_o[c] = acc;
-        if (c == 0) s_l = l;
-    }
+    __shared__ float s_m[kMergeGroups][kMergeCols], s_l[kMergeGroups][kMergeCols], s_a[kMergeGroups][kMergeCols];
+    s_m[sg][tid % kMergeCols] = M;
+    s_l[sg][tid % kMergeCols] = L;
+    s_a[sg][tid % kMergeCols] = A;
     __syncthreads();
-    if (half == 0) {
-        const float lt = l + s_l;
-        out[row * kHeadDim + c] = lt > 0.f ? (acc + s_o[c]) / lt : 0.f;
+    if (sg == 0) {
+        const int cc = tid % kMergeCols;
+        float Mt = -INFINITY;
+        for (int k = 0; k < kMergeGroups; ++k) Mt = fmaxf(Mt, s_m[k][cc]);
+        float Lt = 0.f, At = 0.f;
+        if (Mt != -INFINITY) {
+            for (int k = 0; k < kMergeGroups; ++k) {
+                const float a = exp2f(s_m[k][cc] - Mt);
+                Lt += a * s_l[k][cc];
+                At += a * s_a[k][cc];
+            }
+        }
+        out[row * kHeadDim + c] = Lt > 0.f ? At / Lt : 0.f;
     }
 }
 
@@ -264,7 +279,8 @@ hipError_t launch_decode_partials(const kvq_geom& g, const DecodePlan& plan, int
 }
 
 hipError_t launch_merge(int n_rows, int n_split, const float* partials, float* out, hipStream_t st) {
-    hipLaunchKernelGGL(merge_kernel, dim3(n_rows), dim3(256), 0, st, partials, n_split, out);
+    hipLaunchKernelGGL(merge_kernel, dim3(n_rows, kHeadDim / kMergeCols), dim3(kMergeCols * kMergeGroups), 0, st,
+                       partials, n_split, out);
     return hipGetLastError();
 }
 

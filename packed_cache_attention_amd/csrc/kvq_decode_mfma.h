@@ -87,7 +87,8 @@ struct MfmaSmem {
     LevelTables tab;
     // binary16 hi/lo of q.sigma.scale by padded position: width class w occupies whole
     // 8-position units (its last unit zero-padded), classes in descending width
-    alignas(16) uint16_t qsplit[2][8][8 * kMaxUnits];
+    alignas(16) uint16_t qsplit[2][8][8 * kMaxUnits + 8];  // rows 400 B apart: the 16 rows read by one
+                                                          // b128 load fall in distinct LDS banks
     alignas(16) uint16_t qzero[8];                // zero operand for the off-diagonal B lanes
     int cls_start[9], cls_units[9], cls_ubase[9]; // per width class: record bit offset, units, first unit
     float vsig[kHeadDim];

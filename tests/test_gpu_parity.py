@@ -178,6 +178,50 @@ def test_appends_equal_bulk_and_decode_after_append():
     check_attention(out.cpu().numpy()[0], ref)
 
 
+APPEND_CASES = [(c[0], c[5], c[6], c[7]) for c in CASES if c[0] in
+                ("k3v3-ragged", "k2v2-ragged", "kodd-v5", "k8v8-max", "k0v1", "konly-v16", "k16v16-pass",
+                 "interleaved")]
+
+
+@pytest.mark.parametrize("case", APPEND_CASES, ids=[c[0] for c in APPEND_CASES])
+def test_small_appends_match_bulk(case):
+    """Appends of 1..4 tokens (the one-wave append path) into two sequences at ragged
+    slots, across tile boundaries, give the oracle's bulk bytes."""
+    name, kb, vb, pairing = case
+    say("small appends %s" % name)
+    H, n0, n1 = 2, (61, 3), (9, 70)
+    wl = synth.Workload("app-" + name, 1, 4, H, 1e6, (0,), kb, vb, "decay")
+    seqs = []
+    for i in range(2):
+        K, V, q = synth.gen_layer(wl.with_lens([n0[i] + n1[i]]), i, 0, n_tok=n0[i] + n1[i], seed=11 + i)
+        if pairing == 1:
+            K = K[:, :, torch.randperm(128, generator=torch.Generator().manual_seed(5))].contiguous()
+        seqs.append((K, V, q))
+    # bulk-quantize the first n0 tokens of each sequence (allocation from those tokens)
+    r = run_batch([(K[:n0[i]], V[:n0[i]], q) for i, (K, V, q) in enumerate(seqs)], kb, vb, 128, pairing=pairing,
+                  check_attn=False)
+    g, cache, off = r["g"], r["cache"], r["off"]
+    rows = torch.cat([K for K, _, _ in seqs], 0).cuda()
+    vrows = torch.cat([V for _, V, _ in seqs], 0).cuda()
+    base = [0, n0[0] + n1[0]]
+    done = list(n0)
+    step = 0
+    while done[0] < n0[0] + n1[0] or done[1] < n0[1] + n1[1]:
+        c = [min(1 + (step + i) % 4, n0[i] + n1[i] - done[i]) for i in range(2)]
+        first = torch.tensor(done, dtype=torch.int64, device="cuda")
+        nn = torch.tensor(c, dtype=torch.int32, device="cuda")
+        src = torch.tensor([base[i] + done[i] for i in range(2)], dtype=torch.int64, device="cuda")
+        kvq.quantize_pack(g, rows, vrows, first, nn, src, 4, r["kbits"], r["ksig"], r["vsig"], cache, off)
+        done = [done[i] + c[i] for i in range(2)]
+        step += 1
+    region = kvq.cache_bytes(g)
+    oc = np.zeros(2 * region, np.uint8)
+    for i, (K, V, _) in enumerate(seqs):
+        oracle.quantize_pack(r["ogeom"], oc[i * region:(i + 1) * region], K.numpy(), V.numpy(), 0, r["ob"], r["osig"],
+                             r["ovsig"])
+    np.testing.assert_array_equal(cache.cpu().numpy(), oc)
+
+
 @pytest.mark.parametrize("kernel", [kvq.DECODE_GENERIC, kvq.DECODE_MFMA])
 def test_split_count_invariance(kernel):
     """Any split of the token axis gives the same output up to fp32 re-association (1e-5 of max|o|)."""
