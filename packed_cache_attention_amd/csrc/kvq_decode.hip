@@ -9,6 +9,8 @@
 // with m in log2 units (logits are pre-multiplied by log2 e) and o unnormalised.
 #include <math.h>
 
+#include <algorithm>
+
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -231,6 +233,21 @@ hipError_t launch_decode_mfma(const kvq_geom& g, const DecodePlan& plan, int n_q
                               int64_t max_len, const uint8_t* k_bits, const float* k_sigma, const float* v_sigma,
                               float scale_log2, float* workspace, hipStream_t st);
 
+int mfma_blocks_per_cu(const kvq_geom& g);
+
+// compute units of the current device (256 if it cannot be queried)
+static int device_cus() {
+    static int cached[64];
+    int dev = 0;
+    if (hipGetDevice(&dev) != hipSuccess || dev < 0 || dev >= 64) return 256;
+    if (cached[dev] <= 0) {
+        int n = 0;
+        if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0) n = 256;
+        cached[dev] = n;
+    }
+    return cached[dev];
+}
+
 int plan_decode(const kvq_geom& g, int n_q_heads, int n_seq, int64_t max_len, int kernel, int tiles_per_split,
                 DecodePlan* plan) {
     const int grp = n_q_heads / g.n_kv_heads;
@@ -242,16 +259,22 @@ int plan_decode(const kvq_geom& g, int n_q_heads, int n_seq, int64_t max_len, in
     if (kernel != KVQ_DECODE_MFMA && kernel != KVQ_DECODE_GENERIC) return KVQ_ERR_ARG;
     const int64_t n_tiles = (max_len + kTile - 1) / kTile;
     int64_t T = tiles_per_split;
-    if (T <= 0) {
-        // enough chunks to give every CU several workgroups, but chunks of at least
-        // 4 tiles (MFMA) so the merge traffic stays small against the cache bytes
+    if (T <= 0 && kernel == KVQ_DECODE_MFMA) {
+        // One pass of resident workgroups: every wave of the grid gets the same
+        // whole number of tiles (chunks are a multiple of the 4 waves), as few as
+        // the chip's resident waves allow.
+        const int64_t units = (int64_t)n_seq * g.n_kv_heads;
+        const int64_t slots = (int64_t)device_cus() * std::max(1, mfma_blocks_per_cu(g));
+        int64_t per_wave = std::max<int64_t>(1, (units * n_tiles + 4 * slots - 1) / (4 * slots));
+        while (units * ((n_tiles + 4 * per_wave - 1) / (4 * per_wave)) > slots && 4 * per_wave < n_tiles) ++per_wave;
+        T = 4 * per_wave;
+    } else if (T <= 0) {
+        // enough chunks to give every CU several workgroups
         const int64_t units = (int64_t)n_seq * g.n_kv_heads;
         const int64_t target = 512;
         int64_t want = (target + units - 1) / (units > 0 ? units : 1);
         if (want < 1) want = 1;
-        T = (n_tiles + want - 1) / want;
-        const int64_t minT = kernel == KVQ_DECODE_MFMA ? 4 : 1;
-        if (T < minT) T = minT;
+        T = std::max<int64_t>(1, (n_tiles + want - 1) / want);
     }
     int64_t ns = n_tiles > 0 ? (n_tiles + T - 1) / T : 1;
     if (ns > 65535) return KVQ_ERR_CAPACITY;

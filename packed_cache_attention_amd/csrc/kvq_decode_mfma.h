@@ -90,12 +90,12 @@ struct MfmaSmem {
     alignas(16) uint16_t qsplit[2][8][8 * kMaxUnits + 8];  // rows 400 B apart: the 16 rows read by one
                                                           // b128 load fall in distinct LDS banks
     alignas(16) uint16_t qzero[8];                // zero operand for the off-diagonal B lanes
-    int cls_start[9], cls_units[9], cls_ubase[9]; // per width class: record bit offset, units, first unit
     float vsig[kHeadDim];
     alignas(16) float alpha[kWaves][8];
     float wm[kWaves][8], wl[kWaves][8];
-    float wo[kWaves][8][kHeadDim];
 };
+// the waves' unnormalised outputs, combined at the end in the (then idle) tile buffers
+typedef float WaveOut[kWaves][8][kHeadDim];
 
 __device__ __forceinline__ float dpp_ror8(float x) {
     // row_ror:8 within each row of 16 lanes: lane l receives lane l ^ 8
@@ -222,8 +222,8 @@ __device__ __forceinline__ void decode_v(const LevelTables& t, const uint32_t* r
 }
 
 // s_waitcnt immediates (gfx9 encoding: vmcnt[3:0] | expcnt << 4 | lgkmcnt << 8 | vmcnt[5:4] << 14)
-constexpr int kWaitVm0 = 0x0F70;    // vmcnt(0)
 constexpr int kWaitLgkm0 = 0xC07F;  // lgkmcnt(0)
+constexpr int wait_vm(int n) { return (n & 15) | (7 << 4) | (15 << 8) | ((n >> 4) & 3) << 14; }  // vmcnt(n)
 
 typedef __attribute__((address_space(3))) uint8_t lds_u8;
 
@@ -243,20 +243,51 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
 #pragma clang diagnostic pop
 
 template <int V, int RD>
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void decode_mfma_kernel(
+__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, const int64_t* __restrict__ seq_byte_off,
     const int32_t* __restrict__ seq_len, int64_t max_len, int64_t capacity, const uint8_t* __restrict__ k_bits,
     const float* __restrict__ k_sigma, const float* __restrict__ v_sigma, float scale_log2, int n_q, int g,
     int pairing, int k_budget, int tiles_per_split, int n_split, float* __restrict__ ws) {
-    constexpr int NW = (16 * V + 31) / 32;  // words of one lane's V piece
-    constexpr int SK = 4 * RD;
-    constexpr int TB = kTile * SK + kHeadDim * 8 * V + 2 * kTile * 4;
+    constexpr int NW = (16 * V + 31) / 32;       // words of one lane's V piece
+    constexpr int SK = 4 * RD;                   // K record bytes
+    constexpr int KB = kTile * SK;               // K section of a tile
+    constexpr int VB = kHeadDim * 8 * V + 2 * kTile * 4;  // V runs and scales
+    constexpr int TB = KB + VB;
+    constexpr int KI = RD / 4;                   // 16-byte DMA instructions of a K section
+    constexpr int VI = (VB / 16 + 63) / 64;      // ... of a V section
+    constexpr int WB = 2 * KB + VB;              // per wave: two K buffers, one V buffer
+    constexpr int BUF = kWaves * WB > (int)sizeof(WaveOut) ? kWaves * WB : (int)sizeof(WaveOut);
     __shared__ MfmaSmem sm;
-    __shared__ __attribute__((aligned(16))) uint8_t tbuf_all[kWaves * TB];  // one tile buffer per wave
-    constexpr int KCH = RD / 4;              // 16-byte chunks per K record
-    constexpr int RCH = (TB - kTile * SK) / 16;  // chunks of the V section and scales
+    __shared__ __attribute__((aligned(16))) uint8_t bufs[BUF];
     const int split = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+
+    // ---- every global load of the prologue goes out before anything waits on one
+    const int my_w = k_bits[kvh * kMaxBlocks + lane];
+    const float my_ksig = k_sigma[kvh * kMaxBlocks + lane];
+    float my_vsig = 0.f;
+    if (tid < kHeadDim) {
+        const int i = pairing == KVQ_PAIR_HALF ? (tid & (kMaxBlocks - 1)) : (tid >> 1);
+        my_vsig = v_sigma[kvh * kMaxBlocks + i];
+    }
+    const int qp = pairing == KVQ_PAIR_HALF ? lane : 2 * lane;
+    const int qq = pairing == KVQ_PAIR_HALF ? lane + kMaxBlocks : 2 * lane + 1;
+    uint32_t qv[2][2] = {{0u, 0u}, {0u, 0u}};  // heads wave and wave + 4: coordinates qp, qq
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int hh = wave + kWaves * e;
+        if (hh < g) {
+            const uint16_t* qrow = q + ((int64_t)s * n_q + kvh * g + hh) * kHeadDim;
+            qv[e][0] = qrow[qp];
+            qv[e][1] = qrow[qq];
+        }
+    }
+    constexpr int kTabChunks = (int)(sizeof(LevelTables) / 16);
+    static_assert(kTabChunks <= 512, "the level tables are staged in two 16-byte pieces per thread");
+    const uint4* tsrc = (const uint4*)&g_level_tables;
+    const uint4 tab0 = tsrc[tid];
+    const uint4 tab1 = tid + 256 < kTabChunks ? tsrc[tid + 256] : uint4{0u, 0u, 0u, 0u};
+
     const int64_t len = min(max((int64_t)seq_len[s], (int64_t)0), max_len);
     const int64_t n_tiles_seq = (len + kTile - 1) / kTile;
     const int64_t t0 = (int64_t)split * tiles_per_split;
@@ -272,44 +303,47 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     const bool lo_row = row >= 8;
 
     const uint8_t* head_base = cache + seq_byte_off[s] + (int64_t)kvh * (capacity / kTile) * TB;
-    uint8_t* tbuf = tbuf_all + wave * TB;
-    const uint32_t tbuf_lds = (uint32_t)(uintptr_t)(lds_u8*)tbuf;
+    uint8_t* wbuf = bufs + wave * WB;
+    const uint32_t wbuf_lds = (uint32_t)(uintptr_t)(lds_u8*)wbuf;
 
-    // Tile DMA into this wave's buffer.  K record chunks are stored chunk-major
-    // (chunk k of record r at 16*(64*k + r)), the rest of the tile linearly after them.
-    auto dma_tile = [&](int64_t tau) {
+    // Tile DMA.  A K section goes to K buffer kb with record chunks chunk-major
+    // (chunk k of record r at 16*(64*k + r)); a V section (runs, then scales) goes
+    // linearly to the V buffer.  Each wave issues, in order: K(n+1) when tile n
+    // starts and V(n+1) when tile n's V reads have returned, so at the start of a
+    // tile its K section is complete once at most VI loads are outstanding, and its
+    // V section once at most KI are (none after the wave's last tile).
+    auto dma_k = [&](int64_t tau, int kb) {
         const uint8_t* tile = head_base + tau * TB;
 #pragma unroll
-        for (int k = 0; k < KCH; ++k)
-            dma16(tile + lane * SK + 16 * k, tbuf_lds + 1024 * k);
+        for (int k = 0; k < KI; ++k) dma16(tile + lane * SK + 16 * k, wbuf_lds + kb * KB + 1024 * k);
+    };
+    auto dma_v = [&](int64_t tau) {
+        const uint8_t* vsec = head_base + tau * TB + KB;
 #pragma unroll
-        for (int j = 0; j < (RCH + 63) / 64; ++j) {
+        for (int j = 0; j < VI; ++j) {
             const int ch = 64 * j + lane;
-            if (64 * j + 63 < RCH || ch < RCH)
-                dma16(tile + kTile * SK + 16 * ch, tbuf_lds + kTile * SK + 1024 * j);
+            if (64 * j + 63 < VB / 16 || ch < VB / 16) dma16(vsec + 16 * ch, wbuf_lds + 2 * KB + 1024 * j);
         }
     };
     int64_t tau = t0 + wave;
-    if (tau < t1) dma_tile(tau);  // independent of the per-head tables: goes out first
+    if (tau < t1) {
+        dma_k(tau, 0);
+        dma_v(tau);
+    }
 
     // ------------------------------------------------------------------ prologue
+    ((uint4*)&sm.tab)[tid] = tab0;
+    if (tid + 256 < kTabChunks) ((uint4*)&sm.tab)[tid + 256] = tab1;
     {
-        const uint4* src = (const uint4*)&g_level_tables;
-        uint4* dst = (uint4*)&sm.tab;
-        for (int i = tid; i < (int)(sizeof(LevelTables) / 16); i += 256) dst[i] = src[i];
         uint4* qz = (uint4*)&sm.qsplit[0][0][0];
         for (int i = tid; i < (int)(sizeof(sm.qsplit) / 16); i += 256) qz[i] = uint4{0, 0, 0, 0};
         if (tid == 0) *(uint4*)sm.qzero = uint4{0, 0, 0, 0};
-        for (int c = tid; c < kHeadDim; c += 256) {
-            const int i = pairing == KVQ_PAIR_HALF ? (c & (kMaxBlocks - 1)) : (c >> 1);
-            sm.vsig[c] = v_sigma[kvh * kMaxBlocks + i];
-        }
+        if (tid < kHeadDim) sm.vsig[tid] = my_vsig;
     }
     // width classes (descending): every wave ranks the blocks; a block's two fields sit
     // at its rank within its class.  Wave w fills the q split of heads w, w+4.
-    const int my_w = k_bits[kvh * kMaxBlocks + lane];
-    const float my_ksig = k_sigma[kvh * kMaxBlocks + lane];
     int my_pos = 0;
+    int cstart[9], cunits[9], cubase[9];
     {
         const unsigned long long below = (1ull << lane) - 1ull;
         int start = 0, ubase = 0;
@@ -317,7 +351,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
         for (int w = 8; w >= 1; --w) {
             const unsigned long long mk = __ballot(my_w == w);
             const int nfw = 2 * __popcll(mk), units = (nfw + 7) >> 3;
-            if (tid == 0) { sm.cls_start[w] = start; sm.cls_units[w] = units; sm.cls_ubase[w] = ubase; }
+            cstart[w] = start;
+            cunits[w] = units;
+            cubase[w] = ubase;
             if (my_w == w) my_pos = 8 * ubase + 2 * __popcll(mk & below);
             start += nfw * w;
             ubase += units;
@@ -325,29 +361,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     }
     __syncthreads();  // zeroed q split before it is filled
     if (my_w > 0) {
-        const int p = pairing == KVQ_PAIR_HALF ? lane : 2 * lane;
-        const int qq = pairing == KVQ_PAIR_HALF ? lane + kMaxBlocks : 2 * lane + 1;
-        for (int hh = wave; hh < g; hh += kWaves) {
-            const uint16_t* qrow = q + ((int64_t)s * n_q + kvh * g + hh) * kHeadDim;
-            const uint32_t qa = qrow[p], qb2 = qrow[qq];
 #pragma unroll
-            for (int e = 0; e < 2; ++e) {
-                const float v = h2f(e ? qb2 : qa) * my_ksig * scale_log2;
+        for (int e = 0; e < 2; ++e) {
+            const int hh = wave + kWaves * e;
+            if (hh >= g) continue;
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+                const float v = h2f(qv[e][f]) * my_ksig * scale_log2;
                 const _Float16 hi = (_Float16)v;
                 const _Float16 lo = (_Float16)(v - (float)hi);
-                sm.qsplit[0][hh][my_pos + e] = __builtin_bit_cast(uint16_t, hi);
-                sm.qsplit[1][hh][my_pos + e] = __builtin_bit_cast(uint16_t, lo);
+                sm.qsplit[0][hh][my_pos + f] = __builtin_bit_cast(uint16_t, hi);
+                sm.qsplit[1][hh][my_pos + f] = __builtin_bit_cast(uint16_t, lo);
             }
         }
     }
     __syncthreads();
-    int cstart[9], cunits[9], cubase[9];
-#pragma unroll
-    for (int w = 1; w <= 8; ++w) {
-        cstart[w] = __builtin_amdgcn_readfirstlane(sm.cls_start[w]);
-        cunits[w] = __builtin_amdgcn_readfirstlane(sm.cls_units[w]);
-        cubase[w] = __builtin_amdgcn_readfirstlane(sm.cls_ubase[w]);
-    }
     const uint16_t* qb_src = &sm.qsplit[(col >> 3) & 1][col & 7][0];
 
     floatx4 o[8];
@@ -356,41 +384,25 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     float mref = -INFINITY, lrun = 0.f;
 
     // ------------------------------------------------------------------ tiles
+    int kb = 0;
     for (; tau < t1; tau += kWaves) {
         const int nvalid = (int)min((int64_t)kTile, len - tau * kTile);
-        // this tile has landed in the wave's buffer: move what this lane needs to registers
-        __builtin_amdgcn_s_waitcnt(kWaitVm0);
+        const bool more = tau + kWaves < t1;
+        // K section landed: the lane's record to registers, then the next K section
+        // into the other K buffer
+        __builtin_amdgcn_s_waitcnt(wait_vm(VI));
         __builtin_amdgcn_wave_barrier();
         uint32_t rec[RD + 2];
+        const uint8_t* kbuf = wbuf + kb * KB;
 #pragma unroll
-        for (int k = 0; k < KCH; ++k) {
-            const uint4 v4 = *(const uint4*)(tbuf + 16 * (64 * k + qslot));
+        for (int k = 0; k < RD / 4; ++k) {
+            const uint4 v4 = *(const uint4*)(kbuf + 16 * (64 * k + qslot));
             rec[4 * k] = v4.x; rec[4 * k + 1] = v4.y; rec[4 * k + 2] = v4.z; rec[4 * k + 3] = v4.w;
         }
         rec[RD] = 0;
         rec[RD + 1] = 0;
-        const uint8_t* vsec = tbuf + kTile * SK;
-        uint32_t vraw[8][NW + 1];
-#pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-            const int byte0 = (16 * ct + row) * 8 * V + 2 * V * grp;
-            const uint32_t* w = (const uint32_t*)(vsec + (byte0 & ~3));
-#pragma unroll
-            for (int k = 0; k <= NW; ++k) vraw[ct][k] = w[k];
-        }
-        const float* scl = (const float*)(vsec + kHeadDim * 8 * V);
-        float sk[16], sv[16];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float4 a = *(const float4*)(scl + 16 * grp + 4 * i);
-            const float4 b = *(const float4*)(scl + kTile + 16 * grp + 4 * i);
-            sk[4 * i] = a.x; sk[4 * i + 1] = a.y; sk[4 * i + 2] = a.z; sk[4 * i + 3] = a.w;
-            sv[4 * i] = b.x; sv[4 * i + 1] = b.y; sv[4 * i + 2] = b.z; sv[4 * i + 3] = b.w;
-        }
-        // the buffer is free once these reads have returned: fetch the next tile into it
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-        __builtin_amdgcn_wave_barrier();
-        if (tau + kWaves < t1) dma_tile(tau + kWaves);
+        if (more) dma_k(tau + kWaves, kb ^ 1);
+        kb ^= 1;
         // ---- QK: this lane's token, 8 fields of one width class per instruction
         floatx16 acc = {};
         qk_class<8, RD>(sm, rec, cstart[8], cunits[8], cubase[8], qb_src, bdiag, acc);
@@ -401,6 +413,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
         qk_class<3, RD>(sm, rec, cstart[3], cunits[3], cubase[3], qb_src, bdiag, acc);
         qk_class<2, RD>(sm, rec, cstart[2], cunits[2], cubase[2], qb_src, bdiag, acc);
         qk_class<1, RD>(sm, rec, cstart[1], cunits[1], cubase[1], qb_src, bdiag, acc);
+        // ---- V section landed (scales, runs)
+        if (more) __builtin_amdgcn_s_waitcnt(wait_vm(KI));
+        else __builtin_amdgcn_s_waitcnt(wait_vm(0));
+        __builtin_amdgcn_wave_barrier();
+        const uint8_t* vsec = wbuf + 2 * KB;
+        const float* scl = (const float*)(vsec + kHeadDim * 8 * V);
+        float sk[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 a = *(const float4*)(scl + 16 * grp + 4 * i);
+            sk[4 * i] = a.x; sk[4 * i + 1] = a.y; sk[4 * i + 2] = a.z; sk[4 * i + 3] = a.w;
+        }
         // ---- logits: hi + lo columns (lanes l and l^8), token scale, ragged-tail mask
         float z[16];
 #pragma unroll
@@ -431,6 +455,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
             }
             __builtin_amdgcn_wave_barrier();
         }
+        float sv[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 b = *(const float4*)(scl + kTile + 16 * grp + 4 * i);
+            sv[4 * i] = b.x; sv[4 * i + 1] = b.y; sv[4 * i + 2] = b.z; sv[4 * i + 3] = b.w;
+        }
         float psum = 0.f;
         H8 pa[2];
 #pragma unroll
@@ -446,11 +476,21 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
         // ---- PV: B operand = 16 consecutive slots of coordinate 16*ct + lane%16
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct) {
-            const uint32_t sh = (uint32_t)(((16 * ct + row) * 8 * V + 2 * V * grp) & 3) * 8;
+            const int byte0 = (16 * ct + row) * 8 * V + 2 * V * grp;
+            const uint32_t* wv = (const uint32_t*)(vsec + (byte0 & ~3));
+            uint32_t vraw[NW + 1];
+#pragma unroll
+            for (int k = 0; k <= NW; ++k) vraw[k] = wv[k];
             H8 b0, b1;
-            decode_v<V>(sm.tab, vraw[ct], sh, b0, b1);
+            decode_v<V>(sm.tab, vraw, (uint32_t)(byte0 & 3) * 8, b0, b1);
             o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[0].h, b0.h, o[ct], 0, 0, 0);
             o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[1].h, b1.h, o[ct], 0, 0, 0);
+        }
+        // the V buffer is free once its reads have returned
+        if (more) {
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+            __builtin_amdgcn_wave_barrier();
+            dma_v(tau + kWaves);
         }
     }
 
@@ -462,12 +502,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
     for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
         for (int j = 0; j < 4; ++j) o[ct][j] = xor32_sum(o[ct][j]);
+    WaveOut& wo = *(WaveOut*)bufs;
+    __syncthreads();  // every wave is done with its tile buffers
     if (lane < 8) { sm.wm[wave][lane] = mref; sm.wl[wave][lane] = lsum; }
     if (lane < 32) {
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
-            for (int j = 0; j < 4; ++j) sm.wo[wave][4 * (lane >> 4) + j][16 * ct + (lane & 15)] = o[ct][j];
+            for (int j = 0; j < 4; ++j) wo[wave][4 * (lane >> 4) + j][16 * ct + (lane & 15)] = o[ct][j];
     }
     __syncthreads();
     // merge the four waves and write this chunk's partials
@@ -483,7 +525,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void d
             for (int w = 0; w < kWaves; ++w) {
                 const float a = exp2f(sm.wm[w][hh] - M);
                 l += a * sm.wl[w][hh];
-                acc += a * sm.wo[w][hh][c];
+                acc += a * wo[w][hh][c];
             }
         }
         float* part = ws + (((int64_t)s * n_q + kvh * g + hh) * n_split + split) * D2;
@@ -511,6 +553,22 @@ hipError_t launch_mfma_v(const kvq_geom& g, const DecodePlan& plan, int n_q_head
     KVQ_LAUNCH(0) KVQ_LAUNCH(4) KVQ_LAUNCH(8) KVQ_LAUNCH(12) KVQ_LAUNCH(16)
 #undef KVQ_LAUNCH
     return hipErrorInvalidValue;
+}
+
+// resident workgroups per CU of the instantiation serving geometry g (0 if unknown)
+template <int V>
+int mfma_blocks_per_cu_v(const kvq_geom& g) {
+    const int rd = (int)(k_record_bytes(g.k_budget) / 4);
+    int n = 0;
+#define KVQ_OCC(RDV)                                                                                         \
+    if (rd == RDV) {                                                                                          \
+        if (hipOccupancyMaxActiveBlocksPerMultiprocessor(&n, decode_mfma_kernel<V, RDV>, 256, 0) != hipSuccess) \
+            n = 0;                                                                                            \
+        return n;                                                                                             \
+    }
+    KVQ_OCC(0) KVQ_OCC(4) KVQ_OCC(8) KVQ_OCC(12) KVQ_OCC(16)
+#undef KVQ_OCC
+    return 0;
 }
 
 }  // namespace kvq

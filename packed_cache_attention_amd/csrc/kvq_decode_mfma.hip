@@ -15,6 +15,25 @@ hipError_t launch_mfma_v(const kvq_geom& g, const DecodePlan& plan, int n_q_head
     const float*, float, float*, hipStream_t);
 KVQ_EXTERN(1) KVQ_EXTERN(2) KVQ_EXTERN(3) KVQ_EXTERN(4) KVQ_EXTERN(5) KVQ_EXTERN(6) KVQ_EXTERN(7) KVQ_EXTERN(8)
 #undef KVQ_EXTERN
+template <int V>
+int mfma_blocks_per_cu_v(const kvq_geom& g);
+#define KVQ_EXTERN(VB) extern template int mfma_blocks_per_cu_v<VB>(const kvq_geom&);
+KVQ_EXTERN(1) KVQ_EXTERN(2) KVQ_EXTERN(3) KVQ_EXTERN(4) KVQ_EXTERN(5) KVQ_EXTERN(6) KVQ_EXTERN(7) KVQ_EXTERN(8)
+#undef KVQ_EXTERN
+
+int mfma_blocks_per_cu(const kvq_geom& g) {
+    switch (g.v_bits) {
+        case 1: return mfma_blocks_per_cu_v<1>(g);
+        case 2: return mfma_blocks_per_cu_v<2>(g);
+        case 3: return mfma_blocks_per_cu_v<3>(g);
+        case 4: return mfma_blocks_per_cu_v<4>(g);
+        case 5: return mfma_blocks_per_cu_v<5>(g);
+        case 6: return mfma_blocks_per_cu_v<6>(g);
+        case 7: return mfma_blocks_per_cu_v<7>(g);
+        case 8: return mfma_blocks_per_cu_v<8>(g);
+        default: return 0;
+    }
+}
 
 hipError_t launch_decode_mfma(const kvq_geom& g, const DecodePlan& plan, int n_q_heads, const uint16_t* q,
                               const uint8_t* cache, const int64_t* seq_byte_off, const int32_t* seq_len, int n_seq,

@@ -5,4 +5,5 @@ namespace kvq {
 template hipError_t launch_mfma_v<5>(const kvq_geom&, const DecodePlan&, int, const uint16_t*, const uint8_t*,
                                      const int64_t*, const int32_t*, int, int64_t, const uint8_t*, const float*,
                                      const float*, float, float*, hipStream_t);
+template int mfma_blocks_per_cu_v<5>(const kvq_geom&);
 }  // namespace kvq
