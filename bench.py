@@ -15,9 +15,15 @@ Phases, all on the GPU through the C ABI (libkvq.so):
 
 value = algorithmic bytes of one step (packed cache read by attention + queries
 + outputs + appended token) / measured step time, in GB/s.  The dominant kernel's
-duration is measured with HIP events around each split-phase launch on the stream
-it runs on.  A CPU baseline runs the oracle (test infrastructure) on a bounded
-sample of the same workload.
+average duration is measured with one pair of HIP events around the 36 layers'
+split-phase launches issued back to back on the stream they run on (the GPU is
+held by a spin while the host enqueues them), which matches the kernel durations
+rocprofv3 reports.  A CPU baseline runs the oracle (test infrastructure) on a
+bounded sample of the same workload.
+
+`python bench.py --traffic-from FETCH.csv WRITE.csv` instead turns two rocprofv3
+--pmc runs (FETCH_SIZE, then WRITE_SIZE, of this script with --copy-probe-mib)
+into HBM bytes per decode launch, calibrated against the plain copy kernel.
 """
 from __future__ import annotations
 
@@ -41,9 +47,49 @@ def log(msg):
 
 
 def kernel_source_hash(kernel: str) -> str:
-    name = "kvq_decode_mfma.hip" if kernel == "mfma" else "kvq_decode.hip"
-    with open(os.path.join(ROOT, "packed_cache_attention_amd", "csrc", name), "rb") as f:
-        return hashlib.sha256(f.read()).hexdigest()[:16]
+    names = (["kvq_decode_mfma.h", "kvq_decode_mfma.hip", "kvq_internal.h"] if kernel == "mfma"
+             else ["kvq_decode.hip", "kvq_internal.h"])
+    h = hashlib.sha256()
+    for name in names:
+        with open(os.path.join(ROOT, "packed_cache_attention_amd", "csrc", name), "rb") as f:
+            h.update(f.read())
+    return h.hexdigest()[:16]
+
+
+def traffic_from(fetch_csv: str, write_csv: str, copy_mib: int, workload: str):
+    """HBM bytes per decode launch from rocprofv3 FETCH_SIZE / WRITE_SIZE runs (KiB per
+    dispatch), each scaled by the ratio of known bytes to the counter's reading for the
+    plain copy kernel of copy_mib MiB in the same run."""
+    import csv
+
+    def per_kernel(path, counter):
+        rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
+        rows.sort(key=lambda r: int(r["Dispatch_Id"]))
+        dec = [float(r["Counter_Value"]) for r in rows if "decode_mfma_kernel" in r["Kernel_Name"]]
+        # the copy probe: the last three copy dispatches of the run (nothing follows them)
+        cp = [r for r in rows if "copy" in r["Kernel_Name"].lower()][-3:]
+        big = [float(r["Counter_Value"]) for r in cp]
+        return (sum(dec) / len(dec) if dec else None), (sum(big) / len(big) if big else None), len(dec), \
+            (cp[0]["Kernel_Name"][:60] if cp else "")
+
+    f_dec, f_copy, n_f, copy_name = per_kernel(fetch_csv, "FETCH_SIZE")
+    w_dec, w_copy, n_w, _ = per_kernel(write_csv, "WRITE_SIZE")
+    copy_bytes = copy_mib * (1 << 20)
+    ff = copy_bytes / (f_copy * 1024.0)
+    fw = copy_bytes / (w_copy * 1024.0)
+    hbm = f_dec * 1024.0 * ff + w_dec * 1024.0 * fw
+    out = {"kernel": "decode_mfma_kernel", "source_sha256_16": kernel_source_hash("mfma"),
+           "fetch_kib_per_launch": round(f_dec, 1), "write_kib_per_launch": round(w_dec, 1),
+           "launches": [n_f, n_w], "copy_kernel": copy_name, "copy_bytes": copy_bytes,
+           "copy_fetch_kib": round(f_copy, 1), "copy_write_kib": round(w_copy, 1),
+           "fetch_scale": round(ff, 4), "write_scale": round(fw, 4), "hbm_bytes_per_launch": int(hbm)}
+    tf = {}
+    if os.path.exists(TRAFFIC_FILE):
+        tf = json.load(open(TRAFFIC_FILE))
+    tf[workload] = out
+    with open(TRAFFIC_FILE, "w") as f:
+        json.dump(tf, f, indent=1, sort_keys=True)
+    print(json.dumps(out))
 
 
 def main():
@@ -59,7 +105,13 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
+    if args.traffic_from:
+        traffic_from(args.traffic_from[0], args.traffic_from[1], args.copy_probe_mib or 256,
+                     {"c2": "c2-llama8b-layer-32k-k2v2", "c3": "c3-qwen3b-36layer-128k-k3v3",
+                      "c4": "c4-qwen3b-36layer-512k-k3v3", "c5": "c5-r1qwen7b-28layer-16seq-4k32k-k3v2"}[args.workload])
+        return
 
     world = int(os.environ.get("WORLD_SIZE", "1"))
     if args.gpus != 1 or world != 1:
@@ -241,25 +293,29 @@ def main():
     log("timed %d steps: %.4f ms/step (wall %.4f ms/step), %.1f GB/s = %.1f%% of HBM peak"
         % (args.steps, ms_step, wall * 1e3 / args.steps, value, 100 * value / HBM_PEAK_GBPS))
 
-    # ------------------------------------------------------------ dominant kernel: events around each launch
-    # The GPU is first held by a spin so the host enqueues the whole step ahead of it;
-    # the event pairs then bracket back-to-back work with no host gaps.
+    # ------------------------------------------------------------ dominant kernel: back-to-back launches
+    # One event pair brackets the 36 layers' split-phase launches, enqueued while a
+    # spin holds the GPU, so the span is the kernels' own time.
     ksteps = min(args.steps, 10)
     durs = []
+    kd0 = torch.cuda.Event(enable_timing=True)
+    kd1 = torch.cuda.Event(enable_timing=True)
     for _ in range(ksteps):
-        ev = ([torch.cuda.Event(enable_timing=True) for _ in range(L)],
-              [torch.cuda.Event(enable_timing=True) for _ in range(L)])
         torch.cuda._sleep(20_000_000)
-        step(ev)
+        kd0.record()
+        for l in range(L):
+            kvq.decode_partials(g, Qall[l], cache[l], off, seq_len, max_len, kbits[l], ksig[l], vsig[l],
+                                partials[l], kernel=kern, tiles_per_split=args.tiles_per_split)
+        kd1.record()
         torch.cuda.synchronize()
-        durs += [ev[0][l].elapsed_time(ev[1][l]) / 1e3 for l in range(L)]
+        durs.append(kd0.elapsed_time(kd1) / 1e3 / L)
     kdur = float(np.mean(durs))
-    ln = seq_len.cpu().numpy().astype(np.int64) - 1 - np.arange(ksteps).mean()
+    ln = seq_len.cpu().numpy().astype(np.int64)
     launch_bytes = float(ln.sum()) * H * bytes_per_token_head
     achieved = launch_bytes / kdur / 1e9
     kernel_name = "decode_mfma_kernel" if plan["kernel"] == kvq.DECODE_MFMA else "decode_generic_kernel"
     log("%s: %.2f us/launch avg over %d launches, %.1f GB/s algorithmic (%.1f%% of peak)"
-        % (kernel_name, kdur * 1e6, len(durs), achieved, 100 * achieved / HBM_PEAK_GBPS))
+        % (kernel_name, kdur * 1e6, len(durs) * L, achieved, 100 * achieved / HBM_PEAK_GBPS))
 
     traffic = None
     src_hash = kernel_source_hash("mfma" if kernel_name == "decode_mfma_kernel" else "generic")
@@ -321,36 +377,43 @@ def main():
     print(json.dumps(result), flush=True)
 
 
-def cpu_baseline(wl, Kall, Vall, Qall, lens, row0, bytes_per_token_head):
-    """Oracle (CPU, fp64) on a bounded sample: layer 0 of sequence 0, all KV heads,
-    a token window sized to keep the run around 10-20 s; reports the packed bytes
-    its decode attention processes per second."""
+def cpu_baseline(wl, Kall, Vall, Qall, lens, row0, bytes_per_token_head, budget_s=12.0):
+    """Oracle (CPU, fp64) on a bounded sample: sequence 0 at its full length, layer
+    after layer until about budget_s seconds of oracle work: exact energies,
+    allocation, quantize+pack, then decode attention of the layer's queries.
+    Reports the packed bytes its decode attention processes per second."""
     import numpy as np
     import oracle
     n_threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or min(16, os.cpu_count() or 1)
     os.environ["OMP_NUM_THREADS"] = str(n_threads)
-    n = min(lens[0], 32768)
+    n = lens[0]
     H = wl.n_kv_heads
-    K = Kall[0, int(row0[0]):int(row0[0]) + n].cpu().numpy()
-    V = Vall[0, int(row0[0]):int(row0[0]) + n].cpu().numpy()
-    q = Qall[0, 0].cpu().numpy()
-    t0 = time.perf_counter()
-    eK = oracle.block_energy(K)
-    eV = oracle.block_energy(V)
-    kb, ks = oracle.allocate(eK, wl.k_budget)
-    _, vs = oracle.allocate(eV, wl.v_bits * 64, oracle.UNIFORM)
-    geom = oracle.Geometry(H, wl.k_budget, wl.v_bits, ((n + 63) // 64) * 64)
-    region = np.zeros(geom.seq_bytes, np.uint8)
-    oracle.quantize_pack(geom, region, K, V, 0, kb, ks, vs)
-    t1 = time.perf_counter()
-    oracle.decode_attention(geom, region, q, n, kb, ks, vs)
-    t2 = time.perf_counter()
-    attn_bytes = n * H * bytes_per_token_head
-    return {"value": round(attn_bytes / (t2 - t1) / 1e9, 5), "unit": "GB/s", "cores": n_threads, "kind": "oracle",
-            "sample": "layer 0, %d KV heads x %d tokens, %d query heads (decode attention, fp64, %.2f s); "
-                      "oracle energy+allocation+quantize of the same sample took %.2f s (%.0f tokens/s)"
-                      % (H, n, wl.n_q_heads, t2 - t1, t1 - t0, n / (t1 - t0)),
-            "quantize_tokens_per_s": round(n / (t1 - t0), 1)}
+    t_prep = t_attn = 0.0
+    layers = 0
+    while layers < wl.n_layers and t_prep + t_attn < budget_s:
+        K = Kall[layers, int(row0[0]):int(row0[0]) + n].cpu().numpy()
+        V = Vall[layers, int(row0[0]):int(row0[0]) + n].cpu().numpy()
+        q = Qall[layers, 0].cpu().numpy()
+        t0 = time.perf_counter()
+        eK = oracle.block_energy(K)
+        eV = oracle.block_energy(V)
+        kb, ks = oracle.allocate(eK, wl.k_budget)
+        _, vs = oracle.allocate(eV, wl.v_bits * 64, oracle.UNIFORM)
+        geom = oracle.Geometry(H, wl.k_budget, wl.v_bits, ((n + 63) // 64) * 64)
+        region = np.zeros(geom.seq_bytes, np.uint8)
+        oracle.quantize_pack(geom, region, K, V, 0, kb, ks, vs)
+        t1 = time.perf_counter()
+        oracle.decode_attention(geom, region, q, n, kb, ks, vs)
+        t2 = time.perf_counter()
+        t_prep += t1 - t0
+        t_attn += t2 - t1
+        layers += 1
+    attn_bytes = layers * n * H * bytes_per_token_head
+    return {"value": round(attn_bytes / t_attn / 1e9, 5), "unit": "GB/s", "cores": n_threads, "kind": "oracle",
+            "sample": "sequence 0 (%d tokens), layers 0..%d, %d KV heads, %d query heads: decode attention "
+                      "(fp64) %.2f s; energy+allocation+quantize of the same layers %.2f s (%.0f tokens/s)"
+                      % (n, layers - 1, H, wl.n_q_heads, t_attn, t_prep, layers * n / t_prep),
+            "quantize_tokens_per_s": round(layers * n / t_prep, 1)}
 
 
 if __name__ == "__main__":
