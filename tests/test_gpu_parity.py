@@ -243,3 +243,67 @@ def test_c2_full_size(kernel):
     say("c2 full %s kernel=%d" % (wl.name, kernel))
     K, V, q = synth.gen_layer(wl, 0, 0)
     run_batch([(K, V, q)], wl.k_budget, wl.v_bits, 32768, kernel=kernel)
+
+
+# ----------------------------------------------------------------- the model-shaped workloads at full size
+
+@pytest.mark.parametrize("layer", [0, 17, 35])
+def test_c3_full_size_sampled_layers(layer):
+    """Qwen2.5-3B-shaped 128K K3V3 (the bench workload): one layer per case at its
+    full 131072-token context, every stage against the oracle, decode in the
+    automatic launch plan the bench uses."""
+    wl = synth.WORKLOADS["c3"]
+    say("c3 full layer %d" % layer)
+    K, V, q = synth.gen_layer(wl, 0, layer)
+    n = K.shape[0]
+    r = run_batch([(K, V, q)], wl.k_budget, wl.v_bits, synth.ceil_to(n + 64, 64))
+    say("c3 layer %d: attention ok, worst rel %.2e" % (layer, check_attention(r["out"], r["ref"])))
+
+
+def test_c4_full_size_layer0():
+    """The same shape at 524288 tokens (one layer): long-context tiling and the split merge."""
+    wl = synth.WORKLOADS["c4"]
+    say("c4 full layer 0")
+    K, V, q = synth.gen_layer(wl, 0, 0)
+    run_batch([(K, V, q)], wl.k_budget, wl.v_bits, synth.ceil_to(K.shape[0] + 64, 64))
+
+
+def test_c5_batch_append_then_attend():
+    """R1-Distill-Qwen-7B-shaped batch (28 q / 4 KV heads, 16 sequences of 4K..32K,
+    K3V2), one layer: bulk prefill, then the decode step's append of one token per
+    sequence, then attention over the n+1 tokens -- bytes and outputs against the
+    oracle's quantization of all n+1 tokens."""
+    wl = synth.WORKLOADS["c5"]
+    layer = 27
+    say("c5 batch layer %d" % layer)
+    seqs, new = [], []
+    for s, n in enumerate(wl.seq_lens):
+        K, V, q = synth.gen_layer(wl, s, layer)
+        kn, vn, qn = synth.gen_new_token(wl, s, layer, n, 0)
+        seqs.append((K, V, q))
+        new.append((kn, vn, qn))
+    cap = synth.ceil_to(max(wl.seq_lens) + 64, 64)
+    r = run_batch(seqs, wl.k_budget, wl.v_bits, cap, check_attn=False)
+    g, cache, off = r["g"], r["cache"], r["off"]
+    S, H, d = len(seqs), wl.n_kv_heads, 128
+    kn = torch.stack([x[0] for x in new]).cuda()
+    vn = torch.stack([x[1] for x in new]).cuda()
+    lens = torch.tensor(wl.seq_lens, dtype=torch.int64, device="cuda")
+    kvq.quantize_pack(g, kn, vn, lens, torch.ones(S, dtype=torch.int32, device="cuda"),
+                      torch.arange(S, dtype=torch.int64, device="cuda"), 1, r["kbits"], r["ksig"], r["vsig"], cache,
+                      off)
+    region = kvq.cache_bytes(g)
+    oc = np.zeros(S * region, np.uint8)
+    for i, ((K, V, _), (k1, v1, _)) in enumerate(zip(seqs, new)):
+        oracle.quantize_pack(r["ogeom"], oc[i * region:(i + 1) * region], torch.cat([K, k1[None]]).numpy(),
+                             torch.cat([V, v1[None]]).numpy(), 0, r["ob"], r["osig"], r["ovsig"])
+    np.testing.assert_array_equal(cache.cpu().numpy(), oc)
+    say("c5: appended bytes ok")
+    q = torch.stack([x[2] for x in new]).cuda().contiguous()
+    seq_len = (lens + 1).to(torch.int32)
+    ws = torch.empty(kvq.decode_workspace_bytes(g, wl.n_q_heads, S, cap) // 4, dtype=torch.float32, device="cuda")
+    out = torch.empty(S, wl.n_q_heads, d, dtype=torch.float32, device="cuda")
+    kvq.packed_decode_attn(g, q, cache, off, seq_len, cap, r["kbits"], r["ksig"], r["vsig"], out, ws)
+    ref = np.stack([oracle.decode_attention(r["ogeom"], oc[i * region:(i + 1) * region], new[i][2].numpy(),
+                                            wl.seq_lens[i] + 1, r["ob"], r["osig"], r["ovsig"]) for i in range(S)])
+    say("c5: attention worst rel %.2e" % check_attention(out.cpu().numpy(), ref))
