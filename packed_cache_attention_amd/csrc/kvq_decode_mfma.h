@@ -89,13 +89,14 @@ struct MfmaSmem {
     // 8-position units (its last unit zero-padded), classes in descending width
     alignas(16) uint16_t qsplit[2][8][8 * kMaxUnits + 8];  // rows 400 B apart: the 16 rows read by one
                                                           // b128 load fall in distinct LDS banks
-    alignas(16) uint16_t qzero[8];                // zero operand for the off-diagonal B lanes
     float vsig[kHeadDim];
     alignas(16) float alpha[kWaves][8];
-    float wm[kWaves][8], wl[kWaves][8];
+    alignas(16) float wm[8][kWaves];  // per head: each wave's reference max (log2 units)
+    alignas(16) float wl[8][kWaves];  // ... and its sum of weights
 };
-// the waves' unnormalised outputs, combined at the end in the (then idle) tile buffers
-typedef float WaveOut[kWaves][8][kHeadDim];
+// the waves' unnormalised outputs [wave][coordinate][head], combined at the end in
+// the (then idle) tile buffers
+typedef float WaveOut[kWaves][kHeadDim][8];
 
 __device__ __forceinline__ float dpp_ror8(float x) {
     // row_ror:8 within each row of 16 lanes: lane l receives lane l ^ 8
@@ -169,26 +170,42 @@ __device__ __forceinline__ uint32_t decode_pair(const LevelTables& t, uint32_t l
     }
 }
 
-// QK over the units of one width class: window of 8 fields -> A operand, q split -> B
+// Both operands of unit j of a width class: the window of 8 fields -> A, the q split
+// of the lane's B column -> B (the column's zero row off the diagonal)
+template <int W, int RD>
+__device__ __forceinline__ void qk_unit(const MfmaSmem& sm, const uint32_t (&rec)[RD + 2], int st,
+                                        const uint16_t* qrow, H8& a, H8& b) {
+    const int d = min(st >> 5, RD > 0 ? RD - 1 : 0);
+    const uint32_t sh = (uint32_t)(st & 31);
+    const uint32_t d0 = rec[d], d1 = rec[d + 1];
+    const uint32_t lo = alignbit(d1, d0, sh);
+    const uint32_t hi = W <= 4 ? 0u : alignbit(rec[d + 2], d1, sh);
+    a.u[0] = decode_pair<W, 0>(sm.tab, lo, hi);
+    a.u[1] = decode_pair<W, 2 * W>(sm.tab, lo, hi);
+    a.u[2] = decode_pair<W, 4 * W>(sm.tab, lo, hi);
+    a.u[3] = decode_pair<W, 6 * W>(sm.tab, lo, hi);
+    const uint4 q4 = *(const uint4*)qrow;
+    b.u[0] = q4.x; b.u[1] = q4.y; b.u[2] = q4.z; b.u[3] = q4.w;
+}
+
+// QK over the units of one width class, two units per step into two accumulators
+// (independent MFMA chains, both units' lookups in flight together).  qb / qs: the
+// lane's q split row and its stride per unit (0 off the diagonal).
 template <int W, int RD>
 __device__ __forceinline__ void qk_class(const MfmaSmem& sm, const uint32_t (&rec)[RD + 2], int start, int units,
-                                         int ubase, const uint16_t* qb_src, bool bdiag, floatx16& acc) {
-    for (int j = 0; j < units; ++j) {
-        const int st = start + j * 8 * W;
-        const int d = min(st >> 5, RD > 0 ? RD - 1 : 0);
-        const uint32_t sh = (uint32_t)(st & 31);
-        const uint32_t d0 = rec[d], d1 = rec[d + 1];
-        const uint32_t lo = alignbit(d1, d0, sh);
-        const uint32_t hi = W <= 4 ? 0u : alignbit(rec[d + 2], d1, sh);
-        H8 a;
-        a.u[0] = decode_pair<W, 0>(sm.tab, lo, hi);
-        a.u[1] = decode_pair<W, 2 * W>(sm.tab, lo, hi);
-        a.u[2] = decode_pair<W, 4 * W>(sm.tab, lo, hi);
-        a.u[3] = decode_pair<W, 6 * W>(sm.tab, lo, hi);
-        H8 b;
-        const uint4 q4 = *(const uint4*)(bdiag ? qb_src + 8 * (ubase + j) : sm.qzero);
-        b.u[0] = q4.x; b.u[1] = q4.y; b.u[2] = q4.z; b.u[3] = q4.w;
-        acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a.h, b.h, acc, 0, 0, 0);
+                                         int ubase, const uint16_t* qb, int qs, floatx16& acc0, floatx16& acc1) {
+    int j = 0;
+    for (; j + 1 < units; j += 2) {
+        H8 a0, b0, a1, b1;
+        qk_unit<W, RD>(sm, rec, start + j * 8 * W, qb + qs * (ubase + j), a0, b0);
+        qk_unit<W, RD>(sm, rec, start + (j + 1) * 8 * W, qb + qs * (ubase + j + 1), a1, b1);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0.h, b0.h, acc0, 0, 0, 0);
+        acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1.h, b1.h, acc1, 0, 0, 0);
+    }
+    if (j < units) {
+        H8 a0, b0;
+        qk_unit<W, RD>(sm, rec, start + j * 8 * W, qb + qs * (ubase + j), a0, b0);
+        acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0.h, b0.h, acc0, 0, 0, 0);
     }
 }
 
@@ -263,32 +280,30 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
     // ---- every global load of the prologue goes out before anything waits on one
+    // (no load sits under a branch, so none is waited for on its own)
+    const int64_t len_raw = seq_len[s];
+    const int64_t seq_off = seq_byte_off[s];
     const int my_w = k_bits[kvh * kMaxBlocks + lane];
     const float my_ksig = k_sigma[kvh * kMaxBlocks + lane];
-    float my_vsig = 0.f;
-    if (tid < kHeadDim) {
-        const int i = pairing == KVQ_PAIR_HALF ? (tid & (kMaxBlocks - 1)) : (tid >> 1);
-        my_vsig = v_sigma[kvh * kMaxBlocks + i];
-    }
+    const int vs_blk = pairing == KVQ_PAIR_HALF ? (tid & (kMaxBlocks - 1)) : ((tid >> 1) & (kMaxBlocks - 1));
+    const float my_vsig = v_sigma[kvh * kMaxBlocks + vs_blk];  // used by threads < 128
     const int qp = pairing == KVQ_PAIR_HALF ? lane : 2 * lane;
     const int qq = pairing == KVQ_PAIR_HALF ? lane + kMaxBlocks : 2 * lane + 1;
-    uint32_t qv[2][2] = {{0u, 0u}, {0u, 0u}};  // heads wave and wave + 4: coordinates qp, qq
+    uint32_t qv[2][2];  // heads wave and wave + 4 (clamped; unused past the group): coordinates qp, qq
 #pragma unroll
     for (int e = 0; e < 2; ++e) {
-        const int hh = wave + kWaves * e;
-        if (hh < g) {
-            const uint16_t* qrow = q + ((int64_t)s * n_q + kvh * g + hh) * kHeadDim;
-            qv[e][0] = qrow[qp];
-            qv[e][1] = qrow[qq];
-        }
+        const int hh = min(wave + kWaves * e, g - 1);
+        const uint16_t* qrow = q + ((int64_t)s * n_q + kvh * g + hh) * kHeadDim;
+        qv[e][0] = qrow[qp];
+        qv[e][1] = qrow[qq];
     }
     constexpr int kTabChunks = (int)(sizeof(LevelTables) / 16);
-    static_assert(kTabChunks <= 512, "the level tables are staged in two 16-byte pieces per thread");
+    static_assert(kTabChunks > 256 && kTabChunks <= 512, "the level tables are staged in two 16-byte pieces per thread");
     const uint4* tsrc = (const uint4*)&g_level_tables;
     const uint4 tab0 = tsrc[tid];
-    const uint4 tab1 = tid + 256 < kTabChunks ? tsrc[tid + 256] : uint4{0u, 0u, 0u, 0u};
+    const uint4 tab1 = tsrc[min(tid + 256, kTabChunks - 1)];
 
-    const int64_t len = min(max((int64_t)seq_len[s], (int64_t)0), max_len);
+    const int64_t len = min(max(len_raw, (int64_t)0), max_len);
     const int64_t n_tiles_seq = (len + kTile - 1) / kTile;
     const int64_t t0 = (int64_t)split * tiles_per_split;
     const int64_t t1 = min(t0 + tiles_per_split, n_tiles_seq);
@@ -302,7 +317,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     const int row = lane & 15;       // PV row = (hi|lo) * 8 + head
     const bool lo_row = row >= 8;
 
-    const uint8_t* head_base = cache + seq_byte_off[s] + (int64_t)kvh * (capacity / kTile) * TB;
+    const uint8_t* head_base = cache + seq_off + (int64_t)kvh * (capacity / kTile) * TB;
     uint8_t* wbuf = bufs + wave * WB;
     const uint32_t wbuf_lds = (uint32_t)(uintptr_t)(lds_u8*)wbuf;
 
@@ -337,7 +352,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     {
         uint4* qz = (uint4*)&sm.qsplit[0][0][0];
         for (int i = tid; i < (int)(sizeof(sm.qsplit) / 16); i += 256) qz[i] = uint4{0, 0, 0, 0};
-        if (tid == 0) *(uint4*)sm.qzero = uint4{0, 0, 0, 0};
         if (tid < kHeadDim) sm.vsig[tid] = my_vsig;
     }
     // width classes (descending): every wave ranks the blocks; a block's two fields sit
@@ -376,7 +390,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         }
     }
     __syncthreads();
-    const uint16_t* qb_src = &sm.qsplit[(col >> 3) & 1][col & 7][0];
+    // B operand rows: the lane's column (hi|lo, head) on the diagonal, else a row that
+    // stays zero (the last unit of hi row 0: at most 22 units are ever filled)
+    const uint16_t* qb = bdiag ? &sm.qsplit[(col >> 3) & 1][col & 7][0] : &sm.qsplit[0][0][8 * (kMaxUnits - 1)];
+    const int qs = bdiag ? 8 : 0;
 
     floatx4 o[8];
 #pragma unroll
@@ -404,15 +421,18 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         if (more) dma_k(tau + kWaves, kb ^ 1);
         kb ^= 1;
         // ---- QK: this lane's token, 8 fields of one width class per instruction
-        floatx16 acc = {};
-        qk_class<8, RD>(sm, rec, cstart[8], cunits[8], cubase[8], qb_src, bdiag, acc);
-        qk_class<7, RD>(sm, rec, cstart[7], cunits[7], cubase[7], qb_src, bdiag, acc);
-        qk_class<6, RD>(sm, rec, cstart[6], cunits[6], cubase[6], qb_src, bdiag, acc);
-        qk_class<5, RD>(sm, rec, cstart[5], cunits[5], cubase[5], qb_src, bdiag, acc);
-        qk_class<4, RD>(sm, rec, cstart[4], cunits[4], cubase[4], qb_src, bdiag, acc);
-        qk_class<3, RD>(sm, rec, cstart[3], cunits[3], cubase[3], qb_src, bdiag, acc);
-        qk_class<2, RD>(sm, rec, cstart[2], cunits[2], cubase[2], qb_src, bdiag, acc);
-        qk_class<1, RD>(sm, rec, cstart[1], cunits[1], cubase[1], qb_src, bdiag, acc);
+        floatx16 acc0 = {}, acc1 = {};
+        qk_class<8, RD>(sm, rec, cstart[8], cunits[8], cubase[8], qb, qs, acc0, acc1);
+        qk_class<7, RD>(sm, rec, cstart[7], cunits[7], cubase[7], qb, qs, acc0, acc1);
+        qk_class<6, RD>(sm, rec, cstart[6], cunits[6], cubase[6], qb, qs, acc0, acc1);
+        qk_class<5, RD>(sm, rec, cstart[5], cunits[5], cubase[5], qb, qs, acc0, acc1);
+        qk_class<4, RD>(sm, rec, cstart[4], cunits[4], cubase[4], qb, qs, acc0, acc1);
+        qk_class<3, RD>(sm, rec, cstart[3], cunits[3], cubase[3], qb, qs, acc0, acc1);
+        qk_class<2, RD>(sm, rec, cstart[2], cunits[2], cubase[2], qb, qs, acc0, acc1);
+        qk_class<1, RD>(sm, rec, cstart[1], cunits[1], cubase[1], qb, qs, acc0, acc1);
+        floatx16 acc;
+#pragma unroll
+        for (int i = 0; i < 16; ++i) acc[i] = acc0[i] + acc1[i];
         // ---- V section landed (scales, runs)
         if (more) __builtin_amdgcn_s_waitcnt(wait_vm(KI));
         else __builtin_amdgcn_s_waitcnt(wait_vm(0));
@@ -504,33 +524,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         for (int j = 0; j < 4; ++j) o[ct][j] = xor32_sum(o[ct][j]);
     WaveOut& wo = *(WaveOut*)bufs;
     __syncthreads();  // every wave is done with its tile buffers
-    if (lane < 8) { sm.wm[wave][lane] = mref; sm.wl[wave][lane] = lsum; }
+    if (lane < 8) { sm.wm[lane][wave] = mref; sm.wl[lane][wave] = lsum; }
     if (lane < 32) {
+        // lane l holds rows 4*(l/16) .. +3 (heads) of coordinates 16*ct + l%16
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct)
-#pragma unroll
-            for (int j = 0; j < 4; ++j) wo[wave][4 * (lane >> 4) + j][16 * ct + (lane & 15)] = o[ct][j];
+            *(float4*)&wo[wave][16 * ct + (lane & 15)][4 * (lane >> 4)] = float4{o[ct][0], o[ct][1], o[ct][2], o[ct][3]};
     }
     __syncthreads();
-    // merge the four waves and write this chunk's partials
+    // merge the four waves: thread (half, c) writes coordinate c of heads 4*half .. 4*half+3
     const int D2 = kHeadDim + 2;
-    for (int idx = tid; idx < g * kHeadDim; idx += 256) {
-        const int hh = idx >> 7, c = idx & 127;
-        float M = -INFINITY;
+    const int c = tid & (kHeadDim - 1), h0 = 4 * (tid >> 7);
+    if (h0 < g) {
+        float4 ow[kWaves];
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) M = fmaxf(M, sm.wm[w][hh]);
-        float l = 0.f, acc = 0.f;
-        if (M != -INFINITY) {
+        for (int w = 0; w < kWaves; ++w) ow[w] = *(const float4*)&wo[w][c][h0];
+        const float vs = sm.vsig[c];
 #pragma unroll
-            for (int w = 0; w < kWaves; ++w) {
-                const float a = exp2f(sm.wm[w][hh] - M);
-                l += a * sm.wl[w][hh];
-                acc += a * wo[w][hh][c];
+        for (int j = 0; j < 4; ++j) {
+            const int hh = h0 + j;
+            if (hh >= g) break;
+            const float4 mw = *(const float4*)sm.wm[hh];
+            const float4 lw = *(const float4*)sm.wl[hh];
+            const float M = fmaxf(fmaxf(mw.x, mw.y), fmaxf(mw.z, mw.w));
+            float l = 0.f, acc = 0.f;
+            if (M != -INFINITY) {
+                const float f0 = __builtin_amdgcn_exp2f(mw.x - M), f1 = __builtin_amdgcn_exp2f(mw.y - M);
+                const float f2 = __builtin_amdgcn_exp2f(mw.z - M), f3 = __builtin_amdgcn_exp2f(mw.w - M);
+                l = f0 * lw.x + f1 * lw.y + f2 * lw.z + f3 * lw.w;
+                const float o0 = j == 0 ? ow[0].x : j == 1 ? ow[0].y : j == 2 ? ow[0].z : ow[0].w;
+                const float o1 = j == 0 ? ow[1].x : j == 1 ? ow[1].y : j == 2 ? ow[1].z : ow[1].w;
+                const float o2 = j == 0 ? ow[2].x : j == 1 ? ow[2].y : j == 2 ? ow[2].z : ow[2].w;
+                const float o3 = j == 0 ? ow[3].x : j == 1 ? ow[3].y : j == 2 ? ow[3].z : ow[3].w;
+                acc = f0 * o0 + f1 * o1 + f2 * o2 + f3 * o3;
             }
+            float* part = ws + (((int64_t)s * n_q + kvh * g + hh) * n_split + split) * D2;
+            part[2 + c] = acc * vs;
+            if (c == 0) { part[0] = M; part[1] = l; }
         }
-        float* part = ws + (((int64_t)s * n_q + kvh * g + hh) * n_split + split) * D2;
-        part[2 + c] = acc * sm.vsig[c];
-        if (c == 0) { part[0] = M; part[1] = l; }
     }
 }
 
