@@ -8,10 +8,12 @@ synthetic seeded inputs (packed_cache_attention_amd.synth).
 Phases, all on the GPU through the C ABI (libkvq.so):
   prefill  (untimed setup, measured separately): per layer, exact block energies
            of K and V, greedy K / uniform V allocation, bulk quantize+pack.
-  step     (the timed unit): per layer, append the new token's K/V
-           (kvq_quantize_pack), split-K decode attention over the packed cache
-           (kvq_decode_partials) and the log-sum-exp merge (kvq_merge_partials).
-           The 36-layer step is captured once in a HIP graph and replayed.
+  step     (the timed unit): per layer, append the new token's K/V and run the
+           split-K decode attention over the packed cache in one launch
+           (kvq_decode_step_partials: the append happens inside the attention
+           kernel), then the log-sum-exp merge (kvq_merge_partials).  --unfused
+           appends with kvq_quantize_pack as a launch of its own instead.  The
+           36-layer step is captured once in a HIP graph and replayed.
 
 value = algorithmic bytes of one step (packed cache read by attention + queries
 + outputs + appended token) / measured step time, in GB/s.  The dominant kernel's
@@ -105,6 +107,8 @@ def main():
     ap.add_argument("--copy-probe-mib", type=int, default=0,
                     help="also run a plain device copy of this many MiB (counter calibration)")
     ap.add_argument("--seed", type=int, default=0)
+    ap.add_argument("--unfused", action="store_true",
+                    help="append with kvq_quantize_pack as a launch of its own instead of inside the attention kernel")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
     args = ap.parse_args()
     if args.traffic_from:
@@ -238,11 +242,15 @@ def main():
 
     def step(ev=None):
         for l in range(L):
-            kvq.quantize_pack(g, Knew[l], Vnew[l], cur, ones32, src_new, 1, kbits[l], ksig[l], vsig[l], cache[l], off)
-            if ev: ev[0][l].record()
-            kvq.decode_partials(g, Qall[l], cache[l], off, seq_len, max_len, kbits[l], ksig[l], vsig[l],
-                                partials[l], kernel=kern, tiles_per_split=args.tiles_per_split)
-            if ev: ev[1][l].record()
+            if args.unfused:
+                kvq.quantize_pack(g, Knew[l], Vnew[l], cur, ones32, src_new, 1, kbits[l], ksig[l], vsig[l],
+                                  cache[l], off)
+                kvq.decode_partials(g, Qall[l], cache[l], off, seq_len, max_len, kbits[l], ksig[l], vsig[l],
+                                    partials[l], kernel=kern, tiles_per_split=args.tiles_per_split)
+            else:  # append inside the attention kernel
+                kvq.decode_step_partials(g, Qall[l], Knew[l], Vnew[l], cache[l], off, seq_len, max_len, kbits[l],
+                                         ksig[l], vsig[l], partials[l], kernel=kern,
+                                         tiles_per_split=args.tiles_per_split)
             kvq.merge_partials(S, Hq, n_split, partials[l], out[l])
         cur.add_(1)
         seq_len.add_(1)
@@ -295,7 +303,8 @@ def main():
 
     # ------------------------------------------------------------ dominant kernel: back-to-back launches
     # One event pair brackets the 36 layers' split-phase launches, enqueued while a
-    # spin holds the GPU, so the span is the kernels' own time.
+    # spin holds the GPU, so the span is the kernels' own time.  Fused, these are the
+    # next step's launches (its appends write the same bytes on every repetition).
     ksteps = min(args.steps, 10)
     durs = []
     kd0 = torch.cuda.Event(enable_timing=True)
@@ -304,14 +313,21 @@ def main():
         torch.cuda._sleep(20_000_000)
         kd0.record()
         for l in range(L):
-            kvq.decode_partials(g, Qall[l], cache[l], off, seq_len, max_len, kbits[l], ksig[l], vsig[l],
-                                partials[l], kernel=kern, tiles_per_split=args.tiles_per_split)
+            if args.unfused:
+                kvq.decode_partials(g, Qall[l], cache[l], off, seq_len, max_len, kbits[l], ksig[l], vsig[l],
+                                    partials[l], kernel=kern, tiles_per_split=args.tiles_per_split)
+            else:
+                kvq.decode_step_partials(g, Qall[l], Knew[l], Vnew[l], cache[l], off, seq_len, max_len, kbits[l],
+                                         ksig[l], vsig[l], partials[l], kernel=kern,
+                                         tiles_per_split=args.tiles_per_split)
         kd1.record()
         torch.cuda.synchronize()
         durs.append(kd0.elapsed_time(kd1) / 1e3 / L)
     kdur = float(np.mean(durs))
     ln = seq_len.cpu().numpy().astype(np.int64)
     launch_bytes = float(ln.sum()) * H * bytes_per_token_head
+    if not args.unfused:  # the appended token: fp16 K and V read, packed bytes written
+        launch_bytes += S * H * (2 * d * 2 + bytes_per_token_head)
     achieved = launch_bytes / kdur / 1e9
     kernel_name = "decode_mfma_kernel" if plan["kernel"] == kvq.DECODE_MFMA else "decode_generic_kernel"
     log("%s: %.2f us/launch avg over %d launches, %.1f GB/s algorithmic (%.1f%% of peak)"
@@ -358,7 +374,7 @@ def main():
         "config": {"workload": wl.name, "layers": L, "q_heads": Hq, "kv_heads": H, "head_dim": d,
                    "batch": S, "context": lens if S > 1 else lens[0], "k_budget": wl.k_budget,
                    "v_bits": wl.v_bits, "capacity": cap, "graph": graph is not None,
-                   "split_chunks": n_split, "kernel": kernel_name},
+                   "split_chunks": n_split, "kernel": kernel_name, "append": "separate launch" if args.unfused else "inside the attention kernel"},
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "step_bytes": int(step_bytes),
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),

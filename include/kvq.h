@@ -199,6 +199,29 @@ int32_t kvq_decode_partials(const kvq_geom *g, int32_t n_q_heads, const void *q,
                             const uint8_t *k_bits, const float *k_sigma, const float *v_sigma, float softmax_scale,
                             float *partials, size_t partials_bytes, int32_t kernel, int32_t tiles_per_split,
                             void *stream);
+/* The decode step (the batch workload's step: each sequence appends its new token,
+ * then attends all its tokens including it).  For every sequence s with
+ * seq_len[s] >= 1, the rows k_new / v_new of s (element (s, h, c) at
+ * base[s*new_stride_seq + h*new_stride_head + c], binary16) are quantized and packed
+ * into slot seq_len[s] - 1 exactly as kvq_quantize_pack would (that slot's bits must
+ * be zero), and the attention over slots [0, seq_len[s]) is computed as by
+ * kvq_decode_partials / kvq_packed_decode_attn_ex.  With the matrix-core kernel the
+ * append happens inside the attention kernel (the wave that owns the last tile);
+ * otherwise a one-wave append kernel runs first on the same stream.  The results
+ * (cache bytes, partials, out) are those of the two separate calls.
+ * Requirements: those of both calls; k_new, v_new 4-byte aligned, strides even. */
+int32_t kvq_decode_step_partials(const kvq_geom *g, int32_t n_q_heads, const void *q, const void *k_new,
+                                 const void *v_new, int64_t new_stride_seq, int64_t new_stride_head,
+                                 uint8_t *cache, const int64_t *seq_byte_off, const int32_t *seq_len,
+                                 int32_t n_seq, int64_t max_len, const uint8_t *k_bits, const float *k_sigma,
+                                 const float *v_sigma, float softmax_scale, float *partials,
+                                 size_t partials_bytes, int32_t kernel, int32_t tiles_per_split, void *stream);
+int32_t kvq_decode_step(const kvq_geom *g, int32_t n_q_heads, const void *q, const void *k_new, const void *v_new,
+                        int64_t new_stride_seq, int64_t new_stride_head, uint8_t *cache,
+                        const int64_t *seq_byte_off, const int32_t *seq_len, int32_t n_seq, int64_t max_len,
+                        const uint8_t *k_bits, const float *k_sigma, const float *v_sigma, float softmax_scale,
+                        float *out, void *workspace, size_t workspace_bytes, int32_t kernel,
+                        int32_t tiles_per_split, void *stream);
 /* Log-sum-exp merge of n_split partials per (sequence, head) in the format above:
  * out[s][h][c] = sum_k 2^(m_k - M) o_k,c / sum_k 2^(m_k - M) l_k, M = max_k m_k; rows
  * with no tokens give 0.  out: device float [n_seq][n_q_heads][128]. */

@@ -235,9 +235,9 @@ int32_t kvq_decode_partials(const kvq_geom* g, int32_t n_q_heads, const void* q,
     int32_t st = check_decode(g, n_q_heads, q, cache, seq_byte_off, seq_len, n_seq, max_len, k_bits, k_sigma, v_sigma,
                               partials, partials_bytes, kernel, tiles_per_split, &plan, fn);
     if (st || n_seq == 0) return st;
-    return hip_status(launch_decode_partials(*g, plan, n_q_heads, (const uint16_t*)q, cache, seq_byte_off, seq_len,
-                                             n_seq, max_len, k_bits, k_sigma, v_sigma, softmax_scale, partials,
-                                             (hipStream_t)stream),
+    return hip_status(launch_decode_partials(*g, plan, n_q_heads, (const uint16_t*)q, (uint8_t*)cache, seq_byte_off,
+                                             seq_len, n_seq, max_len, k_bits, k_sigma, v_sigma, softmax_scale,
+                                             partials, (hipStream_t)stream),
                       fn);
 }
 
@@ -264,9 +264,9 @@ int32_t kvq_packed_decode_attn_ex(const kvq_geom* g, int32_t n_q_heads, const vo
     if (st || n_seq == 0) return st;
     if (!out) return fail(KVQ_ERR_ARG, fn, "null pointer");
     if (!aligned(out, 16)) return fail(KVQ_ERR_ALIGN, fn, "alignment");
-    hipError_t e = launch_decode_partials(*g, plan, n_q_heads, (const uint16_t*)q, cache, seq_byte_off, seq_len,
-                                          n_seq, max_len, k_bits, k_sigma, v_sigma, softmax_scale, (float*)workspace,
-                                          (hipStream_t)stream);
+    hipError_t e = launch_decode_partials(*g, plan, n_q_heads, (const uint16_t*)q, (uint8_t*)cache, seq_byte_off,
+                                          seq_len, n_seq, max_len, k_bits, k_sigma, v_sigma, softmax_scale,
+                                          (float*)workspace, (hipStream_t)stream);
     if (e != hipSuccess) return hip_status(e, fn);
     return hip_status(launch_merge(n_seq * n_q_heads, plan.n_split, (const float*)workspace, out, (hipStream_t)stream),
                       fn);
@@ -279,6 +279,59 @@ int32_t kvq_packed_decode_attn(const kvq_geom* g, int32_t n_q_heads, const void*
     return kvq_packed_decode_attn_ex(g, n_q_heads, q, cache, seq_byte_off, seq_len, n_seq, max_len, k_bits, k_sigma,
                                      v_sigma, softmax_scale, out, workspace, workspace_bytes, KVQ_DECODE_AUTO, 0,
                                      stream);
+}
+
+namespace {
+int32_t check_step_rows(const void* k_new, const void* v_new, int64_t stride_seq, int64_t stride_head, const char* fn) {
+    if (!k_new || !v_new) return fail(KVQ_ERR_ARG, fn, "null new-token pointer");
+    if (stride_seq < 0 || stride_head < 0) return fail(KVQ_ERR_ARG, fn, "negative stride");
+    if (!aligned(k_new, 4) || !aligned(v_new, 4) || (stride_seq & 1) || (stride_head & 1))
+        return fail(KVQ_ERR_ALIGN, fn, "new-token alignment");
+    return KVQ_OK;
+}
+}  // namespace
+
+int32_t kvq_decode_step_partials(const kvq_geom* g, int32_t n_q_heads, const void* q, const void* k_new,
+                                 const void* v_new, int64_t new_stride_seq, int64_t new_stride_head, uint8_t* cache,
+                                 const int64_t* seq_byte_off, const int32_t* seq_len, int32_t n_seq, int64_t max_len,
+                                 const uint8_t* k_bits, const float* k_sigma, const float* v_sigma,
+                                 float softmax_scale, float* partials, size_t partials_bytes, int32_t kernel,
+                                 int32_t tiles_per_split, void* stream) {
+    const char* fn = "kvq_decode_step_partials";
+    DecodePlan plan;
+    int32_t st = check_decode(g, n_q_heads, q, cache, seq_byte_off, seq_len, n_seq, max_len, k_bits, k_sigma, v_sigma,
+                              partials, partials_bytes, kernel, tiles_per_split, &plan, fn);
+    if (st || n_seq == 0) return st;
+    st = check_step_rows(k_new, v_new, new_stride_seq, new_stride_head, fn);
+    if (st) return st;
+    const AppendArgs app{(const uint16_t*)k_new, (const uint16_t*)v_new, new_stride_seq, new_stride_head};
+    return hip_status(launch_decode_partials(*g, plan, n_q_heads, (const uint16_t*)q, cache, seq_byte_off, seq_len,
+                                             n_seq, max_len, k_bits, k_sigma, v_sigma, softmax_scale, partials,
+                                             (hipStream_t)stream, app),
+                      fn);
+}
+
+int32_t kvq_decode_step(const kvq_geom* g, int32_t n_q_heads, const void* q, const void* k_new, const void* v_new,
+                        int64_t new_stride_seq, int64_t new_stride_head, uint8_t* cache, const int64_t* seq_byte_off,
+                        const int32_t* seq_len, int32_t n_seq, int64_t max_len, const uint8_t* k_bits,
+                        const float* k_sigma, const float* v_sigma, float softmax_scale, float* out, void* workspace,
+                        size_t workspace_bytes, int32_t kernel, int32_t tiles_per_split, void* stream) {
+    const char* fn = "kvq_decode_step";
+    DecodePlan plan;
+    int32_t st = check_decode(g, n_q_heads, q, cache, seq_byte_off, seq_len, n_seq, max_len, k_bits, k_sigma, v_sigma,
+                              workspace, workspace_bytes, kernel, tiles_per_split, &plan, fn);
+    if (st || n_seq == 0) return st;
+    st = check_step_rows(k_new, v_new, new_stride_seq, new_stride_head, fn);
+    if (st) return st;
+    if (!out) return fail(KVQ_ERR_ARG, fn, "null pointer");
+    if (!aligned(out, 16)) return fail(KVQ_ERR_ALIGN, fn, "alignment");
+    const AppendArgs app{(const uint16_t*)k_new, (const uint16_t*)v_new, new_stride_seq, new_stride_head};
+    hipError_t e = launch_decode_partials(*g, plan, n_q_heads, (const uint16_t*)q, cache, seq_byte_off, seq_len,
+                                          n_seq, max_len, k_bits, k_sigma, v_sigma, softmax_scale, (float*)workspace,
+                                          (hipStream_t)stream, app);
+    if (e != hipSuccess) return hip_status(e, fn);
+    return hip_status(launch_merge(n_seq * n_q_heads, plan.n_split, (const float*)workspace, out, (hipStream_t)stream),
+                      fn);
 }
 
 }  // extern "C"

@@ -229,9 +229,9 @@ __global__ __launch_bounds__(kMergeCols * kMergeGroups) void merge_kernel(const 
 }
 
 hipError_t launch_decode_mfma(const kvq_geom& g, const DecodePlan& plan, int n_q_heads, const uint16_t* q,
-                              const uint8_t* cache, const int64_t* seq_byte_off, const int32_t* seq_len, int n_seq,
+                              uint8_t* cache, const int64_t* seq_byte_off, const int32_t* seq_len, int n_seq,
                               int64_t max_len, const uint8_t* k_bits, const float* k_sigma, const float* v_sigma,
-                              float scale_log2, float* workspace, hipStream_t st);
+                              float scale_log2, float* workspace, hipStream_t st, const AppendArgs& app);
 
 int mfma_blocks_per_cu(const kvq_geom& g);
 
@@ -286,14 +286,22 @@ int plan_decode(const kvq_geom& g, int n_q_heads, int n_seq, int64_t max_len, in
 }
 
 hipError_t launch_decode_partials(const kvq_geom& g, const DecodePlan& plan, int n_q_heads, const uint16_t* q,
-                                  const uint8_t* cache, const int64_t* seq_byte_off, const int32_t* seq_len,
+                                  uint8_t* cache, const int64_t* seq_byte_off, const int32_t* seq_len,
                                   int n_seq, int64_t max_len, const uint8_t* k_bits, const float* k_sigma,
-                                  const float* v_sigma, float softmax_scale, float* partials, hipStream_t st) {
+                                  const float* v_sigma, float softmax_scale, float* partials, hipStream_t st,
+                                  const AppendArgs& app) {
     const float scale_log2 = softmax_scale * kLog2e;
     const int grp = n_q_heads / g.n_kv_heads;
+    // the matrix-core kernel appends inside (the tail tile's wave); the generic one
+    // gets the append as a kernel of its own first
     if (plan.kernel == KVQ_DECODE_MFMA)
         return launch_decode_mfma(g, plan, n_q_heads, q, cache, seq_byte_off, seq_len, n_seq, max_len, k_bits,
-                                  k_sigma, v_sigma, scale_log2, partials, st);
+                                  k_sigma, v_sigma, scale_log2, partials, st, app);
+    if (app.k) {
+        const hipError_t e = launch_append_step(g, n_seq, app, seq_len, k_bits, k_sigma, v_sigma, cache,
+                                                seq_byte_off, st);
+        if (e != hipSuccess) return e;
+    }
     dim3 grid(plan.n_split, g.n_kv_heads, n_seq);
     hipLaunchKernelGGL(decode_generic_kernel, grid, dim3(256), 0, st, q, cache, seq_byte_off, seq_len, max_len,
                        g.capacity_tokens, k_bits, k_sigma, v_sigma, scale_log2, n_q_heads, grp, g.rope_pairing,

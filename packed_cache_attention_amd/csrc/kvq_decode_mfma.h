@@ -261,10 +261,10 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
 
 template <int V, int RD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma_kernel(
-    const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, const int64_t* __restrict__ seq_byte_off,
+    const uint16_t* __restrict__ q, uint8_t* __restrict__ cache, const int64_t* __restrict__ seq_byte_off,
     const int32_t* __restrict__ seq_len, int64_t max_len, int64_t capacity, const uint8_t* __restrict__ k_bits,
     const float* __restrict__ k_sigma, const float* __restrict__ v_sigma, float scale_log2, int n_q, int g,
-    int pairing, int k_budget, int tiles_per_split, int n_split, float* __restrict__ ws) {
+    int pairing, int k_budget, int tiles_per_split, int n_split, float* __restrict__ ws, AppendArgs app) {
     constexpr int NW = (16 * V + 31) / 32;       // words of one lane's V piece
     constexpr int SK = 4 * RD;                   // K record bytes
     constexpr int KB = kTile * SK;               // K section of a tile
@@ -303,10 +303,27 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     const uint4 tab0 = tsrc[tid];
     const uint4 tab1 = tsrc[min(tid + 256, kTabChunks - 1)];
 
+    // the step's new token (coordinates 2l, 2l+1 for its norm; block l's p, q for its codes)
+    uint32_t nk_pair = 0, nv_pair = 0, nk_p = 0, nk_q = 0, nv_p = 0, nv_q = 0;
+    float my_vsig_blk = 0.f;
+    if (app.k != nullptr) {
+        const uint16_t* kr = app.k + (int64_t)s * app.stride_seq + (int64_t)kvh * app.stride_head;
+        const uint16_t* vr = app.v + (int64_t)s * app.stride_seq + (int64_t)kvh * app.stride_head;
+        nk_pair = *(const uint32_t*)(kr + 2 * lane);
+        nv_pair = *(const uint32_t*)(vr + 2 * lane);
+        nk_p = kr[qp]; nk_q = kr[qq];
+        nv_p = vr[qp]; nv_q = vr[qq];
+        my_vsig_blk = v_sigma[kvh * kMaxBlocks + lane];
+    }
+
     const int64_t len = min(max(len_raw, (int64_t)0), max_len);
     const int64_t n_tiles_seq = (len + kTile - 1) / kTile;
     const int64_t t0 = (int64_t)split * tiles_per_split;
     const int64_t t1 = min(t0 + tiles_per_split, n_tiles_seq);
+    // the wave whose tiles include slot len-1 appends the new token there first
+    const int64_t tail_tau = (len - 1) / kTile;
+    const bool appender = app.k != nullptr && len > 0 && tail_tau >= t0 && tail_tau < t1 &&
+                          (int)((tail_tau - t0) % kWaves) == wave;
 
     // lane roles
     const int col = lane & 31;
@@ -341,7 +358,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         }
     };
     int64_t tau = t0 + wave;
-    if (tau < t1) {
+    if (tau < t1 && !appender) {
         dma_k(tau, 0);
         dma_v(tau);
     }
@@ -356,7 +373,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     }
     // width classes (descending): every wave ranks the blocks; a block's two fields sit
     // at its rank within its class.  Wave w fills the q split of heads w, w+4.
-    int my_pos = 0;
+    int my_pos = 0, my_koff = 0;  // q split position and K record bit offset of block `lane`
     int cstart[9], cunits[9], cubase[9];
     {
         const unsigned long long below = (1ull << lane) - 1ull;
@@ -368,7 +385,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
             cstart[w] = start;
             cunits[w] = units;
             cubase[w] = ubase;
-            if (my_w == w) my_pos = 8 * ubase + 2 * __popcll(mk & below);
+            if (my_w == w) {
+                my_pos = 8 * ubase + 2 * __popcll(mk & below);
+                my_koff = start + 2 * w * __popcll(mk & below);
+            }
             start += nfw * w;
             ubase += units;
         }
@@ -395,6 +415,72 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     const uint16_t* qb = bdiag ? &sm.qsplit[(col >> 3) & 1][col & 7][0] : &sm.qsplit[0][0][8 * (kMaxUnits - 1)];
     const int qs = bdiag ? 8 : 0;
 
+    // ---- the step's append (one wave): quantize and pack the new token into slot
+    // len-1, exactly as the quantize path does, then fetch this wave's first tile.
+    // The tail tile's copy in LDS is patched with the same bytes when it arrives, so
+    // it does not matter whether the tile fetch sees the stores.
+    const int tail_p = (int)((len - 1) & (kTile - 1));
+    uint32_t ap_rec = 0, ap_vcp = 0, ap_vcq = 0;
+    float ap_sk = 0.f, ap_sv = 0.f;
+    if (appender) {
+        // staging: the wave's own (still idle) buffers, or the spare end of the shared
+        // buffer when they are too small
+        constexpr int kStage = 2048 + 4 * 16;  // 510 thresholds, then one record (<= 16 words)
+        static_assert(WB >= kStage || BUF - kWaves * WB >= kStage, "no room to stage the append");
+        uint8_t* stage = WB >= kStage ? wbuf : bufs + kWaves * WB;
+        float* s_thr = (float*)stage;
+        uint32_t* s_rec = (uint32_t*)(stage + 2048);
+#pragma unroll
+        for (int k = 0; k < 8; ++k)
+            if (64 * k + lane < 510) s_thr[64 * k + lane] = c_thresholds[64 * k + lane];
+        if (lane < 16) s_rec[lane] = 0;
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_wave_barrier();
+        ap_sk = token_norm(nk_pair);
+        ap_sv = token_norm(nv_pair);
+        const uint32_t kcp = encode(s_thr, nk_p, my_w, my_ksig, ap_sk);
+        const uint32_t kcq = encode(s_thr, nk_q, my_w, my_ksig, ap_sk);
+        ap_vcp = encode(s_thr, nv_p, V, my_vsig_blk, ap_sv);
+        ap_vcq = encode(s_thr, nv_q, V, my_vsig_blk, ap_sv);
+        if (my_w > 0) {
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+                const uint32_t code = f ? kcq : kcp;
+                const int off = my_koff + f * my_w, k = off >> 5, sh = off & 31;
+                atomicOr(&s_rec[k], code << sh);
+                if (sh + my_w > 32) atomicOr(&s_rec[k + 1], code >> (32 - sh));
+            }
+        }
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_wave_barrier();
+        ap_rec = lane < RD ? s_rec[lane] : 0u;
+        uint8_t* tile = (uint8_t*)head_base + tail_tau * TB;
+        if (lane < RD) ((uint32_t*)(tile + tail_p * SK))[lane] = ap_rec;
+        uint32_t* vrun = (uint32_t*)(tile + KB);
+        const int vb = tail_p * V, vk = vb >> 5, vsh = vb & 31;
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            const uint32_t code = f ? ap_vcq : ap_vcp;
+            uint32_t* run = vrun + (f ? qq : qp) * 2 * V;
+            if (code != 0) {
+                atomicOr(run + vk, code << vsh);
+                if (vsh + V > 32 && (code >> (32 - vsh)) != 0) atomicOr(run + vk + 1, code >> (32 - vsh));
+            }
+        }
+        if (lane == 0) {
+            float* scl = (float*)(tile + KB + kHeadDim * 8 * V);
+            scl[tail_p] = ap_sk;
+            scl[kTile + tail_p] = ap_sv;
+        }
+        // the stores are done (and the staging reads returned) before the buffers refill
+        __builtin_amdgcn_s_waitcnt(0);
+        __builtin_amdgcn_wave_barrier();
+        if (tau < t1) {
+            dma_k(tau, 0);
+            dma_v(tau);
+        }
+    }
+
     floatx4 o[8];
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) o[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
@@ -409,8 +495,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         // into the other K buffer
         __builtin_amdgcn_s_waitcnt(wait_vm(VI));
         __builtin_amdgcn_wave_barrier();
+        uint8_t* kbuf = wbuf + kb * KB;
+        const bool tail_here = appender && tau == tail_tau;
+        if (tail_here) {  // the appended record into the LDS copy (word k of record p: chunk-major)
+            if (lane < RD) *(uint32_t*)(kbuf + 16 * (64 * (lane >> 2) + tail_p) + 4 * (lane & 3)) = ap_rec;
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+            __builtin_amdgcn_wave_barrier();
+        }
         uint32_t rec[RD + 2];
-        const uint8_t* kbuf = wbuf + kb * KB;
 #pragma unroll
         for (int k = 0; k < RD / 4; ++k) {
             const uint4 v4 = *(const uint4*)(kbuf + 16 * (64 * k + qslot));
@@ -437,8 +529,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         if (more) __builtin_amdgcn_s_waitcnt(wait_vm(KI));
         else __builtin_amdgcn_s_waitcnt(wait_vm(0));
         __builtin_amdgcn_wave_barrier();
-        const uint8_t* vsec = wbuf + 2 * KB;
+        uint8_t* vsec = wbuf + 2 * KB;
         const float* scl = (const float*)(vsec + kHeadDim * 8 * V);
+        if (tail_here) {  // the appended V codes and scales into the LDS copy
+            const int vb = tail_p * V, vk = vb >> 5, vsh = vb & 31;
+#pragma unroll
+            for (int f = 0; f < 2; ++f) {
+                const uint32_t code = f ? ap_vcq : ap_vcp;
+                uint32_t* run = (uint32_t*)vsec + (f ? qq : qp) * 2 * V;
+                atomicOr(run + vk, code << vsh);
+                if (vsh + V > 32) atomicOr(run + vk + 1, code >> (32 - vsh));
+            }
+            if (lane == 0) {
+                ((float*)scl)[tail_p] = ap_sk;
+                ((float*)scl)[kTile + tail_p] = ap_sv;
+            }
+            __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+            __builtin_amdgcn_wave_barrier();
+        }
         float sk[16];
 #pragma unroll
         for (int i = 0; i < 4; ++i) {
@@ -568,9 +676,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
 // launch for one value width V (instantiated in kvq_decode_mfma_v<V>.hip)
 template <int V>
 hipError_t launch_mfma_v(const kvq_geom& g, const DecodePlan& plan, int n_q_heads, const uint16_t* q,
-                         const uint8_t* cache, const int64_t* seq_byte_off, const int32_t* seq_len, int n_seq,
+                         uint8_t* cache, const int64_t* seq_byte_off, const int32_t* seq_len, int n_seq,
                          int64_t max_len, const uint8_t* k_bits, const float* k_sigma, const float* v_sigma,
-                         float scale_log2, float* partials, hipStream_t st) {
+                         float scale_log2, float* partials, hipStream_t st, const AppendArgs& app) {
     const int grp = n_q_heads / g.n_kv_heads;
     const int rd = (int)(k_record_bytes(g.k_budget) / 4);
     dim3 grid(plan.n_split, g.n_kv_heads, n_seq);
@@ -578,7 +686,7 @@ hipError_t launch_mfma_v(const kvq_geom& g, const DecodePlan& plan, int n_q_head
     if (rd == RDV) {                                                                                            \
         hipLaunchKernelGGL((decode_mfma_kernel<V, RDV>), grid, dim3(256), 0, st, q, cache, seq_byte_off,       \
                            seq_len, max_len, g.capacity_tokens, k_bits, k_sigma, v_sigma, scale_log2, n_q_heads, \
-                           grp, g.rope_pairing, g.k_budget, plan.tiles_per_split, plan.n_split, partials);      \
+                           grp, g.rope_pairing, g.k_budget, plan.tiles_per_split, plan.n_split, partials, app); \
         return hipGetLastError();                                                                               \
     }
     KVQ_LAUNCH(0) KVQ_LAUNCH(4) KVQ_LAUNCH(8) KVQ_LAUNCH(12) KVQ_LAUNCH(16)

@@ -7,12 +7,12 @@ namespace kvq {
 
 template <int V>
 hipError_t launch_mfma_v(const kvq_geom& g, const DecodePlan& plan, int n_q_heads, const uint16_t* q,
-                         const uint8_t* cache, const int64_t* seq_byte_off, const int32_t* seq_len, int n_seq,
+                         uint8_t* cache, const int64_t* seq_byte_off, const int32_t* seq_len, int n_seq,
                          int64_t max_len, const uint8_t* k_bits, const float* k_sigma, const float* v_sigma,
-                         float scale_log2, float* partials, hipStream_t st);
+                         float scale_log2, float* partials, hipStream_t st, const AppendArgs& app);
 #define KVQ_EXTERN(VB) extern template hipError_t launch_mfma_v<VB>(const kvq_geom&, const DecodePlan&, int,      \
-    const uint16_t*, const uint8_t*, const int64_t*, const int32_t*, int, int64_t, const uint8_t*, const float*,   \
-    const float*, float, float*, hipStream_t);
+    const uint16_t*, uint8_t*, const int64_t*, const int32_t*, int, int64_t, const uint8_t*, const float*,         \
+    const float*, float, float*, hipStream_t, const AppendArgs&);
 KVQ_EXTERN(1) KVQ_EXTERN(2) KVQ_EXTERN(3) KVQ_EXTERN(4) KVQ_EXTERN(5) KVQ_EXTERN(6) KVQ_EXTERN(7) KVQ_EXTERN(8)
 #undef KVQ_EXTERN
 template <int V>
@@ -36,14 +36,14 @@ int mfma_blocks_per_cu(const kvq_geom& g) {
 }
 
 hipError_t launch_decode_mfma(const kvq_geom& g, const DecodePlan& plan, int n_q_heads, const uint16_t* q,
-                              const uint8_t* cache, const int64_t* seq_byte_off, const int32_t* seq_len, int n_seq,
+                              uint8_t* cache, const int64_t* seq_byte_off, const int32_t* seq_len, int n_seq,
                               int64_t max_len, const uint8_t* k_bits, const float* k_sigma, const float* v_sigma,
-                              float scale_log2, float* partials, hipStream_t st) {
+                              float scale_log2, float* partials, hipStream_t st, const AppendArgs& app) {
     switch (g.v_bits) {
 #define KVQ_CASE(VB)                                                                                            \
     case VB:                                                                                                    \
         return launch_mfma_v<VB>(g, plan, n_q_heads, q, cache, seq_byte_off, seq_len, n_seq, max_len, k_bits,  \
-                                 k_sigma, v_sigma, scale_log2, partials, st);
+                                 k_sigma, v_sigma, scale_log2, partials, st, app);
         KVQ_CASE(1) KVQ_CASE(2) KVQ_CASE(3) KVQ_CASE(4) KVQ_CASE(5) KVQ_CASE(6) KVQ_CASE(7) KVQ_CASE(8)
 #undef KVQ_CASE
         default: return hipErrorInvalidValue;

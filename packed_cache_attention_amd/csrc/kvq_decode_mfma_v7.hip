@@ -2,8 +2,8 @@
 #include "kvq_decode_mfma.h"
 
 namespace kvq {
-template hipError_t launch_mfma_v<7>(const kvq_geom&, const DecodePlan&, int, const uint16_t*, const uint8_t*,
+template hipError_t launch_mfma_v<7>(const kvq_geom&, const DecodePlan&, int, const uint16_t*, uint8_t*,
                                      const int64_t*, const int32_t*, int, int64_t, const uint8_t*, const float*,
-                                     const float*, float, float*, hipStream_t);
+                                     const float*, float, float*, hipStream_t, const AppendArgs&);
 template int mfma_blocks_per_cu_v<7>(const kvq_geom&);
 }  // namespace kvq

@@ -16,35 +16,6 @@
 
 namespace kvq {
 
-// code = #{ j in 1..2^w-1 : x >= RN32(s * RN32(sig * thr_w[j])) }; the products are
-// non-decreasing in j, so the count is found by binary lifting.
-__device__ __forceinline__ uint32_t code_of(const float* thr_all, float x, int w, float sig, float s) {
-    const float* thr = thr_all + KVQ_CB_OFF(w);
-    uint32_t code = 0;
-    for (int bit = 1 << (w - 1); bit >= 1; bit >>= 1) {
-        const uint32_t cand = code + bit;
-        const float a = sig * thr[cand];
-        const float b = s * a;
-        if (x >= b) code = cand;
-    }
-    return code;
-}
-
-__device__ __forceinline__ uint32_t encode(const float* thr_all, uint32_t bits16, int w, float sig, float s) {
-    if (w == 0) return 0;
-    if (w == 16) return bits16;
-    return code_of(thr_all, h2f(bits16), w, sig, s);
-}
-
-// balanced pairwise binary32 tree over the 128 squares (lane l: coordinates 2l, 2l+1)
-__device__ __forceinline__ float token_norm(uint32_t pair) {
-    const float a = h2f(pair & 0xffffu), b = h2f(pair >> 16);
-    float t = a * a + b * b;  // both squares exact in binary32
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) t = t + __shfl_xor(t, m);
-    return sqrtf(t);  // correctly rounded on gfx950
-}
-
 __global__ __launch_bounds__(256) void quantize_pack_kernel(
     const uint16_t* __restrict__ kx, const uint16_t* __restrict__ vx, int64_t stride_tok, int64_t stride_head,
     const int64_t* __restrict__ first_slot, const int32_t* __restrict__ n_new, const int64_t* __restrict__ src_row0,
@@ -185,14 +156,16 @@ __global__ __launch_bounds__(64) void append_kernel(
     const int64_t* __restrict__ first_slot, const int32_t* __restrict__ n_new, const int64_t* __restrict__ src_row0,
     int max_new, int64_t capacity, const uint8_t* __restrict__ k_bits, const float* __restrict__ k_sigma,
     const float* __restrict__ v_sigma, uint8_t* __restrict__ cache, const int64_t* __restrict__ seq_byte_off,
-    int pairing, int k_budget, int v_bits) {
+    int pairing, int k_budget, int v_bits, const int32_t* __restrict__ step_len) {
     const int s = blockIdx.z, h = blockIdx.y, j = blockIdx.x;
-    const int64_t first = first_slot[s];
-    const int n = n_new[s];
+    // either explicit runs (first_slot, n_new, src_row0) or the decode step: one token
+    // per sequence, row s, into slot step_len[s] - 1
+    const int64_t first = step_len ? (int64_t)step_len[s] - 1 : first_slot[s];
+    const int n = step_len ? 1 : n_new[s];
     if (first < 0 || n <= 0 || n > max_new || first + n > capacity || j >= n) return;
     const int lane = threadIdx.x;
     const int64_t slot = first + j;
-    const int64_t row = src_row0[s] + j;
+    const int64_t row = step_len ? (int64_t)s : src_row0[s] + j;
     const int64_t tau = slot / kTile;
     const int p = (int)(slot - tau * kTile);
     const int64_t SK = k_record_bytes(k_budget);
@@ -281,7 +254,7 @@ hipError_t launch_quantize_pack(const kvq_geom& g, const uint16_t* k, const uint
         dim3 grid(max_new, g.n_kv_heads, n_seq);
         hipLaunchKernelGGL(append_kernel, grid, dim3(64), 0, st, k, v, stride_tok, stride_head, first_slot, n_new,
                            src_row0, max_new, g.capacity_tokens, k_bits, k_sigma, v_sigma, cache, seq_byte_off,
-                           g.rope_pairing, g.k_budget, g.v_bits);
+                           g.rope_pairing, g.k_budget, g.v_bits, (const int32_t*)nullptr);
         return hipGetLastError();
     }
     // a run of max_new slots starting anywhere touches at most ceil(max_new/64) + 1 tiles
@@ -290,6 +263,17 @@ hipError_t launch_quantize_pack(const kvq_geom& g, const uint16_t* k, const uint
     hipLaunchKernelGGL(quantize_pack_kernel, grid, dim3(256), 0, st, k, v, stride_tok, stride_head, first_slot,
                        n_new, src_row0, max_new, g.capacity_tokens, k_bits, k_sigma, v_sigma, cache, seq_byte_off,
                        g.rope_pairing, g.k_budget, g.v_bits);
+    return hipGetLastError();
+}
+
+hipError_t launch_append_step(const kvq_geom& g, int n_seq, const AppendArgs& app, const int32_t* seq_len,
+                              const uint8_t* k_bits, const float* k_sigma, const float* v_sigma, uint8_t* cache,
+                              const int64_t* seq_byte_off, hipStream_t st) {
+    dim3 grid(1, g.n_kv_heads, n_seq);
+    hipLaunchKernelGGL(append_kernel, grid, dim3(64), 0, st, app.k, app.v, app.stride_seq, app.stride_head,
+                       (const int64_t*)nullptr, (const int32_t*)nullptr, (const int64_t*)nullptr, 1,
+                       g.capacity_tokens, k_bits, k_sigma, v_sigma, cache, seq_byte_off, g.rope_pairing, g.k_budget,
+                       g.v_bits, seq_len);
     return hipGetLastError();
 }
 

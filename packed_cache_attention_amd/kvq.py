@@ -77,6 +77,11 @@ def lib() -> C.CDLL:
     L.kvq_merge_partials.restype = I32
     L.kvq_decode_n_split.argtypes = [G, I32, I32, I64, I32, I32]
     L.kvq_decode_n_split.restype = I32
+    L.kvq_decode_step_partials.argtypes = [G, I32, P, P, P, I64, I64, P, P, P, I32, I64, P, P, P, F32, P, SZ, I32,
+                                           I32, P]
+    L.kvq_decode_step_partials.restype = I32
+    L.kvq_decode_step.argtypes = [G, I32, P, P, P, I64, I64, P, P, P, I32, I64, P, P, P, F32, P, P, SZ, I32, I32, P]
+    L.kvq_decode_step.restype = I32
     L.kvq_decode_plan.argtypes = [G, I32, I32, I64, I32, I32, P, P, P, P]
     L.kvq_decode_plan.restype = I32
     if L.kvq_version() != LAYOUT_VERSION:
@@ -87,7 +92,8 @@ def lib() -> C.CDLL:
 EXPORTS = ["kvq_version", "kvq_status_string", "kvq_tile_bytes", "kvq_cache_bytes", "kvq_get_codebook",
            "kvq_block_energy", "kvq_allocate_bits", "kvq_quantize_pack", "kvq_decode_workspace_bytes",
            "kvq_decode_workspace_bytes_ex", "kvq_packed_decode_attn", "kvq_packed_decode_attn_ex",
-           "kvq_decode_partials", "kvq_merge_partials", "kvq_decode_n_split", "kvq_decode_plan"]
+           "kvq_decode_partials", "kvq_merge_partials", "kvq_decode_n_split", "kvq_decode_plan",
+           "kvq_decode_step_partials", "kvq_decode_step"]
 
 
 def status_string(st: int) -> str:
@@ -228,6 +234,46 @@ def decode_partials(g: Geom, q: torch.Tensor, cache: torch.Tensor, seq_byte_off:
         C.byref(g), n_q, _ptr(q), _ptr(cache), _ptr(seq_byte_off), _ptr(seq_len), n_seq, max_len, _ptr(k_bits),
         _ptr(k_sigma), _ptr(v_sigma), float(softmax_scale), _ptr(partials), partials.numel() * 4, kernel,
         tiles_per_split, _stream(stream)))
+
+
+def _step_rows(k_new: torch.Tensor, v_new: torch.Tensor):
+    assert k_new.dtype == torch.float16 and v_new.dtype == torch.float16 and k_new.dim() == 3
+    assert k_new.stride() == v_new.stride() and k_new.stride(2) == 1
+    return k_new.stride(0), k_new.stride(1)
+
+
+def decode_step_partials(g: Geom, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, cache: torch.Tensor,
+                         seq_byte_off: torch.Tensor, seq_len: torch.Tensor, max_len: int, k_bits: torch.Tensor,
+                         k_sigma: torch.Tensor, v_sigma: torch.Tensor, partials: torch.Tensor,
+                         softmax_scale: float | None = None, kernel: int = DECODE_AUTO, tiles_per_split: int = 0,
+                         stream=None):
+    """The decode step's split phase: append k_new/v_new [n_seq, n_kv, 128] into slot
+    seq_len-1 of each sequence, then partials over all seq_len tokens."""
+    assert q.dtype == torch.float16 and q.is_contiguous() and partials.dtype == torch.float32
+    ss, sh = _step_rows(k_new, v_new)
+    n_seq, n_q = q.shape[0], q.shape[1]
+    if softmax_scale is None:
+        softmax_scale = g.head_dim ** -0.5
+    _check("kvq_decode_step_partials", lib().kvq_decode_step_partials(
+        C.byref(g), n_q, _ptr(q), _ptr(k_new), _ptr(v_new), ss, sh, _ptr(cache), _ptr(seq_byte_off), _ptr(seq_len),
+        n_seq, max_len, _ptr(k_bits), _ptr(k_sigma), _ptr(v_sigma), float(softmax_scale), _ptr(partials),
+        partials.numel() * 4, kernel, tiles_per_split, _stream(stream)))
+
+
+def decode_step(g: Geom, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor, cache: torch.Tensor,
+                seq_byte_off: torch.Tensor, seq_len: torch.Tensor, max_len: int, k_bits: torch.Tensor,
+                k_sigma: torch.Tensor, v_sigma: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
+                softmax_scale: float | None = None, kernel: int = DECODE_AUTO, tiles_per_split: int = 0, stream=None):
+    """Append the step's token per sequence, then attention (out [n_seq, n_q, 128] fp32)."""
+    assert q.dtype == torch.float16 and q.is_contiguous() and out.dtype == torch.float32 and out.is_contiguous()
+    ss, sh = _step_rows(k_new, v_new)
+    n_seq, n_q = q.shape[0], q.shape[1]
+    if softmax_scale is None:
+        softmax_scale = g.head_dim ** -0.5
+    _check("kvq_decode_step", lib().kvq_decode_step(
+        C.byref(g), n_q, _ptr(q), _ptr(k_new), _ptr(v_new), ss, sh, _ptr(cache), _ptr(seq_byte_off), _ptr(seq_len),
+        n_seq, max_len, _ptr(k_bits), _ptr(k_sigma), _ptr(v_sigma), float(softmax_scale), _ptr(out), _ptr(workspace),
+        workspace.numel() * workspace.element_size(), kernel, tiles_per_split, _stream(stream)))
 
 
 def merge_partials(n_seq: int, n_q: int, n_split: int, partials: torch.Tensor, out: torch.Tensor, stream=None):

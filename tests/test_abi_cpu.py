@@ -100,3 +100,11 @@ def test_host_validation_rejects_before_gpu():
     assert L.kvq_packed_decode_attn_ex(*d_args(16, 512, 16)) == -6
     assert L.kvq_packed_decode_attn_ex(*d_args(16, 512, 1 << 30, q=FAKE + 8)) == -4
     assert kvq.status_string(-6) == "workspace too small"
+    # decode step: the decode checks, then the new-token rows
+    s_args = lambda kn, ss, ws=1 << 30: (C.byref(good), 16, FAKE, kn, FAKE, ss, 128, FAKE, FAKE, FAKE, 1, 512, FAKE,
+                                         FAKE, FAKE, 0.1, FAKE, FAKE, ws, 0, 0, None)
+    assert L.kvq_decode_step(*s_args(None, 256)) == -1
+    assert L.kvq_decode_step(*s_args(FAKE + 2, 256)) == -4
+    assert L.kvq_decode_step(*s_args(FAKE, 255)) == -4
+    assert L.kvq_decode_step(*s_args(FAKE, -2)) == -1
+    assert L.kvq_decode_step(*s_args(FAKE, 256, ws=16)) == -6

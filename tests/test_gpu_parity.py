@@ -307,3 +307,66 @@ def test_c5_batch_append_then_attend():
     ref = np.stack([oracle.decode_attention(r["ogeom"], oc[i * region:(i + 1) * region], new[i][2].numpy(),
                                             wl.seq_lens[i] + 1, r["ob"], r["osig"], r["ovsig"]) for i in range(S)])
     say("c5: attention worst rel %.2e" % check_attention(out.cpu().numpy(), ref))
+
+
+STEP_CASES = [(c[0], c[1], c[2], c[5], c[6], c[7]) for c in CASES if c[0] in
+              ("k3v3-ragged", "k2v2-ragged", "kodd-v5", "k8v8-max", "k0v1", "konly-v16", "k16v16-pass",
+               "interleaved", "gqa16")]
+
+
+@pytest.mark.parametrize("tiles", [0, 1, 4, 8])
+@pytest.mark.parametrize("case", STEP_CASES, ids=[c[0] for c in STEP_CASES])
+def test_decode_step_equals_append_then_attend(case, tiles):
+    """kvq_decode_step (append inside the attention kernel where it applies) gives the
+    bytes and outputs of kvq_quantize_pack followed by kvq_packed_decode_attn, over
+    three steps whose new tokens cross tile boundaries (appending waves 0-3, and a wave
+    whose tail tile is its second), and the oracle's attention."""
+    name, H, grp, kb, vb, pairing = case
+    say("decode step %s tiles=%d" % (name, tiles))
+    n0 = [62, 127, 1, 200, 290]
+    steps = 3
+    wl = synth.Workload("step-" + name, 1, H * grp, H, 1e6, (0,), kb, vb, "decay")
+    seqs = []
+    for i, n in enumerate(n0):
+        K, V, q = synth.gen_layer(wl.with_lens([n + steps]), i, 0, n_tok=n + steps, seed=21 + i)
+        if pairing == 1:
+            K = K[:, :, torch.randperm(128, generator=torch.Generator().manual_seed(8))].contiguous()
+        seqs.append((K, V, q))
+    cap = 384
+    r = run_batch([(K[:n], V[:n], q) for (K, V, q), n in zip(seqs, n0)], kb, vb, cap, pairing=pairing,
+                  check_attn=False)
+    g, off = r["g"], r["off"]
+    S = len(seqs)
+    cache_a, cache_b = r["cache"].clone(), r["cache"].clone()
+    nq = H * grp
+    ws = torch.empty(kvq.decode_workspace_bytes(g, nq, S, cap, kvq.DECODE_AUTO, tiles) // 4, dtype=torch.float32,
+                     device="cuda")
+    region = kvq.cache_bytes(g)
+    for st in range(steps):
+        kn = torch.stack([K[n0[i] + st] for i, (K, _, _) in enumerate(seqs)]).cuda()
+        vn = torch.stack([V[n0[i] + st] for i, (_, V, _) in enumerate(seqs)]).cuda()
+        q = torch.stack([x[2] for x in seqs]).cuda().contiguous()
+        lens = torch.tensor([n + st for n in n0], dtype=torch.int64, device="cuda")
+        seq_len = (lens + 1).to(torch.int32)
+        # the two calls
+        kvq.quantize_pack(g, kn, vn, lens, torch.ones(S, dtype=torch.int32, device="cuda"),
+                          torch.arange(S, dtype=torch.int64, device="cuda"), 1, r["kbits"], r["ksig"], r["vsig"],
+                          cache_a, off)
+        out_a = torch.empty(S, nq, 128, dtype=torch.float32, device="cuda")
+        kvq.packed_decode_attn(g, q, cache_a, off, seq_len, cap, r["kbits"], r["ksig"], r["vsig"], out_a, ws,
+                               tiles_per_split=tiles)
+        # the fused step
+        out_b = torch.empty_like(out_a)
+        kvq.decode_step(g, q, kn, vn, cache_b, off, seq_len, cap, r["kbits"], r["ksig"], r["vsig"], out_b, ws,
+                        tiles_per_split=tiles)
+        np.testing.assert_array_equal(cache_b.cpu().numpy(), cache_a.cpu().numpy())
+        np.testing.assert_array_equal(out_b.cpu().numpy(), out_a.cpu().numpy())
+    # and both equal the oracle's quantization of every token, and its attention
+    oc = np.zeros(S * region, np.uint8)
+    for i, (K, V, _) in enumerate(seqs):
+        oracle.quantize_pack(r["ogeom"], oc[i * region:(i + 1) * region], K.numpy(), V.numpy(), 0, r["ob"], r["osig"],
+                             r["ovsig"])
+    np.testing.assert_array_equal(cache_b.cpu().numpy(), oc)
+    ref = np.stack([oracle.decode_attention(r["ogeom"], oc[i * region:(i + 1) * region], seqs[i][2].numpy(),
+                                            n0[i] + steps, r["ob"], r["osig"], r["ovsig"]) for i in range(S)])
+    check_attention(out_b.cpu().numpy(), ref)
