@@ -93,6 +93,7 @@ struct MfmaSmem {
     alignas(16) float alpha[kWaves][8];
     alignas(16) float wm[8][kWaves];  // per head: each wave's reference max (log2 units)
     alignas(16) float wl[8][kWaves];  // ... and its sum of weights
+    uint32_t arec[16];                // the appended token's K record, assembled
 };
 // the waves' unnormalised outputs [wave][coordinate][head], combined at the end in
 // the (then idle) tile buffers
@@ -276,7 +277,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     constexpr int BUF = kWaves * WB > (int)sizeof(WaveOut) ? kWaves * WB : (int)sizeof(WaveOut);
     __shared__ MfmaSmem sm;
     __shared__ __attribute__((aligned(16))) uint8_t bufs[BUF];
-    const int split = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
+    // grid (KV head, chunk, sequence): dispatch walks the heads fastest, so a
+    // sequence's last chunks -- the short tail chunk in particular -- go out last and
+    // land beside full workgroups instead of displacing one
+    const int kvh = blockIdx.x, split = blockIdx.y, s = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
 
     // ---- every global load of the prologue goes out before anything waits on one
@@ -322,8 +326,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     const int64_t t1 = min(t0 + tiles_per_split, n_tiles_seq);
     // the wave whose tiles include slot len-1 appends the new token there first
     const int64_t tail_tau = (len - 1) / kTile;
-    const bool appender = app.k != nullptr && len > 0 && tail_tau >= t0 && tail_tau < t1 &&
-                          (int)((tail_tau - t0) % kWaves) == wave;
+    const bool wg_appends = app.k != nullptr && len > 0 && tail_tau >= t0 && tail_tau < t1;
+    const int app_wave = (int)((tail_tau - t0) % kWaves);
+    const bool appender = wg_appends && app_wave == wave;
+    float thr_a = 0.f, thr_b = 0.f;  // the codebook thresholds, staged for the appender by the whole group
+    if (wg_appends) {
+        thr_a = c_thresholds[tid];
+        thr_b = c_thresholds[min(tid + 256, 509)];
+    }
 
     // lane roles
     const int col = lane & 31;
@@ -357,13 +367,24 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
             if (64 * j + 63 < VB / 16 || ch < VB / 16) dma16(vsec + 16 * ch, wbuf_lds + 2 * KB + 1024 * j);
         }
     };
+    constexpr bool kStageInK1 = KB >= 510 * 4;  // see the staging area below
     int64_t tau = t0 + wave;
-    if (tau < t1 && !appender) {
+    if (tau < t1 && (kStageInK1 || !appender)) {
         dma_k(tau, 0);
         dma_v(tau);
     }
 
     // ------------------------------------------------------------------ prologue
+    // the appender's staging area for the thresholds: its second K buffer when that
+    // holds them (idle until its first tile starts), else its own buffers (which then
+    // fill only after the append) or the spare end of the shared buffer
+    static_assert(WB >= 510 * 4 || BUF - kWaves * WB >= 510 * 4, "no room to stage the thresholds");
+    float* const s_thr = (float*)(kStageInK1 ? bufs + app_wave * WB + KB
+                                            : WB >= 510 * 4 ? bufs + app_wave * WB : bufs + kWaves * WB);
+    if (wg_appends) {
+        s_thr[tid] = thr_a;
+        if (tid + 256 < 510) s_thr[tid + 256] = thr_b;
+    }
     ((uint4*)&sm.tab)[tid] = tab0;
     if (tid + 256 < kTabChunks) ((uint4*)&sm.tab)[tid + 256] = tab1;
     {
@@ -415,33 +436,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     const uint16_t* qb = bdiag ? &sm.qsplit[(col >> 3) & 1][col & 7][0] : &sm.qsplit[0][0][8 * (kMaxUnits - 1)];
     const int qs = bdiag ? 8 : 0;
 
-    // ---- the step's append (one wave): quantize and pack the new token into slot
-    // len-1, exactly as the quantize path does, then fetch this wave's first tile.
-    // The tail tile's copy in LDS is patched with the same bytes when it arrives, so
-    // it does not matter whether the tile fetch sees the stores.
+    // ---- the step's append (one wave): quantize and pack the new token for slot
+    // len-1 exactly as the quantize path does.  The bytes go into the LDS copy of
+    // the tail tile when it arrives, and to the cache after the tiles.
     const int tail_p = (int)((len - 1) & (kTile - 1));
     uint32_t ap_rec = 0, ap_vcp = 0, ap_vcq = 0;
     float ap_sk = 0.f, ap_sv = 0.f;
     if (appender) {
-        // staging: the wave's own (still idle) buffers, or the spare end of the shared
-        // buffer when they are too small
-        constexpr int kStage = 2048 + 4 * 16;  // 510 thresholds, then one record (<= 16 words)
-        static_assert(WB >= kStage || BUF - kWaves * WB >= kStage, "no room to stage the append");
-        uint8_t* stage = WB >= kStage ? wbuf : bufs + kWaves * WB;
-        float* s_thr = (float*)stage;
-        uint32_t* s_rec = (uint32_t*)(stage + 2048);
-#pragma unroll
-        for (int k = 0; k < 8; ++k)
-            if (64 * k + lane < 510) s_thr[64 * k + lane] = c_thresholds[64 * k + lane];
+        uint32_t* s_rec = sm.arec + 0;
         if (lane < 16) s_rec[lane] = 0;
-        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
-        __builtin_amdgcn_wave_barrier();
         ap_sk = token_norm(nk_pair);
         ap_sv = token_norm(nv_pair);
         const uint32_t kcp = encode(s_thr, nk_p, my_w, my_ksig, ap_sk);
         const uint32_t kcq = encode(s_thr, nk_q, my_w, my_ksig, ap_sk);
         ap_vcp = encode(s_thr, nv_p, V, my_vsig_blk, ap_sv);
         ap_vcq = encode(s_thr, nv_q, V, my_vsig_blk, ap_sv);
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+        __builtin_amdgcn_wave_barrier();
         if (my_w > 0) {
 #pragma unroll
             for (int f = 0; f < 2; ++f) {
@@ -454,28 +465,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         __builtin_amdgcn_wave_barrier();
         ap_rec = lane < RD ? s_rec[lane] : 0u;
-        uint8_t* tile = (uint8_t*)head_base + tail_tau * TB;
-        if (lane < RD) ((uint32_t*)(tile + tail_p * SK))[lane] = ap_rec;
-        uint32_t* vrun = (uint32_t*)(tile + KB);
-        const int vb = tail_p * V, vk = vb >> 5, vsh = vb & 31;
-#pragma unroll
-        for (int f = 0; f < 2; ++f) {
-            const uint32_t code = f ? ap_vcq : ap_vcp;
-            uint32_t* run = vrun + (f ? qq : qp) * 2 * V;
-            if (code != 0) {
-                atomicOr(run + vk, code << vsh);
-                if (vsh + V > 32 && (code >> (32 - vsh)) != 0) atomicOr(run + vk + 1, code >> (32 - vsh));
-            }
-        }
-        if (lane == 0) {
-            float* scl = (float*)(tile + KB + kHeadDim * 8 * V);
-            scl[tail_p] = ap_sk;
-            scl[kTile + tail_p] = ap_sv;
-        }
-        // the stores are done (and the staging reads returned) before the buffers refill
-        __builtin_amdgcn_s_waitcnt(0);
+        // the staging reads have returned: the buffers may refill
+        __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         __builtin_amdgcn_wave_barrier();
-        if (tau < t1) {
+        if (!kStageInK1 && tau < t1) {
             dma_k(tau, 0);
             dma_v(tau);
         }
@@ -622,6 +615,28 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         }
     }
 
+    // ---- the appended token into the cache (the tail tile was read from LDS already)
+    if (appender) {
+        uint8_t* tile = (uint8_t*)head_base + tail_tau * TB;
+        if (lane < RD) ((uint32_t*)(tile + tail_p * SK))[lane] = ap_rec;
+        uint32_t* vrun = (uint32_t*)(tile + KB);
+        const int vb = tail_p * V, vk = vb >> 5, vsh = vb & 31;
+#pragma unroll
+        for (int f = 0; f < 2; ++f) {
+            const uint32_t code = f ? ap_vcq : ap_vcp;
+            uint32_t* run = vrun + (f ? qq : qp) * 2 * V;
+            if (code != 0) {
+                atomicOr(run + vk, code << vsh);
+                if (vsh + V > 32 && (code >> (32 - vsh)) != 0) atomicOr(run + vk + 1, code >> (32 - vsh));
+            }
+        }
+        if (lane == 0) {
+            float* scl = (float*)(tile + KB + kHeadDim * 8 * V);
+            scl[tail_p] = ap_sk;
+            scl[kTile + tail_p] = ap_sv;
+        }
+    }
+
     // ------------------------------------------------------------------ combine
     // l: sum over the four slot groups (lanes l, l^16, l^32, l^48) of a head's hi row
     const float lsum = xor32_sum(xor16_sum(lrun));
@@ -681,7 +696,7 @@ hipError_t launch_mfma_v(const kvq_geom& g, const DecodePlan& plan, int n_q_head
                          float scale_log2, float* partials, hipStream_t st, const AppendArgs& app) {
     const int grp = n_q_heads / g.n_kv_heads;
     const int rd = (int)(k_record_bytes(g.k_budget) / 4);
-    dim3 grid(plan.n_split, g.n_kv_heads, n_seq);
+    dim3 grid(g.n_kv_heads, plan.n_split, n_seq);
 #define KVQ_LAUNCH(RDV)                                                                                        \
     if (rd == RDV) {                                                                                            \
         hipLaunchKernelGGL((decode_mfma_kernel<V, RDV>), grid, dim3(256), 0, st, q, cache, seq_byte_off,       \
