@@ -16,6 +16,19 @@
 
 namespace kvq {
 
+// Bulk quantize + pack, one workgroup per (sequence, KV head, tile), lane = token.
+// The tile's fp16 rows are staged in LDS (rows 65 dwords apart: a coordinate read
+// by 64 lanes touches distinct banks).  Norms: waves 0-1 form the two 64-leaf
+// halves of each K row's pairwise tree, waves 2-3 those of V (the root adds the
+// halves, as the tree does).  Codes: each wave takes a run of K-order fields
+// holding about a quarter of the record's bits, and a quarter of the V
+// coordinates; for a field every lane searches at the same width, and the K record
+// bits are gathered in registers and OR-ed into the LDS records word by word.
+constexpr int kRowDw = kHeadDim / 2 + 1;
+constexpr int kQWaves = 4;
+constexpr int kGroup = 4;   // K fields encoded side by side (independent searches)
+constexpr int kVGroup = 8;  // V coordinates encoded side by side
+
 __global__ __launch_bounds__(256) void quantize_pack_kernel(
     const uint16_t* __restrict__ kx, const uint16_t* __restrict__ vx, int64_t stride_tok, int64_t stride_head,
     const int64_t* __restrict__ first_slot, const int32_t* __restrict__ n_new, const int64_t* __restrict__ src_row0,
@@ -30,112 +43,239 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
     const int64_t tile0 = tau * kTile;
     const int64_t lo_slot = max(first, tile0), hi_slot = min(first + (int64_t)n, tile0 + kTile);
     if (lo_slot >= hi_slot) return;
+    const int lo_p = (int)(lo_slot - tile0), hi_p = (int)(hi_slot - tile0);
 
     const int64_t SK = k_record_bytes(k_budget);
     const int64_t TB = tile_bytes(kHeadDim, k_budget, v_bits);
-    const int64_t n_tiles = capacity / kTile;
-    uint8_t* tile = cache + seq_byte_off[s] + ((int64_t)h * n_tiles + tau) * TB;
+    const int RW = (int)(SK / 4), RS = RW + 1;  // record words, LDS record stride (odd)
+    const int VW = 2 * v_bits, VS = VW + 1;     // run words, LDS run stride
+    uint8_t* tile = cache + seq_byte_off[s] + ((int64_t)h * (capacity / kTile) + tau) * TB;
 
-    __shared__ uint16_t s_kc[kTile][kHeadDim];
-    __shared__ uint16_t s_vc[kTile][kHeadDim];
+    __shared__ uint32_t s_k[kTile * kRowDw], s_v[kTile * kRowDw];
+    __shared__ float s_thr[510];
+    __shared__ float s_half[4][kTile];
     __shared__ float s_ks[kTile], s_vs[kTile];
-    __shared__ uint8_t s_w[kHeadDim];          // key width per coordinate
-    __shared__ float s_ksig[kHeadDim], s_vsig[kHeadDim];
-    __shared__ uint8_t s_fc[kHeadDim];         // K order: coordinate of field f
-    __shared__ uint16_t s_fo[kHeadDim];        // bit offset of field f in the record
-    __shared__ uint8_t s_fw[kHeadDim];         // width of field f
-    __shared__ uint8_t s_first[64];            // first field touching record dword k
-    __shared__ int s_nf;
-    __shared__ float s_thr[510];               // the codebook thresholds, staged once
+    // K order, field f: x = coordinate | width << 7 | bit offset << 12 | (later fields of
+    // the same width) << 23, y = the block's sigma bits; padded so that reads of up to
+    // kGroup fields from any f stay in the array
+    __shared__ uint2 s_meta[kHeadDim + kGroup];
+    __shared__ float s_vsig[kHeadDim];
+    __shared__ int s_range[kQWaves + 1];                  // wave w encodes fields [s_range[w], s_range[w+1])
+    extern __shared__ uint32_t s_dyn[];                  // records [64][RS], then runs [128][VS]
+    uint32_t* s_rec = s_dyn;
+    uint32_t* s_run = s_dyn + kTile * RS;
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-    // ---- phase 0: per-head tables and the K order ----
+    // ---- phase 0: rows, thresholds, K order, zeroed records and runs
+    const int64_t row0 = src_row0[s] + (tile0 - first);  // source row of slot 0 (only rows of valid slots are read)
+    const uint16_t* ksrc = kx + (int64_t)h * stride_head;
+    const uint16_t* vsrc = vx + (int64_t)h * stride_head;
+    if ((((uintptr_t)kx | (uintptr_t)vx) & 15) == 0 && ((stride_tok | stride_head) & 7) == 0) {
+        const int j = tid & 15;  // 16-byte piece of a 256-byte row
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const int p = (tid >> 4) + 16 * i;
+            if (p >= lo_p && p < hi_p) {
+                const uint4 a = *(const uint4*)(ksrc + (row0 + p) * stride_tok + 8 * j);
+                const uint4 b = *(const uint4*)(vsrc + (row0 + p) * stride_tok + 8 * j);
+                uint32_t* dk = s_k + p * kRowDw + 4 * j;
+                uint32_t* dv = s_v + p * kRowDw + 4 * j;
+                dk[0] = a.x; dk[1] = a.y; dk[2] = a.z; dk[3] = a.w;
+                dv[0] = b.x; dv[1] = b.y; dv[2] = b.z; dv[3] = b.w;
+            }
+        }
+    } else {  // rows only 4-byte aligned: one coordinate pair per lane
+        for (int p = wave; p < hi_p; p += kQWaves) {
+            if (p < lo_p) continue;
+            s_k[p * kRowDw + lane] = *(const uint32_t*)(ksrc + (row0 + p) * stride_tok + 2 * lane);
+            s_v[p * kRowDw + lane] = *(const uint32_t*)(vsrc + (row0 + p) * stride_tok + 2 * lane);
+        }
+    }
     for (int i = tid; i < 510; i += 256) s_thr[i] = c_thresholds[i];
+    for (int i = tid; i < kTile * RS + kHeadDim * VS; i += 256) s_dyn[i] = 0u;
+    if (tid < kHeadDim) {
+        const int blk = pairing == KVQ_PAIR_HALF ? (tid & (kMaxBlocks - 1)) : (tid >> 1);
+        s_vsig[tid] = v_sigma[h * kMaxBlocks + blk];
+    }
     if (tid < kMaxBlocks) {
-        // rank blocks by (width desc, index asc) with wave ballots; offsets are prefix
-        // sums of 2*width in that order
+        // rank blocks by (width desc, index asc); a block's fields p, q follow every
+        // wider block and the lower-indexed blocks of its own width
         const int i = tid;
         const int w = k_bits[h * kMaxBlocks + i];
-        const int p = pairing == KVQ_PAIR_HALF ? i : 2 * i;
-        const int q = pairing == KVQ_PAIR_HALF ? i + kMaxBlocks : 2 * i + 1;
-        s_w[p] = s_w[q] = (uint8_t)w;
-        s_ksig[p] = s_ksig[q] = k_sigma[h * kMaxBlocks + i];
-        s_vsig[p] = s_vsig[q] = v_sigma[h * kMaxBlocks + i];
+        const float sig = k_sigma[h * kMaxBlocks + i];
         const unsigned long long below = (1ull << i) - 1ull;
-        int rank = 0, off = 0;
+        int rank = 0, off = 0, after = 0;
         for (int wc = 16; wc >= 1; --wc) {
             const unsigned long long mk = __ballot(w == wc);
             if (wc > w) { rank += __popcll(mk); off += 2 * wc * __popcll(mk); }
-            if (wc == w) { rank += __popcll(mk & below); off += 2 * wc * __popcll(mk & below); }
+            if (wc == w) {
+                rank += __popcll(mk & below);
+                off += 2 * wc * __popcll(mk & below);
+                after = __popcll(mk & ~below) - 1;  // same-width blocks ranked after this one
+            }
         }
+        const int nf = 2 * __popcll(__ballot(w > 0));
         if (w > 0) {
-            s_fc[2 * rank] = (uint8_t)p; s_fo[2 * rank] = (uint16_t)off; s_fw[2 * rank] = (uint8_t)w;
-            s_fc[2 * rank + 1] = (uint8_t)q; s_fo[2 * rank + 1] = (uint16_t)(off + w); s_fw[2 * rank + 1] = (uint8_t)w;
+            const int pc = pairing == KVQ_PAIR_HALF ? i : 2 * i;
+            const int qc = pairing == KVQ_PAIR_HALF ? i + kMaxBlocks : 2 * i + 1;
+            const uint32_t sb = __float_as_uint(sig);
+            s_meta[2 * rank] = make_uint2(pc | w << 7 | off << 12 | (2 * after + 1) << 23, sb);
+            s_meta[2 * rank + 1] = make_uint2(qc | w << 7 | (off + w) << 12 | (2 * after) << 23, sb);
         }
-        const unsigned long long nz = __ballot(w > 0);
-        if (i == 0) s_nf = 2 * __popcll(nz);
-    }
-    __syncthreads();
-    const int nf = s_nf;
-    if (tid < (int)(SK / 4)) {
-        int f = 0;
-        while (f < nf && s_fo[f] + s_fw[f] <= 32 * tid) ++f;
-        s_first[tid] = (uint8_t)f;
-    }
-
-    // ---- phase 1: codes ----
-    for (int64_t slot = lo_slot + wave; slot < hi_slot; slot += 4) {
-        const int p = (int)(slot - tile0);
-        const int64_t row = src_row0[s] + (slot - first);
-        const uint32_t kp = *(const uint32_t*)(kx + row * stride_tok + (int64_t)h * stride_head + 2 * lane);
-        const uint32_t vp = *(const uint32_t*)(vx + row * stride_tok + (int64_t)h * stride_head + 2 * lane);
-        const float sk = token_norm(kp), sv = token_norm(vp);
-        const int c0 = 2 * lane, c1 = 2 * lane + 1;
-        s_kc[p][c0] = (uint16_t)encode(s_thr, kp & 0xffffu, s_w[c0], s_ksig[c0], sk);
-        s_kc[p][c1] = (uint16_t)encode(s_thr, kp >> 16, s_w[c1], s_ksig[c1], sk);
-        s_vc[p][c0] = (uint16_t)encode(s_thr, vp & 0xffffu, v_bits, s_vsig[c0], sv);
-        s_vc[p][c1] = (uint16_t)encode(s_thr, vp >> 16, v_bits, s_vsig[c1], sv);
-        if (lane == 0) { s_ks[p] = sk; s_vs[p] = sv; }
+        if (i < kGroup) s_meta[kHeadDim + i] = make_uint2(0u, 0u);
+        // split the fields into four runs of about a quarter of the record's bits each
+        int wsum = w;
+#pragma unroll
+        for (int m = 1; m < 64; m <<= 1) wsum += __shfl_xor(wsum, m);
+        const int total = 2 * wsum;
+        // the field at rank 2r starts at `off`; run w starts at the first field whose
+        // offset reaches w/4 of the total (offsets increase with rank)
+        for (int wv = 0; wv <= kQWaves; ++wv) {
+            const int bound = (int)(((int64_t)total * wv + kQWaves - 1) / kQWaves);
+            const unsigned long long before = __ballot(w > 0 && off < bound);
+            // fields before the bound: 2 per block that starts before it, minus a q
+            // field that already starts past it
+            const unsigned long long qpast = __ballot(w > 0 && off < bound && off + w >= bound);
+            if (i == 0) s_range[wv] = wv == kQWaves ? nf : 2 * __popcll(before) - __popcll(qpast);
+        }
     }
     __syncthreads();
 
-    // ---- phase 2: assemble the tile ----
-    const int lo_p = (int)(lo_slot - tile0), hi_p = (int)(hi_slot - tile0);
-    const bool whole = lo_p == 0 && hi_p == kTile;
-    // K records (each belongs to one slot: plain stores)
-    const int skd = (int)(SK / 4);
+    // ---- phase 1: token norms (lane = token)
+    {
+        const uint32_t* rows = wave < 2 ? s_k : s_v;
+        const uint32_t* r = rows + lane * kRowDw + 32 * (wave & 1);
+        float t[32];
+#pragma unroll
+        for (int k = 0; k < 32; ++k) {
+            const uint32_t pr = r[k];
+            const float a = h2f(pr & 0xffffu), b = h2f(pr >> 16);
+            t[k] = a * a + b * b;
+        }
+#pragma unroll
+        for (int m = 1; m < 32; m <<= 1)
+#pragma unroll
+            for (int k = 0; k < 32; k += 2 * m) t[k] = t[k] + t[k + m];
+        s_half[wave][lane] = t[0];
+    }
+    __syncthreads();
+    if (tid < kTile) s_ks[tid] = sqrtf(s_half[0][tid] + s_half[1][tid]);
+    else if (tid < 2 * kTile) s_vs[tid - kTile] = sqrtf(s_half[2][tid - kTile] + s_half[3][tid - kTile]);
+    __syncthreads();
+
+    // ---- phase 2: codes (lane = token), K record bits gathered per word
+    const bool valid = lane >= lo_p && lane < hi_p;
+    {
+        const float sk = s_ks[lane];
+        const uint16_t* krow = (const uint16_t*)(s_k + lane * kRowDw);
+        const int f0 = s_range[wave], f1 = s_range[wave + 1];
+        int cur = f0 < f1 ? (int)((s_meta[f0].x >> 12) & 2047) >> 5 : 0;
+        uint32_t acc = 0u, nxt = 0u;
+        for (int f = f0; f < f1;) {
+            // up to kGroup fields of one width (the K order sorts by width) searched side by side
+            uint2 m[kGroup];
+#pragma unroll
+            for (int i = 0; i < kGroup; ++i) m[i] = s_meta[f + i];
+            const int wf = (m[0].x >> 7) & 31;
+            const int gn = min(min(kGroup, (int)(m[0].x >> 23) + 1), f1 - f);
+            uint32_t code[kGroup];
+            if (wf == 16) {
+#pragma unroll
+                for (int i = 0; i < kGroup; ++i) code[i] = krow[m[i].x & 127];
+            } else {
+                float x[kGroup], sg[kGroup];
+#pragma unroll
+                for (int i = 0; i < kGroup; ++i) {
+                    x[i] = h2f(krow[m[i].x & 127]);
+                    sg[i] = __uint_as_float(m[i].y);
+                    code[i] = 0u;
+                }
+                const float* thr = s_thr + KVQ_CB_OFF(wf);
+                for (int bit = 1 << (wf - 1); bit >= 1; bit >>= 1) {
+#pragma unroll
+                    for (int i = 0; i < kGroup; ++i) {
+                        const uint32_t cand = code[i] + bit;
+                        const float a = sg[i] * thr[cand];
+                        const float b = sk * a;
+                        if (x[i] >= b) code[i] = cand;
+                    }
+                }
+            }
+#pragma unroll
+            for (int i = 0; i < kGroup; ++i) {
+                if (i < gn) {
+                    const int of = (m[i].x >> 12) & 2047;
+                    const int k = of >> 5, sh = of & 31;
+                    if (k != cur) {  // fields are consecutive in bits: the window moves by one word
+                        if (valid && acc) atomicOr(&s_rec[lane * RS + cur], acc);
+                        acc = nxt;
+                        nxt = 0u;
+                        cur = k;
+                    }
+                    acc |= code[i] << sh;
+                    if (sh + wf > 32) nxt |= code[i] >> (32 - sh);
+                }
+            }
+            f += gn;
+        }
+        if (valid && acc) atomicOr(&s_rec[lane * RS + cur], acc);
+        if (valid && nxt) atomicOr(&s_rec[lane * RS + cur + 1], nxt);
+
+        const float sv = s_vs[lane];
+        const uint16_t* vrow = (const uint16_t*)(s_v + lane * kRowDw);
+        const int bit0 = lane * v_bits, vk = bit0 >> 5, vsh = bit0 & 31;
+        const float* vthr = s_thr + KVQ_CB_OFF(v_bits);
+        for (int c0 = 32 * wave; c0 < 32 * wave + 32; c0 += kVGroup) {
+            uint32_t code[kVGroup];
+            if (v_bits == 16) {
+#pragma unroll
+                for (int i = 0; i < kVGroup; ++i) code[i] = vrow[c0 + i];
+            } else {
+                float x[kVGroup], sg[kVGroup];
+#pragma unroll
+                for (int i = 0; i < kVGroup; ++i) {
+                    x[i] = h2f(vrow[c0 + i]);
+                    sg[i] = s_vsig[c0 + i];
+                    code[i] = 0u;
+                }
+                for (int bit = 1 << (v_bits - 1); bit >= 1; bit >>= 1) {
+#pragma unroll
+                    for (int i = 0; i < kVGroup; ++i) {
+                        const uint32_t cand = code[i] + bit;
+                        const float a = sg[i] * vthr[cand];
+                        const float b = sv * a;
+                        if (x[i] >= b) code[i] = cand;
+                    }
+                }
+            }
+            if (valid) {
+#pragma unroll
+                for (int i = 0; i < kVGroup; ++i) {
+                    if (code[i]) {
+                        atomicOr(&s_run[(c0 + i) * VS + vk], code[i] << vsh);
+                        if (vsh + v_bits > 32) atomicOr(&s_run[(c0 + i) * VS + vk + 1], code[i] >> (32 - vsh));
+                    }
+                }
+            }
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 3: the tile's records (valid slots), runs and scales
     uint32_t* krec = (uint32_t*)tile;
-    for (int idx = tid; idx < kTile * skd; idx += 256) {
-        const int p = idx / skd, k = idx - p * skd;
-        if (p < lo_p || p >= hi_p) continue;
-        uint32_t val = 0;
-        const int lo_bit = 32 * k;
-        for (int f = s_first[k]; f < nf && s_fo[f] < lo_bit + 32; ++f) {
-            const uint32_t code = s_kc[p][s_fc[f]];
-            const int sh = (int)s_fo[f] - lo_bit;
-            val |= sh >= 0 ? (code << sh) : (code >> (-sh));
-        }
-        krec[idx] = val;
+    for (int idx = tid; idx < kTile * RW; idx += 256) {
+        const int p = idx / RW, k = idx - p * RW;
+        if (p >= lo_p && p < hi_p) krec[idx] = s_rec[p * RS + k];
     }
-    // V runs (shared by slots: read-modify-write unless the whole tile is new)
-    const int vd = 2 * v_bits;
+    const bool whole = lo_p == 0 && hi_p == kTile;
     uint32_t* vrun = (uint32_t*)(tile + kTile * SK);
-    for (int idx = tid; idx < kHeadDim * vd; idx += 256) {
-        const int c = idx / vd, k = idx - c * vd;
-        const int lo_bit = 32 * k;
-        const int pa = max(lo_bit / v_bits, lo_p);
-        const int pb = min((lo_bit + 31) / v_bits, hi_p - 1);
-        uint32_t val = 0;
-        for (int p = pa; p <= pb; ++p) {
-            const uint32_t code = s_vc[p][c];
-            const int sh = p * v_bits - lo_bit;
-            val |= sh >= 0 ? (code << sh) : (code >> (-sh));
-        }
+    for (int idx = tid; idx < kHeadDim * VW; idx += 256) {
+        const int c = idx / VW, k = idx - c * VW;
+        const uint32_t val = s_run[c * VS + k];
         if (whole) vrun[idx] = val;
-        else if (pa <= pb) vrun[idx] |= val;
+        else if (val) vrun[idx] |= val;
     }
-    // scales
     float* scl = (float*)(tile + kTile * SK + kHeadDim * 8 * v_bits);
     if (tid >= lo_p && tid < hi_p) {
         scl[tid] = s_ks[tid];
@@ -260,7 +400,18 @@ hipError_t launch_quantize_pack(const kvq_geom& g, const uint16_t* k, const uint
     // a run of max_new slots starting anywhere touches at most ceil(max_new/64) + 1 tiles
     const int tiles = (max_new + kTile - 1) / kTile + 1;
     dim3 grid(tiles, g.n_kv_heads, n_seq);
-    hipLaunchKernelGGL(quantize_pack_kernel, grid, dim3(256), 0, st, k, v, stride_tok, stride_head, first_slot,
+    // records [64][words + 1] and runs [128][2 v_bits + 1] in dynamic LDS; beside the
+    // ~38 KB of static LDS the widest geometry (raw K, 16-bit V) needs ~72 KB per
+    // workgroup, which gfx950's 160 KB LDS holds once the launch limit is raised
+    const size_t dyn = (size_t)4 * (kTile * (k_record_bytes(g.k_budget) / 4 + 1) + kHeadDim * (2 * g.v_bits + 1));
+    static size_t dyn_set = 0;
+    if (dyn > dyn_set && dyn > 16384) {
+        const hipError_t e = hipFuncSetAttribute((const void*)quantize_pack_kernel,
+                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
+        if (e != hipSuccess) return e;
+        dyn_set = dyn;
+    }
+    hipLaunchKernelGGL(quantize_pack_kernel, grid, dim3(256), dyn, st, k, v, stride_tok, stride_head, first_slot,
                        n_new, src_row0, max_new, g.capacity_tokens, k_bits, k_sigma, v_sigma, cache, seq_byte_off,
                        g.rope_pairing, g.k_budget, g.v_bits);
     return hipGetLastError();
