@@ -25,11 +25,14 @@ namespace kvq {
 // coordinates; for a field every lane searches at the same width, and the K record
 // bits are gathered in registers and OR-ed into the LDS records word by word.
 constexpr int kRowDw = kHeadDim / 2 + 1;
-constexpr int kQWaves = 4;
+typedef __attribute__((address_space(3))) const float lds_cf32;  // LDS pointer (32-bit addresses)
+__device__ __forceinline__ uint32_t lds_off(lds_cf32* p) { return (uint32_t)(uintptr_t)p; }
+constexpr int kQWaves = 8;  // waves per workgroup
+constexpr int kQThreads = 64 * kQWaves;
 constexpr int kGroup = 4;   // K fields encoded side by side (independent searches)
 constexpr int kVGroup = 8;  // V coordinates encoded side by side
 
-__global__ __launch_bounds__(256) void quantize_pack_kernel(
+__global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(
     const uint16_t* __restrict__ kx, const uint16_t* __restrict__ vx, int64_t stride_tok, int64_t stride_head,
     const int64_t* __restrict__ first_slot, const int32_t* __restrict__ n_new, const int64_t* __restrict__ src_row0,
     int max_new, int64_t capacity, const uint8_t* __restrict__ k_bits, const float* __restrict__ k_sigma,
@@ -53,7 +56,7 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
 
     __shared__ uint32_t s_k[kTile * kRowDw], s_v[kTile * kRowDw];
     __shared__ float s_thr[510];
-    __shared__ float s_half[4][kTile];
+    __shared__ float s_quarter[kQWaves][kTile];
     __shared__ float s_ks[kTile], s_vs[kTile];
     // K order, field f: x = coordinate | width << 7 | bit offset << 12 | (later fields of
     // the same width) << 23, y = the block's sigma bits; padded so that reads of up to
@@ -74,8 +77,8 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
     if ((((uintptr_t)kx | (uintptr_t)vx) & 15) == 0 && ((stride_tok | stride_head) & 7) == 0) {
         const int j = tid & 15;  // 16-byte piece of a 256-byte row
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const int p = (tid >> 4) + 16 * i;
+        for (int i = 0; i < kTile * 16 / kQThreads; ++i) {
+            const int p = (tid >> 4) + (kQThreads / 16) * i;
             if (p >= lo_p && p < hi_p) {
                 const uint4 a = *(const uint4*)(ksrc + (row0 + p) * stride_tok + 8 * j);
                 const uint4 b = *(const uint4*)(vsrc + (row0 + p) * stride_tok + 8 * j);
@@ -92,8 +95,8 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
             s_v[p * kRowDw + lane] = *(const uint32_t*)(vsrc + (row0 + p) * stride_tok + 2 * lane);
         }
     }
-    for (int i = tid; i < 510; i += 256) s_thr[i] = c_thresholds[i];
-    for (int i = tid; i < kTile * RS + kHeadDim * VS; i += 256) s_dyn[i] = 0u;
+    for (int i = tid; i < 510; i += kQThreads) s_thr[i] = c_thresholds[i];
+    for (int i = tid; i < kTile * RS + kHeadDim * VS; i += kQThreads) s_dyn[i] = 0u;
     if (tid < kHeadDim) {
         const int blk = pairing == KVQ_PAIR_HALF ? (tid & (kMaxBlocks - 1)) : (tid >> 1);
         s_vsig[tid] = v_sigma[h * kMaxBlocks + blk];
@@ -142,26 +145,33 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
     }
     __syncthreads();
 
-    // ---- phase 1: token norms (lane = token)
+    // ---- phase 1: token norms (lane = token).  Waves 0-3 sum the squares of the K
+    // row's four 32-coordinate quarters, waves 4-7 those of V, each as the pairwise
+    // tree over its 16 coordinate pairs; the root adds them as (Q0 + Q1) + (Q2 + Q3),
+    // which is the balanced tree over all 64 pairs.
     {
-        const uint32_t* rows = wave < 2 ? s_k : s_v;
-        const uint32_t* r = rows + lane * kRowDw + 32 * (wave & 1);
-        float t[32];
+        const uint32_t* rows = wave < 4 ? s_k : s_v;
+        const uint32_t* r = rows + lane * kRowDw + 16 * (wave & 3);
+        float t[16];
 #pragma unroll
-        for (int k = 0; k < 32; ++k) {
+        for (int k = 0; k < 16; ++k) {
             const uint32_t pr = r[k];
             const float a = h2f(pr & 0xffffu), b = h2f(pr >> 16);
             t[k] = a * a + b * b;
         }
 #pragma unroll
-        for (int m = 1; m < 32; m <<= 1)
+        for (int m = 1; m < 16; m <<= 1)
 #pragma unroll
-            for (int k = 0; k < 32; k += 2 * m) t[k] = t[k] + t[k + m];
-        s_half[wave][lane] = t[0];
+            for (int k = 0; k < 16; k += 2 * m) t[k] = t[k] + t[k + m];
+        s_quarter[wave][lane] = t[0];
     }
     __syncthreads();
-    if (tid < kTile) s_ks[tid] = sqrtf(s_half[0][tid] + s_half[1][tid]);
-    else if (tid < 2 * kTile) s_vs[tid - kTile] = sqrtf(s_half[2][tid - kTile] + s_half[3][tid - kTile]);
+    if (tid < 2 * kTile) {
+        const int p = tid & (kTile - 1), q0 = tid < kTile ? 0 : 4;
+        const float r = sqrtf((s_quarter[q0][p] + s_quarter[q0 + 1][p]) + (s_quarter[q0 + 2][p] + s_quarter[q0 + 3][p]));
+        if (tid < kTile) s_ks[p] = r;
+        else s_vs[p] = r;
+    }
     __syncthreads();
 
     // ---- phase 2: codes (lane = token), K record bits gathered per word
@@ -169,43 +179,59 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
     {
         const float sk = s_ks[lane];
         const uint16_t* krow = (const uint16_t*)(s_k + lane * kRowDw);
-        const int f0 = s_range[wave], f1 = s_range[wave + 1];
-        int cur = f0 < f1 ? (int)((s_meta[f0].x >> 12) & 2047) >> 5 : 0;
+        // the field tables are the same for every lane: keep them in scalar registers
+        const int f0 = __builtin_amdgcn_readfirstlane(s_range[wave]);
+        const int f1 = __builtin_amdgcn_readfirstlane(s_range[wave + 1]);
+        int cur = f0 < f1 ? (int)((__builtin_amdgcn_readfirstlane(s_meta[f0].x) >> 12) & 2047) >> 5 : 0;
         uint32_t acc = 0u, nxt = 0u;
         for (int f = f0; f < f1;) {
             // up to kGroup fields of one width (the K order sorts by width) searched side by side
-            uint2 m[kGroup];
+            uint32_t mx[kGroup];
+            float sg[kGroup];
 #pragma unroll
-            for (int i = 0; i < kGroup; ++i) m[i] = s_meta[f + i];
-            const int wf = (m[0].x >> 7) & 31;
-            const int gn = min(min(kGroup, (int)(m[0].x >> 23) + 1), f1 - f);
+            for (int i = 0; i < kGroup; ++i) {
+                const uint2 m = s_meta[f + i];
+                mx[i] = __builtin_amdgcn_readfirstlane(m.x);
+                sg[i] = __uint_as_float(__builtin_amdgcn_readfirstlane(m.y));
+            }
+            const int wf = (mx[0] >> 7) & 31;
+            const int gn = min(min(kGroup, (int)(mx[0] >> 23) + 1), f1 - f);
             uint32_t code[kGroup];
             if (wf == 16) {
 #pragma unroll
-                for (int i = 0; i < kGroup; ++i) code[i] = krow[m[i].x & 127];
+                for (int i = 0; i < kGroup; ++i) code[i] = krow[mx[i] & 127];
             } else {
-                float x[kGroup], sg[kGroup];
+                // binary lifting on threshold addresses: t[i] points at the largest
+                // threshold found so far that the value reaches (the code's entry)
+                lds_cf32* thr = (lds_cf32*)(s_thr + KVQ_CB_OFF(wf));
+                float x[kGroup];
+                lds_cf32* t[kGroup];
 #pragma unroll
                 for (int i = 0; i < kGroup; ++i) {
-                    x[i] = h2f(krow[m[i].x & 127]);
-                    sg[i] = __uint_as_float(m[i].y);
-                    code[i] = 0u;
+                    x[i] = h2f(krow[mx[i] & 127]);
+                    t[i] = thr;
                 }
-                const float* thr = s_thr + KVQ_CB_OFF(wf);
                 for (int bit = 1 << (wf - 1); bit >= 1; bit >>= 1) {
+                    lds_cf32* c[kGroup];
+                    float a[kGroup];
 #pragma unroll
                     for (int i = 0; i < kGroup; ++i) {
-                        const uint32_t cand = code[i] + bit;
-                        const float a = sg[i] * thr[cand];
-                        const float b = sk * a;
-                        if (x[i] >= b) code[i] = cand;
+                        c[i] = t[i] + bit;
+                        a[i] = *c[i];
+                    }
+#pragma unroll
+                    for (int i = 0; i < kGroup; ++i) {
+                        const float b = sk * (sg[i] * a[i]);
+                        if (x[i] >= b) t[i] = c[i];
                     }
                 }
+#pragma unroll
+                for (int i = 0; i < kGroup; ++i) code[i] = (lds_off(t[i]) - lds_off(thr)) >> 2;
             }
 #pragma unroll
             for (int i = 0; i < kGroup; ++i) {
                 if (i < gn) {
-                    const int of = (m[i].x >> 12) & 2047;
+                    const int of = (mx[i] >> 12) & 2047;
                     const int k = of >> 5, sh = of & 31;
                     if (k != cur) {  // fields are consecutive in bits: the window moves by one word
                         if (valid && acc) atomicOr(&s_rec[lane * RS + cur], acc);
@@ -225,37 +251,56 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
         const float sv = s_vs[lane];
         const uint16_t* vrow = (const uint16_t*)(s_v + lane * kRowDw);
         const int bit0 = lane * v_bits, vk = bit0 >> 5, vsh = bit0 & 31;
-        const float* vthr = s_thr + KVQ_CB_OFF(v_bits);
-        for (int c0 = 32 * wave; c0 < 32 * wave + 32; c0 += kVGroup) {
+        lds_cf32* vthr = (lds_cf32*)(s_thr + KVQ_CB_OFF(v_bits));
+        constexpr int kVPer = kHeadDim / kQWaves;  // V coordinates per wave
+        // codes of G consecutive tokens (G * v_bits <= 32, G <= 16) are OR-ed across
+        // lanes into the group's first lane before the LDS update, so few lanes share a
+        // run word in one atomic
+        const int lg = v_bits == 1 ? 4 : v_bits == 2 ? 4 : v_bits <= 4 ? 3 : v_bits <= 8 ? 2 : 1;
+        const int G = 1 << lg;
+        const int gbits = G * v_bits;
+        for (int c0 = kVPer * wave; c0 < kVPer * wave + kVPer; c0 += kVGroup) {
             uint32_t code[kVGroup];
             if (v_bits == 16) {
 #pragma unroll
                 for (int i = 0; i < kVGroup; ++i) code[i] = vrow[c0 + i];
             } else {
                 float x[kVGroup], sg[kVGroup];
+                lds_cf32* t[kVGroup];
 #pragma unroll
                 for (int i = 0; i < kVGroup; ++i) {
                     x[i] = h2f(vrow[c0 + i]);
                     sg[i] = s_vsig[c0 + i];
-                    code[i] = 0u;
+                    t[i] = vthr;
                 }
                 for (int bit = 1 << (v_bits - 1); bit >= 1; bit >>= 1) {
+                    lds_cf32* c[kVGroup];
+                    float a[kVGroup];
 #pragma unroll
                     for (int i = 0; i < kVGroup; ++i) {
-                        const uint32_t cand = code[i] + bit;
-                        const float a = sg[i] * vthr[cand];
-                        const float b = sv * a;
-                        if (x[i] >= b) code[i] = cand;
+                        c[i] = t[i] + bit;
+                        a[i] = *c[i];
+                    }
+#pragma unroll
+                    for (int i = 0; i < kVGroup; ++i) {
+                        const float b = sv * (sg[i] * a[i]);
+                        if (x[i] >= b) t[i] = c[i];
                     }
                 }
-            }
-            if (valid) {
 #pragma unroll
-                for (int i = 0; i < kVGroup; ++i) {
-                    if (code[i]) {
-                        atomicOr(&s_run[(c0 + i) * VS + vk], code[i] << vsh);
-                        if (vsh + v_bits > 32) atomicOr(&s_run[(c0 + i) * VS + vk + 1], code[i] >> (32 - vsh));
-                    }
+                for (int i = 0; i < kVGroup; ++i) code[i] = (lds_off(t[i]) - lds_off(vthr)) >> 2;
+            }
+#pragma unroll
+            for (int i = 0; i < kVGroup; ++i) {
+                uint32_t u = valid ? code[i] : 0u;
+                u |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x101, 0xf, 0xf, true) << v_bits;
+                if (lg >= 2) u |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x102, 0xf, 0xf, true) << (2 * v_bits);
+                if (lg >= 3) u |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x104, 0xf, 0xf, true) << (4 * v_bits);
+                if (lg >= 4) u |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x108, 0xf, 0xf, true) << (8 * v_bits);
+                if (gbits < 32) u &= (1u << gbits) - 1u;
+                if ((lane & (G - 1)) == 0 && u) {
+                    atomicOr(&s_run[(c0 + i) * VS + vk], u << vsh);
+                    if (vsh + gbits > 32) atomicOr(&s_run[(c0 + i) * VS + vk + 1], u >> (32 - vsh));
                 }
             }
         }
@@ -264,13 +309,13 @@ __global__ __launch_bounds__(256) void quantize_pack_kernel(
 
     // ---- phase 3: the tile's records (valid slots), runs and scales
     uint32_t* krec = (uint32_t*)tile;
-    for (int idx = tid; idx < kTile * RW; idx += 256) {
+    for (int idx = tid; idx < kTile * RW; idx += kQThreads) {
         const int p = idx / RW, k = idx - p * RW;
         if (p >= lo_p && p < hi_p) krec[idx] = s_rec[p * RS + k];
     }
     const bool whole = lo_p == 0 && hi_p == kTile;
     uint32_t* vrun = (uint32_t*)(tile + kTile * SK);
-    for (int idx = tid; idx < kHeadDim * VW; idx += 256) {
+    for (int idx = tid; idx < kHeadDim * VW; idx += kQThreads) {
         const int c = idx / VW, k = idx - c * VW;
         const uint32_t val = s_run[c * VS + k];
         if (whole) vrun[idx] = val;
@@ -411,7 +456,7 @@ hipError_t launch_quantize_pack(const kvq_geom& g, const uint16_t* k, const uint
         if (e != hipSuccess) return e;
         dyn_set = dyn;
     }
-    hipLaunchKernelGGL(quantize_pack_kernel, grid, dim3(256), dyn, st, k, v, stride_tok, stride_head, first_slot,
+    hipLaunchKernelGGL(quantize_pack_kernel, grid, dim3(kQThreads), dyn, st, k, v, stride_tok, stride_head, first_slot,
                        n_new, src_row0, max_new, g.capacity_tokens, k_bits, k_sigma, v_sigma, cache, seq_byte_off,
                        g.rope_pairing, g.k_budget, g.v_bits);
     return hipGetLastError();
