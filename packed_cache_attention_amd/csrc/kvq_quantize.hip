@@ -18,19 +18,33 @@ namespace kvq {
 
 // Bulk quantize + pack, one workgroup per (sequence, KV head, tile), lane = token.
 // The tile's fp16 rows are staged in LDS (rows 65 dwords apart: a coordinate read
-// by 64 lanes touches distinct banks).  Norms: waves 0-1 form the two 64-leaf
-// halves of each K row's pairwise tree, waves 2-3 those of V (the root adds the
-// halves, as the tree does).  Codes: each wave takes a run of K-order fields
-// holding about a quarter of the record's bits, and a quarter of the V
-// coordinates; for a field every lane searches at the same width, and the K record
-// bits are gathered in registers and OR-ed into the LDS records word by word.
+// by 64 lanes touches distinct banks).  Norms: waves 0-3 sum the four 16-pair
+// quarters of each K row, waves 4-7 those of V.  Codes: each wave takes a run of
+// K-order fields (about an eighth of the work) and 16 of the V coordinates.  A
+// field's width is the same for every lane, so the binary lifting runs without
+// divergence, several fields side by side.  Each coordinate is read by one wave
+// only, which overwrites its fp16 value with the code; the store phase then builds
+// every K record word and V run word in one thread from those code rows.
 constexpr int kRowDw = kHeadDim / 2 + 1;
-typedef __attribute__((address_space(3))) const float lds_cf32;  // LDS pointer (32-bit addresses)
-__device__ __forceinline__ uint32_t lds_off(lds_cf32* p) { return (uint32_t)(uintptr_t)p; }
 constexpr int kQWaves = 8;  // waves per workgroup
 constexpr int kQThreads = 64 * kQWaves;
-constexpr int kGroup = 4;   // K fields encoded side by side (independent searches)
-constexpr int kVGroup = 8;  // V coordinates encoded side by side
+constexpr int kGroup = 4;   // K fields searched side by side
+constexpr int kVGroup = 8;  // V coordinates searched side by side
+
+// LDS byte address of a shared-memory object
+typedef __attribute__((address_space(3))) const float lds_cf32;
+__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_cf32*)p; }
+
+// One step of binary lifting on threshold addresses: `at` is the LDS byte address of
+// the threshold of the code found so far (the table start for code 0); the candidate
+// lies `inc` bytes further (4 << open bit position).  The step moves to the candidate
+// when the value reaches its product RN(s * RN(sig * t)); a NaN threshold never does.
+__device__ __forceinline__ uint32_t lift(uint32_t at, uint32_t inc, float x, float sig, float s) {
+    const uint32_t c = at + inc;
+    const float a = *(lds_cf32*)(uintptr_t)c;
+    const float b = s * (sig * a);
+    return x >= b ? c : at;
+}
 
 __global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(
     const uint16_t* __restrict__ kx, const uint16_t* __restrict__ vx, int64_t stride_tok, int64_t stride_head,
@@ -50,27 +64,25 @@ __global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(
 
     const int64_t SK = k_record_bytes(k_budget);
     const int64_t TB = tile_bytes(kHeadDim, k_budget, v_bits);
-    const int RW = (int)(SK / 4), RS = RW + 1;  // record words, LDS record stride (odd)
-    const int VW = 2 * v_bits, VS = VW + 1;     // run words, LDS run stride
+    const int RW = (int)(SK / 4);  // words per K record
+    const int VW = 2 * v_bits;     // words per V run
     uint8_t* tile = cache + seq_byte_off[s] + ((int64_t)h * (capacity / kTile) + tau) * TB;
 
     __shared__ uint32_t s_k[kTile * kRowDw], s_v[kTile * kRowDw];
-    __shared__ float s_thr[510];
+    __shared__ float s_thr[512];  // the codebook thresholds, then a NaN
     __shared__ float s_quarter[kQWaves][kTile];
     __shared__ float s_ks[kTile], s_vs[kTile];
-    // K order, field f: x = coordinate | width << 7 | bit offset << 12 | (later fields of
-    // the same width) << 23, y = the block's sigma bits; padded so that reads of up to
-    // kGroup fields from any f stay in the array
-    __shared__ uint2 s_meta[kHeadDim + kGroup];
+    // K order, field f: coordinate | width << 7 | bit offset << 12, and the block's
+    // sigma; padded so that a group read from any f stays in the arrays
+    __shared__ uint32_t s_fx[kHeadDim + kGroup];
+    __shared__ float s_fsig[kHeadDim + kGroup];
     __shared__ float s_vsig[kHeadDim];
-    __shared__ int s_range[kQWaves + 1];                  // wave w encodes fields [s_range[w], s_range[w+1])
-    extern __shared__ uint32_t s_dyn[];                  // records [64][RS], then runs [128][VS]
-    uint32_t* s_rec = s_dyn;
-    uint32_t* s_run = s_dyn + kTile * RS;
+    __shared__ int s_range[kQWaves + 1];  // wave w encodes fields [s_range[w], s_range[w+1])
+    __shared__ uint8_t s_wfirst[64];      // the field holding bit 32k of the record (nf: none)
 
     const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
 
-    // ---- phase 0: rows, thresholds, K order, zeroed records and runs
+    // ---- phase 0: rows, thresholds, K order
     const int64_t row0 = src_row0[s] + (tile0 - first);  // source row of slot 0 (only rows of valid slots are read)
     const uint16_t* ksrc = kx + (int64_t)h * stride_head;
     const uint16_t* vsrc = vx + (int64_t)h * stride_head;
@@ -96,7 +108,7 @@ __global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(
         }
     }
     for (int i = tid; i < 510; i += kQThreads) s_thr[i] = c_thresholds[i];
-    for (int i = tid; i < kTile * RS + kHeadDim * VS; i += kQThreads) s_dyn[i] = 0u;
+    if (tid == 0) s_thr[510] = __builtin_nanf("");
     if (tid < kHeadDim) {
         const int blk = pairing == KVQ_PAIR_HALF ? (tid & (kMaxBlocks - 1)) : (tid >> 1);
         s_vsig[tid] = v_sigma[h * kMaxBlocks + blk];
@@ -108,39 +120,40 @@ __global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(
         const int w = k_bits[h * kMaxBlocks + i];
         const float sig = k_sigma[h * kMaxBlocks + i];
         const unsigned long long below = (1ull << i) - 1ull;
-        int rank = 0, off = 0, after = 0;
+        int rank = 0, off = 0;
         for (int wc = 16; wc >= 1; --wc) {
             const unsigned long long mk = __ballot(w == wc);
             if (wc > w) { rank += __popcll(mk); off += 2 * wc * __popcll(mk); }
-            if (wc == w) {
-                rank += __popcll(mk & below);
-                off += 2 * wc * __popcll(mk & below);
-                after = __popcll(mk & ~below) - 1;  // same-width blocks ranked after this one
-            }
+            if (wc == w) { rank += __popcll(mk & below); off += 2 * wc * __popcll(mk & below); }
         }
         const int nf = 2 * __popcll(__ballot(w > 0));
+        s_wfirst[i] = (uint8_t)nf;
         if (w > 0) {
             const int pc = pairing == KVQ_PAIR_HALF ? i : 2 * i;
             const int qc = pairing == KVQ_PAIR_HALF ? i + kMaxBlocks : 2 * i + 1;
-            const uint32_t sb = __float_as_uint(sig);
-            s_meta[2 * rank] = make_uint2(pc | w << 7 | off << 12 | (2 * after + 1) << 23, sb);
-            s_meta[2 * rank + 1] = make_uint2(qc | w << 7 | (off + w) << 12 | (2 * after) << 23, sb);
+            s_fx[2 * rank] = pc | w << 7 | off << 12;
+            s_fx[2 * rank + 1] = qc | w << 7 | (off + w) << 12;
+            s_fsig[2 * rank] = s_fsig[2 * rank + 1] = sig;
+            // a word boundary inside a field (at most one: w <= 16) names its first field
+            const int kp = (off + 31) >> 5, kq = (off + w + 31) >> 5;
+            if (32 * kp < off + w) s_wfirst[kp] = (uint8_t)(2 * rank);
+            if (32 * kq < off + 2 * w) s_wfirst[kq] = (uint8_t)(2 * rank + 1);
         }
-        if (i < kGroup) s_meta[kHeadDim + i] = make_uint2(0u, 0u);
-        // split the fields into four runs of about a quarter of the record's bits each
+        if (i < kGroup) { s_fx[kHeadDim + i] = 0u; s_fsig[kHeadDim + i] = 0.f; }
+        // split the fields into runs of about an eighth of the work each, a field of
+        // width w costing about w + 2 lifting steps (its steps plus its share of the
+        // per-group work); run v starts at the first field whose cost prefix reaches
+        // v/8 of the total.  Field 2r (p) has prefix off + 4r, field 2r + 1 (q) has
+        // off + w + 4r + 2.
         int wsum = w;
 #pragma unroll
         for (int m = 1; m < 64; m <<= 1) wsum += __shfl_xor(wsum, m);
-        const int total = 2 * wsum;
-        // the field at rank 2r starts at `off`; run w starts at the first field whose
-        // offset reaches w/4 of the total (offsets increase with rank)
+        const int total = 2 * wsum + 2 * nf;
         for (int wv = 0; wv <= kQWaves; ++wv) {
             const int bound = (int)(((int64_t)total * wv + kQWaves - 1) / kQWaves);
-            const unsigned long long before = __ballot(w > 0 && off < bound);
-            // fields before the bound: 2 per block that starts before it, minus a q
-            // field that already starts past it
-            const unsigned long long qpast = __ballot(w > 0 && off < bound && off + w >= bound);
-            if (i == 0) s_range[wv] = wv == kQWaves ? nf : 2 * __popcll(before) - __popcll(qpast);
+            const unsigned long long pb = __ballot(w > 0 && off + 4 * rank < bound);
+            const unsigned long long qb = __ballot(w > 0 && off + w + 4 * rank + 2 < bound);
+            if (i == 0) s_range[wv] = wv == kQWaves ? nf : __popcll(pb) + __popcll(qb);
         }
     }
     __syncthreads();
@@ -174,152 +187,127 @@ __global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(
     }
     __syncthreads();
 
-    // ---- phase 2: codes (lane = token), K record bits gathered per word
+    // ---- phase 2: codes (lane = token), written over the lane's own fp16 values
     const bool valid = lane >= lo_p && lane < hi_p;
     {
+        // K: groups of kGroup consecutive fields.  Widths fall along the K order, so
+        // the group's first searched field is its widest (w0); a field of width w joins
+        // the lifting for its last w steps, where the open bit position is the same for
+        // every field of the group.  Width-16 fields keep the raw fp16 bits.
         const float sk = s_ks[lane];
-        const uint16_t* krow = (const uint16_t*)(s_k + lane * kRowDw);
-        // the field tables are the same for every lane: keep them in scalar registers
+        uint16_t* krow = (uint16_t*)(s_k + lane * kRowDw);
         const int f0 = __builtin_amdgcn_readfirstlane(s_range[wave]);
         const int f1 = __builtin_amdgcn_readfirstlane(s_range[wave + 1]);
-        int cur = f0 < f1 ? (int)((__builtin_amdgcn_readfirstlane(s_meta[f0].x) >> 12) & 2047) >> 5 : 0;
-        uint32_t acc = 0u, nxt = 0u;
-        for (int f = f0; f < f1;) {
-            // up to kGroup fields of one width (the K order sorts by width) searched side by side
-            uint32_t mx[kGroup];
-            float sg[kGroup];
+        const uint32_t thr0 = lds_addr(s_thr), nan_at = thr0 + 4u * 510u;
+        for (int f = f0; f < f1; f += kGroup) {
+            const int gn = min(kGroup, f1 - f);
+            uint32_t fx[kGroup], at[kGroup], tb[kGroup];
+            int ws[kGroup];  // search width (0: no search)
+            int w0 = 0;
+            float x[kGroup], sg[kGroup];
 #pragma unroll
             for (int i = 0; i < kGroup; ++i) {
-                const uint2 m = s_meta[f + i];
-                mx[i] = __builtin_amdgcn_readfirstlane(m.x);
-                sg[i] = __uint_as_float(__builtin_amdgcn_readfirstlane(m.y));
+                fx[i] = __builtin_amdgcn_readfirstlane(s_fx[f + i]);
+                sg[i] = s_fsig[f + i];
+                const int w = (fx[i] >> 7) & 31;
+                ws[i] = i < gn && w != 16 ? w : 0;
+                w0 = max(w0, ws[i]);
+                x[i] = h2f(krow[fx[i] & 127]);
+                tb[i] = thr0 + 4u * KVQ_CB_OFF(ws[i]);
+                at[i] = tb[i];
             }
-            const int wf = (mx[0] >> 7) & 31;
-            const int gn = min(min(kGroup, (int)(mx[0] >> 23) + 1), f1 - f);
-            uint32_t code[kGroup];
-            if (wf == 16) {
+            // a field with fewer than w0 bits waits at its table start, its candidate
+            // being the NaN, until its own top bit comes up
+            for (int sh = w0 - 1; sh >= 0; --sh) {
 #pragma unroll
-                for (int i = 0; i < kGroup; ++i) code[i] = krow[mx[i] & 127];
-            } else {
-                // binary lifting on threshold addresses: t[i] points at the largest
-                // threshold found so far that the value reaches (the code's entry)
-                lds_cf32* thr = (lds_cf32*)(s_thr + KVQ_CB_OFF(wf));
-                float x[kGroup];
-                lds_cf32* t[kGroup];
-#pragma unroll
-                for (int i = 0; i < kGroup; ++i) {
-                    x[i] = h2f(krow[mx[i] & 127]);
-                    t[i] = thr;
-                }
-                for (int bit = 1 << (wf - 1); bit >= 1; bit >>= 1) {
-                    lds_cf32* c[kGroup];
-                    float a[kGroup];
-#pragma unroll
-                    for (int i = 0; i < kGroup; ++i) {
-                        c[i] = t[i] + bit;
-                        a[i] = *c[i];
-                    }
-#pragma unroll
-                    for (int i = 0; i < kGroup; ++i) {
-                        const float b = sk * (sg[i] * a[i]);
-                        if (x[i] >= b) t[i] = c[i];
-                    }
-                }
-#pragma unroll
-                for (int i = 0; i < kGroup; ++i) code[i] = (lds_off(t[i]) - lds_off(thr)) >> 2;
+                for (int i = 0; i < kGroup; ++i) at[i] = lift(at[i], sh < ws[i] ? 4u << sh : nan_at - tb[i], x[i], sg[i], sk);
             }
 #pragma unroll
-            for (int i = 0; i < kGroup; ++i) {
-                if (i < gn) {
-                    const int of = (mx[i] >> 12) & 2047;
-                    const int k = of >> 5, sh = of & 31;
-                    if (k != cur) {  // fields are consecutive in bits: the window moves by one word
-                        if (valid && acc) atomicOr(&s_rec[lane * RS + cur], acc);
-                        acc = nxt;
-                        nxt = 0u;
-                        cur = k;
-                    }
-                    acc |= code[i] << sh;
-                    if (sh + wf > 32) nxt |= code[i] >> (32 - sh);
-                }
-            }
-            f += gn;
+            for (int i = 0; i < kGroup; ++i)
+                if (ws[i] > 0) krow[fx[i] & 127] = (uint16_t)((at[i] - tb[i]) >> 2);
         }
-        if (valid && acc) atomicOr(&s_rec[lane * RS + cur], acc);
-        if (valid && nxt) atomicOr(&s_rec[lane * RS + cur + 1], nxt);
 
-        const float sv = s_vs[lane];
-        const uint16_t* vrow = (const uint16_t*)(s_v + lane * kRowDw);
-        const int bit0 = lane * v_bits, vk = bit0 >> 5, vsh = bit0 & 31;
-        lds_cf32* vthr = (lds_cf32*)(s_thr + KVQ_CB_OFF(v_bits));
-        constexpr int kVPer = kHeadDim / kQWaves;  // V coordinates per wave
-        // codes of G consecutive tokens (G * v_bits <= 32, G <= 16) are OR-ed across
-        // lanes into the group's first lane before the LDS update, so few lanes share a
-        // run word in one atomic
-        const int lg = v_bits == 1 ? 4 : v_bits == 2 ? 4 : v_bits <= 4 ? 3 : v_bits <= 8 ? 2 : 1;
-        const int G = 1 << lg;
-        const int gbits = G * v_bits;
-        for (int c0 = kVPer * wave; c0 < kVPer * wave + kVPer; c0 += kVGroup) {
-            uint32_t code[kVGroup];
-            if (v_bits == 16) {
-#pragma unroll
-                for (int i = 0; i < kVGroup; ++i) code[i] = vrow[c0 + i];
-            } else {
+        // V: kVGroup coordinates at a time; slots outside the call get code 0 (16-bit
+        // V keeps the raw rows, whose invalid slots the run builder skips)
+        if (v_bits != 16) {
+            const float sv = s_vs[lane];
+            uint16_t* vrow = (uint16_t*)(s_v + lane * kRowDw);
+            const uint32_t vthr = thr0 + 4u * KVQ_CB_OFF(v_bits);
+            constexpr int kVPer = kHeadDim / kQWaves;
+            for (int c0 = kVPer * wave; c0 < kVPer * wave + kVPer; c0 += kVGroup) {
+                uint32_t at[kVGroup];
                 float x[kVGroup], sg[kVGroup];
-                lds_cf32* t[kVGroup];
 #pragma unroll
                 for (int i = 0; i < kVGroup; ++i) {
                     x[i] = h2f(vrow[c0 + i]);
                     sg[i] = s_vsig[c0 + i];
-                    t[i] = vthr;
+                    at[i] = vthr;
                 }
-                for (int bit = 1 << (v_bits - 1); bit >= 1; bit >>= 1) {
-                    lds_cf32* c[kVGroup];
-                    float a[kVGroup];
+                for (int sh = v_bits - 1; sh >= 0; --sh) {
 #pragma unroll
-                    for (int i = 0; i < kVGroup; ++i) {
-                        c[i] = t[i] + bit;
-                        a[i] = *c[i];
-                    }
-#pragma unroll
-                    for (int i = 0; i < kVGroup; ++i) {
-                        const float b = sv * (sg[i] * a[i]);
-                        if (x[i] >= b) t[i] = c[i];
-                    }
+                    for (int i = 0; i < kVGroup; ++i) at[i] = lift(at[i], 4u << sh, x[i], sg[i], sv);
                 }
 #pragma unroll
-                for (int i = 0; i < kVGroup; ++i) code[i] = (lds_off(t[i]) - lds_off(vthr)) >> 2;
-            }
-#pragma unroll
-            for (int i = 0; i < kVGroup; ++i) {
-                uint32_t u = valid ? code[i] : 0u;
-                u |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x101, 0xf, 0xf, true) << v_bits;
-                if (lg >= 2) u |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x102, 0xf, 0xf, true) << (2 * v_bits);
-                if (lg >= 3) u |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x104, 0xf, 0xf, true) << (4 * v_bits);
-                if (lg >= 4) u |= (uint32_t)__builtin_amdgcn_update_dpp(0, (int)u, 0x108, 0xf, 0xf, true) << (8 * v_bits);
-                if (gbits < 32) u &= (1u << gbits) - 1u;
-                if ((lane & (G - 1)) == 0 && u) {
-                    atomicOr(&s_run[(c0 + i) * VS + vk], u << vsh);
-                    if (vsh + gbits > 32) atomicOr(&s_run[(c0 + i) * VS + vk + 1], u >> (32 - vsh));
-                }
+                for (int i = 0; i < kVGroup; ++i) vrow[c0 + i] = valid ? (uint16_t)((at[i] - vthr) >> 2) : (uint16_t)0;
             }
         }
     }
     __syncthreads();
 
     // ---- phase 3: the tile's records (valid slots), runs and scales
+    // K record word k of slot `lane`: the fields from s_wfirst[k] on that start
+    // before bit 32k + 32, each field's code shifted to its offset
     uint32_t* krec = (uint32_t*)tile;
-    for (int idx = tid; idx < kTile * RW; idx += kQThreads) {
-        const int p = idx / RW, k = idx - p * RW;
-        if (p >= lo_p && p < hi_p) krec[idx] = s_rec[p * RS + k];
+    {
+        const uint16_t* krow = (const uint16_t*)(s_k + lane * kRowDw);
+        const int nf = __builtin_amdgcn_readfirstlane(s_range[kQWaves]);
+        for (int k = wave; k < RW; k += kQWaves) {
+            const int lo = 32 * k;
+            uint32_t val = 0u;
+            for (int f = __builtin_amdgcn_readfirstlane(s_wfirst[k]); f < nf; f += kGroup) {
+                uint32_t fx[kGroup], code[kGroup];
+#pragma unroll
+                for (int i = 0; i < kGroup; ++i) fx[i] = __builtin_amdgcn_readfirstlane(s_fx[f + i]);
+#pragma unroll
+                for (int i = 0; i < kGroup; ++i) code[i] = krow[fx[i] & 127];
+                bool done = false;
+#pragma unroll
+                for (int i = 0; i < kGroup; ++i) {
+                    const int of = (fx[i] >> 12) & 2047;
+                    if (f + i >= nf || of >= lo + 32) done = true;
+                    if (!done) val |= of >= lo ? code[i] << (of - lo) : code[i] >> (lo - of);
+                }
+                if (done) break;
+            }
+            if (valid) krec[lane * RW + k] = val;
+        }
     }
     const bool whole = lo_p == 0 && hi_p == kTile;
     uint32_t* vrun = (uint32_t*)(tile + kTile * SK);
+    // one thread per run word; a wave's 64 lanes take one word index k of 64
+    // coordinates, so the slots involved are the same in every lane and the code
+    // reads of one slot are 64 neighbouring bytes
     for (int idx = tid; idx < kHeadDim * VW; idx += kQThreads) {
-        const int c = idx / VW, k = idx - c * VW;
-        const uint32_t val = s_run[c * VS + k];
-        if (whole) vrun[idx] = val;
-        else if (val) vrun[idx] |= val;
+        const int c = idx & (kHeadDim - 1), k = __builtin_amdgcn_readfirstlane(idx >> 7);
+        uint32_t val = 0u;
+        if (v_bits == 16) {
+            const uint16_t* col = (const uint16_t*)s_v + c;
+#pragma unroll
+            for (int e = 0; e < 2; ++e) {
+                const int p = 2 * k + e;
+                if (p >= lo_p && p < hi_p) val |= (uint32_t)col[p * 2 * kRowDw] << (16 * e);
+            }
+        } else {
+            // word k holds bits [32k, 32k + 32): slots plo..phi, slot p at bit p*v_bits - 32k
+            const int plo = 32 * k / v_bits, phi = min(kTile - 1, (32 * k + 31) / v_bits);
+            const uint16_t* col = (const uint16_t*)s_v + c;
+            const int sh0 = plo * v_bits - 32 * k;  // in (-v_bits, 0]
+            val = (uint32_t)col[plo * 2 * kRowDw] >> -sh0;
+            for (int p = plo + 1; p <= phi; ++p) val |= (uint32_t)col[p * 2 * kRowDw] << (p * v_bits - 32 * k);
+        }
+        uint32_t* dst = vrun + c * VW + k;
+        if (whole) *dst = val;
+        else if (val) *dst |= val;
     }
     float* scl = (float*)(tile + kTile * SK + kHeadDim * 8 * v_bits);
     if (tid >= lo_p && tid < hi_p) {
@@ -445,18 +433,7 @@ hipError_t launch_quantize_pack(const kvq_geom& g, const uint16_t* k, const uint
     // a run of max_new slots starting anywhere touches at most ceil(max_new/64) + 1 tiles
     const int tiles = (max_new + kTile - 1) / kTile + 1;
     dim3 grid(tiles, g.n_kv_heads, n_seq);
-    // records [64][words + 1] and runs [128][2 v_bits + 1] in dynamic LDS; beside the
-    // ~38 KB of static LDS the widest geometry (raw K, 16-bit V) needs ~72 KB per
-    // workgroup, which gfx950's 160 KB LDS holds once the launch limit is raised
-    const size_t dyn = (size_t)4 * (kTile * (k_record_bytes(g.k_budget) / 4 + 1) + kHeadDim * (2 * g.v_bits + 1));
-    static size_t dyn_set = 0;
-    if (dyn > dyn_set && dyn > 16384) {
-        const hipError_t e = hipFuncSetAttribute((const void*)quantize_pack_kernel,
-                                                 hipFuncAttributeMaxDynamicSharedMemorySize, (int)dyn);
-        if (e != hipSuccess) return e;
-        dyn_set = dyn;
-    }
-    hipLaunchKernelGGL(quantize_pack_kernel, grid, dim3(kQThreads), dyn, st, k, v, stride_tok, stride_head, first_slot,
+    hipLaunchKernelGGL(quantize_pack_kernel, grid, dim3(kQThreads), 0, st, k, v, stride_tok, stride_head, first_slot,
                        n_new, src_row0, max_new, g.capacity_tokens, k_bits, k_sigma, v_sigma, cache, seq_byte_off,
                        g.rope_pairing, g.k_budget, g.v_bits);
     return hipGetLastError();
