@@ -80,7 +80,8 @@ __global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(
     __shared__ int s_range[kQWaves + 1];  // wave w encodes fields [s_range[w], s_range[w+1])
     __shared__ uint8_t s_wfirst[64];      // the field holding bit 32k of the record (nf: none)
 
-    const int tid = threadIdx.x, lane = tid & 63, wave = tid >> 6;
+    const int tid = threadIdx.x, lane = tid & 63;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform in the wave
 
     // ---- phase 0: rows, thresholds, K order
     const int64_t row0 = src_row0[s] + (tile0 - first);  // source row of slot 0 (only rows of valid slots are read)
@@ -264,20 +265,25 @@ __global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(
         for (int k = wave; k < RW; k += kQWaves) {
             const int lo = 32 * k;
             uint32_t val = 0u;
-            for (int f = __builtin_amdgcn_readfirstlane(s_wfirst[k]); f < nf; f += kGroup) {
-                uint32_t fx[kGroup], code[kGroup];
-#pragma unroll
-                for (int i = 0; i < kGroup; ++i) fx[i] = __builtin_amdgcn_readfirstlane(s_fx[f + i]);
-#pragma unroll
-                for (int i = 0; i < kGroup; ++i) code[i] = krow[fx[i] & 127];
+            int f = __builtin_amdgcn_readfirstlane(s_wfirst[k]);
+            if (f < nf) {
+                // the field holding bit 32k starts at or before it; the rest start inside
+                const uint32_t fx0 = __builtin_amdgcn_readfirstlane(s_fx[f]);
+                val = (uint32_t)krow[fx0 & 127] >> (lo - (int)((fx0 >> 12) & 2047));
                 bool done = false;
+                for (++f; f < nf && !done; f += kGroup) {
+                    uint32_t fx[kGroup], code[kGroup];
 #pragma unroll
-                for (int i = 0; i < kGroup; ++i) {
-                    const int of = (fx[i] >> 12) & 2047;
-                    if (f + i >= nf || of >= lo + 32) done = true;
-                    if (!done) val |= of >= lo ? code[i] << (of - lo) : code[i] >> (lo - of);
+                    for (int i = 0; i < kGroup; ++i) fx[i] = __builtin_amdgcn_readfirstlane(s_fx[f + i]);
+#pragma unroll
+                    for (int i = 0; i < kGroup; ++i) code[i] = krow[fx[i] & 127];
+#pragma unroll
+                    for (int i = 0; i < kGroup; ++i) {
+                        const int of = (fx[i] >> 12) & 2047;
+                        if (f + i >= nf || of >= lo + 32) done = true;
+                        if (!done) val |= code[i] << (of - lo);
+                    }
                 }
-                if (done) break;
             }
             if (valid) krec[lane * RW + k] = val;
         }
