@@ -222,6 +222,45 @@ def test_small_appends_match_bulk(case):
     np.testing.assert_array_equal(cache.cpu().numpy(), oc)
 
 
+BULK_VIEW_CASES = [(c[0], c[5], c[6], c[7]) for c in CASES if c[0] in
+                   ("k3v3-ragged", "k8v8-max", "konly-v16", "k16v16-pass", "interleaved")]
+
+
+@pytest.mark.parametrize("align", ["4byte", "16byte-oddstride"])
+@pytest.mark.parametrize("case", BULK_VIEW_CASES, ids=[c[0] for c in BULK_VIEW_CASES])
+def test_bulk_quantize_from_strided_unaligned_rows(case, align):
+    """Bulk quantize+pack of 150 tokens starting mid-tile (slot 70: a partial first
+    tile, a whole tile, a partial last tile) from K/V views whose rows are only 4-byte
+    aligned or whose token/head strides are not multiples of 8 elements gives the
+    oracle's bytes for the whole sequence."""
+    name, kb, vb, pairing = case
+    say("bulk from views %s %s" % (name, align))
+    H, n0, n1 = 2, 70, 150
+    wl = synth.Workload("views-" + name, 1, 4, H, 1e6, (0,), kb, vb, "decay")
+    K, V, q = synth.gen_layer(wl.with_lens([n0 + n1]), 0, 0, n_tok=n0 + n1, seed=21)
+    r = run_batch([(K[:n0], V[:n0], q)], kb, vb, 256, pairing=pairing, check_attn=False)
+    g, cache, off = r["g"], r["cache"], r["off"]
+    lead = 2 if align == "4byte" else 8   # element offset of coordinate 0 within a padded row
+    width = 134 if align == "4byte" else 140
+    kb_ = torch.zeros(n0 + n1, H + 1, width, dtype=torch.float16, device="cuda")
+    vb_ = torch.zeros_like(kb_)
+    kb_[:, :H, lead:lead + 128] = K.cuda()
+    vb_[:, :H, lead:lead + 128] = V.cuda()
+    kv, vv = kb_[:, :H, lead:lead + 128], vb_[:, :H, lead:lead + 128]
+    if align == "4byte":
+        assert kv.data_ptr() % 16 != 0 and kv.data_ptr() % 4 == 0
+    else:
+        assert kv.data_ptr() % 16 == 0 and kv.stride(0) % 8 != 0
+    assert kv.stride(1) % 8 != 0 or kv.stride(0) % 8 != 0
+    first = torch.tensor([n0], dtype=torch.int64, device="cuda")
+    nn = torch.tensor([n1], dtype=torch.int32, device="cuda")
+    src = torch.tensor([n0], dtype=torch.int64, device="cuda")
+    kvq.quantize_pack(g, kv, vv, first, nn, src, n1, r["kbits"], r["ksig"], r["vsig"], cache, off)
+    oc = np.zeros_like(r["oc"])
+    oracle.quantize_pack(r["ogeom"], oc, K.numpy(), V.numpy(), 0, r["ob"], r["osig"], r["ovsig"])
+    np.testing.assert_array_equal(cache.cpu().numpy(), oc)
+
+
 @pytest.mark.parametrize("kernel", [kvq.DECODE_GENERIC, kvq.DECODE_MFMA])
 def test_split_count_invariance(kernel):
     """Any split of the token axis gives the same output up to fp32 re-association (1e-5 of max|o|)."""
