@@ -133,48 +133,77 @@ __device__ __forceinline__ double u128_to_f64(uint64_t lo, uint64_t hi) {
     return ldexp((double)keep, drop);
 }
 
-// one wave per unit; lane i = block i
-__global__ __launch_bounds__(64) void allocate_kernel(const uint64_t* __restrict__ energy, int nb, int budget,
-                                                     int mode, uint8_t* __restrict__ bits,
-                                                     float* __restrict__ sigma) {
-    const int u = blockIdx.x, i = threadIdx.x;
-    const bool act = i < nb;
-    const uint64_t lo = act ? energy[((int64_t)u * nb + i) * 2] : 0ull;
-    const uint64_t hi = act ? energy[((int64_t)u * nb + i) * 2 + 1] : 0ull;
-    const double E = ldexp(u128_to_f64(lo, hi), -48);
-    uint64_t tlo = lo, thi = hi;
-    for (int off = 32; off >= 1; off >>= 1) {
-        const uint64_t olo = __shfl_xor(tlo, off), ohi = __shfl_xor(thi, off);
-        tlo += olo;
-        thi += ohi + (tlo < olo ? 1ull : 0ull);
-    }
-    const double Etot = ldexp(u128_to_f64(tlo, thi), -48);
-    int b = 0;
-    if (budget == 16 * nb) {
-        b = 16;
-    } else if (mode == KVQ_UNIFORM) {
-        b = budget / nb;
-    } else {
-        for (int step = 0; step < budget; ++step) {
-            double g = (act && b < 8) ? E * (double)c_gain_dd[b] : -1.0;
-            int idx = i;
-            for (int off = 32; off >= 1; off >>= 1) {
-                const double og = __shfl_xor(g, off);
-                const int oi = __shfl_xor(idx, off);
-                if (og > g || (og == g && oi < idx)) { g = og; idx = oi; }
-            }
-            if (idx == i) ++b;
+// One workgroup per unit.  Wave 0 (lane i = block i) forms E_i, E_tot and sigma.
+// Greedy: step after step the block with the largest marginal gain E_i * dD[b_i]
+// (lowest index on ties) gains one bit.  A block's gains fall strictly with its
+// width (dD strictly decreasing; all zero when E_i = 0), so the candidate (i, w) is
+// always taken after (i, w - 1), and the greedy order is the order of all 8 nb
+// candidates (i, w) by gain descending, then block, then width ascending: the first
+// `budget` of them are taken, and b_i counts block i's.  Thread t holds candidate
+// (t / 8, t % 8) and finds its rank in that order by comparing against every other.
+constexpr int kAllocThreads = 8 * 64;
+
+__global__ __launch_bounds__(kAllocThreads) void allocate_kernel(const uint64_t* __restrict__ energy, int nb,
+                                                                int budget, int mode, uint8_t* __restrict__ bits,
+                                                                float* __restrict__ sigma) {
+    __shared__ double s_E[64];
+    __shared__ uint64_t s_key[kAllocThreads];
+    const int u = blockIdx.x, tid = threadIdx.x;
+    const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (wave == 0) {
+        const int i = tid;
+        const bool act = i < nb;
+        const uint64_t lo = act ? energy[((int64_t)u * nb + i) * 2] : 0ull;
+        const uint64_t hi = act ? energy[((int64_t)u * nb + i) * 2 + 1] : 0ull;
+        const double E = ldexp(u128_to_f64(lo, hi), -48);
+        uint64_t tlo = lo, thi = hi;
+        for (int off = 32; off >= 1; off >>= 1) {
+            const uint64_t olo = __shfl_xor(tlo, off), ohi = __shfl_xor(thi, off);
+            tlo += olo;
+            thi += ohi + (tlo < olo ? 1ull : 0ull);
+        }
+        const double Etot = ldexp(u128_to_f64(tlo, thi), -48);
+        s_E[i] = E;
+        if (act) {
+            sigma[(int64_t)u * nb + i] = Etot > 0.0 ? (float)sqrt(E / (2.0 * Etot)) : 0.0f;
+            if (budget == 16 * nb) bits[(int64_t)u * nb + i] = 16;
+            else if (mode == KVQ_UNIFORM) bits[(int64_t)u * nb + i] = (uint8_t)(budget / nb);
         }
     }
-    if (act) {
-        bits[(int64_t)u * nb + i] = (uint8_t)b;
-        sigma[(int64_t)u * nb + i] = Etot > 0.0 ? (float)sqrt(E / (2.0 * Etot)) : 0.0f;
+    if (budget == 16 * nb || mode == KVQ_UNIFORM) return;  // uniform over the workgroup
+    __syncthreads();
+    const int i = tid >> 3, w = tid & 7;
+    const bool act = i < nb;
+    // gains are >= 0, so their bit patterns order like the values; candidates of
+    // absent blocks get gain 0 and the largest indices, so they precede nobody
+    const double gain = act ? s_E[i] * (double)c_gain_dd[w] : 0.0;
+    const uint64_t key = __double_as_longlong(gain);
+    s_key[tid] = key;
+    __syncthreads();
+    // rank = #{j : key_j > key, or key_j == key and j < tid}; indices j of other waves
+    // are all below or all above this wave's, only its own 64 need the index test
+    int rank = 0;
+    const int lo_j = 64 * wave;
+    for (int j = 0; j < lo_j; j += 2) {
+        const uint64_t a = s_key[j], b2 = s_key[j + 1];
+        rank += (a >= key) + (b2 >= key);
     }
+    for (int j = lo_j; j < lo_j + 64; ++j) {
+        const uint64_t a = s_key[j];
+        rank += (a > key || (a == key && j < tid)) ? 1 : 0;
+    }
+    for (int j = lo_j + 64; j < kAllocThreads; j += 2) {
+        const uint64_t a = s_key[j], b2 = s_key[j + 1];
+        rank += (a > key) + (b2 > key);
+    }
+    const unsigned long long taken = __ballot(rank < budget);
+    if (act && w == 0) bits[(int64_t)u * nb + i] = (uint8_t)__popcll((taken >> (tid & 56)) & 0xffull);
 }
 
 hipError_t launch_allocate(const uint64_t* energy, int n_units, int nb, int budget, int mode, uint8_t* bits,
                            float* sigma, hipStream_t st) {
-    hipLaunchKernelGGL(allocate_kernel, dim3(n_units), dim3(64), 0, st, energy, nb, budget, mode, bits, sigma);
+    hipLaunchKernelGGL(allocate_kernel, dim3(n_units), dim3(kAllocThreads), 0, st, energy, nb, budget, mode, bits,
+                       sigma);
     return hipGetLastError();
 }
 

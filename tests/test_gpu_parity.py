@@ -60,6 +60,37 @@ def test_energy_and_allocation_bit_exact(d, pairing):
             np.testing.assert_array_equal(sig.cpu().numpy().view(np.uint32), os_.view(np.uint32))
 
 
+@pytest.mark.parametrize("d", [16, 128])
+def test_allocation_ties_and_zero_energies(d):
+    """Energies with many exact ties (equal blocks, blocks whose gains collide across
+    widths at powers of two), zero-energy blocks and 128-bit values: widths and
+    scales equal the oracle's greedy at every budget."""
+    say("alloc ties d=%d" % d)
+    nb, H = d // 2, 6
+    r = np.random.default_rng(7 + d)
+    e = np.zeros((H, nb, 2), np.uint64)
+    base = r.integers(1, 1 << 40, size=4, dtype=np.uint64)
+    for h in range(H):
+        pick = r.integers(0, 4, size=nb)
+        e[h, :, 0] = base[pick]                     # only 4 distinct values: ties everywhere
+        e[h, r.random(nb) < 0.25, 0] = 0            # zero-energy blocks
+        if h % 2:
+            e[h, ::3, 0] <<= np.uint64(r.integers(0, 20))  # equal up to a power of two
+        if h == 5:
+            e[h, :, 1] = r.integers(0, 4, size=nb, dtype=np.uint64)  # values above 2^64
+    if H > 0:
+        e[0] = 0                                    # an all-zero unit
+    g = kvq.geom(H, 0, 3, 0, head_dim=d)
+    ed = torch.from_numpy(e.view(np.int64)).cuda()
+    for budget in sorted(set([0, 1, 2, nb - 1, nb, nb + 1, 3 * nb, 5 * nb + 3, 8 * nb - 1, 8 * nb])):
+        bits = torch.empty(H, nb, dtype=torch.uint8, device="cuda")
+        sig = torch.empty(H, nb, dtype=torch.float32, device="cuda")
+        kvq.allocate_bits(g, ed, int(budget), kvq.GREEDY, bits, sig)
+        ob, os_ = oracle.allocate(e, int(budget), oracle.GREEDY)
+        np.testing.assert_array_equal(bits.cpu().numpy(), ob, err_msg="budget %d" % budget)
+        np.testing.assert_array_equal(sig.cpu().numpy().view(np.uint32), os_.view(np.uint32))
+
+
 def test_energy_accumulates_exactly_with_strides():
     say("energy strided")
     H, d = 4, 128
