@@ -207,24 +207,47 @@ __global__ __launch_bounds__(kMergeCols * kMergeGroups) void merge_kernel(const 
         }
         M = mx;
     }
-    __shared__ float s_m[kMergeGroups][kMergeCols], s_l[kMergeGroups][kMergeCols], s_a[kMergeGroups][kMergeCols];
-    s_m[sg][tid % kMergeCols] = M;
-    s_l[sg][tid % kMergeCols] = L;
-    s_a[sg][tid % kMergeCols] = A;
+    // the wave's two split groups (lanes l and l ^ 32 share a column) first, then the
+    // 16 waves' results through LDS, each half of wave 0 taking eight of them
+    {
+        const float oM = __shfl_xor(M, 32), oL = __shfl_xor(L, 32), oA = __shfl_xor(A, 32);
+        const float Mx = fmaxf(M, oM);
+        if (Mx != -INFINITY) {
+            const float a = exp2f(M - Mx), b = exp2f(oM - Mx);
+            L = a * L + b * oL;
+            A = a * A + b * oA;
+        }
+        M = Mx;
+    }
+    constexpr int kWavesM = kMergeGroups / 2;
+    __shared__ float s_m[kWavesM][kMergeCols], s_l[kWavesM][kMergeCols], s_a[kWavesM][kMergeCols];
+    const int wv = tid / 64, cc = tid % kMergeCols;
+    if ((tid & 63) < kMergeCols) {
+        s_m[wv][cc] = M;
+        s_l[wv][cc] = L;
+        s_a[wv][cc] = A;
+    }
     __syncthreads();
-    if (sg == 0) {
-        const int cc = tid % kMergeCols;
+    if (wv == 0) {
+        const int k0 = (tid / kMergeCols) * (kWavesM / 2);
         float Mt = -INFINITY;
-        for (int k = 0; k < kMergeGroups; ++k) Mt = fmaxf(Mt, s_m[k][cc]);
+        for (int k = k0; k < k0 + kWavesM / 2; ++k) Mt = fmaxf(Mt, s_m[k][cc]);
         float Lt = 0.f, At = 0.f;
         if (Mt != -INFINITY) {
-            for (int k = 0; k < kMergeGroups; ++k) {
+            for (int k = k0; k < k0 + kWavesM / 2; ++k) {
                 const float a = exp2f(s_m[k][cc] - Mt);
                 Lt += a * s_l[k][cc];
                 At += a * s_a[k][cc];
             }
         }
-        out[row * kHeadDim + c] = Lt > 0.f ? At / Lt : 0.f;
+        const float oM = __shfl_xor(Mt, 32), oL = __shfl_xor(Lt, 32), oA = __shfl_xor(At, 32);
+        const float Mx = fmaxf(Mt, oM);
+        if (Mx != -INFINITY) {
+            const float a = exp2f(Mt - Mx), b = exp2f(oM - Mx);
+            Lt = a * Lt + b * oL;
+            At = a * At + b * oA;
+        }
+        if (tid < kMergeCols) out[row * kHeadDim + c] = Lt > 0.f ? At / Lt : 0.f;
     }
 }
 
