@@ -12,19 +12,12 @@ namespace kvq {
 // Block energy
 // ---------------------------------------------------------------------------
 // A binary16 pattern with exponent field e and fraction m is M * 2^(e-25) with
-// M = 1024 + m (e >= 1), or m * 2^-24 (e = 0).  Its square is M^2 << (2e - 2)
-// units of 2^-48 (M^2 << 0 for e = 0): an integer below 2^82, accumulated in a
-// 128-bit (lo, hi) pair.
-__device__ __forceinline__ void acc_square(uint32_t h, uint64_t& lo, uint64_t& hi) {
-    const uint32_t e = (h >> 10) & 31u, m = h & 1023u;
-    const uint64_t M = e ? (1024u | m) : m;
-    const uint32_t sh = e ? 2u * e - 2u : 0u;
-    const uint64_t sq = M * M;
-    const uint64_t l = sq << sh;
-    const uint64_t u = sh > 42u ? (sq >> (64u - sh)) : 0ull;
-    lo += l;
-    hi += u + (lo < l ? 1ull : 0ull);
-}
+// M = 1024 + m (e >= 1), or m * 2^-24 (e = 0).  Its square is M^2 << sh(e) units of
+// 2^-48, sh(e) = max(2e - 2, 0): an integer below 2^82.  A workgroup sums M^2 per
+// (coordinate, exponent) in 32-bit LDS counters (M^2 < 2^22 and at most 1024 rows
+// per workgroup keep every counter below 2^32), then forms each coordinate's
+// 128-bit total as the sum of counter << sh(e) -- exact, and a handful of
+// instructions per element instead of a 128-bit add.
 
 // 128-bit add of (alo, ahi) into a (lo, hi) pair in global memory with two 64-bit
 // atomics: the carry out of the low word is forwarded to the high word, so the
@@ -35,80 +28,101 @@ __device__ __forceinline__ void atomic_add_u128(uint64_t* p, uint64_t alo, uint6
     if (ahi + carry) atomicAdd((unsigned long long*)(p + 1), (unsigned long long)(ahi + carry));
 }
 
-// grid: (n_heads, row blocks); block: 256 threads = 4 row lanes x 64 coordinate pairs.
-// Thread (r, j) accumulates coordinates 2j, 2j+1 of rows r, r+4, ... of its row range.
-__global__ __launch_bounds__(256) void block_energy_kernel(const uint16_t* __restrict__ x, int64_t n_tok,
+constexpr int kEnergyMaxRows = 1024;  // rows per workgroup (keeps the 32-bit counters exact)
+constexpr int kHistStride = 33;       // counters per coordinate: 32 exponents + 1 (bank spread)
+
+__device__ __forceinline__ void hist_add(uint32_t* hist_c, uint32_t h) {
+    const uint32_t e = (h >> 10) & 31u, m = h & 1023u;
+    const uint32_t M = e ? (1024u | m) : m;
+    atomicAdd(hist_c + e, M * M);
+}
+
+// grid: (n_heads, row blocks); block: 1024 threads = 16 row lanes x 64 coordinate
+// pairs.  Thread (r, j) reads coordinates 2j, 2j+1 of rows r, r+16, ... of its row
+// range, sixteen rows per batch.  Few, large workgroups: every workgroup ends in one
+// 128-bit atomic per block, and those atomics all meet in the head's 64 counters.
+constexpr int kEnergyRowLanes = 16;
+constexpr int kEnergyThreads = 64 * kEnergyRowLanes;
+
+__global__ __launch_bounds__(kEnergyThreads) void block_energy_kernel(const uint16_t* __restrict__ x, int64_t n_tok,
                                                           int64_t stride_tok, int64_t stride_head, int d,
                                                           int pairing, int64_t rows_per_block,
                                                           uint64_t* __restrict__ energy) {
+    __shared__ uint32_t s_hist[kHeadDim * kHistStride];
+    __shared__ uint64_t s_lo[kHeadDim], s_hi[kHeadDim];
     const int h = blockIdx.x;
     const int j = threadIdx.x & 63;
-    const int r = threadIdx.x >> 6;
+    const int r = threadIdx.x >> 6;  // row lane
     const int npairs = d >> 1;
+    for (int i = threadIdx.x; i < kHeadDim * kHistStride; i += kEnergyThreads) s_hist[i] = 0u;
+    __syncthreads();
     const int64_t row0 = (int64_t)blockIdx.y * rows_per_block;
     const int64_t row1 = min(row0 + rows_per_block, n_tok);
-    uint64_t lo0 = 0, hi0 = 0, lo1 = 0, hi1 = 0;
     if (j < npairs) {
         const uint16_t* base = x + (int64_t)h * stride_head + 2 * j;
+        uint32_t* h0 = s_hist + (2 * j) * kHistStride;
+        uint32_t* h1 = h0 + kHistStride;
         int64_t t = row0 + r;
-        // four independent rows in flight per iteration
-        for (; t + 12 < row1; t += 16) {
-            uint32_t w0 = *(const uint32_t*)(base + t * stride_tok);
-            uint32_t w1 = *(const uint32_t*)(base + (t + 4) * stride_tok);
-            uint32_t w2 = *(const uint32_t*)(base + (t + 8) * stride_tok);
-            uint32_t w3 = *(const uint32_t*)(base + (t + 12) * stride_tok);
-            acc_square(w0 & 0xffffu, lo0, hi0); acc_square(w0 >> 16, lo1, hi1);
-            acc_square(w1 & 0xffffu, lo0, hi0); acc_square(w1 >> 16, lo1, hi1);
-            acc_square(w2 & 0xffffu, lo0, hi0); acc_square(w2 >> 16, lo1, hi1);
-            acc_square(w3 & 0xffffu, lo0, hi0); acc_square(w3 >> 16, lo1, hi1);
+        constexpr int RL = kEnergyRowLanes;
+        for (; t + 15 * RL < row1; t += 16 * RL) {
+            uint32_t w[16];
+#pragma unroll
+            for (int k = 0; k < 16; ++k) w[k] = *(const uint32_t*)(base + (t + RL * k) * stride_tok);
+#pragma unroll
+            for (int k = 0; k < 16; ++k) { hist_add(h0, w[k] & 0xffffu); hist_add(h1, w[k] >> 16); }
         }
-        for (; t < row1; t += 4) {
-            uint32_t w0 = *(const uint32_t*)(base + t * stride_tok);
-            acc_square(w0 & 0xffffu, lo0, hi0); acc_square(w0 >> 16, lo1, hi1);
+        for (; t + 3 * RL < row1; t += 4 * RL) {
+            uint32_t w[4];
+#pragma unroll
+            for (int k = 0; k < 4; ++k) w[k] = *(const uint32_t*)(base + (t + RL * k) * stride_tok);
+#pragma unroll
+            for (int k = 0; k < 4; ++k) { hist_add(h0, w[k] & 0xffffu); hist_add(h1, w[k] >> 16); }
         }
-    }
-    // reduce the 4 row lanes per coordinate, then pair coordinates into blocks
-    __shared__ uint64_t s_lo[4][128], s_hi[4][128];
-    s_lo[r][2 * j] = lo0; s_hi[r][2 * j] = hi0;
-    s_lo[r][2 * j + 1] = lo1; s_hi[r][2 * j + 1] = hi1;
-    __syncthreads();
-    uint64_t clo = 0, chi = 0;
-    if (threadIdx.x < 128) {
-        const int c = threadIdx.x;
-        clo = s_lo[0][c];
-        chi = s_hi[0][c];
-        for (int q = 1; q < 4; ++q) {
-            clo += s_lo[q][c];
-            chi += s_hi[q][c] + (clo < s_lo[q][c] ? 1ull : 0ull);
+        for (; t < row1; t += RL) {
+            const uint32_t w0 = *(const uint32_t*)(base + t * stride_tok);
+            hist_add(h0, w0 & 0xffffu); hist_add(h1, w0 >> 16);
         }
     }
     __syncthreads();
-    if (threadIdx.x < 128) {
-        s_lo[0][threadIdx.x] = clo;
-        s_hi[0][threadIdx.x] = chi;
+    // coordinate totals: sum over exponents of counter << sh(e)
+    if ((int)threadIdx.x < 2 * npairs) {
+        const uint32_t* hc = s_hist + threadIdx.x * kHistStride;
+        uint64_t lo = 0, hi = 0;
+#pragma unroll
+        for (int e = 0; e < 32; ++e) {
+            const uint64_t v = hc[e];
+            const int sh = e ? 2 * e - 2 : 0;
+            const uint64_t l = v << sh;
+            const uint64_t u = sh > 32 ? v >> (64 - sh) : 0ull;
+            lo += l;
+            hi += u + (lo < l ? 1ull : 0ull);
+        }
+        s_lo[threadIdx.x] = lo;
+        s_hi[threadIdx.x] = hi;
     }
     __syncthreads();
     if ((int)threadIdx.x < npairs) {
         const int i = threadIdx.x;
         const int p = pairing == KVQ_PAIR_HALF ? i : 2 * i;
         const int q = pairing == KVQ_PAIR_HALF ? i + npairs : 2 * i + 1;
-        uint64_t lo = s_lo[0][p], hi = s_hi[0][p];
-        lo += s_lo[0][q];
-        hi += s_hi[0][q] + (lo < s_lo[0][q] ? 1ull : 0ull);
+        uint64_t lo = s_lo[p], hi = s_hi[p];
+        lo += s_lo[q];
+        hi += s_hi[q] + (lo < s_lo[q] ? 1ull : 0ull);
         if (lo | hi) atomic_add_u128(energy + ((int64_t)h * npairs + i) * 2, lo, hi);
     }
 }
 
 hipError_t launch_block_energy(const uint16_t* x, int64_t n_tok, int64_t stride_tok, int64_t stride_head,
                                int n_heads, int d, int pairing, uint64_t* energy, hipStream_t st) {
-    // about 2048 workgroups in total, at least 64 rows each
-    int64_t blocks_per_head = (2048 + n_heads - 1) / n_heads;
+    // about 512 workgroups in total, 256 .. kEnergyMaxRows rows each
+    const int64_t blocks_per_head = (512 + n_heads - 1) / n_heads;
     int64_t rows = (n_tok + blocks_per_head - 1) / blocks_per_head;
-    if (rows < 64) rows = 64;
+    if (rows < 256) rows = 256;
     rows = (rows + 15) / 16 * 16;
+    if (rows > kEnergyMaxRows) rows = kEnergyMaxRows;
     const int64_t nby = (n_tok + rows - 1) / rows;
     dim3 grid(n_heads, (unsigned)nby);
-    hipLaunchKernelGGL(block_energy_kernel, grid, dim3(256), 0, st, x, n_tok, stride_tok, stride_head, d, pairing,
+    hipLaunchKernelGGL(block_energy_kernel, grid, dim3(kEnergyThreads), 0, st, x, n_tok, stride_tok, stride_head, d, pairing,
                        rows, energy);
     return hipGetLastError();
 }
