@@ -63,6 +63,8 @@ def lib() -> C.CDLL:
     L.or_dequant.argtypes = [P, I64, I32, P, P, P, P, P, P]
     L.or_attend.argtypes = [P, P, P, I64, I32, F64, P]
     L.or_decode_attention.argtypes = [P, I64, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, I64, F64, P]
+    L.or_decode_attention_window.argtypes = [P, I64, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, I64, P, P, I64,
+                                             F64, P]
     return L
 
 
@@ -297,4 +299,27 @@ def decode_attention(geom: Geometry, region: np.ndarray, q16: np.ndarray, seq_le
                               _p(np.ascontiguousarray(ksig, np.float32)), _p(np.ascontiguousarray(vsig, np.float32)),
                               _p(T["lev"]), _p(T["lev_off"]), _p(np.ascontiguousarray(q16).view(np.uint16)),
                               seq_len, float(scale), _p(out))
+    return out
+
+
+def decode_attention_window(geom: Geometry, region: np.ndarray, q16: np.ndarray, n_packed: int,
+                            wk16: np.ndarray, wv16: np.ndarray, kbits: np.ndarray, ksig: np.ndarray,
+                            vsig: np.ndarray, scale: float | None = None) -> np.ndarray:
+    """Exact fp64 attention of q16 [H_q, d] over packed slots [0, n_packed) followed by
+    the window tokens wk16/wv16 [n_win, H, d] (binary16, sequence order) taken exactly
+    -- the fp16 recent-window variant (the most recent tokens kept unquantized)."""
+    T = tables()
+    d = geom.d
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    nq = q16.shape[0]
+    wk = np.ascontiguousarray(wk16).view(np.uint16).reshape(-1, geom.H, d)
+    wv = np.ascontiguousarray(wv16).view(np.uint16).reshape(-1, geom.H, d)
+    assert wk.shape == wv.shape
+    out = np.zeros((nq, d), np.float64)
+    lib().or_decode_attention_window(
+        _p(np.ascontiguousarray(region)), geom.n_tiles, geom.H, nq, d, geom.pairing, geom.kb, geom.vb,
+        _p(np.ascontiguousarray(kbits, np.uint8)), _p(np.ascontiguousarray(ksig, np.float32)),
+        _p(np.ascontiguousarray(vsig, np.float32)), _p(T["lev"]), _p(T["lev_off"]),
+        _p(np.ascontiguousarray(q16).view(np.uint16)), n_packed, _p(wk), _p(wv), wk.shape[0], float(scale), _p(out))
     return out

@@ -603,3 +603,57 @@ void or_decode_attention(const uint8_t *region, int64_t n_tiles, int n_kv, int n
         free(kc); free(vc); free(kscale); free(vscale); free(kh); free(vh);
     }
 }
+
+/*
+ * Decode attention over a packed prefix plus an fp16 window of the most recent
+ * tokens (the recent-key buffer variant: those tokens are kept unquantized).
+ *   slots [0, n_packed) of the packed region, dequantized as above, followed by
+ *   the n_win window tokens wk/wv : binary16 [n_win][n_kv][d] in sequence order,
+ *   taken at their exact binary16 values;
+ * then the same exact softmax attention over all n_packed + n_win tokens.
+ */
+void or_decode_attention_window(const uint8_t *region, int64_t n_tiles, int n_kv, int n_q, int d, int pairing,
+                                int k_budget, int v_bits, const uint8_t *kbits, const float *ksig,
+                                const float *vsig, const uint16_t *levels, const int *lev_off,
+                                const uint16_t *q, int64_t n_packed, const uint16_t *wk, const uint16_t *wv,
+                                int64_t n_win, double scale, double *out)
+{
+    int64_t tile = or_tile_bytes(d, k_budget, v_bits);
+    int g = n_q / n_kv;
+    int64_t n = n_packed + n_win;
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int h = 0; h < n_q; h++) {
+        int kv = h / g;
+        const uint8_t *reg = region + (int64_t)kv * n_tiles * tile;
+        int nb = d / 2;
+        int kw[256], vw[256];
+        float ks[256], vs[256];
+        for (int i = 0; i < nb; i++) {
+            int p, qq;
+            block_coords(d, pairing, i, &p, &qq);
+            kw[p] = kw[qq] = kbits[kv * nb + i];
+            vw[p] = vw[qq] = v_bits;
+            ks[p] = ks[qq] = ksig[kv * nb + i];
+            vs[p] = vs[qq] = vsig[kv * nb + i];
+        }
+        size_t np1 = (size_t)(n_packed > 0 ? n_packed : 1), n1 = (size_t)(n > 0 ? n : 1);
+        uint16_t *kc = (uint16_t *)malloc(sizeof(uint16_t) * np1 * d);
+        uint16_t *vc = (uint16_t *)malloc(sizeof(uint16_t) * np1 * d);
+        float *kscale = (float *)malloc(sizeof(float) * np1);
+        float *vscale = (float *)malloc(sizeof(float) * np1);
+        double *kh = (double *)malloc(sizeof(double) * n1 * d);
+        double *vh = (double *)malloc(sizeof(double) * n1 * d);
+        or_unpack(reg, d, pairing, k_budget, v_bits, kbits + kv * nb, 0, n_packed, kc, vc, kscale, vscale);
+        or_dequant(kc, n_packed, d, kw, ks, kscale, levels, lev_off, kh);
+        or_dequant(vc, n_packed, d, vw, vs, vscale, levels, lev_off, vh);
+        for (int64_t t = 0; t < n_win; t++)
+            for (int c = 0; c < d; c++) {
+                kh[(n_packed + t) * d + c] = h2d(wk[(t * n_kv + kv) * d + c]);
+                vh[(n_packed + t) * d + c] = h2d(wv[(t * n_kv + kv) * d + c]);
+            }
+        double qd[256];
+        for (int c = 0; c < d; c++) qd[c] = h2d(q[h * d + c]);
+        or_attend(qd, kh, vh, n, d, scale, out + (int64_t)h * d);
+        free(kc); free(vc); free(kscale); free(vscale); free(kh); free(vh);
+    }
+}

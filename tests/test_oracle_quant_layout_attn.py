@@ -194,6 +194,45 @@ def test_attention_special_cases():
     assert (oe == 0).all()
 
 
+def test_window_attention_pins():
+    """fp16 recent window: a window holding every token is textbook attention on the
+    fp16 inputs; an empty window is the packed-only attention; with the passthrough
+    widths (K16V16) moving tokens between the packed prefix and the window changes
+    nothing; a window token enters at its exact value, a packed one dequantized."""
+    H, g, n, cap = 2, 3, 150, 192
+    k = rng.standard_normal((n, H, 128)).astype(np.float16)
+    v = rng.standard_normal((n, H, 128)).astype(np.float16)
+    q = rng.standard_normal((H * g, 128)).astype(np.float16)
+    sc = 1 / np.sqrt(128)
+    geom = oracle.Geometry(H, 192, 3, cap)
+    kbits, ksig = oracle.allocate(oracle.block_energy(k), 192)
+    _, vsig = oracle.allocate(oracle.block_energy(v), 192, oracle.UNIFORM)
+    region = np.zeros(geom.seq_bytes, np.uint8)
+    oracle.quantize_pack(geom, region, k, v, 0, kbits, ksig, vsig)
+    # every token in the window: no quantization at all
+    allw = oracle.decode_attention_window(geom, region, q, 0, k, v, kbits, ksig, vsig)
+    for h in range(H * g):
+        ref = _textbook_attention(q[h], k[:, h // g], v[:, h // g], sc)
+        np.testing.assert_allclose(allw[h], ref, rtol=1e-12, atol=1e-14)
+    # empty window: the packed-only attention
+    now = oracle.decode_attention_window(geom, region, q, n, k[:0], v[:0], kbits, ksig, vsig)
+    np.testing.assert_array_equal(now, oracle.decode_attention(geom, region, q, n, kbits, ksig, vsig))
+    # packed prefix + window differs from all-packed only through the window tokens'
+    # quantization error: closer to the exact attention than the all-packed result
+    mix = oracle.decode_attention_window(geom, region, q, n - 40, k[n - 40:], v[n - 40:], kbits, ksig, vsig)
+    allp = oracle.decode_attention(geom, region, q, n, kbits, ksig, vsig)
+    assert np.abs(mix - allw).max() < np.abs(allp - allw).max()
+    # passthrough widths: where a token sits does not matter
+    gp = oracle.Geometry(H, 1024, 16, cap)
+    kb16, ks16 = oracle.allocate(oracle.block_energy(k), 1024)
+    _, vs16 = oracle.allocate(oracle.block_energy(v), 1024)
+    reg16 = np.zeros(gp.seq_bytes, np.uint8)
+    oracle.quantize_pack(gp, reg16, k, v, 0, kb16, ks16, vs16)
+    for split in (0, 1, 64, 149, 150):
+        o = oracle.decode_attention_window(gp, reg16, q, split, k[split:], v[split:], kb16, ks16, vs16)
+        np.testing.assert_allclose(o, allw, rtol=1e-12, atol=1e-14)
+
+
 @pytest.mark.parametrize("cfg,n,heads", [("c1", 1024, [0]), ("c2", 8192, [0, 5])])
 def test_fidelity_gate_beats_uniform(cfg, n, heads):
     """Block-GTQ's query-key logit MAE is no worse than either uniform baseline."""
