@@ -222,6 +222,40 @@ int32_t kvq_decode_step(const kvq_geom *g, int32_t n_q_heads, const void *q, con
                         const uint8_t *k_bits, const float *k_sigma, const float *v_sigma, float softmax_scale,
                         float *out, void *workspace, size_t workspace_bytes, int32_t kernel,
                         int32_t tiles_per_split, void *stream);
+/* The fp16 recent-window variant (the page's recent-key buffer: the newest tokens are
+ * kept unquantized; "RoPE-Aware Bit Allocation for KV-Cache Quantization", the
+ * evaluation's remark that its reasoning run keeps no such buffer).  For a sequence of
+ * seq_len[s] = n tokens and a window of W tokens (1 <= W <= 1024), tokens
+ * [0, max(n - W, 0)) live in the packed cache (slots 0..) and the last min(n, W)
+ * tokens in a caller-owned binary16 ring: token t at row t mod W of
+ *   win_k / win_v : [n_seq][n_kv_heads][W][128] binary16, 16-byte aligned.
+ * kvq_window_decode_attn: attention of q over the packed tokens (dequantized, as
+ *   kvq_packed_decode_attn) and the window tokens (their exact binary16 values), one
+ *   softmax over all n tokens; out as kvq_packed_decode_attn.  max_len >= every
+ *   seq_len[s]; the packed part needs capacity_tokens >= max_len - W and a workspace
+ *   of kvq_decode_workspace_bytes_ex(g, n_q_heads, n_seq, max(max_len - W, 0), kernel,
+ *   tiles_per_split) bytes.  Nothing is written but out and the workspace.
+ * kvq_window_decode_step: one decode step with seq_len[s] already counting the new
+ *   token (rows k_new / v_new of s, as in kvq_decode_step, but 16-byte aligned with
+ *   strides a multiple of 8 elements): when n > W the token leaving the window
+ *   (position n - W - 1, ring row (n - 1) mod W) is quantized and packed into slot
+ *   n - W - 1 exactly as kvq_quantize_pack would, inside the attention launch; the
+ *   attention is that of kvq_window_decode_attn with the new token in the window;
+ *   then the new token is written to ring row (n - 1) mod W.  The caller fills the
+ *   ring for the prefill (tokens [n - W, n)) and quantizes the rest. */
+int32_t kvq_window_decode_attn(const kvq_geom *g, int32_t window, int32_t n_q_heads, const void *q,
+                               const void *win_k, const void *win_v, const uint8_t *cache,
+                               const int64_t *seq_byte_off, const int32_t *seq_len, int32_t n_seq, int64_t max_len,
+                               const uint8_t *k_bits, const float *k_sigma, const float *v_sigma,
+                               float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
+                               int32_t kernel, int32_t tiles_per_split, void *stream);
+int32_t kvq_window_decode_step(const kvq_geom *g, int32_t window, int32_t n_q_heads, const void *q,
+                               const void *k_new, const void *v_new, int64_t new_stride_seq,
+                               int64_t new_stride_head, void *win_k, void *win_v, uint8_t *cache,
+                               const int64_t *seq_byte_off, const int32_t *seq_len, int32_t n_seq, int64_t max_len,
+                               const uint8_t *k_bits, const float *k_sigma, const float *v_sigma,
+                               float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
+                               int32_t kernel, int32_t tiles_per_split, void *stream);
 /* Log-sum-exp merge of n_split partials per (sequence, head) in the format above:
  * out[s][h][c] = sum_k 2^(m_k - M) o_k,c / sum_k 2^(m_k - M) l_k, M = max_k m_k; rows
  * with no tokens give 0.  out: device float [n_seq][n_q_heads][128]. */

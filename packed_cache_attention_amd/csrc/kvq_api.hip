@@ -334,4 +334,91 @@ int32_t kvq_decode_step(const kvq_geom* g, int32_t n_q_heads, const void* q, con
                       fn);
 }
 
+namespace {
+constexpr int kWindowLimit = 1024;  // window tokens per (sequence, KV head): one merge thread each
+
+int32_t check_window(const kvq_geom* g, int32_t window, const void* win_k, const void* win_v, int64_t max_len,
+                     const char* fn) {
+    if (window < 1 || window > kWindowLimit) return fail(KVQ_ERR_ARG, fn, "window outside 1..1024");
+    if (!win_k || !win_v) return fail(KVQ_ERR_ARG, fn, "null window pointer");
+    if (!aligned(win_k, 16) || !aligned(win_v, 16)) return fail(KVQ_ERR_ALIGN, fn, "window alignment");
+    if (max_len < 0) return fail(KVQ_ERR_ARG, fn, "negative count");
+    (void)g;
+    return KVQ_OK;
+}
+
+int32_t window_decode(const kvq_geom* g, int32_t window, int32_t n_q_heads, const void* q, const void* k_new,
+                      const void* v_new, int64_t new_stride_seq, int64_t new_stride_head, void* win_k, void* win_v,
+                      uint8_t* cache, const int64_t* seq_byte_off, const int32_t* seq_len, int32_t n_seq,
+                      int64_t max_len, const uint8_t* k_bits, const float* k_sigma, const float* v_sigma,
+                      float softmax_scale, float* out, void* workspace, size_t workspace_bytes, int32_t kernel,
+                      int32_t tiles_per_split, void* stream, const char* fn) {
+    int32_t st = check_window(g, window, win_k, win_v, max_len, fn);
+    if (st) return st;
+    const int64_t packed_max = max_len > window ? max_len - window : 0;
+    DecodePlan plan;
+    st = check_decode(g, n_q_heads, q, cache, seq_byte_off, seq_len, n_seq, packed_max, k_bits, k_sigma, v_sigma,
+                      workspace, workspace_bytes, kernel, tiles_per_split, &plan, fn);
+    if (st || n_seq == 0) return st;
+    if (k_new) {
+        if (!v_new) return fail(KVQ_ERR_ARG, fn, "null new-token pointer");
+        if (new_stride_seq < 0 || new_stride_head < 0) return fail(KVQ_ERR_ARG, fn, "negative stride");
+        if (!aligned(k_new, 16) || !aligned(v_new, 16) || (new_stride_seq & 7) || (new_stride_head & 7))
+            return fail(KVQ_ERR_ALIGN, fn, "new-token rows must be 16-byte aligned");
+    }
+    if (!out) return fail(KVQ_ERR_ARG, fn, "null pointer");
+    if (!aligned(out, 16)) return fail(KVQ_ERR_ALIGN, fn, "alignment");
+    // the packed part: the token leaving the window (if any) is appended in the same
+    // launch as the attention over the packed tokens
+    const int64_t ring_stride_seq = (int64_t)g->n_kv_heads * window * kHeadDim;
+    const AppendArgs app{k_new ? (const uint16_t*)win_k : nullptr, k_new ? (const uint16_t*)win_v : nullptr,
+                         ring_stride_seq, (int64_t)window * kHeadDim, window};
+    hipError_t e = launch_decode_partials(*g, plan, n_q_heads, (const uint16_t*)q, cache, seq_byte_off, seq_len,
+                                          n_seq, packed_max, k_bits, k_sigma, v_sigma, softmax_scale,
+                                          (float*)workspace, (hipStream_t)stream, app);
+    if (e != hipSuccess) return hip_status(e, fn);
+    WindowArgs w;
+    w.q = (const uint16_t*)q;
+    w.n_q = n_q_heads;
+    w.g = n_q_heads / g->n_kv_heads;
+    w.n_kv = g->n_kv_heads;
+    w.window = window;
+    w.scale_log2 = softmax_scale * kLog2e;
+    w.win_k = (uint16_t*)win_k;
+    w.win_v = (uint16_t*)win_v;
+    w.seq_len = seq_len;
+    w.k_new = (const uint16_t*)k_new;
+    w.v_new = (const uint16_t*)v_new;
+    w.new_stride_seq = new_stride_seq;
+    w.new_stride_head = new_stride_head;
+    return hip_status(launch_merge_window(n_seq, plan.n_split, (const float*)workspace, out, w, (hipStream_t)stream),
+                      fn);
+}
+}  // namespace
+
+int32_t kvq_window_decode_attn(const kvq_geom* g, int32_t window, int32_t n_q_heads, const void* q,
+                               const void* win_k, const void* win_v, const uint8_t* cache,
+                               const int64_t* seq_byte_off, const int32_t* seq_len, int32_t n_seq, int64_t max_len,
+                               const uint8_t* k_bits, const float* k_sigma, const float* v_sigma,
+                               float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
+                               int32_t kernel, int32_t tiles_per_split, void* stream) {
+    return window_decode(g, window, n_q_heads, q, nullptr, nullptr, 0, 0, (void*)win_k, (void*)win_v,
+                         (uint8_t*)cache, seq_byte_off, seq_len, n_seq, max_len, k_bits, k_sigma, v_sigma,
+                         softmax_scale, out, workspace, workspace_bytes, kernel, tiles_per_split, stream,
+                         "kvq_window_decode_attn");
+}
+
+int32_t kvq_window_decode_step(const kvq_geom* g, int32_t window, int32_t n_q_heads, const void* q,
+                               const void* k_new, const void* v_new, int64_t new_stride_seq,
+                               int64_t new_stride_head, void* win_k, void* win_v, uint8_t* cache,
+                               const int64_t* seq_byte_off, const int32_t* seq_len, int32_t n_seq, int64_t max_len,
+                               const uint8_t* k_bits, const float* k_sigma, const float* v_sigma,
+                               float softmax_scale, float* out, void* workspace, size_t workspace_bytes,
+                               int32_t kernel, int32_t tiles_per_split, void* stream) {
+    if (!k_new) return fail(KVQ_ERR_ARG, "kvq_window_decode_step", "null new-token pointer");
+    return window_decode(g, window, n_q_heads, q, k_new, v_new, new_stride_seq, new_stride_head, win_k, win_v, cache,
+                         seq_byte_off, seq_len, n_seq, max_len, k_bits, k_sigma, v_sigma, softmax_scale, out,
+                         workspace, workspace_bytes, kernel, tiles_per_split, stream, "kvq_window_decode_step");
+}
+
 }  // extern "C"

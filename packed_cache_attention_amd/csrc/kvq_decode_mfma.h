@@ -311,8 +311,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     uint32_t nk_pair = 0, nv_pair = 0, nk_p = 0, nk_q = 0, nv_p = 0, nv_q = 0;
     float my_vsig_blk = 0.f;
     if (app.k != nullptr) {
-        const uint16_t* kr = app.k + (int64_t)s * app.stride_seq + (int64_t)kvh * app.stride_head;
-        const uint16_t* vr = app.v + (int64_t)s * app.stride_seq + (int64_t)kvh * app.stride_head;
+        // with a window the token is the ring row leaving it (needs the length first)
+        const int64_t ring_row = app.window > 0 && len_raw > 0 ? ((len_raw - 1) % app.window) * kHeadDim : 0;
+        const uint16_t* kr = app.k + (int64_t)s * app.stride_seq + (int64_t)kvh * app.stride_head + ring_row;
+        const uint16_t* vr = app.v + (int64_t)s * app.stride_seq + (int64_t)kvh * app.stride_head + ring_row;
         nk_pair = *(const uint32_t*)(kr + 2 * lane);
         nv_pair = *(const uint32_t*)(vr + 2 * lane);
         nk_p = kr[qp]; nk_q = kr[qq];
@@ -320,7 +322,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         my_vsig_blk = v_sigma[kvh * kMaxBlocks + lane];
     }
 
-    const int64_t len = min(max(len_raw, (int64_t)0), max_len);
+    const int64_t len = min(max(len_raw - app.window, (int64_t)0), max_len);  // packed tokens
     const int64_t n_tiles_seq = (len + kTile - 1) / kTile;
     const int64_t t0 = (int64_t)split * tiles_per_split;
     const int64_t t1 = min(t0 + tiles_per_split, n_tiles_seq);

@@ -76,11 +76,16 @@ hipError_t launch_quantize_pack(const kvq_geom& g, const uint16_t* k, const uint
 
 // The decode step's new token per sequence (row s at k + s*stride_seq + h*stride_head),
 // written to slot seq_len[s] - 1 before attention; k == nullptr: no append.
+// window > 0 (the fp16 recent window): the packed cache holds the first
+// seq_len[s] - window tokens, attention reads only those, and the appended token is
+// the one leaving the window -- row ((seq_len[s] - 1) mod window) of the ring at
+// k + s*stride_seq + h*stride_head, written to packed slot seq_len[s] - window - 1.
 struct AppendArgs {
     const uint16_t* k;
     const uint16_t* v;
     int64_t stride_seq;
     int64_t stride_head;
+    int32_t window;
 };
 
 struct DecodePlan {
@@ -96,11 +101,27 @@ hipError_t launch_decode_partials(const kvq_geom& g, const DecodePlan& plan, int
                                   uint8_t* cache, const int64_t* seq_byte_off, const int32_t* seq_len,
                                   int n_seq, int64_t max_len, const uint8_t* k_bits, const float* k_sigma,
                                   const float* v_sigma, float softmax_scale, float* partials, hipStream_t st,
-                                  const AppendArgs& app = AppendArgs{nullptr, nullptr, 0, 0});
+                                  const AppendArgs& app = AppendArgs{nullptr, nullptr, 0, 0, 0});
 // one token per sequence into slot seq_len[s] - 1 (the decode step's append, alone)
 hipError_t launch_append_step(const kvq_geom& g, int n_seq, const AppendArgs& app, const int32_t* seq_len,
                               const uint8_t* k_bits, const float* k_sigma, const float* v_sigma, uint8_t* cache,
                               const int64_t* seq_byte_off, hipStream_t st);
 hipError_t launch_merge(int n_rows, int n_split, const float* partials, float* out, hipStream_t st);
+// the split merge of the packed part folded with exact attention over the fp16 window
+// (ring [n_seq][n_kv][window][128]); with k_new, the step's new token is read from
+// k_new/v_new and written to its ring row after use
+struct WindowArgs {
+    const uint16_t* q;
+    int n_q, g, n_kv, window;
+    float scale_log2;
+    uint16_t* win_k;
+    uint16_t* win_v;
+    const int32_t* seq_len;
+    const uint16_t* k_new;
+    const uint16_t* v_new;
+    int64_t new_stride_seq, new_stride_head;
+};
+hipError_t launch_merge_window(int n_seq, int n_split, const float* partials, float* out, const WindowArgs& w,
+                               hipStream_t st);
 
 }  // namespace kvq

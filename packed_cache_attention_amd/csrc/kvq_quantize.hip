@@ -335,16 +335,19 @@ __global__ __launch_bounds__(64) void append_kernel(
     const int64_t* __restrict__ first_slot, const int32_t* __restrict__ n_new, const int64_t* __restrict__ src_row0,
     int max_new, int64_t capacity, const uint8_t* __restrict__ k_bits, const float* __restrict__ k_sigma,
     const float* __restrict__ v_sigma, uint8_t* __restrict__ cache, const int64_t* __restrict__ seq_byte_off,
-    int pairing, int k_budget, int v_bits, const int32_t* __restrict__ step_len) {
+    int pairing, int k_budget, int v_bits, const int32_t* __restrict__ step_len, int window) {
     const int s = blockIdx.z, h = blockIdx.y, j = blockIdx.x;
     // either explicit runs (first_slot, n_new, src_row0) or the decode step: one token
-    // per sequence, row s, into slot step_len[s] - 1
-    const int64_t first = step_len ? (int64_t)step_len[s] - 1 : first_slot[s];
+    // per sequence, row s, into slot step_len[s] - 1; with an fp16 window of `window`
+    // tokens, the token leaving it (ring row (step_len[s] - 1) mod window of row s)
+    // into slot step_len[s] - window - 1
+    const int64_t first = step_len ? (int64_t)step_len[s] - 1 - window : first_slot[s];
     const int n = step_len ? 1 : n_new[s];
     if (first < 0 || n <= 0 || n > max_new || first + n > capacity || j >= n) return;
     const int lane = threadIdx.x;
     const int64_t slot = first + j;
     const int64_t row = step_len ? (int64_t)s : src_row0[s] + j;
+    const int64_t ring_row = window > 0 ? ((int64_t)step_len[s] - 1) % window * kHeadDim : 0;  // first >= 0 here
     const int64_t tau = slot / kTile;
     const int p = (int)(slot - tau * kTile);
     const int64_t SK = k_record_bytes(k_budget);
@@ -359,8 +362,8 @@ __global__ __launch_bounds__(64) void append_kernel(
     const int c0 = 2 * lane, c1 = 2 * lane + 1;
     const int b0 = pairing == KVQ_PAIR_HALF ? (c0 & (kMaxBlocks - 1)) : (c0 >> 1);
     const int b1 = pairing == KVQ_PAIR_HALF ? (c1 & (kMaxBlocks - 1)) : (c1 >> 1);
-    const uint32_t kp = *(const uint32_t*)(kx + row * stride_tok + (int64_t)h * stride_head + c0);
-    const uint32_t vp = *(const uint32_t*)(vx + row * stride_tok + (int64_t)h * stride_head + c0);
+    const uint32_t kp = *(const uint32_t*)(kx + row * stride_tok + (int64_t)h * stride_head + ring_row + c0);
+    const uint32_t vp = *(const uint32_t*)(vx + row * stride_tok + (int64_t)h * stride_head + ring_row + c0);
     const int w0 = k_bits[h * kMaxBlocks + b0], w1 = k_bits[h * kMaxBlocks + b1];
     const float ks0 = k_sigma[h * kMaxBlocks + b0], ks1 = k_sigma[h * kMaxBlocks + b1];
     const float vs0 = v_sigma[h * kMaxBlocks + b0], vs1 = v_sigma[h * kMaxBlocks + b1];
@@ -433,7 +436,7 @@ hipError_t launch_quantize_pack(const kvq_geom& g, const uint16_t* k, const uint
         dim3 grid(max_new, g.n_kv_heads, n_seq);
         hipLaunchKernelGGL(append_kernel, grid, dim3(64), 0, st, k, v, stride_tok, stride_head, first_slot, n_new,
                            src_row0, max_new, g.capacity_tokens, k_bits, k_sigma, v_sigma, cache, seq_byte_off,
-                           g.rope_pairing, g.k_budget, g.v_bits, (const int32_t*)nullptr);
+                           g.rope_pairing, g.k_budget, g.v_bits, (const int32_t*)nullptr, 0);
         return hipGetLastError();
     }
     // a run of max_new slots starting anywhere touches at most ceil(max_new/64) + 1 tiles
@@ -452,7 +455,7 @@ hipError_t launch_append_step(const kvq_geom& g, int n_seq, const AppendArgs& ap
     hipLaunchKernelGGL(append_kernel, grid, dim3(64), 0, st, app.k, app.v, app.stride_seq, app.stride_head,
                        (const int64_t*)nullptr, (const int32_t*)nullptr, (const int64_t*)nullptr, 1,
                        g.capacity_tokens, k_bits, k_sigma, v_sigma, cache, seq_byte_off, g.rope_pairing, g.k_budget,
-                       g.v_bits, seq_len);
+                       g.v_bits, seq_len, app.window);
     return hipGetLastError();
 }
 

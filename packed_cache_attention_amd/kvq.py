@@ -82,6 +82,12 @@ def lib() -> C.CDLL:
     L.kvq_decode_step_partials.restype = I32
     L.kvq_decode_step.argtypes = [G, I32, P, P, P, I64, I64, P, P, P, I32, I64, P, P, P, F32, P, P, SZ, I32, I32, P]
     L.kvq_decode_step.restype = I32
+    L.kvq_window_decode_attn.argtypes = [G, I32, I32, P, P, P, P, P, P, I32, I64, P, P, P, F32, P, P, SZ, I32, I32,
+                                         P]
+    L.kvq_window_decode_attn.restype = I32
+    L.kvq_window_decode_step.argtypes = [G, I32, I32, P, P, P, I64, I64, P, P, P, P, P, I32, I64, P, P, P, F32, P, P,
+                                         SZ, I32, I32, P]
+    L.kvq_window_decode_step.restype = I32
     L.kvq_decode_plan.argtypes = [G, I32, I32, I64, I32, I32, P, P, P, P]
     L.kvq_decode_plan.restype = I32
     if L.kvq_version() != LAYOUT_VERSION:
@@ -93,7 +99,7 @@ EXPORTS = ["kvq_version", "kvq_status_string", "kvq_tile_bytes", "kvq_cache_byte
            "kvq_block_energy", "kvq_allocate_bits", "kvq_quantize_pack", "kvq_decode_workspace_bytes",
            "kvq_decode_workspace_bytes_ex", "kvq_packed_decode_attn", "kvq_packed_decode_attn_ex",
            "kvq_decode_partials", "kvq_merge_partials", "kvq_decode_n_split", "kvq_decode_plan",
-           "kvq_decode_step_partials", "kvq_decode_step"]
+           "kvq_decode_step_partials", "kvq_decode_step", "kvq_window_decode_attn", "kvq_window_decode_step"]
 
 
 def status_string(st: int) -> str:
@@ -274,6 +280,50 @@ def decode_step(g: Geom, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tens
         C.byref(g), n_q, _ptr(q), _ptr(k_new), _ptr(v_new), ss, sh, _ptr(cache), _ptr(seq_byte_off), _ptr(seq_len),
         n_seq, max_len, _ptr(k_bits), _ptr(k_sigma), _ptr(v_sigma), float(softmax_scale), _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), kernel, tiles_per_split, _stream(stream)))
+
+
+def _window_ring(g: Geom, window: int, win_k: torch.Tensor, win_v: torch.Tensor):
+    assert win_k.dtype == torch.float16 and win_v.dtype == torch.float16
+    assert win_k.is_contiguous() and win_v.is_contiguous() and win_k.shape == win_v.shape
+    assert win_k.shape[1:] == (g.n_kv_heads, window, g.head_dim)
+
+
+def window_decode_attn(g: Geom, window: int, q: torch.Tensor, win_k: torch.Tensor, win_v: torch.Tensor,
+                       cache: torch.Tensor, seq_byte_off: torch.Tensor, seq_len: torch.Tensor, max_len: int,
+                       k_bits: torch.Tensor, k_sigma: torch.Tensor, v_sigma: torch.Tensor, out: torch.Tensor,
+                       workspace: torch.Tensor, softmax_scale: float | None = None, kernel: int = DECODE_AUTO,
+                       tiles_per_split: int = 0, stream=None):
+    """Attention over the packed tokens and the fp16 window ring win_k/win_v [n_seq, n_kv, window, 128]."""
+    assert q.dtype == torch.float16 and q.is_contiguous() and out.dtype == torch.float32 and out.is_contiguous()
+    _window_ring(g, window, win_k, win_v)
+    n_seq, n_q = q.shape[0], q.shape[1]
+    if softmax_scale is None:
+        softmax_scale = g.head_dim ** -0.5
+    _check("kvq_window_decode_attn", lib().kvq_window_decode_attn(
+        C.byref(g), window, n_q, _ptr(q), _ptr(win_k), _ptr(win_v), _ptr(cache), _ptr(seq_byte_off), _ptr(seq_len),
+        n_seq, max_len, _ptr(k_bits), _ptr(k_sigma), _ptr(v_sigma), float(softmax_scale), _ptr(out),
+        _ptr(workspace), workspace.numel() * workspace.element_size(), kernel, tiles_per_split, _stream(stream)))
+
+
+def window_decode_step(g: Geom, window: int, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                       win_k: torch.Tensor, win_v: torch.Tensor, cache: torch.Tensor, seq_byte_off: torch.Tensor,
+                       seq_len: torch.Tensor, max_len: int, k_bits: torch.Tensor, k_sigma: torch.Tensor,
+                       v_sigma: torch.Tensor, out: torch.Tensor, workspace: torch.Tensor,
+                       softmax_scale: float | None = None, kernel: int = DECODE_AUTO, tiles_per_split: int = 0,
+                       stream=None):
+    """One step with the fp16 window: the token leaving the window is packed, the new one
+    enters the ring, attention over all (seq_len counts the new token)."""
+    assert q.dtype == torch.float16 and q.is_contiguous() and out.dtype == torch.float32 and out.is_contiguous()
+    _window_ring(g, window, win_k, win_v)
+    ss, sh = _step_rows(k_new, v_new)
+    n_seq, n_q = q.shape[0], q.shape[1]
+    if softmax_scale is None:
+        softmax_scale = g.head_dim ** -0.5
+    _check("kvq_window_decode_step", lib().kvq_window_decode_step(
+        C.byref(g), window, n_q, _ptr(q), _ptr(k_new), _ptr(v_new), ss, sh, _ptr(win_k), _ptr(win_v), _ptr(cache),
+        _ptr(seq_byte_off), _ptr(seq_len), n_seq, max_len, _ptr(k_bits), _ptr(k_sigma), _ptr(v_sigma),
+        float(softmax_scale), _ptr(out), _ptr(workspace), workspace.numel() * workspace.element_size(), kernel,
+        tiles_per_split, _stream(stream)))
 
 
 def merge_partials(n_seq: int, n_q: int, n_split: int, partials: torch.Tensor, out: torch.Tensor, stream=None):

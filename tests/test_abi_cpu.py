@@ -108,3 +108,19 @@ def test_host_validation_rejects_before_gpu():
     assert L.kvq_decode_step(*s_args(FAKE, 255)) == -4
     assert L.kvq_decode_step(*s_args(FAKE, -2)) == -1
     assert L.kvq_decode_step(*s_args(FAKE, 256, ws=16)) == -6
+    # fp16 window: window range, ring and new-row alignment, workspace, before any HIP call
+    w_args = lambda win, wk, kn, ss, ws=1 << 30: (C.byref(good), win, 16, FAKE, kn, FAKE, ss, 128, wk, FAKE, FAKE, FAKE,
+                                                  FAKE, 1, 512, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, ws, 0, 0, None)
+    assert L.kvq_window_decode_step(*w_args(0, FAKE, FAKE, 256)) == -1
+    assert L.kvq_window_decode_step(*w_args(1025, FAKE, FAKE, 256)) == -1
+    assert L.kvq_window_decode_step(*w_args(64, None, FAKE, 256)) == -1
+    assert L.kvq_window_decode_step(*w_args(64, FAKE + 4, FAKE, 256)) == -4
+    assert L.kvq_window_decode_step(*w_args(64, FAKE, None, 256)) == -1
+    assert L.kvq_window_decode_step(*w_args(64, FAKE, FAKE + 4, 256)) == -4
+    assert L.kvq_window_decode_step(*w_args(64, FAKE, FAKE, 260)) == -4
+    assert L.kvq_window_decode_step(*w_args(64, FAKE, FAKE, 256, ws=16)) == -6
+    a_args = lambda win, wk, ws=1 << 30: (C.byref(good), win, 16, FAKE, wk, FAKE, FAKE, FAKE, FAKE, 1, 512, FAKE,
+                                          FAKE, FAKE, 0.1, FAKE, FAKE, ws, 0, 0, None)
+    assert L.kvq_window_decode_attn(*a_args(2000, FAKE)) == -1
+    assert L.kvq_window_decode_attn(*a_args(64, FAKE + 8)) == -4
+    assert L.kvq_window_decode_attn(*a_args(64, FAKE, ws=16)) == -6
