@@ -110,6 +110,8 @@ def main():
     ap.add_argument("--unfused", action="store_true",
                     help="append with kvq_quantize_pack as a launch of its own instead of inside the attention kernel")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--window", type=int, default=128,
+                    help="also time the fp16 recent-window step with this many recent tokens unquantized (0: skip)")
     args = ap.parse_args()
     if args.traffic_from:
         traffic_from(args.traffic_from[0], args.traffic_from[1], args.copy_probe_mib or 256,
@@ -333,6 +335,71 @@ def main():
     log("%s: %.2f us/launch avg over %d launches, %.1f GB/s algorithmic (%.1f%% of peak)"
         % (kernel_name, kdur * 1e6, len(durs) * L, achieved, 100 * achieved / HBM_PEAK_GBPS))
 
+    # ------------------------------------------------------------ the fp16 recent-window variant
+    # The newest W tokens of each (layer, sequence, head) sit binary16 in a ring, the
+    # rest in the packed cache; one window step packs the token leaving the window
+    # inside the attention launch, then merges with exact attention over the window
+    # and writes the new token to the ring.  Lengths stay fixed over the repetitions
+    # (every step evicts and inserts at the same rows: identical work).
+    wres = None
+    if args.window > 0:
+        W = args.window
+        win_k = torch.empty(L, S, H, W, d, dtype=torch.float16, device=dev)
+        win_v = torch.empty_like(win_k)
+        for s_ in range(S):
+            t = torch.arange(max(lens[s_] - W, 0), lens[s_], device=dev)
+            src = int(row0[s_]) + t
+            win_k[:, s_, :, t % W] = Kall[:, src].permute(0, 2, 1, 3)
+            win_v[:, s_, :, t % W] = Vall[:, src].permute(0, 2, 1, 3)
+        wlen = seq_len.clone()
+        wmax = int(wlen.max())
+        wws_n = kvq.decode_workspace_bytes(g, Hq, S, max(wmax - W, 0), kern, args.tiles_per_split) // 4
+        wws = torch.empty(L, wws_n, dtype=torch.float32, device=dev)
+        wout = torch.empty(L, S, Hq, d, dtype=torch.float32, device=dev)
+
+        def wstep():
+            for l in range(L):
+                kvq.window_decode_step(g, W, Qall[l], Knew[l], Vnew[l], win_k[l], win_v[l], cache[l], off, wlen,
+                                       wmax, kbits[l], ksig[l], vsig[l], wout[l], wws[l], kernel=kern,
+                                       tiles_per_split=args.tiles_per_split)
+
+        for _ in range(max(1, args.warmup)):
+            wstep()
+        torch.cuda.synchronize()
+        wgraph = None
+        if not args.no_graph:
+            s_cap = torch.cuda.Stream()
+            s_cap.wait_stream(torch.cuda.current_stream())
+            wgraph = torch.cuda.CUDAGraph()
+            with torch.cuda.stream(s_cap):
+                with torch.cuda.graph(wgraph, stream=s_cap):
+                    wstep()
+            torch.cuda.current_stream().wait_stream(s_cap)
+            torch.cuda.synchronize()
+            for _ in range(args.warmup):
+                wgraph.replay()
+        torch.cuda.synchronize()
+        e0.record()
+        for _ in range(args.steps):
+            if wgraph is not None:
+                wgraph.replay()
+            else:
+                wstep()
+        e1.record()
+        torch.cuda.synchronize()
+        wms = e0.elapsed_time(e1) / args.steps
+        wl_ = wlen.cpu().numpy().astype(np.int64)
+        npk = np.maximum(wl_ - W, 0)
+        nwin = np.minimum(wl_, W)
+        wbytes = L * (int(npk.sum()) * H * bytes_per_token_head + int(nwin.sum()) * H * 2 * d * 2
+                      + S * Hq * d * (2 + 4) + S * H * (2 * d * 2 + bytes_per_token_head) + S * H * 2 * d * 2)
+        wval = wbytes / (wms / 1e3) / 1e9
+        log("window step (W=%d): %.4f ms/step, %.1f GB/s = %.1f%% of HBM peak" % (W, wms, wval,
+                                                                              100 * wval / HBM_PEAK_GBPS))
+        wres = {"window": W, "ms_per_step": round(wms, 5), "value": round(wval, 2), "unit": "GB/s",
+                "pct_hbm_peak": round(100 * wval / HBM_PEAK_GBPS, 2), "step_bytes": int(wbytes),
+                "entry_point": "kvq_window_decode_step"}
+
     traffic = None
     src_hash = kernel_source_hash("mfma" if kernel_name == "decode_mfma_kernel" else "generic")
     if os.path.exists(TRAFFIC_FILE):
@@ -389,6 +456,7 @@ def main():
                      "algorithmic_bytes_per_launch": int(launch_bytes),
                      "bytes_per_token_head": bytes_per_token_head},
         "cpu_baseline": cpu,
+        "window_step": wres,
     }
     print(json.dumps(result), flush=True)
 

@@ -290,6 +290,20 @@ __global__ __launch_bounds__(kMergeCols * kMergeGroups) void merge_window_kernel
         return w.win_v + (((int64_t)s * w.n_kv + kvh) * w.window + t % w.window) * kHeadDim;
     };
 
+    // the window's K pieces (first 128 tokens: eight lanes per token) and V values
+    // (four tokens per split group) go out with the partials' loads
+    const int kj = tid & 7;
+    uint4 kpre[2] = {uint4{0, 0, 0, 0}, uint4{0, 0, 0, 0}};
+    if (tid / 8 < nw) {
+        const uint4* kr = (const uint4*)krow(tid / 8) + 2 * kj;
+        kpre[0] = kr[0];
+        kpre[1] = kr[1];
+    }
+    constexpr int kVPre = 4;
+    uint32_t vpre[kVPre];
+#pragma unroll
+    for (int u = 0; u < kVPre; ++u) vpre[u] = sg + kMergeGroups * u < nw ? vrow(sg + kMergeGroups * u)[c] : 0u;
+
     // ---- the packed part's partials (as merge_kernel)
     const float* part = ws + row * n_split * D2;
     float M = -INFINITY, L = 0.f, A = 0.f;
@@ -332,39 +346,55 @@ __global__ __launch_bounds__(kMergeCols * kMergeGroups) void merge_window_kernel
     if ((tid & 63) < kMergeCols) { s_m[wv][cc] = M; s_l[wv][cc] = L; s_a[wv][cc] = A; }
     __syncthreads();  // s_q ready too
 
-    // ---- window logits: thread i takes token i
-    if (tid < nw) {
-        const uint4* kr = (const uint4*)krow(tid);
+    // ---- window logits: eight lanes per token, 16 coordinates each
+    for (int i = tid / 8; i < nw; i += kMergeCols * kMergeGroups / 8) {
+        const int j = kj;
+        const uint4* kr = (const uint4*)krow(i) + 2 * j;
         float z = 0.f;
-#pragma unroll 4
-        for (int k = 0; k < kHeadDim / 8; ++k) {
-            const uint4 v4 = kr[k];
+#pragma unroll
+        for (int k = 0; k < 2; ++k) {
+            const uint4 v4 = i == tid / 8 ? kpre[k] : kr[k];
             const uint32_t wd[4] = {v4.x, v4.y, v4.z, v4.w};
 #pragma unroll
             for (int e = 0; e < 4; ++e) {
-                z += s_q[8 * k + 2 * e] * h2f(wd[e] & 0xffffu);
-                z += s_q[8 * k + 2 * e + 1] * h2f(wd[e] >> 16);
+                z += s_q[16 * j + 8 * k + 2 * e] * h2f(wd[e] & 0xffffu);
+                z += s_q[16 * j + 8 * k + 2 * e + 1] * h2f(wd[e] >> 16);
             }
         }
-        s_z[tid] = z * w.scale_log2;
+        z += __shfl_xor(z, 1);
+        z += __shfl_xor(z, 2);
+        z += __shfl_xor(z, 4);
+        if (j == 0) s_z[i] = z * w.scale_log2;
     }
     __syncthreads();
-    if (wv == 0) {  // window max and weight sum
-        float mx = -INFINITY;
-        for (int i = tid; i < nw; i += 64) mx = fmaxf(mx, s_z[i]);
+    {  // window max, then weight sum: per wave, then across the 16 waves
+        float mx = tid < nw ? s_z[tid] : -INFINITY;
         for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-        float l = 0.f;
-        if (mx != -INFINITY)
-            for (int i = tid; i < nw; i += 64) l += exp2f(s_z[i] - mx);
+        if ((tid & 63) == 0) s_red[0][wv] = mx;
+        __syncthreads();
+        mx = s_red[0][tid & 15];
+        for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+        float l = (tid < nw && mx != -INFINITY) ? exp2f(s_z[tid] - mx) : 0.f;
+        if (tid < nw) s_z[tid] = l;  // the weights themselves from here on
         for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
-        if (tid == 0) { s_wm = mx; s_wl = l; }
+        if ((tid & 63) == 0) s_red[1][wv] = l;
+        __syncthreads();
+        if (tid == 0) {
+            float t = 0.f;
+            for (int k = 0; k < kMergeGroups / 2; ++k) t += s_red[1][k];
+            s_wm = mx;
+            s_wl = t;
+        }
     }
     __syncthreads();
     const float wm = s_wm, wl = s_wl;
     // window output for column c: group sg takes tokens sg, sg + 32, ...
     float oacc = 0.f;
-    if (nw > 0)
-        for (int i = sg; i < nw; i += kMergeGroups) oacc += exp2f(s_z[i] - wm) * h2f(vrow(i)[c]);
+#pragma unroll
+    for (int u = 0; u < kVPre; ++u)
+        if (sg + kMergeGroups * u < nw) oacc += s_z[sg + kMergeGroups * u] * h2f(vpre[u]);
+    for (int i = sg + kMergeGroups * kVPre; i < nw; i += kMergeGroups) oacc += s_z[i] * h2f(vrow(i)[c]);
+    __syncthreads();  // s_red's rows 0 and 1 were read above
     s_red[sg][cc] = oacc;
     __syncthreads();
     if (wv == 0) {
