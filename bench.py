@@ -353,7 +353,7 @@ def main():
             win_v[:, s_, :, t % W] = Vall[:, src].permute(0, 2, 1, 3)
         wlen = seq_len.clone()
         wmax = int(wlen.max())
-        wws_n = kvq.decode_workspace_bytes(g, Hq, S, max(wmax - W, 0), kern, args.tiles_per_split) // 4
+        wws_n = kvq.window_workspace_bytes(g, W, Hq, S, wmax, kern, args.tiles_per_split) // 4
         wws = torch.empty(L, wws_n, dtype=torch.float32, device=dev)
         wout = torch.empty(L, S, Hq, d, dtype=torch.float32, device=dev)
 

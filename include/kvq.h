@@ -232,9 +232,10 @@ int32_t kvq_decode_step(const kvq_geom *g, int32_t n_q_heads, const void *q, con
  * kvq_window_decode_attn: attention of q over the packed tokens (dequantized, as
  *   kvq_packed_decode_attn) and the window tokens (their exact binary16 values), one
  *   softmax over all n tokens; out as kvq_packed_decode_attn.  max_len >= every
- *   seq_len[s]; the packed part needs capacity_tokens >= max_len - W and a workspace
- *   of kvq_decode_workspace_bytes_ex(g, n_q_heads, n_seq, max(max_len - W, 0), kernel,
- *   tiles_per_split) bytes.  Nothing is written but out and the workspace.
+ *   seq_len[s]; the packed part needs capacity_tokens >= max_len - W, and the
+ *   workspace kvq_window_workspace_bytes(...) bytes (the packed part's chunks plus one
+ *   chunk for the window, computed in the same launch).  Nothing is written but out
+ *   and the workspace.
  * kvq_window_decode_step: one decode step with seq_len[s] already counting the new
  *   token (rows k_new / v_new of s, as in kvq_decode_step, but 16-byte aligned with
  *   strides a multiple of 8 elements): when n > W the token leaving the window
@@ -243,6 +244,8 @@ int32_t kvq_decode_step(const kvq_geom *g, int32_t n_q_heads, const void *q, con
  *   attention is that of kvq_window_decode_attn with the new token in the window;
  *   then the new token is written to ring row (n - 1) mod W.  The caller fills the
  *   ring for the prefill (tokens [n - W, n)) and quantizes the rest. */
+int64_t kvq_window_workspace_bytes(const kvq_geom *g, int32_t window, int32_t n_q_heads, int32_t n_seq,
+                                   int64_t max_len, int32_t kernel, int32_t tiles_per_split);
 int32_t kvq_window_decode_attn(const kvq_geom *g, int32_t window, int32_t n_q_heads, const void *q,
                                const void *win_k, const void *win_v, const uint8_t *cache,
                                const int64_t *seq_byte_off, const int32_t *seq_len, int32_t n_seq, int64_t max_len,

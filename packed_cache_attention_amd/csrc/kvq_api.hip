@@ -358,8 +358,12 @@ int32_t window_decode(const kvq_geom* g, int32_t window, int32_t n_q_heads, cons
     const int64_t packed_max = max_len > window ? max_len - window : 0;
     DecodePlan plan;
     st = check_decode(g, n_q_heads, q, cache, seq_byte_off, seq_len, n_seq, packed_max, k_bits, k_sigma, v_sigma,
-                      workspace, workspace_bytes, kernel, tiles_per_split, &plan, fn);
+                      workspace, (size_t)INT64_MAX, kernel, tiles_per_split, &plan, fn);
     if (st || n_seq == 0) return st;
+    const int n_chunks = plan.n_split + window_chunks(window);  // the packed chunks and the window's
+    if (n_chunks > 65535) return fail(KVQ_ERR_CAPACITY, fn, "chunks");
+    const int64_t ws_need = plan.workspace / plan.n_split * n_chunks;
+    if ((int64_t)workspace_bytes < ws_need) return fail(KVQ_ERR_WORKSPACE, fn, "workspace bytes");
     if (k_new) {
         if (!v_new) return fail(KVQ_ERR_ARG, fn, "null new-token pointer");
         if (new_stride_seq < 0 || new_stride_head < 0) return fail(KVQ_ERR_ARG, fn, "negative stride");
@@ -368,33 +372,42 @@ int32_t window_decode(const kvq_geom* g, int32_t window, int32_t n_q_heads, cons
     }
     if (!out) return fail(KVQ_ERR_ARG, fn, "null pointer");
     if (!aligned(out, 16)) return fail(KVQ_ERR_ALIGN, fn, "alignment");
-    // the packed part: the token leaving the window (if any) is appended in the same
-    // launch as the attention over the packed tokens
-    const int64_t ring_stride_seq = (int64_t)g->n_kv_heads * window * kHeadDim;
-    const AppendArgs app{k_new ? (const uint16_t*)win_k : nullptr, k_new ? (const uint16_t*)win_v : nullptr,
-                         ring_stride_seq, (int64_t)window * kHeadDim, window};
+    // one launch: the packed chunks (the token leaving the window packed by the tail
+    // tile's wave, which then writes the new token to its ring row) and the window chunk
+    AppendArgs app{};
+    app.k = k_new ? (const uint16_t*)win_k : nullptr;
+    app.v = k_new ? (const uint16_t*)win_v : nullptr;
+    app.stride_seq = (int64_t)g->n_kv_heads * window * kHeadDim;
+    app.stride_head = (int64_t)window * kHeadDim;
+    app.window = window;
+    app.ring_k = (uint16_t*)win_k;
+    app.ring_v = (uint16_t*)win_v;
+    app.k_new = (const uint16_t*)k_new;
+    app.v_new = (const uint16_t*)v_new;
+    app.new_stride_seq = new_stride_seq;
+    app.new_stride_head = new_stride_head;
     hipError_t e = launch_decode_partials(*g, plan, n_q_heads, (const uint16_t*)q, cache, seq_byte_off, seq_len,
                                           n_seq, packed_max, k_bits, k_sigma, v_sigma, softmax_scale,
                                           (float*)workspace, (hipStream_t)stream, app);
     if (e != hipSuccess) return hip_status(e, fn);
-    WindowArgs w;
-    w.q = (const uint16_t*)q;
-    w.n_q = n_q_heads;
-    w.g = n_q_heads / g->n_kv_heads;
-    w.n_kv = g->n_kv_heads;
-    w.window = window;
-    w.scale_log2 = softmax_scale * kLog2e;
-    w.win_k = (uint16_t*)win_k;
-    w.win_v = (uint16_t*)win_v;
-    w.seq_len = seq_len;
-    w.k_new = (const uint16_t*)k_new;
-    w.v_new = (const uint16_t*)v_new;
-    w.new_stride_seq = new_stride_seq;
-    w.new_stride_head = new_stride_head;
-    return hip_status(launch_merge_window(n_seq, plan.n_split, (const float*)workspace, out, w, (hipStream_t)stream),
+    return hip_status(launch_merge(n_seq * n_q_heads, n_chunks, (const float*)workspace, out,
+                                   (hipStream_t)stream),
                       fn);
 }
 }  // namespace
+
+int64_t kvq_window_workspace_bytes(const kvq_geom* g, int32_t window, int32_t n_q_heads, int32_t n_seq,
+                                   int64_t max_len, int32_t kernel, int32_t tiles_per_split) {
+    const char* fn = "kvq_window_workspace_bytes";
+    if (window < 1 || window > kWindowLimit) return fail(KVQ_ERR_ARG, fn, "window outside 1..1024");
+    if (max_len < 0) return fail(KVQ_ERR_ARG, fn, "negative count");
+    const int64_t packed_max = max_len > window ? max_len - window : 0;
+    const int64_t ws = kvq_decode_workspace_bytes_ex(g, n_q_heads, n_seq, packed_max, kernel, tiles_per_split);
+    if (ws < 0) return ws;
+    const int32_t ns = kvq_decode_n_split(g, n_q_heads, n_seq, packed_max, kernel, tiles_per_split);
+    if (ns < 0) return ns;
+    return ws / ns * (ns + window_chunks(window));
+}
 
 int32_t kvq_window_decode_attn(const kvq_geom* g, int32_t window, int32_t n_q_heads, const void* q,
                                const void* win_k, const void* win_v, const uint8_t* cache,

@@ -38,17 +38,23 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, const int64_t* __restrict__ seq_byte_off,
     const int32_t* __restrict__ seq_len, int64_t max_len, int64_t capacity, const uint8_t* __restrict__ k_bits,
     const float* __restrict__ k_sigma, const float* __restrict__ v_sigma, float scale_log2, int n_q, int g,
-    int pairing, int k_budget, int v_bits, int tiles_per_split, int n_split, float* __restrict__ ws, int len_sub) {
+    int pairing, int k_budget, int v_bits, int tiles_per_split, int n_split, float* __restrict__ ws,
+    AppendArgs app) {
     const int split = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
     const int tid = threadIdx.x;
+    __shared__ float s_x[kTile][kHeadDim + 1];  // dequantized K, then V, of the current tile
+    if (app.window > 0 && split >= n_split - window_chunks(app.window)) {  // the fp16 window's chunks
+        window_chunk<kGenericMaxGroup>(app, q, n_q, g, s, kvh, seq_len, scale_log2, ws, n_split,
+                                       split - (n_split - window_chunks(app.window)), &s_x[0][0]);
+        return;
+    }
     // packed tokens (seq_len less the fp16 window, if any)
-    const int64_t len = min(max((int64_t)seq_len[s] - len_sub, (int64_t)0), max_len);
+    const int64_t len = min(max((int64_t)seq_len[s] - app.window, (int64_t)0), max_len);
     const int64_t n_tiles_seq = (len + kTile - 1) / kTile;
     const int64_t t0 = (int64_t)split * tiles_per_split;
     const int64_t t1 = min(t0 + tiles_per_split, n_tiles_seq);
     const int D2 = kHeadDim + 2;
 
-    __shared__ float s_x[kTile][kHeadDim + 1];  // dequantized K, then V, of the current tile
     __shared__ float s_q[kGenericMaxGroup][kHeadDim];
     __shared__ float s_p[kGenericMaxGroup][kTile];
     __shared__ float s_m[kGenericMaxGroup], s_l[kGenericMaxGroup], s_a[kGenericMaxGroup];
@@ -252,192 +258,6 @@ __global__ __launch_bounds__(kMergeCols * kMergeGroups) void merge_kernel(const 
     }
 }
 
-// Merge with the fp16 recent window (the recent tokens kept unquantized): per row
-// (sequence, query head) and 32 output columns, the packed part's split partials are
-// merged as above, then exact attention over the window tokens -- positions
-// [len - nw, len), nw = min(len, window), each at ring row (position mod window), the
-// newest from k_new/v_new when given -- is folded in as one more partial.  Logits are
-// fp32 dot products of the binary16 values, in log2 units like the partials.  With
-// k_new, one workgroup per (sequence, KV head) then writes the new token to its ring
-// row; no workgroup of this launch reads that row (it held the token that left).
-constexpr int kWindowMax = 1024;
-
-__global__ __launch_bounds__(kMergeCols * kMergeGroups) void merge_window_kernel(const float* __restrict__ ws,
-                                                                                  int n_split, float* __restrict__ out,
-                                                                                  WindowArgs w) {
-    const int64_t row = blockIdx.x;
-    const int s = (int)(row / w.n_q), h = (int)(row % w.n_q), kvh = h / w.g;
-    const int tid = threadIdx.x, sg = tid / kMergeCols, cc = tid % kMergeCols, c = blockIdx.y * kMergeCols + cc;
-    constexpr int D2 = kHeadDim + 2;
-    __shared__ float s_q[kHeadDim];
-    __shared__ float s_z[kWindowMax];
-    __shared__ float s_red[kMergeGroups][kMergeCols];
-    __shared__ float s_m[kMergeGroups / 2][kMergeCols], s_l[kMergeGroups / 2][kMergeCols],
-        s_a[kMergeGroups / 2][kMergeCols];
-    __shared__ float s_wm, s_wl;
-    const int64_t len = max((int64_t)w.seq_len[s], (int64_t)0);
-    const int nw = (int)min(len, (int64_t)w.window);
-    const int64_t t0 = len - nw;
-    if (tid < kHeadDim) s_q[tid] = h2f(w.q[row * kHeadDim + tid]);
-    auto krow = [&](int i) -> const uint16_t* {  // window token i (position t0 + i)
-        const int64_t t = t0 + i;
-        if (w.k_new && t == len - 1) return w.k_new + (int64_t)s * w.new_stride_seq + (int64_t)kvh * w.new_stride_head;
-        return w.win_k + (((int64_t)s * w.n_kv + kvh) * w.window + t % w.window) * kHeadDim;
-    };
-    auto vrow = [&](int i) -> const uint16_t* {
-        const int64_t t = t0 + i;
-        if (w.v_new && t == len - 1) return w.v_new + (int64_t)s * w.new_stride_seq + (int64_t)kvh * w.new_stride_head;
-        return w.win_v + (((int64_t)s * w.n_kv + kvh) * w.window + t % w.window) * kHeadDim;
-    };
-
-    // the window's K pieces (first 128 tokens: eight lanes per token) and V values
-    // (four tokens per split group) go out with the partials' loads
-    const int kj = tid & 7;
-    uint4 kpre[2] = {uint4{0, 0, 0, 0}, uint4{0, 0, 0, 0}};
-    if (tid / 8 < nw) {
-        const uint4* kr = (const uint4*)krow(tid / 8) + 2 * kj;
-        kpre[0] = kr[0];
-        kpre[1] = kr[1];
-    }
-    constexpr int kVPre = 4;
-    uint32_t vpre[kVPre];
-#pragma unroll
-    for (int u = 0; u < kVPre; ++u) vpre[u] = sg + kMergeGroups * u < nw ? vrow(sg + kMergeGroups * u)[c] : 0u;
-
-    // ---- the packed part's partials (as merge_kernel)
-    const float* part = ws + row * n_split * D2;
-    float M = -INFINITY, L = 0.f, A = 0.f;
-    for (int sp0 = sg; sp0 < n_split; sp0 += kMergeGroups * kMergeUnroll) {
-        float m[kMergeUnroll], l[kMergeUnroll], o[kMergeUnroll];
-#pragma unroll
-        for (int u = 0; u < kMergeUnroll; ++u) {
-            const int sp = sp0 + u * kMergeGroups;
-            const float* p = part + (int64_t)min(sp, n_split - 1) * D2;
-            m[u] = sp < n_split ? p[0] : -INFINITY;
-            l[u] = p[1];
-            o[u] = p[2 + c];
-        }
-        float mx = M;
-#pragma unroll
-        for (int u = 0; u < kMergeUnroll; ++u) mx = fmaxf(mx, m[u]);
-        if (mx == -INFINITY) continue;
-        const float r = exp2f(M - mx);
-        L *= r;
-        A *= r;
-#pragma unroll
-        for (int u = 0; u < kMergeUnroll; ++u) {
-            const float a = exp2f(m[u] - mx);
-            L += a * l[u];
-            A += a * o[u];
-        }
-        M = mx;
-    }
-    {
-        const float oM = __shfl_xor(M, 32), oL = __shfl_xor(L, 32), oA = __shfl_xor(A, 32);
-        const float Mx = fmaxf(M, oM);
-        if (Mx != -INFINITY) {
-            const float a = exp2f(M - Mx), b = exp2f(oM - Mx);
-            L = a * L + b * oL;
-            A = a * A + b * oA;
-        }
-        M = Mx;
-    }
-    const int wv = tid / 64;
-    if ((tid & 63) < kMergeCols) { s_m[wv][cc] = M; s_l[wv][cc] = L; s_a[wv][cc] = A; }
-    __syncthreads();  // s_q ready too
-
-    // ---- window logits: eight lanes per token, 16 coordinates each
-    for (int i = tid / 8; i < nw; i += kMergeCols * kMergeGroups / 8) {
-        const int j = kj;
-        const uint4* kr = (const uint4*)krow(i) + 2 * j;
-        float z = 0.f;
-#pragma unroll
-        for (int k = 0; k < 2; ++k) {
-            const uint4 v4 = i == tid / 8 ? kpre[k] : kr[k];
-            const uint32_t wd[4] = {v4.x, v4.y, v4.z, v4.w};
-#pragma unroll
-            for (int e = 0; e < 4; ++e) {
-                z += s_q[16 * j + 8 * k + 2 * e] * h2f(wd[e] & 0xffffu);
-                z += s_q[16 * j + 8 * k + 2 * e + 1] * h2f(wd[e] >> 16);
-            }
-        }
-        z += __shfl_xor(z, 1);
-        z += __shfl_xor(z, 2);
-        z += __shfl_xor(z, 4);
-        if (j == 0) s_z[i] = z * w.scale_log2;
-    }
-    __syncthreads();
-    {  // window max, then weight sum: per wave, then across the 16 waves
-        float mx = tid < nw ? s_z[tid] : -INFINITY;
-        for (int off = 32; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-        if ((tid & 63) == 0) s_red[0][wv] = mx;
-        __syncthreads();
-        mx = s_red[0][tid & 15];
-        for (int off = 8; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
-        float l = (tid < nw && mx != -INFINITY) ? exp2f(s_z[tid] - mx) : 0.f;
-        if (tid < nw) s_z[tid] = l;  // the weights themselves from here on
-        for (int off = 32; off >= 1; off >>= 1) l += __shfl_xor(l, off);
-        if ((tid & 63) == 0) s_red[1][wv] = l;
-        __syncthreads();
-        if (tid == 0) {
-            float t = 0.f;
-            for (int k = 0; k < kMergeGroups / 2; ++k) t += s_red[1][k];
-            s_wm = mx;
-            s_wl = t;
-        }
-    }
-    __syncthreads();
-    const float wm = s_wm, wl = s_wl;
-    // window output for column c: group sg takes tokens sg, sg + 32, ...
-    float oacc = 0.f;
-#pragma unroll
-    for (int u = 0; u < kVPre; ++u)
-        if (sg + kMergeGroups * u < nw) oacc += s_z[sg + kMergeGroups * u] * h2f(vpre[u]);
-    for (int i = sg + kMergeGroups * kVPre; i < nw; i += kMergeGroups) oacc += s_z[i] * h2f(vrow(i)[c]);
-    __syncthreads();  // s_red's rows 0 and 1 were read above
-    s_red[sg][cc] = oacc;
-    __syncthreads();
-    if (wv == 0) {
-        const int k0 = (tid / kMergeCols) * (kMergeGroups / 4);
-        float Mt = -INFINITY;
-        for (int k = k0; k < k0 + kMergeGroups / 4; ++k) Mt = fmaxf(Mt, s_m[k][cc]);
-        float Lt = 0.f, At = 0.f;
-        if (Mt != -INFINITY) {
-            for (int k = k0; k < k0 + kMergeGroups / 4; ++k) {
-                const float a = exp2f(s_m[k][cc] - Mt);
-                Lt += a * s_l[k][cc];
-                At += a * s_a[k][cc];
-            }
-        }
-        const float oM = __shfl_xor(Mt, 32), oL = __shfl_xor(Lt, 32), oA = __shfl_xor(At, 32);
-        float Mx = fmaxf(Mt, oM);
-        if (Mx != -INFINITY) {
-            const float a = exp2f(Mt - Mx), b = exp2f(oM - Mx);
-            Lt = a * Lt + b * oL;
-            At = a * At + b * oA;
-        }
-        if (tid < kMergeCols) {
-            float ow = 0.f;
-            for (int k = 0; k < kMergeGroups; ++k) ow += s_red[k][cc];
-            const float M2 = fmaxf(Mx, wm);
-            if (M2 != -INFINITY) {
-                const float a = exp2f(Mx - M2), b = exp2f(wm - M2);
-                Lt = a * Lt + b * wl;
-                At = a * At + b * ow;
-            }
-            out[row * kHeadDim + c] = Lt > 0.f ? At / Lt : 0.f;
-        }
-    }
-    // ---- the new token into its ring row (one workgroup per sequence and KV head)
-    if (w.k_new && len > 0 && h % w.g == 0 && blockIdx.y == 0 && tid < 2 * (kHeadDim / 2)) {
-        const bool isv = tid >= kHeadDim / 2;
-        const int e = tid & (kHeadDim / 2 - 1);
-        const uint16_t* src = (isv ? w.v_new : w.k_new) + (int64_t)s * w.new_stride_seq + (int64_t)kvh * w.new_stride_head;
-        uint16_t* dst = (isv ? w.win_v : w.win_k) + (((int64_t)s * w.n_kv + kvh) * w.window + (len - 1) % w.window) * kHeadDim;
-        ((uint32_t*)dst)[e] = ((const uint32_t*)src)[e];
-    }
-}
-
 hipError_t launch_decode_mfma(const kvq_geom& g, const DecodePlan& plan, int n_q_heads, const uint16_t* q,
                               uint8_t* cache, const int64_t* seq_byte_off, const int32_t* seq_len, int n_seq,
                               int64_t max_len, const uint8_t* k_bits, const float* k_sigma, const float* v_sigma,
@@ -512,17 +332,11 @@ hipError_t launch_decode_partials(const kvq_geom& g, const DecodePlan& plan, int
                                                 seq_byte_off, st);
         if (e != hipSuccess) return e;
     }
-    dim3 grid(plan.n_split, g.n_kv_heads, n_seq);
+    const int n_chunks = plan.n_split + (app.window > 0 ? window_chunks(app.window) : 0);  // + the window's
+    dim3 grid(n_chunks, g.n_kv_heads, n_seq);
     hipLaunchKernelGGL(decode_generic_kernel, grid, dim3(256), 0, st, q, cache, seq_byte_off, seq_len, max_len,
                        g.capacity_tokens, k_bits, k_sigma, v_sigma, scale_log2, n_q_heads, grp, g.rope_pairing,
-                       g.k_budget, g.v_bits, plan.tiles_per_split, plan.n_split, partials, app.window);
-    return hipGetLastError();
-}
-
-hipError_t launch_merge_window(int n_seq, int n_split, const float* partials, float* out, const WindowArgs& w,
-                               hipStream_t st) {
-    hipLaunchKernelGGL(merge_window_kernel, dim3(n_seq * w.n_q, kHeadDim / kMergeCols), dim3(kMergeCols * kMergeGroups),
-                       0, st, partials, n_split, out, w);
+                       g.k_budget, g.v_bits, plan.tiles_per_split, n_chunks, partials, app);
     return hipGetLastError();
 }
 

@@ -282,6 +282,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     // land beside full workgroups instead of displacing one
     const int kvh = blockIdx.x, split = blockIdx.y, s = blockIdx.z;
     const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    if (app.window > 0 && split >= n_split - window_chunks(app.window)) {  // the fp16 window's chunks
+        window_chunk<8>(app, q, n_q, g, s, kvh, seq_len, scale_log2, ws, n_split,
+                        split - (n_split - window_chunks(app.window)), (float*)bufs);
+        return;
+    }
 
     // ---- every global load of the prologue goes out before anything waits on one
     // (no load sits under a branch, so none is waited for on its own)
@@ -381,6 +386,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     // holds them (idle until its first tile starts), else its own buffers (which then
     // fill only after the append) or the spare end of the shared buffer
     static_assert(WB >= 510 * 4 || BUF - kWaves * WB >= 510 * 4, "no room to stage the thresholds");
+    static_assert(BUF >= (8 * kHeadDim + 2 * 8 * kWindowChunk) * 4, "the window chunk's scratch lives in the tile buffers");
     float* const s_thr = (float*)(kStageInK1 ? bufs + app_wave * WB + KB
                                             : WB >= 510 * 4 ? bufs + app_wave * WB : bufs + kWaves * WB);
     if (wg_appends) {
@@ -473,6 +479,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         if (!kStageInK1 && tau < t1) {
             dma_k(tau, 0);
             dma_v(tau);
+        }
+        if (app.window > 0 && app.k_new != nullptr) {  // the step's new token takes the ring row just read
+            const int64_t nr = (int64_t)s * app.new_stride_seq + (int64_t)kvh * app.new_stride_head + 2 * lane;
+            const uint32_t kn = *(const uint32_t*)(app.k_new + nr);
+            const uint32_t vn = *(const uint32_t*)(app.v_new + nr);
+            const int64_t rr = (int64_t)s * app.stride_seq + (int64_t)kvh * app.stride_head +
+                               ((len_raw - 1) % app.window) * kHeadDim + 2 * lane;
+            *(uint32_t*)(app.ring_k + rr) = kn;
+            *(uint32_t*)(app.ring_v + rr) = vn;
         }
     }
 
@@ -698,12 +713,13 @@ hipError_t launch_mfma_v(const kvq_geom& g, const DecodePlan& plan, int n_q_head
                          float scale_log2, float* partials, hipStream_t st, const AppendArgs& app) {
     const int grp = n_q_heads / g.n_kv_heads;
     const int rd = (int)(k_record_bytes(g.k_budget) / 4);
-    dim3 grid(g.n_kv_heads, plan.n_split, n_seq);
+    const int n_chunks = plan.n_split + (app.window > 0 ? window_chunks(app.window) : 0);  // + the window's
+    dim3 grid(g.n_kv_heads, n_chunks, n_seq);
 #define KVQ_LAUNCH(RDV)                                                                                        \
     if (rd == RDV) {                                                                                            \
         hipLaunchKernelGGL((decode_mfma_kernel<V, RDV>), grid, dim3(256), 0, st, q, cache, seq_byte_off,       \
                            seq_len, max_len, g.capacity_tokens, k_bits, k_sigma, v_sigma, scale_log2, n_q_heads, \
-                           grp, g.rope_pairing, g.k_budget, plan.tiles_per_split, plan.n_split, partials, app); \
+                           grp, g.rope_pairing, g.k_budget, plan.tiles_per_split, n_chunks, partials, app);     \
         return hipGetLastError();                                                                               \
     }
     KVQ_LAUNCH(0) KVQ_LAUNCH(4) KVQ_LAUNCH(8) KVQ_LAUNCH(12) KVQ_LAUNCH(16)

@@ -76,17 +76,160 @@ hipError_t launch_quantize_pack(const kvq_geom& g, const uint16_t* k, const uint
 
 // The decode step's new token per sequence (row s at k + s*stride_seq + h*stride_head),
 // written to slot seq_len[s] - 1 before attention; k == nullptr: no append.
-// window > 0 (the fp16 recent window): the packed cache holds the first
-// seq_len[s] - window tokens, attention reads only those, and the appended token is
-// the one leaving the window -- row ((seq_len[s] - 1) mod window) of the ring at
-// k + s*stride_seq + h*stride_head, written to packed slot seq_len[s] - window - 1.
+//
+// window > 0 (the fp16 recent window): ring_k / ring_v hold the newest `window`
+// tokens of every (sequence, KV head) at rows [s][h][t mod window][128] (strides
+// stride_seq / stride_head); the packed cache holds the first seq_len[s] - window
+// tokens and attention over the packed part reads only those.  k / v then point at
+// the ring: in a step the token leaving the window (ring row (seq_len[s] - 1) mod
+// window) is packed into slot seq_len[s] - window - 1 by the wave that appends, which
+// then writes the step's new token (k_new / v_new rows, null: no step) to that ring
+// row.  The same launch computes the window's attention as one more chunk (the last,
+// index n_split - 1), reading the new token from k_new; when nothing leaves the
+// window (seq_len[s] <= window) that chunk's workgroup writes the new ring row.
 struct AppendArgs {
     const uint16_t* k;
     const uint16_t* v;
     int64_t stride_seq;
     int64_t stride_head;
     int32_t window;
+    uint16_t* ring_k;
+    uint16_t* ring_v;
+    const uint16_t* k_new;
+    const uint16_t* v_new;
+    int64_t new_stride_seq;
+    int64_t new_stride_head;
 };
+
+// window token i of sequence s (position len - nw + i; ring row (r0 + i) mod window with
+// r0 = (len - nw) mod window; the newest from k_new in a step)
+__device__ __forceinline__ const uint16_t* window_row(const AppendArgs& a, const uint16_t* ring, const uint16_t* nw_row,
+                                                      int s, int kvh, int i, int nw, int r0) {
+    if (nw_row != nullptr && i == nw - 1) return nw_row + (int64_t)s * a.new_stride_seq + (int64_t)kvh * a.new_stride_head;
+    int r = r0 + i;
+    if (r >= a.window) r -= a.window;
+    return ring + (int64_t)s * a.stride_seq + (int64_t)kvh * a.stride_head + (int64_t)r * kHeadDim;
+}
+
+// The window's chunks: window tokens (positions [len - nw, len), nw = min(len, window),
+// at their binary16 values) are split into groups of kWindowChunk, each attended by
+// one workgroup as one more split partial in the decode partials' format (m in log2
+// units, l, unnormalised o) -- the last window_chunks(window) partials of the row.
+constexpr int kWindowChunk = 32;
+__host__ __device__ inline int window_chunks(int window) { return (window + kWindowChunk - 1) / kWindowChunk; }
+
+// Window chunk wc of (s, kvh) for the g query heads: 256 threads, g <= GMAX <= 16;
+// scratch: LDS of at least (g * 128 + 2 * g * 32) floats.
+template <int GMAX>
+__device__ __forceinline__ void window_chunk(const AppendArgs& a, const uint16_t* __restrict__ q, int n_q, int g,
+                                             int s, int kvh, const int32_t* __restrict__ seq_len, float scale_log2,
+                                             float* __restrict__ ws, int n_split, int wc, float* scratch) {
+    const int tid = threadIdx.x;
+    const int64_t len = seq_len[s] > 0 ? (int64_t)seq_len[s] : 0;
+    const int nw = (int)(len < a.window ? len : a.window);
+    const int r0 = (int)((len - nw) % a.window);
+    const int base = wc * kWindowChunk;
+    const int nc = nw - base < kWindowChunk ? (nw - base > 0 ? nw - base : 0) : kWindowChunk;
+    float* s_q = scratch;                 // [g][128]
+    float* s_p = scratch + g * kHeadDim;  // [g][32]: logits, then weights
+    float* s_o = s_p + g * kWindowChunk;  // [g][32]: unused rows pad the odd tokens' share below
+    for (int i = tid; i < g * kHeadDim; i += 256) s_q[i] = h2f(q[((int64_t)s * n_q + (int64_t)kvh * g) * kHeadDim + i]);
+    __syncthreads();
+    if (nc > 0) {  // logits: token i = tid / 8, coordinates 16j .. 16j + 15
+        const int i = tid >> 3, j = tid & 7;
+        const int ii = i < nc ? i : nc - 1;  // a valid row for every load
+        const uint4* kr = (const uint4*)(window_row(a, a.ring_k, a.k_new, s, kvh, base + ii, nw, r0) + 16 * j);
+        const uint4 k0 = kr[0], k1 = kr[1];
+        const uint32_t kw[8] = {k0.x, k0.y, k0.z, k0.w, k1.x, k1.y, k1.z, k1.w};
+        float kf[16];
+#pragma unroll
+        for (int e = 0; e < 8; ++e) { kf[2 * e] = h2f(kw[e] & 0xffffu); kf[2 * e + 1] = h2f(kw[e] >> 16); }
+#pragma unroll
+        for (int h = 0; h < GMAX; ++h) {
+            if (h < g) {
+                const float* qh = s_q + h * kHeadDim + 16 * j;
+                float z = 0.f;
+#pragma unroll
+                for (int e = 0; e < 16; ++e) z += qh[e] * kf[e];
+                z += __shfl_xor(z, 1);
+                z += __shfl_xor(z, 2);
+                z += __shfl_xor(z, 4);
+                if (j == 0 && i < nc) s_p[h * kWindowChunk + i] = z * scale_log2;
+            }
+        }
+    }
+    __syncthreads();
+    // per head (32 lanes, one token each): max, weights, their sum
+    float mh = -INFINITY, lh = 0.f;
+    {
+        const int h = tid >> 5, l = tid & 31;
+        if (h < g && nc > 0) {
+            float z = l < nc ? s_p[h * kWindowChunk + l] : -INFINITY;
+            float mx = z;
+            for (int off = 16; off >= 1; off >>= 1) mx = fmaxf(mx, __shfl_xor(mx, off));
+            const float pw = l < nc ? exp2f(z - mx) : 0.f;
+            float ps = pw;
+            for (int off = 16; off >= 1; off >>= 1) ps += __shfl_xor(ps, off);
+            if (l < nc) s_p[h * kWindowChunk + l] = pw;
+            mh = mx;
+            lh = ps;
+        }
+    }
+    __syncthreads();
+    // output: thread (c, hh) takes coordinate c of every head over the tokens of parity hh
+    const int c = tid & (kHeadDim - 1), hh = tid >> 7;
+    float oacc[GMAX];
+#pragma unroll
+    for (int h = 0; h < GMAX; ++h) oacc[h] = 0.f;
+    if (nc > 0) {
+        uint32_t vr[kWindowChunk / 2];
+#pragma unroll
+        for (int u = 0; u < kWindowChunk / 2; ++u) {
+            const int i = min(hh + 2 * u, nc - 1);
+            vr[u] = window_row(a, a.ring_v, a.v_new, s, kvh, base + i, nw, r0)[c];
+        }
+#pragma unroll
+        for (int u = 0; u < kWindowChunk / 2; ++u) {
+            const int i = hh + 2 * u;
+            if (i < nc) {
+                const float vv = h2f(vr[u]);
+#pragma unroll
+                for (int h = 0; h < GMAX; ++h)
+                    if (h < g) oacc[h] += s_p[h * kWindowChunk + i] * vv;
+            }
+        }
+    }
+    // the odd tokens' share into LDS (over s_q, no longer read), then the even lanes write
+    __syncthreads();
+    if (hh == 1) {
+#pragma unroll
+        for (int h = 0; h < GMAX; ++h)
+            if (h < g) s_q[h * kHeadDim + c] = oacc[h];
+    }
+    if ((tid & 31) == 0 && (tid >> 5) < g) { s_o[2 * (tid >> 5)] = mh; s_o[2 * (tid >> 5) + 1] = lh; }
+    __syncthreads();
+    constexpr int D2 = kHeadDim + 2;
+    const int split = n_split - window_chunks(a.window) + wc;
+    if (hh == 0) {
+#pragma unroll
+        for (int h = 0; h < GMAX; ++h) {
+            if (h < g) {
+                float* part = ws + (((int64_t)s * n_q + (int64_t)kvh * g + h) * n_split + split) * D2;
+                part[2 + c] = oacc[h] + s_q[h * kHeadDim + c];
+                if (c == 0) { part[0] = s_o[2 * h]; part[1] = s_o[2 * h + 1]; }
+            }
+        }
+    }
+    // a step in which nothing leaves the window: the new token's ring row is free
+    if (wc == 0 && a.k_new != nullptr && len >= 1 && len <= a.window && tid < kHeadDim) {
+        const bool isv = tid >= kHeadDim / 2;
+        const int e = tid & (kHeadDim / 2 - 1);
+        const uint16_t* src = (isv ? a.v_new : a.k_new) + (int64_t)s * a.new_stride_seq + (int64_t)kvh * a.new_stride_head;
+        uint16_t* dst = (isv ? a.ring_v : a.ring_k) + (int64_t)s * a.stride_seq + (int64_t)kvh * a.stride_head +
+                        ((len - 1) % a.window) * kHeadDim;
+        ((uint32_t*)dst)[e] = ((const uint32_t*)src)[e];
+    }
+}
 
 struct DecodePlan {
     int kernel;           // KVQ_DECODE_GENERIC or KVQ_DECODE_MFMA
@@ -101,27 +244,12 @@ hipError_t launch_decode_partials(const kvq_geom& g, const DecodePlan& plan, int
                                   uint8_t* cache, const int64_t* seq_byte_off, const int32_t* seq_len,
                                   int n_seq, int64_t max_len, const uint8_t* k_bits, const float* k_sigma,
                                   const float* v_sigma, float softmax_scale, float* partials, hipStream_t st,
-                                  const AppendArgs& app = AppendArgs{nullptr, nullptr, 0, 0, 0});
+                                  const AppendArgs& app = AppendArgs{});
 // one token per sequence into slot seq_len[s] - 1 (the decode step's append, alone)
 hipError_t launch_append_step(const kvq_geom& g, int n_seq, const AppendArgs& app, const int32_t* seq_len,
                               const uint8_t* k_bits, const float* k_sigma, const float* v_sigma, uint8_t* cache,
                               const int64_t* seq_byte_off, hipStream_t st);
 hipError_t launch_merge(int n_rows, int n_split, const float* partials, float* out, hipStream_t st);
-// the split merge of the packed part folded with exact attention over the fp16 window
-// (ring [n_seq][n_kv][window][128]); with k_new, the step's new token is read from
-// k_new/v_new and written to its ring row after use
-struct WindowArgs {
-    const uint16_t* q;
-    int n_q, g, n_kv, window;
-    float scale_log2;
-    uint16_t* win_k;
-    uint16_t* win_v;
-    const int32_t* seq_len;
-    const uint16_t* k_new;
-    const uint16_t* v_new;
-    int64_t new_stride_seq, new_stride_head;
-};
-hipError_t launch_merge_window(int n_seq, int n_split, const float* partials, float* out, const WindowArgs& w,
-                               hipStream_t st);
+
 
 }  // namespace kvq

@@ -335,8 +335,9 @@ __global__ __launch_bounds__(64) void append_kernel(
     const int64_t* __restrict__ first_slot, const int32_t* __restrict__ n_new, const int64_t* __restrict__ src_row0,
     int max_new, int64_t capacity, const uint8_t* __restrict__ k_bits, const float* __restrict__ k_sigma,
     const float* __restrict__ v_sigma, uint8_t* __restrict__ cache, const int64_t* __restrict__ seq_byte_off,
-    int pairing, int k_budget, int v_bits, const int32_t* __restrict__ step_len, int window) {
+    int pairing, int k_budget, int v_bits, const int32_t* __restrict__ step_len, AppendArgs app) {
     const int s = blockIdx.z, h = blockIdx.y, j = blockIdx.x;
+    const int window = app.window;
     // either explicit runs (first_slot, n_new, src_row0) or the decode step: one token
     // per sequence, row s, into slot step_len[s] - 1; with an fp16 window of `window`
     // tokens, the token leaving it (ring row (step_len[s] - 1) mod window of row s)
@@ -426,6 +427,14 @@ __global__ __launch_bounds__(64) void append_kernel(
         scl[p] = sk;
         scl[kTile + p] = sv;
     }
+    if (window > 0 && app.k_new != nullptr) {  // the step's new token takes the ring row just read
+        const int64_t nr = (int64_t)s * app.new_stride_seq + (int64_t)h * app.new_stride_head + c0;
+        const uint32_t kn = *(const uint32_t*)(app.k_new + nr);
+        const uint32_t vn = *(const uint32_t*)(app.v_new + nr);
+        const int64_t rr = row * stride_tok + (int64_t)h * stride_head + ring_row + c0;
+        *(uint32_t*)(app.ring_k + rr) = kn;
+        *(uint32_t*)(app.ring_v + rr) = vn;
+    }
 }
 
 hipError_t launch_quantize_pack(const kvq_geom& g, const uint16_t* k, const uint16_t* v, int64_t stride_tok,
@@ -436,7 +445,7 @@ hipError_t launch_quantize_pack(const kvq_geom& g, const uint16_t* k, const uint
         dim3 grid(max_new, g.n_kv_heads, n_seq);
         hipLaunchKernelGGL(append_kernel, grid, dim3(64), 0, st, k, v, stride_tok, stride_head, first_slot, n_new,
                            src_row0, max_new, g.capacity_tokens, k_bits, k_sigma, v_sigma, cache, seq_byte_off,
-                           g.rope_pairing, g.k_budget, g.v_bits, (const int32_t*)nullptr, 0);
+                           g.rope_pairing, g.k_budget, g.v_bits, (const int32_t*)nullptr, AppendArgs{});
         return hipGetLastError();
     }
     // a run of max_new slots starting anywhere touches at most ceil(max_new/64) + 1 tiles
@@ -455,7 +464,7 @@ hipError_t launch_append_step(const kvq_geom& g, int n_seq, const AppendArgs& ap
     hipLaunchKernelGGL(append_kernel, grid, dim3(64), 0, st, app.k, app.v, app.stride_seq, app.stride_head,
                        (const int64_t*)nullptr, (const int32_t*)nullptr, (const int64_t*)nullptr, 1,
                        g.capacity_tokens, k_bits, k_sigma, v_sigma, cache, seq_byte_off, g.rope_pairing, g.k_budget,
-                       g.v_bits, seq_len, app.window);
+                       g.v_bits, seq_len, app);
     return hipGetLastError();
 }
 

@@ -82,6 +82,8 @@ def lib() -> C.CDLL:
     L.kvq_decode_step_partials.restype = I32
     L.kvq_decode_step.argtypes = [G, I32, P, P, P, I64, I64, P, P, P, I32, I64, P, P, P, F32, P, P, SZ, I32, I32, P]
     L.kvq_decode_step.restype = I32
+    L.kvq_window_workspace_bytes.argtypes = [G, I32, I32, I32, I64, I32, I32]
+    L.kvq_window_workspace_bytes.restype = I64
     L.kvq_window_decode_attn.argtypes = [G, I32, I32, P, P, P, P, P, P, I32, I64, P, P, P, F32, P, P, SZ, I32, I32,
                                          P]
     L.kvq_window_decode_attn.restype = I32
@@ -99,7 +101,8 @@ EXPORTS = ["kvq_version", "kvq_status_string", "kvq_tile_bytes", "kvq_cache_byte
            "kvq_block_energy", "kvq_allocate_bits", "kvq_quantize_pack", "kvq_decode_workspace_bytes",
            "kvq_decode_workspace_bytes_ex", "kvq_packed_decode_attn", "kvq_packed_decode_attn_ex",
            "kvq_decode_partials", "kvq_merge_partials", "kvq_decode_n_split", "kvq_decode_plan",
-           "kvq_decode_step_partials", "kvq_decode_step", "kvq_window_decode_attn", "kvq_window_decode_step"]
+           "kvq_decode_step_partials", "kvq_decode_step", "kvq_window_decode_attn", "kvq_window_decode_step",
+           "kvq_window_workspace_bytes"]
 
 
 def status_string(st: int) -> str:
@@ -280,6 +283,14 @@ def decode_step(g: Geom, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tens
         C.byref(g), n_q, _ptr(q), _ptr(k_new), _ptr(v_new), ss, sh, _ptr(cache), _ptr(seq_byte_off), _ptr(seq_len),
         n_seq, max_len, _ptr(k_bits), _ptr(k_sigma), _ptr(v_sigma), float(softmax_scale), _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), kernel, tiles_per_split, _stream(stream)))
+
+
+def window_workspace_bytes(g: Geom, window: int, n_q_heads: int, n_seq: int, max_len: int,
+                           kernel: int = DECODE_AUTO, tiles_per_split: int = 0) -> int:
+    r = lib().kvq_window_workspace_bytes(C.byref(g), window, n_q_heads, n_seq, max_len, kernel, tiles_per_split)
+    if r < 0:
+        raise KvqError("kvq_window_workspace_bytes", r)
+    return r
 
 
 def _window_ring(g: Geom, window: int, win_k: torch.Tensor, win_v: torch.Tensor):

@@ -61,8 +61,8 @@ def test_window_steps_match_oracle(case):
     q = torch.stack([x[2] for x in seqs]).cuda().contiguous()
 
     def ws_for(max_len):
-        return torch.empty(max(kvq.decode_workspace_bytes(g, nq, S, max(max_len - W, 0), kernel), 16) // 4,
-                           dtype=torch.float32, device="cuda")
+        return torch.empty(kvq.window_workspace_bytes(g, W, nq, S, max_len, kernel) // 4, dtype=torch.float32,
+                           device="cuda")
 
     def ref_attention(lens):
         oc = cache.cpu().numpy()
