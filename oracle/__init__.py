@@ -65,6 +65,7 @@ def lib() -> C.CDLL:
     L.or_decode_attention.argtypes = [P, I64, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, I64, F64, P]
     L.or_decode_attention_window.argtypes = [P, I64, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, I64, P, P, I64,
                                              F64, P]
+    L.or_prefill_attention.argtypes = [P, I64, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, I64, I64, F64, P]
     return L
 
 
@@ -322,4 +323,26 @@ def decode_attention_window(geom: Geometry, region: np.ndarray, q16: np.ndarray,
         _p(np.ascontiguousarray(kbits, np.uint8)), _p(np.ascontiguousarray(ksig, np.float32)),
         _p(np.ascontiguousarray(vsig, np.float32)), _p(T["lev"]), _p(T["lev_off"]),
         _p(np.ascontiguousarray(q16).view(np.uint16)), n_packed, _p(wk), _p(wv), wk.shape[0], float(scale), _p(out))
+    return out
+
+
+def prefill_attention(geom: Geometry, region: np.ndarray, q16: np.ndarray, q_start: int,
+                      kbits: np.ndarray, ksig: np.ndarray, vsig: np.ndarray, scale: float | None = None) -> np.ndarray:
+    """Causal fp64 attention of a chunk of queries q16 [n_tok, H_q, d] whose first sits
+    at position q_start: query j attends packed slots [0, q_start + j] (its own token
+    included, so the chunk must already be packed).  Row j equals decode attention at
+    length q_start + j + 1."""
+    T = tables()
+    d = geom.d
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    qq = np.ascontiguousarray(q16).view(np.uint16)
+    n_tok, nq = qq.shape[0], qq.shape[1]
+    assert q_start + n_tok <= geom.capacity
+    out = np.zeros((n_tok, nq, d), np.float64)
+    lib().or_prefill_attention(_p(np.ascontiguousarray(region)), geom.n_tiles, geom.H, nq, d, geom.pairing,
+                               geom.kb, geom.vb, _p(np.ascontiguousarray(kbits, np.uint8)),
+                               _p(np.ascontiguousarray(ksig, np.float32)),
+                               _p(np.ascontiguousarray(vsig, np.float32)), _p(T["lev"]), _p(T["lev_off"]),
+                               _p(qq), int(q_start), n_tok, float(scale), _p(out))
     return out

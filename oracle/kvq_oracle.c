@@ -657,3 +657,56 @@ void or_decode_attention_window(const uint8_t *region, int64_t n_tiles, int n_kv
         free(kc); free(vc); free(kscale); free(vscale); free(kh); free(vh);
     }
 }
+
+/*
+ * Chunked prefill attention over the packed cache (causal): a chunk of n_tok
+ * queries whose first sits at position q_start; query j (position q_start + j)
+ * attends slots [0, q_start + j] of the packed region -- the chunk's own tokens are
+ * read from the packed cache too, so they must have been packed before the call.
+ * Each query row is the same exact softmax attention as decode at length
+ * q_start + j + 1 (the page's packed-cache serving path, with the causal mask of
+ * ordinary prefill).
+ *   q   : binary16 [n_tok][n_q][d]
+ *   out : fp64     [n_tok][n_q][d]
+ */
+void or_prefill_attention(const uint8_t *region, int64_t n_tiles, int n_kv, int n_q, int d, int pairing,
+                          int k_budget, int v_bits, const uint8_t *kbits, const float *ksig, const float *vsig,
+                          const uint16_t *levels, const int *lev_off, const uint16_t *q, int64_t q_start,
+                          int64_t n_tok, double scale, double *out)
+{
+    int64_t tile = or_tile_bytes(d, k_budget, v_bits);
+    int g = n_q / n_kv;
+    int64_t n = q_start + n_tok;  /* slots any query of the chunk may read */
+    size_t n1 = (size_t)(n > 0 ? n : 1);
+#pragma omp parallel for schedule(dynamic, 1)
+    for (int kv = 0; kv < n_kv; kv++) {
+        const uint8_t *reg = region + (int64_t)kv * n_tiles * tile;
+        int nb = d / 2;
+        int kw[256], vw[256];
+        float ks[256], vs[256];
+        for (int i = 0; i < nb; i++) {
+            int p, qq;
+            block_coords(d, pairing, i, &p, &qq);
+            kw[p] = kw[qq] = kbits[kv * nb + i];
+            vw[p] = vw[qq] = v_bits;
+            ks[p] = ks[qq] = ksig[kv * nb + i];
+            vs[p] = vs[qq] = vsig[kv * nb + i];
+        }
+        uint16_t *kc = (uint16_t *)malloc(sizeof(uint16_t) * n1 * d);
+        uint16_t *vc = (uint16_t *)malloc(sizeof(uint16_t) * n1 * d);
+        float *kscale = (float *)malloc(sizeof(float) * n1);
+        float *vscale = (float *)malloc(sizeof(float) * n1);
+        double *kh = (double *)malloc(sizeof(double) * n1 * d);
+        double *vh = (double *)malloc(sizeof(double) * n1 * d);
+        or_unpack(reg, d, pairing, k_budget, v_bits, kbits + kv * nb, 0, n, kc, vc, kscale, vscale);
+        or_dequant(kc, n, d, kw, ks, kscale, levels, lev_off, kh);
+        or_dequant(vc, n, d, vw, vs, vscale, levels, lev_off, vh);
+        double qd[256];
+        for (int64_t j = 0; j < n_tok; j++)
+            for (int h = kv * g; h < (kv + 1) * g; h++) {
+                for (int c = 0; c < d; c++) qd[c] = h2d(q[(j * n_q + h) * d + c]);
+                or_attend(qd, kh, vh, q_start + j + 1, d, scale, out + (j * n_q + h) * d);
+            }
+        free(kc); free(vc); free(kscale); free(vscale); free(kh); free(vh);
+    }
+}

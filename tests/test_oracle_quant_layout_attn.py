@@ -233,6 +233,64 @@ def test_window_attention_pins():
         np.testing.assert_allclose(o, allw, rtol=1e-12, atol=1e-14)
 
 
+def test_prefill_attention_pins():
+    """Chunked prefill (causal): with the passthrough widths (K16V16) every row is
+    textbook causal attention on the fp16 inputs (the mask admits exactly the slots
+    up to the query's own position); with packed widths row j is the decode
+    attention at length q_start + j + 1; the chunk's first query at position 0 sees
+    only slot 0 (output = its dequantized value); a zero query averages the
+    dequantized values it sees; slots past the chunk's last query never matter."""
+    H, g, n, cap = 2, 3, 150, 192
+    k = rng.standard_normal((n, H, 128)).astype(np.float16)
+    v = rng.standard_normal((n, H, 128)).astype(np.float16)
+    sc = 1 / np.sqrt(128)
+    # passthrough: textbook causal attention, chunk in the middle and at the start
+    gp = oracle.Geometry(H, 1024, 16, cap)
+    kb16, ks16 = oracle.allocate(oracle.block_energy(k), 1024)
+    _, vs16 = oracle.allocate(oracle.block_energy(v), 1024)
+    reg16 = np.zeros(gp.seq_bytes, np.uint8)
+    oracle.quantize_pack(gp, reg16, k, v, 0, kb16, ks16, vs16)
+    for q0, nt in ((70, 30), (0, 9)):
+        q = rng.standard_normal((nt, H * g, 128)).astype(np.float16)
+        o = oracle.prefill_attention(gp, reg16, q, q0, kb16, ks16, vs16)
+        for j in range(nt):
+            for h in range(H * g):
+                ref = _textbook_attention(q[j, h], k[:q0 + j + 1, h // g], v[:q0 + j + 1, h // g], sc)
+                np.testing.assert_allclose(o[j, h], ref, rtol=1e-12, atol=1e-14)
+    # packed widths: rows are decode attention at their own lengths
+    geom = oracle.Geometry(H, 192, 3, cap)
+    kbits, ksig = oracle.allocate(oracle.block_energy(k), 192)
+    _, vsig = oracle.allocate(oracle.block_energy(v), 192, oracle.UNIFORM)
+    region = np.zeros(geom.seq_bytes, np.uint8)
+    res = oracle.quantize_pack(geom, region, k, v, 0, kbits, ksig, vsig)
+    q0, nt = 100, 50
+    q = rng.standard_normal((nt, H * g, 128)).astype(np.float16)
+    o = oracle.prefill_attention(geom, region, q, q0, kbits, ksig, vsig)
+    for j in (0, 1, 17, 49):
+        np.testing.assert_array_equal(o[j], oracle.decode_attention(geom, region, q[j], q0 + j + 1,
+                                                                    kbits, ksig, vsig))
+    # position 0 sees slot 0 only; a zero query is the mean of what it sees
+    vw = np.full(128, 3, np.int32)
+    vhat = [oracle.dequant(res[h][1], vw, oracle.per_coord(vsig[h], 128, 0), res[h][3]) for h in range(H)]
+    qz = rng.standard_normal((4, H * g, 128)).astype(np.float16)
+    qz[2] = 0
+    oz = oracle.prefill_attention(geom, region, qz, 0, kbits, ksig, vsig)
+    for h in range(H * g):
+        np.testing.assert_allclose(oz[0, h], vhat[h // g][0], rtol=1e-13, atol=1e-15)
+        np.testing.assert_allclose(oz[2, h], vhat[h // g][:3].mean(0), rtol=1e-12, atol=1e-14)
+    # slots after the chunk's last query are never read (chunk ends at slot 127)
+    q0, nt = 70, 58
+    q = rng.standard_normal((nt, H * g, 128)).astype(np.float16)
+    o = oracle.prefill_attention(geom, region, q, q0, kbits, ksig, vsig)
+    spoiled = region.copy()
+    view_len = geom.n_tiles * geom.tile
+    for h in range(H):
+        t = spoiled[h * view_len:(h + 1) * view_len].reshape(geom.n_tiles, geom.tile)
+        t[2, :] = 0xA5  # tile 2 = slots 128..191
+    o2 = oracle.prefill_attention(geom, spoiled, q, q0, kbits, ksig, vsig)
+    np.testing.assert_array_equal(o2, o)
+
+
 @pytest.mark.parametrize("cfg,n,heads", [("c1", 1024, [0]), ("c2", 8192, [0, 5])])
 def test_fidelity_gate_beats_uniform(cfg, n, heads):
     """Block-GTQ's query-key logit MAE is no worse than either uniform baseline."""
