@@ -259,6 +259,40 @@ int32_t kvq_window_decode_step(const kvq_geom *g, int32_t window, int32_t n_q_he
                                const uint8_t *k_bits, const float *k_sigma, const float *v_sigma,
                                float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
                                int32_t kernel, int32_t tiles_per_split, void *stream);
+/* Chunked prefill attention over the packed cache, causal ("RoPE-Aware Bit Allocation
+ * for KV-Cache Quantization": the long contexts only the packed cache holds are
+ * filled chunk by chunk; each chunk's queries attend everything packed before them
+ * and their own chunk, which the caller packs first with kvq_quantize_pack).
+ *   q        : device binary16 [n_seq][max_q][n_q_heads][128] (post-RoPE), 16-byte aligned
+ *   q_start  : device int32 [n_seq], position of sequence s's first chunk query
+ *   n_q      : device int32 [n_seq], its number of queries, 0 <= n_q[s] <= max_q
+ *   out      : device float [n_seq][max_q][n_q_heads][128], 16-byte aligned
+ * Query j < n_q[s] of sequence s (position q_start[s] + j) attends slots
+ * [0, q_start[s] + j] of the packed cache: its row of out is what
+ * kvq_packed_decode_attn gives for that query at seq_len q_start[s] + j + 1 (same
+ * scale, same dequantization, within the same fp32-accumulate tolerance).  Rows
+ * j >= n_q[s] are written as 0.  max_len must bound every q_start[s] + n_q[s] and be
+ * <= capacity_tokens (device values outside the contract are clamped so that reads
+ * stay inside the sequence's region; their results are unspecified).
+ * n_split: key-range splits per block of 128 query rows (0 = the planner's choice:
+ * enough workgroups to fill the device, at least 8 tiles per split); with 1 the
+ * attention kernel writes out itself, otherwise its partials (the decode partials'
+ * format, in the workspace) are merged by kvq_merge_partials' kernel on the same
+ * stream.  workspace: kvq_prefill_workspace_bytes(...) bytes (may be NULL when that is 0).
+ * Served: head_dim 128, k_budget <= 512 (block widths 0..8), v_bits 1..8, and
+ * n_q_heads / n_kv_heads <= 128; otherwise KVQ_ERR_SHAPE.  The binary16 MFMA
+ * operands bound |softmax weight * s^V_t| by 2^8 * ||v_t||, so value norms must stay
+ * below 255 (as in the matrix-core decode kernel).  Nothing but out and the
+ * workspace is written. */
+int32_t kvq_prefill_plan(const kvq_geom *g, int32_t n_q_heads, int32_t n_seq, int32_t max_q, int64_t max_len,
+                         int32_t n_split, int32_t *n_split_out, int64_t *workspace_out);
+int64_t kvq_prefill_workspace_bytes(const kvq_geom *g, int32_t n_q_heads, int32_t n_seq, int32_t max_q,
+                                    int64_t max_len, int32_t n_split);
+int32_t kvq_packed_prefill_attn(const kvq_geom *g, int32_t n_q_heads, const void *q, const uint8_t *cache,
+                                const int64_t *seq_byte_off, const int32_t *q_start, const int32_t *n_q,
+                                int32_t n_seq, int32_t max_q, int64_t max_len, const uint8_t *k_bits,
+                                const float *k_sigma, const float *v_sigma, float softmax_scale, float *out,
+                                void *workspace, size_t workspace_bytes, int32_t n_split, void *stream);
 /* Log-sum-exp merge of n_split partials per (sequence, head) in the format above:
  * out[s][h][c] = sum_k 2^(m_k - M) o_k,c / sum_k 2^(m_k - M) l_k, M = max_k m_k; rows
  * with no tokens give 0.  out: device float [n_seq][n_q_heads][128]. */

@@ -434,4 +434,65 @@ int32_t kvq_window_decode_step(const kvq_geom* g, int32_t window, int32_t n_q_he
                          workspace, workspace_bytes, kernel, tiles_per_split, stream, "kvq_window_decode_step");
 }
 
+
+// ---------------------------------------------------------------- chunked prefill
+namespace {
+int32_t check_prefill_shape(const kvq_geom* g, int32_t n_q_heads, int32_t n_seq, int32_t max_q, int64_t max_len,
+                            int32_t n_split, PrefillPlan* plan, const char* fn) {
+    int32_t st = check_geom(g, true, fn);
+    if (st) return st;
+    if (n_q_heads < 1 || n_q_heads % g->n_kv_heads) return fail(KVQ_ERR_SHAPE, fn, "n_q_heads");
+    if (n_seq < 0 || max_q < 0 || max_len < 0 || n_split < 0) return fail(KVQ_ERR_ARG, fn, "negative count");
+    if (n_seq > 65535) return fail(KVQ_ERR_SHAPE, fn, "n_seq");
+    if ((int64_t)n_seq * max_q * n_q_heads > 2147483647LL) return fail(KVQ_ERR_SHAPE, fn, "n_seq * max_q * n_q_heads");
+    if (max_len > g->capacity_tokens) return fail(KVQ_ERR_CAPACITY, fn, "max_len > capacity");
+    st = plan_prefill(*g, n_q_heads, n_seq, max_q, max_len, n_split, plan);
+    if (st) return fail(st, fn, "geometry not served by the prefill kernel (K16, V16 or group > 128)");
+    if ((int64_t)plan->n_qb * g->n_kv_heads > 2147483647LL) return fail(KVQ_ERR_SHAPE, fn, "grid");
+    return KVQ_OK;
+}
+}  // namespace
+
+int32_t kvq_prefill_plan(const kvq_geom* g, int32_t n_q_heads, int32_t n_seq, int32_t max_q, int64_t max_len,
+                         int32_t n_split, int32_t* n_split_out, int64_t* workspace_out) {
+    PrefillPlan plan;
+    const int32_t st = check_prefill_shape(g, n_q_heads, n_seq, max_q, max_len, n_split, &plan, "kvq_prefill_plan");
+    if (st) return st;
+    if (n_split_out) *n_split_out = plan.n_split;
+    if (workspace_out) *workspace_out = plan.workspace;
+    return KVQ_OK;
+}
+
+int64_t kvq_prefill_workspace_bytes(const kvq_geom* g, int32_t n_q_heads, int32_t n_seq, int32_t max_q,
+                                    int64_t max_len, int32_t n_split) {
+    PrefillPlan plan;
+    const int32_t st =
+        check_prefill_shape(g, n_q_heads, n_seq, max_q, max_len, n_split, &plan, "kvq_prefill_workspace_bytes");
+    return st ? st : plan.workspace;
+}
+
+int32_t kvq_packed_prefill_attn(const kvq_geom* g, int32_t n_q_heads, const void* q, const uint8_t* cache,
+                                const int64_t* seq_byte_off, const int32_t* q_start, const int32_t* n_q,
+                                int32_t n_seq, int32_t max_q, int64_t max_len, const uint8_t* k_bits,
+                                const float* k_sigma, const float* v_sigma, float softmax_scale, float* out,
+                                void* workspace, size_t workspace_bytes, int32_t n_split, void* stream) {
+    const char* fn = "kvq_packed_prefill_attn";
+    PrefillPlan plan;
+    int32_t st = check_prefill_shape(g, n_q_heads, n_seq, max_q, max_len, n_split, &plan, fn);
+    if (st) return st;
+    if (n_seq == 0 || max_q == 0) return KVQ_OK;
+    if (!q || !cache || !seq_byte_off || !q_start || !n_q || !k_bits || !k_sigma || !v_sigma || !out)
+        return fail(KVQ_ERR_ARG, fn, "null pointer");
+    if (plan.workspace > 0 && !workspace) return fail(KVQ_ERR_ARG, fn, "null workspace");
+    if (!aligned(q, 16) || !aligned(cache, 16) || !aligned(out, 16) || !aligned(workspace, 16) ||
+        !aligned(seq_byte_off, 8) || !aligned(q_start, 4) || !aligned(n_q, 4) || !aligned(k_sigma, 4) ||
+        !aligned(v_sigma, 4))
+        return fail(KVQ_ERR_ALIGN, fn, "alignment");
+    if ((int64_t)workspace_bytes < plan.workspace) return fail(KVQ_ERR_WORKSPACE, fn, "workspace bytes");
+    return hip_status(launch_prefill(*g, plan, n_q_heads, (const uint16_t*)q, cache, seq_byte_off, q_start, n_q, n_seq,
+                                     max_q, max_len, k_bits, k_sigma, v_sigma, softmax_scale, out, (float*)workspace,
+                                     (hipStream_t)stream),
+                      fn);
+}
+
 }  // extern "C"

@@ -251,5 +251,19 @@ hipError_t launch_append_step(const kvq_geom& g, int n_seq, const AppendArgs& ap
                               const int64_t* seq_byte_off, hipStream_t st);
 hipError_t launch_merge(int n_rows, int n_split, const float* partials, float* out, hipStream_t st);
 
+// chunked prefill attention (kvq_prefill.hip)
+struct PrefillPlan {
+    int n_qb;           // query blocks (128 query rows each) per (sequence, KV head)
+    int n_split;        // key-range splits per query block (1: the kernel writes the output itself)
+    int64_t workspace;  // bytes of split partials (0 when n_split == 1)
+};
+int plan_prefill(const kvq_geom& g, int n_q_heads, int n_seq, int max_q, int64_t max_len, int n_split_req,
+                 PrefillPlan* plan);
+hipError_t launch_prefill(const kvq_geom& g, const PrefillPlan& plan, int n_q_heads, const uint16_t* q,
+                          const uint8_t* cache, const int64_t* seq_byte_off, const int32_t* q_start,
+                          const int32_t* n_q, int n_seq, int max_q, int64_t max_len, const uint8_t* k_bits,
+                          const float* k_sigma, const float* v_sigma, float softmax_scale, float* out, float* ws,
+                          hipStream_t st);
+
 
 }  // namespace kvq

@@ -92,6 +92,12 @@ def lib() -> C.CDLL:
     L.kvq_window_decode_step.restype = I32
     L.kvq_decode_plan.argtypes = [G, I32, I32, I64, I32, I32, P, P, P, P]
     L.kvq_decode_plan.restype = I32
+    L.kvq_prefill_plan.argtypes = [G, I32, I32, I32, I64, I32, P, P]
+    L.kvq_prefill_plan.restype = I32
+    L.kvq_prefill_workspace_bytes.argtypes = [G, I32, I32, I32, I64, I32]
+    L.kvq_prefill_workspace_bytes.restype = I64
+    L.kvq_packed_prefill_attn.argtypes = [G, I32, P, P, P, P, P, I32, I32, I64, P, P, P, F32, P, P, SZ, I32, P]
+    L.kvq_packed_prefill_attn.restype = I32
     if L.kvq_version() != LAYOUT_VERSION:
         raise RuntimeError("libkvq.so layout version mismatch")
     return L
@@ -102,7 +108,8 @@ EXPORTS = ["kvq_version", "kvq_status_string", "kvq_tile_bytes", "kvq_cache_byte
            "kvq_decode_workspace_bytes_ex", "kvq_packed_decode_attn", "kvq_packed_decode_attn_ex",
            "kvq_decode_partials", "kvq_merge_partials", "kvq_decode_n_split", "kvq_decode_plan",
            "kvq_decode_step_partials", "kvq_decode_step", "kvq_window_decode_attn", "kvq_window_decode_step",
-           "kvq_window_workspace_bytes"]
+           "kvq_window_workspace_bytes", "kvq_prefill_plan", "kvq_prefill_workspace_bytes",
+           "kvq_packed_prefill_attn"]
 
 
 def status_string(st: int) -> str:
@@ -350,3 +357,36 @@ def decode_plan(g: Geom, n_q_heads: int, n_seq: int, max_len: int, kernel: int =
     _check("kvq_decode_plan", lib().kvq_decode_plan(C.byref(g), n_q_heads, n_seq, max_len, kernel, tiles_per_split,
                                                      C.byref(k), C.byref(t), C.byref(n), C.byref(w)))
     return {"kernel": k.value, "tiles_per_split": t.value, "n_split": n.value, "workspace": w.value}
+
+
+def prefill_plan(g: Geom, n_q_heads: int, n_seq: int, max_q: int, max_len: int, n_split: int = 0) -> dict:
+    n, w = C.c_int32(), C.c_int64()
+    _check("kvq_prefill_plan", lib().kvq_prefill_plan(C.byref(g), n_q_heads, n_seq, max_q, max_len, n_split,
+                                                       C.byref(n), C.byref(w)))
+    return {"n_split": n.value, "workspace": w.value}
+
+
+def prefill_workspace_bytes(g: Geom, n_q_heads: int, n_seq: int, max_q: int, max_len: int, n_split: int = 0) -> int:
+    r = lib().kvq_prefill_workspace_bytes(C.byref(g), n_q_heads, n_seq, max_q, max_len, n_split)
+    if r < 0:
+        raise KvqError("kvq_prefill_workspace_bytes", r)
+    return r
+
+
+def packed_prefill_attn(g: Geom, q: torch.Tensor, cache: torch.Tensor, seq_byte_off: torch.Tensor,
+                        q_start: torch.Tensor, n_q: torch.Tensor, max_len: int, k_bits: torch.Tensor,
+                        k_sigma: torch.Tensor, v_sigma: torch.Tensor, out: torch.Tensor,
+                        workspace: torch.Tensor | None = None, softmax_scale: float | None = None, n_split: int = 0,
+                        stream=None):
+    """Causal chunk attention: q [n_seq, max_q, n_q_heads, 128] fp16 contiguous -> out (same shape) fp32."""
+    assert q.dtype == torch.float16 and q.is_contiguous() and q.dim() == 4
+    assert out.dtype == torch.float32 and out.is_contiguous() and out.shape == q.shape
+    assert q_start.dtype == torch.int32 and n_q.dtype == torch.int32 and seq_byte_off.dtype == torch.int64
+    n_seq, max_q, n_qh = q.shape[0], q.shape[1], q.shape[2]
+    if softmax_scale is None:
+        softmax_scale = g.head_dim ** -0.5
+    ws_bytes = 0 if workspace is None else workspace.numel() * workspace.element_size()
+    _check("kvq_packed_prefill_attn", lib().kvq_packed_prefill_attn(
+        C.byref(g), n_qh, _ptr(q), _ptr(cache), _ptr(seq_byte_off), _ptr(q_start), _ptr(n_q), n_seq, max_q, max_len,
+        _ptr(k_bits), _ptr(k_sigma), _ptr(v_sigma), float(softmax_scale), _ptr(out), _ptr(workspace), ws_bytes,
+        n_split, _stream(stream)))

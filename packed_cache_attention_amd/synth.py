@@ -156,6 +156,20 @@ def gen_new_token(wl: Workload, seq: int, layer: int, pos: int, step: int, seed:
     return torch.stack(ks, 0), torch.stack(vs, 0), torch.cat(qs, 0)
 
 
+def gen_chunk_queries(wl: Workload, seq: int, layer: int, pos0: int, n_tok: int, seed: int = 0, device="cpu"):
+    """A prefill chunk's queries [n_tok, H_q, d] (fp16) at positions pos0 .. pos0 + n_tok - 1:
+    N(0, 1) rows rotated by RoPE at their own positions, one stream per KV head's group
+    (query head = KV head * group + i)."""
+    d, grp = wl.head_dim, wl.group
+    pos = torch.arange(pos0, pos0 + n_tok, device=device).repeat_interleave(grp)
+    out = []
+    for h in range(wl.n_kv_heads):
+        g = torch.Generator(device=device).manual_seed(seed * 10 ** 7 + 5 * 10 ** 6 + stream_id(wl, seq, layer, h))
+        q = torch.randn(n_tok * grp, d, generator=g, device=device, dtype=torch.float64)
+        out.append(_rope(q, pos, wl.theta).reshape(n_tok, grp, d).to(torch.float16))
+    return torch.cat(out, 1)
+
+
 def fp16_cache_bytes(wl: Workload) -> int:
     """Bytes an fp16 K/V cache of this workload would take (all layers, all sequences)."""
     return 2 * 2 * wl.head_dim * wl.n_kv_heads * wl.n_layers * sum(wl.seq_lens)

@@ -124,3 +124,19 @@ def test_host_validation_rejects_before_gpu():
     assert L.kvq_window_decode_attn(*a_args(2000, FAKE)) == -1
     assert L.kvq_window_decode_attn(*a_args(64, FAKE + 8)) == -4
     assert L.kvq_window_decode_attn(*a_args(64, FAKE, ws=16)) == -6
+    # chunked prefill: served geometries, capacity, pointers, alignment, workspace
+    p_args = lambda g_, nq, max_len, ws, q=FAKE, n_split=4, wsp=FAKE: (
+        C.byref(g_), nq, q, FAKE, FAKE, FAKE, FAKE, 1, 64, max_len, FAKE, FAKE, FAKE, 0.1, FAKE, wsp, ws, n_split,
+        None)
+    assert kvq.prefill_plan(good, 16, 1, 64, 512, 4) == {"n_split": 4, "workspace": 64 * 16 * 4 * 130 * 4}
+    assert kvq.prefill_workspace_bytes(good, 16, 1, 64, 512, 1) == 0
+    assert L.kvq_packed_prefill_attn(*p_args(good, 3, 512, 1 << 30)) == -2           # GQA ratio
+    assert L.kvq_packed_prefill_attn(*p_args(good, 2 * 129, 512, 1 << 30)) == -2     # group > 128
+    assert L.kvq_packed_prefill_attn(*p_args(kvq.geom(2, 1024, 3, 1024), 16, 512, 1 << 30)) == -2  # K16
+    assert L.kvq_packed_prefill_attn(*p_args(kvq.geom(2, 192, 16, 1024), 16, 512, 1 << 30)) == -2  # V16
+    assert L.kvq_packed_prefill_attn(*p_args(good, 16, 2048, 1 << 30)) == -5
+    assert L.kvq_packed_prefill_attn(*p_args(good, 16, 512, 16)) == -6
+    assert L.kvq_packed_prefill_attn(*p_args(good, 16, 512, 1 << 30, q=FAKE + 8)) == -4
+    assert L.kvq_packed_prefill_attn(*p_args(good, 16, 512, 1 << 30, q=None)) == -1
+    assert L.kvq_packed_prefill_attn(*p_args(good, 16, 512, 1 << 30, wsp=None)) == -1
+    assert L.kvq_packed_prefill_attn(*p_args(good, 16, 512, 1 << 30, n_split=-1)) == -1

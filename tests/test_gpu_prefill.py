@@ -1,0 +1,105 @@
+"""GPU parity for chunked prefill attention over the packed cache (causal): a chunk
+of queries at positions q_start .. q_start + n - 1 attends every slot up to its own
+position, the chunk itself packed first ("RoPE-Aware Bit Allocation for KV-Cache
+Quantization": the long contexts only the packed cache holds are filled chunk by
+chunk).  Checked against the oracle's causal attention row by row (2e-3 of the
+row's largest output per (sequence, query, head)); rows past a sequence's queries
+must be exactly zero.  Cases: GQA groups 1..8 (including 3 and 7, whose 128-row
+blocks are not full), K budgets 128..512 (block widths up to 8), value widths 2..8,
+both RoPE pairings, ragged batches with empty and one-query chunks, chunks at the
+start of the context and deep into it, forced key-range splits, and the 128K
+Qwen2.5-3B-shaped layer at full size on sampled rows."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from packed_cache_attention_amd import kvq, synth
+
+from pipeline import check_attention, run_batch, say
+
+pytestmark = pytest.mark.gpu
+
+CASES = [
+    # name, H_kv, group, k_budget, v_bits, pairing, [(q_start, n_q)], n_split
+    ("k3v3-g8", 2, 8, 192, 3, 0, [(1000, 77)], 0),
+    ("k3v3-g8-split3", 2, 8, 192, 3, 0, [(1000, 77)], 3),
+    ("k3v3-g8-split1", 2, 8, 192, 3, 0, [(1000, 77)], 1),
+    ("k2v2-g4-ragged", 2, 4, 128, 2, 0, [(300, 150), (0, 64)], 0),
+    ("k3v2-g7-batch", 2, 7, 192, 2, 0, [(500, 37), (64, 1), (200, 0)], 2),
+    ("k4v4-g2-interleaved", 1, 2, 256, 4, 1, [(250, 130)], 0),
+    ("k8v8-g1", 1, 1, 512, 8, 0, [(100, 140)], 0),
+    ("kodd-v5-g3", 1, 3, 131, 5, 0, [(190, 100)], 0),
+    ("k1v1-g8-start", 2, 8, 64, 1, 0, [(0, 200)], 0),
+]
+
+
+def _run(H, grp, kb, vb, pairing, chunks, n_split, seed=7, layer=0):
+    nq = H * grp
+    S = len(chunks)
+    wl = synth.Workload("pf", 1, nq, H, 1e6, (0,), kb, vb, "decay")
+    lens = [a + n for a, n in chunks]
+    seqs = [synth.gen_layer(wl.with_lens([lens[i]]), i, layer, n_tok=lens[i], seed=seed + i) for i in range(S)]
+    cap = 64 * ((max(lens) + 63) // 64 + 1)
+    # the whole context, chunk included, packed first (bytes checked against the oracle)
+    r = run_batch(seqs, kb, vb, cap, pairing=pairing, check_attn=False)
+    g, ogeom, region = r["g"], r["ogeom"], kvq.cache_bytes(r["g"])
+    max_q = max(n for _, n in chunks)
+    q = torch.zeros(S, max(max_q, 1), nq, 128, dtype=torch.float16)
+    for i, (a, n) in enumerate(chunks):
+        if n:
+            q[i, :n] = synth.gen_chunk_queries(wl, i, layer, a, n, seed=seed)
+    qd = q.cuda().contiguous()
+    out = torch.full(qd.shape, float("nan"), dtype=torch.float32, device="cuda")
+    ws_bytes = kvq.prefill_workspace_bytes(g, nq, S, qd.shape[1], max(lens), n_split)
+    ws = torch.empty(max(ws_bytes // 4, 4), dtype=torch.float32, device="cuda")
+    qs = torch.tensor([a for a, _ in chunks], dtype=torch.int32, device="cuda")
+    ns = torch.tensor([n for _, n in chunks], dtype=torch.int32, device="cuda")
+    kvq.packed_prefill_attn(g, qd, r["cache"], r["off"], qs, ns, max(lens), r["kbits"], r["ksig"], r["vsig"], out,
+                            ws, n_split=n_split)
+    o = out.cpu().numpy()
+    worst = 0.0
+    for i, (a, n) in enumerate(chunks):
+        assert (o[i, n:] == 0).all(), "rows past the chunk's queries must be zero"
+        if n == 0:
+            continue
+        ref = oracle.prefill_attention(ogeom, r["oc"][i * region:(i + 1) * region], q[i, :n].numpy(), a,
+                                       r["ob"], r["osig"], r["ovsig"])
+        worst = max(worst, check_attention(o[i, :n], ref))
+    return worst
+
+
+@pytest.mark.parametrize("case", CASES, ids=[c[0] for c in CASES])
+def test_prefill_matches_oracle(case):
+    name, H, grp, kb, vb, pairing, chunks, n_split = case
+    say("prefill %s" % name)
+    worst = _run(H, grp, kb, vb, pairing, chunks, n_split)
+    say("prefill %s ok, worst rel %.2e" % (name, worst))
+
+
+def test_prefill_c3_full_size_sampled_rows():
+    """Qwen2.5-3B-shaped 128K K3V3 layer: the last 512-token chunk of a chunked prefill
+    (queries at 130560 .. 131071 over the whole packed context) in the automatic plan;
+    sampled query rows against the oracle's decode attention at each row's length."""
+    wl = synth.WORKLOADS["c3"]
+    say("prefill c3 full size")
+    K, V, _ = synth.gen_layer(wl, 0, 0)
+    n = K.shape[0]
+    r = run_batch([(K, V, torch.zeros(wl.n_q_heads, 128, dtype=torch.float16))], wl.k_budget, wl.v_bits,
+                  synth.ceil_to(n + 64, 64), check_attn=False)
+    g, region = r["g"], kvq.cache_bytes(r["g"])
+    nt = 512
+    a = n - nt
+    q = synth.gen_chunk_queries(wl, 0, 0, a, nt).unsqueeze(0).contiguous()
+    qd = q.cuda()
+    out = torch.empty(qd.shape, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(kvq.prefill_workspace_bytes(g, wl.n_q_heads, 1, nt, n) // 4, 4), dtype=torch.float32,
+                     device="cuda")
+    kvq.packed_prefill_attn(g, qd, r["cache"], r["off"], torch.tensor([a], dtype=torch.int32, device="cuda"),
+                            torch.tensor([nt], dtype=torch.int32, device="cuda"), n, r["kbits"], r["ksig"], r["vsig"],
+                            out, ws)
+    o = out.cpu().numpy()[0]
+    for j in (0, 1, 255, 511):
+        ref = oracle.decode_attention(r["ogeom"], r["oc"][:region], q[0, j].numpy(), a + j + 1, r["ob"], r["osig"],
+                                      r["ovsig"])
+        say("row %d worst rel %.2e" % (j, check_attention(o[j][None], ref[None])))
