@@ -40,6 +40,7 @@ ROOT = os.path.dirname(os.path.abspath(__file__))
 sys.path.insert(0, ROOT)
 
 HBM_PEAK_GBPS = 8000.0
+MFMA_F16_PEAK_TFLOPS = 2500.0  # dense fp16 matrix-core peak (no sparsity)
 METRIC = "packed-cache decode-attn GB/s (% HBM peak) + quantize tokens/s, 128K K3V3"
 TRAFFIC_FILE = os.path.join(ROOT, "profiles", "decode_traffic.json")
 
@@ -110,6 +111,10 @@ def main():
     ap.add_argument("--unfused", action="store_true",
                     help="append with kvq_quantize_pack as a launch of its own instead of inside the attention kernel")
     ap.add_argument("--traffic-from", nargs=2, metavar=("FETCH_CSV", "WRITE_CSV"))
+    ap.add_argument("--prefill-chunk", type=int, default=2048,
+                    help="also time chunked prefill attention: each sequence's last N tokens as one chunk of "
+                         "queries over its whole packed context (0: skip)")
+    ap.add_argument("--prefill-split", type=int, default=0, help="key-range splits for the chunk (0: planner)")
     ap.add_argument("--window", type=int, default=128,
                     help="also time the fp16 recent-window step with this many recent tokens unquantized (0: skip)")
     args = ap.parse_args()
@@ -400,6 +405,68 @@ def main():
                 "pct_hbm_peak": round(100 * wval / HBM_PEAK_GBPS, 2), "step_bytes": int(wbytes),
                 "entry_point": "kvq_window_decode_step"}
 
+    # ------------------------------------------------------------ chunked prefill attention
+    # Each sequence's last C tokens as one chunk of queries (positions n - C .. n - 1)
+    # attending its whole packed context causally, every layer once per repetition.
+    # Algorithmic work: 4 d flops per (query head, attended key) (QK and PV, multiply
+    # and add); the kernel issues twice that on the matrix cores (hi + lo operand
+    # splits for q and for the softmax weights).
+    pres = None
+    if args.prefill_chunk > 0:
+        C_ = args.prefill_chunk
+        qstart = [max(n - C_, 0) for n in lens]
+        nqs = [n - a for n, a in zip(lens, qstart)]
+        max_q = max(nqs)
+        pq = torch.zeros(L, S, max_q, Hq, d, dtype=torch.float16, device=dev)
+        for l in range(L):
+            for s_ in range(S):
+                pq[l, s_, :nqs[s_]] = synth.gen_chunk_queries(wl, s_, l, qstart[s_], nqs[s_], seed=args.seed,
+                                                              device=dev)
+        pqs = torch.tensor(qstart, dtype=torch.int32, device=dev)
+        pns = torch.tensor(nqs, dtype=torch.int32, device=dev)
+        pmax = max(lens)
+        pplan = kvq.prefill_plan(g, Hq, S, max_q, pmax, args.prefill_split)
+        pws = torch.empty(max(pplan["workspace"] // 4, 4), dtype=torch.float32, device=dev)
+        pout = torch.empty(S, max_q, Hq, d, dtype=torch.float32, device=dev)
+
+        def pstep():
+            for l in range(L):
+                kvq.packed_prefill_attn(g, pq[l], cache[l], off, pqs, pns, pmax, kbits[l], ksig[l], vsig[l], pout,
+                                        pws, n_split=args.prefill_split)
+
+        pstep()
+        torch.cuda.synchronize()
+        preps = 2
+        e0.record()
+        for _ in range(preps):
+            pstep()
+        e1.record()
+        torch.cuda.synchronize()
+        pms = e0.elapsed_time(e1) / (preps * L)
+        pairs = sum(Hq * (n_ * a + n_ * (n_ + 1) // 2) for a, n_ in zip(qstart, nqs))
+        pflops = 4 * d * pairs
+        ptf = pflops / (pms / 1e3) / 1e12
+        # the chunk's own quantize + pack (its K/V rows are already resident)
+        qfirst = torch.tensor(qstart, dtype=torch.int64, device=dev)
+        qsrc = torch.tensor([int(r0) + a for r0, a in zip(row0, qstart)], dtype=torch.int64, device=dev)
+        chunk_cache = torch.zeros_like(cache[0])
+        kvq.quantize_pack(g, Kall[0], Vall[0], qfirst, pns, qsrc, max_q, kbits[0], ksig[0], vsig[0], chunk_cache, off)
+        torch.cuda.synchronize()
+        e0.record()
+        for l in range(L):
+            kvq.quantize_pack(g, Kall[l], Vall[l], qfirst, pns, qsrc, max_q, kbits[l], ksig[l], vsig[l],
+                              chunk_cache, off)
+        e1.record()
+        torch.cuda.synchronize()
+        qms = e0.elapsed_time(e1) / L
+        log("prefill chunk (%d queries per sequence, n_split %d): attention %.3f ms per layer = %.1f TFLOP/s "
+            "(%.1f%% of the fp16 MFMA peak), chunk quantize %.4f ms per layer"
+            % (C_, pplan["n_split"], pms, ptf, 100 * ptf / MFMA_F16_PEAK_TFLOPS, qms))
+        pres = {"chunk": C_, "entry_point": "kvq_packed_prefill_attn", "n_split": pplan["n_split"],
+                "ms_per_layer": round(pms, 5), "tflops": round(ptf, 2), "peak_tflops": MFMA_F16_PEAK_TFLOPS,
+                "frac": round(ptf / MFMA_F16_PEAK_TFLOPS, 4), "flops_per_layer": int(pflops),
+                "issued_mfma_tflops": round(2 * ptf, 2), "quantize_chunk_ms_per_layer": round(qms, 5)}
+
     traffic = None
     src_hash = kernel_source_hash("mfma" if kernel_name == "decode_mfma_kernel" else "generic")
     if os.path.exists(TRAFFIC_FILE):
@@ -457,6 +524,7 @@ def main():
                      "bytes_per_token_head": bytes_per_token_head},
         "cpu_baseline": cpu,
         "window_step": wres,
+        "prefill_chunk": pres,
     }
     print(json.dumps(result), flush=True)
 

@@ -274,7 +274,7 @@ int32_t kvq_window_decode_step(const kvq_geom *g, int32_t window, int32_t n_q_he
  * j >= n_q[s] are written as 0.  max_len must bound every q_start[s] + n_q[s] and be
  * <= capacity_tokens (device values outside the contract are clamped so that reads
  * stay inside the sequence's region; their results are unspecified).
- * n_split: key-range splits per block of 128 query rows (0 = the planner's choice:
+ * n_split: key-range splits per block of 256 query rows (0 = the planner's choice:
  * enough workgroups to fill the device, at least 8 tiles per split); with 1 the
  * attention kernel writes out itself, otherwise its partials (the decode partials'
  * format, in the workspace) are merged by kvq_merge_partials' kernel on the same

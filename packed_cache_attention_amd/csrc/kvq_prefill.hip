@@ -10,12 +10,15 @@
 //   z = s_t * sum_c (q_c sigma_c scale log2e) level[code_{t,c}]
 // and o = sum_t 2^(z_t - m) s^V_t level[vcode_{t,c}], times sigma^V_c at the end.
 //
-// One workgroup = 128 query rows (4 waves x 32) of one (sequence, KV head): row r
+// One workgroup = 256 query rows (8 waves x 32) of one (sequence, KV head): row r
 // is query token r / g, head r % g of the group.  Per 64-slot tile the workgroup
 // dequantizes K and V once into LDS as exact binary16 levels (K in K order, the
 // query operand permuted to match), then every wave runs
 //   S^T[key][row] = K . q'^T          v_mfma_f32_32x32x16_f16, q' split hi + lo
-//   O^T[coord][row] += V^T . P'^T     v_mfma_f32_32x32x16_f16, p.s^V split hi + lo
+//   O^T[coord][row] += V^T . P'^T     v_mfma_f32_32x32x16_f16, P' = p.s^V in binary16
+// (q' needs the split: a logit's error is its size times the operand's relative
+// error; a softmax weight's rounding moves the output by at most 2^-11 of the
+// weighted values, well inside the attention tolerance).
 // The QK accumulator holds a column (query row) per lane, so its row max is a lane
 // local max plus one permlane32 swap, and the accumulator itself, converted to
 // binary16, is the B operand of PV (keys permuted to the accumulator's row order,
@@ -27,35 +30,42 @@
 
 namespace kvq {
 
-constexpr int kPfRows = 128;                 // query rows per workgroup
+constexpr int kPfWaves = 8;                  // waves per workgroup, 32 query rows each
+constexpr int kPfThreads = 64 * kPfWaves;
+constexpr int kPfRows = 32 * kPfWaves;       // query rows per workgroup
 constexpr int kPfKS = kHeadDim + 8;          // binary16 per dequantized K row (272 B: conflict-free b128 reads)
 constexpr int kPfVS = kTile + 4;             // binary16 per dequantized V row (136 B: conflict-free b64 reads)
 constexpr int kPfMaxTB = kTile * 128 + kHeadDim * 8 * 8 + 2 * kTile * 4;  // largest tile served (K8, V8)
 constexpr int kPfChunks = kPfMaxTB / 16;
-constexpr int kPfDmaPerThread = (kPfChunks + 255) / 256;
+constexpr int kPfDmaPerThread = (kPfChunks + kPfThreads - 1) / kPfThreads;
 constexpr float kPfSlack = 8.f;
+constexpr int kPfMaxGroup = 128;             // query heads per KV head served
+static_assert(kPfMaxGroup <= kPfRows, "a workgroup holds at least one query token");
 
 struct PfSmem {
+    // the workgroup's query rows (binary16 [rows][128]) are staged over stage, kd and vd
+    // during the prologue
     alignas(16) uint8_t stage[2][kPfMaxTB];  // packed tiles, double-buffered
-    // dequantized K [key][K-order position] and V [coordinate][key]; the query rows
-    // (binary16 [128][128]) are staged here during the prologue
-    alignas(16) uint16_t kd[kTile * kPfKS];
-    alignas(16) uint16_t vd[kHeadDim * kPfVS];
+    alignas(16) uint16_t kd[kTile * kPfKS];   // dequantized K [key][K-order position]
+    alignas(16) uint16_t vd[kHeadDim * kPfVS];// dequantized V [coordinate][key]
+    uint32_t vpair[1024];    // value widths <= 5: entry a | b << v = levels (a, b) as a binary16 pair
     uint16_t lev[512];       // binary16 levels, width w at KVQ_CB_OFF(w)
     float fsig[kHeadDim];    // K-order position -> sigma^K of its block times scale log2e (0 past the fields)
     uint8_t fcoord[kHeadDim];// K-order position -> coordinate
     float vsig[kHeadDim];    // coordinate -> sigma^V
 };
-static_assert(sizeof(uint16_t) * (kTile * kPfKS + kHeadDim * kPfVS) >= kPfRows * kHeadDim * 2,
-              "the query rows are staged in the dequantized tiles");
+static_assert(2 * kPfMaxTB + sizeof(uint16_t) * (kTile * kPfKS + kHeadDim * kPfVS) >= kPfRows * kHeadDim * 2,
+              "the query rows are staged over the tile buffers");
+static_assert(kTile % kPfWaves == 0 && (kTile / kPfWaves) % 8 == 0 && (kHeadDim / kPfWaves) % 16 == 0,
+              "dequantization shares: whole batches of eight keys / coordinate pairs per wave");
 
 __device__ __forceinline__ uint32_t pack_h2(float a, float b) {
     return (uint32_t)__builtin_bit_cast(uint16_t, (_Float16)a) |
            ((uint32_t)__builtin_bit_cast(uint16_t, (_Float16)b) << 16);
 }
 
-// grid: x = q block + n_qb * KV head, y = split, z = sequence; 256 threads
-__global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(
+// grid: x = q block + n_qb * KV head, y = split, z = sequence; kPfThreads threads
+__global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2))) void prefill_kernel(
     const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, const int64_t* __restrict__ seq_byte_off,
     const int32_t* __restrict__ q_start, const int32_t* __restrict__ n_qtok, int max_q, int64_t max_len,
     int64_t capacity,
@@ -86,11 +96,10 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         const uint32_t base = (uint32_t)(uintptr_t)(lds_u8*)sm.stage[buf];
 #pragma unroll
         for (int k = 0; k < kPfDmaPerThread; ++k) {
-            const int ch = (4 * k + wave) * 64 + lane;
-            if ((4 * k + wave) * 64 < n_chunks && ch < n_chunks) dma16(src + 16 * ch, base + 16 * 64 * (4 * k + wave));
+            const int ch0 = (kPfWaves * k + wave) * 64, ch = ch0 + lane;
+            if (ch0 < n_chunks && ch < n_chunks) dma16(src + 16 * ch, base + 16 * ch0);
         }
     };
-    if (t0 < t1) dma_tile(t0, 0);
 
     // ---------------------------------------------------------------- prologue
     // this thread's row (the lane's QK/PV column) and its position
@@ -136,12 +145,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         sm.vsig[cp] = vs;
         sm.vsig[cq] = vs;
     }
-    for (int i = tid; i < 510; i += 256) sm.lev[i] = c_levels[i];
-    // the workgroup's query rows, binary16 [128][128], into the tile area (zero rows
+    for (int i = tid; i < 510; i += kPfThreads) sm.lev[i] = c_levels[i];
+    const bool vpairs = v_bits <= 5;
+    if (vpairs)
+        for (int e = tid; e < (1 << (2 * v_bits)); e += kPfThreads)
+            sm.vpair[e] = (uint32_t)c_levels[KVQ_CB_OFF(v_bits) + (e & ((1 << v_bits) - 1))] |
+                          ((uint32_t)c_levels[KVQ_CB_OFF(v_bits) + (e >> v_bits)] << 16);
+    // the workgroup's query rows, binary16 [rows][128], over the tile buffers (zero rows
     // where no valid query is)
     {
-        uint4* qs = (uint4*)sm.kd;
-        for (int i = tid; i < kPfRows * kHeadDim / 8; i += 256) {
+        uint4* qs = (uint4*)sm.stage;
+        for (int i = tid; i < kPfRows * kHeadDim / 8; i += kPfThreads) {
             const int rr = i >> 4, part = i & 15;
             const int jj = j0 + rr / g, hh = rr % g;
             uint4 v = uint4{0, 0, 0, 0};
@@ -154,7 +168,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     // B operands of QK: lane (h, col) holds K-order positions 16 ks + 8 h + i of row r
     uint32_t qh[8][4], ql[8][4];
     {
-        const uint16_t* qrow = sm.kd + r * kHeadDim;
+        const uint16_t* qrow = (const uint16_t*)sm.stage + r * kHeadDim;
 #pragma unroll
         for (int ks = 0; ks < 8; ++ks)
 #pragma unroll
@@ -168,8 +182,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             }
     }
     __syncthreads();  // the staged queries are consumed: the tile area is free
+    if (t0 < t1) dma_tile(t0, 0);
     // K-order positions past the fields stay zero in every dequantized K row
-    for (int i = tid; i < kTile * (kHeadDim / 2); i += 256) {
+    for (int i = tid; i < kTile * (kHeadDim / 2); i += kPfThreads) {
         const int t = i >> 6, pp = 2 * (i & 63);
         if (pp >= n_fields) *(uint32_t*)&sm.kd[t * kPfKS + pp] = 0u;
     }
@@ -180,7 +195,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
     const int kword = my_koff >> 5, kshift = my_koff & 31;
     const int sp = lane & 31, vpar = lane >> 5;                  // V: slots 2sp, 2sp+1; coordinate parity
     const int vbit = 2 * sp * v_bits, vword = vbit >> 5, vshift = vbit & 31;
-    const uint32_t vmask = (1u << v_bits) - 1u;
+    const uint32_t vmask = (1u << v_bits) - 1u, vmask2 = (1u << (2 * v_bits)) - 1u;
     const int vcb = 2 * KVQ_CB_OFF(v_bits);
 
     floatx16 o[4];
@@ -196,29 +211,56 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         __syncthreads();                         // ... every wave's; the other buffer is free
         if (tau + 1 < t1) dma_tile(tau + 1, buf ^ 1);
         const uint8_t* st = sm.stage[buf];
-        // ---- dequantize K: wave w keys 16w .. 16w+15, lane = block (two fields)
+        // ---- dequantize K: wave w keys [KPW w, KPW (w+1)), lane = block (two fields);
+        // eight keys at a time, every read of a batch issued before the first use
+        constexpr int KPW = kTile / kPfWaves, CPW = kHeadDim / kPfWaves;
         if (kw > 0) {
-#pragma unroll 4
-            for (int i = 0; i < 16; ++i) {
-                const int t = 16 * wave + i;
-                const uint32_t* rec = (const uint32_t*)(st + t * SK);
-                const uint32_t x = alignbit(rec[kword + 1], rec[kword], kshift);
-                const uint32_t a = lds_u16(sm.lev, kcb + 2 * (x & kmask));
-                const uint32_t b = lds_u16(sm.lev, kcb + 2 * ((x >> kw) & kmask));
-                *(uint32_t*)&sm.kd[t * kPfKS + my_pos] = a | (b << 16);
+#pragma unroll
+            for (int i0 = 0; i0 < KPW; i0 += 8) {
+                uint32_t lo[8], hi[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t* rec = (const uint32_t*)(st + (KPW * wave + i0 + i) * SK);
+                    lo[i] = rec[kword];
+                    hi[i] = rec[kword + 1];
+                }
+                uint32_t la[8], lb[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t x = alignbit(hi[i], lo[i], kshift);
+                    la[i] = lds_u16(sm.lev, kcb + 2 * (x & kmask));
+                    lb[i] = lds_u16(sm.lev, kcb + 2 * ((x >> kw) & kmask));
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) *(uint32_t*)&sm.kd[(KPW * wave + i0 + i) * kPfKS + my_pos] = la[i] | (lb[i] << 16);
             }
         }
-        // ---- dequantize V: wave w coordinates 32w .. 32w+31, lane = (slot pair, parity)
+        // ---- dequantize V: wave w coordinates [CPW w, CPW (w+1)), lane = (slot pair,
+        // coordinate parity); one pair lookup per two slots for widths <= 5
         {
             const uint32_t* runs = (const uint32_t*)(st + KB);
-#pragma unroll 4
-            for (int i = 0; i < 16; ++i) {
-                const int c = 32 * wave + 2 * i + vpar;
-                const uint32_t* run = runs + c * 2 * v_bits;
-                const uint32_t x = alignbit(run[vword + 1], run[vword], vshift);
-                const uint32_t a = lds_u16(sm.lev, vcb + 2 * (x & vmask));
-                const uint32_t b = lds_u16(sm.lev, vcb + 2 * ((x >> v_bits) & vmask));
-                *(uint32_t*)&sm.vd[c * kPfVS + 2 * sp] = a | (b << 16);
+#pragma unroll
+            for (int i0 = 0; i0 < CPW / 2; i0 += 8) {
+                uint32_t lo[8], hi[8];
+#pragma unroll
+                for (int i = 0; i < 8; ++i) {
+                    const uint32_t* run = runs + (CPW * wave + 2 * (i0 + i) + vpar) * 2 * v_bits;
+                    lo[i] = run[vword];
+                    hi[i] = run[vword + 1];
+                }
+                uint32_t lv[8];
+                if (vpairs) {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) lv[i] = lds_u32(sm.vpair, 4 * (alignbit(hi[i], lo[i], vshift) & vmask2));
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const uint32_t x = alignbit(hi[i], lo[i], vshift);
+                        lv[i] = lds_u16(sm.lev, vcb + 2 * (x & vmask)) | (lds_u16(sm.lev, vcb + 2 * ((x >> v_bits) & vmask)) << 16);
+                    }
+                }
+#pragma unroll
+                for (int i = 0; i < 8; ++i) *(uint32_t*)&sm.vd[(CPW * wave + 2 * (i0 + i) + vpar) * kPfVS + 2 * sp] = lv[i];
             }
         }
         __syncthreads();
@@ -226,6 +268,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
         const float* skl = (const float*)(st + KB + VR);
         const float* svl = skl + kTile;
         const int64_t key0 = tau * kTile;
+        // keys of this tile the row may see: index <= lim (-1: none)
+        const int lim = row_valid ? (int)min(max(rpos - key0, (int64_t)-1), (int64_t)kTile) : -1;
 #pragma unroll
         for (int kb = 0; kb < 2; ++kb) {
             floatx16 acc;
@@ -242,7 +286,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
                 acc = __builtin_amdgcn_mfma_f32_32x32x16_f16(a.h, bl.h, acc, 0, 0, 0);
             }
             // logits: element i is key 32 kb + 8 (i/4) + 4 h + i%4
-            const bool need_mask = !row_valid || key0 + 32 * kb + 31 > rpos;
+            const bool need_mask = lim < 32 * kb + 31;
             float tm = -INFINITY;
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
@@ -253,7 +297,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
                 if (need_mask) {
 #pragma unroll
                     for (int e = 0; e < 4; ++e)
-                        if (!row_valid || key0 + kk + e > rpos) acc[4 * jj + e] = -INFINITY;
+                        if (kk + e > lim) acc[4 * jj + e] = -INFINITY;
                 }
 #pragma unroll
                 for (int e = 0; e < 4; ++e) tm = fmaxf(tm, acc[4 * jj + e]);
@@ -271,7 +315,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
             }
             const float mb = mref == -INFINITY ? 0.f : mref;  // rows that have seen nothing keep p = 0
             float psum = 0.f;
-            uint32_t ph[8], pl[8];  // P' as binary16 pairs, hi and lo, in the accumulator's key order
+            uint32_t ph[8];  // P' (p s^V) as binary16 pairs in the accumulator's key order
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const float4 sv = *(const float4*)(svl + 32 * kb + 8 * jj + 4 * h);
@@ -283,21 +327,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
                     psum += p;
                     pv[e] = p * svv[e];
                 }
-#pragma unroll
-                for (int e = 0; e < 4; e += 2) {
-                    const _Float16 a = (_Float16)pv[e], b = (_Float16)pv[e + 1];
-                    ph[2 * jj + e / 2] = (uint32_t)__builtin_bit_cast(uint16_t, a) |
-                                         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
-                    pl[2 * jj + e / 2] = pack_h2(pv[e] - (float)a, pv[e + 1] - (float)b);
-                }
+                ph[2 * jj] = pack_h2(pv[0], pv[1]);
+                ph[2 * jj + 1] = pack_h2(pv[2], pv[3]);
             }
             lrun += psum;
             // PV: MFMA m takes keys 32 kb + 16 m + 8 (i/4) + 4 h + i%4, i = 0..7
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
-                H8 bh, bl;
+                H8 bp;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) { bh.u[u] = ph[4 * m + u]; bl.u[u] = pl[4 * m + u]; }
+                for (int u = 0; u < 4; ++u) bp.u[u] = ph[4 * m + u];
 #pragma unroll
                 for (int cb = 0; cb < 4; ++cb) {
                     const uint16_t* vrow = &sm.vd[(32 * cb + col) * kPfVS + 32 * kb + 16 * m + 4 * h];
@@ -305,8 +344,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
                     const uint2 v1 = *(const uint2*)(vrow + 8);
                     H8 a;
                     a.u[0] = v0.x; a.u[1] = v0.y; a.u[2] = v1.x; a.u[3] = v1.y;
-                    o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a.h, bh.h, o[cb], 0, 0, 0);
-                    o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a.h, bl.h, o[cb], 0, 0, 0);
+                    o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a.h, bp.h, o[cb], 0, 0, 0);
                 }
             }
         }
@@ -347,7 +385,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(2))) void p
 int plan_prefill(const kvq_geom& g, int n_q_heads, int n_seq, int max_q, int64_t max_len, int n_split_req,
                  PrefillPlan* plan) {
     const int grp = n_q_heads / g.n_kv_heads;
-    if (g.head_dim != kHeadDim || g.v_bits > 8 || g.k_budget > 8 * kMaxBlocks || grp > kPfRows)
+    if (g.head_dim != kHeadDim || g.v_bits > 8 || g.k_budget > 8 * kMaxBlocks || grp > kPfMaxGroup)
         return KVQ_ERR_SHAPE;
     const int qt = kPfRows / grp;
     plan->n_qb = (max_q + qt - 1) / qt;
@@ -359,7 +397,7 @@ int plan_prefill(const kvq_geom& g, int n_q_heads, int n_seq, int max_q, int64_t
             int dev = 0, cus = 0, occ = 0;
             if (hipGetDevice(&dev) == hipSuccess &&
                 hipDeviceGetAttribute(&cus, hipDeviceAttributeMultiprocessorCount, dev) == hipSuccess &&
-                hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, prefill_kernel, 256, 0) == hipSuccess && occ > 0)
+                hipOccupancyMaxActiveBlocksPerMultiprocessor(&occ, prefill_kernel, kPfThreads, 0) == hipSuccess && occ > 0)
                 slots = cus * occ;
             else
                 slots = 512;
@@ -383,7 +421,7 @@ hipError_t launch_prefill(const kvq_geom& g, const PrefillPlan& plan, int n_q_he
                           const float* v_sigma, float softmax_scale, float* out, float* ws, hipStream_t st) {
     const int grp = n_q_heads / g.n_kv_heads;
     dim3 grid(plan.n_qb * g.n_kv_heads, plan.n_split, n_seq);
-    hipLaunchKernelGGL(prefill_kernel, grid, dim3(256), 0, st, q, cache, seq_byte_off, q_start, n_q, max_q,
+    hipLaunchKernelGGL(prefill_kernel, grid, dim3(kPfThreads), 0, st, q, cache, seq_byte_off, q_start, n_q, max_q,
                        max_len, g.capacity_tokens, k_bits, k_sigma, v_sigma, softmax_scale * kLog2e, n_q_heads, grp,
                        g.rope_pairing, (int)k_record_bytes(g.k_budget), g.v_bits, plan.n_qb, plan.n_split, ws, out);
     hipError_t e = hipGetLastError();
