@@ -340,7 +340,48 @@ hipError_t launch_decode_partials(const kvq_geom& g, const DecodePlan& plan, int
     return hipGetLastError();
 }
 
+// The same merge for a few splits per row (the prefill's key-range splits): thread
+// (row, coordinate), two rows per workgroup, every split's partial in one pass with
+// a running maximum.
+constexpr int kMergeSmallMax = 16;
+__global__ __launch_bounds__(2 * kHeadDim) void merge_small_kernel(const float* __restrict__ ws, int n_split,
+                                                                   int64_t n_rows, float* __restrict__ out) {
+    const int64_t row = (int64_t)blockIdx.x * 2 + (threadIdx.x >> 7);
+    const int c = threadIdx.x & (kHeadDim - 1);
+    if (row >= n_rows) return;
+    constexpr int D2 = kHeadDim + 2;
+    const float* part = ws + row * n_split * D2;
+    float m[kMergeSmallMax], l[kMergeSmallMax], o[kMergeSmallMax];
+    float M = -INFINITY;
+#pragma unroll
+    for (int j = 0; j < kMergeSmallMax; ++j) {
+        if (j < n_split) {
+            m[j] = part[j * D2];
+            l[j] = part[j * D2 + 1];
+            o[j] = part[j * D2 + 2 + c];
+            M = fmaxf(M, m[j]);
+        }
+    }
+    float L = 0.f, A = 0.f;
+    if (M != -INFINITY) {
+#pragma unroll
+        for (int j = 0; j < kMergeSmallMax; ++j) {
+            if (j < n_split) {
+                const float a = exp2f(m[j] - M);
+                L += a * l[j];
+                A += a * o[j];
+            }
+        }
+    }
+    out[row * kHeadDim + c] = L > 0.f ? A / L : 0.f;
+}
+
 hipError_t launch_merge(int n_rows, int n_split, const float* partials, float* out, hipStream_t st) {
+    if (n_split <= kMergeSmallMax) {
+        hipLaunchKernelGGL(merge_small_kernel, dim3((n_rows + 1) / 2), dim3(2 * kHeadDim), 0, st, partials, n_split,
+                           (int64_t)n_rows, out);
+        return hipGetLastError();
+    }
     hipLaunchKernelGGL(merge_kernel, dim3(n_rows, kHeadDim / kMergeCols), dim3(kMergeCols * kMergeGroups), 0, st,
                        partials, n_split, out);
     return hipGetLastError();
