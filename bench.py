@@ -409,8 +409,8 @@ def main():
     # Each sequence's last C tokens as one chunk of queries (positions n - C .. n - 1)
     # attending its whole packed context causally, every layer once per repetition.
     # Algorithmic work: 4 d flops per (query head, attended key) (QK and PV, multiply
-    # and add); the kernel issues 1.5 times that on the matrix cores (QK runs twice,
-    # for the hi and lo parts of q).
+    # and add); the kernel issues twice that on the matrix cores (hi + lo operand
+    # splits of q and of the softmax weights).
     pres = None
     if args.prefill_chunk > 0:
         C_ = args.prefill_chunk
@@ -465,7 +465,7 @@ def main():
         pres = {"chunk": C_, "entry_point": "kvq_packed_prefill_attn", "n_split": pplan["n_split"],
                 "ms_per_layer": round(pms, 5), "tflops": round(ptf, 2), "peak_tflops": MFMA_F16_PEAK_TFLOPS,
                 "frac": round(ptf / MFMA_F16_PEAK_TFLOPS, 4), "flops_per_layer": int(pflops),
-                "issued_mfma_tflops": round(1.5 * ptf, 2), "quantize_chunk_ms_per_layer": round(qms, 5)}
+                "issued_mfma_tflops": round(2 * ptf, 2), "quantize_chunk_ms_per_layer": round(qms, 5)}
 
     traffic = None
     src_hash = kernel_source_hash("mfma" if kernel_name == "decode_mfma_kernel" else "generic")

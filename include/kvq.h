@@ -279,11 +279,12 @@ int32_t kvq_window_decode_step(const kvq_geom *g, int32_t window, int32_t n_q_he
  * attention kernel writes out itself, otherwise its partials (the decode partials'
  * format, in the workspace) are merged by kvq_merge_partials' kernel on the same
  * stream.  workspace: kvq_prefill_workspace_bytes(...) bytes (may be NULL when that is 0).
- * Served: head_dim 128, k_budget <= 512 (block widths 0..8), v_bits 1..8, and
- * n_q_heads / n_kv_heads <= 128; otherwise KVQ_ERR_SHAPE.  The binary16 MFMA
- * operands bound |softmax weight * s^V_t| by 2^8 * ||v_t||, so value norms must stay
- * below 255 (as in the matrix-core decode kernel).  Nothing but out and the
- * workspace is written. */
+ * Served: head_dim 128 (every budget and value width, the K16 / V16 passthroughs
+ * included) and n_q_heads / n_kv_heads <= 128; otherwise KVQ_ERR_SHAPE.  The
+ * binary16 MFMA operands bound |softmax weight * s^V_t| by 2^8 * ||v_t||, so value
+ * norms must stay below 255 (as in the matrix-core decode kernel; no bound at V16,
+ * whose weights enter without a token scale).
+ * Nothing but out and the workspace is written. */
 int32_t kvq_prefill_plan(const kvq_geom *g, int32_t n_q_heads, int32_t n_seq, int32_t max_q, int64_t max_len,
                          int32_t n_split, int32_t *n_split_out, int64_t *workspace_out);
 int64_t kvq_prefill_workspace_bytes(const kvq_geom *g, int32_t n_q_heads, int32_t n_seq, int32_t max_q,

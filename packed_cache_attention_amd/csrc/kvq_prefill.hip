@@ -15,10 +15,10 @@
 // dequantizes K and V once into LDS as exact binary16 levels (K in K order, the
 // query operand permuted to match), then every wave runs
 //   S^T[key][row] = K . q'^T          v_mfma_f32_32x32x16_f16, q' split hi + lo
-//   O^T[coord][row] += V^T . P'^T     v_mfma_f32_32x32x16_f16, P' = p.s^V in binary16
-// (q' needs the split: a logit's error is its size times the operand's relative
-// error; a softmax weight's rounding moves the output by at most 2^-11 of the
-// weighted values, well inside the attention tolerance).
+//   O^T[coord][row] += V^T . P'^T     v_mfma_f32_32x32x16_f16, P' = p.s^V split hi + lo
+// (both operands split so that products keep about 22 bits, as in decode: a single
+// binary16 weight would move the output by up to 2^-11 of the weighted values,
+// which values cancelling across all coordinates could blow past the tolerance).
 // The QK accumulator holds a column (query row) per lane, so its row max is a lane
 // local max plus one permlane32 swap, and the accumulator itself, converted to
 // binary16, is the B operand of PV (keys permuted to the accumulator's row order,
@@ -35,7 +35,7 @@ constexpr int kPfThreads = 64 * kPfWaves;
 constexpr int kPfRows = 32 * kPfWaves;       // query rows per workgroup
 constexpr int kPfKS = kHeadDim + 8;          // binary16 per dequantized K row (272 B: conflict-free b128 reads)
 constexpr int kPfVS = kTile + 4;             // binary16 per dequantized V row (136 B: conflict-free b64 reads)
-constexpr int kPfMaxTB = kTile * 128 + kHeadDim * 8 * 8 + 2 * kTile * 4;  // largest tile served (K8, V8)
+constexpr int kPfMaxTB = kTile * 256 + kHeadDim * 8 * 16 + 2 * kTile * 4;  // largest tile (K16, V16 passthrough)
 constexpr int kPfChunks = kPfMaxTB / 16;
 constexpr int kPfDmaPerThread = (kPfChunks + kPfThreads - 1) / kPfThreads;
 constexpr float kPfSlack = 8.f;
@@ -116,7 +116,8 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
         const unsigned long long below = (1ull << lane) - 1ull;
         int bits = 0, nf = 0;
 #pragma unroll
-        for (int w = 8; w >= 1; --w) {
+        for (int w = 16; w >= 1; --w) {
+            if (w > 8 && w < 16) continue;
             const unsigned long long mk = __ballot(my_w == w);
             if (my_w == w) {
                 my_pos = nf + 2 * __popcll(mk & below);
@@ -127,21 +128,24 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
         }
         n_fields = nf;
     }
+    // passthrough widths: K16 (every block 16 bits: 256-byte records) and V16
+    const bool k16 = sk_bytes == 16 * kMaxBlocks * 2 / 8, v16 = v_bits == 16;
     const int cp = pairing == KVQ_PAIR_HALF ? lane : 2 * lane;
     const int cq = pairing == KVQ_PAIR_HALF ? lane + kMaxBlocks : 2 * lane + 1;
     if (wave == 0) {
         if (my_w > 0) {
             sm.fcoord[my_pos] = (uint8_t)cp;
             sm.fcoord[my_pos + 1] = (uint8_t)cq;
-            sm.fsig[my_pos] = my_ks * scale_log2;
-            sm.fsig[my_pos + 1] = my_ks * scale_log2;
+            const float f = k16 ? scale_log2 : my_ks * scale_log2;  // passthrough: the raw value, no sigma
+            sm.fsig[my_pos] = f;
+            sm.fsig[my_pos + 1] = f;
         }
         if (2 * lane >= n_fields) {
             sm.fcoord[2 * lane] = 0; sm.fcoord[2 * lane + 1] = 0;
             sm.fsig[2 * lane] = 0.f; sm.fsig[2 * lane + 1] = 0.f;
         }
     } else if (wave == 1) {
-        const float vs = v_sigma[kvh * kMaxBlocks + lane];
+        const float vs = v16 ? 1.f : v_sigma[kvh * kMaxBlocks + lane];
         sm.vsig[cp] = vs;
         sm.vsig[cq] = vs;
     }
@@ -190,13 +194,13 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
     }
 
     // per-lane dequantization constants
-    const int kw = my_w, kcb = 2 * KVQ_CB_OFF(kw > 0 ? kw : 1);  // byte offset of the width's levels
-    const uint32_t kmask = kw > 0 ? (1u << kw) - 1u : 0u;
+    const int kw = my_w, kcb = 2 * KVQ_CB_OFF(kw > 0 && kw <= 8 ? kw : 1);  // byte offset of the width's levels
+    const uint32_t kmask = kw > 0 && kw <= 8 ? (1u << kw) - 1u : 0u;
     const int kword = my_koff >> 5, kshift = my_koff & 31;
     const int sp = lane & 31, vpar = lane >> 5;                  // V: slots 2sp, 2sp+1; coordinate parity
     const int vbit = 2 * sp * v_bits, vword = vbit >> 5, vshift = vbit & 31;
-    const uint32_t vmask = (1u << v_bits) - 1u, vmask2 = (1u << (2 * v_bits)) - 1u;
-    const int vcb = 2 * KVQ_CB_OFF(v_bits);
+    const uint32_t vmask = v16 ? 0xffffu : (1u << v_bits) - 1u, vmask2 = vpairs ? (1u << (2 * v_bits)) - 1u : 0u;
+    const int vcb = 2 * KVQ_CB_OFF(v16 ? 1 : v_bits);
 
     floatx16 o[4];
 #pragma unroll
@@ -224,15 +228,19 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
                     lo[i] = rec[kword];
                     hi[i] = rec[kword + 1];
                 }
-                uint32_t la[8], lb[8];
+                uint32_t lk[8];
+                if (k16) {  // the block's two raw binary16 values are one record word
 #pragma unroll
-                for (int i = 0; i < 8; ++i) {
-                    const uint32_t x = alignbit(hi[i], lo[i], kshift);
-                    la[i] = lds_u16(sm.lev, kcb + 2 * (x & kmask));
-                    lb[i] = lds_u16(sm.lev, kcb + 2 * ((x >> kw) & kmask));
+                    for (int i = 0; i < 8; ++i) lk[i] = lo[i];
+                } else {
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) {
+                        const uint32_t x = alignbit(hi[i], lo[i], kshift);
+                        lk[i] = lds_u16(sm.lev, kcb + 2 * (x & kmask)) | (lds_u16(sm.lev, kcb + 2 * ((x >> kw) & kmask)) << 16);
+                    }
                 }
 #pragma unroll
-                for (int i = 0; i < 8; ++i) *(uint32_t*)&sm.kd[(KPW * wave + i0 + i) * kPfKS + my_pos] = la[i] | (lb[i] << 16);
+                for (int i = 0; i < 8; ++i) *(uint32_t*)&sm.kd[(KPW * wave + i0 + i) * kPfKS + my_pos] = lk[i];
             }
         }
         // ---- dequantize V: wave w coordinates [CPW w, CPW (w+1)), lane = (slot pair,
@@ -249,7 +257,10 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
                     hi[i] = run[vword + 1];
                 }
                 uint32_t lv[8];
-                if (vpairs) {
+                if (v16) {  // two slots' raw binary16 values are one run word
+#pragma unroll
+                    for (int i = 0; i < 8; ++i) lv[i] = lo[i];
+                } else if (vpairs) {
 #pragma unroll
                     for (int i = 0; i < 8; ++i) lv[i] = lds_u32(sm.vpair, 4 * (alignbit(hi[i], lo[i], vshift) & vmask2));
                 } else {
@@ -291,7 +302,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
                 const int kk = 32 * kb + 8 * jj + 4 * h;
-                const float4 sc = *(const float4*)(skl + kk);
+                const float4 sc = k16 ? float4{1.f, 1.f, 1.f, 1.f} : *(const float4*)(skl + kk);
                 acc[4 * jj + 0] *= sc.x; acc[4 * jj + 1] *= sc.y;
                 acc[4 * jj + 2] *= sc.z; acc[4 * jj + 3] *= sc.w;
                 if (need_mask) {
@@ -315,10 +326,10 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
             }
             const float mb = mref == -INFINITY ? 0.f : mref;  // rows that have seen nothing keep p = 0
             float psum = 0.f;
-            uint32_t ph[8];  // P' (p s^V) as binary16 pairs in the accumulator's key order
+            uint32_t ph[8], pl[8];  // P' (p s^V) as binary16 hi + lo pairs in the accumulator's key order
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const float4 sv = *(const float4*)(svl + 32 * kb + 8 * jj + 4 * h);
+                const float4 sv = v16 ? float4{1.f, 1.f, 1.f, 1.f} : *(const float4*)(svl + 32 * kb + 8 * jj + 4 * h);
                 const float svv[4] = {sv.x, sv.y, sv.z, sv.w};
                 float pv[4];
 #pragma unroll
@@ -327,16 +338,21 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
                     psum += p;
                     pv[e] = p * svv[e];
                 }
-                ph[2 * jj] = pack_h2(pv[0], pv[1]);
-                ph[2 * jj + 1] = pack_h2(pv[2], pv[3]);
+#pragma unroll
+                for (int e = 0; e < 4; e += 2) {
+                    const _Float16 a = (_Float16)pv[e], b = (_Float16)pv[e + 1];
+                    ph[2 * jj + e / 2] = (uint32_t)__builtin_bit_cast(uint16_t, a) |
+                                         ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+                    pl[2 * jj + e / 2] = pack_h2(pv[e] - (float)a, pv[e + 1] - (float)b);
+                }
             }
             lrun += psum;
             // PV: MFMA m takes keys 32 kb + 16 m + 8 (i/4) + 4 h + i%4, i = 0..7
 #pragma unroll
             for (int m = 0; m < 2; ++m) {
-                H8 bp;
+                H8 bh, bl;
 #pragma unroll
-                for (int u = 0; u < 4; ++u) bp.u[u] = ph[4 * m + u];
+                for (int u = 0; u < 4; ++u) { bh.u[u] = ph[4 * m + u]; bl.u[u] = pl[4 * m + u]; }
 #pragma unroll
                 for (int cb = 0; cb < 4; ++cb) {
                     const uint16_t* vrow = &sm.vd[(32 * cb + col) * kPfVS + 32 * kb + 16 * m + 4 * h];
@@ -344,7 +360,8 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
                     const uint2 v1 = *(const uint2*)(vrow + 8);
                     H8 a;
                     a.u[0] = v0.x; a.u[1] = v0.y; a.u[2] = v1.x; a.u[3] = v1.y;
-                    o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a.h, bp.h, o[cb], 0, 0, 0);
+                    o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a.h, bh.h, o[cb], 0, 0, 0);
+                    o[cb] = __builtin_amdgcn_mfma_f32_32x32x16_f16(a.h, bl.h, o[cb], 0, 0, 0);
                 }
             }
         }
@@ -385,8 +402,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
 int plan_prefill(const kvq_geom& g, int n_q_heads, int n_seq, int max_q, int64_t max_len, int n_split_req,
                  PrefillPlan* plan) {
     const int grp = n_q_heads / g.n_kv_heads;
-    if (g.head_dim != kHeadDim || g.v_bits > 8 || g.k_budget > 8 * kMaxBlocks || grp > kPfMaxGroup)
-        return KVQ_ERR_SHAPE;
+    if (g.head_dim != kHeadDim || grp > kPfMaxGroup) return KVQ_ERR_SHAPE;
     const int qt = kPfRows / grp;
     plan->n_qb = (max_q + qt - 1) / qt;
     const int64_t max_tiles = (max_len + kTile - 1) / kTile;

@@ -132,8 +132,10 @@ def test_host_validation_rejects_before_gpu():
     assert kvq.prefill_workspace_bytes(good, 16, 1, 64, 512, 1) == 0
     assert L.kvq_packed_prefill_attn(*p_args(good, 3, 512, 1 << 30)) == -2           # GQA ratio
     assert L.kvq_packed_prefill_attn(*p_args(good, 2 * 129, 512, 1 << 30)) == -2     # group > 128
-    assert L.kvq_packed_prefill_attn(*p_args(kvq.geom(2, 1024, 3, 1024), 16, 512, 1 << 30)) == -2  # K16
-    assert L.kvq_packed_prefill_attn(*p_args(kvq.geom(2, 192, 16, 1024), 16, 512, 1 << 30)) == -2  # V16
+    # passthrough widths (K16, the K-only V16) are served
+    assert kvq.prefill_plan(kvq.geom(2, 1024, 16, 1024), 16, 1, 64, 512, 1)["n_split"] == 1
+    assert kvq.prefill_plan(kvq.geom(2, 192, 16, 1024), 16, 1, 64, 512, 2)["n_split"] == 2
+    assert L.kvq_packed_prefill_attn(*p_args(kvq.geom(2, 192, 3, 1024, head_dim=64), 16, 512, 1 << 30)) == -2
     assert L.kvq_packed_prefill_attn(*p_args(good, 16, 2048, 1 << 30)) == -5
     assert L.kvq_packed_prefill_attn(*p_args(good, 16, 512, 16)) == -6
     assert L.kvq_packed_prefill_attn(*p_args(good, 16, 512, 1 << 30, q=FAKE + 8)) == -4

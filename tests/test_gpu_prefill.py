@@ -4,8 +4,9 @@ position, the chunk itself packed first ("RoPE-Aware Bit Allocation for KV-Cache
 Quantization": the long contexts only the packed cache holds are filled chunk by
 chunk).  Checked against the oracle's causal attention row by row (2e-3 of the
 row's largest output per (sequence, query, head)); rows past a sequence's queries
-must be exactly zero.  Cases: GQA groups 1..8 (including 3 and 7, whose 128-row
-blocks are not full), K budgets 128..512 (block widths up to 8), value widths 2..8,
+must be exactly zero.  Cases: GQA groups 1..8 (including 3 and 7, whose 256-row
+blocks are not full), K budgets 64..512 (block widths up to 8) and the K16 / V16
+passthrough widths (the K-only mode), value widths 1..8,
 both RoPE pairings, ragged batches with empty and one-query chunks, chunks at the
 start of the context and deep into it, forced key-range splits, and the 128K
 Qwen2.5-3B-shaped layer at full size on sampled rows."""
@@ -31,6 +32,8 @@ CASES = [
     ("k8v8-g1", 1, 1, 512, 8, 0, [(100, 140)], 0),
     ("kodd-v5-g3", 1, 3, 131, 5, 0, [(190, 100)], 0),
     ("k1v1-g8-start", 2, 8, 64, 1, 0, [(0, 200)], 0),
+    ("konly-k3-v16-g4", 2, 4, 192, 16, 0, [(260, 70)], 0),
+    ("k16v16-g2-passthrough", 1, 2, 1024, 16, 0, [(90, 50), (0, 7)], 2),
 ]
 
 
