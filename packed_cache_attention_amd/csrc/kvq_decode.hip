@@ -175,12 +175,12 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
     }
 }
 
-// grid: n_seq * n_q rows; block: 256 threads = 2 split halves x 128 coordinates
+// grid: (n_seq * n_q rows, 4 groups of 32 coordinates); block: 1024 threads = 32 split groups x 32 coordinates
 // Split merge: out = sum_j 2^(m_j - M) o_j / sum_j 2^(m_j - M) l_j.  A workgroup
 // takes 32 coordinates of one row; its 32 split groups stride over the splits with
-// their own running maximum, eight splits' loads in flight at a time, and are
+// their own running maximum, sixteen splits' loads in flight at a time (512 splits in one pass), and are
 // combined through LDS at the end.
-constexpr int kMergeCols = 32, kMergeGroups = 32, kMergeUnroll = 8;
+constexpr int kMergeCols = 32, kMergeGroups = 32, kMergeUnroll = 16;
 
 __global__ __launch_bounds__(kMergeCols * kMergeGroups) void merge_kernel(const float* __restrict__ ws, int n_split,
                                                                            float* __restrict__ out) {
