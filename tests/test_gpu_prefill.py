@@ -106,3 +106,56 @@ def test_prefill_c3_full_size_sampled_rows():
         ref = oracle.decode_attention(r["ogeom"], r["oc"][:region], q[0, j].numpy(), a + j + 1, r["ob"], r["osig"],
                                       r["ovsig"])
         say("row %d worst rel %.2e" % (j, check_attention(o[j][None], ref[None])))
+
+
+def test_prefill_rows_equal_gpu_decode():
+    """Both HIP paths on the same packed cache: prefill row j equals the decode kernel's
+    output for that query at length q_start + j + 1 (within the attention tolerance)."""
+    H, grp, kb, vb = 2, 8, 192, 3
+    nq_heads = H * grp
+    wl = synth.Workload("pf-dec", 1, nq_heads, H, 1e6, (0,), kb, vb, "decay")
+    a, n = 900, 70
+    K, V, _ = synth.gen_layer(wl.with_lens([a + n]), 0, 0, n_tok=a + n, seed=3)
+    cap = 64 * ((a + n + 63) // 64 + 1)
+    r = run_batch([(K, V, torch.zeros(nq_heads, 128, dtype=torch.float16))], kb, vb, cap, check_attn=False)
+    g = r["g"]
+    q = synth.gen_chunk_queries(wl, 0, 0, a, n, seed=3).unsqueeze(0).contiguous().cuda()
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    ws = torch.empty(max(kvq.prefill_workspace_bytes(g, nq_heads, 1, n, a + n) // 4, 4), dtype=torch.float32,
+                     device="cuda")
+    kvq.packed_prefill_attn(g, q, r["cache"], r["off"], torch.tensor([a], dtype=torch.int32, device="cuda"),
+                            torch.tensor([n], dtype=torch.int32, device="cuda"), a + n, r["kbits"], r["ksig"],
+                            r["vsig"], out, ws)
+    rows = [0, 1, 33, 69]
+    # the decode kernel: one sequence per sampled row, all sharing the same region
+    qd = torch.stack([q[0, j] for j in rows]).contiguous()
+    lens = torch.tensor([a + j + 1 for j in rows], dtype=torch.int32, device="cuda")
+    off = r["off"][:1].repeat(len(rows)).contiguous()
+    dout = torch.empty(len(rows), nq_heads, 128, dtype=torch.float32, device="cuda")
+    dws = torch.empty(kvq.decode_workspace_bytes(g, nq_heads, len(rows), a + n) // 4 + 4, dtype=torch.float32,
+                      device="cuda")
+    kvq.packed_decode_attn(g, qd, r["cache"], off, lens, a + n, r["kbits"], r["ksig"], r["vsig"], dout, dws)
+    po = out.cpu().numpy()[0][rows]
+    say("prefill vs decode kernel, worst rel %.2e" % check_attention(po, dout.cpu().numpy().astype(np.float64)))
+
+
+def test_prefill_clamps_query_counts_to_max_q():
+    """A sequence whose device query count exceeds max_q is clamped to max_q (no row past
+    the output is touched): the result equals the call with n_q = max_q."""
+    H, grp, kb, vb = 1, 4, 128, 2
+    nq_heads = H * grp
+    wl = synth.Workload("pf-clamp", 1, nq_heads, H, 1e6, (0,), kb, vb, "decay")
+    a, n = 200, 40
+    K, V, _ = synth.gen_layer(wl.with_lens([a + n + 30]), 0, 0, n_tok=a + n + 30, seed=5)
+    cap = 64 * ((a + n + 30 + 63) // 64 + 1)
+    r = run_batch([(K, V, torch.zeros(nq_heads, 128, dtype=torch.float16))], kb, vb, cap, check_attn=False)
+    g = r["g"]
+    q = synth.gen_chunk_queries(wl, 0, 0, a, n, seed=5).unsqueeze(0).contiguous().cuda()
+    outs = []
+    for nqv in (n, n + 30):
+        out = torch.full(q.shape, float("nan"), dtype=torch.float32, device="cuda")
+        kvq.packed_prefill_attn(g, q, r["cache"], r["off"], torch.tensor([a], dtype=torch.int32, device="cuda"),
+                                torch.tensor([nqv], dtype=torch.int32, device="cuda"), a + n + 30, r["kbits"],
+                                r["ksig"], r["vsig"], out, None, n_split=1)
+        outs.append(out.cpu().numpy())
+    np.testing.assert_array_equal(outs[0], outs[1])
