@@ -159,3 +159,31 @@ def test_prefill_clamps_query_counts_to_max_q():
                                 r["ksig"], r["vsig"], out, None, n_split=1)
         outs.append(out.cpu().numpy())
     np.testing.assert_array_equal(outs[0], outs[1])
+
+
+def test_prefill_c4_full_size_sampled_rows():
+    """The same shape at 524288 tokens: the last 256-query chunk over the whole packed
+    context (8193 tiles per KV head, split over workgroups and merged), sampled rows
+    against the oracle's decode attention at each row's length."""
+    wl = synth.WORKLOADS["c4"]
+    say("prefill c4 full size")
+    K, V, _ = synth.gen_layer(wl, 0, 0)
+    n = K.shape[0]
+    r = run_batch([(K, V, torch.zeros(wl.n_q_heads, 128, dtype=torch.float16))], wl.k_budget, wl.v_bits,
+                  synth.ceil_to(n + 64, 64), check_attn=False)
+    g, region = r["g"], kvq.cache_bytes(r["g"])
+    nt = 256
+    a = n - nt
+    q = synth.gen_chunk_queries(wl, 0, 0, a, nt).unsqueeze(0).contiguous()
+    out = torch.empty(q.shape, dtype=torch.float32, device="cuda")
+    plan = kvq.prefill_plan(g, wl.n_q_heads, 1, nt, n)
+    say("plan %s" % plan)
+    ws = torch.empty(max(plan["workspace"] // 4, 4), dtype=torch.float32, device="cuda")
+    kvq.packed_prefill_attn(g, q.cuda(), r["cache"], r["off"], torch.tensor([a], dtype=torch.int32, device="cuda"),
+                            torch.tensor([nt], dtype=torch.int32, device="cuda"), n, r["kbits"], r["ksig"], r["vsig"],
+                            out, ws)
+    o = out.cpu().numpy()[0]
+    for j in (0, 255):
+        ref = oracle.decode_attention(r["ogeom"], r["oc"][:region], q[0, j].numpy(), a + j + 1, r["ob"], r["osig"],
+                                      r["ovsig"])
+        say("row %d worst rel %.2e" % (j, check_attention(o[j][None], ref[None])))
