@@ -115,6 +115,8 @@ def main():
                     help="also time chunked prefill attention: each sequence's last N tokens as one chunk of "
                          "queries over its whole packed context (0: skip)")
     ap.add_argument("--prefill-split", type=int, default=0, help="key-range splits for the chunk (0: planner)")
+    ap.add_argument("--read-probe-gib", type=float, default=4.0,
+                    help="size of the plain read-bandwidth probe (0: skip)")
     ap.add_argument("--window", type=int, default=128,
                     help="also time the fp16 recent-window step with this many recent tokens unquantized (0: skip)")
     args = ap.parse_args()
@@ -291,17 +293,25 @@ def main():
     torch.cuda.synchronize()
     e0 = torch.cuda.Event(enable_timing=True)
     e1 = torch.cuda.Event(enable_timing=True)
+    # an event between consecutive steps as well (recording does not synchronise), for
+    # the per-step spread
+    sev = [torch.cuda.Event(enable_timing=True) for _ in range(args.steps + 1)]
     w0 = time.perf_counter()
     e0.record()
-    for _ in range(args.steps):
+    sev[0].record()
+    for i in range(args.steps):
         if graph is not None:
             graph.replay()
         else:
             step()
+        sev[i + 1].record()
     e1.record()
     torch.cuda.synchronize()
     wall = time.perf_counter() - w0
     ms_step = e0.elapsed_time(e1) / args.steps
+    per_step = np.array([sev[i].elapsed_time(sev[i + 1]) for i in range(args.steps)])
+    step_pct = {"p10": round(float(np.percentile(per_step, 10)), 5), "p50": round(float(np.percentile(per_step, 50)), 5),
+                "p90": round(float(np.percentile(per_step, 90)), 5)}
     attn_b1, app_b1 = seq_bytes()
     step_bytes = 0.5 * (attn_b0 + attn_b1) + app_b0
     value = step_bytes / (ms_step / 1e3) / 1e9
@@ -478,6 +488,62 @@ def main():
         except Exception:
             traffic = None
 
+    # ------------------------------------------------------------ achievable read bandwidth
+    # A plain streaming read of 4 GiB (far beyond the 256 MB MALL) with the library's
+    # probe kernel (eight 128-bit loads in flight per thread, many workgroups) is the
+    # read ceiling a simple kernel reaches here; the decode figures are also given
+    # against it.
+    probe = None
+    if args.read_probe_gib > 0:
+        nprobe = int(args.read_probe_gib * (1 << 30)) // 16 * 16
+        pbuf = torch.ones(nprobe // 4, dtype=torch.float32, device=dev)
+        cus = torch.cuda.get_device_properties(dev).multi_processor_count
+        best = None
+        for per_cu in (8, 16, 32):
+            nb = cus * per_cu
+            sink = torch.empty(nb, dtype=torch.int32, device=dev)
+            kvq.read_probe(pbuf, sink, nb)
+            torch.cuda.synchronize()
+            e0.record()
+            for _ in range(5):
+                kvq.read_probe(pbuf, sink, nb)
+            e1.record()
+            torch.cuda.synchronize()
+            gbps = nprobe / (e0.elapsed_time(e1) / 5 / 1e3) / 1e9
+            if best is None or gbps > best[0]:
+                best = (gbps, nb)
+        del pbuf
+        torch.cuda.empty_cache()
+        pgbps = best[0]
+        # the same read over each layer's packed cache, 36 launches back to back as the
+        # decode issues them: what a plain kernel needs per layer-sized launch
+        lbytes = cache[0].numel()
+        lus, nbl = None, 0
+        for per_cu in (2, 4, 8, 16, 32):
+            nb = cus * per_cu
+            sink = torch.empty(nb, dtype=torch.int32, device=dev)
+            ldur = []
+            for _ in range(3):
+                torch.cuda._sleep(20_000_000)
+                kd0.record()
+                for l in range(L):
+                    kvq.read_probe(cache[l], sink, nb)
+                kd1.record()
+                torch.cuda.synchronize()
+                ldur.append(kd0.elapsed_time(kd1) / L)
+            t = 1e3 * float(np.median(ldur))
+            if lus is None or t < lus:
+                lus, nbl = t, nb
+        probe = {"kind": "kvq_read_probe (plain 128-bit streaming read)", "bytes": nprobe, "workgroups": best[1],
+                 "GBps": round(pgbps, 1), "pct_hbm_peak": round(100 * pgbps / HBM_PEAK_GBPS, 2),
+                 "decode_kernel_pct_of_probe": round(100 * achieved / pgbps, 2),
+                 "step_pct_of_probe": round(100 * value / pgbps, 2),
+                 "per_layer_read": {"bytes": lbytes, "avg_launch_us": round(lus, 3), "workgroups": nbl,
+                                    "GBps": round(lbytes / (lus / 1e6) / 1e9, 1)}}
+        log("read probe: %.0f GB/s (%.1f%% of HBM peak, %d workgroups); decode kernel at %.1f%% of it; "
+            "a plain read of one layer's %.1f MB cache takes %.2f us per launch back to back"
+            % (pgbps, 100 * pgbps / HBM_PEAK_GBPS, best[1], 100 * achieved / pgbps, lbytes / 1e6, lus))
+
     if args.copy_probe_mib:
         n = args.copy_probe_mib * (1 << 20) // 4
         a = torch.empty(n, dtype=torch.float32, device=dev).normal_()
@@ -512,6 +578,8 @@ def main():
         "pct_hbm_peak": round(100 * value / HBM_PEAK_GBPS, 2),
         "step_bytes": int(step_bytes),
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
+        "ms_per_step_percentiles": step_pct,
+        "read_probe": probe,
         "quantize_tokens_per_s": round(rows / t_quant, 1),
         "prefill": {"energy_ms": round(t_energy * 1e3, 4), "energy_GBps": round(energy_bytes / t_energy / 1e9, 1),
                     "allocate_ms": round(t_alloc * 1e3, 4), "quantize_ms": round(t_quant * 1e3, 4),
@@ -561,7 +629,17 @@ def cpu_baseline(wl, Kall, Vall, Qall, lens, row0, bytes_per_token_head, budget_
         t_attn += t2 - t1
         layers += 1
     attn_bytes = layers * n * H * bytes_per_token_head
+    cpu_model = None
+    try:
+        with open("/proc/cpuinfo") as f:
+            for line in f:
+                if line.startswith("model name"):
+                    cpu_model = line.split(":", 1)[1].strip()
+                    break
+    except OSError:
+        pass
     return {"value": round(attn_bytes / t_attn / 1e9, 5), "unit": "GB/s", "cores": n_threads, "kind": "oracle",
+            "cpu": cpu_model,
             "sample": "sequence 0 (%d tokens), layers 0..%d, %d KV heads, %d query heads: decode attention "
                       "(fp64) %.2f s; energy+allocation+quantize of the same layers %.2f s (%.0f tokens/s)"
                       % (n, layers - 1, H, wl.n_q_heads, t_attn, t_prep, layers * n / t_prep),

@@ -294,6 +294,12 @@ int32_t kvq_packed_prefill_attn(const kvq_geom *g, int32_t n_q_heads, const void
                                 int32_t n_seq, int32_t max_q, int64_t max_len, const uint8_t *k_bits,
                                 const float *k_sigma, const float *v_sigma, float softmax_scale, float *out,
                                 void *workspace, size_t workspace_bytes, int32_t n_split, void *stream);
+/* Measurement helper (not a step of the method): a plain streaming read of `bytes`
+ * (a multiple of 16; src 16-byte aligned) by n_blocks workgroups of 256 threads, each
+ * writing one 32-bit word to sink[block] so the loads stay live (sink: n_blocks words).
+ * Timed by the caller, it gives the read rate a simple kernel reaches on the device --
+ * the ceiling the attention kernels are compared against. */
+int32_t kvq_read_probe(const void *src, int64_t bytes, uint32_t *sink, int32_t n_blocks, void *stream);
 /* Log-sum-exp merge of n_split partials per (sequence, head) in the format above:
  * out[s][h][c] = sum_k 2^(m_k - M) o_k,c / sum_k 2^(m_k - M) l_k, M = max_k m_k; rows
  * with no tokens give 0.  out: device float [n_seq][n_q_heads][128]. */

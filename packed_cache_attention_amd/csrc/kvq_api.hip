@@ -495,4 +495,14 @@ int32_t kvq_packed_prefill_attn(const kvq_geom* g, int32_t n_q_heads, const void
                       fn);
 }
 
+// ---------------------------------------------------------------- measurement helper
+int32_t kvq_read_probe(const void* src, int64_t bytes, uint32_t* sink, int32_t n_blocks, void* stream) {
+    const char* fn = "kvq_read_probe";
+    if (bytes < 0 || n_blocks < 1 || n_blocks > (1 << 24)) return fail(KVQ_ERR_ARG, fn, "counts");
+    if (bytes == 0) return KVQ_OK;
+    if (!src || !sink) return fail(KVQ_ERR_ARG, fn, "null pointer");
+    if (!aligned(src, 16) || (bytes & 15) || !aligned(sink, 4)) return fail(KVQ_ERR_ALIGN, fn, "alignment");
+    return hip_status(launch_read_probe(src, bytes, sink, n_blocks, (hipStream_t)stream), fn);
+}
+
 }  // extern "C"

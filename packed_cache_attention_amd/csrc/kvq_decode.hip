@@ -387,4 +387,40 @@ hipError_t launch_merge(int n_rows, int n_split, const float* partials, float* o
     return hipGetLastError();
 }
 
+// ---------------------------------------------------------------- read-bandwidth probe
+// A plain streaming read of n16 16-byte words: every thread keeps eight 128-bit loads
+// in flight over a grid-stride loop and folds them with XOR; one word per workgroup
+// is written so the loads stay live.  It measures the read rate a simple kernel
+// reaches on this device (the ceiling the attention kernels are compared with).
+__global__ __launch_bounds__(256) void read_probe_kernel(const uint4* __restrict__ src, int64_t n16,
+                                                         uint32_t* __restrict__ sink) {
+    const int64_t stride = (int64_t)gridDim.x * 256;
+    int64_t i = (int64_t)blockIdx.x * 256 + threadIdx.x;
+    uint32_t acc = 0;
+    for (; i + 7 * stride < n16; i += 8 * stride) {
+        uint4 v[8];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) v[u] = src[i + u * stride];
+#pragma unroll
+        for (int u = 0; u < 8; ++u) acc ^= v[u].x ^ v[u].y ^ v[u].z ^ v[u].w;
+    }
+    for (; i < n16; i += stride) {
+        const uint4 v = src[i];
+        acc ^= v.x ^ v.y ^ v.z ^ v.w;
+    }
+    __shared__ uint32_t s_acc[256];
+    s_acc[threadIdx.x] = acc;
+    __syncthreads();
+    if (threadIdx.x == 0) {
+        uint32_t r = 0;
+        for (int t = 0; t < 256; ++t) r ^= s_acc[t];
+        sink[blockIdx.x] = r;
+    }
+}
+
+hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* sink, int n_blocks, hipStream_t st) {
+    hipLaunchKernelGGL(read_probe_kernel, dim3(n_blocks), dim3(256), 0, st, (const uint4*)src, bytes / 16, sink);
+    return hipGetLastError();
+}
+
 }  // namespace kvq

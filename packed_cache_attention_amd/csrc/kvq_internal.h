@@ -251,6 +251,10 @@ hipError_t launch_append_step(const kvq_geom& g, int n_seq, const AppendArgs& ap
                               const int64_t* seq_byte_off, hipStream_t st);
 hipError_t launch_merge(int n_rows, int n_split, const float* partials, float* out, hipStream_t st);
 
+// plain streaming read of `bytes` (a multiple of 16) by n_blocks workgroups; one word per
+// workgroup to sink (kvq_decode.hip)
+hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* sink, int n_blocks, hipStream_t st);
+
 // chunked prefill attention (kvq_prefill.hip)
 struct PrefillPlan {
     int n_qb;           // query blocks (128 query rows each) per (sequence, KV head)

@@ -98,6 +98,8 @@ def lib() -> C.CDLL:
     L.kvq_prefill_workspace_bytes.restype = I64
     L.kvq_packed_prefill_attn.argtypes = [G, I32, P, P, P, P, P, I32, I32, I64, P, P, P, F32, P, P, SZ, I32, P]
     L.kvq_packed_prefill_attn.restype = I32
+    L.kvq_read_probe.argtypes = [P, I64, P, I32, P]
+    L.kvq_read_probe.restype = I32
     if L.kvq_version() != LAYOUT_VERSION:
         raise RuntimeError("libkvq.so layout version mismatch")
     return L
@@ -109,7 +111,7 @@ EXPORTS = ["kvq_version", "kvq_status_string", "kvq_tile_bytes", "kvq_cache_byte
            "kvq_decode_partials", "kvq_merge_partials", "kvq_decode_n_split", "kvq_decode_plan",
            "kvq_decode_step_partials", "kvq_decode_step", "kvq_window_decode_attn", "kvq_window_decode_step",
            "kvq_window_workspace_bytes", "kvq_prefill_plan", "kvq_prefill_workspace_bytes",
-           "kvq_packed_prefill_attn"]
+           "kvq_packed_prefill_attn", "kvq_read_probe"]
 
 
 def status_string(st: int) -> str:
@@ -390,3 +392,10 @@ def packed_prefill_attn(g: Geom, q: torch.Tensor, cache: torch.Tensor, seq_byte_
         C.byref(g), n_qh, _ptr(q), _ptr(cache), _ptr(seq_byte_off), _ptr(q_start), _ptr(n_q), n_seq, max_q, max_len,
         _ptr(k_bits), _ptr(k_sigma), _ptr(v_sigma), float(softmax_scale), _ptr(out), _ptr(workspace), ws_bytes,
         n_split, _stream(stream)))
+
+
+def read_probe(buf: torch.Tensor, sink: torch.Tensor, n_blocks: int, stream=None):
+    """Measurement helper: stream-read all of buf (contiguous, 16-byte multiple) once."""
+    assert buf.is_contiguous() and sink.dtype == torch.int32 and sink.numel() >= n_blocks
+    _check("kvq_read_probe", lib().kvq_read_probe(_ptr(buf), buf.numel() * buf.element_size(), _ptr(sink), n_blocks,
+                                                   _stream(stream)))

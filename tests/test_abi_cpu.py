@@ -142,3 +142,10 @@ def test_host_validation_rejects_before_gpu():
     assert L.kvq_packed_prefill_attn(*p_args(good, 16, 512, 1 << 30, q=None)) == -1
     assert L.kvq_packed_prefill_attn(*p_args(good, 16, 512, 1 << 30, wsp=None)) == -1
     assert L.kvq_packed_prefill_attn(*p_args(good, 16, 512, 1 << 30, n_split=-1)) == -1
+    # read probe (measurement helper): counts, pointers, alignment
+    assert L.kvq_read_probe(FAKE, -16, FAKE, 4, None) == -1
+    assert L.kvq_read_probe(FAKE, 1024, FAKE, 0, None) == -1
+    assert L.kvq_read_probe(None, 1024, FAKE, 4, None) == -1
+    assert L.kvq_read_probe(FAKE + 4, 1024, FAKE, 4, None) == -4
+    assert L.kvq_read_probe(FAKE, 1000, FAKE, 4, None) == -4
+    assert L.kvq_read_probe(FAKE, 0, FAKE, 4, None) == 0
