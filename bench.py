@@ -488,6 +488,42 @@ def main():
         except Exception:
             traffic = None
 
+    # ------------------------------------------------------------ layer-batched capability
+    # Not a model-realistic step (layer l+1's query depends on layer l): the 36 layers'
+    # caches are consecutive, so the same decode kernel can attend all of them in one
+    # launch as one geometry of L * H_kv KV heads -- the kernel's throughput with the
+    # per-launch cost amortised.  Labelled as such; never the headline.
+    batched = None
+    if S == 1:
+        gb = kvq.geom(L * H, wl.k_budget, wl.v_bits, cap)
+        qb_ = Qall.view(1, L * Hq, d)
+        bplan = kvq.decode_plan(gb, L * Hq, 1, max_len, kern, 0)
+        bpart = torch.empty(1, L * Hq, bplan["n_split"], d + 2, dtype=torch.float32, device=dev)
+        bk, bs, bv = kbits.view(L * H, d // 2), ksig.view(L * H, d // 2), vsig.view(L * H, d // 2)
+
+        def bstep():
+            kvq.decode_partials(gb, qb_, cache.view(-1), off[:1], seq_len, max_len, bk, bs, bv, bpart, kernel=kern)
+
+        bstep()
+        torch.cuda.synchronize()
+        bdur = []
+        for _ in range(5):
+            torch.cuda._sleep(20_000_000)
+            kd0.record()
+            bstep()
+            kd1.record()
+            torch.cuda.synchronize()
+            bdur.append(kd0.elapsed_time(kd1))
+        bms = float(np.median(bdur))
+        bbytes = L * int(seq_len[0].item()) * H * bytes_per_token_head
+        bgbps = bbytes / (bms / 1e3) / 1e9
+        batched = {"label": "kernel capability: all %d layers in one launch (not a model step)" % L,
+                   "entry_point": "kvq_decode_partials", "n_split": bplan["n_split"],
+                   "tiles_per_split": bplan["tiles_per_split"], "launch_us": round(bms * 1e3, 2),
+                   "bytes": bbytes, "GBps": round(bgbps, 1), "frac": round(bgbps / HBM_PEAK_GBPS, 4)}
+        log("layer-batched capability: %d layers in one launch %.1f us = %.0f GB/s (%.1f%% of HBM peak)"
+            % (L, bms * 1e3, bgbps, 100 * bgbps / HBM_PEAK_GBPS))
+
     # ------------------------------------------------------------ achievable read bandwidth
     # A plain streaming read of 4 GiB (far beyond the 256 MB MALL) with the library's
     # probe kernel (eight 128-bit loads in flight per thread, many workgroups) is the
@@ -593,6 +629,7 @@ def main():
         "cpu_baseline": cpu,
         "window_step": wres,
         "prefill_chunk": pres,
+        "layer_batched": batched,
     }
     print(json.dumps(result), flush=True)
 
