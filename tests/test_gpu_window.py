@@ -28,6 +28,26 @@ CASES = [
 ]
 
 
+def _random_cases(n):
+    # seeded random valid cases: heads, group, budgets, window, ragged starts, steps, kernel
+    r = np.random.default_rng(77)
+    out = []
+    for i in range(n):
+        H = int(r.integers(1, 4))
+        grp = int(r.choice([1, 2, 4, 7, 8, 16]))
+        kb = int(r.integers(0, 257))
+        vb = 16 if r.random() < 0.2 else int(r.integers(1, 9))
+        W = int(r.integers(1, 200))
+        n0 = tuple(int(x) for x in r.integers(1, 400, int(r.integers(1, 4))))
+        steps = int(r.integers(1, 4))
+        kernel = kvq.DECODE_GENERIC if r.random() < 0.3 else kvq.DECODE_AUTO
+        out.append(("random%d" % i, H, grp, kb, vb, W, n0, steps, kernel))
+    return out
+
+
+CASES += _random_cases(6)
+
+
 def _window_tokens(X, n, W):
     """Tokens [max(n - W, 0), n) of X [N, H, d] (the window, in sequence order)."""
     return X[max(n - W, 0):n]
