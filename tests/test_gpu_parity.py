@@ -330,6 +330,36 @@ def test_c3_full_size_sampled_layers(layer):
     say("c3 layer %d: attention ok, worst rel %.2e" % (layer, check_attention(r["out"], r["ref"])))
 
 
+def test_c3_full_size_fused_step_as_benchmarked():
+    """The launch the benchmark times, at its size: one 128K Qwen2.5-3B-shaped layer,
+    kvq_decode_step (the new token quantized and packed inside the attention kernel,
+    then the split merge) in the automatic plan with max_len = capacity; the cache
+    bytes against the oracle's packing of the same token into its own copy, the
+    output against its attention over all n + 1 tokens."""
+    wl = synth.WORKLOADS["c3"]
+    layer = 17
+    say("c3 full-size fused step, layer %d" % layer)
+    K, V, _ = synth.gen_layer(wl, 0, layer)
+    n = K.shape[0]
+    kn, vn, qn = synth.gen_new_token(wl, 0, layer, n, 0)
+    cap = synth.ceil_to(n + 64, 64)
+    r = run_batch([(K, V, qn)], wl.k_budget, wl.v_bits, cap, check_attn=False)
+    g, region = r["g"], kvq.cache_bytes(r["g"])
+    plan = kvq.decode_plan(g, wl.n_q_heads, 1, cap)
+    say("plan %s" % plan)
+    ws = torch.empty(plan["workspace"] // 4 + 4, dtype=torch.float32, device="cuda")
+    out = torch.empty(1, wl.n_q_heads, 128, dtype=torch.float32, device="cuda")
+    kvq.decode_step(g, qn[None].cuda().contiguous(), kn[None].cuda().contiguous(), vn[None].cuda().contiguous(),
+                    r["cache"], r["off"], torch.tensor([n + 1], dtype=torch.int32, device="cuda"), cap, r["kbits"],
+                    r["ksig"], r["vsig"], out, ws)
+    oc = r["oc"].copy()
+    oracle.quantize_pack(r["ogeom"], oc[:region], kn[None].numpy(), vn[None].numpy(), n, r["ob"], r["osig"],
+                         r["ovsig"])
+    np.testing.assert_array_equal(r["cache"].cpu().numpy(), oc)
+    ref = oracle.decode_attention(r["ogeom"], oc[:region], qn.numpy(), n + 1, r["ob"], r["osig"], r["ovsig"])
+    say("c3 fused step: bytes ok, attention worst rel %.2e" % check_attention(out.cpu().numpy(), ref[None]))
+
+
 def test_c4_full_size_layer0():
     """The same shape at 524288 tokens (one layer): long-context tiling and the split merge."""
     wl = synth.WORKLOADS["c4"]
