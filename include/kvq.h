@@ -260,9 +260,10 @@ int32_t kvq_window_decode_step(const kvq_geom *g, int32_t window, int32_t n_q_he
                                float softmax_scale, float *out, void *workspace, size_t workspace_bytes,
                                int32_t kernel, int32_t tiles_per_split, void *stream);
 /* Chunked prefill attention over the packed cache, causal ("RoPE-Aware Bit Allocation
- * for KV-Cache Quantization": the long contexts only the packed cache holds are
- * filled chunk by chunk; each chunk's queries attend everything packed before them
- * and their own chunk, which the caller packs first with kvq_quantize_pack).
+ * for KV-Cache Quantization", abstract: at 256K and 512K only the packed cache fits in
+ * memory.  Read here as a prompt filled into it chunk by chunk, each chunk's queries
+ * attending everything packed before them and their own chunk, which the caller packs
+ * first with kvq_quantize_pack).
  *   q        : device binary16 [n_seq][max_q][n_q_heads][128] (post-RoPE), 16-byte aligned
  *   q_start  : device int32 [n_seq], position of sequence s's first chunk query
  *   n_q      : device int32 [n_seq], its number of queries, 0 <= n_q[s] <= max_q

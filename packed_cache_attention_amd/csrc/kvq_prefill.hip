@@ -1,8 +1,8 @@
 // kvq_prefill.hip -- chunked prefill attention over the packed cache (causal) on
 // the CDNA4 matrix cores, for the packed-cache serving path of "RoPE-Aware Bit
-// Allocation for KV-Cache Quantization" (abstract: long contexts that only the
-// packed cache holds are filled chunk by chunk, and each chunk's queries attend
-// everything packed so far).
+// Allocation for KV-Cache Quantization" (abstract: at 256K and 512K only the packed
+// cache fits; such a prompt is read here as filled chunk by chunk, each chunk's
+// queries attending everything packed so far).
 //
 // A chunk of queries of one sequence sits at positions q_start .. q_start+n_q-1;
 // query j attends slots [0, q_start + j] of the packed cache (the chunk is packed

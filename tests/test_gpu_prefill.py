@@ -1,8 +1,8 @@
 """GPU parity for chunked prefill attention over the packed cache (causal): a chunk
 of queries at positions q_start .. q_start + n - 1 attends every slot up to its own
 position, the chunk itself packed first ("RoPE-Aware Bit Allocation for KV-Cache
-Quantization": the long contexts only the packed cache holds are filled chunk by
-chunk).  Checked against the oracle's causal attention row by row (2e-3 of the
+Quantization", abstract: at 256K and 512K only the packed cache fits; a prompt of that
+length is read here as filled chunk by chunk).  Checked against the oracle's causal attention row by row (2e-3 of the
 row's largest output per (sequence, query, head)); rows past a sequence's queries
 must be exactly zero.  Cases: GQA groups 1..8 (including 3 and 7, whose 256-row
 blocks are not full), K budgets 64..512 (block widths up to 8) and the K16 / V16
