@@ -470,3 +470,43 @@ def test_decode_step_equals_append_then_attend(case, tiles):
     ref = np.stack([oracle.decode_attention(r["ogeom"], oc[i * region:(i + 1) * region], seqs[i][2].numpy(),
                                             n0[i] + steps, r["ob"], r["osig"], r["ovsig"]) for i in range(S)])
     check_attention(out_b.cpu().numpy(), ref)
+
+
+def test_layer_batched_geometry_equals_per_layer_calls():
+    """The bench's layer-batched capability reading: L layers' regions laid end to end
+    are one region of L * H_kv KV heads, so one decode call over that geometry gives
+    each layer's per-layer result (up to the merge order)."""
+    L, H, grp, kb, vb, n = 3, 2, 8, 192, 3, 700
+    wl = synth.Workload("lb", L, H * grp, H, 1e6, (n,), kb, vb, "decay")
+    cap = synth.ceil_to(n + 64, 64)
+    per_layer, caches, bits, ks, vs, qs = [], [], [], [], [], []
+    for l in range(L):
+        K, V, q = synth.gen_layer(wl, 0, l)
+        r = run_batch([(K, V, q)], kb, vb, cap)
+        per_layer.append(r["out"][0])
+        caches.append(r["cache"]); bits.append(r["kbits"]); ks.append(r["ksig"]); vs.append(r["vsig"])
+        qs.append(q)
+    gb = kvq.geom(L * H, kb, vb, cap)
+    cache = torch.cat(caches).contiguous()
+    q = torch.cat(qs)[None].cuda().contiguous()
+    out = torch.empty(1, L * H * grp, 128, dtype=torch.float32, device="cuda")
+    ws = torch.empty(kvq.decode_workspace_bytes(gb, L * H * grp, 1, n) // 4 + 4, dtype=torch.float32, device="cuda")
+    kvq.packed_decode_attn(gb, q, cache, torch.zeros(1, dtype=torch.int64, device="cuda"),
+                           torch.tensor([n], dtype=torch.int32, device="cuda"), n, torch.cat(bits), torch.cat(ks),
+                           torch.cat(vs), out, ws)
+    o = out.cpu().numpy()[0].reshape(L, H * grp, 128)
+    for l in range(L):
+        np.testing.assert_allclose(o[l], per_layer[l], rtol=0, atol=2e-6 * np.abs(per_layer[l]).max())
+
+
+def test_read_probe_reads_every_word():
+    """The bandwidth probe folds every 16-byte word it reads: with each word's four
+    dwords XOR-ed, the XOR of the workgroups' results equals the whole buffer's."""
+    g = torch.Generator().manual_seed(3)
+    buf = torch.randint(-2 ** 31, 2 ** 31 - 1, (1 << 20,), dtype=torch.int32, generator=g)
+    want = np.bitwise_xor.reduce(buf.numpy().view(np.uint32))
+    for nb in (1, 7, 256, 2048):
+        sink = torch.zeros(nb, dtype=torch.int32, device="cuda")
+        kvq.read_probe(buf.cuda(), sink, nb)
+        got = np.bitwise_xor.reduce(sink.cpu().numpy().view(np.uint32))
+        assert got == want, (nb, got, want)
