@@ -175,17 +175,28 @@ __global__ __launch_bounds__(256) void decode_generic_kernel(
     }
 }
 
-// grid: (n_seq * n_q rows, 4 groups of 32 coordinates); block: 1024 threads = 32 split groups x 32 coordinates
+// grid: (n_seq * n_q rows, 16 groups of 8 coordinates); block: 256 threads = 32 split groups x 8 coordinates
 // Split merge: out = sum_j 2^(m_j - M) o_j / sum_j 2^(m_j - M) l_j.  A workgroup
-// takes 32 coordinates of one row; its 32 split groups stride over the splits with
-// their own running maximum, sixteen splits' loads in flight at a time (512 splits in one pass), and are
-// combined through LDS at the end.
-constexpr int kMergeCols = 32, kMergeGroups = 32, kMergeUnroll = 16;
+// takes 8 coordinates of one row, so a row's merge spreads over 16 compute units;
+// its 32 split groups stride over the splits with their own running maximum,
+// sixteen splits' loads in flight at a time (512 splits in one pass).  A wave's
+// eight split groups (lanes 8 apart) combine by lane swaps, the four waves through LDS.
+constexpr int kMergeCols = 8, kMergeGroups = 32, kMergeUnroll = 16;
+
+__device__ __forceinline__ void merge_pair(float& M, float& L, float& A, float oM, float oL, float oA) {
+    const float Mx = fmaxf(M, oM);
+    if (Mx != -INFINITY) {
+        const float a = exp2f(M - Mx), b = exp2f(oM - Mx);
+        L = a * L + b * oL;
+        A = a * A + b * oA;
+    }
+    M = Mx;
+}
 
 __global__ __launch_bounds__(kMergeCols * kMergeGroups) void merge_kernel(const float* __restrict__ ws, int n_split,
                                                                            float* __restrict__ out) {
     const int64_t row = blockIdx.x;
-    const int tid = threadIdx.x, sg = tid / kMergeCols, c = blockIdx.y * kMergeCols + tid % kMergeCols;
+    const int tid = threadIdx.x, sg = tid / kMergeCols, cc = tid % kMergeCols, c = blockIdx.y * kMergeCols + cc;
     constexpr int D2 = kHeadDim + 2;
     const float* part = ws + row * n_split * D2;
     float M = -INFINITY, L = 0.f, A = 0.f;
@@ -214,47 +225,24 @@ __global__ __launch_bounds__(kMergeCols * kMergeGroups) void merge_kernel(const 
         }
         M = mx;
     }
-    // the wave's two split groups (lanes l and l ^ 32 share a column) first, then the
-    // 16 waves' results through LDS, each half of wave 0 taking eight of them
-    {
-        const float oM = __shfl_xor(M, 32), oL = __shfl_xor(L, 32), oA = __shfl_xor(A, 32);
-        const float Mx = fmaxf(M, oM);
-        if (Mx != -INFINITY) {
-            const float a = exp2f(M - Mx), b = exp2f(oM - Mx);
-            L = a * L + b * oL;
-            A = a * A + b * oA;
-        }
-        M = Mx;
-    }
-    constexpr int kWavesM = kMergeGroups / 2;
+    // the wave's eight split groups: lanes l, l ^ 8, l ^ 16, l ^ 32 ... share a coordinate
+#pragma unroll
+    for (int mask = kMergeCols; mask < 64; mask <<= 1)
+        merge_pair(M, L, A, __shfl_xor(M, mask), __shfl_xor(L, mask), __shfl_xor(A, mask));
+    constexpr int kWavesM = kMergeCols * kMergeGroups / 64;
     __shared__ float s_m[kWavesM][kMergeCols], s_l[kWavesM][kMergeCols], s_a[kWavesM][kMergeCols];
-    const int wv = tid / 64, cc = tid % kMergeCols;
+    const int wv = tid / 64;
     if ((tid & 63) < kMergeCols) {
         s_m[wv][cc] = M;
         s_l[wv][cc] = L;
         s_a[wv][cc] = A;
     }
     __syncthreads();
-    if (wv == 0) {
-        const int k0 = (tid / kMergeCols) * (kWavesM / 2);
-        float Mt = -INFINITY;
-        for (int k = k0; k < k0 + kWavesM / 2; ++k) Mt = fmaxf(Mt, s_m[k][cc]);
-        float Lt = 0.f, At = 0.f;
-        if (Mt != -INFINITY) {
-            for (int k = k0; k < k0 + kWavesM / 2; ++k) {
-                const float a = exp2f(s_m[k][cc] - Mt);
-                Lt += a * s_l[k][cc];
-                At += a * s_a[k][cc];
-            }
-        }
-        const float oM = __shfl_xor(Mt, 32), oL = __shfl_xor(Lt, 32), oA = __shfl_xor(At, 32);
-        const float Mx = fmaxf(Mt, oM);
-        if (Mx != -INFINITY) {
-            const float a = exp2f(Mt - Mx), b = exp2f(oM - Mx);
-            Lt = a * Lt + b * oL;
-            At = a * At + b * oA;
-        }
-        if (tid < kMergeCols) out[row * kHeadDim + c] = Lt > 0.f ? At / Lt : 0.f;
+    if (tid < kMergeCols) {
+        float Mt = s_m[0][cc], Lt = s_l[0][cc], At = s_a[0][cc];
+#pragma unroll
+        for (int k = 1; k < kWavesM; ++k) merge_pair(Mt, Lt, At, s_m[k][cc], s_l[k][cc], s_a[k][cc]);
+        out[row * kHeadDim + c] = Lt > 0.f ? At / Lt : 0.f;
     }
 }
 
