@@ -260,6 +260,15 @@ __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
 }
 #pragma clang diagnostic pop
 
+// Workgroup barrier that orders LDS only: its fences wait for this wave's LDS
+// operations (lgkmcnt) and not for its outstanding global loads, so a tile's DMA in
+// flight does not hold the barrier.
+__device__ __forceinline__ void lds_barrier() {
+    __builtin_amdgcn_fence(__ATOMIC_RELEASE, "workgroup", "local");
+    __builtin_amdgcn_s_barrier();
+    __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
+}
+
 template <int V, int RD>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma_kernel(
     const uint16_t* __restrict__ q, uint8_t* __restrict__ cache, const int64_t* __restrict__ seq_byte_off,
@@ -376,10 +385,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     };
     constexpr bool kStageInK1 = KB >= 510 * 4;  // see the staging area below
     int64_t tau = t0 + wave;
-    if (tau < t1 && (kStageInK1 || !appender)) {
-        dma_k(tau, 0);
-        dma_v(tau);
-    }
 
     // ------------------------------------------------------------------ prologue
     // the appender's staging area for the thresholds: its second K buffer when that
@@ -422,7 +427,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
             ubase += units;
         }
     }
-    __syncthreads();  // zeroed q split before it is filled
+    lds_barrier();  // zeroed q split before it is filled
     if (my_w > 0) {
 #pragma unroll
         for (int e = 0; e < 2; ++e) {
@@ -438,7 +443,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
             }
         }
     }
-    __syncthreads();
+    // The first tile's DMA goes out once the prologue's own loads have been consumed:
+    // loads complete in issue order, so a wait for any load issued before the DMA
+    // but used after it would also wait for the whole tile.  The barriers here order
+    // LDS only, so each wave starts on its tile as soon as its own K section lands.
+    if (tau < t1 && (kStageInK1 || !appender)) {
+        dma_k(tau, 0);
+        dma_v(tau);
+    }
+    lds_barrier();
     // B operand rows: the lane's column (hi|lo, head) on the diagonal, else a row that
     // stays zero (the last unit of hi row 0: at most 22 units are ever filled)
     const uint16_t* qb = bdiag ? &sm.qsplit[(col >> 3) & 1][col & 7][0] : &sm.qsplit[0][0][8 * (kMaxUnits - 1)];
