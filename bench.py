@@ -68,7 +68,12 @@ def traffic_from(fetch_csv: str, write_csv: str, copy_mib: int, workload: str):
     def per_kernel(path, counter):
         rows = [r for r in csv.DictReader(open(path)) if r["Counter_Name"] == counter]
         rows.sort(key=lambda r: int(r["Dispatch_Id"]))
-        dec = [float(r["Counter_Value"]) for r in rows if "decode_mfma_kernel" in r["Kernel_Name"]]
+        dec_rows = [r for r in rows if "decode_mfma_kernel" in r["Kernel_Name"]]
+        # the per-layer step launches only (the layer-batched capability launch has a
+        # larger grid): the modal grid size among the decode dispatches
+        grids = [r["Grid_Size"] for r in dec_rows]
+        grid = max(set(grids), key=grids.count) if grids else None
+        dec = [float(r["Counter_Value"]) for r in dec_rows if r["Grid_Size"] == grid]
         # the copy probe: the last three copy dispatches of the run (nothing follows them)
         cp = [r for r in rows if "copy" in r["Kernel_Name"].lower()][-3:]
         big = [float(r["Counter_Value"]) for r in cp]
