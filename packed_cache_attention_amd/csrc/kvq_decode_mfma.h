@@ -447,10 +447,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     // loads complete in issue order, so a wait for any load issued before the DMA
     // but used after it would also wait for the whole tile.  The barriers here order
     // LDS only, so each wave starts on its tile as soon as its own K section lands.
-    if (tau < t1 && (kStageInK1 || !appender)) {
-        dma_k(tau, 0);
-        dma_v(tau);
-    }
+    if (tau < t1 && (kStageInK1 || !appender)) dma_k(tau, 0);
     lds_barrier();
     // B operand rows: the lane's column (hi|lo, head) on the diagonal, else a row that
     // stays zero (the last unit of hi row 0: at most 22 units are ever filled)
@@ -489,10 +486,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         // the staging reads have returned: the buffers may refill
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         __builtin_amdgcn_wave_barrier();
-        if (!kStageInK1 && tau < t1) {
-            dma_k(tau, 0);
-            dma_v(tau);
-        }
+        if (!kStageInK1 && tau < t1) dma_k(tau, 0);
         if (app.window > 0 && app.k_new != nullptr) {  // the step's new token takes the ring row just read
             const int64_t nr = (int64_t)s * app.new_stride_seq + (int64_t)kvh * app.new_stride_head + 2 * lane;
             const uint32_t kn = *(const uint32_t*)(app.k_new + nr);
@@ -511,13 +505,23 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
 
     // ------------------------------------------------------------------ tiles
     int kb = 0;
+    bool first = true;
     for (; tau < t1; tau += kWaves) {
         const int nvalid = (int)min((int64_t)kTile, len - tau * kTile);
         const bool more = tau + kWaves < t1;
         // K section landed: the lane's record to registers, then the next K section
-        // into the other K buffer
-        __builtin_amdgcn_s_waitcnt(wait_vm(VI));
-        __builtin_amdgcn_wave_barrier();
+        // into the other K buffer.  The first tile's V section is requested only once
+        // its K section is in (the start of the launch asks for K sections alone, so
+        // they arrive sooner); later V sections are already in flight behind it.
+        if (first) {
+            __builtin_amdgcn_s_waitcnt(wait_vm(0));
+            __builtin_amdgcn_wave_barrier();
+            dma_v(tau);
+            first = false;
+        } else {
+            __builtin_amdgcn_s_waitcnt(wait_vm(VI));
+            __builtin_amdgcn_wave_barrier();
+        }
         uint8_t* kbuf = wbuf + kb * KB;
         const bool tail_here = appender && tau == tail_tau;
         if (tail_here) {  // the appended record into the LDS copy (word k of record p: chunk-major)
