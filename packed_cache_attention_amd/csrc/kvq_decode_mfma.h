@@ -366,10 +366,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
 
     // Tile DMA.  A K section goes to K buffer kb with record chunks chunk-major
     // (chunk k of record r at 16*(64*k + r)); a V section (runs, then scales) goes
-    // linearly to the V buffer.  Each wave issues, in order: K(n+1) when tile n
-    // starts and V(n+1) when tile n's V reads have returned, so at the start of a
-    // tile its K section is complete once at most VI loads are outstanding, and its
-    // V section once at most KI are (none after the wave's last tile).
+    // linearly to the V buffer.  Each wave issues, in order: K(n+1) once tile n's V
+    // section has landed and V(n+1) once tile n's V reads have returned (the first
+    // tile: K in the prologue, V once that K is in), so at the start of a tile its K
+    // section is complete once at most VI loads are outstanding, and its V section
+    // once none are.
     auto dma_k = [&](int64_t tau, int kb) {
         const uint8_t* tile = head_base + tau * TB;
 #pragma unroll
@@ -537,7 +538,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         }
         rec[RD] = 0;
         rec[RD + 1] = 0;
-        if (more) dma_k(tau + kWaves, kb ^ 1);
         kb ^= 1;
         // ---- QK: this lane's token, 8 fields of one width class per instruction
         floatx16 acc0 = {}, acc1 = {};
@@ -552,10 +552,11 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         floatx16 acc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[i] = acc0[i] + acc1[i];
-        // ---- V section landed (scales, runs)
-        if (more) __builtin_amdgcn_s_waitcnt(wait_vm(KI));
-        else __builtin_amdgcn_s_waitcnt(wait_vm(0));
+        // ---- V section landed (scales, runs); the next K section then goes out (into
+        // the K buffer this tile's records left), behind this tile's V in the queue
+        __builtin_amdgcn_s_waitcnt(wait_vm(0));
         __builtin_amdgcn_wave_barrier();
+        if (more) dma_k(tau + kWaves, kb);
         uint8_t* vsec = wbuf + 2 * KB;
         const float* scl = (const float*)(vsec + kHeadDim * 8 * V);
         if (tail_here) {  // the appended V codes and scales into the LDS copy
