@@ -118,3 +118,51 @@ def test_window_steps_match_oracle(case):
     for i, (K, V, _) in enumerate(seqs):
         for t in range(max(lens[i] - W, 0), lens[i]):
             assert torch.equal(wk[i, :, t % W], K[t]) and torch.equal(wv[i, :, t % W], V[t])
+
+
+def test_c3_full_size_window_step_as_benchmarked():
+    """The window step the benchmark times, at its size: one 128K Qwen2.5-3B-shaped layer
+    with W = 128 (131072 tokens: the first 130944 packed, the newest 128 in the ring),
+    one kvq_window_decode_step in the automatic plan with max_len = capacity.  The token
+    leaving the window is packed inside the attention launch (bytes against the
+    oracle's packing), the new token takes its ring row (exact), and the output matches
+    the oracle's attention over the packed prefix and the fp16 window."""
+    wl = synth.WORKLOADS["c3"]
+    layer, W = 5, 128
+    say("c3 full-size window step, layer %d, W %d" % (layer, W))
+    K, V, _ = synth.gen_layer(wl, 0, layer)
+    n = K.shape[0]
+    kn, vn, qn = synth.gen_new_token(wl, 0, layer, n, 0)
+    cap = synth.ceil_to(n + 64, 64)
+    npk = n - W
+    r = run_batch([(K[:npk], V[:npk], qn)], wl.k_budget, wl.v_bits, cap, check_attn=False)
+    g, region, H = r["g"], kvq.cache_bytes(r["g"]), wl.n_kv_heads
+    win_k = torch.empty(1, H, W, 128, dtype=torch.float16)
+    win_v = torch.empty_like(win_k)
+    for t in range(npk, n):
+        win_k[0, :, t % W] = K[t]
+        win_v[0, :, t % W] = V[t]
+    win_k, win_v = win_k.cuda(), win_v.cuda()
+    ws = torch.empty(kvq.window_workspace_bytes(g, W, wl.n_q_heads, 1, cap) // 4 + 4, dtype=torch.float32,
+                     device="cuda")
+    out = torch.empty(1, wl.n_q_heads, 128, dtype=torch.float32, device="cuda")
+    kvq.window_decode_step(g, W, qn[None].cuda().contiguous(), kn[None].cuda().contiguous(),
+                           vn[None].cuda().contiguous(), win_k, win_v, r["cache"], r["off"],
+                           torch.tensor([n + 1], dtype=torch.int32, device="cuda"), cap, r["kbits"], r["ksig"],
+                           r["vsig"], out, ws)
+    # the token leaving the window (position n - W) packed at its slot
+    oc = r["oc"].copy()
+    oracle.quantize_pack(r["ogeom"], oc[:region], K[npk:npk + 1].numpy(), V[npk:npk + 1].numpy(), npk, r["ob"],
+                         r["osig"], r["ovsig"])
+    np.testing.assert_array_equal(r["cache"].cpu().numpy(), oc)
+    # the new token in the ring row the leaving token held; the other rows untouched
+    wk, wv = win_k.cpu(), win_v.cpu()
+    assert torch.equal(wk[0, :, n % W], kn) and torch.equal(wv[0, :, n % W], vn)
+    for t in range(npk + 1, n):
+        assert torch.equal(wk[0, :, t % W], K[t]) and torch.equal(wv[0, :, t % W], V[t])
+    # attention: packed prefix [0, n - W], fp16 window [n - W + 1, n]
+    kw = torch.cat([K[npk + 1:n], kn[None]]).numpy()
+    vw = torch.cat([V[npk + 1:n], vn[None]]).numpy()
+    ref = oracle.decode_attention_window(r["ogeom"], oc[:region], qn.numpy(), npk + 1, kw, vw, r["ob"], r["osig"],
+                                         r["ovsig"])
+    say("c3 window step: bytes and ring ok, attention worst rel %.2e" % check_attention(out.cpu().numpy(), ref[None]))
