@@ -80,18 +80,19 @@ def test_prefill_matches_oracle(case):
     say("prefill %s ok, worst rel %.2e" % (name, worst))
 
 
-def test_prefill_c3_full_size_sampled_rows():
-    """Qwen2.5-3B-shaped 128K K3V3 layer: the last 512-token chunk of a chunked prefill
-    (queries at 130560 .. 131071 over the whole packed context) in the automatic plan;
-    sampled query rows against the oracle's decode attention at each row's length."""
+@pytest.mark.parametrize("nt", [512, 2048])
+def test_prefill_c3_full_size_sampled_rows(nt):
+    """Qwen2.5-3B-shaped 128K K3V3 layer: the last nt-token chunk of a chunked prefill
+    (queries at 131072 - nt .. 131071 over the whole packed context) in the automatic
+    plan -- 2048 is the chunk the benchmark times; sampled query rows against the
+    oracle's decode attention at each row's length."""
     wl = synth.WORKLOADS["c3"]
-    say("prefill c3 full size")
+    say("prefill c3 full size, chunk %d" % nt)
     K, V, _ = synth.gen_layer(wl, 0, 0)
     n = K.shape[0]
     r = run_batch([(K, V, torch.zeros(wl.n_q_heads, 128, dtype=torch.float16))], wl.k_budget, wl.v_bits,
                   synth.ceil_to(n + 64, 64), check_attn=False)
     g, region = r["g"], kvq.cache_bytes(r["g"])
-    nt = 512
     a = n - nt
     q = synth.gen_chunk_queries(wl, 0, 0, a, nt).unsqueeze(0).contiguous()
     qd = q.cuda()
@@ -102,7 +103,7 @@ def test_prefill_c3_full_size_sampled_rows():
                             torch.tensor([nt], dtype=torch.int32, device="cuda"), n, r["kbits"], r["ksig"], r["vsig"],
                             out, ws)
     o = out.cpu().numpy()[0]
-    for j in (0, 1, 255, 511):
+    for j in (0, 1, nt // 2 - 1, nt - 1):
         ref = oracle.decode_attention(r["ogeom"], r["oc"][:region], q[0, j].numpy(), a + j + 1, r["ob"], r["osig"],
                                       r["ovsig"])
         say("row %d worst rel %.2e" % (j, check_attention(o[j][None], ref[None])))
