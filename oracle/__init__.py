@@ -20,7 +20,12 @@ import numpy as np
 
 _HERE = os.path.dirname(os.path.abspath(__file__))
 _SRC = os.path.join(_HERE, "kvq_oracle.c")
-_LIB = os.path.join(_HERE, "liboracle.so")
+# KVQ_ORACLE_SANITIZE=1 builds and loads an AddressSanitizer + UBSan build instead (the
+# process must preload the sanitizer runtimes: LD_PRELOAD="$(gcc -print-file-name=libasan.so)
+# $(gcc -print-file-name=libubsan.so)" ASAN_OPTIONS=detect_leaks=0)
+_SANITIZE = os.environ.get("KVQ_ORACLE_SANITIZE") == "1"
+_LIB = os.path.join(_HERE, "liboracle_san.so" if _SANITIZE else "liboracle.so")
+_SAN_FLAGS = ["-fsanitize=address,undefined", "-fno-sanitize-recover=undefined", "-fno-omit-frame-pointer", "-g"]
 
 PAIR_HALF, PAIR_INTERLEAVED = 0, 1
 GREEDY, UNIFORM = 0, 1
@@ -33,7 +38,8 @@ def build(force: bool = False) -> str:
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(
             ["gcc", "-O2", "-std=c11", "-D_DEFAULT_SOURCE", "-ffp-contract=off", "-fno-fast-math",
-             "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wno-unused-function", _SRC, "-o", tmp, "-lm"])
+             "-fopenmp", "-fPIC", "-shared", "-Wall", "-Wno-unused-function"] + (_SAN_FLAGS if _SANITIZE else []) +
+            [_SRC, "-o", tmp, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -66,6 +72,8 @@ def lib() -> C.CDLL:
     L.or_decode_attention_window.argtypes = [P, I64, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, I64, P, P, I64,
                                              F64, P]
     L.or_prefill_attention.argtypes = [P, I64, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, I64, I64, F64, P]
+    L.or_attend_partial.argtypes = [P, P, P, I64, I32, F64, P, P, P]
+    L.or_merge_partials.argtypes = [P, I64, I32, I32, P]
     return L
 
 
@@ -253,6 +261,27 @@ def attend(q: np.ndarray, khat: np.ndarray, vhat: np.ndarray, scale: float) -> n
     lib().or_attend(_p(np.ascontiguousarray(q, np.float64)), _p(np.ascontiguousarray(khat, np.float64)),
                     _p(np.ascontiguousarray(vhat, np.float64)), n, d, scale, _p(o))
     return o
+
+
+def attend_partial(q: np.ndarray, khat: np.ndarray, vhat: np.ndarray, scale: float):
+    """Partial (m, l, o) of one query over a chunk of tokens (m in log2 units, o
+    unnormalised) -- the split-K format; see or_attend_partial."""
+    n, d = khat.shape
+    o = np.zeros(d, np.float64)
+    m = C.c_double()
+    l_ = C.c_double()
+    lib().or_attend_partial(_p(np.ascontiguousarray(q, np.float64)), _p(np.ascontiguousarray(khat, np.float64)),
+                            _p(np.ascontiguousarray(vhat, np.float64)), n, d, scale, C.byref(m), C.byref(l_), _p(o))
+    return m.value, l_.value, o
+
+
+def merge_partials(partials: np.ndarray) -> np.ndarray:
+    """fp64 log-sum-exp merge of partials [rows, n_split, d + 2] (binary32: m, l, o)."""
+    p = np.ascontiguousarray(partials, np.float32)
+    rows, ns, d2 = p.shape
+    out = np.zeros((rows, d2 - 2), np.float64)
+    lib().or_merge_partials(_p(p), rows, ns, d2 - 2, _p(out))
+    return out
 
 
 class Geometry:

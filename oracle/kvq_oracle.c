@@ -710,3 +710,71 @@ void or_prefill_attention(const uint8_t *region, int64_t n_tiles, int n_kv, int 
         free(kc); free(vc); free(kscale); free(vscale); free(kh); free(vh);
     }
 }
+
+/* ------------------------------------------------------------------------- */
+/* Split attention and the log-sum-exp merge                                 */
+/* ------------------------------------------------------------------------- */
+/*
+ * A long sequence is attended in chunks whose partial results are combined
+ * afterwards (the split-K softmax merge).  The partial of one query over a chunk of
+ * n tokens is, with logits taken in log2 units (z_t = scale * log2(e) * q.khat_t):
+ *   m = max_t z_t   (-inf for an empty chunk),
+ *   l = sum_t 2^(z_t - m),
+ *   o_c = sum_t 2^(z_t - m) vhat_{t,c}   (unnormalised).
+ * Any reference value in place of the maximum gives the same merged result, as long
+ * as l and o use the same one.
+ */
+void or_attend_partial(const double *q, const double *khat, const double *vhat, int64_t n, int d,
+                       double scale, double *m, double *l, double *o)
+{
+    for (int c = 0; c < d; c++) o[c] = 0;
+    *m = -INFINITY;
+    *l = 0;
+    if (n == 0) return;
+    double *z = (double *)malloc(sizeof(double) * (size_t)n);
+    double mx = -INFINITY;
+    for (int64_t t = 0; t < n; t++) {
+        double s = 0;
+        for (int c = 0; c < d; c++) s += q[c] * khat[t * d + c];
+        z[t] = scale * M_LOG2E * s;
+        if (z[t] > mx) mx = z[t];
+    }
+    double lsum = 0;
+    for (int64_t t = 0; t < n; t++) {
+        double w = exp2(z[t] - mx);
+        lsum += w;
+        for (int c = 0; c < d; c++) o[c] += w * vhat[t * d + c];
+    }
+    *m = mx;
+    *l = lsum;
+    free(z);
+}
+
+/*
+ * Merge of n_split partials of rows, in the library's partials format:
+ *   part[(row * n_split + j) * (d + 2) + {0: m_j, 1: l_j, 2 + c: o_j,c}]  (binary32)
+ * out[row][c] = sum_j 2^(m_j - M) o_j,c / sum_j 2^(m_j - M) l_j with M = max_j m_j,
+ * computed in fp64; a row whose partials are all empty (M = -inf) or whose weight sum
+ * is 0 gives 0.
+ */
+void or_merge_partials(const float *part, int64_t n_rows, int n_split, int d, double *out)
+{
+    for (int64_t r = 0; r < n_rows; r++) {
+        const float *p = part + r * n_split * (int64_t)(d + 2);
+        double M = -INFINITY;
+        for (int j = 0; j < n_split; j++)
+            if ((double)p[j * (d + 2)] > M) M = p[j * (d + 2)];
+        double L = 0;
+        double *o = out + r * d;
+        for (int c = 0; c < d; c++) o[c] = 0;
+        if (M == -INFINITY) continue;
+        for (int j = 0; j < n_split; j++) {
+            const float *pj = p + j * (d + 2);
+            if ((double)pj[0] == -INFINITY) continue;
+            double w = exp2((double)pj[0] - M);
+            L += w * (double)pj[1];
+            for (int c = 0; c < d; c++) o[c] += w * (double)pj[2 + c];
+        }
+        for (int c = 0; c < d; c++) o[c] = (L > 0) ? o[c] / L : 0.0;
+    }
+}

@@ -41,6 +41,56 @@ def test_token_scale_properties():
     assert oracle.token_scale(np.zeros(128, np.float16)) == 0.0
 
 
+def _golden_token(case):
+    x = np.zeros(case["d"], np.uint16)
+    for k, v in case["coords_fp16_bits"].items():
+        if ".." in k:
+            a, b = map(int, k.split(".."))
+            x[a:b + 1] = v
+        else:
+            x[int(k)] = v
+    return x
+
+
+def _tree_sum32(sq):
+    """Balanced pairwise binary32 sum, pairs (0,1), (2,3), ... at every level."""
+    s = np.array(sq, np.float32)
+    while len(s) > 1:
+        s = (s[0::2] + s[1::2]).astype(np.float32)
+    return s[0]
+
+
+def test_token_scale_tree_order_golden():
+    """The per-token scale's summation order decides codes bit for bit; two hand-derived
+    tokens (tests/golden/token_scale_tree.json) separate the balanced coordinate-order
+    tree from a sequential sum, an exactly rounded sum and a tree that pairs j with
+    j + n/2.  The alternatives are evaluated here only to show that each would fail."""
+    g = json.load(open(os.path.join(GOLDEN, "token_scale_tree.json")))
+    for case in g["cases"]:
+        x = _golden_token(case)
+        s = np.float32(oracle.token_scale(x))
+        assert int(s.view(np.uint32)) == case["expected_scale_bits"], case["name"]
+        sq = x.view(np.float16).astype(np.float32) ** 2
+        assert np.float32(np.sqrt(_tree_sum32(sq))) == s
+        alts = {}
+        seq = np.float32(0)
+        for v in sq:
+            seq = np.float32(seq + v)
+        alts["sequential binary32 sum in coordinate order"] = seq
+        back = np.float32(0)
+        for v in sq[::-1]:
+            back = np.float32(back + v)
+        alts["sequential sum from the last coordinate down"] = back
+        stride = sq.copy()
+        while len(stride) > 1:
+            stride = (stride[:len(stride) // 2] + stride[len(stride) // 2:]).astype(np.float32)
+        alts["balanced tree pairing coordinate j with j + n/2 at each level"] = stride[0]
+        alts["exact sum rounded once"] = np.float32(np.sum(sq.astype(np.float64)))
+        # each alternative the fixture names gives a different scale
+        for name in case["alternatives"]:
+            assert np.float32(np.sqrt(alts[name])) != s, (case["name"], name)
+
+
 # ---------------- codes ----------------
 
 def _brute(y, w):
@@ -70,6 +120,42 @@ def test_codes_are_nearest_levels(w):
     codes2, scale2 = oracle.encode((x.astype(np.float32) * 4).astype(np.float16), width, sig)
     np.testing.assert_array_equal(codes2, codes)
     np.testing.assert_array_equal(scale2, scale * 4)
+
+
+@pytest.mark.parametrize("w", range(1, 9))
+def test_dequant_cell_bound(w):
+    """A dequantized coordinate is the level of the cell its code names: for an inner
+    cell |khat - k| <= s * sigma * (half the gap to the farther neighbouring level),
+    and for the two outer cells khat lies on the far side of the one threshold that
+    bounds them.  Checked per coordinate against the codebook's own thresholds (the
+    midpoints of neighbouring binary16 levels) with the rounding of the binary32
+    threshold products as the only slack."""
+    d, n = 128, 96
+    r = np.random.default_rng(100 + w)
+    x = (r.standard_normal((n, d)) * np.exp(r.uniform(-2, 2, (1, d)))).astype(np.float16)
+    width = np.full(d, w, np.int32)
+    sig = np.exp(r.uniform(-4, 0, d)).astype(np.float32)
+    codes, scale = oracle.encode(x, width, sig)
+    khat = oracle.dequant(codes, width, sig, scale)
+    lv = oracle.codebook(w)["levels_h"]
+    thr = np.concatenate([[-np.inf], 0.5 * (lv[1:] + lv[:-1]), [np.inf]])
+    unit = scale[:, None].astype(np.float64) * sig[None, :].astype(np.float64)
+    xx = x.astype(np.float64)
+    c = codes.astype(np.int64)
+    slack = 4.0 * 2.0 ** -24 * unit * np.max(np.abs(lv)) + 1e-300
+    lo, hi = thr[c], thr[c + 1]
+    # the value lies in its cell (up to the threshold products' rounding)
+    assert np.all(xx >= unit * lo - slack) and np.all(xx <= unit * hi + slack)
+    half = np.maximum(lv[c] - lo, hi - lv[c])
+    inner = (c > 0) & (c < (1 << w) - 1)
+    assert inner.sum() > n * d // 4 or w == 1
+    err = np.abs(khat - xx)
+    assert np.all(err[inner] <= (unit * half)[inner] * (1 + 1e-6) + slack[inner])
+    # the dequantized value is s * sigma * level, an exact binary16 level times the scales
+    np.testing.assert_allclose(khat, unit * lv[c], rtol=1e-15, atol=0)
+    top = c == (1 << w) - 1
+    assert np.all(khat[top] >= unit[top] * lv[-1] * (1 - 1e-15))
+    assert np.all(xx[c == 0] <= (unit * thr[1])[c == 0] + slack[c == 0])
 
 
 def test_codes_passthrough_and_zero_width():
@@ -194,6 +280,75 @@ def test_attention_special_cases():
     assert (oe == 0).all()
 
 
+def test_attention_shift_permutation_and_dominance():
+    """Exact attention is unchanged by a constant added to every logit (an extra
+    coordinate with q = 1 and khat = C for all tokens), by any reordering of the
+    tokens, and returns the value row of a token whose logit exceeds the others' by
+    far more than the double exponent range can weigh."""
+    r = np.random.default_rng(5)
+    n, d = 300, 128
+    q = r.standard_normal(d)
+    K = r.standard_normal((n, d))
+    V = r.standard_normal((n, d))
+    sc = 1 / np.sqrt(d)
+    o = oracle.attend(q, K, V, sc)
+    for C in (-3e4, -7.5, 0.25, 40.0, 3e4):
+        q1 = np.concatenate([q, [1.0]])
+        K1 = np.concatenate([K, np.full((n, 1), C)], 1)
+        V1 = np.concatenate([V, r.standard_normal((n, 1))], 1)
+        o1 = oracle.attend(q1, K1, V1, sc)
+        np.testing.assert_allclose(o1[:d], o, rtol=1e-11, atol=1e-13)
+    perm = r.permutation(n)
+    np.testing.assert_allclose(oracle.attend(q, K[perm], V[perm], sc), o, rtol=1e-11, atol=1e-13)
+    K2 = K.copy()
+    K2[123] = q * 1e4  # logit ~ 1e4 * |q|^2 / sqrt(d), others O(1)
+    np.testing.assert_array_equal(oracle.attend(q, K2, V, sc), V[123])
+    # the reference -- text book softmax in numpy on the same operands
+    z = K @ q * sc
+    p = np.exp(z - z.max())
+    np.testing.assert_allclose(o, (p / p.sum()) @ V, rtol=1e-12, atol=1e-14)
+
+
+def test_split_merge_equals_full_attention():
+    """Split-K: exact attention of every chunk of a partition of the tokens (empty
+    chunks included), merged by the log-sum-exp rule, equals exact attention over all
+    tokens; shifting a partial's reference by delta (l, o scaled by 2^-delta) leaves
+    the merge unchanged; a row of empty partials merges to 0; one chunk merges to o/l."""
+    r = np.random.default_rng(11)
+    n, d = 517, 128
+    q = r.standard_normal(d)
+    K = r.standard_normal((n, d)) * 2.0
+    V = r.standard_normal((n, d))
+    sc = 1 / np.sqrt(d)
+    full = oracle.attend(q, K, V, sc)
+    for n_split in (1, 2, 7, 33):
+        cuts = np.sort(r.integers(0, n + 1, n_split - 1))
+        bounds = np.concatenate([[0], cuts, [n]])
+        part = np.zeros((1, n_split, d + 2), np.float64)
+        for j in range(n_split):
+            a, b = bounds[j], bounds[j + 1]
+            m, l_, o = oracle.attend_partial(q, K[a:b], V[a:b], sc)
+            if b == a:
+                assert m == -np.inf and l_ == 0 and not o.any()
+            part[0, j, 0], part[0, j, 1], part[0, j, 2:] = m, l_, o
+        # the merge takes binary32 partials, so allow their rounding
+        merged = oracle.merge_partials(part.astype(np.float32))[0]
+        np.testing.assert_allclose(merged, full, rtol=0, atol=2e-6 * np.abs(full).max())
+        shifted = part.copy()
+        fin = np.isfinite(shifted[0, :, 0])
+        delta = r.uniform(-5, 5, n_split)
+        shifted[0, fin, 0] += delta[fin]
+        shifted[0, fin, 1:] *= 2.0 ** -delta[fin, None]
+        np.testing.assert_allclose(oracle.merge_partials(shifted.astype(np.float32))[0], merged,
+                                   rtol=0, atol=2e-6 * np.abs(full).max())
+    single = np.zeros((1, 1, d + 2), np.float32)
+    single[0, 0, 0], single[0, 0, 1], single[0, 0, 2:] = 3.0, 4.0, np.arange(d)
+    np.testing.assert_array_equal(oracle.merge_partials(single)[0], np.arange(d) / 4.0)
+    empty = np.zeros((2, 3, d + 2), np.float32)
+    empty[:, :, 0] = -np.inf
+    assert not oracle.merge_partials(empty).any()
+
+
 def test_window_attention_pins():
     """fp16 recent window: a window holding every token is textbook attention on the
     fp16 inputs; an empty window is the packed-only attention; with the passthrough
@@ -291,12 +446,27 @@ def test_prefill_attention_pins():
     np.testing.assert_array_equal(o2, o)
 
 
-@pytest.mark.parametrize("cfg,n,heads", [("c1", 1024, [0]), ("c2", 8192, [0, 5])])
-def test_fidelity_gate_beats_uniform(cfg, n, heads):
-    """Block-GTQ's query-key logit MAE is no worse than either uniform baseline."""
+# (config, tokens, [(sequence, layer, KV head), ...]): every seeded config, sampled
+# layers and heads (the model-shaped configs draw each (sequence, layer, head) from a
+# stream of its own; the 512K config shares the 128K one's streams, so it is sampled
+# at other layers)
+GATE_CASES = [
+    ("c1", 1024, [(0, 0, 0)]),
+    ("c2", 8192, [(0, 0, 0), (0, 0, 5)]),
+    ("c3", 4096, [(0, 0, 0), (0, 17, 1), (0, 35, 0)]),
+    ("c4", 8192, [(0, 5, 1), (0, 29, 0)]),
+    ("c5", 4096, [(3, 0, 0), (11, 27, 3), (7, 13, 2)]),
+]
+
+
+@pytest.mark.parametrize("cfg,n,units", GATE_CASES)
+def test_fidelity_gate_beats_uniform(cfg, n, units):
+    """Block-GTQ's query-key logit MAE is no worse than either uniform baseline at the
+    same K budget (the page's per-layer comparison against uniform TQ-MSE), on sampled
+    layers and heads of every seeded config."""
     wl = synth.WORKLOADS[cfg]
-    for h in heads:
-        k, _, q = synth.gen_head(wl, 0, 0, h, n)
+    for seq, layer, h in units:
+        k, _, q = synth.gen_head(wl, seq, layer, h, n)
         r = baselines.mae_report(q.numpy(), k.numpy(), wl.k_budget)
-        assert r["blockgtq"] <= r["u_same"] and r["blockgtq"] <= r["u_rot"], r
-        assert r["blockgtq"] < 0.7 * min(r["u_same"], r["u_rot"]), r
+        assert r["blockgtq"] <= r["u_same"] and r["blockgtq"] <= r["u_rot"], (cfg, seq, layer, h, r)
+        assert r["blockgtq"] < 0.7 * min(r["u_same"], r["u_rot"]), (cfg, seq, layer, h, r)
