@@ -14,7 +14,9 @@
  * Conventions for every call:
  *  - All buffers are owned by the caller; pointers marked "device" are device
  *    memory on the current HIP device.  The library allocates no device memory
- *    and keeps no pointer after returning.
+ *    and keeps no pointer after returning (the one device buffer of its own is the
+ *    fixed array of kvq_packed_decode_attn_noalloc, reserved when the library is
+ *    loaded on a GPU).
  *  - `stream` is a hipStream_t (NULL = default stream).  Calls enqueue work and
  *    return without synchronising; asynchronous faults surface at the caller's
  *    next synchronisation.
@@ -182,6 +184,24 @@ int32_t kvq_packed_decode_attn_ex(const kvq_geom *g, int32_t n_q_heads, const vo
                                   const float *v_sigma, float softmax_scale, float *out, void *workspace,
                                   size_t workspace_bytes, int32_t kernel, int32_t tiles_per_split,
                                   void *stream);
+
+/* Allocation-free variant of kvq_packed_decode_attn, for callers that cannot allocate
+ * device memory: code under HIP graph capture, tight serving loops, harnesses that forbid
+ * hipMalloc.  Same arguments, meaning and result as kvq_packed_decode_attn (automatic
+ * kernel and split plan) without the workspace: the split partials live in a device array
+ * owned by the library, KVQ_NOALLOC_SCRATCH_BYTES bytes per GPU, reserved when the library
+ * is loaded on that GPU and held until the process ends.  The call allocates nothing
+ * (no hipMalloc or allocating library routine).  Returns KVQ_ERR_WORKSPACE when the plan's
+ * partials (kvq_decode_workspace_bytes for the same arguments) exceed that size.  All
+ * calls on one GPU share its array: calls that overlap in time on one GPU (different
+ * streams, or threads without ordering) race and give undefined results; calls ordered on
+ * one stream are safe.  The first call on each device looks the array up (a HIP symbol
+ * query) under a lock. */
+#define KVQ_NOALLOC_SCRATCH_BYTES (8u << 20)
+int32_t kvq_packed_decode_attn_noalloc(const kvq_geom *g, int32_t n_q_heads, const void *q, const uint8_t *cache,
+                                       const int64_t *seq_byte_off, const int32_t *seq_len, int32_t n_seq,
+                                       int64_t max_len, const uint8_t *k_bits, const float *k_sigma,
+                                       const float *v_sigma, float softmax_scale, float *out, void *stream);
 
 /* The two phases of kvq_packed_decode_attn_ex, for callers that merge partials
  * themselves (e.g. partials gathered from several devices that each hold a token

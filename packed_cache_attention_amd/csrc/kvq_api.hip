@@ -5,6 +5,8 @@
 #include <stdlib.h>
 #include <string.h>
 
+#include <mutex>
+
 #include "kvq_internal.h"
 
 namespace {
@@ -171,7 +173,8 @@ namespace {
 int32_t check_decode(const kvq_geom* g, int32_t n_q_heads, const void* q, const uint8_t* cache,
                      const int64_t* seq_byte_off, const int32_t* seq_len, int32_t n_seq, int64_t max_len,
                      const uint8_t* k_bits, const float* k_sigma, const float* v_sigma, const void* ws,
-                     size_t ws_bytes, int32_t kernel, int32_t tiles_per_split, DecodePlan* plan, const char* fn) {
+                     size_t ws_bytes, int32_t kernel, int32_t tiles_per_split, DecodePlan* plan, const char* fn,
+                     bool ws_owned_by_library = false) {
     int32_t st = check_geom(g, true, fn);
     if (st) return st;
     if (n_q_heads < 1 || n_q_heads % g->n_kv_heads) return fail(KVQ_ERR_SHAPE, fn, "n_q_heads");
@@ -182,7 +185,7 @@ int32_t check_decode(const kvq_geom* g, int32_t n_q_heads, const void* q, const 
     st = plan_decode(*g, n_q_heads, n_seq, max_len, kernel, tiles_per_split, plan);
     if (st) return fail(st, fn, "no kernel for this geometry");
     if (n_seq == 0) return KVQ_OK;
-    if (!q || !cache || !seq_byte_off || !seq_len || !k_bits || !k_sigma || !v_sigma || !ws)
+    if (!q || !cache || !seq_byte_off || !seq_len || !k_bits || !k_sigma || !v_sigma || (!ws && !ws_owned_by_library))
         return fail(KVQ_ERR_ARG, fn, "null pointer");
     if (!aligned(q, 16) || !aligned(cache, 16) || !aligned(ws, 16) || !aligned(seq_byte_off, 8) ||
         !aligned(seq_len, 4) || !aligned(k_sigma, 4) || !aligned(v_sigma, 4))
@@ -279,6 +282,60 @@ int32_t kvq_packed_decode_attn(const kvq_geom* g, int32_t n_q_heads, const void*
     return kvq_packed_decode_attn_ex(g, n_q_heads, q, cache, seq_byte_off, seq_len, n_seq, max_len, k_bits, k_sigma,
                                      v_sigma, softmax_scale, out, workspace, workspace_bytes, KVQ_DECODE_AUTO, 0,
                                      stream);
+}
+
+// ---------------------------------------------------------------- allocation-free decode
+// The split partials of kvq_packed_decode_attn_noalloc live in a library-owned device
+// array (one per GPU, alive until the process ends) instead of a caller workspace.
+// The array's name is a host-side stand-in: its device address is looked up once per
+// device with hipGetSymbolAddress, and only that address is handed to kernels.
+static __device__ __align__(256) uint8_t scratch[KVQ_NOALLOC_SCRATCH_BYTES];
+
+namespace {
+constexpr int kMaxDevices = 64;
+std::mutex g_scratch_mu;
+void* g_scratch_ptr[kMaxDevices];
+
+// the current device's copy of `scratch` (looked up on the device's first call)
+int32_t scratch_address(void** out, const char* fn) {
+    int dev = -1;
+    hipError_t e = hipGetDevice(&dev);
+    if (e != hipSuccess) return hip_status(e, fn);
+    if (dev < 0 || dev >= kMaxDevices) return fail(KVQ_ERR_ARG, fn, "device ordinal beyond the scratch table");
+    std::lock_guard<std::mutex> lock(g_scratch_mu);
+    if (g_scratch_ptr[dev] == nullptr) {
+        void* ptr = nullptr;
+        e = hipGetSymbolAddress(&ptr, HIP_SYMBOL(scratch));
+        if (e != hipSuccess) return hip_status(e, fn);
+        if (ptr == nullptr || !aligned(ptr, 256)) return fail(KVQ_ERR_HIP, fn, "scratch symbol address");
+        g_scratch_ptr[dev] = ptr;
+    }
+    *out = g_scratch_ptr[dev];
+    return KVQ_OK;
+}
+}  // namespace
+
+int32_t kvq_packed_decode_attn_noalloc(const kvq_geom* g, int32_t n_q_heads, const void* q, const uint8_t* cache,
+                                       const int64_t* seq_byte_off, const int32_t* seq_len, int32_t n_seq,
+                                       int64_t max_len, const uint8_t* k_bits, const float* k_sigma,
+                                       const float* v_sigma, float softmax_scale, float* out, void* stream) {
+    const char* fn = "kvq_packed_decode_attn_noalloc";
+    DecodePlan plan;
+    int32_t st = check_decode(g, n_q_heads, q, cache, seq_byte_off, seq_len, n_seq, max_len, k_bits, k_sigma, v_sigma,
+                              nullptr, (size_t)KVQ_NOALLOC_SCRATCH_BYTES, KVQ_DECODE_AUTO, 0, &plan, fn, true);
+    if (st == KVQ_ERR_WORKSPACE)
+        return fail(st, fn, "the plan's partials exceed KVQ_NOALLOC_SCRATCH_BYTES; use kvq_packed_decode_attn");
+    if (st || n_seq == 0) return st;
+    if (!out) return fail(KVQ_ERR_ARG, fn, "null pointer");
+    if (!aligned(out, 16)) return fail(KVQ_ERR_ALIGN, fn, "alignment");
+    void* ws = nullptr;
+    st = scratch_address(&ws, fn);
+    if (st) return st;
+    hipError_t e = launch_decode_partials(*g, plan, n_q_heads, (const uint16_t*)q, (uint8_t*)cache, seq_byte_off,
+                                          seq_len, n_seq, max_len, k_bits, k_sigma, v_sigma, softmax_scale,
+                                          (float*)ws, (hipStream_t)stream);
+    if (e != hipSuccess) return hip_status(e, fn);
+    return hip_status(launch_merge(n_seq * n_q_heads, plan.n_split, (const float*)ws, out, (hipStream_t)stream), fn);
 }
 
 namespace {

@@ -71,6 +71,8 @@ def lib() -> C.CDLL:
     L.kvq_packed_decode_attn.restype = I32
     L.kvq_packed_decode_attn_ex.argtypes = [G, I32, P, P, P, P, I32, I64, P, P, P, F32, P, P, SZ, I32, I32, P]
     L.kvq_packed_decode_attn_ex.restype = I32
+    L.kvq_packed_decode_attn_noalloc.argtypes = [G, I32, P, P, P, P, I32, I64, P, P, P, F32, P, P]
+    L.kvq_packed_decode_attn_noalloc.restype = I32
     L.kvq_decode_partials.argtypes = [G, I32, P, P, P, P, I32, I64, P, P, P, F32, P, SZ, I32, I32, P]
     L.kvq_decode_partials.restype = I32
     L.kvq_merge_partials.argtypes = [I32, I32, I32, P, P, P]
@@ -108,6 +110,7 @@ def lib() -> C.CDLL:
 EXPORTS = ["kvq_version", "kvq_status_string", "kvq_tile_bytes", "kvq_cache_bytes", "kvq_get_codebook",
            "kvq_block_energy", "kvq_allocate_bits", "kvq_quantize_pack", "kvq_decode_workspace_bytes",
            "kvq_decode_workspace_bytes_ex", "kvq_packed_decode_attn", "kvq_packed_decode_attn_ex",
+           "kvq_packed_decode_attn_noalloc",
            "kvq_decode_partials", "kvq_merge_partials", "kvq_decode_n_split", "kvq_decode_plan",
            "kvq_decode_step_partials", "kvq_decode_step", "kvq_window_decode_attn", "kvq_window_decode_step",
            "kvq_window_workspace_bytes", "kvq_prefill_plan", "kvq_prefill_workspace_bytes",
@@ -229,6 +232,25 @@ def packed_decode_attn(g: Geom, q: torch.Tensor, cache: torch.Tensor, seq_byte_o
         C.byref(g), n_q, _ptr(q), _ptr(cache), _ptr(seq_byte_off), _ptr(seq_len), n_seq, max_len, _ptr(k_bits),
         _ptr(k_sigma), _ptr(v_sigma), float(softmax_scale), _ptr(out), _ptr(workspace),
         workspace.numel() * workspace.element_size(), kernel, tiles_per_split, _stream(stream)))
+
+
+NOALLOC_SCRATCH_BYTES = 8 << 20  # KVQ_NOALLOC_SCRATCH_BYTES
+
+
+def packed_decode_attn_noalloc(g: Geom, q: torch.Tensor, cache: torch.Tensor, seq_byte_off: torch.Tensor,
+                               seq_len: torch.Tensor, max_len: int, k_bits: torch.Tensor, k_sigma: torch.Tensor,
+                               v_sigma: torch.Tensor, out: torch.Tensor, softmax_scale: float | None = None,
+                               stream=None):
+    """As packed_decode_attn (automatic plan) with the partials in the library's own
+    device array instead of a workspace: nothing is allocated."""
+    assert q.dtype == torch.float16 and q.is_contiguous() and out.dtype == torch.float32 and out.is_contiguous()
+    assert seq_len.dtype == torch.int32 and seq_byte_off.dtype == torch.int64
+    n_seq, n_q = q.shape[0], q.shape[1]
+    if softmax_scale is None:
+        softmax_scale = g.head_dim ** -0.5
+    _check("kvq_packed_decode_attn_noalloc", lib().kvq_packed_decode_attn_noalloc(
+        C.byref(g), n_q, _ptr(q), _ptr(cache), _ptr(seq_byte_off), _ptr(seq_len), n_seq, max_len, _ptr(k_bits),
+        _ptr(k_sigma), _ptr(v_sigma), float(softmax_scale), _ptr(out), _stream(stream)))
 
 
 def decode_n_split(g: Geom, n_q_heads: int, n_seq: int, max_len: int, kernel: int = DECODE_AUTO,

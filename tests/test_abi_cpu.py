@@ -108,6 +108,17 @@ def test_host_validation_rejects_before_gpu():
     assert L.kvq_decode_step(*s_args(FAKE, 255)) == -4
     assert L.kvq_decode_step(*s_args(FAKE, -2)) == -1
     assert L.kvq_decode_step(*s_args(FAKE, 256, ws=16)) == -6
+    # allocation-free decode: the decode checks, and a plan whose partials exceed the
+    # library's fixed array is refused (KVQ_ERR_WORKSPACE) before any HIP call
+    n_args = lambda nq, max_len, n_seq=1, q=FAKE, out=FAKE: (C.byref(good), nq, q, FAKE, FAKE, FAKE, n_seq, max_len,
+                                                             FAKE, FAKE, FAKE, 0.1, out, None)
+    assert L.kvq_packed_decode_attn_noalloc(*n_args(3, 512)) == -2
+    assert L.kvq_packed_decode_attn_noalloc(*n_args(16, 2048)) == -5
+    assert L.kvq_packed_decode_attn_noalloc(*n_args(16, 512, q=FAKE + 8)) == -4
+    assert L.kvq_packed_decode_attn_noalloc(*n_args(16, 512, out=None)) == -1
+    assert kvq.decode_workspace_bytes(good, 16, 60000, 512) > kvq.NOALLOC_SCRATCH_BYTES
+    assert L.kvq_packed_decode_attn_noalloc(*n_args(16, 512, n_seq=60000)) == -6
+    assert L.kvq_packed_decode_attn_noalloc(*n_args(16, 512, n_seq=0)) == 0  # nothing to do
     # fp16 window: window range, ring and new-row alignment, workspace, before any HIP call
     w_args = lambda win, wk, kn, ss, ws=1 << 30: (C.byref(good), win, 16, FAKE, kn, FAKE, ss, 128, wk, FAKE, FAKE, FAKE,
                                                   FAKE, 1, 512, FAKE, FAKE, FAKE, 0.1, FAKE, FAKE, ws, 0, 0, None)
