@@ -209,9 +209,12 @@ int32_t kvq_packed_decode_attn_noalloc(const kvq_geom *g, int32_t n_q_heads, con
  *
  * kvq_decode_partials writes, for every (sequence s, query head h, chunk k < n_split),
  * 130 floats at partials[((s*n_q_heads + h)*n_split + k)*130]:
- *   [0] m = max over the chunk's tokens of softmax_scale * q.khat * log2(e)  (-inf if empty)
+ *   [0] m = a reference for the chunk's logits z_t = softmax_scale * q.khat_t * log2(e):
+ *           max_t z_t - 8 <= m <= max_t z_t + e (a running maximum that moves lazily,
+ *           plus an integer e >= 0 taken from the value norms); -inf if the chunk is empty
  *   [1] l = sum_t 2^(z_t - m)
  *   [2..129] o_c = sum_t 2^(z_t - m) vhat_{t,c}          (unnormalised)
+ * Any reference gives the same merged result: the merge weighs chunk k by 2^(m_k - M).
  * n_split is kvq_decode_n_split(...) for the same arguments; partials_bytes must be
  * at least kvq_decode_workspace_bytes_ex(...). */
 int32_t kvq_decode_partials(const kvq_geom *g, int32_t n_q_heads, const void *q, const uint8_t *cache,
@@ -301,10 +304,10 @@ int32_t kvq_window_decode_step(const kvq_geom *g, int32_t window, int32_t n_q_he
  * format, in the workspace) are merged by kvq_merge_partials' kernel on the same
  * stream.  workspace: kvq_prefill_workspace_bytes(...) bytes (may be NULL when that is 0).
  * Served: head_dim 128 (every budget and value width, the K16 / V16 passthroughs
- * included) and n_q_heads / n_kv_heads <= 128; otherwise KVQ_ERR_SHAPE.  The
- * binary16 MFMA operands bound |softmax weight * s^V_t| by 2^8 * ||v_t||, so value
- * norms must stay below 255 (as in the matrix-core decode kernel; no bound at V16,
- * whose weights enter without a token scale).
+ * included) and n_q_heads / n_kv_heads <= 128; otherwise KVQ_ERR_SHAPE.  Any finite
+ * binary16 keys and values are served: the weights entering the binary16 matrix
+ * operands are scaled by a power of two chosen from the value norms seen, so no value
+ * norm overflows them (the same holds for every decode call).
  * Nothing but out and the workspace is written. */
 int32_t kvq_prefill_plan(const kvq_geom *g, int32_t n_q_heads, int32_t n_seq, int32_t max_q, int64_t max_len,
                          int32_t n_split, int32_t *n_split_out, int64_t *workspace_out);

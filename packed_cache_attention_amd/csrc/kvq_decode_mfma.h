@@ -28,7 +28,13 @@
 //
 // The running max is a lazy reference: it only moves (and the accumulators are
 // only rescaled) when a head's tile max exceeds it by more than 8 (log2 units),
-// so p <= 2^8.  Each wave loads tile n+1 while it computes tile n.
+// so p <= 2^8.  The binary16 PV operand p.s^V must stay finite for any value norm
+// s^V a binary16 row can have (up to 65504 sqrt(128)), so the reference also carries
+// a wave-uniform power of two: weights are taken against R = m + e with the integer
+// e >= 0 the least that keeps every s^V seen so far at most 2^(7+e); p.s^V.2^-e then
+// stays below 2^15, and o and l, both relative to R, are rescaled exactly as when m
+// moves.  With value norms below 2^7 e stays 0.  Each wave loads tile n+1 while it
+// computes tile n.
 #pragma once
 #include <math.h>
 
@@ -43,6 +49,7 @@ typedef float floatx16 __attribute__((ext_vector_type(16)));
 constexpr int kMaxUnits = 24;  // 128 coordinates in 8-wide units, plus one partial unit per width class
 constexpr int kWaves = 4;
 constexpr float kRescaleSlack = 8.f;
+constexpr int kVNormExp = 7;  // value norms are kept at most 2^kVNormExp after the power-of-two shift
 
 // level tables: pairs (widths 1..5): entry a | b << w -> half2(level_w[a], level_w[b]);
 // singles (widths 6..8)
@@ -91,7 +98,7 @@ struct MfmaSmem {
                                                           // b128 load fall in distinct LDS banks
     float vsig[kHeadDim];
     alignas(16) float alpha[kWaves][8];
-    alignas(16) float wm[8][kWaves];  // per head: each wave's reference max (log2 units)
+    alignas(16) float wm[8][kWaves];  // per head: each wave's reference R (log2 units)
     alignas(16) float wl[8][kWaves];  // ... and its sum of weights
     uint32_t arec[16];                // the appended token's K record, assembled
 };
@@ -503,6 +510,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
 #pragma unroll
     for (int ct = 0; ct < 8; ++ct) o[ct] = floatx4{0.f, 0.f, 0.f, 0.f};
     float mref = -INFINITY, lrun = 0.f;
+    float vexp = 0.f, vlim = (float)(1 << kVNormExp);  // the reference's power of two e, and 2^(7+e)
 
     // ------------------------------------------------------------------ tiles
     int kb = 0;
@@ -590,15 +598,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
             for (int i = 0; i < 16; ++i)
                 if (16 * grp + i >= nvalid) z[i] = -INFINITY;
         }
-        // ---- softmax weights against the lazy reference max
+        // ---- softmax weights against the lazy reference R = mref + vexp
         float tm = z[0];
 #pragma unroll
         for (int i = 1; i < 16; ++i) tm = fmaxf(tm, z[i]);
         tm = xor32_max(xor16_max(tm));
-        if (__ballot(tm > mref + kRescaleSlack)) {
+        float sv[16];
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            const float4 b = *(const float4*)(scl + kTile + 16 * grp + 4 * i);
+            sv[4 * i] = b.x; sv[4 * i + 1] = b.y; sv[4 * i + 2] = b.z; sv[4 * i + 3] = b.w;
+        }
+        float smax = sv[0];
+#pragma unroll
+        for (int i = 1; i < 16; ++i) smax = fmaxf(smax, sv[i]);
+        if (__ballot(tm > mref + kRescaleSlack || smax > vlim)) {
+            // the tile's largest value norm (all four slot groups) sets the power of two
+            const float smx = xor32_max(xor16_max(smax));
+            const float vnew = fmaxf(vexp, (float)(__builtin_amdgcn_frexp_expf(smx) - kVNormExp));
             const float mnew = fmaxf(mref, tm);
-            const float alpha = __builtin_amdgcn_exp2f(mref - mnew);
+            const float alpha = __builtin_amdgcn_exp2f((mref + vexp) - (mnew + vnew));
             mref = mnew;
+            vexp = vnew;
+            vlim = __builtin_amdgcn_ldexpf(1.f, kVNormExp + (int)vnew);
             lrun *= alpha;
             if (lane < 8) sm.alpha[wave][lane] = alpha;
             __builtin_amdgcn_fence(__ATOMIC_SEQ_CST, "wavefront");
@@ -611,17 +633,12 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
             }
             __builtin_amdgcn_wave_barrier();
         }
-        float sv[16];
-#pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float4 b = *(const float4*)(scl + kTile + 16 * grp + 4 * i);
-            sv[4 * i] = b.x; sv[4 * i + 1] = b.y; sv[4 * i + 2] = b.z; sv[4 * i + 3] = b.w;
-        }
+        const float rref = mref + vexp;
         float psum = 0.f;
         H8 pa[2];
 #pragma unroll
         for (int i = 0; i < 16; ++i) {
-            const float p = __builtin_amdgcn_exp2f(z[i] - mref);
+            const float p = __builtin_amdgcn_exp2f(z[i] - rref);
             psum += p;
             const float pv = p * sv[i];
             const _Float16 ph = (_Float16)pv;
@@ -682,7 +699,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         for (int j = 0; j < 4; ++j) o[ct][j] = xor32_sum(o[ct][j]);
     WaveOut& wo = *(WaveOut*)bufs;
     __syncthreads();  // every wave is done with its tile buffers
-    if (lane < 8) { sm.wm[lane][wave] = mref; sm.wl[lane][wave] = lsum; }
+    if (lane < 8) { sm.wm[lane][wave] = mref + vexp; sm.wl[lane][wave] = lsum; }
     if (lane < 32) {
         // lane l holds rows 4*(l/16) .. +3 (heads) of coordinates 16*ct + l%16
 #pragma unroll

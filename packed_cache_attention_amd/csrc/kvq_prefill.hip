@@ -23,7 +23,10 @@
 // local max plus one permlane32 swap, and the accumulator itself, converted to
 // binary16, is the B operand of PV (keys permuted to the accumulator's row order,
 // the V operand read in the same order).  The running max is lazy (moves when a
-// row's tile max exceeds it by more than 8 in log2 units).  Tiles stream HBM -> LDS
+// row's tile max exceeds it by more than 8 in log2 units), and the reference carries
+// the decode kernel's power of two e (R = m + e, every s^V seen so far at most
+// 2^(7+e)), so the binary16 operand p.s^V.2^-e stays below 2^15 for any binary16
+// value rows (e = 0 for value norms below 2^7).  Tiles stream HBM -> LDS
 // with global_load_lds_dwordx4, double-buffered.  Long key ranges split over
 // workgroups into the decode path's partial format (merged by the same merge).
 #include "kvq_decode_mfma.h"
@@ -208,6 +211,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
 #pragma unroll
         for (int i = 0; i < 16; ++i) o[cb][i] = 0.f;
     float mref = -INFINITY, lrun = 0.f;
+    float vexp = 0.f, vlim = (float)(1 << kVNormExp);  // the reference's power of two e, and 2^(7+e)
 
     for (int64_t tau = t0; tau < t1; ++tau) {
         const int buf = (int)((tau - t0) & 1);
@@ -314,29 +318,40 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
                 for (int e = 0; e < 4; ++e) tm = fmaxf(tm, acc[4 * jj + e]);
             }
             tm = xor32_max(tm);
-            if (__ballot(tm > mref + kPfSlack)) {
+            float svv[4][4];  // this lane's keys' value norms (1 for the V16 passthrough)
+            float smax = 0.f;
+#pragma unroll
+            for (int jj = 0; jj < 4; ++jj) {
+                const float4 sv = v16 ? float4{1.f, 1.f, 1.f, 1.f} : *(const float4*)(svl + 32 * kb + 8 * jj + 4 * h);
+                svv[jj][0] = sv.x; svv[jj][1] = sv.y; svv[jj][2] = sv.z; svv[jj][3] = sv.w;
+                smax = fmaxf(smax, fmaxf(fmaxf(sv.x, sv.y), fmaxf(sv.z, sv.w)));
+            }
+            if (__ballot(tm > mref + kPfSlack || smax > vlim)) {
+                // the half tile's largest value norm (both lanes' keys) sets the power of two
+                const float vnew = fmaxf(vexp, (float)(__builtin_amdgcn_frexp_expf(xor32_max(smax)) - kVNormExp));
                 const float mnew = fmaxf(mref, tm);
-                const float alpha = mref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f(mref - mnew);
+                const float alpha =
+                    mref == -INFINITY ? 0.f : __builtin_amdgcn_exp2f((mref + vexp) - (mnew + vnew));
                 mref = mnew;
+                vexp = vnew;
+                vlim = __builtin_amdgcn_ldexpf(1.f, kVNormExp + (int)vnew);
                 lrun *= alpha;
 #pragma unroll
                 for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
                     for (int i = 0; i < 16; ++i) o[cb][i] *= alpha;
             }
-            const float mb = mref == -INFINITY ? 0.f : mref;  // rows that have seen nothing keep p = 0
+            const float mb = mref == -INFINITY ? 0.f : mref + vexp;  // rows that have seen nothing keep p = 0
             float psum = 0.f;
-            uint32_t ph[8], pl[8];  // P' (p s^V) as binary16 hi + lo pairs in the accumulator's key order
+            uint32_t ph[8], pl[8];  // P' (p s^V 2^-e) as binary16 hi + lo pairs in the accumulator's key order
 #pragma unroll
             for (int jj = 0; jj < 4; ++jj) {
-                const float4 sv = v16 ? float4{1.f, 1.f, 1.f, 1.f} : *(const float4*)(svl + 32 * kb + 8 * jj + 4 * h);
-                const float svv[4] = {sv.x, sv.y, sv.z, sv.w};
                 float pv[4];
 #pragma unroll
                 for (int e = 0; e < 4; ++e) {
                     const float p = __builtin_amdgcn_exp2f(acc[4 * jj + e] - mb);
                     psum += p;
-                    pv[e] = p * svv[e];
+                    pv[e] = p * svv[jj][e];
                 }
 #pragma unroll
                 for (int e = 0; e < 4; e += 2) {
@@ -386,7 +401,7 @@ __global__ __launch_bounds__(kPfThreads) __attribute__((amdgpu_waves_per_eu(2)))
             }
     } else {
         float* part = ws + (orow * n_split + split) * (kHeadDim + 2);
-        if (h == 0) { part[0] = mref; part[1] = lsum; }
+        if (h == 0) { part[0] = mref == -INFINITY ? mref : mref + vexp; part[1] = lsum; }
 #pragma unroll
         for (int cb = 0; cb < 4; ++cb)
 #pragma unroll
