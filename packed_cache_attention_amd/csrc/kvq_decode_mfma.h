@@ -201,18 +201,22 @@ __device__ __forceinline__ void qk_unit(const MfmaSmem& sm, const uint32_t (&rec
 // lane's q split row and its stride per unit (0 off the diagonal).
 template <int W, int RD>
 __device__ __forceinline__ void qk_class(const MfmaSmem& sm, const uint32_t (&rec)[RD + 2], int start, int units,
-                                         int ubase, const uint16_t* qb, int qs, floatx16& acc0, floatx16& acc1) {
+                                         int ubase, const uint16_t* qb, uint32_t qmask, floatx16& acc0,
+                                         floatx16& acc1) {
+    // unit u's q split sits 8 positions (16 bytes) after unit u - 1's on the diagonal
+    const char* qc = (const char*)qb;
     int j = 0;
     for (; j + 1 < units; j += 2) {
         H8 a0, b0, a1, b1;
-        qk_unit<W, RD>(sm, rec, start + j * 8 * W, qb + qs * (ubase + j), a0, b0);
-        qk_unit<W, RD>(sm, rec, start + (j + 1) * 8 * W, qb + qs * (ubase + j + 1), a1, b1);
+        qk_unit<W, RD>(sm, rec, start + j * 8 * W, (const uint16_t*)(qc + ((16u * (ubase + j)) & qmask)), a0, b0);
+        qk_unit<W, RD>(sm, rec, start + (j + 1) * 8 * W, (const uint16_t*)(qc + ((16u * (ubase + j + 1)) & qmask)),
+                       a1, b1);
         acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0.h, b0.h, acc0, 0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1.h, b1.h, acc1, 0, 0, 0);
     }
     if (j < units) {
         H8 a0, b0;
-        qk_unit<W, RD>(sm, rec, start + j * 8 * W, qb + qs * (ubase + j), a0, b0);
+        qk_unit<W, RD>(sm, rec, start + j * 8 * W, (const uint16_t*)(qc + ((16u * (ubase + j)) & qmask)), a0, b0);
         acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0.h, b0.h, acc0, 0, 0, 0);
     }
 }
@@ -256,14 +260,25 @@ typedef __attribute__((address_space(3))) uint8_t lds_u8;
 // (global_load_lds_dwordx4; M0 holds the wave-uniform LDS base).  Written as asm so
 // that the compiler does not order every later LDS read behind it: the caller
 // waits for it explicitly (vmcnt) before reading the buffer, and issues it only
-// after its own reads of that buffer have returned (lgkmcnt).
+// after its own reads of that buffer have returned (lgkmcnt).  The decode kernel
+// reads each tile once and marks its loads non-temporal (STREAM), so the packed
+// stream does not push a launch's small shared inputs (level tables, queries,
+// scales) out of L2 between launches; the prefill kernel re-reads tiles from many
+// workgroups and keeps them cacheable.
 #pragma clang diagnostic push
 #pragma clang diagnostic ignored "-Winline-asm"  // M0 is reserved, and this asm does overwrite it
+template <bool STREAM = false>
 __device__ __forceinline__ void dma16(const void* gptr, uint32_t lds_base) {
-    asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
-                 :
-                 : "v"(gptr), "s"(lds_base)
-                 : "memory", "m0");
+    if (STREAM)
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off nt"
+                     :
+                     : "v"(gptr), "s"(lds_base)
+                     : "memory", "m0");
+    else
+        asm volatile("s_mov_b32 m0, %1\n\ts_nop 0\n\tglobal_load_lds_dwordx4 %0, off"
+                     :
+                     : "v"(gptr), "s"(lds_base)
+                     : "memory", "m0");
 }
 #pragma clang diagnostic pop
 
@@ -365,7 +380,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     const int qslot = 16 * (2 * ((m >> 2) & 1) + (lane >> 5)) + 4 * (m >> 3) + (m & 3);  // QK token
     const int grp = lane >> 4;       // PV k group: slots 16*grp .. 16*grp+15
     const int row = lane & 15;       // PV row = (hi|lo) * 8 + head
-    const bool lo_row = row >= 8;
+    const float mlo = row >= 8 ? -1.f : 0.f;  // lo rows subtract the hi part of each weight
 
     const uint8_t* head_base = cache + seq_off + (int64_t)kvh * (capacity / kTile) * TB;
     uint8_t* wbuf = bufs + wave * WB;
@@ -381,14 +396,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     auto dma_k = [&](int64_t tau, int kb) {
         const uint8_t* tile = head_base + tau * TB;
 #pragma unroll
-        for (int k = 0; k < KI; ++k) dma16(tile + lane * SK + 16 * k, wbuf_lds + kb * KB + 1024 * k);
+        for (int k = 0; k < KI; ++k) dma16<true>(tile + lane * SK + 16 * k, wbuf_lds + kb * KB + 1024 * k);
     };
     auto dma_v = [&](int64_t tau) {
         const uint8_t* vsec = head_base + tau * TB + KB;
 #pragma unroll
         for (int j = 0; j < VI; ++j) {
             const int ch = 64 * j + lane;
-            if (64 * j + 63 < VB / 16 || ch < VB / 16) dma16(vsec + 16 * ch, wbuf_lds + 2 * KB + 1024 * j);
+            if (64 * j + 63 < VB / 16 || ch < VB / 16) dma16<true>(vsec + 16 * ch, wbuf_lds + 2 * KB + 1024 * j);
         }
     };
     constexpr bool kStageInK1 = KB >= 510 * 4;  // see the staging area below
@@ -460,7 +475,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     // B operand rows: the lane's column (hi|lo, head) on the diagonal, else a row that
     // stays zero (the last unit of hi row 0: at most 22 units are ever filled)
     const uint16_t* qb = bdiag ? &sm.qsplit[(col >> 3) & 1][col & 7][0] : &sm.qsplit[0][0][8 * (kMaxUnits - 1)];
-    const int qs = bdiag ? 8 : 0;
+    const uint32_t qmask = bdiag ? ~0u : 0u;
 
     // ---- the step's append (one wave): quantize and pack the new token for slot
     // len-1 exactly as the quantize path does.  The bytes go into the LDS copy of
@@ -549,14 +564,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         kb ^= 1;
         // ---- QK: this lane's token, 8 fields of one width class per instruction
         floatx16 acc0 = {}, acc1 = {};
-        qk_class<8, RD>(sm, rec, cstart[8], cunits[8], cubase[8], qb, qs, acc0, acc1);
-        qk_class<7, RD>(sm, rec, cstart[7], cunits[7], cubase[7], qb, qs, acc0, acc1);
-        qk_class<6, RD>(sm, rec, cstart[6], cunits[6], cubase[6], qb, qs, acc0, acc1);
-        qk_class<5, RD>(sm, rec, cstart[5], cunits[5], cubase[5], qb, qs, acc0, acc1);
-        qk_class<4, RD>(sm, rec, cstart[4], cunits[4], cubase[4], qb, qs, acc0, acc1);
-        qk_class<3, RD>(sm, rec, cstart[3], cunits[3], cubase[3], qb, qs, acc0, acc1);
-        qk_class<2, RD>(sm, rec, cstart[2], cunits[2], cubase[2], qb, qs, acc0, acc1);
-        qk_class<1, RD>(sm, rec, cstart[1], cunits[1], cubase[1], qb, qs, acc0, acc1);
+        qk_class<8, RD>(sm, rec, cstart[8], cunits[8], cubase[8], qb, qmask, acc0, acc1);
+        qk_class<7, RD>(sm, rec, cstart[7], cunits[7], cubase[7], qb, qmask, acc0, acc1);
+        qk_class<6, RD>(sm, rec, cstart[6], cunits[6], cubase[6], qb, qmask, acc0, acc1);
+        qk_class<5, RD>(sm, rec, cstart[5], cunits[5], cubase[5], qb, qmask, acc0, acc1);
+        qk_class<4, RD>(sm, rec, cstart[4], cunits[4], cubase[4], qb, qmask, acc0, acc1);
+        qk_class<3, RD>(sm, rec, cstart[3], cunits[3], cubase[3], qb, qmask, acc0, acc1);
+        qk_class<2, RD>(sm, rec, cstart[2], cunits[2], cubase[2], qb, qmask, acc0, acc1);
+        qk_class<1, RD>(sm, rec, cstart[1], cunits[1], cubase[1], qb, qmask, acc0, acc1);
         floatx16 acc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[i] = acc0[i] + acc1[i];
@@ -636,14 +651,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         const float rref = mref + vexp;
         float psum = 0.f;
         H8 pa[2];
+        // hi rows take RZ16(p s^V) and lo rows the binary16 residual p s^V - hi (exact in
+        // binary32), so the two rows together carry about 21 bits of each weight
 #pragma unroll
-        for (int i = 0; i < 16; ++i) {
-            const float p = __builtin_amdgcn_exp2f(z[i] - rref);
-            psum += p;
-            const float pv = p * sv[i];
-            const _Float16 ph = (_Float16)pv;
-            const _Float16 pl = (_Float16)(pv - (float)ph);
-            pa[i >> 3].s[i & 7] = __builtin_bit_cast(uint16_t, lo_row ? pl : ph);
+        for (int i = 0; i < 16; i += 2) {
+            const float p0 = __builtin_amdgcn_exp2f(z[i] - rref), p1 = __builtin_amdgcn_exp2f(z[i + 1] - rref);
+            psum += p0 + p1;
+            const float pv0 = p0 * sv[i], pv1 = p1 * sv[i + 1];
+            const auto hi = __builtin_amdgcn_cvt_pkrtz(pv0, pv1);
+            const float r0 = __builtin_fmaf((float)hi[0], mlo, pv0), r1 = __builtin_fmaf((float)hi[1], mlo, pv1);
+            pa[i >> 3].u[(i & 7) >> 1] = __builtin_bit_cast(uint32_t, __builtin_amdgcn_cvt_pkrtz(r0, r1));
         }
         lrun += psum;
         // ---- PV: B operand = 16 consecutive slots of coordinate 16*ct + lane%16
