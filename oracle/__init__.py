@@ -74,6 +74,11 @@ def lib() -> C.CDLL:
     L.or_prefill_attention.argtypes = [P, I64, I32, I32, I32, I32, I32, I32, P, P, P, P, P, P, I64, I64, F64, P]
     L.or_attend_partial.argtypes = [P, P, P, I64, I32, F64, P, P, P]
     L.or_merge_partials.argtypes = [P, I64, I32, I32, P]
+    L.or_hadamard_units.argtypes = [P, I32, P, P]
+    L.or_hadamard_f32.argtypes = [P, I32, P, P]
+    L.or_rot_encode.argtypes = [P, I64, I64, I32, I32, P, P, P, P, P]
+    L.or_rot_query.argtypes = [P, I32, P, C.c_float, P]
+    L.or_rot_back.argtypes = [P, I32, P, P]
     return L
 
 
@@ -374,4 +379,115 @@ def prefill_attention(geom: Geometry, region: np.ndarray, q16: np.ndarray, q_sta
                                _p(np.ascontiguousarray(ksig, np.float32)),
                                _p(np.ascontiguousarray(vsig, np.float32)), _p(T["lev"]), _p(T["lev_off"]),
                                _p(qq), int(q_start), n_tok, float(scale), _p(out))
+    return out
+
+
+# --------------------------------------------------------------------------
+# TQ-MSE proper: randomized Walsh-Hadamard rotation (next-3 variant)
+# --------------------------------------------------------------------------
+
+def rot_sigma() -> np.float32:
+    """The rotated codebook's coordinate scale 1/sqrt(128) = sqrt(2)/16 rounded to
+    binary32 (sqrt(2) correctly rounded in fp64, then to binary32, then an exact /16)."""
+    return np.float32(np.float32(np.sqrt(2.0)) / np.float32(16.0))
+
+
+def hadamard_units(x16: np.ndarray, signs: np.ndarray) -> np.ndarray:
+    """Exact S_i = sum_j H[i][j] sg_j x_j of one binary16 row, as int64 counts of 2^-24."""
+    x = np.ascontiguousarray(x16).view(np.uint16)
+    out = np.zeros(x.shape[-1], np.int64)
+    lib().or_hadamard_units(_p(x), x.shape[-1], _p(np.ascontiguousarray(signs, np.uint8)), _p(out))
+    return out
+
+
+def hadamard_f32(x16: np.ndarray, signs: np.ndarray) -> np.ndarray:
+    """RN32 of the exact rotated sums of one binary16 row."""
+    x = np.ascontiguousarray(x16).view(np.uint16)
+    out = np.zeros(x.shape[-1], np.float32)
+    lib().or_hadamard_f32(_p(x), x.shape[-1], _p(np.ascontiguousarray(signs, np.uint8)), _p(out))
+    return out
+
+
+def rot_encode(x16: np.ndarray, w: int, signs: np.ndarray):
+    """Codes [n, d] and per-token scales [n] of binary16 rows [n, d] under the rotation,
+    every coordinate at width w (1..8); see or_rot_encode."""
+    x = np.ascontiguousarray(x16).view(np.uint16)
+    n, d = x.shape
+    T = tables()
+    codes = np.zeros((n, d), np.uint16)
+    scale = np.zeros(n, np.float32)
+    lib().or_rot_encode(_p(x), n, d, d, w, _p(np.ascontiguousarray(signs, np.uint8)), _p(T["thr"]),
+                        _p(T["thr_off"]), _p(codes), _p(scale))
+    return codes, scale
+
+
+def rot_query(q16: np.ndarray, signs: np.ndarray) -> np.ndarray:
+    """A binary16 query rotated once: RN16(RN32(RN32(S_i) * rot_sigma()))."""
+    q = np.ascontiguousarray(q16).view(np.uint16)
+    out = np.zeros(q.shape[-1], np.uint16)
+    lib().or_rot_query(_p(q), q.shape[-1], _p(np.ascontiguousarray(signs, np.uint8)), float(rot_sigma()), _p(out))
+    return out
+
+
+def rot_back(y: np.ndarray, signs: np.ndarray) -> np.ndarray:
+    """R^T y = diag(sg) H y / sqrt(d) in fp64 (an output rotated back)."""
+    yy = np.ascontiguousarray(y, np.float64)
+    out = np.zeros(yy.shape[-1], np.float64)
+    lib().or_rot_back(_p(yy), yy.shape[-1], _p(np.ascontiguousarray(signs, np.uint8)), _p(out))
+    return out
+
+
+def quantize_pack_rot(geom: "Geometry", region: np.ndarray, k16: np.ndarray, v16: np.ndarray, first_slot: int,
+                      k_signs: np.ndarray, v_signs: np.ndarray | None, vsig: np.ndarray | None):
+    """The rotated variant of quantize_pack: keys rotated and coded at the uniform width
+    k_budget / (d/2) (no allocation: rotation spreads every block's energy over all
+    coordinates); values rotated the same way when v_signs is given, else coded as in
+    quantize_pack with the per-block scales vsig.  Packed in layout v1 with uniform
+    key widths.  Returns per-head (kcodes, vcodes, kscale, vscale)."""
+    d, H = geom.d, geom.H
+    nb = d // 2
+    assert geom.kb % nb == 0 and 1 <= geom.kb // nb <= 8 and geom.vb <= 8
+    wk = geom.kb // nb
+    kbits = np.full((H, nb), wk, np.uint8)
+    vw = np.full(d, geom.vb, np.int32)
+    out = []
+    for h in range(H):
+        kc, ks = rot_encode(np.ascontiguousarray(k16[:, h, :]), wk, k_signs[h])
+        if v_signs is not None:
+            vc, vs = rot_encode(np.ascontiguousarray(v16[:, h, :]), geom.vb, v_signs[h])
+        else:
+            vc, vs = encode(np.ascontiguousarray(v16[:, h, :]), vw, per_coord(vsig[h], d, geom.pairing))
+        view = region[h * geom.n_tiles * geom.tile:(h + 1) * geom.n_tiles * geom.tile]
+        pack(view, d, geom.pairing, geom.kb, geom.vb, kbits[h], first_slot, kc, vc, ks, vs)
+        out.append((kc, vc, ks, vs))
+    return out
+
+
+def decode_attention_rot(geom: "Geometry", region: np.ndarray, q16: np.ndarray, seq_len: int, k_signs: np.ndarray,
+                         v_signs: np.ndarray | None, vsig: np.ndarray | None,
+                         scale: float | None = None) -> np.ndarray:
+    """Exact fp64 attention of the rotated variant for one sequence: each query head is
+    rotated once (rot_query with its KV head's key signs), the keys are dequantized in
+    rotated coordinates (s * rot_sigma() * level), softmax attention as usual, and with
+    rotated values the output is rotated back once (rot_back with the value signs)."""
+    d, H = geom.d, geom.H
+    nb = d // 2
+    wk = geom.kb // nb
+    if scale is None:
+        scale = 1.0 / np.sqrt(d)
+    nq = q16.shape[0]
+    g = nq // H
+    sig_r = np.full(d, rot_sigma(), np.float32)
+    out = np.zeros((nq, d), np.float64)
+    kbits = np.full(nb, wk, np.uint8)
+    for kv in range(H):
+        view = region[kv * geom.n_tiles * geom.tile:(kv + 1) * geom.n_tiles * geom.tile]
+        kc, vc, ks, vs = unpack(view, d, geom.pairing, geom.kb, geom.vb, kbits, 0, seq_len)
+        khat = dequant(kc, np.full(d, wk, np.int32), sig_r, ks)
+        vsig_c = sig_r if v_signs is not None else per_coord(vsig[kv], d, geom.pairing)
+        vhat = dequant(vc, np.full(d, geom.vb, np.int32), vsig_c, vs)
+        for h in range(kv * g, (kv + 1) * g):
+            qr = rot_query(q16[h], k_signs[kv]).view(np.float16).astype(np.float64)
+            o = attend(qr, khat, vhat, scale)
+            out[h] = rot_back(o, v_signs[kv]) if v_signs is not None else o
     return out

@@ -37,12 +37,14 @@ def quantize_blockgtq(k16: np.ndarray, budget: int, mode: int = GREEDY, pairing:
     return dequant(codes, w, s, scale)
 
 
-def quantize_rot(k16: np.ndarray, bits_per_dim: int, seed: int = 0) -> np.ndarray:
-    """TurboQuant-MSE style: norm, random-sign WHT, per-coordinate Lloyd-Max, inverse."""
+def quantize_rot(k16: np.ndarray, bits_per_dim: int, seed: int = 0, signs: np.ndarray | None = None) -> np.ndarray:
+    """TurboQuant-MSE style: norm, random-sign WHT, per-coordinate Lloyd-Max, inverse.
+    signs: the +-1 diagonal (drawn from `seed` when not given)."""
     n, d = k16.shape
     x = k16.astype(np.float64)
-    rng = np.random.default_rng(seed)
-    signs = rng.choice([-1.0, 1.0], size=d)
+    if signs is None:
+        rng = np.random.default_rng(seed)
+        signs = rng.choice([-1.0, 1.0], size=d)
     R = hadamard(d) * signs[None, :]          # y = R x  (orthogonal)
     norm = np.linalg.norm(x, axis=1)
     safe = np.where(norm > 0, norm, 1.0)

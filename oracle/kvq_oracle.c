@@ -778,3 +778,102 @@ void or_merge_partials(const float *part, int64_t n_rows, int n_split, int d, do
         for (int c = 0; c < d; c++) o[c] = (L > 0) ? o[c] / L : 0.0;
     }
 }
+
+/* ------------------------------------------------------------------------- */
+/* Randomized Walsh-Hadamard rotation (TurboQuant-MSE proper)                */
+/* ------------------------------------------------------------------------- */
+/*
+ * TQ-MSE rotates each vector by a random orthogonal matrix before scalar
+ * quantization, so that every rotated coordinate of a unit vector follows (about)
+ * N(0, 1/d) and one Gaussian codebook serves all coordinates.  The rotation read
+ * here is R = H diag(sg) / sqrt(d): H the d x d Sylvester Hadamard matrix
+ * (H[i][j] = (-1)^popcount(i & j)), sg a seeded vector of signs (an input: sg_j =
+ * -1 where signs[j] is 1, else +1).  R is orthogonal, so ||R x|| = ||x||.
+ *
+ * Exact rotated sums: for binary16 x, S_i = sum_j H[i][j] sg_j x_j = sqrt(d) (R x)_i
+ * is a sum of +-multiples of 2^-24 below 2^47 in magnitude, kept exactly as an
+ * integer count of 2^-24 and rounded once to binary32.
+ */
+static int hsign(int i, int j) { return __builtin_popcount((unsigned)(i & j)) & 1 ? -1 : 1; }
+
+/* integer value of a finite binary16 in units of 2^-24 */
+static int64_t h2units(uint16_t h)
+{
+    int e = (h >> 10) & 31, m = h & 1023;
+    int64_t M = (e == 0) ? m : (1024 + m);
+    int64_t v = (e == 0) ? M : (M << (e - 1));
+    return (h >> 15) ? -v : v;
+}
+
+/* exact S_i = sum_j H[i][j] sg_j x_j (units of 2^-24) for a binary16 row x[d] */
+void or_hadamard_units(const uint16_t *x, int d, const uint8_t *signs, int64_t *S)
+{
+    for (int i = 0; i < d; i++) {
+        int64_t acc = 0;
+        for (int j = 0; j < d; j++) {
+            int64_t t = h2units(x[j]);
+            if (signs[j]) t = -t;
+            acc += hsign(i, j) * t;
+        }
+        S[i] = acc;
+    }
+}
+
+/* the rotated sums rounded once to binary32: RN32(S_i * 2^-24) */
+void or_hadamard_f32(const uint16_t *x, int d, const uint8_t *signs, float *S)
+{
+    int64_t u[256];
+    or_hadamard_units(x, d, signs, u);
+    for (int i = 0; i < d; i++) S[i] = ldexpf((float)u[i], -24);  /* int64 -> float is RN; the scaling is exact */
+}
+
+/*
+ * Codes of n binary16 rows under the rotation (all coordinates at width w, 1..8):
+ *   s = or_token_scale(x) (the norm of the unrotated row; R keeps it);
+ *   code_i = #{ j in 1..2^w-1 : S_i >= RN32(s * t_w[j]) }.
+ * In exact arithmetic this compares the normalised rotated coordinate
+ * (R x)_i sqrt(d) / s with the Gaussian thresholds t_w: the codebook N(0, 1/d) at
+ * scale s.  Outputs codes [n][d] and scale [n].
+ */
+void or_rot_encode(const uint16_t *x, int64_t n, int64_t stride_tok, int d, int w, const uint8_t *signs,
+                   const float *thr_tab, const int *thr_off, uint16_t *codes, float *scale)
+{
+    float S[256];
+    for (int64_t t = 0; t < n; t++) {
+        const uint16_t *row = x + t * stride_tok;
+        float s = or_token_scale(row, d);
+        scale[t] = s;
+        or_hadamard_f32(row, d, signs, S);
+        const float *thr = thr_tab + thr_off[w];
+        for (int c = 0; c < d; c++) {
+            int k = 0;
+            for (int j = 1; j < (1 << w); j++) {
+                float b = s * thr[j];
+                if (S[c] >= b) k++;
+            }
+            codes[t * d + c] = (uint16_t)k;
+        }
+    }
+}
+
+/* binary16 query rotated once: RN16(RN32(RN32(S_i) * sigma)), sigma = RN32(1/sqrt(d)) */
+void or_rot_query(const uint16_t *q, int d, const uint8_t *signs, float sigma, uint16_t *out)
+{
+    float S[256];
+    or_hadamard_f32(q, d, signs, S);
+    for (int i = 0; i < d; i++) {
+        float p = S[i] * sigma;
+        out[i] = d2h((double)p);
+    }
+}
+
+/* x = R^T y = diag(sg) H y / sqrt(d), fp64 (the output rotated back) */
+void or_rot_back(const double *y, int d, const uint8_t *signs, double *x)
+{
+    for (int j = 0; j < d; j++) {
+        double acc = 0;
+        for (int i = 0; i < d; i++) acc += hsign(i, j) * y[i];
+        acc /= sqrt((double)d);
+        x[j] = signs[j] ? -acc : acc;
+    }
+}
