@@ -318,6 +318,42 @@ int32_t kvq_packed_prefill_attn(const kvq_geom *g, int32_t n_q_heads, const void
                                 int32_t n_seq, int32_t max_q, int64_t max_len, const uint8_t *k_bits,
                                 const float *k_sigma, const float *v_sigma, float softmax_scale, float *out,
                                 void *workspace, size_t workspace_bytes, int32_t n_split, void *stream);
+/* The TurboQuant-MSE rotation variant (TQ-MSE proper: the uniform baseline Block-GTQ
+ * is measured against in "RoPE-Aware Bit Allocation for KV-Cache Quantization",
+ * abstract; the related-papers page for "Quantization Dominates Rank Reduction for
+ * KV-Cache" names its key path "WHT + MSE").  Each KV head has a seeded sign vector sg
+ * (128 bytes: 1 = -1, 0 = +1, the caller's random draw) and the rotation
+ * R = H diag(sg) / sqrt(128), H the 128 x 128 Sylvester Hadamard matrix.
+ *
+ * kvq_rot_quantize_pack: as kvq_quantize_pack, but every key is rotated and each of its
+ *   128 rotated coordinates coded at the uniform width w = k_budget / 64 (1..8):
+ *   S = H (sg * k) is formed exactly (binary16 values are integer counts of 2^-24) and
+ *   rounded once to binary32, s = the token norm of the unrotated row (R keeps it), and
+ *   code_i = #{ j in 1..2^w-1 : S_i >= RN32(s * thr_w[j]) }, packed in layout v1 with all
+ *   block widths w.  Values: rotated and coded the same way at width v_bits when
+ *   v_signs != NULL, else coded as kvq_quantize_pack does with the block scales v_sigma.
+ *     k_signs, v_signs : device uint8 [n_kv_heads][128];  v_sigma : device float [n_kv_heads][64]
+ *   Requirements: those of kvq_quantize_pack; k_budget a multiple of 64 in 64..512,
+ *   v_bits 1..8; otherwise KVQ_ERR_BUDGET.
+ * Attention over such a cache is kvq_packed_decode_attn on rotated queries with block
+ * widths w everywhere, key scales sigma_rot = RN32(1/sqrt(128)) (bits KVQ_ROT_SIGMA_BITS)
+ * and, for rotated values, value scales sigma_rot, followed by kvq_rot_back:
+ * kvq_rot_queries: q_rot[r] = RN16(RN32(RN32(S_i) * sigma_rot)) with S = H (sg * q[r]) exact,
+ *   sg the key signs of row r's KV head (query head r % n_q_heads over the group size);
+ *   q, q_rot : device binary16 [n_seq][n_q_heads][128] (a rotated query must fit binary16).
+ * kvq_rot_back: out[r] <- diag(sg) H out[r] / sqrt(128) in place (binary32), sg the value
+ *   signs of row r's KV head: the attention output rotated back once per head. */
+#define KVQ_ROT_SIGMA_BITS 0x3DB504F3u
+int32_t kvq_rot_quantize_pack(const kvq_geom *g, const void *k, const void *v, int64_t stride_tok,
+                              int64_t stride_head, int32_t n_seq, const int64_t *first_slot, const int32_t *n_new,
+                              const int64_t *src_row0, int32_t max_new, const uint8_t *k_signs,
+                              const uint8_t *v_signs, const float *v_sigma, uint8_t *cache,
+                              const int64_t *seq_byte_off, void *stream);
+int32_t kvq_rot_queries(const kvq_geom *g, int32_t n_q_heads, int32_t n_seq, const void *q, void *q_rot,
+                        const uint8_t *k_signs, void *stream);
+int32_t kvq_rot_back(const kvq_geom *g, int32_t n_q_heads, int32_t n_seq, float *out, const uint8_t *v_signs,
+                     void *stream);
+
 /* Measurement helper (not a step of the method): a plain streaming read of `bytes`
  * (a multiple of 16; src 16-byte aligned) by n_blocks workgroups of 256 threads, each
  * writing one 32-bit word to sink[block] so the loads stay live (sink: n_blocks words).

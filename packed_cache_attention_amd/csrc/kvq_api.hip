@@ -552,6 +552,76 @@ int32_t kvq_packed_prefill_attn(const kvq_geom* g, int32_t n_q_heads, const void
                       fn);
 }
 
+// ---------------------------------------------------------------- rotation variant
+namespace {
+int32_t check_rot_geom(const kvq_geom* g, const char* fn) {
+    int32_t st = check_geom(g, true, fn);
+    if (st) return st;
+    if (g->k_budget % kMaxBlocks || g->k_budget < kMaxBlocks || g->k_budget > 8 * kMaxBlocks)
+        return fail(KVQ_ERR_BUDGET, fn, "rotated keys need a uniform width 1..8 (k_budget a multiple of 64)");
+    if (g->v_bits > 8) return fail(KVQ_ERR_BUDGET, fn, "v_bits 1..8");
+    return KVQ_OK;
+}
+}  // namespace
+
+int32_t kvq_rot_quantize_pack(const kvq_geom* g, const void* k, const void* v, int64_t stride_tok,
+                              int64_t stride_head, int32_t n_seq, const int64_t* first_slot, const int32_t* n_new,
+                              const int64_t* src_row0, int32_t max_new, const uint8_t* k_signs,
+                              const uint8_t* v_signs, const float* v_sigma, uint8_t* cache,
+                              const int64_t* seq_byte_off, void* stream) {
+    const char* fn = "kvq_rot_quantize_pack";
+    int32_t st = check_rot_geom(g, fn);
+    if (st) return st;
+    if (n_seq < 0 || max_new < 0) return fail(KVQ_ERR_ARG, fn, "negative count");
+    if (n_seq > 65535) return fail(KVQ_ERR_SHAPE, fn, "n_seq");
+    if (max_new > g->capacity_tokens) return fail(KVQ_ERR_CAPACITY, fn, "max_new > capacity");
+    if (stride_tok < 0 || stride_head < 0) return fail(KVQ_ERR_ARG, fn, "negative stride");
+    if (n_seq == 0 || max_new == 0) return KVQ_OK;
+    if (!k || !v || !first_slot || !n_new || !src_row0 || !k_signs || (!v_signs && !v_sigma) || !cache ||
+        !seq_byte_off)
+        return fail(KVQ_ERR_ARG, fn, "null pointer");
+    if (!aligned(k, 4) || !aligned(v, 4) || (stride_tok & 1) || (stride_head & 1) || !aligned(cache, 16) ||
+        !aligned(first_slot, 8) || !aligned(src_row0, 8) || !aligned(seq_byte_off, 8) || !aligned(n_new, 4) ||
+        !aligned(v_sigma, 4))
+        return fail(KVQ_ERR_ALIGN, fn, "alignment");
+    return hip_status(launch_rot_quantize(*g, (const uint16_t*)k, (const uint16_t*)v, stride_tok, stride_head, n_seq,
+                                          first_slot, n_new, src_row0, max_new, k_signs, v_signs, v_sigma, cache,
+                                          seq_byte_off, (hipStream_t)stream),
+                      fn);
+}
+
+int32_t kvq_rot_queries(const kvq_geom* g, int32_t n_q_heads, int32_t n_seq, const void* q, void* q_rot,
+                        const uint8_t* k_signs, void* stream) {
+    const char* fn = "kvq_rot_queries";
+    int32_t st = check_rot_geom(g, fn);
+    if (st) return st;
+    if (n_q_heads < 1 || n_q_heads % g->n_kv_heads) return fail(KVQ_ERR_SHAPE, fn, "n_q_heads");
+    if (n_seq < 0) return fail(KVQ_ERR_ARG, fn, "negative count");
+    if ((int64_t)n_seq * n_q_heads > 2147483647LL) return fail(KVQ_ERR_SHAPE, fn, "n_seq * n_q_heads");
+    if (n_seq == 0) return KVQ_OK;
+    if (!q || !q_rot || !k_signs) return fail(KVQ_ERR_ARG, fn, "null pointer");
+    if (!aligned(q, 4) || !aligned(q_rot, 4)) return fail(KVQ_ERR_ALIGN, fn, "alignment");
+    return hip_status(launch_rot_queries((const uint16_t*)q, (uint16_t*)q_rot, k_signs, n_seq * n_q_heads, n_q_heads,
+                                         n_q_heads / g->n_kv_heads, (hipStream_t)stream),
+                      fn);
+}
+
+int32_t kvq_rot_back(const kvq_geom* g, int32_t n_q_heads, int32_t n_seq, float* out, const uint8_t* v_signs,
+                     void* stream) {
+    const char* fn = "kvq_rot_back";
+    int32_t st = check_rot_geom(g, fn);
+    if (st) return st;
+    if (n_q_heads < 1 || n_q_heads % g->n_kv_heads) return fail(KVQ_ERR_SHAPE, fn, "n_q_heads");
+    if (n_seq < 0) return fail(KVQ_ERR_ARG, fn, "negative count");
+    if ((int64_t)n_seq * n_q_heads > 2147483647LL) return fail(KVQ_ERR_SHAPE, fn, "n_seq * n_q_heads");
+    if (n_seq == 0) return KVQ_OK;
+    if (!out || !v_signs) return fail(KVQ_ERR_ARG, fn, "null pointer");
+    if (!aligned(out, 8)) return fail(KVQ_ERR_ALIGN, fn, "alignment");
+    return hip_status(launch_rot_back(out, v_signs, n_seq * n_q_heads, n_q_heads, n_q_heads / g->n_kv_heads,
+                                      (hipStream_t)stream),
+                      fn);
+}
+
 // ---------------------------------------------------------------- measurement helper
 int32_t kvq_read_probe(const void* src, int64_t bytes, uint32_t* sink, int32_t n_blocks, void* stream) {
     const char* fn = "kvq_read_probe";

@@ -255,6 +255,15 @@ hipError_t launch_merge(int n_rows, int n_split, const float* partials, float* o
 // workgroup to sink (kvq_decode.hip)
 hipError_t launch_read_probe(const void* src, int64_t bytes, uint32_t* sink, int n_blocks, hipStream_t st);
 
+// the TurboQuant-MSE rotation variant (kvq_rotate.hip)
+hipError_t launch_rot_quantize(const kvq_geom& g, const uint16_t* k, const uint16_t* v, int64_t stride_tok,
+                               int64_t stride_head, int n_seq, const int64_t* first_slot, const int32_t* n_new,
+                               const int64_t* src_row0, int max_new, const uint8_t* k_signs, const uint8_t* v_signs,
+                               const float* v_sigma, uint8_t* cache, const int64_t* seq_byte_off, hipStream_t st);
+hipError_t launch_rot_queries(const uint16_t* q, uint16_t* qr, const uint8_t* k_signs, int n_rows, int n_q, int g,
+                              hipStream_t st);
+hipError_t launch_rot_back(float* out, const uint8_t* v_signs, int n_rows, int n_q, int g, hipStream_t st);
+
 // chunked prefill attention (kvq_prefill.hip)
 struct PrefillPlan {
     int n_qb;           // query blocks (128 query rows each) per (sequence, KV head)

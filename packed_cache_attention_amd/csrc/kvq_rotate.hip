@@ -1,0 +1,275 @@
+// kvq_rotate.hip -- the TurboQuant-MSE rotation variant: keys (and optionally values)
+// rotated by a seeded random-sign Walsh-Hadamard transform before uniform scalar
+// quantization, queries rotated once per step, outputs rotated back once per head.
+// "RoPE-Aware Bit Allocation for KV-Cache Quantization" (abstract) builds Block-GTQ on
+// TurboQuant-MSE; the related-papers page for "Quantization Dominates Rank Reduction
+// for KV-Cache" names its key path "WHT + MSE".  This file is that baseline on the GPU.
+//
+// Rotation R = H diag(sg) / sqrt(128), H the Sylvester Hadamard matrix.  A binary16
+// row x gives the exact sums S = H (sg * x) = sqrt(128) R x: every binary16 value is
+// an integer count of 2^-24 below 2^40, so the sums are exact in 64-bit integers
+// (|S| < 2^47); each is rounded once to binary32.  Codes compare S with the token
+// norm times the Gaussian thresholds: code = #{j : S_i >= RN32(s * t_j)} (the
+// normalised rotated coordinate S_i / s against the codebook of N(0, 1)).
+//
+// Lane l of a wave holds coordinates 2l and 2l + 1, so the transform's first
+// butterfly stage is lane-local and stage h = 2^k (k >= 1) pairs lane l with lane
+// l ^ 2^(k-1).
+#include "kvq_internal.h"
+
+#pragma clang fp contract(off)
+
+namespace kvq {
+
+constexpr float kRotSigma = 0.0883883461356163f;  // RN32(1 / sqrt(128)): bits 0x3DB504F3
+static_assert(__builtin_bit_cast(uint32_t, kRotSigma) == 0x3DB504F3u, "rotation scale");
+
+// value of a binary16 pattern in units of 2^-24 (exact)
+__device__ __forceinline__ int64_t h2units(uint32_t h) {
+    const int e = (h >> 10) & 31, m = h & 1023;
+    const int64_t v = e == 0 ? (int64_t)m : ((int64_t)(1024 + m) << (e - 1));
+    return (h & 0x8000u) ? -v : v;
+}
+
+__device__ __forceinline__ int64_t shfl_xor64(int64_t v, int m) {
+    const uint32_t lo = (uint32_t)v, hi = (uint32_t)((uint64_t)v >> 32);
+    const uint32_t plo = (uint32_t)__shfl_xor((int)lo, m), phi = (uint32_t)__shfl_xor((int)hi, m);
+    return (int64_t)(((uint64_t)phi << 32) | plo);
+}
+
+// The Walsh-Hadamard transform of the 128 values a wave holds (lane l: a = value
+// 2l, b = value 2l + 1), in place, exact in 64-bit integers.
+__device__ __forceinline__ void fwht64(int64_t& a, int64_t& b, int lane) {
+    {
+        const int64_t s = a + b, d = a - b;
+        a = s;
+        b = d;
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        const int64_t pa = shfl_xor64(a, m), pb = shfl_xor64(b, m);
+        const bool upper = lane & m;  // this lane holds the second member of each pair
+        a = upper ? pa - a : a + pa;
+        b = upper ? pb - b : b + pb;
+    }
+}
+
+// The same transform on binary32 values (the output rotated back: rounding here is
+// ordinary floating point, within the attention tolerance).
+__device__ __forceinline__ void fwht64f(float& a, float& b, int lane) {
+    {
+        const float s = a + b, d = a - b;
+        a = s;
+        b = d;
+    }
+#pragma unroll
+    for (int m = 1; m < 64; m <<= 1) {
+        const float pa = __shfl_xor(a, m), pb = __shfl_xor(b, m);
+        const bool upper = lane & m;
+        a = upper ? pa - a : a + pa;
+        b = upper ? pb - b : b + pb;
+    }
+}
+
+// RN32 of the exact sum (units of 2^-24): a correctly rounded 64-bit integer
+// conversion, then an exact power-of-two scaling (results are normal)
+__device__ __forceinline__ float units_to_f32(int64_t u) { return __builtin_amdgcn_ldexpf(__ll2float_rn(u), -24); }
+
+// the lane's two rotated sums of a binary16 row (signs: 1 -> -1)
+__device__ __forceinline__ void rotated_pair(uint32_t pair, const uint8_t* __restrict__ sg, int lane, float& s0,
+                                             float& s1) {
+    int64_t a = h2units(pair & 0xffffu), b = h2units(pair >> 16);
+    if (sg[2 * lane]) a = -a;
+    if (sg[2 * lane + 1]) b = -b;
+    fwht64(a, b, lane);
+    s0 = units_to_f32(a);
+    s1 = units_to_f32(b);
+}
+
+// ---------------------------------------------------------------- quantize + pack
+// One workgroup (4 waves) per (sequence, KV head, tile touched by the call).  Phase 1:
+// each wave takes tokens p = wave, wave + 4, ...; lane l forms the token norm from its
+// coordinate pair (the pairwise tree), the rotated sums of coordinates 2l, 2l + 1
+// and their codes, written to LDS code rows.  Phase 2: the tile's K records (every
+// block at the same width, so field f of the K order is coordinate c_f = p(f/2) or
+// q(f/2) at bit w*f), V runs and scales, one thread per word.
+constexpr int kRotWaves = 4;
+constexpr int kRotThreads = 64 * kRotWaves;
+
+__global__ __launch_bounds__(kRotThreads) void rot_quantize_kernel(
+    const uint16_t* __restrict__ kx, const uint16_t* __restrict__ vx, int64_t stride_tok, int64_t stride_head,
+    const int64_t* __restrict__ first_slot, const int32_t* __restrict__ n_new, const int64_t* __restrict__ src_row0,
+    int max_new, int64_t capacity, const uint8_t* __restrict__ k_signs, const uint8_t* __restrict__ v_signs,
+    const float* __restrict__ v_sigma, uint8_t* __restrict__ cache, const int64_t* __restrict__ seq_byte_off,
+    int pairing, int wk, int v_bits) {
+    const int s = blockIdx.z, h = blockIdx.y;
+    const int64_t first = first_slot[s];
+    const int n = n_new[s];
+    if (first < 0 || n <= 0 || n > max_new || first + n > capacity) return;
+    const int64_t tau = first / kTile + blockIdx.x;
+    const int64_t tile0 = tau * kTile;
+    const int64_t lo_slot = max(first, tile0), hi_slot = min(first + (int64_t)n, tile0 + kTile);
+    if (lo_slot >= hi_slot) return;
+    const int lo_p = (int)(lo_slot - tile0), hi_p = (int)(hi_slot - tile0);
+    const int k_budget = wk * kMaxBlocks;
+    const int64_t SK = k_record_bytes(k_budget);
+    const int64_t TB = tile_bytes(kHeadDim, k_budget, v_bits);
+    const int RW = (int)(SK / 4), VW = 2 * v_bits;
+    uint8_t* tile = cache + seq_byte_off[s] + ((int64_t)h * (capacity / kTile) + tau) * TB;
+
+    __shared__ uint8_t s_kc[kTile][kHeadDim + 4];  // codes [slot][coordinate]
+    __shared__ uint8_t s_vc[kTile][kHeadDim + 4];
+    __shared__ float s_ks[kTile], s_vs[kTile];
+    __shared__ float s_thr[512];
+    __shared__ uint8_t s_ksg[kHeadDim], s_vsg[kHeadDim];
+    __shared__ float s_vsig[kHeadDim];
+    const int tid = threadIdx.x, lane = tid & 63, wave = __builtin_amdgcn_readfirstlane(tid >> 6);
+    const bool vrot = v_signs != nullptr;
+    for (int i = tid; i < 510; i += kRotThreads) s_thr[i] = c_thresholds[i];
+    if (tid < kHeadDim) {
+        s_ksg[tid] = k_signs[h * kHeadDim + tid];
+        s_vsg[tid] = vrot ? v_signs[h * kHeadDim + tid] : 0;
+        const int blk = pairing == KVQ_PAIR_HALF ? (tid & (kMaxBlocks - 1)) : (tid >> 1);
+        s_vsig[tid] = vrot ? 1.f : v_sigma[h * kMaxBlocks + blk];
+    }
+    for (int i = tid; i < kTile * (kHeadDim + 4) / 4; i += kRotThreads) {
+        ((uint32_t*)s_kc)[i] = 0u;
+        ((uint32_t*)s_vc)[i] = 0u;
+    }
+    __syncthreads();
+
+    // ---- phase 1: norms, rotated sums, codes (lane: coordinates 2l, 2l + 1); the
+    // wave's rows are all requested before the first is used
+    const int64_t row0 = src_row0[s] + (tile0 - first);
+    constexpr int kPer = kTile / kRotWaves;
+    uint32_t kpr[kPer], vpr[kPer];
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int p = lo_p + wave + kRotWaves * i;
+        const int64_t r = row0 + min(p, hi_p - 1);  // a valid row for every load
+        kpr[i] = *(const uint32_t*)(kx + r * stride_tok + (int64_t)h * stride_head + 2 * lane);
+        vpr[i] = *(const uint32_t*)(vx + r * stride_tok + (int64_t)h * stride_head + 2 * lane);
+    }
+#pragma unroll
+    for (int i = 0; i < kPer; ++i) {
+        const int p = lo_p + wave + kRotWaves * i;
+        if (p >= hi_p) break;
+        const uint32_t kp = kpr[i], vp = vpr[i];
+        const float sk = token_norm(kp), sv = token_norm(vp);
+        float k0, k1;
+        rotated_pair(kp, s_ksg, lane, k0, k1);
+        s_kc[p][2 * lane] = (uint8_t)code_of(s_thr, k0, wk, 1.f, sk);
+        s_kc[p][2 * lane + 1] = (uint8_t)code_of(s_thr, k1, wk, 1.f, sk);
+        float v0, v1;
+        if (vrot) {
+            rotated_pair(vp, s_vsg, lane, v0, v1);
+        } else {
+            v0 = h2f(vp & 0xffffu);
+            v1 = h2f(vp >> 16);
+        }
+        s_vc[p][2 * lane] = (uint8_t)code_of(s_thr, v0, v_bits, s_vsig[2 * lane], sv);
+        s_vc[p][2 * lane + 1] = (uint8_t)code_of(s_thr, v1, v_bits, s_vsig[2 * lane + 1], sv);
+        if (lane == 0) {
+            s_ks[p] = sk;
+            s_vs[p] = sv;
+        }
+    }
+    __syncthreads();
+
+    // ---- phase 2: K records of the call's slots (field f = block f/2's p or q coordinate)
+    const bool whole = lo_p == 0 && hi_p == kTile;
+    for (int idx = tid; idx < kTile * RW; idx += kRotThreads) {
+        const int p = idx / RW, k = idx - p * RW;
+        if (p < lo_p || p >= hi_p) continue;
+        uint32_t val = 0u;
+        const int f_lo = (32 * k) / wk, f_hi = min(2 * kMaxBlocks - 1, (32 * k + 31) / wk);
+        for (int f = f_lo; f <= f_hi; ++f) {
+            const int b = f >> 1;
+            const int c = pairing == KVQ_PAIR_HALF ? b + (f & 1) * kMaxBlocks : 2 * b + (f & 1);
+            const int off = wk * f - 32 * k;
+            const uint32_t code = s_kc[p][c];
+            val |= off >= 0 ? code << off : code >> -off;
+        }
+        ((uint32_t*)tile)[p * RW + k] = val;
+    }
+    // V runs: word k of run c holds slots with bits in [32k, 32k + 32)
+    uint32_t* vrun = (uint32_t*)(tile + kTile * SK);
+    for (int idx = tid; idx < kHeadDim * VW; idx += kRotThreads) {
+        const int c = idx & (kHeadDim - 1), k = idx >> 7;
+        const int plo = 32 * k / v_bits, phi = min(kTile - 1, (32 * k + 31) / v_bits);
+        uint32_t val = 0u;
+        for (int p = plo; p <= phi; ++p) {
+            if (p < lo_p || p >= hi_p) continue;
+            const int off = p * v_bits - 32 * k;
+            const uint32_t code = s_vc[p][c];
+            val |= off >= 0 ? code << off : code >> -off;
+        }
+        uint32_t* dst = vrun + c * VW + k;
+        if (whole) *dst = val;
+        else if (val) *dst |= val;
+    }
+    float* scl = (float*)(tile + kTile * SK + kHeadDim * 8 * v_bits);
+    if (tid >= lo_p && tid < hi_p) {
+        scl[tid] = s_ks[tid];
+        scl[kTile + tid] = s_vs[tid];
+    }
+}
+
+// ---------------------------------------------------------------- queries, outputs
+// row r of n_rows: query head r % n_q (KV head (r % n_q) / g); one wave per row.
+__global__ __launch_bounds__(256) void rot_query_kernel(const uint16_t* __restrict__ q, uint16_t* __restrict__ qr,
+                                                        const uint8_t* __restrict__ k_signs, int n_rows, int n_q,
+                                                        int g) {
+    const int lane = threadIdx.x & 63;
+    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= n_rows) return;
+    const int kvh = (r % n_q) / g;
+    const uint32_t pair = *(const uint32_t*)(q + (int64_t)r * kHeadDim + 2 * lane);
+    float s0, s1;
+    rotated_pair(pair, k_signs + kvh * kHeadDim, lane, s0, s1);
+    const _Float16 a = (_Float16)(s0 * kRotSigma), b = (_Float16)(s1 * kRotSigma);
+    *(uint32_t*)(qr + (int64_t)r * kHeadDim + 2 * lane) =
+        (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+}
+
+// out row r <- diag(sg) H out_r / sqrt(128), in place
+__global__ __launch_bounds__(256) void rot_back_kernel(float* __restrict__ out, const uint8_t* __restrict__ v_signs,
+                                                       int n_rows, int n_q, int g) {
+    const int lane = threadIdx.x & 63;
+    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+    if (r >= n_rows) return;
+    const int kvh = (r % n_q) / g;
+    float2* row = (float2*)(out + (int64_t)r * kHeadDim);
+    const float2 y = row[lane];
+    float a = y.x, b = y.y;
+    fwht64f(a, b, lane);
+    const uint8_t* sg = v_signs + kvh * kHeadDim;
+    a *= kRotSigma;
+    b *= kRotSigma;
+    row[lane] = float2{sg[2 * lane] ? -a : a, sg[2 * lane + 1] ? -b : b};
+}
+
+hipError_t launch_rot_quantize(const kvq_geom& g, const uint16_t* k, const uint16_t* v, int64_t stride_tok,
+                               int64_t stride_head, int n_seq, const int64_t* first_slot, const int32_t* n_new,
+                               const int64_t* src_row0, int max_new, const uint8_t* k_signs, const uint8_t* v_signs,
+                               const float* v_sigma, uint8_t* cache, const int64_t* seq_byte_off, hipStream_t st) {
+    const int max_tiles = (max_new + kTile - 1) / kTile + 1;  // a range may straddle one more tile
+    dim3 grid(max_tiles, g.n_kv_heads, n_seq);
+    hipLaunchKernelGGL(rot_quantize_kernel, grid, dim3(kRotThreads), 0, st, k, v, stride_tok, stride_head, first_slot,
+                       n_new, src_row0, max_new, g.capacity_tokens, k_signs, v_signs, v_sigma, cache, seq_byte_off,
+                       g.rope_pairing, g.k_budget / kMaxBlocks, g.v_bits);
+    return hipGetLastError();
+}
+
+hipError_t launch_rot_queries(const uint16_t* q, uint16_t* qr, const uint8_t* k_signs, int n_rows, int n_q, int g,
+                              hipStream_t st) {
+    hipLaunchKernelGGL(rot_query_kernel, dim3((n_rows + 3) / 4), dim3(256), 0, st, q, qr, k_signs, n_rows, n_q, g);
+    return hipGetLastError();
+}
+
+hipError_t launch_rot_back(float* out, const uint8_t* v_signs, int n_rows, int n_q, int g, hipStream_t st) {
+    hipLaunchKernelGGL(rot_back_kernel, dim3((n_rows + 3) / 4), dim3(256), 0, st, out, v_signs, n_rows, n_q, g);
+    return hipGetLastError();
+}
+
+}  // namespace kvq

@@ -100,6 +100,12 @@ def lib() -> C.CDLL:
     L.kvq_prefill_workspace_bytes.restype = I64
     L.kvq_packed_prefill_attn.argtypes = [G, I32, P, P, P, P, P, I32, I32, I64, P, P, P, F32, P, P, SZ, I32, P]
     L.kvq_packed_prefill_attn.restype = I32
+    L.kvq_rot_quantize_pack.argtypes = [G, P, P, I64, I64, I32, P, P, P, I32, P, P, P, P, P, P]
+    L.kvq_rot_quantize_pack.restype = I32
+    L.kvq_rot_queries.argtypes = [G, I32, I32, P, P, P, P]
+    L.kvq_rot_queries.restype = I32
+    L.kvq_rot_back.argtypes = [G, I32, I32, P, P, P]
+    L.kvq_rot_back.restype = I32
     L.kvq_read_probe.argtypes = [P, I64, P, I32, P]
     L.kvq_read_probe.restype = I32
     if L.kvq_version() != LAYOUT_VERSION:
@@ -114,7 +120,7 @@ EXPORTS = ["kvq_version", "kvq_status_string", "kvq_tile_bytes", "kvq_cache_byte
            "kvq_decode_partials", "kvq_merge_partials", "kvq_decode_n_split", "kvq_decode_plan",
            "kvq_decode_step_partials", "kvq_decode_step", "kvq_window_decode_attn", "kvq_window_decode_step",
            "kvq_window_workspace_bytes", "kvq_prefill_plan", "kvq_prefill_workspace_bytes",
-           "kvq_packed_prefill_attn", "kvq_read_probe"]
+           "kvq_packed_prefill_attn", "kvq_read_probe", "kvq_rot_quantize_pack", "kvq_rot_queries", "kvq_rot_back"]
 
 
 def status_string(st: int) -> str:
@@ -414,6 +420,36 @@ def packed_prefill_attn(g: Geom, q: torch.Tensor, cache: torch.Tensor, seq_byte_
         C.byref(g), n_qh, _ptr(q), _ptr(cache), _ptr(seq_byte_off), _ptr(q_start), _ptr(n_q), n_seq, max_q, max_len,
         _ptr(k_bits), _ptr(k_sigma), _ptr(v_sigma), float(softmax_scale), _ptr(out), _ptr(workspace), ws_bytes,
         n_split, _stream(stream)))
+
+
+ROT_SIGMA_BITS = 0x3DB504F3  # KVQ_ROT_SIGMA_BITS: RN32(1/sqrt(128))
+
+
+def rot_quantize_pack(g: Geom, k: torch.Tensor, v: torch.Tensor, first_slot: torch.Tensor, n_new: torch.Tensor,
+                      src_row0: torch.Tensor, max_new: int, k_signs: torch.Tensor, v_signs: torch.Tensor | None,
+                      v_sigma: torch.Tensor | None, cache: torch.Tensor, seq_byte_off: torch.Tensor, stream=None):
+    """The rotated variant of quantize_pack (keys, and values when v_signs is given,
+    rotated by their KV head's random-sign Walsh-Hadamard transform; uniform widths)."""
+    assert k.dtype == torch.float16 and v.dtype == torch.float16 and k.stride() == v.stride() and k.stride(2) == 1
+    assert k_signs.dtype == torch.uint8 and (v_signs is None or v_signs.dtype == torch.uint8)
+    n_seq = first_slot.shape[0]
+    _check("kvq_rot_quantize_pack", lib().kvq_rot_quantize_pack(
+        C.byref(g), _ptr(k), _ptr(v), k.stride(0), k.stride(1), n_seq, _ptr(first_slot), _ptr(n_new), _ptr(src_row0),
+        max_new, _ptr(k_signs), _ptr(v_signs), _ptr(v_sigma), _ptr(cache), _ptr(seq_byte_off), _stream(stream)))
+
+
+def rot_queries(g: Geom, q: torch.Tensor, q_rot: torch.Tensor, k_signs: torch.Tensor, stream=None):
+    """q [n_seq, n_q, 128] fp16 -> q_rot (same shape), rotated once by the key signs."""
+    assert q.dtype == torch.float16 and q.is_contiguous() and q_rot.is_contiguous() and q_rot.dtype == torch.float16
+    _check("kvq_rot_queries", lib().kvq_rot_queries(C.byref(g), q.shape[1], q.shape[0], _ptr(q), _ptr(q_rot),
+                                                     _ptr(k_signs), _stream(stream)))
+
+
+def rot_back(g: Geom, out: torch.Tensor, v_signs: torch.Tensor, stream=None):
+    """out [n_seq, n_q, 128] fp32, rotated back in place by the value signs."""
+    assert out.dtype == torch.float32 and out.is_contiguous()
+    _check("kvq_rot_back", lib().kvq_rot_back(C.byref(g), out.shape[1], out.shape[0], _ptr(out), _ptr(v_signs),
+                                               _stream(stream)))
 
 
 def read_probe(buf: torch.Tensor, sink: torch.Tensor, n_blocks: int, stream=None):

@@ -170,6 +170,17 @@ def gen_chunk_queries(wl: Workload, seq: int, layer: int, pos0: int, n_tok: int,
     return torch.cat(out, 1)
 
 
+def rot_signs(n_kv_heads: int, seed: int = 0, layer: int = 0, d: int = HEAD_DIM, device="cpu") -> torch.Tensor:
+    """The random sign diagonal of a rotated cache: uint8 [n_kv_heads, d], 1 meaning -1,
+    drawn once per (layer, KV head) from a generator seeded with seed * 10**7 + 9 * 10**6 +
+    layer * n_kv_heads + head (a draw, no arithmetic of the method)."""
+    out = []
+    for h in range(n_kv_heads):
+        g = torch.Generator().manual_seed(seed * 10 ** 7 + 9 * 10 ** 6 + layer * n_kv_heads + h)
+        out.append(torch.randint(0, 2, (d,), generator=g, dtype=torch.uint8))
+    return torch.stack(out).to(device)
+
+
 def fp16_cache_bytes(wl: Workload) -> int:
     """Bytes an fp16 K/V cache of this workload would take (all layers, all sequences)."""
     return 2 * 2 * wl.head_dim * wl.n_kv_heads * wl.n_layers * sum(wl.seq_lens)

@@ -153,6 +153,27 @@ def test_host_validation_rejects_before_gpu():
     assert L.kvq_packed_prefill_attn(*p_args(good, 16, 512, 1 << 30, q=None)) == -1
     assert L.kvq_packed_prefill_attn(*p_args(good, 16, 512, 1 << 30, wsp=None)) == -1
     assert L.kvq_packed_prefill_attn(*p_args(good, 16, 512, 1 << 30, n_split=-1)) == -1
+    # rotated variant: uniform key widths 1..8 (k_budget a multiple of 64), v_bits <= 8,
+    # pointers, alignment, capacity, GQA ratio -- all before any HIP call
+    r_args = lambda g_, max_new=4, k=FAKE, vsg=FAKE, vsig=FAKE: (
+        C.byref(g_), k, FAKE, 256, 128, 1, FAKE, FAKE, FAKE, max_new, FAKE, vsg, vsig, FAKE, FAKE, None)
+    assert L.kvq_rot_quantize_pack(*r_args(kvq.geom(2, 160, 3, 1024))) == -3
+    assert L.kvq_rot_quantize_pack(*r_args(kvq.geom(2, 192, 16, 1024))) == -3
+    assert L.kvq_rot_quantize_pack(*r_args(kvq.geom(2, 0, 3, 1024))) == -3
+    assert L.kvq_rot_quantize_pack(*r_args(good, max_new=2048)) == -5
+    assert L.kvq_rot_quantize_pack(*r_args(good, k=None)) == -1
+    assert L.kvq_rot_quantize_pack(*r_args(good, vsg=None, vsig=None)) == -1
+    assert L.kvq_rot_quantize_pack(*r_args(good, k=FAKE + 2)) == -4
+    assert L.kvq_rot_quantize_pack(*r_args(good, max_new=0)) == 0  # nothing to do
+    assert L.kvq_rot_queries(C.byref(good), 3, 1, FAKE, FAKE, FAKE, None) == -2
+    assert L.kvq_rot_queries(C.byref(good), 16, 1, FAKE, None, FAKE, None) == -1
+    assert L.kvq_rot_queries(C.byref(good), 16, 1, FAKE + 2, FAKE, FAKE, None) == -4
+    assert L.kvq_rot_queries(C.byref(kvq.geom(2, 100, 3, 1024)), 16, 1, FAKE, FAKE, FAKE, None) == -3
+    assert L.kvq_rot_queries(C.byref(good), 16, 0, FAKE, FAKE, FAKE, None) == 0
+    assert L.kvq_rot_back(C.byref(good), 16, 1, FAKE + 4, FAKE, None) == -4
+    assert L.kvq_rot_back(C.byref(good), 16, 1, FAKE, None, None) == -1
+    assert L.kvq_rot_back(C.byref(good), 16, -1, FAKE, FAKE, None) == -1
+    assert L.kvq_rot_back(C.byref(kvq.geom(2, 192, 16, 1024)), 16, 1, FAKE, FAKE, None) == -3
     # read probe (measurement helper): counts, pointers, alignment
     assert L.kvq_read_probe(FAKE, -16, FAKE, 4, None) == -1
     assert L.kvq_read_probe(FAKE, 1024, FAKE, 0, None) == -1

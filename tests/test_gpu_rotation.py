@@ -1,0 +1,168 @@
+"""GPU parity of the rotated (TurboQuant-MSE proper) variant against the oracle.
+
+Page: "RoPE-Aware Bit Allocation for KV-Cache Quantization", abstract -- Block-GTQ is
+built on TurboQuant-MSE, whose base step rotates each key by a random-sign
+Walsh-Hadamard transform and codes every rotated coordinate with the Gaussian
+Lloyd-Max codebook at one uniform width (the related-papers page for "Quantization
+Dominates Rank Reduction for KV-Cache" names its key path "WHT + MSE").
+
+Compared: the packed cache bytes of kvq_rot_quantize_pack (bit-exact, one call for a
+ragged batch, then a ragged append into partly filled tiles), the rotated queries of
+kvq_rot_queries (bit-exact), and decode attention over the rotated cache --
+kvq_rot_queries, kvq_packed_decode_attn with uniform widths and the rotation scale,
+then kvq_rot_back -- against the oracle's exact attention of the same method, within
+the attention tolerance.  Values are rotated (their own signs) or coded unrotated with
+per-block scales; both RoPE pairings."""
+import numpy as np
+import pytest
+import torch
+
+import oracle
+from packed_cache_attention_amd import kvq, synth
+
+from pipeline import check_attention, say
+
+pytestmark = pytest.mark.gpu
+
+D = 128
+SIG_ROT = np.array([0x3DB504F3], np.uint32).view(np.float32)[0]
+
+
+def _batch(H, grp, kb, vb, lens, seed, layer=0):
+    wl = synth.Workload("rot", 1, H * grp, H, 1e6, (0,), kb, vb, "decay")
+    return [synth.gen_layer(wl.with_lens([n]), i, layer, n_tok=n, seed=seed) for i, n in enumerate(lens)]
+
+
+def _gpu_pack(g, seqs, first, ksg, vsg, vsig, cache, off):
+    lens = [s[0].shape[0] for s in seqs]
+    rows = torch.cat([s[0] for s in seqs], 0).cuda()
+    vrows = torch.cat([s[1] for s in seqs], 0).cuda()
+    row0 = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    kvq.rot_quantize_pack(g, rows, vrows, torch.tensor(first, dtype=torch.int64, device="cuda"),
+                          torch.tensor(lens, dtype=torch.int32, device="cuda"),
+                          torch.tensor(row0, dtype=torch.int64, device="cuda"), max(lens), ksg.cuda(),
+                          None if vsg is None else vsg.cuda(), None if vsig is None else torch.from_numpy(vsig).cuda(),
+                          cache, off)
+
+
+def _oracle_pack(ogeom, oc, seqs, first, ksg, vsg, vsig):
+    region = ogeom.seq_bytes
+    for i, (K, V, _) in enumerate(seqs):
+        if K.shape[0]:
+            oracle.quantize_pack_rot(ogeom, oc[i * region:(i + 1) * region], K.numpy(), V.numpy(), first[i],
+                                     ksg.numpy(), None if vsg is None else vsg.numpy(), vsig)
+
+
+def _check_bytes(cache, oc, what):
+    gc = cache.cpu().numpy()
+    if not np.array_equal(gc, oc):
+        bad = np.nonzero(gc != oc)[0]
+        raise AssertionError("%s: packed bytes differ at %d positions, first %s" % (what, len(bad), bad[:8]))
+
+
+def _run(H, grp, kb, vb, pairing, vrot, lens, extra, cap, kernel=kvq.DECODE_AUTO, tiles=0, seed=3, qscale=1.0):
+    """Pack `lens` tokens per sequence, append `extra` more, decode; returns worst rel error."""
+    say("rotation: H %d g %d kb %d vb %d pairing %d vrot %d lens %s extra %s kernel %d tiles %d"
+        % (H, grp, kb, vb, pairing, vrot, lens, extra, kernel, tiles))
+    full = [n + e for n, e in zip(lens, extra)]
+    seqs = _batch(H, grp, kb, vb, full, seed)
+    ksg = synth.rot_signs(H, seed=seed)
+    vsg = synth.rot_signs(H, seed=seed + 1) if vrot else None
+    vsig = None
+    if not vrot:
+        ev = np.zeros((H, D // 2, 2), np.uint64)
+        for _, V, _ in seqs:
+            oracle.block_energy(V.numpy(), pairing, ev)
+        _, vsig = oracle.allocate(ev, vb * (D // 2), oracle.UNIFORM)
+    g = kvq.geom(H, kb, vb, cap, rope_pairing=pairing)
+    ogeom = oracle.Geometry(H, kb, vb, cap, pairing=pairing)
+    region = kvq.cache_bytes(g)
+    assert region == ogeom.seq_bytes
+    nseq = len(seqs)
+    cache = torch.zeros(nseq * region, dtype=torch.uint8, device="cuda")
+    off = torch.arange(nseq, dtype=torch.int64, device="cuda") * region
+    oc = np.zeros(nseq * region, np.uint8)
+    head = [(K[:n], V[:n], q) for (K, V, q), n in zip(seqs, lens)]
+    _gpu_pack(g, head, [0] * nseq, ksg, vsg, vsig, cache, off)
+    _oracle_pack(ogeom, oc, head, [0] * nseq, ksg, vsg, vsig)
+    _check_bytes(cache, oc, "first call")
+    if any(extra):
+        tail = [(K[n:], V[n:], q) for (K, V, q), n in zip(seqs, lens)]
+        _gpu_pack(g, tail, list(lens), ksg, vsg, vsig, cache, off)
+        _oracle_pack(ogeom, oc, tail, list(lens), ksg, vsg, vsig)
+        _check_bytes(cache, oc, "append")
+    # queries rotated once
+    q = torch.stack([(s[2].float() * qscale).half() for s in seqs], 0).cuda().contiguous()
+    q_rot = torch.empty_like(q)
+    kvq.rot_queries(g, q, q_rot, ksg.cuda())
+    qc, qr = q.cpu().numpy(), q_rot.cpu().numpy().view(np.uint16)
+    for i in range(nseq):
+        for h in range(H * grp):
+            np.testing.assert_array_equal(qr[i, h], oracle.rot_query(qc[i, h], ksg[h // grp].numpy()))
+    # attention over the rotated cache, then the output rotated back
+    seq_len = torch.tensor(full, dtype=torch.int32, device="cuda")
+    max_len = max(full)
+    kbits = torch.full((H, D // 2), kb // (D // 2), dtype=torch.uint8, device="cuda")
+    ksig = torch.full((H, D // 2), float(SIG_ROT), dtype=torch.float32, device="cuda")
+    vs = ksig if vrot else torch.from_numpy(vsig).cuda()
+    ws = torch.empty(kvq.decode_workspace_bytes(g, H * grp, nseq, max_len, kernel, tiles) // 4 + 4,
+                     dtype=torch.float32, device="cuda")
+    out = torch.empty(nseq, H * grp, D, dtype=torch.float32, device="cuda")
+    kvq.packed_decode_attn(g, q_rot, cache, off, seq_len, max_len, kbits, ksig, vs, out, ws, kernel=kernel,
+                           tiles_per_split=tiles)
+    if vrot:
+        kvq.rot_back(g, out, vsg.cuda())
+    o = out.cpu().numpy()
+    ref = np.stack([oracle.decode_attention_rot(ogeom, oc[i * region:(i + 1) * region], qc[i], full[i],
+                                                ksg.numpy(), None if vsg is None else vsg.numpy(), vsig)
+                    for i in range(nseq)])
+    worst = check_attention(o, ref)
+    say("worst rel %.2e" % worst)
+    return worst
+
+
+@pytest.mark.parametrize("vrot", [True, False], ids=["vrot", "vplain"])
+@pytest.mark.parametrize("pairing", [kvq.PAIR_HALF, kvq.PAIR_INTERLEAVED], ids=["half", "interleaved"])
+@pytest.mark.parametrize("geom", [(2, 8, 192, 3), (2, 4, 128, 2), (1, 7, 64, 1), (3, 2, 256, 4)],
+                         ids=["k3v3g8", "k2v2g4", "k1v1g7", "k4v4g2"])
+def test_rotated_pack_and_decode(geom, pairing, vrot):
+    H, grp, kb, vb = geom
+    _run(H, grp, kb, vb, pairing, vrot, lens=(1000, 333, 64, 1), extra=(5, 64, 0, 130), cap=1152)
+
+
+@pytest.mark.parametrize("kernel", [kvq.DECODE_AUTO, kvq.DECODE_GENERIC])
+@pytest.mark.parametrize("vb", [8, 5])
+def test_rotated_widest(kernel, vb):
+    """Width 8 everywhere (records of 128 bytes: the generic kernel serves them)."""
+    _run(2, 4, 512, vb, kvq.PAIR_HALF, True, lens=(700, 70), extra=(1, 63), cap=832, kernel=kernel)
+
+
+@pytest.mark.parametrize("tiles", [1, 3])
+def test_rotated_split_plans(tiles):
+    _run(2, 8, 192, 3, kvq.PAIR_HALF, True, lens=(1000, 129, 640), extra=(24, 0, 1), cap=1088, tiles=tiles,
+         kernel=kvq.DECODE_MFMA)
+
+
+def test_rotated_queries_large_and_tiny():
+    """Queries of magnitude 10^-6 .. 10^2 (still fitting binary16 once rotated)."""
+    _run(2, 8, 192, 3, kvq.PAIR_HALF, True, lens=(300,), extra=(0,), cap=320, qscale=100.0)
+    _run(2, 8, 192, 3, kvq.PAIR_HALF, True, lens=(300,), extra=(0,), cap=320, qscale=1e-6)
+
+
+def test_rotated_c3_layer_full_size():
+    """One 128K-token Qwen2.5-3B-shaped layer (2 KV heads, 16 query heads, K3V3) through
+    the rotated path in the automatic plan the decode kernel is timed in."""
+    wl = synth.WORKLOADS["c3"]
+    n = wl.seq_lens[0]
+    _run(wl.n_kv_heads, wl.group, wl.k_budget, wl.v_bits, kvq.PAIR_HALF, True, lens=(n - 1,), extra=(1,),
+         cap=synth.ceil_to(n + 64, 64), seed=7)
+
+
+def test_rot_abi_rejections():
+    g = kvq.geom(2, 160, 3, 128)  # 160 is not a multiple of 64
+    q = torch.zeros(1, 4, D, dtype=torch.float16, device="cuda")
+    with pytest.raises(kvq.KvqError):
+        kvq.rot_queries(g, q, torch.empty_like(q), torch.zeros(2, D, dtype=torch.uint8, device="cuda"))
+    g = kvq.geom(2, 192, 16, 128)  # 16-bit values are not rotated
+    with pytest.raises(kvq.KvqError):
+        kvq.rot_back(g, torch.zeros(1, 4, D, device="cuda"), torch.zeros(2, D, dtype=torch.uint8, device="cuda"))
