@@ -23,6 +23,13 @@ held by a spin while the host enqueues them), which matches the kernel durations
 rocprofv3 reports.  A CPU baseline runs the oracle (test infrastructure) on a
 bounded sample of the same workload.
 
+After the timed steps, --reps more steps are timed one by one (median, p10, p90).
+Labelled lines (--extra) repeat the step measurement on the other workloads -- the
+32K Llama-3.1-8B-shaped layer (its 19 MB step fits the 256 MB memory-side cache, so
+a 1 GiB read evicts it before every repetition), the 512K context, the 16-sequence
+batch -- and on the 128K shape in the K-only value mode (V16) and with the generic
+decode kernel; each reports its median step and its kernel's roofline fraction.
+
 `python bench.py --traffic-from FETCH.csv WRITE.csv` instead turns two rocprofv3
 --pmc runs (FETCH_SIZE, then WRITE_SIZE, of this script with --copy-probe-mib)
 into HBM bytes per decode launch, calibrated against the plain copy kernel.
@@ -100,6 +107,204 @@ def traffic_from(fetch_csv: str, write_csv: str, copy_mib: int, workload: str):
     print(json.dumps(out))
 
 
+MALL_BYTES = 256 << 20  # MI355X Infinity Cache (memory-side, in front of HBM)
+
+
+def gen_inputs(wl, seed, dev):
+    """Seeded K/V rows of every (layer, sequence) [L, rows, H, d], the decode step's new
+    token [L, S, H, d] and its queries [L, S, H_q, d], resident on dev (binary16)."""
+    import numpy as np
+    import torch
+    from packed_cache_attention_amd import synth
+    L, Hq, H, d = wl.n_layers, wl.n_q_heads, wl.n_kv_heads, wl.head_dim
+    lens = list(wl.seq_lens)
+    S = len(lens)
+    rows = sum(lens)
+    Kall = torch.empty(L, rows, H, d, dtype=torch.float16, device=dev)
+    Vall = torch.empty_like(Kall)
+    Qall = torch.empty(L, S, Hq, d, dtype=torch.float16, device=dev)
+    row0 = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    for l in range(L):
+        for s in range(S):
+            k, v, _ = synth.gen_layer(wl, s, l, seed=seed, device=dev)
+            Kall[l, row0[s]:row0[s] + lens[s]] = k
+            Vall[l, row0[s]:row0[s] + lens[s]] = v
+    Knew = torch.empty(L, S, H, d, dtype=torch.float16, device=dev)
+    Vnew = torch.empty_like(Knew)
+    for l in range(L):
+        for s in range(S):
+            k, v, q = synth.gen_new_token(wl, s, l, lens[s], 0, seed=seed, device=dev)
+            Knew[l, s], Vnew[l, s] = k, v
+            Qall[l, s] = q
+    torch.cuda.synchronize()
+    return Kall, Vall, Qall, Knew, Vnew, row0
+
+
+class MallFlush:
+    """Evicts the 256 MB memory-side cache: a plain streaming read of 1 GiB (the
+    library's read probe) enqueued before a timed repetition."""
+
+    def __init__(self, dev):
+        import torch
+        from packed_cache_attention_amd import kvq
+        self.kvq = kvq
+        self.buf = torch.ones((4 * MALL_BYTES) // 4, dtype=torch.float32, device=dev)
+        self.nb = 8 * torch.cuda.get_device_properties(dev).multi_processor_count
+        self.sink = torch.empty(self.nb, dtype=torch.int32, device=dev)
+
+    def __call__(self):
+        self.kvq.read_probe(self.buf, self.sink, self.nb)
+
+
+def time_reps(run, reps, flush=None):
+    """Milliseconds of each of `reps` calls of run(), one event pair around each (after
+    the flush, when given, so it is not timed)."""
+    import numpy as np
+    import torch
+    evs = [(torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)) for _ in range(reps)]
+    for a, b in evs:
+        if flush is not None:
+            flush()
+        a.record()
+        run()
+        b.record()
+    torch.cuda.synchronize()
+    return np.array([a.elapsed_time(b) for a, b in evs])
+
+
+def pct(x):
+    import numpy as np
+    return {"p10": round(float(np.percentile(x, 10)), 5), "p50": round(float(np.percentile(x, 50)), 5),
+            "p90": round(float(np.percentile(x, 90)), 5)}
+
+
+def workload_line(args, key, kern_name, v_bits=None, label=None, reps=60, flush=None):
+    """One labelled decode-step measurement on another workload (or the K-only value
+    mode of one): the same fused step as the headline (per layer the append inside the
+    attention launch, then the merge), captured in a HIP graph, `reps` repetitions
+    timed one by one (each after a memory-side-cache flush when the step's bytes fit in
+    it), and the split-phase kernel's average launch time (36 or 28 layers back to
+    back; a flushed single launch each when they fit).  Reports medians."""
+    import dataclasses
+    import numpy as np
+    import torch
+    from packed_cache_attention_amd import kvq, synth
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS[key]
+    if v_bits is not None:
+        wl = dataclasses.replace(wl, v_bits=v_bits, name=wl.name.rsplit("-", 1)[0] + "-k%dv%d" % (wl.k_budget // 64,
+                                                                                                 v_bits))
+    kern = {"auto": kvq.DECODE_AUTO, "generic": kvq.DECODE_GENERIC, "mfma": kvq.DECODE_MFMA}[kern_name]
+    L, Hq, H, d = wl.n_layers, wl.n_q_heads, wl.n_kv_heads, wl.head_dim
+    lens = list(wl.seq_lens)
+    S = len(lens)
+    warm = 3
+    cap = synth.ceil_to(max(lens) + 2 * warm + reps + 16, 64)
+    g = kvq.geom(H, wl.k_budget, wl.v_bits, cap)
+    region = kvq.cache_bytes(g)
+    tpb = kvq.tile_bytes(g) // 64
+    t0 = time.perf_counter()
+    Kall, Vall, Qall, Knew, Vnew, row0 = gen_inputs(wl, args.seed, dev)
+    cache = torch.zeros(L, S * region, dtype=torch.uint8, device=dev)
+    e = torch.zeros(2, H, d // 2, 2, dtype=torch.int64, device=dev)
+    kbits = torch.empty(L, H, d // 2, dtype=torch.uint8, device=dev)
+    ksig = torch.empty(L, H, d // 2, dtype=torch.float32, device=dev)
+    vbits = torch.empty_like(kbits)
+    vsig = torch.empty_like(ksig)
+    off = torch.arange(S, dtype=torch.int64, device=dev) * region
+    v_budget = (16 if wl.v_bits == 16 else wl.v_bits) * (d // 2)
+    first0 = torch.zeros(S, dtype=torch.int64, device=dev)
+    nnew0 = torch.tensor(lens, dtype=torch.int32, device=dev)
+    src0 = torch.tensor(row0, dtype=torch.int64, device=dev)
+    for l in range(L):
+        e.zero_()
+        for s in range(S):
+            xs = slice(int(row0[s]), int(row0[s]) + lens[s])
+            kvq.block_energy(g, Kall[l, xs], e[0])
+            kvq.block_energy(g, Vall[l, xs], e[1])
+        kvq.allocate_bits(g, e[0], wl.k_budget, kvq.GREEDY, kbits[l], ksig[l])
+        kvq.allocate_bits(g, e[1], v_budget, kvq.UNIFORM, vbits[l], vsig[l])
+        kvq.quantize_pack(g, Kall[l], Vall[l], first0, nnew0, src0, max(lens), kbits[l], ksig[l], vsig[l], cache[l],
+                          off)
+    torch.cuda.synchronize()
+    del Kall, Vall
+    t_setup = time.perf_counter() - t0
+    seq_len = torch.tensor([n + 1 for n in lens], dtype=torch.int32, device=dev)
+    plan = kvq.decode_plan(g, Hq, S, cap, kern, 0)
+    partials = torch.empty(L, plan["workspace"] // 4, dtype=torch.float32, device=dev)  # partials (+ query table)
+    out = torch.empty(L, S, Hq, d, dtype=torch.float32, device=dev)
+
+    def launch(l):
+        kvq.decode_step_partials(g, Qall[l], Knew[l], Vnew[l], cache[l], off, seq_len, cap, kbits[l], ksig[l], vsig[l],
+                                 partials[l], kernel=kern)
+
+    def step():
+        for l in range(L):
+            launch(l)
+            kvq.merge_partials(S, Hq, plan["n_split"], partials[l], out[l])
+        seq_len.add_(1)
+
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize()
+    s_cap = torch.cuda.Stream()
+    s_cap.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s_cap):
+        with torch.cuda.graph(graph, stream=s_cap):
+            step()
+    torch.cuda.current_stream().wait_stream(s_cap)
+    torch.cuda.synchronize()
+    for _ in range(warm):
+        graph.replay()
+    torch.cuda.synchronize()
+    ln0 = seq_len.cpu().numpy().astype(np.int64)
+    cache_read = L * int(ln0.sum() + S * (reps - 1) / 2) * H * tpb  # mean over the repetitions
+    step_bytes = cache_read + L * (S * Hq * d * (2 + 4) + S * H * (2 * d * 2 + tpb))
+    flushed = flush is not None and step_bytes < 2 * MALL_BYTES
+    ms = time_reps(graph.replay, reps, flush if flushed else None)
+    med = float(np.median(ms))
+    # the split-phase kernel: layers back to back (or one flushed launch each)
+    kd0 = torch.cuda.Event(enable_timing=True)
+    kd1 = torch.cuda.Event(enable_timing=True)
+    ln = seq_len.cpu().numpy().astype(np.int64)
+    launch_bytes = float(ln.sum()) * H * tpb + S * H * (2 * d * 2 + tpb)
+    if flushed:
+        us = 1e3 * time_reps(lambda: launch(0), reps, flush)
+    else:
+        us = []
+        for _ in range(5):
+            torch.cuda._sleep(20_000_000)
+            kd0.record()
+            for l in range(L):
+                launch(l)
+            kd1.record()
+            torch.cuda.synchronize()
+            us.append(1e3 * kd0.elapsed_time(kd1) / L)
+        us = np.array(us)
+    kus = float(np.median(us))
+    kname = "decode_mfma_kernel" if plan["kernel"] == kvq.DECODE_MFMA else "decode_generic_kernel"
+    gbps = step_bytes / (med / 1e3) / 1e9
+    kgbps = launch_bytes / (kus / 1e6) / 1e9
+    res = {"label": label or wl.name, "workload": wl.name, "layers": L, "q_heads": Hq, "kv_heads": H, "batch": S,
+           "context": lens if S > 1 else lens[0], "k_budget": wl.k_budget, "v_bits": wl.v_bits,
+           "entry_point": "kvq_decode_step_partials + kvq_merge_partials (graph)", "kernel": kname,
+           "n_split": plan["n_split"], "tiles_per_split": plan["tiles_per_split"], "reps": reps,
+           "mall_flushed": flushed, "ms_per_step_median": round(med, 5), "ms_per_step_percentiles": pct(ms),
+           "value": round(gbps, 2), "unit": "GB/s", "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2),
+           "step_bytes": int(step_bytes),
+           "roofline": {"kernel": kname, "bound": "hbm", "achieved": round(kgbps, 2), "peak": HBM_PEAK_GBPS,
+                        "unit": "GB/s", "frac": round(kgbps / HBM_PEAK_GBPS, 4), "avg_launch_us": round(kus, 3),
+                        "algorithmic_bytes_per_launch": int(launch_bytes), "bytes_per_token_head": tpb},
+           "setup_s": round(t_setup, 2)}
+    log("%s: %.4f ms/step median of %d%s = %.1f GB/s (%.1f%% of HBM peak); %s %.2f us/launch = %.1f%% of peak"
+        % (res["label"], med, reps, " (flushed)" if flushed else "", gbps, 100 * gbps / HBM_PEAK_GBPS, kname, kus,
+           100 * kgbps / HBM_PEAK_GBPS))
+    del cache, partials, out, graph
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -124,6 +329,11 @@ def main():
                     help="size of the plain read-bandwidth probe (0: skip)")
     ap.add_argument("--window", type=int, default=128,
                     help="also time the fp16 recent-window step with this many recent tokens unquantized (0: skip)")
+    ap.add_argument("--reps", type=int, default=60,
+                    help="repetitions timed one by one after the timed steps, for the median and percentiles")
+    ap.add_argument("--extra", default="c2,c4,c5,c3-konly,c3-generic",
+                    help="labelled lines on other workloads: c2, c4, c5 (fused step), c3-konly (the K-only "
+                         "value mode, V16, at the 128K shape), c3-generic (the generic kernel at K3V3); '' = none")
     args = ap.parse_args()
     if args.traffic_from:
         traffic_from(args.traffic_from[0], args.traffic_from[1], args.copy_probe_mib or 256,
@@ -154,7 +364,7 @@ def main():
     lens = list(wl.seq_lens)
     S = len(lens)
     # every step appends one token: eager warm-up, graph warm-up, timed steps, kernel-timing steps
-    extra = 2 * max(1, args.warmup) + args.steps + min(args.steps, 10) + 4
+    extra = 2 * max(1, args.warmup) + args.steps + min(args.steps, 10) + 4 + args.reps
     cap = synth.ceil_to(max(lens) + extra, 64)
     g = kvq.geom(H, wl.k_budget, wl.v_bits, cap)
     region = kvq.cache_bytes(g)
@@ -167,25 +377,7 @@ def main():
     # ------------------------------------------------------------ inputs (resident in HBM)
     t0 = time.perf_counter()
     rows = sum(lens)
-    Kall = torch.empty(L, rows, H, d, dtype=torch.float16, device=dev)
-    Vall = torch.empty_like(Kall)
-    Qall = torch.empty(L, S, Hq, d, dtype=torch.float16, device=dev)
-    row0 = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
-    for l in range(L):
-        for s in range(S):
-            k, v, q = synth.gen_layer(wl, s, l, seed=args.seed, device=dev)
-            Kall[l, row0[s]:row0[s] + lens[s]] = k
-            Vall[l, row0[s]:row0[s] + lens[s]] = v
-            Qall[l, s] = q
-    # the decode step's new token per (layer, sequence)
-    Knew = torch.empty(L, S, H, d, dtype=torch.float16, device=dev)
-    Vnew = torch.empty_like(Knew)
-    for l in range(L):
-        for s in range(S):
-            k, v, q = synth.gen_new_token(wl, s, l, lens[s], 0, seed=args.seed, device=dev)
-            Knew[l, s], Vnew[l, s] = k, v
-            Qall[l, s] = q
-    torch.cuda.synchronize()
+    Kall, Vall, Qall, Knew, Vnew, row0 = gen_inputs(wl, args.seed, dev)
     log("generated inputs in %.1f s (%.2f GB fp16 K/V)" % (time.perf_counter() - t0, 2 * Kall.numel() * 2 / 1e9))
 
     # ------------------------------------------------------------ prefill: energy, allocation, bulk quantize
@@ -250,7 +442,7 @@ def main():
     max_len = cap
     plan = kvq.decode_plan(g, Hq, S, max_len, kern, args.tiles_per_split)
     n_split = plan["n_split"]
-    partials = torch.empty(L, S, Hq, n_split, d + 2, dtype=torch.float32, device=dev)
+    partials = torch.empty(L, plan["workspace"] // 4, dtype=torch.float32, device=dev)  # partials (+ query table)
     out = torch.empty(L, S, Hq, d, dtype=torch.float32, device=dev)
     log("decode plan: %s" % plan)
 
@@ -322,6 +514,19 @@ def main():
     value = step_bytes / (ms_step / 1e3) / 1e9
     log("timed %d steps: %.4f ms/step (wall %.4f ms/step), %.1f GB/s = %.1f%% of HBM peak"
         % (args.steps, ms_step, wall * 1e3 / args.steps, value, 100 * value / HBM_PEAK_GBPS))
+    # then `reps` more steps timed one by one (each step reads far more than the
+    # memory-side cache holds: 36 layers of distinct caches, so no flush is needed)
+    median = None
+    if args.reps > 0:
+        rms = time_reps(graph.replay if graph is not None else step, args.reps)
+        attn_b2, _ = seq_bytes()
+        mbytes = 0.5 * (attn_b1 + attn_b2) + app_b0
+        mmed = float(np.median(rms))
+        median = {"reps": args.reps, "ms_per_step_median": round(mmed, 5), "ms_per_step_percentiles": pct(rms),
+                  "value_at_median": round(mbytes / (mmed / 1e3) / 1e9, 2), "mall_flushed": False,
+                  "step_bytes": int(mbytes)}
+        log("median of %d steps timed one by one: %.4f ms/step (p10 %.4f, p90 %.4f)"
+            % (args.reps, mmed, median["ms_per_step_percentiles"]["p10"], median["ms_per_step_percentiles"]["p90"]))
 
     # ------------------------------------------------------------ dominant kernel: back-to-back launches
     # One event pair brackets the 36 layers' split-phase launches, enqueued while a
@@ -503,7 +708,7 @@ def main():
         gb = kvq.geom(L * H, wl.k_budget, wl.v_bits, cap)
         qb_ = Qall.view(1, L * Hq, d)
         bplan = kvq.decode_plan(gb, L * Hq, 1, max_len, kern, 0)
-        bpart = torch.empty(1, L * Hq, bplan["n_split"], d + 2, dtype=torch.float32, device=dev)
+        bpart = torch.empty(bplan["workspace"] // 4, dtype=torch.float32, device=dev)
         bk, bs, bv = kbits.view(L * H, d // 2), ksig.view(L * H, d // 2), vsig.view(L * H, d // 2)
 
         def bstep():
@@ -599,6 +804,23 @@ def main():
     if not args.no_cpu_baseline:
         cpu = cpu_baseline(wl, Kall, Vall, Qall, lens, row0, bytes_per_token_head)
 
+    # ------------------------------------------------------------ labelled lines on the other workloads
+    others = {}
+    keys = [k for k in args.extra.split(",") if k]
+    if keys:
+        flush = MallFlush(dev)
+        for k in keys:
+            if k == "c3-konly":
+                others[k] = workload_line(args, "c3", "auto", v_bits=16, reps=args.reps or 60, flush=flush,
+                                          label="K-only value mode (V16) at the 128K Qwen2.5-3B shape")
+            elif k == "c3-generic":
+                others[k] = workload_line(args, "c3", "generic", reps=args.reps or 60, flush=flush,
+                                          label="the generic decode kernel at the headline workload")
+            else:
+                others[k] = workload_line(args, k, args.kernel, reps=args.reps or 60, flush=flush)
+        del flush
+        torch.cuda.empty_cache()
+
     result = {
         "metric": METRIC,
         "value": round(value, 2),
@@ -620,6 +842,7 @@ def main():
         "step_bytes": int(step_bytes),
         "wall_ms_per_step": round(wall * 1e3 / args.steps, 5),
         "ms_per_step_percentiles": step_pct,
+        "median_of_reps": median,
         "read_probe": probe,
         "quantize_tokens_per_s": round(rows / t_quant, 1),
         "prefill": {"energy_ms": round(t_energy * 1e3, 4), "energy_GBps": round(energy_bytes / t_energy / 1e9, 1),
@@ -635,6 +858,7 @@ def main():
         "window_step": wres,
         "prefill_chunk": pres,
         "layer_batched": batched,
+        "other_workloads": others or None,
     }
     print(json.dumps(result), flush=True)
 
@@ -646,8 +870,11 @@ def cpu_baseline(wl, Kall, Vall, Qall, lens, row0, bytes_per_token_head, budget_
     Reports the packed bytes its decode attention processes per second."""
     import numpy as np
     import oracle
-    n_threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or min(16, os.cpu_count() or 1)
-    os.environ["OMP_NUM_THREADS"] = str(n_threads)
+    # threads: OMP_NUM_THREADS when set (the GPU hosts here give each GPU 16 cores and
+    # set it to 16), else every core of the host
+    host_cores = os.cpu_count() or 1
+    n_threads = int(os.environ.get("OMP_NUM_THREADS", "0")) or host_cores
+    n_threads = oracle.set_threads(n_threads)
     n = lens[0]
     H = wl.n_kv_heads
     t_prep = t_attn = 0.0
@@ -680,8 +907,28 @@ def cpu_baseline(wl, Kall, Vall, Qall, lens, row0, bytes_per_token_head, budget_
                     break
     except OSError:
         pass
-    return {"value": round(attn_bytes / t_attn / 1e9, 5), "unit": "GB/s", "cores": n_threads, "kind": "oracle",
-            "cpu": cpu_model,
+    # one thread, one layer: the same work without OpenMP (layer 0 of sequence 0)
+    oracle.set_threads(1)
+    K = Kall[0, int(row0[0]):int(row0[0]) + n].cpu().numpy()
+    V = Vall[0, int(row0[0]):int(row0[0]) + n].cpu().numpy()
+    q = Qall[0, 0].cpu().numpy()
+    t0 = time.perf_counter()
+    eK = oracle.block_energy(K)
+    eV = oracle.block_energy(V)
+    kb, ks = oracle.allocate(eK, wl.k_budget)
+    _, vs = oracle.allocate(eV, wl.v_bits * 64, oracle.UNIFORM)
+    geom = oracle.Geometry(H, wl.k_budget, wl.v_bits, ((n + 63) // 64) * 64)
+    region = np.zeros(geom.seq_bytes, np.uint8)
+    oracle.quantize_pack(geom, region, K, V, 0, kb, ks, vs)
+    t1 = time.perf_counter()
+    oracle.decode_attention(geom, region, q, n, kb, ks, vs)
+    t2 = time.perf_counter()
+    oracle.set_threads(n_threads)
+    one = {"threads": 1, "layers": 1, "prepare_s": round(t1 - t0, 3), "attention_s": round(t2 - t1, 3),
+           "attention_GBps": round(n * H * bytes_per_token_head / (t2 - t1) / 1e9, 5),
+           "quantize_tokens_per_s": round(n / (t1 - t0), 1)}
+    return {"value": round(attn_bytes / t_attn / 1e9, 5), "unit": "GB/s", "cores": n_threads,
+            "host_cores": host_cores, "kind": "oracle", "cpu": cpu_model, "one_thread": one,
             "sample": "sequence 0 (%d tokens), layers 0..%d, %d KV heads, %d query heads: decode attention "
                       "(fp64) %.2f s; energy+allocation+quantize of the same layers %.2f s (%.0f tokens/s)"
                       % (n, layers - 1, H, wl.n_q_heads, t_attn, t_prep, layers * n / t_prep),

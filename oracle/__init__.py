@@ -50,6 +50,8 @@ def lib() -> C.CDLL:
     L = C.CDLL(_LIB)
     P = C.c_void_p
     I32, I64, F64 = C.c_int, C.c_int64, C.c_double
+    L.or_set_threads.argtypes = [I32]
+    L.or_max_threads.restype = I32
     L.or_lloyd_max.argtypes = [I32, P, P, P]
     L.or_lloyd_max.restype = I32
     L.or_round_fp16.argtypes = [P, I32, P]
@@ -491,3 +493,10 @@ def decode_attention_rot(geom: "Geometry", region: np.ndarray, q16: np.ndarray, 
             o = attend(qr, khat, vhat, scale)
             out[h] = rot_back(o, v_signs[kv]) if v_signs is not None else o
     return out
+
+
+def set_threads(n: int) -> int:
+    """Thread count of the oracle's OpenMP loops (timing only; results do not depend on
+    it).  Returns the count now in force."""
+    lib().or_set_threads(int(n))
+    return int(lib().or_max_threads())

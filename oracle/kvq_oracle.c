@@ -21,6 +21,7 @@
 #include <stdint.h>
 #include <stdlib.h>
 #include <string.h>
+#include <omp.h>
 
 typedef unsigned __int128 u128;
 
@@ -877,3 +878,7 @@ void or_rot_back(const double *y, int d, const uint8_t *signs, double *x)
         x[j] = signs[j] ? -acc : acc;
     }
 }
+
+/* thread count of the OpenMP loops above (a timing control: results do not depend on it) */
+void or_set_threads(int n) { omp_set_num_threads(n > 0 ? n : 1); }
+int or_max_threads(void) { return omp_get_max_threads(); }
