@@ -15,7 +15,8 @@ HERE = os.path.dirname(os.path.abspath(__file__))
 PKG = os.path.dirname(HERE)
 OUT = os.path.join(PKG, "libkvq.so")
 BUILD = os.path.join(PKG, "_build")
-SOURCES = ["kvq_api.hip", "kvq_energy_alloc.hip", "kvq_quantize.hip", "kvq_decode.hip", "kvq_decode_mfma.hip", "kvq_prefill.hip", "kvq_rotate.hip"] + \
+SOURCES = ["kvq_api.hip", "kvq_energy_alloc.hip", "kvq_quantize.hip", "kvq_decode.hip", "kvq_decode_mfma.hip", "kvq_prefill.hip", "kvq_rotate.hip",
+           "kvq_decode_generic.hip"] + \
     ["kvq_decode_mfma_v%d.hip" % v for v in range(1, 9)]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",

@@ -419,7 +419,7 @@ int32_t window_decode(const kvq_geom* g, int32_t window, int32_t n_q_heads, cons
     if (st || n_seq == 0) return st;
     const int n_chunks = plan.n_split + window_chunks(window);  // the packed chunks and the window's
     if (n_chunks > 65535) return fail(KVQ_ERR_CAPACITY, fn, "chunks");
-    const int64_t ws_need = plan.workspace / plan.n_split * n_chunks;
+    const int64_t ws_need = plan_workspace(plan, n_chunks);
     if ((int64_t)workspace_bytes < ws_need) return fail(KVQ_ERR_WORKSPACE, fn, "workspace bytes");
     if (k_new) {
         if (!v_new) return fail(KVQ_ERR_ARG, fn, "null new-token pointer");
@@ -461,9 +461,10 @@ int64_t kvq_window_workspace_bytes(const kvq_geom* g, int32_t window, int32_t n_
     const int64_t packed_max = max_len > window ? max_len - window : 0;
     const int64_t ws = kvq_decode_workspace_bytes_ex(g, n_q_heads, n_seq, packed_max, kernel, tiles_per_split);
     if (ws < 0) return ws;
-    const int32_t ns = kvq_decode_n_split(g, n_q_heads, n_seq, packed_max, kernel, tiles_per_split);
-    if (ns < 0) return ns;
-    return ws / ns * (ns + window_chunks(window));
+    DecodePlan plan;
+    if (plan_decode(*g, n_q_heads, n_seq, packed_max, kernel, tiles_per_split, &plan))
+        return fail(KVQ_ERR_SHAPE, fn, "no kernel for this geometry");
+    return plan_workspace(plan, plan.n_split + window_chunks(window));
 }
 
 int32_t kvq_window_decode_attn(const kvq_geom* g, int32_t window, int32_t n_q_heads, const void* q,

@@ -18,163 +18,6 @@ namespace kvq {
 constexpr int kGenericMaxGroup = 16;
 constexpr bool kMfmaKernel = true;
 
-// bits [pos, pos + w) of a little-endian bitstream at base (w <= 16); reads only
-// the (aligned) dwords that hold the field
-__device__ __forceinline__ uint32_t read_field(const uint8_t* base, int pos, int w) {
-    const uint32_t* dw = (const uint32_t*)base;
-    const int k = pos >> 5, sh = pos & 31;
-    uint32_t v = dw[k] >> sh;
-    if (sh + w > 32) v |= dw[k + 1] << (32 - sh);
-    return v & ((1u << w) - 1u);
-}
-
-__device__ __forceinline__ float level(uint32_t code, int w) {
-    if (w == 16) return h2f(code);
-    return h2f(c_levels[min(KVQ_CB_OFF(w) + (int)code, 509)]);
-}
-
-// grid: (n_split, n_kv, n_seq); block: 256 threads
-__global__ __launch_bounds__(256) void decode_generic_kernel(
-    const uint16_t* __restrict__ q, const uint8_t* __restrict__ cache, const int64_t* __restrict__ seq_byte_off,
-    const int32_t* __restrict__ seq_len, int64_t max_len, int64_t capacity, const uint8_t* __restrict__ k_bits,
-    const float* __restrict__ k_sigma, const float* __restrict__ v_sigma, float scale_log2, int n_q, int g,
-    int pairing, int k_budget, int v_bits, int tiles_per_split, int n_split, float* __restrict__ ws,
-    AppendArgs app) {
-    const int split = blockIdx.x, kvh = blockIdx.y, s = blockIdx.z;
-    const int tid = threadIdx.x;
-    __shared__ float s_x[kTile][kHeadDim + 1];  // dequantized K, then V, of the current tile
-    if (app.window > 0 && split >= n_split - window_chunks(app.window)) {  // the fp16 window's chunks
-        window_chunk<kGenericMaxGroup>(app, q, n_q, g, s, kvh, seq_len, scale_log2, ws, n_split,
-                                       split - (n_split - window_chunks(app.window)), &s_x[0][0]);
-        return;
-    }
-    // packed tokens (seq_len less the fp16 window, if any)
-    const int64_t len = min(max((int64_t)seq_len[s] - app.window, (int64_t)0), max_len);
-    const int64_t n_tiles_seq = (len + kTile - 1) / kTile;
-    const int64_t t0 = (int64_t)split * tiles_per_split;
-    const int64_t t1 = min(t0 + tiles_per_split, n_tiles_seq);
-    const int D2 = kHeadDim + 2;
-
-    __shared__ float s_q[kGenericMaxGroup][kHeadDim];
-    __shared__ float s_p[kGenericMaxGroup][kTile];
-    __shared__ float s_m[kGenericMaxGroup], s_l[kGenericMaxGroup], s_a[kGenericMaxGroup];
-    __shared__ float s_ksig[kHeadDim], s_vsig[kHeadDim];
-    __shared__ uint8_t s_bw[kMaxBlocks];
-    __shared__ uint8_t s_fc[kHeadDim], s_fw[kHeadDim];
-    __shared__ uint16_t s_fo[kHeadDim];
-    __shared__ int s_nf;
-
-    // per-(KV head) tables: block scales per coordinate and the K order
-    if (tid < kMaxBlocks) {
-        const int i = tid;
-        const int p = pairing == KVQ_PAIR_HALF ? i : 2 * i;
-        const int qq = pairing == KVQ_PAIR_HALF ? i + kMaxBlocks : 2 * i + 1;
-        s_bw[i] = k_bits[kvh * kMaxBlocks + i];
-        s_ksig[p] = s_ksig[qq] = k_sigma[kvh * kMaxBlocks + i];
-        s_vsig[p] = s_vsig[qq] = v_sigma[kvh * kMaxBlocks + i];
-    }
-    for (int idx = tid; idx < g * kHeadDim; idx += 256) {
-        const int j = idx / kHeadDim, c = idx - j * kHeadDim;
-        s_q[j][c] = h2f(q[((int64_t)s * n_q + kvh * g + j) * kHeadDim + c]);
-    }
-    if (tid < g) { s_m[tid] = -INFINITY; s_l[tid] = 0.f; }
-    __syncthreads();
-    if (tid < kMaxBlocks) {
-        const int i = tid, w = s_bw[i];
-        int rank = 0, off = 0;
-        for (int j = 0; j < kMaxBlocks; ++j) {
-            const int wj = s_bw[j];
-            if (wj > w || (wj == w && j < i)) { ++rank; off += 2 * wj; }
-        }
-        if (w > 0) {
-            const int p = pairing == KVQ_PAIR_HALF ? i : 2 * i;
-            const int qq = pairing == KVQ_PAIR_HALF ? i + kMaxBlocks : 2 * i + 1;
-            s_fc[2 * rank] = (uint8_t)p; s_fo[2 * rank] = (uint16_t)off; s_fw[2 * rank] = (uint8_t)w;
-            s_fc[2 * rank + 1] = (uint8_t)qq; s_fo[2 * rank + 1] = (uint16_t)(off + w); s_fw[2 * rank + 1] = (uint8_t)w;
-        }
-        const unsigned long long nz = __ballot(w > 0);
-        if (i == 0) s_nf = 2 * __popcll(nz);
-    }
-    __syncthreads();
-    const int nf = s_nf;
-
-    const int64_t SK = k_record_bytes(k_budget);
-    const int64_t TB = tile_bytes(kHeadDim, k_budget, v_bits);
-    const uint8_t* head = cache + seq_byte_off[s] + (int64_t)kvh * (capacity / kTile) * TB;
-    const int per = (g * kHeadDim + 255) / 256;  // (head, coordinate) outputs per thread
-    float o[kGenericMaxGroup * kHeadDim / 256];
-    for (int r = 0; r < per; ++r) o[r] = 0.f;
-
-    for (int64_t tau = t0; tau < t1; ++tau) {
-        const uint8_t* tile = head + tau * TB;
-        const float* scl = (const float*)(tile + kTile * SK + kHeadDim * 8 * v_bits);
-        const int nvalid = (int)min((int64_t)kTile, len - tau * kTile);
-        // dequantize K (width-0 coordinates are 0)
-        for (int idx = tid; idx < kTile * (kHeadDim + 1); idx += 256) (&s_x[0][0])[idx] = 0.f;
-        __syncthreads();
-        for (int idx = tid; idx < kTile * nf; idx += 256) {
-            const int p = idx / nf, f = idx - p * nf;
-            const int w = s_fw[f], c = s_fc[f];
-            const uint32_t code = read_field(tile + p * SK, s_fo[f], w);
-            const float lv = level(code, w);
-            s_x[p][c] = w == 16 ? lv : scl[p] * s_ksig[c] * lv;
-        }
-        __syncthreads();
-        // logits (log2 units); padding slots of a ragged last tile are masked
-        for (int idx = tid; idx < g * kTile; idx += 256) {
-            const int j = idx / kTile, p = idx - j * kTile;
-            float z = 0.f;
-            for (int c = 0; c < kHeadDim; ++c) z += s_q[j][c] * s_x[p][c];
-            s_p[j][p] = p < nvalid ? z * scale_log2 : -INFINITY;
-        }
-        __syncthreads();
-        // online softmax, one thread per head
-        if (tid < g) {
-            const int j = tid;
-            float mt = -INFINITY;
-            for (int p = 0; p < kTile; ++p) mt = fmaxf(mt, s_p[j][p]);
-            const float mn = fmaxf(s_m[j], mt);
-            const float a = exp2f(s_m[j] - mn);
-            float l = 0.f;
-            for (int p = 0; p < kTile; ++p) {
-                const float e = exp2f(s_p[j][p] - mn);
-                s_p[j][p] = e;
-                l += e;
-            }
-            s_l[j] = s_l[j] * a + l;
-            s_m[j] = mn;
-            s_a[j] = a;
-        }
-        __syncthreads();
-        // dequantize V
-        for (int idx = tid; idx < kTile * kHeadDim; idx += 256) {
-            const int c = idx / kTile, p = idx - c * kTile;
-            const uint32_t code = read_field(tile + kTile * SK + c * 8 * v_bits, p * v_bits, v_bits);
-            const float lv = level(code, v_bits);
-            s_x[p][c] = v_bits == 16 ? lv : scl[kTile + p] * s_vsig[c] * lv;
-        }
-        __syncthreads();
-        for (int r = 0; r < per; ++r) {
-            const int idx = tid + 256 * r;
-            if (idx >= g * kHeadDim) break;
-            const int j = idx / kHeadDim, c = idx - j * kHeadDim;
-            float acc = o[r] * s_a[j];
-            for (int p = 0; p < kTile; ++p) acc += s_p[j][p] * s_x[p][c];
-            o[r] = acc;
-        }
-        __syncthreads();
-    }
-    // partials (an empty chunk writes m = -inf, l = 0, o = 0)
-    for (int r = 0; r < per; ++r) {
-        const int idx = tid + 256 * r;
-        if (idx >= g * kHeadDim) break;
-        const int j = idx / kHeadDim, c = idx - j * kHeadDim;
-        float* part = ws + (((int64_t)s * n_q + kvh * g + j) * n_split + split) * D2;
-        part[2 + c] = o[r];
-        if (c == 0) { part[0] = s_m[j]; part[1] = s_l[j]; }
-    }
-}
-
 // grid: (n_seq * n_q rows, 16 groups of 8 coordinates); block: 256 threads = 32 split groups x 8 coordinates
 // Split merge: out = sum_j 2^(m_j - M) o_j / sum_j 2^(m_j - M) l_j.  A workgroup
 // takes 8 coordinates of one row, so a row's merge spreads over 16 compute units;
@@ -287,19 +130,20 @@ int plan_decode(const kvq_geom& g, int n_q_heads, int n_seq, int64_t max_len, in
         while (units * ((n_tiles + 4 * per_wave - 1) / (4 * per_wave)) > slots && 4 * per_wave < n_tiles) ++per_wave;
         T = 4 * per_wave;
     } else if (T <= 0) {
-        // enough chunks to give every CU several workgroups
+        // the same one-pass rule for the generic kernel (one wave per tile, four per chunk)
         const int64_t units = (int64_t)n_seq * g.n_kv_heads;
-        const int64_t target = 512;
-        int64_t want = (target + units - 1) / (units > 0 ? units : 1);
-        if (want < 1) want = 1;
-        T = std::max<int64_t>(1, (n_tiles + want - 1) / want);
+        const int64_t slots = (int64_t)device_cus() * std::max(1, generic_blocks_per_cu(g, n_q_heads));
+        int64_t per_wave = std::max<int64_t>(1, (units * n_tiles + 4 * slots - 1) / (4 * slots));
+        while (units * ((n_tiles + 4 * per_wave - 1) / (4 * per_wave)) > slots && 4 * per_wave < n_tiles) ++per_wave;
+        T = 4 * per_wave;
     }
     int64_t ns = n_tiles > 0 ? (n_tiles + T - 1) / T : 1;
     if (ns > 65535) return KVQ_ERR_CAPACITY;
     plan->kernel = kernel;
     plan->tiles_per_split = (int)T;
     plan->n_split = (int)ns;
-    plan->workspace = (int64_t)n_seq * n_q_heads * ns * (kHeadDim + 2) * 4;
+    plan->table_bytes = kernel == KVQ_DECODE_GENERIC ? generic_table_bytes(g, n_q_heads, n_seq) : 0;
+    plan->workspace = (int64_t)n_seq * n_q_heads * ns * (kHeadDim + 2) * 4 + plan->table_bytes;
     return 0;
 }
 
@@ -321,11 +165,8 @@ hipError_t launch_decode_partials(const kvq_geom& g, const DecodePlan& plan, int
         if (e != hipSuccess) return e;
     }
     const int n_chunks = plan.n_split + (app.window > 0 ? window_chunks(app.window) : 0);  // + the window's
-    dim3 grid(n_chunks, g.n_kv_heads, n_seq);
-    hipLaunchKernelGGL(decode_generic_kernel, grid, dim3(256), 0, st, q, cache, seq_byte_off, seq_len, max_len,
-                       g.capacity_tokens, k_bits, k_sigma, v_sigma, scale_log2, n_q_heads, grp, g.rope_pairing,
-                       g.k_budget, g.v_bits, plan.tiles_per_split, n_chunks, partials, app);
-    return hipGetLastError();
+    return launch_decode_generic(g, plan.tiles_per_split, n_chunks, n_q_heads, q, cache, seq_byte_off, seq_len,
+                                 n_seq, max_len, k_bits, k_sigma, v_sigma, scale_log2, partials, st, app);
 }
 
 // The same merge for a few splits per row (the prefill's key-range splits): thread

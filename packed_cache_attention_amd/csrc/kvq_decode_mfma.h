@@ -106,34 +106,6 @@ struct MfmaSmem {
 // the (then idle) tile buffers
 typedef float WaveOut[kWaves][kHeadDim][8];
 
-__device__ __forceinline__ float dpp_ror8(float x) {
-    // row_ror:8 within each row of 16 lanes: lane l receives lane l ^ 8
-    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
-}
-
-// permlane{16,32}_swap(x, x) returns the even rows (halves) of x in its first result
-// and the odd ones in its second: lane l sees x at l & ~16 (~32) and at l | 16 (| 32).
-// The two results are copied into named integers before any bit cast (a bit cast
-// applied directly to the second element reads the first).
-__device__ __forceinline__ void pair16(float x, float& a, float& b) {
-    const uint32_t u = __builtin_bit_cast(uint32_t, x);
-    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
-    const uint32_t r0 = r[0], r1 = r[1];
-    a = __builtin_bit_cast(float, r0);
-    b = __builtin_bit_cast(float, r1);
-}
-__device__ __forceinline__ void pair32(float x, float& a, float& b) {
-    const uint32_t u = __builtin_bit_cast(uint32_t, x);
-    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
-    const uint32_t r0 = r[0], r1 = r[1];
-    a = __builtin_bit_cast(float, r0);
-    b = __builtin_bit_cast(float, r1);
-}
-// max / sum of the value in lanes l and l ^ 16 (l ^ 32); both lanes get the same result
-__device__ __forceinline__ float xor16_max(float x) { float a, b; pair16(x, a, b); return fmaxf(a, b); }
-__device__ __forceinline__ float xor32_max(float x) { float a, b; pair32(x, a, b); return fmaxf(a, b); }
-__device__ __forceinline__ float xor16_sum(float x) { float a, b; pair16(x, a, b); return a + b; }
-__device__ __forceinline__ float xor32_sum(float x) { float a, b; pair32(x, a, b); return a + b; }
 
 // byte offset 4 * (bits [r, r + n) of x), for a table of dwords
 template <int R, int N>

@@ -58,6 +58,62 @@ __device__ __forceinline__ float token_norm(uint32_t pair) {
     return sqrtf(t);  // correctly rounded on gfx950
 }
 
+// ---- cross-lane helpers (DPP within a row of 16 lanes, permlane swaps across rows)
+__device__ __forceinline__ float dpp_ror8(float x) {
+    // row_ror:8 within each row of 16 lanes: lane l receives lane l ^ 8
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x128, 0xf, 0xf, false));
+}
+
+// permlane{16,32}_swap(x, x) returns the even rows (halves) of x in its first result
+// and the odd ones in its second: lane l sees x at l & ~16 (~32) and at l | 16 (| 32).
+// The two results are copied into named integers before any bit cast (a bit cast
+// applied directly to the second element reads the first).
+__device__ __forceinline__ void pair16(float x, float& a, float& b) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane16_swap(u, u, false, false);
+    const uint32_t r0 = r[0], r1 = r[1];
+    a = __builtin_bit_cast(float, r0);
+    b = __builtin_bit_cast(float, r1);
+}
+__device__ __forceinline__ void pair32(float x, float& a, float& b) {
+    const uint32_t u = __builtin_bit_cast(uint32_t, x);
+    const auto r = __builtin_amdgcn_permlane32_swap(u, u, false, false);
+    const uint32_t r0 = r[0], r1 = r[1];
+    a = __builtin_bit_cast(float, r0);
+    b = __builtin_bit_cast(float, r1);
+}
+// max / sum of the value in lanes l and l ^ 16 (l ^ 32); both lanes get the same result
+__device__ __forceinline__ float xor16_max(float x) { float a, b; pair16(x, a, b); return fmaxf(a, b); }
+__device__ __forceinline__ float xor32_max(float x) { float a, b; pair32(x, a, b); return fmaxf(a, b); }
+__device__ __forceinline__ float xor16_sum(float x) { float a, b; pair16(x, a, b); return a + b; }
+__device__ __forceinline__ float xor32_sum(float x) { float a, b; pair32(x, a, b); return a + b; }
+// lane l ^ 1 and l ^ 2 (quad permutations) and l ^ 4 (half-row mirror: after the quad
+// steps every lane of a quad holds the same value, and lane 7 - l is in the other quad)
+__device__ __forceinline__ float dpp_xor1(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0xB1, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float dpp_xor2(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x4E, 0xf, 0xf, false));
+}
+__device__ __forceinline__ float dpp_mirror8(float x) {
+    return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, x), 0x141, 0xf, 0xf, false));
+}
+// maximum / sum over the 64 lanes of a wave, in every lane
+__device__ __forceinline__ float wave_max64(float x) {
+    x = fmaxf(x, dpp_xor1(x));
+    x = fmaxf(x, dpp_xor2(x));
+    x = fmaxf(x, dpp_mirror8(x));
+    x = fmaxf(x, dpp_ror8(x));
+    return xor32_max(xor16_max(x));
+}
+__device__ __forceinline__ float wave_sum64(float x) {
+    x = x + dpp_xor1(x);
+    x = x + dpp_xor2(x);
+    x = x + dpp_mirror8(x);
+    x = x + dpp_ror8(x);
+    return xor32_sum(xor16_sum(x));
+}
+
 // ---- layout ----
 __host__ __device__ inline int64_t k_record_bytes(int k_budget) { return 16 * ((2 * (int64_t)k_budget + 127) / 128); }
 __host__ __device__ inline int64_t tile_bytes(int d, int k_budget, int v_bits) {
@@ -235,8 +291,13 @@ struct DecodePlan {
     int kernel;           // KVQ_DECODE_GENERIC or KVQ_DECODE_MFMA
     int tiles_per_split;  // 64-token tiles per chunk
     int n_split;          // chunks per (sequence, KV head)
-    int64_t workspace;    // bytes
+    int64_t workspace;    // bytes: the partials of n_split chunks, then table_bytes
+    int64_t table_bytes;  // the generic kernel's query table (0 for the matrix-core kernel)
 };
+// workspace bytes of a plan whose launch carries n_chunks chunks (the window's included)
+inline int64_t plan_workspace(const DecodePlan& p, int n_chunks) {
+    return (p.workspace - p.table_bytes) / p.n_split * n_chunks + p.table_bytes;
+}
 // Returns 0 and fills the plan, or a negative kvq_status.
 int plan_decode(const kvq_geom& g, int n_q_heads, int n_seq, int64_t max_len, int kernel, int tiles_per_split,
                 DecodePlan* plan);
@@ -246,6 +307,15 @@ hipError_t launch_decode_partials(const kvq_geom& g, const DecodePlan& plan, int
                                   const float* v_sigma, float softmax_scale, float* partials, hipStream_t st,
                                   const AppendArgs& app = AppendArgs{});
 // one token per sequence into slot seq_len[s] - 1 (the decode step's append, alone)
+// the vector-ALU kernel (kvq_decode_generic.hip): a query-table launch, then the
+// chunks; the table lives after the partials of all n_chunks chunks
+hipError_t launch_decode_generic(const kvq_geom& g, int tiles_per_split, int n_chunks, int n_q_heads,
+                                 const uint16_t* q, const uint8_t* cache, const int64_t* seq_byte_off,
+                                 const int32_t* seq_len, int n_seq, int64_t max_len, const uint8_t* k_bits,
+                                 const float* k_sigma, const float* v_sigma, float scale_log2, float* partials,
+                                 hipStream_t st, const AppendArgs& app);
+int64_t generic_table_bytes(const kvq_geom& g, int n_q_heads, int n_seq);
+int generic_blocks_per_cu(const kvq_geom& g, int n_q_heads);
 hipError_t launch_append_step(const kvq_geom& g, int n_seq, const AppendArgs& app, const int32_t* seq_len,
                               const uint8_t* k_bits, const float* k_sigma, const float* v_sigma, uint8_t* cache,
                               const int64_t* seq_byte_off, hipStream_t st);

@@ -46,7 +46,14 @@ def test_workspace_bytes_and_plan():
     ws = kvq.decode_workspace_bytes(g, 16, 1, 131072)
     assert ws > 0 and ws % 4 == 0
     ws2 = kvq.decode_workspace_bytes(g, 16, 1, 131072, kvq.DECODE_GENERIC, 8)
-    assert ws2 == 1 * 16 * (2048 // 8) * 130 * 4
+    # the generic kernel's partials, then its query table (per sequence and KV head, 128
+    # fields x the group padded to 4, 8 or 16 heads)
+    assert ws2 == 1 * 16 * (2048 // 8) * 130 * 4 + 1 * 2 * 128 * 8 * 4
+    ws3 = kvq.decode_workspace_bytes(g, 16, 1, 131072, kvq.DECODE_MFMA, 8)
+    assert ws3 == 1 * 16 * (2048 // 8) * 130 * 4
+    # the window call's workspace grows by whole chunks, the table once
+    w = kvq.window_workspace_bytes(g, 128, 16, 1, 131072 + 128, kvq.DECODE_GENERIC, 8)
+    assert w == 1 * 16 * (2048 // 8 + 4) * 130 * 4 + 1 * 2 * 128 * 8 * 4
     assert kvq.decode_workspace_bytes(g, 16, 1, 0) >= 0
 
 
