@@ -36,15 +36,19 @@ typedef __attribute__((address_space(3))) const float lds_cf32;
 __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_cf32*)p; }
 
 // One step of binary lifting on threshold addresses: `at` is the LDS byte address of
-// the threshold of the code found so far (the table start for code 0); the candidate
-// lies `inc` bytes further (4 << open bit position).  The step moves to the candidate
-// when the value reaches its product RN(s * RN(sig * t)); a NaN threshold never does.
-__device__ __forceinline__ uint32_t lift(uint32_t at, uint32_t inc, float x, float sig, float s) {
-    const uint32_t c = at + inc;
+// the threshold of the code found so far (the table start for code 0), `c` the
+// candidate's (at + 4 << open bit position).  The step moves to the candidate when the
+// value reaches its product RN(s * RN(sig * t)); a NaN threshold never does.
+__device__ __forceinline__ uint32_t lift(uint32_t at, uint32_t c, float x, float sig, float s) {
     const float a = *(lds_cf32*)(uintptr_t)c;
     const float b = s * (sig * a);
     return x >= b ? c : at;
 }
+
+// The top bit of a width-w code: the middle threshold of every codebook is exactly +0
+// (the levels are symmetric), and s * (sig * 0) = +0 for the non-negative finite s and
+// sig, so the first lifting step is the test x >= 0 (false for NaN, as the step is).
+__device__ __forceinline__ uint32_t top_bit(float x, int w) { return x >= 0.f ? 4u << (w - 1) : 0u; }
 
 __global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(
     const uint16_t* __restrict__ kx, const uint16_t* __restrict__ vx, int64_t stride_tok, int64_t stride_head,
@@ -215,13 +219,14 @@ __global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(
                 w0 = max(w0, ws[i]);
                 x[i] = h2f(krow[fx[i] & 127]);
                 tb[i] = thr0 + 4u * KVQ_CB_OFF(ws[i]);
-                at[i] = tb[i];
+                at[i] = ws[i] > 0 ? tb[i] + top_bit(x[i], ws[i]) : tb[i];
             }
-            // a field with fewer than w0 bits waits at its table start, its candidate
-            // being the NaN, until its own top bit comes up
-            for (int sh = w0 - 1; sh >= 0; --sh) {
+            // the remaining bits; a field with fewer than w0 bits compares with the NaN
+            // (and stays put) until its own next bit comes up
+            for (int sh = w0 - 2; sh >= 0; --sh) {
 #pragma unroll
-                for (int i = 0; i < kGroup; ++i) at[i] = lift(at[i], sh < ws[i] ? 4u << sh : nan_at - tb[i], x[i], sg[i], sk);
+                for (int i = 0; i < kGroup; ++i)
+                    at[i] = lift(at[i], sh < ws[i] - 1 ? at[i] + (4u << sh) : nan_at, x[i], sg[i], sk);
             }
 #pragma unroll
             for (int i = 0; i < kGroup; ++i)
@@ -242,11 +247,11 @@ __global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(
                 for (int i = 0; i < kVGroup; ++i) {
                     x[i] = h2f(vrow[c0 + i]);
                     sg[i] = s_vsig[c0 + i];
-                    at[i] = vthr;
+                    at[i] = vthr + top_bit(x[i], v_bits);
                 }
-                for (int sh = v_bits - 1; sh >= 0; --sh) {
+                for (int sh = v_bits - 2; sh >= 0; --sh) {
 #pragma unroll
-                    for (int i = 0; i < kVGroup; ++i) at[i] = lift(at[i], 4u << sh, x[i], sg[i], sv);
+                    for (int i = 0; i < kVGroup; ++i) at[i] = lift(at[i], at[i] + (4u << sh), x[i], sg[i], sv);
                 }
 #pragma unroll
                 for (int i = 0; i < kVGroup; ++i) vrow[c0 + i] = valid ? (uint16_t)((at[i] - vthr) >> 2) : (uint16_t)0;

@@ -32,6 +32,10 @@ def test_codebook_matches_oracle(w):
     np.testing.assert_array_equal(lev, cb["levels_fp16"])
     np.testing.assert_array_equal(thr, cb["thresholds"])
     np.testing.assert_array_equal(dd, oracle.tables()["dD"])
+    # the quantizers take a code's top bit as the sign test x >= 0: the middle threshold
+    # of every width is exactly +0 (the levels are symmetric)
+    mid = thr[1 << (w - 1)]
+    assert mid == 0.0 and not np.signbit(mid)
 
 
 @pytest.mark.parametrize("kb,vb", [(192, 3), (128, 2), (192, 2), (1024, 16), (0, 1), (300, 8), (7, 5)])

@@ -1,8 +1,8 @@
 """The decode step replayed from a HIP graph, as the throughput figures time it.
 
-Per layer the step is the fused append + split partials (`kvq_decode_step_partials`)
-and the merge (`kvq_merge_partials`), with the sequences' lengths advanced on the
-device, all captured once; the fp16-window step (`kvq_window_decode_step`) the same
+Per layer the step is either one `kvq_decode_step` call or the split-phase pair
+`kvq_decode_step_partials` + `kvq_merge_partials`, with the sequences' lengths advanced
+on the device, all captured once; the fp16-window step (`kvq_window_decode_step`) the same
 way.  Each replay runs after eager work of the program (the next tokens copied into
 the captured input buffers, an eager run of the same step on a second copy of the
 state, synchronisations), and every replay is compared with that eager run: packed
@@ -36,12 +36,14 @@ def _layers(L, H, grp, kb, vb, n0, extra, cap):
     return out
 
 
-def test_graph_replays_of_the_decode_step_equal_eager_steps():
+@pytest.mark.parametrize("fused", [True, False], ids=["decode_step", "partials+merge"])
+def test_graph_replays_of_the_decode_step_equal_eager_steps(fused):
     L, H, grp, kb, vb = 2, 2, 8, 192, 3
     n0 = [700, 63, 129]
     S, nq = len(n0), H * grp
     cap = 64 * ((max(n0) + STEPS + 63) // 64 + 1)
-    say("graph: %d layers, lengths %s, %d replays" % (L, n0, STEPS))
+    say("graph (%s): %d layers, lengths %s, %d replays" % ("decode_step" if fused else "partials+merge", L, n0,
+                                                         STEPS))
     layers = _layers(L, H, grp, kb, vb, n0, STEPS, cap)
     g, off = layers[0][1]["g"], layers[0][1]["off"]
     region = kvq.cache_bytes(g)
@@ -52,7 +54,7 @@ def test_graph_replays_of_the_decode_step_equal_eager_steps():
         return {"cache": [r["cache"].clone() for _, r in layers],
                 "cur": torch.tensor(n0, dtype=torch.int64, device="cuda"),
                 "seq_len": torch.tensor([n + 1 for n in n0], dtype=torch.int32, device="cuda"),
-                "part": torch.empty(L, S, nq, n_split, 130, dtype=torch.float32, device="cuda"),
+                "part": torch.empty(L, plan["workspace"] // 4, dtype=torch.float32, device="cuda"),
                 "out": torch.full((L, S, nq, 128), float("nan"), dtype=torch.float32, device="cuda")}
 
     qs = [torch.stack([x[2] for x in seqs]).cuda().contiguous() for seqs, _ in layers]
@@ -61,6 +63,10 @@ def test_graph_replays_of_the_decode_step_equal_eager_steps():
 
     def step(st):
         for l, (_, r) in enumerate(layers):
+            if fused:
+                kvq.decode_step(g, qs[l], knew[l], vnew[l], st["cache"][l], off, st["seq_len"], cap, r["kbits"],
+                                r["ksig"], r["vsig"], st["out"][l], st["part"][l])
+                continue
             kvq.decode_step_partials(g, qs[l], knew[l], vnew[l], st["cache"][l], off, st["seq_len"], cap, r["kbits"],
                                      r["ksig"], r["vsig"], st["part"][l])
             kvq.merge_partials(S, nq, n_split, st["part"][l], st["out"][l])
