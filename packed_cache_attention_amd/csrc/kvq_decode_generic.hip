@@ -26,33 +26,60 @@ namespace kvq {
 
 constexpr int kGenWaves = 4;
 constexpr int kGenKRows = 32;  // K record dwords staged at a time (records over 128 bytes are 16-bit: two halves)
+constexpr int kGenericQMax = 16;  // query heads per KV head
 
 // query table row (s, kvh): field f of the K order -> G values q_j[c_f] * sigma_(c_f) *
-// scale * log2(e) (sigma = 1 for 16-bit keys); heads j >= g hold 0
-__global__ __launch_bounds__(kMaxBlocks) void generic_qtable_kernel(const uint16_t* __restrict__ q,
-                                                                     const uint8_t* __restrict__ k_bits,
-                                                                     const float* __restrict__ k_sigma, int n_q,
-                                                                     int g, int G, int pairing, int k16,
-                                                                     float scale_log2, float* __restrict__ table) {
-    const int kvh = blockIdx.x, s = blockIdx.y, i = threadIdx.x;
-    __shared__ uint8_t s_bw[kMaxBlocks];
-    const int w = k_bits[kvh * kMaxBlocks + i];
-    s_bw[i] = (uint8_t)w;
-    __syncthreads();
-    if (w == 0) return;
-    int rank = 0;
-    for (int j = 0; j < kMaxBlocks; ++j) {
-        const int wj = s_bw[j];
-        rank += (wj > w || (wj == w && j < i)) ? 1 : 0;
-    }
-    const int cp = pairing == KVQ_PAIR_HALF ? i : 2 * i;
-    const int cq = pairing == KVQ_PAIR_HALF ? i + kMaxBlocks : 2 * i + 1;
-    const float sig = k16 ? 1.f : k_sigma[kvh * kMaxBlocks + i];
+// scale * log2(e) (sigma = 1 for 16-bit keys); heads j >= g hold 0.  One workgroup of
+// 256 threads per (KV head, sequence): every load is issued first (the group's queries
+// as 8-byte pieces, the widths and scales), the K-order rank of each block comes from
+// ballots over the widths, then thread t writes head j's entries for coordinates t, t + 128.
+__global__ __launch_bounds__(256) void generic_qtable_kernel(const uint16_t* __restrict__ q,
+                                                              const uint8_t* __restrict__ k_bits,
+                                                              const float* __restrict__ k_sigma, int n_q, int g,
+                                                              int G, int pairing, int k16, float scale_log2,
+                                                              float* __restrict__ table) {
+    const int kvh = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
+    __shared__ float s_q[kGenericQMax][kHeadDim];
+    __shared__ int s_pos[kHeadDim];  // coordinate -> field position in the K order (-1: width 0)
+    __shared__ float s_sig[kHeadDim];
     const uint16_t* qs = q + ((int64_t)s * n_q + (int64_t)kvh * g) * kHeadDim;
+    uint2 qv[kGenericQMax * kHeadDim / 4 / 256];
+#pragma unroll
+    for (int i = 0; i < kGenericQMax * kHeadDim / 4 / 256; ++i) {
+        const int e = 4 * (tid + 256 * i);  // element index in [g][128]
+        qv[i] = e < g * kHeadDim ? *(const uint2*)(qs + e) : uint2{0u, 0u};
+    }
+    const int w = tid < kMaxBlocks ? k_bits[kvh * kMaxBlocks + tid] : 0;
+    const float sig = tid < kMaxBlocks ? k_sigma[kvh * kMaxBlocks + tid] : 0.f;
+#pragma unroll
+    for (int i = 0; i < kGenericQMax * kHeadDim / 4 / 256; ++i) {
+        const int e = 4 * (tid + 256 * i);
+        if (e < kGenericQMax * kHeadDim) {
+            float* d = &s_q[0][0] + e;
+            d[0] = h2f(qv[i].x & 0xffffu); d[1] = h2f(qv[i].x >> 16);
+            d[2] = h2f(qv[i].y & 0xffffu); d[3] = h2f(qv[i].y >> 16);
+        }
+    }
+    if (tid < kMaxBlocks) {  // wave 0: lane = block; rank by (width desc, index asc)
+        const unsigned long long below = (1ull << tid) - 1ull;
+        int rank = 0;
+        for (int wc = 16; wc >= 1; --wc) {
+            const unsigned long long mk = __ballot(w == wc);
+            if (wc > w) rank += __popcll(mk);
+            if (wc == w) rank += __popcll(mk & below);
+        }
+        const int cp = pairing == KVQ_PAIR_HALF ? tid : 2 * tid;
+        const int cq = pairing == KVQ_PAIR_HALF ? tid + kMaxBlocks : 2 * tid + 1;
+        s_pos[cp] = w > 0 ? 2 * rank : -1;
+        s_pos[cq] = w > 0 ? 2 * rank + 1 : -1;
+        s_sig[cp] = s_sig[cq] = k16 ? 1.f : sig;
+    }
+    __syncthreads();
     float* t = table + ((int64_t)s * gridDim.x + kvh) * kHeadDim * G;
-    for (int j = 0; j < G; ++j) {
-        t[(2 * rank) * G + j] = j < g ? h2f(qs[j * kHeadDim + cp]) * sig * scale_log2 : 0.f;
-        t[(2 * rank + 1) * G + j] = j < g ? h2f(qs[j * kHeadDim + cq]) * sig * scale_log2 : 0.f;
+    for (int e = tid; e < G * kHeadDim; e += 256) {
+        const int j = e / kHeadDim, c = e - j * kHeadDim;
+        const int f = s_pos[c];
+        if (f >= 0) t[f * G + j] = j < g ? s_q[j][c] * s_sig[c] * scale_log2 : 0.f;
     }
 }
 
@@ -350,7 +377,7 @@ hipError_t launch_decode_generic(const kvq_geom& g, int tiles_per_split, int n_c
     const int G = generic_G(grp);
     // the query table sits after the partials of every chunk
     float* table = partials + (int64_t)n_seq * n_q_heads * n_chunks * (kHeadDim + 2);
-    hipLaunchKernelGGL(generic_qtable_kernel, dim3(g.n_kv_heads, n_seq), dim3(kMaxBlocks), 0, st, q, k_bits, k_sigma,
+    hipLaunchKernelGGL(generic_qtable_kernel, dim3(g.n_kv_heads, n_seq), dim3(256), 0, st, q, k_bits, k_sigma,
                        n_q_heads, grp, G, g.rope_pairing, g.k_budget == 16 * kMaxBlocks ? 1 : 0, scale_log2, table);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
