@@ -305,6 +305,125 @@ def workload_line(args, key, kern_name, v_bits=None, label=None, reps=60, flush=
     return res
 
 
+def rot_line(args, reps=60):
+    """The rotated TurboQuant-MSE variant at the 128K Qwen2.5-3B shape (K3V3: every
+    rotated coordinate at 3 bits, values rotated too).  Prefill: kvq_rot_quantize_pack
+    per layer (timed: tokens/s).  Step per layer: the new token rotated and packed
+    (kvq_rot_quantize_pack), the queries rotated (kvq_rot_queries), the split decode
+    and merge over the rotated cache (the same kernels as the headline, uniform widths,
+    scales RN32(1/sqrt(128))), the outputs rotated back (kvq_rot_back); captured in a
+    HIP graph, `reps` repetitions timed one by one."""
+    import numpy as np
+    import torch
+    from packed_cache_attention_amd import kvq, synth
+    dev = torch.device("cuda:0")
+    wl = synth.WORKLOADS["c3"]
+    L, Hq, H, d = wl.n_layers, wl.n_q_heads, wl.n_kv_heads, wl.head_dim
+    lens = list(wl.seq_lens)
+    S = len(lens)
+    warm = 3
+    cap = synth.ceil_to(max(lens) + 2 * warm + reps + 16, 64)
+    g = kvq.geom(H, wl.k_budget, wl.v_bits, cap)
+    region = kvq.cache_bytes(g)
+    tpb = kvq.tile_bytes(g) // 64
+    Kall, Vall, Qall, Knew, Vnew, row0 = gen_inputs(wl, args.seed, dev)
+    ksg = torch.stack([synth.rot_signs(H, seed=args.seed, layer=l) for l in range(L)]).to(dev)
+    vsg = torch.stack([synth.rot_signs(H, seed=args.seed + 1, layer=l) for l in range(L)]).to(dev)
+    sig = float(np.array([kvq.ROT_SIGMA_BITS], np.uint32).view(np.float32)[0])
+    kbits = torch.full((H, d // 2), wl.k_budget // (d // 2), dtype=torch.uint8, device=dev)
+    rsig = torch.full((H, d // 2), sig, dtype=torch.float32, device=dev)
+    cache = torch.zeros(L, S * region, dtype=torch.uint8, device=dev)
+    off = torch.arange(S, dtype=torch.int64, device=dev) * region
+    first0 = torch.zeros(S, dtype=torch.int64, device=dev)
+    nnew0 = torch.tensor(lens, dtype=torch.int32, device=dev)
+    src0 = torch.tensor(row0, dtype=torch.int64, device=dev)
+
+    def prefill():
+        for l in range(L):
+            kvq.rot_quantize_pack(g, Kall[l], Vall[l], first0, nnew0, src0, max(lens), ksg[l], vsg[l], None, cache[l],
+                                  off)
+
+    prefill()
+    torch.cuda.synchronize()
+    pq = time_reps(prefill, 3)
+    t_q = float(np.median(pq)) / 1e3
+    del Kall, Vall
+    cur = torch.tensor(lens, dtype=torch.int64, device=dev)
+    seq_len = (cur + 1).to(torch.int32)
+    ones32 = torch.ones(S, dtype=torch.int32, device=dev)
+    src_new = torch.arange(S, dtype=torch.int64, device=dev)
+    plan = kvq.decode_plan(g, Hq, S, cap)
+    part = torch.empty(L, plan["workspace"] // 4, dtype=torch.float32, device=dev)
+    qrot = torch.empty_like(Qall)
+    out = torch.empty(L, S, Hq, d, dtype=torch.float32, device=dev)
+
+    def launch(l):
+        kvq.decode_partials(g, qrot[l], cache[l], off, seq_len, cap, kbits, rsig, rsig, part[l])
+
+    def step():
+        for l in range(L):
+            kvq.rot_quantize_pack(g, Knew[l], Vnew[l], cur, ones32, src_new, 1, ksg[l], vsg[l], None, cache[l], off)
+            kvq.rot_queries(g, Qall[l], qrot[l], ksg[l])
+            launch(l)
+            kvq.merge_partials(S, Hq, plan["n_split"], part[l], out[l])
+            kvq.rot_back(g, out[l], vsg[l])
+        cur.add_(1)
+        seq_len.add_(1)
+
+    for _ in range(warm):
+        step()
+    torch.cuda.synchronize()
+    s_cap = torch.cuda.Stream()
+    s_cap.wait_stream(torch.cuda.current_stream())
+    graph = torch.cuda.CUDAGraph()
+    with torch.cuda.stream(s_cap):
+        with torch.cuda.graph(graph, stream=s_cap):
+            step()
+    torch.cuda.current_stream().wait_stream(s_cap)
+    torch.cuda.synchronize()
+    for _ in range(warm):
+        graph.replay()
+    torch.cuda.synchronize()
+    ln0 = seq_len.cpu().numpy().astype(np.int64)
+    step_bytes = L * (int(ln0.sum() + S * (reps - 1) / 2) * H * tpb + S * Hq * d * (2 + 4) + S * H * (2 * d * 2 + tpb))
+    ms = time_reps(graph.replay, reps)
+    med = float(np.median(ms))
+    kd0 = torch.cuda.Event(enable_timing=True)
+    kd1 = torch.cuda.Event(enable_timing=True)
+    us = []
+    for _ in range(5):
+        torch.cuda._sleep(20_000_000)
+        kd0.record()
+        for l in range(L):
+            launch(l)
+        kd1.record()
+        torch.cuda.synchronize()
+        us.append(1e3 * kd0.elapsed_time(kd1) / L)
+    kus = float(np.median(us))
+    ln = seq_len.cpu().numpy().astype(np.int64)
+    launch_bytes = float(ln.sum()) * H * tpb
+    gbps = step_bytes / (med / 1e3) / 1e9
+    kgbps = launch_bytes / (kus / 1e6) / 1e9
+    rows = sum(lens)
+    res = {"label": "rotated TQ-MSE variant (random-sign Hadamard keys and values) at the 128K shape, K3V3",
+           "workload": wl.name + "-rotated", "entry_point": "kvq_rot_quantize_pack + kvq_rot_queries + "
+           "kvq_decode_partials + kvq_merge_partials + kvq_rot_back (graph)", "reps": reps,
+           "ms_per_step_median": round(med, 5), "ms_per_step_percentiles": pct(ms), "value": round(gbps, 2),
+           "unit": "GB/s", "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2), "step_bytes": int(step_bytes),
+           "roofline": {"kernel": "decode_mfma_kernel" if plan["kernel"] == kvq.DECODE_MFMA else
+                        "decode_generic_kernel", "bound": "hbm", "achieved": round(kgbps, 2),
+                        "peak": HBM_PEAK_GBPS, "unit": "GB/s", "frac": round(kgbps / HBM_PEAK_GBPS, 4),
+                        "avg_launch_us": round(kus, 3), "algorithmic_bytes_per_launch": int(launch_bytes)},
+           "rot_quantize_ms": round(t_q * 1e3, 4), "rot_quantize_tokens_per_s": round(rows / t_q, 1),
+           "rot_quantize_GBps": round(rows * H * L * (2 * d * 2 + tpb) / t_q / 1e9, 1)}
+    log("%s: %.4f ms/step median of %d = %.1f GB/s (%.1f%% of HBM peak); decode kernel %.2f us/launch; bulk rotated "
+        "quantize %.3f ms for %d layers (%.3g tokens/s)" % (res["label"], med, reps, gbps, 100 * gbps / HBM_PEAK_GBPS,
+                                                          kus, t_q * 1e3, L, rows / t_q))
+    del cache, part, out, graph
+    torch.cuda.empty_cache()
+    return res
+
+
 def main():
     ap = argparse.ArgumentParser()
     ap.add_argument("--gpus", type=int, default=1)
@@ -331,9 +450,10 @@ def main():
                     help="also time the fp16 recent-window step with this many recent tokens unquantized (0: skip)")
     ap.add_argument("--reps", type=int, default=60,
                     help="repetitions timed one by one after the timed steps, for the median and percentiles")
-    ap.add_argument("--extra", default="c2,c4,c5,c3-konly,c3-generic",
+    ap.add_argument("--extra", default="c2,c4,c5,c3-konly,c3-generic,c3-rot",
                     help="labelled lines on other workloads: c2, c4, c5 (fused step), c3-konly (the K-only "
-                         "value mode, V16, at the 128K shape), c3-generic (the generic kernel at K3V3); '' = none")
+                         "value mode, V16, at the 128K shape), c3-generic (the generic kernel at K3V3), c3-rot (the "
+                         "rotated TQ-MSE variant at the 128K shape); '' = none")
     args = ap.parse_args()
     if args.traffic_from:
         traffic_from(args.traffic_from[0], args.traffic_from[1], args.copy_probe_mib or 256,
@@ -813,6 +933,8 @@ def main():
             if k == "c3-konly":
                 others[k] = workload_line(args, "c3", "auto", v_bits=16, reps=args.reps or 60, flush=flush,
                                           label="K-only value mode (V16) at the 128K Qwen2.5-3B shape")
+            elif k == "c3-rot":
+                others[k] = rot_line(args, reps=args.reps or 60)
             elif k == "c3-generic":
                 others[k] = workload_line(args, "c3", "generic", reps=args.reps or 60, flush=flush,
                                           label="the generic decode kernel at the headline workload")
