@@ -448,6 +448,8 @@ def main():
                     help="size of the plain read-bandwidth probe (0: skip)")
     ap.add_argument("--window", type=int, default=128,
                     help="also time the fp16 recent-window step with this many recent tokens unquantized (0: skip)")
+    ap.add_argument("--ramp", type=int, default=100,
+                    help="untimed steps before the timed region, after the warm-up (clock ramp)")
     ap.add_argument("--reps", type=int, default=60,
                     help="repetitions timed one by one after the timed steps, for the median and percentiles")
     ap.add_argument("--extra", default="c2,c4,c5,c3-konly,c3-generic,c3-rot",
@@ -484,7 +486,7 @@ def main():
     lens = list(wl.seq_lens)
     S = len(lens)
     # every step appends one token: eager warm-up, graph warm-up, timed steps, kernel-timing steps
-    extra = 2 * max(1, args.warmup) + args.steps + min(args.steps, 10) + 4 + args.reps
+    extra = 2 * max(1, args.warmup) + args.steps + min(args.steps, 10) + 4 + args.reps + args.ramp
     cap = synth.ceil_to(max(lens) + extra, 64)
     g = kvq.geom(H, wl.k_budget, wl.v_bits, cap)
     region = kvq.cache_bytes(g)
@@ -605,6 +607,14 @@ def main():
         for _ in range(args.warmup):
             graph.replay()
         torch.cuda.synchronize()
+    # untimed steps that bring the clocks to their steady state (the first ~50 ms of
+    # load run a few percent slower), beyond the requested warm-up
+    for _ in range(args.ramp):
+        if graph is not None:
+            graph.replay()
+        else:
+            step()
+    torch.cuda.synchronize()
     attn_b0, app_b0 = seq_bytes()
     # timed region: exactly `steps` steps, synchronised on both sides
     torch.cuda.synchronize()
