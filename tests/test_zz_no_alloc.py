@@ -14,8 +14,8 @@ from pipeline import check_attention, run_batch, say
 pytestmark = pytest.mark.gpu
 
 
-def _case(lens, seed):
-    wl = synth.WORKLOADS["c3"]
+def _case(lens, seed, wl=None):
+    wl = wl or synth.WORKLOADS["c3"]
     seqs = []
     for i, n in enumerate(lens):
         K, V, q = synth.gen_layer(wl, i, 0, n_tok=n, seed=seed)
@@ -24,9 +24,9 @@ def _case(lens, seed):
     return run_batch(seqs, wl.k_budget, wl.v_bits, cap, check_attn=False), seqs
 
 
-def _compare(lens, seed):
-    say("noalloc: lens %s seed %d" % (list(lens), seed))
-    res, seqs = _case(lens, seed)
+def _compare(lens, seed, wl=None):
+    say("noalloc: lens %s seed %d %s" % (list(lens), seed, wl.name if wl else "c3"))
+    res, seqs = _case(lens, seed, wl)
     g, cache, off = res["g"], res["cache"], res["off"]
     n_seq, n_q = len(lens), seqs[0][2].shape[0]
     q = torch.stack([s[2] for s in seqs], 0).cuda().contiguous()
@@ -54,6 +54,20 @@ def test_noalloc_two_calls_second_smaller():
     """The second call reuses the array the first filled with more partials."""
     _compare((2100, 777, 64, 1), seed=3)
     _compare((900, 130), seed=4)
+
+
+def test_noalloc_generic_kernel():
+    """Geometries the vector-ALU kernel serves (its query table then lives in the array
+    too): the K-only value mode (V16) and a GQA group of 12."""
+    import dataclasses
+    base = synth.WORKLOADS["c3"]
+    konly = dataclasses.replace(base, name="konly", v_bits=16)
+    g12 = dataclasses.replace(base, name="group12", n_q_heads=12, n_kv_heads=1)
+    for wl in (konly, g12):
+        g = kvq.geom(wl.n_kv_heads, wl.k_budget, wl.v_bits, 1024)
+        assert kvq.decode_plan(g, wl.n_q_heads, 2, 1024)["kernel"] == kvq.DECODE_GENERIC
+        _compare((700, 64), seed=5, wl=wl)
+        _compare((130,), seed=6, wl=wl)
 
 
 def test_noalloc_rejects_plan_beyond_the_array():
