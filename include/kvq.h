@@ -165,7 +165,11 @@ int32_t kvq_quantize_pack(const kvq_geom *g, const void *k, const void *v, int64
  *   q        : device binary16 [n_seq][n_q_heads][128] (post-RoPE), contiguous
  *   seq_len  : device int32 [n_seq] (clamped to [0, max_len])
  *   out      : device float [n_seq][n_q_heads][128]
- *   workspace: device scratch of at least kvq_decode_workspace_bytes(...) bytes
+ *   workspace: device scratch of at least kvq_decode_workspace_bytes(...) bytes: the
+ *              split partials, and for the vector-ALU kernel (KVQ_DECODE_GENERIC) after
+ *              them a query table of n_seq * n_kv_heads * 128 * G floats (G = the group
+ *              size padded to 4, 8 or 16); no initial contents are required; calls that
+ *              share a workspace must not overlap in time
  * Requirements: head_dim 128; n_q_heads multiple of n_kv_heads with ratio <= 16
  * (<= 8 for KVQ_DECODE_MFMA); 0 <= max_len <= capacity; q, cache, out and
  * workspace 16-byte aligned. */
@@ -216,7 +220,8 @@ int32_t kvq_packed_decode_attn_noalloc(const kvq_geom *g, int32_t n_q_heads, con
  *   [2..129] o_c = sum_t 2^(z_t - m) vhat_{t,c}          (unnormalised)
  * Any reference gives the same merged result: the merge weighs chunk k by 2^(m_k - M).
  * n_split is kvq_decode_n_split(...) for the same arguments; partials_bytes must be
- * at least kvq_decode_workspace_bytes_ex(...). */
+ * at least kvq_decode_workspace_bytes_ex(...) (with KVQ_DECODE_GENERIC the bytes after
+ * the partials hold that kernel's query table). */
 int32_t kvq_decode_partials(const kvq_geom *g, int32_t n_q_heads, const void *q, const uint8_t *cache,
                             const int64_t *seq_byte_off, const int32_t *seq_len, int32_t n_seq, int64_t max_len,
                             const uint8_t *k_bits, const float *k_sigma, const float *v_sigma, float softmax_scale,
