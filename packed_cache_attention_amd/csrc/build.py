@@ -38,9 +38,15 @@ def torch_lib_dir():
     return None
 
 
-def _compile(src):
-    obj = os.path.join(BUILD, src.replace(".hip", ".o"))
-    cmd = [HIPCC] + FLAGS + ["-c", os.path.join(HERE, src), "-o", obj]
+# host code under AddressSanitizer and UBSan (device code unchanged), for checking the
+# C ABI's host-side validation on the CPU: libkvq_hostsan.so
+HOST_SAN = ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined", "-Xarch_host",
+            "-fno-omit-frame-pointer"]
+
+
+def _compile(src, extra=(), build_dir=BUILD):
+    obj = os.path.join(build_dir, src.replace(".hip", ".o"))
+    cmd = [HIPCC] + FLAGS + list(extra) + ["-c", os.path.join(HERE, src), "-o", obj]
     r = subprocess.run(cmd, capture_output=True, text=True)
     err = "\n".join(l for l in (r.stderr or "").splitlines() if "packed-fp32-ops" not in l)
     if r.returncode != 0:
@@ -48,22 +54,27 @@ def _compile(src):
     return obj, err
 
 
-def build(verbose=False):
-    os.makedirs(BUILD, exist_ok=True)
+def build(verbose=False, host_sanitize=False):
+    extra = HOST_SAN if host_sanitize else []
+    build_dir = BUILD + ("_hostsan" if host_sanitize else "")
+    out = os.path.join(PKG, "libkvq_hostsan.so") if host_sanitize else OUT
+    os.makedirs(build_dir, exist_ok=True)
     with cf.ThreadPoolExecutor(max_workers=min(int(os.environ.get("MAX_JOBS", "8")), len(SOURCES))) as ex:
-        results = list(ex.map(_compile, SOURCES))
+        results = list(ex.map(lambda src: _compile(src, extra, build_dir), SOURCES))
     for obj, err in results:
         if verbose and err.strip():
             print(err, file=sys.stderr)
     objs = [o for o, _ in results]
-    link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", OUT + ".tmp"] + objs
+    link = [HIPCC, "--offload-arch=gfx950", "-shared", "-fPIC", "-o", out + ".tmp"] + objs
+    if host_sanitize:
+        link += ["-Xarch_host", "-fsanitize=address", "-Xarch_host", "-fsanitize=undefined"]
     tl = torch_lib_dir()
     if tl:
         link += ["-L" + tl, "-Wl,-rpath," + tl]
     subprocess.check_call(link)
-    os.replace(OUT + ".tmp", OUT)
-    return OUT
+    os.replace(out + ".tmp", out)
+    return out
 
 
 if __name__ == "__main__":
-    print(build(verbose=True))
+    print(build(verbose=True, host_sanitize="--host-sanitize" in sys.argv))

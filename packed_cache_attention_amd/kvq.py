@@ -13,7 +13,8 @@ import os
 
 import torch  # noqa: F401  (load torch's HIP runtime before the library maps its own soname)
 
-_LIB_PATH = os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
+# KVQ_LIBRARY names another build of the same library (e.g. the host-sanitized one)
+_LIB_PATH = os.environ.get("KVQ_LIBRARY") or os.path.join(os.path.dirname(os.path.abspath(__file__)), "libkvq.so")
 
 OK = 0
 PAIR_HALF, PAIR_INTERLEAVED = 0, 1
