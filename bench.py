@@ -308,9 +308,8 @@ def workload_line(args, key, kern_name, v_bits=None, label=None, reps=60, flush=
 def rot_line(args, reps=60):
     """The rotated TurboQuant-MSE variant at the 128K Qwen2.5-3B shape (K3V3: every
     rotated coordinate at 3 bits, values rotated too).  Prefill: kvq_rot_quantize_pack
-    per layer (timed: tokens/s).  Step per layer: the new token rotated and packed
-    (kvq_rot_quantize_pack), the queries rotated (kvq_rot_queries), the split decode
-    and merge over the rotated cache (the same kernels as the headline, uniform widths,
+    per layer (timed: tokens/s).  Step per layer: the new token rotated and packed and
+    the queries rotated in one launch (kvq_rot_decode_prepare), the split decode and merge over the rotated cache (the same kernels as the headline, uniform widths,
     scales RN32(1/sqrt(128))), the outputs rotated back (kvq_rot_back); captured in a
     HIP graph, `reps` repetitions timed one by one."""
     import numpy as np
@@ -348,10 +347,7 @@ def rot_line(args, reps=60):
     pq = time_reps(prefill, 3)
     t_q = float(np.median(pq)) / 1e3
     del Kall, Vall
-    cur = torch.tensor(lens, dtype=torch.int64, device=dev)
-    seq_len = (cur + 1).to(torch.int32)
-    ones32 = torch.ones(S, dtype=torch.int32, device=dev)
-    src_new = torch.arange(S, dtype=torch.int64, device=dev)
+    seq_len = torch.tensor(lens, dtype=torch.int32, device=dev) + 1
     plan = kvq.decode_plan(g, Hq, S, cap)
     part = torch.empty(L, plan["workspace"] // 4, dtype=torch.float32, device=dev)
     qrot = torch.empty_like(Qall)
@@ -362,12 +358,10 @@ def rot_line(args, reps=60):
 
     def step():
         for l in range(L):
-            kvq.rot_quantize_pack(g, Knew[l], Vnew[l], cur, ones32, src_new, 1, ksg[l], vsg[l], None, cache[l], off)
-            kvq.rot_queries(g, Qall[l], qrot[l], ksg[l])
+            kvq.rot_decode_prepare(g, Qall[l], qrot[l], Knew[l], Vnew[l], cache[l], off, seq_len, ksg[l], vsg[l], None)
             launch(l)
             kvq.merge_partials(S, Hq, plan["n_split"], part[l], out[l])
             kvq.rot_back(g, out[l], vsg[l])
-        cur.add_(1)
         seq_len.add_(1)
 
     for _ in range(warm):
@@ -406,7 +400,7 @@ def rot_line(args, reps=60):
     kgbps = launch_bytes / (kus / 1e6) / 1e9
     rows = sum(lens)
     res = {"label": "rotated TQ-MSE variant (random-sign Hadamard keys and values) at the 128K shape, K3V3",
-           "workload": wl.name + "-rotated", "entry_point": "kvq_rot_quantize_pack + kvq_rot_queries + "
+           "workload": wl.name + "-rotated", "entry_point": "kvq_rot_decode_prepare + "
            "kvq_decode_partials + kvq_merge_partials + kvq_rot_back (graph)", "reps": reps,
            "ms_per_step_median": round(med, 5), "ms_per_step_percentiles": pct(ms), "value": round(gbps, 2),
            "unit": "GB/s", "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2), "step_bytes": int(step_bytes),

@@ -358,6 +358,19 @@ int32_t kvq_rot_queries(const kvq_geom *g, int32_t n_q_heads, int32_t n_seq, con
                         const uint8_t *k_signs, void *stream);
 int32_t kvq_rot_back(const kvq_geom *g, int32_t n_q_heads, int32_t n_seq, float *out, const uint8_t *v_signs,
                      void *stream);
+/* The rotated variant's decode step, first half, in one launch: each sequence's new token
+ * (k_new, v_new: binary16 rows [n_seq][n_kv_heads][128] at element strides
+ * new_stride_seq / new_stride_head) rotated, coded and packed into slot seq_len[s] - 1,
+ * byte for byte as kvq_rot_quantize_pack packs it, and the queries rotated as
+ * kvq_rot_queries rotates them (q, q_rot: [n_seq][n_q_heads][128] binary16).  Slots outside
+ * [0, capacity) are skipped.  Requirements: those of kvq_rot_quantize_pack and
+ * kvq_rot_queries; the slot's bytes zero before the call (appends OR into the runs);
+ * n_seq and n_kv_heads + n_q_heads at most 65535 (else KVQ_ERR_SHAPE).  Errors as those
+ * two calls report them; the caller owns every buffer. */
+int32_t kvq_rot_decode_prepare(const kvq_geom *g, int32_t n_q_heads, int32_t n_seq, const void *q, void *q_rot,
+                               const void *k_new, const void *v_new, int64_t new_stride_seq, int64_t new_stride_head,
+                               uint8_t *cache, const int64_t *seq_byte_off, const int32_t *seq_len,
+                               const uint8_t *k_signs, const uint8_t *v_signs, const float *v_sigma, void *stream);
 
 /* Measurement helper (not a step of the method): a plain streaming read of `bytes`
  * (a multiple of 16; src 16-byte aligned) by n_blocks workgroups of 256 threads, each

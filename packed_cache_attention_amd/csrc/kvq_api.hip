@@ -623,6 +623,39 @@ int32_t kvq_rot_back(const kvq_geom* g, int32_t n_q_heads, int32_t n_seq, float*
                       fn);
 }
 
+extern "C++" namespace kvq {
+// kvq_rotate.hip (C++ linkage inside this extern "C" block)
+hipError_t launch_rot_step(const kvq_geom& g, int n_q_heads, int n_seq, const uint16_t* q, uint16_t* qr,
+                           const uint16_t* k_new, const uint16_t* v_new, int64_t stride_seq, int64_t stride_head,
+                           uint8_t* cache, const int64_t* seq_byte_off, const int32_t* seq_len,
+                           const uint8_t* k_signs, const uint8_t* v_signs, const float* v_sigma, hipStream_t st);
+}  // namespace kvq
+
+int32_t kvq_rot_decode_prepare(const kvq_geom* g, int32_t n_q_heads, int32_t n_seq, const void* q, void* q_rot,
+                               const void* k_new, const void* v_new, int64_t new_stride_seq, int64_t new_stride_head,
+                               uint8_t* cache, const int64_t* seq_byte_off, const int32_t* seq_len,
+                               const uint8_t* k_signs, const uint8_t* v_signs, const float* v_sigma, void* stream) {
+    const char* fn = "kvq_rot_decode_prepare";
+    int32_t st = check_rot_geom(g, fn);
+    if (st) return st;
+    if (n_q_heads < 1 || n_q_heads % g->n_kv_heads) return fail(KVQ_ERR_SHAPE, fn, "n_q_heads");
+    if (n_seq < 0) return fail(KVQ_ERR_ARG, fn, "negative count");
+    if (n_seq > 65535 || g->n_kv_heads + n_q_heads > 65535) return fail(KVQ_ERR_SHAPE, fn, "n_seq or heads");
+    if (n_seq == 0) return KVQ_OK;
+    if (!q || !q_rot || !k_new || !v_new || !cache || !seq_byte_off || !seq_len || !k_signs ||
+        (!v_signs && !v_sigma))
+        return fail(KVQ_ERR_ARG, fn, "null pointer");
+    if (new_stride_seq < 0 || new_stride_head < 0) return fail(KVQ_ERR_ARG, fn, "negative stride");
+    if (!aligned(q, 4) || !aligned(q_rot, 4) || !aligned(k_new, 4) || !aligned(v_new, 4) || (new_stride_seq & 1) ||
+        (new_stride_head & 1) || !aligned(cache, 16) || !aligned(seq_byte_off, 8) || !aligned(seq_len, 4) ||
+        !aligned(v_sigma, 4))
+        return fail(KVQ_ERR_ALIGN, fn, "alignment");
+    return hip_status(launch_rot_step(*g, n_q_heads, n_seq, (const uint16_t*)q, (uint16_t*)q_rot,
+                                      (const uint16_t*)k_new, (const uint16_t*)v_new, new_stride_seq, new_stride_head,
+                                      cache, seq_byte_off, seq_len, k_signs, v_signs, v_sigma, (hipStream_t)stream),
+                      fn);
+}
+
 // ---------------------------------------------------------------- measurement helper
 int32_t kvq_read_probe(const void* src, int64_t bytes, uint32_t* sink, int32_t n_blocks, void* stream) {
     const char* fn = "kvq_read_probe";

@@ -249,6 +249,106 @@ __global__ __launch_bounds__(256) void rot_back_kernel(float* __restrict__ out, 
     row[lane] = float2{sg[2 * lane] ? -a : a, sg[2 * lane + 1] ? -b : b};
 }
 
+// ---------------------------------------------------------------- decode-step preparation
+// One launch for a rotated decode step: block (x < n_kv, s) packs sequence s's new
+// token for KV head x at slot seq_len[s] - 1 (one wave: lane l owns coordinates 2l,
+// 2l + 1; the same norms, rotated sums and codes as rot_quantize_kernel, the record
+// OR-assembled in LDS and stored whole, the V codes OR-ed into their runs -- the slot's
+// bits are zero in a zero-initialised cache); block (x = n_kv + r, s) rotates query
+// head r of sequence s with its KV head's key signs.
+__global__ __launch_bounds__(64) void rot_step_kernel(
+    const uint16_t* __restrict__ q, uint16_t* __restrict__ qr, const uint16_t* __restrict__ kx,
+    const uint16_t* __restrict__ vx, int64_t stride_seq, int64_t stride_head, uint8_t* __restrict__ cache,
+    const int64_t* __restrict__ seq_byte_off, const int32_t* __restrict__ seq_len, int64_t capacity,
+    const uint8_t* __restrict__ k_signs, const uint8_t* __restrict__ v_signs, const float* __restrict__ v_sigma,
+    int n_kv, int n_q, int g, int pairing, int wk, int v_bits) {
+    const int s = blockIdx.y, x = blockIdx.x, lane = threadIdx.x;
+    if (x >= n_kv) {  // a query row
+        const int hq = x - n_kv;
+        const int64_t r = (int64_t)s * n_q + hq;
+        const uint32_t pair = *(const uint32_t*)(q + r * kHeadDim + 2 * lane);
+        float s0, s1;
+        rotated_pair(pair, k_signs + (hq / g) * kHeadDim, lane, s0, s1);
+        const _Float16 a = (_Float16)(s0 * kRotSigma), b = (_Float16)(s1 * kRotSigma);
+        *(uint32_t*)(qr + r * kHeadDim + 2 * lane) =
+            (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
+        return;
+    }
+    const int h = x;
+    const int64_t slot = (int64_t)seq_len[s] - 1;
+    if (slot < 0 || slot >= capacity) return;
+    const int64_t tau = slot / kTile;
+    const int p = (int)(slot - tau * kTile);
+    const int k_budget = wk * kMaxBlocks;
+    const int64_t SK = k_record_bytes(k_budget);
+    const int64_t TB = tile_bytes(kHeadDim, k_budget, v_bits);
+    uint8_t* tile = cache + seq_byte_off[s] + ((int64_t)h * (capacity / kTile) + tau) * TB;
+    __shared__ float s_thr[510];
+    __shared__ uint32_t s_rec[32];  // the slot's K record (at most 8 bits x 128 fields)
+    const bool vrot = v_signs != nullptr;
+    const int c0 = 2 * lane, c1 = 2 * lane + 1;
+    const uint32_t kp = *(const uint32_t*)(kx + (int64_t)s * stride_seq + (int64_t)h * stride_head + c0);
+    const uint32_t vp = *(const uint32_t*)(vx + (int64_t)s * stride_seq + (int64_t)h * stride_head + c0);
+    float vs0 = 1.f, vs1 = 1.f;
+    if (!vrot) {
+        const int b0 = pairing == KVQ_PAIR_HALF ? (c0 & (kMaxBlocks - 1)) : (c0 >> 1);
+        const int b1 = pairing == KVQ_PAIR_HALF ? (c1 & (kMaxBlocks - 1)) : (c1 >> 1);
+        vs0 = v_sigma[h * kMaxBlocks + b0];
+        vs1 = v_sigma[h * kMaxBlocks + b1];
+    }
+    for (int i = lane; i < 510; i += 64) s_thr[i] = c_thresholds[i];
+    if (lane < 32) s_rec[lane] = 0u;
+    const float sk = token_norm(kp), sv = token_norm(vp);
+    float k0, k1, v0, v1;
+    rotated_pair(kp, k_signs + h * kHeadDim, lane, k0, k1);
+    if (vrot) {
+        rotated_pair(vp, v_signs + h * kHeadDim, lane, v0, v1);
+    } else {
+        v0 = h2f(vp & 0xffffu);
+        v1 = h2f(vp >> 16);
+    }
+    __syncthreads();
+    const uint32_t kc[2] = {code_of(s_thr, k0, wk, 1.f, sk), code_of(s_thr, k1, wk, 1.f, sk)};
+    const uint32_t vc[2] = {code_of(s_thr, v0, v_bits, vs0, sv), code_of(s_thr, v1, v_bits, vs1, sv)};
+    // K record: every block has width wk, so field f = 2b + e (block b's first or second
+    // coordinate) sits at bit wk * f
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        const int c = e ? c1 : c0;
+        const int f = pairing == KVQ_PAIR_HALF ? 2 * (c & (kMaxBlocks - 1)) + (c >> 6) : c;
+        const int off = wk * f, k = off >> 5, sh = off & 31;
+        atomicOr(&s_rec[k], kc[e] << sh);
+        if (sh + wk > 32) atomicOr(&s_rec[k + 1], kc[e] >> (32 - sh));
+    }
+    __syncthreads();
+    if (lane < (int)(SK / 4)) ((uint32_t*)(tile + (int64_t)p * SK))[lane] = s_rec[lane];
+    uint32_t* vrun = (uint32_t*)(tile + kTile * SK);
+    const int vb = p * v_bits, vk = vb >> 5, vsh = vb & 31;
+#pragma unroll
+    for (int e = 0; e < 2; ++e) {
+        uint32_t* run = vrun + (e ? c1 : c0) * 2 * v_bits;
+        if (vc[e] == 0) continue;
+        atomicOr(run + vk, vc[e] << vsh);
+        if (vsh + v_bits > 32 && (vc[e] >> (32 - vsh)) != 0) atomicOr(run + vk + 1, vc[e] >> (32 - vsh));
+    }
+    if (lane == 0) {
+        float* scl = (float*)(tile + kTile * SK + kHeadDim * 8 * v_bits);
+        scl[p] = sk;
+        scl[kTile + p] = sv;
+    }
+}
+
+hipError_t launch_rot_step(const kvq_geom& g, int n_q_heads, int n_seq, const uint16_t* q, uint16_t* qr,
+                           const uint16_t* k_new, const uint16_t* v_new, int64_t stride_seq, int64_t stride_head,
+                           uint8_t* cache, const int64_t* seq_byte_off, const int32_t* seq_len,
+                           const uint8_t* k_signs, const uint8_t* v_signs, const float* v_sigma, hipStream_t st) {
+    dim3 grid(g.n_kv_heads + n_q_heads, n_seq);
+    hipLaunchKernelGGL(rot_step_kernel, grid, dim3(64), 0, st, q, qr, k_new, v_new, stride_seq, stride_head, cache,
+                       seq_byte_off, seq_len, g.capacity_tokens, k_signs, v_signs, v_sigma, g.n_kv_heads, n_q_heads,
+                       n_q_heads / g.n_kv_heads, g.rope_pairing, g.k_budget / kMaxBlocks, g.v_bits);
+    return hipGetLastError();
+}
+
 hipError_t launch_rot_quantize(const kvq_geom& g, const uint16_t* k, const uint16_t* v, int64_t stride_tok,
                                int64_t stride_head, int n_seq, const int64_t* first_slot, const int32_t* n_new,
                                const int64_t* src_row0, int max_new, const uint8_t* k_signs, const uint8_t* v_signs,

@@ -107,6 +107,8 @@ def lib() -> C.CDLL:
     L.kvq_rot_queries.restype = I32
     L.kvq_rot_back.argtypes = [G, I32, I32, P, P, P]
     L.kvq_rot_back.restype = I32
+    L.kvq_rot_decode_prepare.argtypes = [G, I32, I32, P, P, P, P, I64, I64, P, P, P, P, P, P, P]
+    L.kvq_rot_decode_prepare.restype = I32
     L.kvq_read_probe.argtypes = [P, I64, P, I32, P]
     L.kvq_read_probe.restype = I32
     if L.kvq_version() != LAYOUT_VERSION:
@@ -121,7 +123,8 @@ EXPORTS = ["kvq_version", "kvq_status_string", "kvq_tile_bytes", "kvq_cache_byte
            "kvq_decode_partials", "kvq_merge_partials", "kvq_decode_n_split", "kvq_decode_plan",
            "kvq_decode_step_partials", "kvq_decode_step", "kvq_window_decode_attn", "kvq_window_decode_step",
            "kvq_window_workspace_bytes", "kvq_prefill_plan", "kvq_prefill_workspace_bytes",
-           "kvq_packed_prefill_attn", "kvq_read_probe", "kvq_rot_quantize_pack", "kvq_rot_queries", "kvq_rot_back"]
+           "kvq_packed_prefill_attn", "kvq_read_probe", "kvq_rot_quantize_pack", "kvq_rot_queries", "kvq_rot_back",
+           "kvq_rot_decode_prepare"]
 
 
 def status_string(st: int) -> str:
@@ -451,6 +454,18 @@ def rot_back(g: Geom, out: torch.Tensor, v_signs: torch.Tensor, stream=None):
     assert out.dtype == torch.float32 and out.is_contiguous()
     _check("kvq_rot_back", lib().kvq_rot_back(C.byref(g), out.shape[1], out.shape[0], _ptr(out), _ptr(v_signs),
                                                _stream(stream)))
+
+
+def rot_decode_prepare(g: Geom, q: torch.Tensor, q_rot: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                       cache: torch.Tensor, seq_byte_off: torch.Tensor, seq_len: torch.Tensor, k_signs: torch.Tensor,
+                       v_signs: torch.Tensor | None, v_sigma: torch.Tensor | None, stream=None):
+    """One launch: the new token [n_seq, n_kv, 128] packed (rotated) at slot seq_len - 1, and
+    q [n_seq, n_q, 128] rotated into q_rot."""
+    assert q.dtype == torch.float16 and q.is_contiguous() and q_rot.is_contiguous() and q_rot.dtype == torch.float16
+    ss, sh = _step_rows(k_new, v_new)
+    _check("kvq_rot_decode_prepare", lib().kvq_rot_decode_prepare(
+        C.byref(g), q.shape[1], q.shape[0], _ptr(q), _ptr(q_rot), _ptr(k_new), _ptr(v_new), ss, sh, _ptr(cache),
+        _ptr(seq_byte_off), _ptr(seq_len), _ptr(k_signs), _ptr(v_signs), _ptr(v_sigma), _stream(stream)))
 
 
 def read_probe(buf: torch.Tensor, sink: torch.Tensor, n_blocks: int, stream=None):

@@ -185,6 +185,14 @@ def test_host_validation_rejects_before_gpu():
     assert L.kvq_rot_back(C.byref(good), 16, 1, FAKE, None, None) == -1
     assert L.kvq_rot_back(C.byref(good), 16, -1, FAKE, FAKE, None) == -1
     assert L.kvq_rot_back(C.byref(kvq.geom(2, 192, 16, 1024)), 16, 1, FAKE, FAKE, None) == -3
+    rp = lambda g_, nq=16, q=FAKE, kn=FAKE, ss=256, vsg=FAKE, vsig=FAKE: (
+        C.byref(g_), nq, 1, q, FAKE, kn, FAKE, ss, 128, FAKE, FAKE, FAKE, FAKE, vsg, vsig, None)
+    assert L.kvq_rot_decode_prepare(*rp(kvq.geom(2, 160, 3, 1024))) == -3
+    assert L.kvq_rot_decode_prepare(*rp(good, nq=3)) == -2
+    assert L.kvq_rot_decode_prepare(*rp(good, q=None)) == -1
+    assert L.kvq_rot_decode_prepare(*rp(good, vsg=None, vsig=None)) == -1
+    assert L.kvq_rot_decode_prepare(*rp(good, kn=FAKE + 2)) == -4
+    assert L.kvq_rot_decode_prepare(*rp(good, ss=255)) == -4
     # read probe (measurement helper): counts, pointers, alignment
     assert L.kvq_read_probe(FAKE, -16, FAKE, 4, None) == -1
     assert L.kvq_read_probe(FAKE, 1024, FAKE, 0, None) == -1

@@ -158,6 +158,75 @@ def test_rotated_c3_layer_full_size():
          cap=synth.ceil_to(n + 64, 64), seed=7)
 
 
+@pytest.mark.parametrize("vrot", [True, False], ids=["vrot", "vplain"])
+@pytest.mark.parametrize("pairing", [kvq.PAIR_HALF, kvq.PAIR_INTERLEAVED], ids=["half", "interleaved"])
+@pytest.mark.parametrize("kb,vb", [(192, 3), (512, 8), (64, 1)], ids=["k3v3", "k8v8", "k1v1"])
+def test_rotated_decode_prepare(kb, vb, pairing, vrot):
+    """kvq_rot_decode_prepare: the new token of each sequence packed at slot seq_len - 1
+    (bytes equal to the oracle's packing of every token; lengths 0, 63, 64, 127 and 300
+    before the step, so the token opens a tile, fills one, or lands mid-tile) and the
+    queries rotated (bits equal to the oracle's), then attention within 2e-3."""
+    H, grp = 2, 4
+    lens = [0, 63, 64, 127, 300]
+    say("rot prepare: kb %d vb %d pairing %d vrot %d" % (kb, vb, pairing, vrot))
+    seqs = _batch(H, grp, kb, vb, [n + 1 for n in lens], seed=31)
+    ksg = synth.rot_signs(H, seed=31)
+    vsg = synth.rot_signs(H, seed=32) if vrot else None
+    vsig = None
+    if not vrot:
+        ev = np.zeros((H, D // 2, 2), np.uint64)
+        for _, V, _ in seqs:
+            oracle.block_energy(V.numpy(), pairing, ev)
+        _, vsig = oracle.allocate(ev, vb * (D // 2), oracle.UNIFORM)
+    cap = 384
+    g = kvq.geom(H, kb, vb, cap, rope_pairing=pairing)
+    ogeom = oracle.Geometry(H, kb, vb, cap, pairing=pairing)
+    region = kvq.cache_bytes(g)
+    S = len(lens)
+    cache = torch.zeros(S * region, dtype=torch.uint8, device="cuda")
+    off = torch.arange(S, dtype=torch.int64, device="cuda") * region
+    head = [(K[:n], V[:n], q) for (K, V, q), n in zip(seqs, lens) if n > 0]
+    idx = [i for i, n in enumerate(lens) if n > 0]
+    # the prefill (sequences with tokens), one call
+    rows = torch.cat([x[0] for x in head], 0).cuda()
+    vrows = torch.cat([x[1] for x in head], 0).cuda()
+    first = torch.zeros(S, dtype=torch.int64, device="cuda")
+    nn = torch.tensor(lens, dtype=torch.int32, device="cuda")
+    row0 = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    kvq.rot_quantize_pack(g, rows, vrows, first, nn, torch.tensor(row0, device="cuda"),
+                          max(lens), ksg.cuda(), None if vsg is None else vsg.cuda(),
+                          None if vsig is None else torch.from_numpy(vsig).cuda(), cache, off)
+    # the step: new tokens and queries
+    kn = torch.stack([K[n] for (K, _, _), n in zip(seqs, lens)]).cuda()
+    vn = torch.stack([V[n] for (_, V, _), n in zip(seqs, lens)]).cuda()
+    q = torch.stack([x[2] for x in seqs]).cuda().contiguous()
+    q_rot = torch.empty_like(q)
+    seq_len = torch.tensor([n + 1 for n in lens], dtype=torch.int32, device="cuda")
+    kvq.rot_decode_prepare(g, q, q_rot, kn, vn, cache, off, seq_len, ksg.cuda(), None if vsg is None else vsg.cuda(),
+                           None if vsig is None else torch.from_numpy(vsig).cuda())
+    oc = np.zeros(S * region, np.uint8)
+    for i, (K, V, _) in enumerate(seqs):
+        oracle.quantize_pack_rot(ogeom, oc[i * region:(i + 1) * region], K.numpy(), V.numpy(), 0, ksg.numpy(),
+                                 None if vsg is None else vsg.numpy(), vsig)
+    _check_bytes(cache, oc, "prepare")
+    qc, qr = q.cpu().numpy(), q_rot.cpu().numpy().view(np.uint16)
+    for i in range(S):
+        for h in range(H * grp):
+            np.testing.assert_array_equal(qr[i, h], oracle.rot_query(qc[i, h], ksg[h // grp].numpy()))
+    kbits = torch.full((H, D // 2), kb // (D // 2), dtype=torch.uint8, device="cuda")
+    ksig = torch.full((H, D // 2), float(SIG_ROT), dtype=torch.float32, device="cuda")
+    vs = ksig if vrot else torch.from_numpy(vsig).cuda()
+    ws = torch.empty(kvq.decode_workspace_bytes(g, H * grp, S, cap) // 4 + 4, dtype=torch.float32, device="cuda")
+    out = torch.empty(S, H * grp, D, dtype=torch.float32, device="cuda")
+    kvq.packed_decode_attn(g, q_rot, cache, off, seq_len, cap, kbits, ksig, vs, out, ws)
+    if vrot:
+        kvq.rot_back(g, out, vsg.cuda())
+    ref = np.stack([oracle.decode_attention_rot(ogeom, oc[i * region:(i + 1) * region], qc[i], lens[i] + 1,
+                                                ksg.numpy(), None if vsg is None else vsg.numpy(), vsig)
+                    for i in range(S)])
+    say("worst rel %.2e" % check_attention(out.cpu().numpy(), ref))
+
+
 def test_rot_abi_rejections():
     g = kvq.geom(2, 160, 3, 128)  # 160 is not a multiple of 64
     q = torch.zeros(1, 4, D, dtype=torch.float16, device="cuda")
