@@ -103,7 +103,7 @@ struct MfmaSmem {
     uint32_t arec[16];                // the appended token's K record, assembled
 };
 // the waves' unnormalised outputs [wave][coordinate][head], combined at the end in
-// the (then idle) tile buffers
+// the (then idle) tile buffers: the shared buffers hold at least this much
 typedef float WaveOut[kWaves][kHeadDim][8];
 
 
@@ -686,30 +686,44 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     for (int ct = 0; ct < 8; ++ct)
 #pragma unroll
         for (int j = 0; j < 4; ++j) o[ct][j] = xor32_sum(o[ct][j]);
-    WaveOut& wo = *(WaveOut*)bufs;
-    __syncthreads();  // every wave is done with its tile buffers
+    // each wave's unnormalised output [coordinate][head]: in the wave's own tile buffers
+    // when they hold it (its LDS reads of them are behind it, so no barrier first), else
+    // in the shared tile buffers once every wave is done with them
+    constexpr int kOutBytes = (int)sizeof(float) * kHeadDim * 8;
+    constexpr bool kOwnOut = WB >= kOutBytes;
+    constexpr int kOutStride = kOwnOut ? WB : kOutBytes;
+    static_assert(kWaves * kOutStride <= BUF, "the wave outputs fit the tile buffers");
+    if (!kOwnOut) __syncthreads();
     if (lane < 8) { sm.wm[lane][wave] = mref + vexp; sm.wl[lane][wave] = lsum; }
     if (lane < 32) {
         // lane l holds rows 4*(l/16) .. +3 (heads) of coordinates 16*ct + l%16
+        float* wo = (float*)(bufs + wave * kOutStride);
 #pragma unroll
         for (int ct = 0; ct < 8; ++ct)
-            *(float4*)&wo[wave][16 * ct + (lane & 15)][4 * (lane >> 4)] = float4{o[ct][0], o[ct][1], o[ct][2], o[ct][3]};
+            *(float4*)&wo[(16 * ct + (lane & 15)) * 8 + 4 * (lane >> 4)] = float4{o[ct][0], o[ct][1], o[ct][2], o[ct][3]};
     }
     __syncthreads();
     // merge the four waves: thread (half, c) writes coordinate c of heads 4*half .. 4*half+3
     const int D2 = kHeadDim + 2;
     const int c = tid & (kHeadDim - 1), h0 = 4 * (tid >> 7);
     if (h0 < g) {
-        float4 ow[kWaves];
+        // every LDS read of the combine goes out before any is used
+        float4 ow[kWaves], mwj[4], lwj[4];
 #pragma unroll
-        for (int w = 0; w < kWaves; ++w) ow[w] = *(const float4*)&wo[w][c][h0];
+        for (int w = 0; w < kWaves; ++w) ow[w] = *(const float4*)((const float*)(bufs + w * kOutStride) + c * 8 + h0);
+#pragma unroll
+        for (int j = 0; j < 4; ++j) {
+            mwj[j] = *(const float4*)sm.wm[h0 + j];
+            lwj[j] = *(const float4*)sm.wl[h0 + j];
+        }
         const float vs = sm.vsig[c];
+        float* const part0 = ws + (((int64_t)s * n_q + kvh * g + h0) * n_split + split) * D2;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
             const int hh = h0 + j;
             if (hh >= g) break;
-            const float4 mw = *(const float4*)sm.wm[hh];
-            const float4 lw = *(const float4*)sm.wl[hh];
+            const float4 mw = mwj[j];
+            const float4 lw = lwj[j];
             const float M = fmaxf(fmaxf(mw.x, mw.y), fmaxf(mw.z, mw.w));
             float l = 0.f, acc = 0.f;
             if (M != -INFINITY) {
@@ -722,7 +736,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
                 const float o3 = j == 0 ? ow[3].x : j == 1 ? ow[3].y : j == 2 ? ow[3].z : ow[3].w;
                 acc = f0 * o0 + f1 * o1 + f2 * o2 + f3 * o3;
             }
-            float* part = ws + (((int64_t)s * n_q + kvh * g + hh) * n_split + split) * D2;
+            float* part = part0 + (int64_t)j * n_split * D2;
             part[2 + c] = acc * vs;
             if (c == 0) { part[0] = M; part[1] = l; }
         }
