@@ -8,13 +8,14 @@
 // Rotation R = H diag(sg) / sqrt(128), H the Sylvester Hadamard matrix.  A binary16
 // row x gives the exact sums S = H (sg * x) = sqrt(128) R x: every binary16 value is
 // an integer count of 2^-24 below 2^40, so the sums are exact in 64-bit integers
-// (|S| < 2^47); each is rounded once to binary32.  Codes compare S with the token
-// norm times the Gaussian thresholds: code = #{j : S_i >= RN32(s * t_j)} (the
-// normalised rotated coordinate S_i / s against the codebook of N(0, 1)).
+// (|S| < 2^47) and in binary64; each is rounded once to binary32.  Codes compare S
+// with the token norm times the Gaussian thresholds: code = #{j : S_i >= RN32(s * t_j)}
+// (the normalised rotated coordinate S_i / s against the codebook of N(0, 1)).
 //
-// Lane l of a wave holds coordinates 2l and 2l + 1, so the transform's first
-// butterfly stage is lane-local and stage h = 2^k (k >= 1) pairs lane l with lane
-// l ^ 2^(k-1).
+// The one-token paths (queries, a decode step's new token, outputs) give a row one
+// wave: lane l holds coordinates 2l and 2l + 1, so the transform's first butterfly
+// stage is lane-local and stage h = 2^k (k >= 1) pairs lane l with lane l ^ 2^(k-1).
+// The bulk quantizer gives a row 16 lanes (below).
 #include "kvq_internal.h"
 
 #pragma clang fp contract(off)
@@ -86,13 +87,97 @@ __device__ __forceinline__ void rotated_pair(uint32_t pair, const uint8_t* __res
     s1 = units_to_f32(b);
 }
 
+// ---------------------------------------------------------------- 16 lanes per token
+// The bulk quantizer gives each token 16 lanes of a row of the wave: lane j holds
+// coordinates 8j .. 8j + 7.  Cross-lane steps pair lane j with j ^ 1, 2, 4, 8 inside
+// the row of 16 through DPP: quad permutations for 1 and 2, a rotate by 8 for 8, and
+// for 4 two rotates (by 12 for lanes 0-3 and 8-11, by 4 for lanes 4-7 and 12-15)
+// selected by the DPP bank mask.
+template <int CTRL>
+__device__ __forceinline__ uint32_t dpp_row(uint32_t x) {
+    return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, CTRL, 0xf, 0xf, false);
+}
+template <int B>
+__device__ __forceinline__ uint32_t row_xor(uint32_t x) {
+    if (B == 0) return dpp_row<0xB1>(x);   // quad_perm [1, 0, 3, 2]
+    if (B == 1) return dpp_row<0x4E>(x);   // quad_perm [2, 3, 0, 1]
+    if (B == 3) return dpp_row<0x128>(x);  // row_ror:8
+    const int t = __builtin_amdgcn_update_dpp(0, (int)x, 0x12C, 0xf, 0x5, false);  // row_ror:12, banks 0, 2
+    return (uint32_t)__builtin_amdgcn_update_dpp(t, (int)x, 0x124, 0xf, 0xA, false);  // row_ror:4, banks 1, 3
+}
+template <int B>
+__device__ __forceinline__ double row_xor64(double v) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint64_t lo = row_xor<B>((uint32_t)u), hi = row_xor<B>((uint32_t)(u >> 32));
+    return __builtin_bit_cast(double, lo | (hi << 32));
+}
+template <int B>
+__device__ __forceinline__ float row_xorf(float v) {
+    return __builtin_bit_cast(float, row_xor<B>(__builtin_bit_cast(uint32_t, v)));
+}
+
+// the token norm from the lane's eight binary16 values: the same balanced pairwise
+// binary32 tree as token_norm (levels 1-3 inside the lane, 4-7 across lanes j ^ 1, 2,
+// 4, 8; after level 5 a lane's four-lane group is uniform, so any lane of the other
+// group completes level 6)
+__device__ __forceinline__ float token_norm8(const uint32_t (&w)[4]) {
+    float l1[4];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float a = h2f(w[i] & 0xffffu), b = h2f(w[i] >> 16);
+        l1[i] = a * a + b * b;  // both squares exact in binary32
+    }
+    float t = (l1[0] + l1[1]) + (l1[2] + l1[3]);
+    t = t + row_xorf<0>(t);
+    t = t + row_xorf<1>(t);
+    t = t + row_xorf<2>(t);
+    t = t + row_xorf<3>(t);
+    return sqrtf(t);
+}
+
+// S = H (sg * x) over the token's 128 values, the lane's eight in a[]: exact in
+// binary64 (each partial sum is a multiple of 2^-24 below 2^23, within 47 bits)
+__device__ __forceinline__ void fwht128(double (&a)[8], int j) {
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (!(i & h)) {
+                const double u = a[i], v = a[i + h];
+                a[i] = u + v;
+                a[i + h] = u - v;
+            }
+    // lane bit b: the lane without it keeps u + v, the lane with it v' - u' (its own
+    // value subtracted from its partner's), both exact: p + sgn * a
+    const double s0 = (j & 1) ? -1.0 : 1.0, s1 = (j & 2) ? -1.0 : 1.0, s2 = (j & 4) ? -1.0 : 1.0,
+                 s3 = (j & 8) ? -1.0 : 1.0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = __builtin_fma(s0, a[i], row_xor64<0>(a[i]));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = __builtin_fma(s1, a[i], row_xor64<1>(a[i]));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = __builtin_fma(s2, a[i], row_xor64<2>(a[i]));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = __builtin_fma(s3, a[i], row_xor64<3>(a[i]));
+}
+
+// binary16 values (sign bits flipped by neg) as binary64
+__device__ __forceinline__ void halves_to_f64(const uint32_t (&w)[4], const uint32_t (&neg)[4], double (&a)[8]) {
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const uint32_t x = w[i] ^ neg[i];
+        a[2 * i] = (double)h2f(x & 0xffffu);
+        a[2 * i + 1] = (double)h2f(x >> 16);
+    }
+}
+
 // ---------------------------------------------------------------- quantize + pack
 // One workgroup (4 waves) per (sequence, KV head, tile touched by the call).  Phase 1:
-// each wave takes tokens p = wave, wave + 4, ...; lane l forms the token norm from its
-// coordinate pair (the pairwise tree), the rotated sums of coordinates 2l, 2l + 1
-// and their codes, written to LDS code rows.  Phase 2: the tile's K records (every
-// block at the same width, so field f of the K order is coordinate c_f = p(f/2) or
-// q(f/2) at bit w*f), V runs and scales, one thread per word.
+// each wave takes four tokens at a time, 16 lanes each (lane j: coordinates 8j ..
+// 8j + 7): the token norm (the pairwise tree), the rotated sums and their codes,
+// written to LDS code rows.  Phase 2: the tile's K records (every block at the same
+// width, so field f of the K order is coordinate c_f = p(f/2) or q(f/2) at bit w*f),
+// V runs and scales, one thread per word.
 constexpr int kRotWaves = 4;
 constexpr int kRotThreads = 64 * kRotWaves;
 
@@ -117,8 +202,8 @@ __global__ __launch_bounds__(kRotThreads) void rot_quantize_kernel(
     const int RW = (int)(SK / 4), VW = 2 * v_bits;
     uint8_t* tile = cache + seq_byte_off[s] + ((int64_t)h * (capacity / kTile) + tau) * TB;
 
-    __shared__ uint8_t s_kc[kTile][kHeadDim + 4];  // codes [slot][coordinate]
-    __shared__ uint8_t s_vc[kTile][kHeadDim + 4];
+    __shared__ __attribute__((aligned(16))) uint8_t s_kc[kTile][kHeadDim + 8];  // codes [slot][coordinate]
+    __shared__ __attribute__((aligned(16))) uint8_t s_vc[kTile][kHeadDim + 8];
     __shared__ float s_ks[kTile], s_vs[kTile];
     __shared__ float s_thr[512];
     __shared__ uint8_t s_ksg[kHeadDim], s_vsg[kHeadDim];
@@ -132,46 +217,68 @@ __global__ __launch_bounds__(kRotThreads) void rot_quantize_kernel(
         const int blk = pairing == KVQ_PAIR_HALF ? (tid & (kMaxBlocks - 1)) : (tid >> 1);
         s_vsig[tid] = vrot ? 1.f : v_sigma[h * kMaxBlocks + blk];
     }
-    for (int i = tid; i < kTile * (kHeadDim + 4) / 4; i += kRotThreads) {
+    for (int i = tid; i < kTile * (kHeadDim + 8) / 4; i += kRotThreads) {
         ((uint32_t*)s_kc)[i] = 0u;
         ((uint32_t*)s_vc)[i] = 0u;
     }
     __syncthreads();
 
-    // ---- phase 1: norms, rotated sums, codes (lane: coordinates 2l, 2l + 1); the
-    // wave's rows are all requested before the first is used
-    const int64_t row0 = src_row0[s] + (tile0 - first);
-    constexpr int kPer = kTile / kRotWaves;
-    uint32_t kpr[kPer], vpr[kPer];
+    // ---- phase 1: norms, rotated sums, codes; four tokens per wave at a time (lanes
+    // 16q .. 16q + 15 take token q of the four), every row requested before the first
+    // is used
+    const int j = lane & 15, tq = lane >> 4;
+    uint32_t kneg[4], vneg[4];  // binary16 sign bits of the lane's coordinates' signs
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int p = lo_p + wave + kRotWaves * i;
-        const int64_t r = row0 + min(p, hi_p - 1);  // a valid row for every load
-        kpr[i] = *(const uint32_t*)(kx + r * stride_tok + (int64_t)h * stride_head + 2 * lane);
-        vpr[i] = *(const uint32_t*)(vx + r * stride_tok + (int64_t)h * stride_head + 2 * lane);
+    for (int i = 0; i < 4; ++i) {
+        kneg[i] = (s_ksg[8 * j + 2 * i] ? 0x8000u : 0u) | (s_ksg[8 * j + 2 * i + 1] ? 0x80000000u : 0u);
+        vneg[i] = (s_vsg[8 * j + 2 * i] ? 0x8000u : 0u) | (s_vsg[8 * j + 2 * i + 1] ? 0x80000000u : 0u);
+    }
+    constexpr int kRounds = kTile / (4 * kRotWaves);
+    const int64_t row0 = src_row0[s] + (tile0 - first);
+    uint32_t kw[kRounds][4], vw[kRounds][4];
+#pragma unroll
+    for (int r = 0; r < kRounds; ++r) {
+        const int p = lo_p + 4 * (kRounds * wave + r) + tq;
+        const int64_t rr = row0 + min(p, hi_p - 1);  // a valid row for every load
+        const uint32_t* kr = (const uint32_t*)(kx + rr * stride_tok + (int64_t)h * stride_head + 8 * j);
+        const uint32_t* vr = (const uint32_t*)(vx + rr * stride_tok + (int64_t)h * stride_head + 8 * j);
+#pragma unroll
+        for (int i = 0; i < 4; ++i) {
+            kw[r][i] = kr[i];
+            vw[r][i] = vr[i];
+        }
     }
 #pragma unroll
-    for (int i = 0; i < kPer; ++i) {
-        const int p = lo_p + wave + kRotWaves * i;
-        if (p >= hi_p) break;
-        const uint32_t kp = kpr[i], vp = vpr[i];
-        const float sk = token_norm(kp), sv = token_norm(vp);
-        float k0, k1;
-        rotated_pair(kp, s_ksg, lane, k0, k1);
-        s_kc[p][2 * lane] = (uint8_t)code_of(s_thr, k0, wk, 1.f, sk);
-        s_kc[p][2 * lane + 1] = (uint8_t)code_of(s_thr, k1, wk, 1.f, sk);
-        float v0, v1;
+    for (int r = 0; r < kRounds; ++r) {
+        const int p0 = lo_p + 4 * (kRounds * wave + r);
+        if (p0 >= hi_p) break;
+        const int p = p0 + tq;
+        const float sk = token_norm8(kw[r]), sv = token_norm8(vw[r]);
+        double a[8];
+        halves_to_f64(kw[r], kneg, a);
+        fwht128(a, j);
+        uint32_t kc[2] = {0u, 0u}, vc[2] = {0u, 0u};
+#pragma unroll
+        for (int i = 0; i < 8; ++i) kc[i >> 2] |= code_of(s_thr, (float)a[i], wk, 1.f, sk) << (8 * (i & 3));
         if (vrot) {
-            rotated_pair(vp, s_vsg, lane, v0, v1);
+            halves_to_f64(vw[r], vneg, a);
+            fwht128(a, j);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) vc[i >> 2] |= code_of(s_thr, (float)a[i], v_bits, 1.f, sv) << (8 * (i & 3));
         } else {
-            v0 = h2f(vp & 0xffffu);
-            v1 = h2f(vp >> 16);
+#pragma unroll
+            for (int i = 0; i < 8; ++i) {
+                const uint32_t x = (vw[r][i >> 1] >> (16 * (i & 1))) & 0xffffu;
+                vc[i >> 2] |= code_of(s_thr, h2f(x), v_bits, s_vsig[8 * j + i], sv) << (8 * (i & 3));
+            }
         }
-        s_vc[p][2 * lane] = (uint8_t)code_of(s_thr, v0, v_bits, s_vsig[2 * lane], sv);
-        s_vc[p][2 * lane + 1] = (uint8_t)code_of(s_thr, v1, v_bits, s_vsig[2 * lane + 1], sv);
-        if (lane == 0) {
-            s_ks[p] = sk;
-            s_vs[p] = sv;
+        if (p < hi_p) {
+            *(uint2*)&s_kc[p][8 * j] = uint2{kc[0], kc[1]};
+            *(uint2*)&s_vc[p][8 * j] = uint2{vc[0], vc[1]};
+            if (j == 0) {
+                s_ks[p] = sk;
+                s_vs[p] = sv;
+            }
         }
     }
     __syncthreads();
