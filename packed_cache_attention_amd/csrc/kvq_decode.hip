@@ -23,7 +23,8 @@ constexpr bool kMfmaKernel = true;
 // takes 8 coordinates of one row, so a row's merge spreads over 16 compute units;
 // its 32 split groups stride over the splits with their own running maximum,
 // sixteen splits' loads in flight at a time (512 splits in one pass).  A wave's
-// eight split groups (lanes 8 apart) combine by lane swaps, the four waves through LDS.
+// eight split groups (lanes 8 apart) combine by DPP and permlane exchanges, the four
+// waves through LDS.
 constexpr int kMergeCols = 8, kMergeGroups = 32, kMergeUnroll = 16;
 
 __device__ __forceinline__ void merge_pair(float& M, float& L, float& A, float oM, float oL, float oA) {
@@ -68,10 +69,28 @@ __global__ __launch_bounds__(kMergeCols * kMergeGroups) void merge_kernel(const 
         }
         M = mx;
     }
-    // the wave's eight split groups: lanes l, l ^ 8, l ^ 16, l ^ 32 ... share a coordinate
-#pragma unroll
-    for (int mask = kMergeCols; mask < 64; mask <<= 1)
-        merge_pair(M, L, A, __shfl_xor(M, mask), __shfl_xor(L, mask), __shfl_xor(A, mask));
+    // the wave's eight split groups: lanes l, l ^ 8, l ^ 16, l ^ 32 share a coordinate;
+    // each exchange hands both lanes the same two operands in the same order (the
+    // lower lane's first), so both hold the same merged triple
+    {
+        const float pM = dpp_ror8(M), pL = dpp_ror8(L), pA = dpp_ror8(A);
+        const bool up = (tid & 8) != 0;
+        float M0 = up ? pM : M, L0 = up ? pL : L, A0 = up ? pA : A;
+        merge_pair(M0, L0, A0, up ? M : pM, up ? L : pL, up ? A : pA);
+        M = M0; L = L0; A = A0;
+    }
+    {
+        float m0, m1, l0, l1, a0, a1;
+        pair16(M, m0, m1); pair16(L, l0, l1); pair16(A, a0, a1);
+        merge_pair(m0, l0, a0, m1, l1, a1);
+        M = m0; L = l0; A = a0;
+    }
+    {
+        float m0, m1, l0, l1, a0, a1;
+        pair32(M, m0, m1); pair32(L, l0, l1); pair32(A, a0, a1);
+        merge_pair(m0, l0, a0, m1, l1, a1);
+        M = m0; L = l0; A = a0;
+    }
     constexpr int kWavesM = kMergeCols * kMergeGroups / 64;
     __shared__ float s_m[kWavesM][kMergeCols], s_l[kWavesM][kMergeCols], s_a[kWavesM][kMergeCols];
     const int wv = tid / 64;

@@ -227,6 +227,52 @@ def test_rotated_decode_prepare(kb, vb, pairing, vrot):
     say("worst rel %.2e" % check_attention(out.cpu().numpy(), ref))
 
 
+@pytest.mark.parametrize("align", ["4byte", "16byte-oddstride"])
+@pytest.mark.parametrize("vrot", [True, False], ids=["vrot", "vplain"])
+def test_rotated_pack_from_strided_unaligned_rows(align, vrot):
+    """The rotated bulk quantizer reads each row 16 bytes per lane: rows only 4-byte
+    aligned, or token/head strides that are not multiples of 8 elements, give the
+    oracle's bytes; 150 tokens from slot 70 (a partial first tile, a whole one, a
+    partial last one) after a 70-token first call."""
+    H, grp, kb, vb, n0, n1 = 2, 4, 192, 3, 70, 150
+    say("rot pack from views %s vrot %d" % (align, vrot))
+    seqs = _batch(H, grp, kb, vb, [n0 + n1], seed=41)
+    K, V, _ = seqs[0]
+    ksg = synth.rot_signs(H, seed=41)
+    vsg = synth.rot_signs(H, seed=42) if vrot else None
+    vsig = None
+    if not vrot:
+        ev = np.zeros((H, D // 2, 2), np.uint64)
+        oracle.block_energy(V.numpy(), kvq.PAIR_HALF, ev)
+        _, vsig = oracle.allocate(ev, vb * (D // 2), oracle.UNIFORM)
+    cap = 256
+    g = kvq.geom(H, kb, vb, cap)
+    ogeom = oracle.Geometry(H, kb, vb, cap)
+    cache = torch.zeros(kvq.cache_bytes(g), dtype=torch.uint8, device="cuda")
+    off = torch.zeros(1, dtype=torch.int64, device="cuda")
+    _gpu_pack(g, [(K[:n0], V[:n0], None)], [0], ksg, vsg, vsig, cache, off)
+    lead = 2 if align == "4byte" else 8
+    width = 134 if align == "4byte" else 140
+    kb_ = torch.zeros(n0 + n1, H + 1, width, dtype=torch.float16, device="cuda")
+    vb_ = torch.zeros_like(kb_)
+    kb_[:, :H, lead:lead + D] = K.cuda()
+    vb_[:, :H, lead:lead + D] = V.cuda()
+    kv, vv = kb_[:, :H, lead:lead + D], vb_[:, :H, lead:lead + D]
+    if align == "4byte":
+        assert kv.data_ptr() % 16 != 0 and kv.data_ptr() % 4 == 0
+    else:
+        assert kv.data_ptr() % 16 == 0 and kv.stride(0) % 8 != 0
+    kvq.rot_quantize_pack(g, kv, vv, torch.tensor([n0], dtype=torch.int64, device="cuda"),
+                          torch.tensor([n1], dtype=torch.int32, device="cuda"),
+                          torch.tensor([n0], dtype=torch.int64, device="cuda"), n1, ksg.cuda(),
+                          None if vsg is None else vsg.cuda(), None if vsig is None else torch.from_numpy(vsig).cuda(),
+                          cache, off)
+    oc = np.zeros(ogeom.seq_bytes, np.uint8)
+    oracle.quantize_pack_rot(ogeom, oc, K.numpy(), V.numpy(), 0, ksg.numpy(), None if vsg is None else vsg.numpy(),
+                             vsig)
+    _check_bytes(cache, oc, "views")
+
+
 def test_rot_abi_rejections():
     g = kvq.geom(2, 160, 3, 128)  # 160 is not a multiple of 64
     q = torch.zeros(1, 4, D, dtype=torch.float16, device="cuda")
