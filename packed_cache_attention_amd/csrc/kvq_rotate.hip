@@ -12,10 +12,11 @@
 // with the token norm times the Gaussian thresholds: code = #{j : S_i >= RN32(s * t_j)}
 // (the normalised rotated coordinate S_i / s against the codebook of N(0, 1)).
 //
-// The one-token paths (queries, a decode step's new token, outputs) give a row one
-// wave: lane l holds coordinates 2l and 2l + 1, so the transform's first butterfly
-// stage is lane-local and stage h = 2^k (k >= 1) pairs lane l with lane l ^ 2^(k-1).
-// The bulk quantizer gives a row 16 lanes (below).
+// Queries and a decode step's new token give a row one wave: lane l holds coordinates
+// 2l and 2l + 1, so the transform's first butterfly stage is lane-local and stage
+// h = 2^k (k >= 1) pairs lane l with lane l ^ 2^(k-1) (the most lanes for these short,
+// latency-bound launches).  The bulk quantizer and the output back-rotation give a row
+// 16 lanes (below).
 #include "kvq_internal.h"
 
 #pragma clang fp contract(off)
@@ -50,23 +51,6 @@ __device__ __forceinline__ void fwht64(int64_t& a, int64_t& b, int lane) {
     for (int m = 1; m < 64; m <<= 1) {
         const int64_t pa = shfl_xor64(a, m), pb = shfl_xor64(b, m);
         const bool upper = lane & m;  // this lane holds the second member of each pair
-        a = upper ? pa - a : a + pa;
-        b = upper ? pb - b : b + pb;
-    }
-}
-
-// The same transform on binary32 values (the output rotated back: rounding here is
-// ordinary floating point, within the attention tolerance).
-__device__ __forceinline__ void fwht64f(float& a, float& b, int lane) {
-    {
-        const float s = a + b, d = a - b;
-        a = s;
-        b = d;
-    }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-        const float pa = __shfl_xor(a, m), pb = __shfl_xor(b, m);
-        const bool upper = lane & m;
         a = upper ? pa - a : a + pa;
         b = upper ? pb - b : b + pb;
     }
@@ -339,21 +323,56 @@ __global__ __launch_bounds__(256) void rot_query_kernel(const uint16_t* __restri
         (uint32_t)__builtin_bit_cast(uint16_t, a) | ((uint32_t)__builtin_bit_cast(uint16_t, b) << 16);
 }
 
-// out row r <- diag(sg) H out_r / sqrt(128), in place
+// The same transform on binary32 values, the lane's eight in a[] (the output rotated
+// back: rounding here is ordinary floating point, within the attention tolerance)
+__device__ __forceinline__ void fwht128f(float (&a)[8], int j) {
+#pragma unroll
+    for (int h = 1; h < 8; h <<= 1)
+#pragma unroll
+        for (int i = 0; i < 8; ++i)
+            if (!(i & h)) {
+                const float u = a[i], v = a[i + h];
+                a[i] = u + v;
+                a[i + h] = u - v;
+            }
+    const float s0 = (j & 1) ? -1.f : 1.f, s1 = (j & 2) ? -1.f : 1.f, s2 = (j & 4) ? -1.f : 1.f,
+                s3 = (j & 8) ? -1.f : 1.f;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = __builtin_fmaf(s0, a[i], row_xorf<0>(a[i]));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = __builtin_fmaf(s1, a[i], row_xorf<1>(a[i]));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = __builtin_fmaf(s2, a[i], row_xorf<2>(a[i]));
+#pragma unroll
+    for (int i = 0; i < 8; ++i) a[i] = __builtin_fmaf(s3, a[i], row_xorf<3>(a[i]));
+}
+
+// out row r <- diag(sg) H out_r / sqrt(128), in place: 16 lanes per row (lane j:
+// coordinates 8j .. 8j + 7), 16 rows per workgroup; a row's lanes exit together, so
+// the DPP exchanges of the rows left stay within live lanes
 __global__ __launch_bounds__(256) void rot_back_kernel(float* __restrict__ out, const uint8_t* __restrict__ v_signs,
                                                        int n_rows, int n_q, int g) {
-    const int lane = threadIdx.x & 63;
-    const int r = blockIdx.x * 4 + (threadIdx.x >> 6);
+    const int j = threadIdx.x & 15;
+    const int r = blockIdx.x * 16 + (threadIdx.x >> 4);
     if (r >= n_rows) return;
     const int kvh = (r % n_q) / g;
-    float2* row = (float2*)(out + (int64_t)r * kHeadDim);
-    const float2 y = row[lane];
-    float a = y.x, b = y.y;
-    fwht64f(a, b, lane);
-    const uint8_t* sg = v_signs + kvh * kHeadDim;
-    a *= kRotSigma;
-    b *= kRotSigma;
-    row[lane] = float2{sg[2 * lane] ? -a : a, sg[2 * lane + 1] ? -b : b};
+    float2* row = (float2*)(out + (int64_t)r * kHeadDim + 8 * j);
+    float a[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+        const float2 y = row[i];
+        a[2 * i] = y.x;
+        a[2 * i + 1] = y.y;
+    }
+    fwht128f(a, j);
+    const uint8_t* sg = v_signs + kvh * kHeadDim + 8 * j;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+        const float x = a[i] * kRotSigma;
+        a[i] = sg[i] ? -x : x;
+    }
+#pragma unroll
+    for (int i = 0; i < 4; ++i) row[i] = float2{a[2 * i], a[2 * i + 1]};
 }
 
 // ---------------------------------------------------------------- decode-step preparation
@@ -475,7 +494,7 @@ hipError_t launch_rot_queries(const uint16_t* q, uint16_t* qr, const uint8_t* k_
 }
 
 hipError_t launch_rot_back(float* out, const uint8_t* v_signs, int n_rows, int n_q, int g, hipStream_t st) {
-    hipLaunchKernelGGL(rot_back_kernel, dim3((n_rows + 3) / 4), dim3(256), 0, st, out, v_signs, n_rows, n_q, g);
+    hipLaunchKernelGGL(rot_back_kernel, dim3((n_rows + 15) / 16), dim3(256), 0, st, out, v_signs, n_rows, n_q, g);
     return hipGetLastError();
 }
 
