@@ -24,13 +24,14 @@ constexpr bool kMfmaKernel = true;
 // its 32 split groups stride over the splits with their own running maximum,
 // sixteen splits' loads in flight at a time (512 splits in one pass).  A wave's
 // eight split groups (lanes 8 apart) combine by DPP and permlane exchanges, the four
-// waves through LDS.
+// waves through LDS.  Weights 2^(m_j - M) use the hardware exp2 (arguments <= 0; a
+// weight below 2^-126 is negligible beside the largest, which is 1).
 constexpr int kMergeCols = 8, kMergeGroups = 32, kMergeUnroll = 16;
 
 __device__ __forceinline__ void merge_pair(float& M, float& L, float& A, float oM, float oL, float oA) {
     const float Mx = fmaxf(M, oM);
     if (Mx != -INFINITY) {
-        const float a = exp2f(M - Mx), b = exp2f(oM - Mx);
+        const float a = __builtin_amdgcn_exp2f(M - Mx), b = __builtin_amdgcn_exp2f(oM - Mx);
         L = a * L + b * oL;
         A = a * A + b * oA;
     }
@@ -49,21 +50,21 @@ __global__ __launch_bounds__(kMergeCols * kMergeGroups) void merge_kernel(const 
 #pragma unroll
         for (int u = 0; u < kMergeUnroll; ++u) {
             const int sp = sp0 + u * kMergeGroups;
-            const float* p = part + (int64_t)min(sp, n_split - 1) * D2;
-            m[u] = sp < n_split ? p[0] : -INFINITY;
-            l[u] = p[1];
-            o[u] = p[2 + c];
+            const int off = min(sp, n_split - 1) * D2;  // within the row's partials (32-bit)
+            m[u] = sp < n_split ? part[off] : -INFINITY;
+            l[u] = part[off + 1];
+            o[u] = part[off + 2 + c];
         }
         float mx = M;
 #pragma unroll
         for (int u = 0; u < kMergeUnroll; ++u) mx = fmaxf(mx, m[u]);
         if (mx == -INFINITY) continue;  // nothing attended yet in these splits
-        const float r = exp2f(M - mx);
+        const float r = __builtin_amdgcn_exp2f(M - mx);
         L *= r;
         A *= r;
 #pragma unroll
         for (int u = 0; u < kMergeUnroll; ++u) {
-            const float a = exp2f(m[u] - mx);
+            const float a = __builtin_amdgcn_exp2f(m[u] - mx);
             L += a * l[u];
             A += a * o[u];
         }
