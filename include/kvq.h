@@ -62,7 +62,7 @@ typedef enum {
 /* decode kernel choice for kvq_packed_decode_attn_ex */
 #define KVQ_DECODE_AUTO 0
 #define KVQ_DECODE_GENERIC 1     /* any widths incl. 16-bit passthrough, GQA ratio <= 16 */
-#define KVQ_DECODE_MFMA 2        /* widths 0..8, v_bits 1..8, GQA ratio <= 8 */
+#define KVQ_DECODE_MFMA 2        /* K widths 0..8 (budget <= 256), v_bits 1..8 or 16, GQA ratio <= 8 */
 
 typedef struct {
     int32_t layout_version;  /* KVQ_LAYOUT_VERSION */

@@ -17,7 +17,7 @@ OUT = os.path.join(PKG, "libkvq.so")
 BUILD = os.path.join(PKG, "_build")
 SOURCES = ["kvq_api.hip", "kvq_energy_alloc.hip", "kvq_quantize.hip", "kvq_decode.hip", "kvq_decode_mfma.hip", "kvq_prefill.hip", "kvq_rotate.hip",
            "kvq_decode_generic.hip"] + \
-    ["kvq_decode_mfma_v%d.hip" % v for v in range(1, 9)]
+    ["kvq_decode_mfma_v%d.hip" % v for v in list(range(1, 9)) + [16]]
 HIPCC = os.environ.get("HIPCC", "/opt/rocm/bin/hipcc")
 FLAGS = ["--offload-arch=gfx950", "-O3", "-std=c++17", "-fPIC", "-Wall", "-Wno-unused-function",
          # packed FP32 instructions are kept out of every kernel

@@ -35,6 +35,11 @@
 // stays below 2^15, and o and l, both relative to R, are rescaled exactly as when m
 // moves.  With value norms below 2^7 e stays 0.  Each wave loads tile n+1 while it
 // computes tile n.
+//
+// 16-bit values (the K-only mode, V = 16) are their own PV operands: each lane loads
+// its 16 slots of a coordinate's run straight from the cache into registers (three
+// batches per tile, the first in flight during QK), with value norm and block scale
+// taken as 1; only the tile's token scales pass through LDS.
 #pragma once
 #include <math.h>
 
@@ -45,6 +50,7 @@ namespace kvq {
 typedef _Float16 half8 __attribute__((ext_vector_type(8)));
 typedef float floatx4 __attribute__((ext_vector_type(4)));
 typedef float floatx16 __attribute__((ext_vector_type(16)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 
 constexpr int kMaxUnits = 24;  // 128 coordinates in 8-wide units, plus one partial unit per width class
 constexpr int kWaves = 4;
@@ -269,14 +275,19 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     const int32_t* __restrict__ seq_len, int64_t max_len, int64_t capacity, const uint8_t* __restrict__ k_bits,
     const float* __restrict__ k_sigma, const float* __restrict__ v_sigma, float scale_log2, int n_q, int g,
     int pairing, int k_budget, int tiles_per_split, int n_split, float* __restrict__ ws, AppendArgs app) {
-    constexpr int NW = (16 * V + 31) / 32;       // words of one lane's V piece
+    // 16-bit values (the K-only mode) need no decoding: the lanes load their PV operands
+    // straight into registers, and only the tile's scales are staged in LDS
+    constexpr bool V16 = V == 16;
     constexpr int SK = 4 * RD;                   // K record bytes
     constexpr int KB = kTile * SK;               // K section of a tile
-    constexpr int VB = kHeadDim * 8 * V + 2 * kTile * 4;  // V runs and scales
+    constexpr int VR = kHeadDim * 8 * V;         // V runs of a tile
+    constexpr int VB = VR + 2 * kTile * 4;       // V runs and scales
+    constexpr int VL = V16 ? 2 * kTile * 4 : VB;  // the part of them staged in LDS
     constexpr int TB = KB + VB;
     constexpr int KI = RD / 4;                   // 16-byte DMA instructions of a K section
-    constexpr int VI = (VB / 16 + 63) / 64;      // ... of a V section
-    constexpr int WB = 2 * KB + VB;              // per wave: two K buffers, one V buffer
+    constexpr int VI = (VL / 16 + 63) / 64;      // ... of a V section
+    constexpr int WB = 2 * KB + VL;              // per wave: two K buffers, one V buffer
+    constexpr int NW = (16 * V + 31) / 32;       // words of one lane's V piece
     constexpr int BUF = kWaves * WB > (int)sizeof(WaveOut) ? kWaves * WB : (int)sizeof(WaveOut);
     __shared__ MfmaSmem sm;
     __shared__ __attribute__((aligned(16))) uint8_t bufs[BUF];
@@ -371,13 +382,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         for (int k = 0; k < KI; ++k) dma16<true>(tile + lane * SK + 16 * k, wbuf_lds + kb * KB + 1024 * k);
     };
     auto dma_v = [&](int64_t tau) {
-        const uint8_t* vsec = head_base + tau * TB + KB;
+        const uint8_t* vsec = head_base + tau * TB + KB + (V16 ? VR : 0);
 #pragma unroll
         for (int j = 0; j < VI; ++j) {
             const int ch = 64 * j + lane;
-            if (64 * j + 63 < VB / 16 || ch < VB / 16) dma16<true>(vsec + 16 * ch, wbuf_lds + 2 * KB + 1024 * j);
+            if (64 * j + 63 < VL / 16 || ch < VL / 16) dma16<true>(vsec + 16 * ch, wbuf_lds + 2 * KB + 1024 * j);
         }
     };
+    // 16-bit values: the lane's PV operands for coordinates 16*ct + row, ct in
+    // [C0, C1), slots 16*grp .. 16*grp + 15 (32 bytes of each coordinate's run),
+    // straight into registers.  They go out in three batches -- before QK, once QK is
+    // done, once the weights are -- so that no more are held than the phase allows.
+    constexpr int kPre = 3, kMid = 3;  // coordinate tiles of the first two batches
+    auto load_v16 = [&](int64_t tau, auto c0, auto c1, u32x4 (&vr)[16]) {
+        constexpr int C0 = decltype(c0)::value, C1 = decltype(c1)::value;
+        const u32x4* vg = (const u32x4*)(head_base + tau * TB + KB + row * (8 * V) + 2 * V * grp);
+#pragma unroll
+        for (int ct = C0; ct < C1; ++ct) {
+            vr[2 * ct] = __builtin_nontemporal_load(vg + ct * 16 * (8 * V) / 16);
+            vr[2 * ct + 1] = __builtin_nontemporal_load(vg + ct * 16 * (8 * V) / 16 + 1);
+        }
+    };
+    using IC0 = std::integral_constant<int, 0>;
+    using IC1 = std::integral_constant<int, kPre>;
+    using IC2 = std::integral_constant<int, kPre + kMid>;
+    using IC3 = std::integral_constant<int, 8>;
     constexpr bool kStageInK1 = KB >= 510 * 4;  // see the staging area below
     int64_t tau = t0 + wave;
 
@@ -464,6 +493,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         const uint32_t kcq = encode(s_thr, nk_q, my_w, my_ksig, ap_sk);
         ap_vcp = encode(s_thr, nv_p, V, my_vsig_blk, ap_sv);
         ap_vcq = encode(s_thr, nv_q, V, my_vsig_blk, ap_sv);
+        if constexpr (V16) {
+            // 16-bit values go into the cache now: the tail tile's operands are loaded
+            // from there, after the first tile's wait for every load (vmcnt counts
+            // these atomics too) -- the tail tile is this wave's alone
+            uint32_t* vrun = (uint32_t*)((uint8_t*)head_base + tail_tau * TB + KB);
+            const int vk = tail_p >> 1, vsh = 16 * (tail_p & 1);
+            if (ap_vcp != 0) atomicOr(vrun + qp * 2 * V + vk, ap_vcp << vsh);
+            if (ap_vcq != 0) atomicOr(vrun + qq * 2 * V + vk, ap_vcq << vsh);
+        }
         __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
         __builtin_amdgcn_wave_barrier();
         if (my_w > 0) {
@@ -534,6 +572,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         rec[RD] = 0;
         rec[RD + 1] = 0;
         kb ^= 1;
+        // 16-bit values: the next K section (into the buffer the previous tile's records
+        // left), then the first half of this tile's value operands, both in flight
+        // during QK; loads complete in issue order, so the operands' own waits never
+        // wait for the DMA
+        u32x4 vr[16];
+        if constexpr (V16) {
+            if (more) dma_k(tau + kWaves, kb);
+            load_v16(tau, IC0{}, IC1{}, vr);
+        }
         // ---- QK: this lane's token, 8 fields of one width class per instruction
         floatx16 acc0 = {}, acc1 = {};
         qk_class<8, RD>(sm, rec, cstart[8], cunits[8], cubase[8], qb, qmask, acc0, acc1);
@@ -548,13 +595,31 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[i] = acc0[i] + acc1[i];
         // ---- V section landed (scales, runs); the next K section then goes out (into
-        // the K buffer this tile's records left), behind this tile's V in the queue
-        __builtin_amdgcn_s_waitcnt(wait_vm(0));
-        __builtin_amdgcn_wave_barrier();
-        if (more) dma_k(tau + kWaves, kb);
+        // the K buffer this tile's records left), behind this tile's V in the queue.
+        // 16-bit values: the scales landed (the next K section and the 16 operand loads
+        // went out after them)
+        if constexpr (V16) {
+            if (more) __builtin_amdgcn_s_waitcnt(wait_vm(2 * kPre + KI));
+            else __builtin_amdgcn_s_waitcnt(wait_vm(2 * kPre));
+            __builtin_amdgcn_wave_barrier();
+            load_v16(tau, IC1{}, IC2{}, vr);
+        } else {
+            __builtin_amdgcn_s_waitcnt(wait_vm(0));
+            __builtin_amdgcn_wave_barrier();
+            if (more) dma_k(tau + kWaves, kb);
+        }
         uint8_t* vsec = wbuf + 2 * KB;
-        const float* scl = (const float*)(vsec + kHeadDim * 8 * V);
-        if (tail_here) {  // the appended V codes and scales into the LDS copy
+        const float* scl = (const float*)(vsec + (V16 ? 0 : VR));
+        if constexpr (V16) {
+            if (tail_here) {  // the appended scales into the LDS copy (its values: below)
+                if (lane == 0) {
+                    ((float*)scl)[tail_p] = ap_sk;
+                    ((float*)scl)[kTile + tail_p] = ap_sv;
+                }
+                __builtin_amdgcn_s_waitcnt(kWaitLgkm0);
+                __builtin_amdgcn_wave_barrier();
+            }
+        } else if (tail_here) {  // the appended V codes and scales into the LDS copy
             const int vb = tail_p * V, vk = vb >> 5, vsh = vb & 31;
 #pragma unroll
             for (int f = 0; f < 2; ++f) {
@@ -591,10 +656,15 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         for (int i = 1; i < 16; ++i) tm = fmaxf(tm, z[i]);
         tm = xor32_max(xor16_max(tm));
         float sv[16];
+        if constexpr (V16) {  // 16-bit values are the values themselves (no norm, no block scale)
 #pragma unroll
-        for (int i = 0; i < 4; ++i) {
-            const float4 b = *(const float4*)(scl + kTile + 16 * grp + 4 * i);
-            sv[4 * i] = b.x; sv[4 * i + 1] = b.y; sv[4 * i + 2] = b.z; sv[4 * i + 3] = b.w;
+            for (int i = 0; i < 16; ++i) sv[i] = 1.f;
+        } else {
+#pragma unroll
+            for (int i = 0; i < 4; ++i) {
+                const float4 b = *(const float4*)(scl + kTile + 16 * grp + 4 * i);
+                sv[4 * i] = b.x; sv[4 * i + 1] = b.y; sv[4 * i + 2] = b.z; sv[4 * i + 3] = b.w;
+            }
         }
         float smax = sv[0];
 #pragma unroll
@@ -636,17 +706,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         }
         lrun += psum;
         // ---- PV: B operand = 16 consecutive slots of coordinate 16*ct + lane%16
+        if constexpr (V16) {
+            load_v16(tau, IC2{}, IC3{}, vr);
 #pragma unroll
-        for (int ct = 0; ct < 8; ++ct) {
-            const int byte0 = (16 * ct + row) * 8 * V + 2 * V * grp;
-            const uint32_t* wv = (const uint32_t*)(vsec + (byte0 & ~3));
-            uint32_t vraw[NW + 1];
+            for (int ct = 0; ct < 8; ++ct) {
+                H8 b0, b1;
 #pragma unroll
-            for (int k = 0; k <= NW; ++k) vraw[k] = wv[k];
-            H8 b0, b1;
-            decode_v<V>(sm.tab, vraw, (uint32_t)(byte0 & 3) * 8, b0, b1);
-            o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[0].h, b0.h, o[ct], 0, 0, 0);
-            o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[1].h, b1.h, o[ct], 0, 0, 0);
+                for (int k = 0; k < 4; ++k) { b0.u[k] = vr[2 * ct][k]; b1.u[k] = vr[2 * ct + 1][k]; }
+                o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[0].h, b0.h, o[ct], 0, 0, 0);
+                o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[1].h, b1.h, o[ct], 0, 0, 0);
+            }
+        } else {
+#pragma unroll
+            for (int ct = 0; ct < 8; ++ct) {
+                const int byte0 = (16 * ct + row) * 8 * V + 2 * V * grp;
+                const uint32_t* wv = (const uint32_t*)(vsec + (byte0 & ~3));
+                uint32_t vraw[NW + 1];
+#pragma unroll
+                for (int k = 0; k <= NW; ++k) vraw[k] = wv[k];
+                H8 b0, b1;
+                decode_v<V>(sm.tab, vraw, (uint32_t)(byte0 & 3) * 8, b0, b1);
+                o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[0].h, b0.h, o[ct], 0, 0, 0);
+                o[ct] = __builtin_amdgcn_mfma_f32_16x16x32_f16(pa[1].h, b1.h, o[ct], 0, 0, 0);
+            }
         }
         // the V buffer is free once its reads have returned
         if (more) {
@@ -663,7 +745,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         uint32_t* vrun = (uint32_t*)(tile + KB);
         const int vb = tail_p * V, vk = vb >> 5, vsh = vb & 31;
 #pragma unroll
-        for (int f = 0; f < 2; ++f) {
+        for (int f = 0; f < 2 && !V16; ++f) {  // (16-bit values: written in the prologue)
             const uint32_t code = f ? ap_vcq : ap_vcp;
             uint32_t* run = vrun + (f ? qq : qp) * 2 * V;
             if (code != 0) {
@@ -716,7 +798,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
             mwj[j] = *(const float4*)sm.wm[h0 + j];
             lwj[j] = *(const float4*)sm.wl[h0 + j];
         }
-        const float vs = sm.vsig[c];
+        const float vs = V16 ? 1.f : sm.vsig[c];
         float* const part0 = ws + (((int64_t)s * n_q + kvh * g + h0) * n_split + split) * D2;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {

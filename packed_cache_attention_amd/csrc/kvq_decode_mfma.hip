@@ -1,6 +1,7 @@
 // kvq_decode_mfma.hip -- dispatch of the matrix-core decode kernel on the value
 // width; the kernel itself is in kvq_decode_mfma.h and its instantiations in
-// kvq_decode_mfma_v1.hip .. kvq_decode_mfma_v8.hip (compiled in parallel).
+// kvq_decode_mfma_v1.hip .. kvq_decode_mfma_v8.hip and kvq_decode_mfma_v16.hip
+// (compiled in parallel).
 #include "kvq_internal.h"
 
 namespace kvq {
@@ -14,11 +15,13 @@ hipError_t launch_mfma_v(const kvq_geom& g, const DecodePlan& plan, int n_q_head
     const uint16_t*, uint8_t*, const int64_t*, const int32_t*, int, int64_t, const uint8_t*, const float*,         \
     const float*, float, float*, hipStream_t, const AppendArgs&);
 KVQ_EXTERN(1) KVQ_EXTERN(2) KVQ_EXTERN(3) KVQ_EXTERN(4) KVQ_EXTERN(5) KVQ_EXTERN(6) KVQ_EXTERN(7) KVQ_EXTERN(8)
+KVQ_EXTERN(16)
 #undef KVQ_EXTERN
 template <int V>
 int mfma_blocks_per_cu_v(const kvq_geom& g);
 #define KVQ_EXTERN(VB) extern template int mfma_blocks_per_cu_v<VB>(const kvq_geom&);
 KVQ_EXTERN(1) KVQ_EXTERN(2) KVQ_EXTERN(3) KVQ_EXTERN(4) KVQ_EXTERN(5) KVQ_EXTERN(6) KVQ_EXTERN(7) KVQ_EXTERN(8)
+KVQ_EXTERN(16)
 #undef KVQ_EXTERN
 
 int mfma_blocks_per_cu(const kvq_geom& g) {
@@ -31,6 +34,7 @@ int mfma_blocks_per_cu(const kvq_geom& g) {
         case 6: return mfma_blocks_per_cu_v<6>(g);
         case 7: return mfma_blocks_per_cu_v<7>(g);
         case 8: return mfma_blocks_per_cu_v<8>(g);
+        case 16: return mfma_blocks_per_cu_v<16>(g);
         default: return 0;
     }
 }
@@ -45,6 +49,7 @@ hipError_t launch_decode_mfma(const kvq_geom& g, const DecodePlan& plan, int n_q
         return launch_mfma_v<VB>(g, plan, n_q_heads, q, cache, seq_byte_off, seq_len, n_seq, max_len, k_bits,  \
                                  k_sigma, v_sigma, scale_log2, partials, st, app);
         KVQ_CASE(1) KVQ_CASE(2) KVQ_CASE(3) KVQ_CASE(4) KVQ_CASE(5) KVQ_CASE(6) KVQ_CASE(7) KVQ_CASE(8)
+        KVQ_CASE(16)
 #undef KVQ_CASE
         default: return hipErrorInvalidValue;
     }

@@ -118,6 +118,8 @@ CASES = [
     ("k8v8-max", 1, 2, 130, 192, 512, 8, 0),
     ("k0v1", 1, 2, 65, 128, 0, 1, 0),
     ("konly-v16", 2, 2, 100, 128, 192, 16, 0),
+    ("konly-v16-gqa8", 2, 8, 333, 384, 192, 16, 0),
+    ("konly-v16-k4-il", 1, 6, 200, 256, 256, 16, 1),
     ("k16v16-pass", 1, 4, 90, 128, 1024, 16, 0),
     ("interleaved", 2, 2, 140, 192, 160, 4, 1),
     ("gqa16", 1, 16, 70, 128, 192, 3, 0),
@@ -330,13 +332,16 @@ def test_c3_full_size_sampled_layers(layer):
     say("c3 layer %d: attention ok, worst rel %.2e" % (layer, check_attention(r["out"], r["ref"])))
 
 
-def test_c3_full_size_fused_step_as_benchmarked():
+@pytest.mark.parametrize("v_bits", [3, 16], ids=["k3v3", "konly-v16"])
+def test_c3_full_size_fused_step_as_benchmarked(v_bits):
     """The launch the benchmark times, at its size: one 128K Qwen2.5-3B-shaped layer,
     kvq_decode_step (the new token quantized and packed inside the attention kernel,
     then the split merge) in the automatic plan with max_len = capacity; the cache
     bytes against the oracle's packing of the same token into its own copy, the
-    output against its attention over all n + 1 tokens."""
-    wl = synth.WORKLOADS["c3"]
+    output against its attention over all n + 1 tokens.  Also in the K-only value
+    mode (16-bit values), the bench's labelled K-only line."""
+    import dataclasses
+    wl = dataclasses.replace(synth.WORKLOADS["c3"], v_bits=v_bits)
     layer = 17
     say("c3 full-size fused step, layer %d" % layer)
     K, V, _ = synth.gen_layer(wl, 0, layer)
@@ -347,6 +352,7 @@ def test_c3_full_size_fused_step_as_benchmarked():
     g, region = r["g"], kvq.cache_bytes(r["g"])
     plan = kvq.decode_plan(g, wl.n_q_heads, 1, cap)
     say("plan %s" % plan)
+    assert plan["kernel"] == kvq.DECODE_MFMA
     ws = torch.empty(plan["workspace"] // 4 + 4, dtype=torch.float32, device="cuda")
     out = torch.empty(1, wl.n_q_heads, 128, dtype=torch.float32, device="cuda")
     kvq.decode_step(g, qn[None].cuda().contiguous(), kn[None].cuda().contiguous(), vn[None].cuda().contiguous(),
@@ -410,8 +416,8 @@ def test_c5_batch_append_then_attend():
 
 
 STEP_CASES = [(c[0], c[1], c[2], c[5], c[6], c[7]) for c in CASES if c[0] in
-              ("k3v3-ragged", "k2v2-ragged", "kodd-v5", "k8v8-max", "k0v1", "konly-v16", "k16v16-pass",
-               "interleaved", "gqa16")]
+              ("k3v3-ragged", "k2v2-ragged", "kodd-v5", "k8v8-max", "k0v1", "konly-v16", "konly-v16-gqa8",
+               "konly-v16-k4-il", "k16v16-pass", "interleaved", "gqa16")]
 
 
 @pytest.mark.parametrize("tiles", [0, 1, 4, 8])

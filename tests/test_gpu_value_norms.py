@@ -48,7 +48,8 @@ def _seqs(lens, H, grp, kb, vb, mode, seed, qscale=3.0):
 
 
 @pytest.mark.parametrize("mode", ["loguniform", "outliers", "both"])
-@pytest.mark.parametrize("geom", [(2, 8, 192, 3), (2, 4, 128, 2), (1, 7, 131, 5)], ids=["k3v3g8", "k2v2g4", "kodd-v5g7"])
+@pytest.mark.parametrize("geom", [(2, 8, 192, 3), (2, 4, 128, 2), (1, 7, 131, 5), (2, 8, 192, 16)],
+                         ids=["k3v3g8", "k2v2g4", "kodd-v5g7", "konly-v16g8"])
 @pytest.mark.parametrize("tiles", [0, 1])
 def test_decode_large_value_norms(mode, geom, tiles):
     H, grp, kb, vb = geom
@@ -59,12 +60,13 @@ def test_decode_large_value_norms(mode, geom, tiles):
     say("worst rel %.2e" % check_attention(r["out"], r["ref"]))
 
 
+@pytest.mark.parametrize("vb", [3, 16], ids=["v3", "v16"])
 @pytest.mark.parametrize("mode", ["outliers", "both"])
-def test_decode_step_appends_large_norm_token(mode):
+def test_decode_step_appends_large_norm_token(mode, vb):
     """The fused step packs a new token of the largest value norm inside the attention
-    kernel and attends it with the rest."""
-    say("value norms: fused step %s" % mode)
-    H, grp, kb, vb = 2, 8, 192, 3
+    kernel and attends it with the rest (3-bit and 16-bit values)."""
+    say("value norms: fused step %s v%d" % (mode, vb))
+    H, grp, kb = 2, 8, 192
     lens = (700, 129)
     seqs = _seqs([n + 1 for n in lens], H, grp, kb, vb, mode, seed=23)
     r = run_batch([(K[:n], V[:n], q) for (K, V, q), n in zip(seqs, lens)], kb, vb, 832, check_attn=False)

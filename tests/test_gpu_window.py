@@ -23,6 +23,7 @@ CASES = [
     ("k2v2-w100", 2, 4, 128, 2, 100, (300, 99), 5, kvq.DECODE_AUTO),
     ("kodd-v5-w37", 1, 3, 131, 5, 37, (90, 3), 40, kvq.DECODE_AUTO),
     ("konly-v16-w64", 2, 2, 192, 16, 64, (130, 64), 3, kvq.DECODE_AUTO),
+    ("konly-v16-g8-w32", 2, 8, 192, 16, 32, (200, 31), 10, kvq.DECODE_AUTO),
     ("k3v2-gqa7-w128", 2, 7, 192, 2, 128, (200, 129), 4, kvq.DECODE_AUTO),
     ("k3v3-w1", 1, 4, 192, 3, 1, (70, 1), 3, kvq.DECODE_AUTO),
 ]

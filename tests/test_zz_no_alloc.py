@@ -58,16 +58,26 @@ def test_noalloc_two_calls_second_smaller():
 
 def test_noalloc_generic_kernel():
     """Geometries the vector-ALU kernel serves (its query table then lives in the array
-    too): the K-only value mode (V16) and a GQA group of 12."""
+    too): K records over 64 bytes (K16 with 16-bit values) and a GQA group of 12."""
     import dataclasses
     base = synth.WORKLOADS["c3"]
-    konly = dataclasses.replace(base, name="konly", v_bits=16)
+    k16 = dataclasses.replace(base, name="k16v16", k_budget=1024, v_bits=16)
     g12 = dataclasses.replace(base, name="group12", n_q_heads=12, n_kv_heads=1)
-    for wl in (konly, g12):
+    for wl in (k16, g12):
         g = kvq.geom(wl.n_kv_heads, wl.k_budget, wl.v_bits, 1024)
         assert kvq.decode_plan(g, wl.n_q_heads, 2, 1024)["kernel"] == kvq.DECODE_GENERIC
         _compare((700, 64), seed=5, wl=wl)
         _compare((130,), seed=6, wl=wl)
+
+
+def test_noalloc_konly_values():
+    """The K-only value mode (16-bit values) on the matrix-core kernel."""
+    import dataclasses
+    konly = dataclasses.replace(synth.WORKLOADS["c3"], name="konly", v_bits=16)
+    g = kvq.geom(konly.n_kv_heads, konly.k_budget, konly.v_bits, 1024)
+    assert kvq.decode_plan(g, konly.n_q_heads, 2, 1024)["kernel"] == kvq.DECODE_MFMA
+    _compare((700, 64), seed=7, wl=konly)
+    _compare((130,), seed=8, wl=konly)
 
 
 def test_noalloc_rejects_plan_beyond_the_array():
