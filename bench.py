@@ -308,9 +308,11 @@ def workload_line(args, key, kern_name, v_bits=None, label=None, reps=60, flush=
 def rot_line(args, reps=60):
     """The rotated TurboQuant-MSE variant at the 128K Qwen2.5-3B shape (K3V3: every
     rotated coordinate at 3 bits, values rotated too).  Prefill: kvq_rot_quantize_pack
-    per layer (timed: tokens/s).  Step per layer: the new token rotated and packed and
-    the queries rotated in one launch (kvq_rot_decode_prepare), the split decode and merge over the rotated cache (the same kernels as the headline, uniform widths,
-    scales RN32(1/sqrt(128))), the outputs rotated back (kvq_rot_back); captured in a
+    per layer (timed: tokens/s).  Step per layer: the queries rotated, the new token
+    rotated and packed and the split decode over the rotated cache in one launch
+    (kvq_rot_decode_step_partials: the headline's kernel with the rotation in its
+    prologue, uniform widths, scales RN32(1/sqrt(128))), the merge, the outputs rotated
+    back (kvq_rot_back); captured in a
     HIP graph, `reps` repetitions timed one by one."""
     import numpy as np
     import torch
@@ -350,15 +352,14 @@ def rot_line(args, reps=60):
     seq_len = torch.tensor(lens, dtype=torch.int32, device=dev) + 1
     plan = kvq.decode_plan(g, Hq, S, cap)
     part = torch.empty(L, plan["workspace"] // 4, dtype=torch.float32, device=dev)
-    qrot = torch.empty_like(Qall)
     out = torch.empty(L, S, Hq, d, dtype=torch.float32, device=dev)
 
     def launch(l):
-        kvq.decode_partials(g, qrot[l], cache[l], off, seq_len, cap, kbits, rsig, rsig, part[l])
+        kvq.rot_decode_step_partials(g, Qall[l], Knew[l], Vnew[l], cache[l], off, seq_len, cap, kbits, rsig, rsig,
+                                     ksg[l], vsg[l], part[l])
 
     def step():
         for l in range(L):
-            kvq.rot_decode_prepare(g, Qall[l], qrot[l], Knew[l], Vnew[l], cache[l], off, seq_len, ksg[l], vsg[l], None)
             launch(l)
             kvq.merge_partials(S, Hq, plan["n_split"], part[l], out[l])
             kvq.rot_back(g, out[l], vsg[l])
@@ -400,8 +401,8 @@ def rot_line(args, reps=60):
     kgbps = launch_bytes / (kus / 1e6) / 1e9
     rows = sum(lens)
     res = {"label": "rotated TQ-MSE variant (random-sign Hadamard keys and values) at the 128K shape, K3V3",
-           "workload": wl.name + "-rotated", "entry_point": "kvq_rot_decode_prepare + "
-           "kvq_decode_partials + kvq_merge_partials + kvq_rot_back (graph)", "reps": reps,
+           "workload": wl.name + "-rotated", "entry_point": "kvq_rot_decode_step_partials + "
+           "kvq_merge_partials + kvq_rot_back (graph)", "reps": reps,
            "ms_per_step_median": round(med, 5), "ms_per_step_percentiles": pct(ms), "value": round(gbps, 2),
            "unit": "GB/s", "pct_hbm_peak": round(100 * gbps / HBM_PEAK_GBPS, 2), "step_bytes": int(step_bytes),
            "roofline": {"kernel": "decode_mfma_kernel" if plan["kernel"] == kvq.DECODE_MFMA else

@@ -371,6 +371,29 @@ int32_t kvq_rot_decode_prepare(const kvq_geom *g, int32_t n_q_heads, int32_t n_s
                                const void *k_new, const void *v_new, int64_t new_stride_seq, int64_t new_stride_head,
                                uint8_t *cache, const int64_t *seq_byte_off, const int32_t *seq_len,
                                const uint8_t *k_signs, const uint8_t *v_signs, const float *v_sigma, void *stream);
+/* The rotated variant's decode step, split phase, in ONE launch: what
+ * kvq_rot_decode_prepare followed by kvq_decode_step_partials' attention does, with the
+ * queries rotated and the new token rotated, coded and packed inside the matrix-core
+ * attention kernel (no q_rot buffer, no separate launch).  q: the UNROTATED queries
+ * [n_seq][n_q_heads][128]; k_new, v_new, strides: as kvq_decode_step_partials (token
+ * seq_len[s] - 1 is appended, then attended); k_bits: every block at the uniform width
+ * w = k_budget / 64; k_sigma: sigma_rot everywhere; v_sigma: sigma_rot (rotated values) or
+ * the value block scales (values coded unrotated, v_signs == NULL, which then also code
+ * the new token's values); k_signs / v_signs: as kvq_rot_quantize_pack.  The packed
+ * bytes equal kvq_rot_decode_prepare's and the partials kvq_decode_partials' on the
+ * rotated queries, bit for bit; merge them with kvq_merge_partials and, for rotated
+ * values, rotate the output back with kvq_rot_back.  Requirements: those of
+ * kvq_rot_quantize_pack's geometry and of kvq_decode_step_partials with the matrix-core
+ * kernel (k_budget <= 256, GQA ratio <= 8), else KVQ_ERR_BUDGET / KVQ_ERR_SHAPE; k_signs
+ * non-NULL (KVQ_ERR_ARG).  Errors as kvq_decode_step_partials reports them.  Written: the
+ * new token's slot in the cache and the partials. */
+int32_t kvq_rot_decode_step_partials(const kvq_geom *g, int32_t n_q_heads, const void *q, const void *k_new,
+                                     const void *v_new, int64_t new_stride_seq, int64_t new_stride_head,
+                                     uint8_t *cache, const int64_t *seq_byte_off, const int32_t *seq_len,
+                                     int32_t n_seq, int64_t max_len, const uint8_t *k_bits, const float *k_sigma,
+                                     const float *v_sigma, const uint8_t *k_signs, const uint8_t *v_signs,
+                                     float softmax_scale, float *partials, size_t partials_bytes,
+                                     int32_t tiles_per_split, void *stream);
 
 /* Measurement helper (not a step of the method): a plain streaming read of `bytes`
  * (a multiple of 16; src 16-byte aligned) by n_blocks workgroups of 256 threads, each

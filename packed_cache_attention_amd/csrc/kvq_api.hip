@@ -656,6 +656,32 @@ int32_t kvq_rot_decode_prepare(const kvq_geom* g, int32_t n_q_heads, int32_t n_s
                       fn);
 }
 
+int32_t kvq_rot_decode_step_partials(const kvq_geom* g, int32_t n_q_heads, const void* q, const void* k_new,
+                                     const void* v_new, int64_t new_stride_seq, int64_t new_stride_head,
+                                     uint8_t* cache, const int64_t* seq_byte_off, const int32_t* seq_len,
+                                     int32_t n_seq, int64_t max_len, const uint8_t* k_bits, const float* k_sigma,
+                                     const float* v_sigma, const uint8_t* k_signs, const uint8_t* v_signs,
+                                     float softmax_scale, float* partials, size_t partials_bytes,
+                                     int32_t tiles_per_split, void* stream) {
+    const char* fn = "kvq_rot_decode_step_partials";
+    int32_t st = check_rot_geom(g, fn);
+    if (st) return st;
+    DecodePlan plan;
+    st = check_decode(g, n_q_heads, q, cache, seq_byte_off, seq_len, n_seq, max_len, k_bits, k_sigma, v_sigma,
+                      partials, partials_bytes, KVQ_DECODE_MFMA, tiles_per_split, &plan, fn);
+    if (st || n_seq == 0) return st;
+    st = check_step_rows(k_new, v_new, new_stride_seq, new_stride_head, fn);
+    if (st) return st;
+    if (!k_signs) return fail(KVQ_ERR_ARG, fn, "null pointer");
+    AppendArgs app{(const uint16_t*)k_new, (const uint16_t*)v_new, new_stride_seq, new_stride_head};
+    app.k_signs = k_signs;
+    app.v_signs = v_signs;
+    return hip_status(launch_decode_partials(*g, plan, n_q_heads, (const uint16_t*)q, cache, seq_byte_off, seq_len,
+                                             n_seq, max_len, k_bits, k_sigma, v_sigma, softmax_scale, partials,
+                                             (hipStream_t)stream, app),
+                      fn);
+}
+
 // ---------------------------------------------------------------- measurement helper
 int32_t kvq_read_probe(const void* src, int64_t bytes, uint32_t* sink, int32_t n_blocks, void* stream) {
     const char* fn = "kvq_read_probe";

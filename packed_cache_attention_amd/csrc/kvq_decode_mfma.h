@@ -269,7 +269,7 @@ __device__ __forceinline__ void lds_barrier() {
     __builtin_amdgcn_fence(__ATOMIC_ACQUIRE, "workgroup", "local");
 }
 
-template <int V, int RD>
+template <int V, int RD, bool ROT = false>
 __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void decode_mfma_kernel(
     const uint16_t* __restrict__ q, uint8_t* __restrict__ cache, const int64_t* __restrict__ seq_byte_off,
     const int32_t* __restrict__ seq_len, int64_t max_len, int64_t capacity, const uint8_t* __restrict__ k_bits,
@@ -319,6 +319,16 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         const uint16_t* qrow = q + ((int64_t)s * n_q + kvh * g + hh) * kHeadDim;
         qv[e][0] = qrow[qp];
         qv[e][1] = qrow[qq];
+    }
+    // the rotated variant's step: the key signs of the lane's two coordinates (the
+    // queries and the new key are rotated here), and the value signs when values rotate
+    uint32_t ksg_p = 0, ksg_q = 0, vsg_p = 0, vsg_q = 0;
+    if constexpr (ROT) {
+        ksg_p = app.k_signs[kvh * kHeadDim + qp];
+        ksg_q = app.k_signs[kvh * kHeadDim + qq];
+        const uint8_t* vsg = app.v_signs != nullptr ? app.v_signs : app.k_signs;
+        vsg_p = vsg[kvh * kHeadDim + qp];
+        vsg_q = vsg[kvh * kHeadDim + qq];
     }
     constexpr int kTabChunks = (int)(sizeof(LevelTables) / 16);
     static_assert(kTabChunks > 256 && kTabChunks <= 512, "the level tables are staged in two 16-byte pieces per thread");
@@ -451,6 +461,17 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
             ubase += units;
         }
     }
+    if constexpr (ROT) {
+        // q_rot = RN16(RN32(RN32(S) * sigma_rot)), S = H (sg * q) exact: the lane's two
+        // coordinates of heads wave and wave + 4
+#pragma unroll
+        for (int e = 0; e < 2; ++e) {
+            float a, b;
+            rotated_pair_f32(qv[e][0], qv[e][1], ksg_p, ksg_q, lane, a, b);
+            qv[e][0] = __builtin_bit_cast(uint16_t, (_Float16)(a * kRotSigma));
+            qv[e][1] = __builtin_bit_cast(uint16_t, (_Float16)(b * kRotSigma));
+        }
+    }
     lds_barrier();  // zeroed q split before it is filled
     if (my_w > 0) {
 #pragma unroll
@@ -489,10 +510,29 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         if (lane < 16) s_rec[lane] = 0;
         ap_sk = token_norm(nk_pair);
         ap_sv = token_norm(nv_pair);
-        const uint32_t kcp = encode(s_thr, nk_p, my_w, my_ksig, ap_sk);
-        const uint32_t kcq = encode(s_thr, nk_q, my_w, my_ksig, ap_sk);
-        ap_vcp = encode(s_thr, nv_p, V, my_vsig_blk, ap_sv);
-        ap_vcq = encode(s_thr, nv_q, V, my_vsig_blk, ap_sv);
+        uint32_t kcp, kcq;
+        if constexpr (ROT) {
+            // rotated coordinates at the uniform width, sigma 1 (the 1/sqrt(128) is in
+            // the comparison), the unrotated row's norm
+            float a, b;
+            rotated_pair_f32(nk_p, nk_q, ksg_p, ksg_q, lane, a, b);
+            kcp = code_of(s_thr, a, my_w, 1.f, ap_sk);
+            kcq = code_of(s_thr, b, my_w, 1.f, ap_sk);
+            if (app.v_signs != nullptr) {
+                float c, d;
+                rotated_pair_f32(nv_p, nv_q, vsg_p, vsg_q, lane, c, d);
+                ap_vcp = code_of(s_thr, c, V, 1.f, ap_sv);
+                ap_vcq = code_of(s_thr, d, V, 1.f, ap_sv);
+            } else {
+                ap_vcp = encode(s_thr, nv_p, V, my_vsig_blk, ap_sv);
+                ap_vcq = encode(s_thr, nv_q, V, my_vsig_blk, ap_sv);
+            }
+        } else {
+            kcp = encode(s_thr, nk_p, my_w, my_ksig, ap_sk);
+            kcq = encode(s_thr, nk_q, my_w, my_ksig, ap_sk);
+            ap_vcp = encode(s_thr, nv_p, V, my_vsig_blk, ap_sv);
+            ap_vcq = encode(s_thr, nv_q, V, my_vsig_blk, ap_sv);
+        }
         if constexpr (V16) {
             // 16-bit values go into the cache now: the tail tile's operands are loaded
             // from there, after the first tile's wait for every load (vmcnt counts
@@ -841,6 +881,20 @@ hipError_t launch_mfma_v(const kvq_geom& g, const DecodePlan& plan, int n_q_head
                            seq_len, max_len, g.capacity_tokens, k_bits, k_sigma, v_sigma, scale_log2, n_q_heads, \
                            grp, g.rope_pairing, g.k_budget, plan.tiles_per_split, n_chunks, partials, app);     \
         return hipGetLastError();                                                                               \
+    }
+    if constexpr (V <= 8) {
+        if (app.k_signs != nullptr) {  // the rotated variant's step (uniform key widths 1..4)
+#define KVQ_LAUNCH_ROT(RDV)                                                                                    \
+    if (rd == RDV) {                                                                                            \
+        hipLaunchKernelGGL((decode_mfma_kernel<V, RDV, true>), grid, dim3(256), 0, st, q, cache, seq_byte_off, \
+                           seq_len, max_len, g.capacity_tokens, k_bits, k_sigma, v_sigma, scale_log2, n_q_heads, \
+                           grp, g.rope_pairing, g.k_budget, plan.tiles_per_split, n_chunks, partials, app);     \
+        return hipGetLastError();                                                                               \
+    }
+            KVQ_LAUNCH_ROT(4) KVQ_LAUNCH_ROT(8) KVQ_LAUNCH_ROT(12) KVQ_LAUNCH_ROT(16)
+#undef KVQ_LAUNCH_ROT
+            return hipErrorInvalidValue;
+        }
     }
     KVQ_LAUNCH(0) KVQ_LAUNCH(4) KVQ_LAUNCH(8) KVQ_LAUNCH(12) KVQ_LAUNCH(16)
 #undef KVQ_LAUNCH

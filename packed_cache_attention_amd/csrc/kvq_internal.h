@@ -114,6 +114,120 @@ __device__ __forceinline__ float wave_sum64(float x) {
     return xor32_sum(xor16_sum(x));
 }
 
+// ---- the rotated variant's exact transform (shared by its quantizer and the fused
+// decode step): binary16 values are integer counts of 2^-24, so the Walsh-Hadamard sums
+// of a row are exact in 64-bit integers and get one binary32 rounding
+constexpr float kRotSigma = 0.0883883461356163f;  // RN32(1 / sqrt(128)): bits 0x3DB504F3
+static_assert(__builtin_bit_cast(uint32_t, kRotSigma) == 0x3DB504F3u, "rotation scale");
+
+// value of a binary16 pattern in units of 2^-24 (exact)
+__device__ __forceinline__ int64_t h2units(uint32_t h) {
+    const int e = (h >> 10) & 31, m = h & 1023;
+    const int64_t v = e == 0 ? (int64_t)m : ((int64_t)(1024 + m) << (e - 1));
+    return (h & 0x8000u) ? -v : v;
+}
+
+// lane l receives x of lane l ^ M: DPP inside each row of 16 lanes for M = 1, 2, 4, 8
+// (quad permutations; for 4 two row rotates, by 12 on banks 0 and 2 and by 4 on banks 1
+// and 3; a rotate by 8), permlane swaps across rows for 16 and 32 -- no LDS traffic
+template <int M>
+__device__ __forceinline__ uint32_t lane_xor(uint32_t x, int lane) {
+    static_assert(M == 1 || M == 2 || M == 4 || M == 8 || M == 16 || M == 32, "lane distance");
+    if constexpr (M == 1) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0xB1, 0xf, 0xf, false);
+    if constexpr (M == 2) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x4E, 0xf, 0xf, false);
+    if constexpr (M == 4) {
+        const int t = __builtin_amdgcn_update_dpp(0, (int)x, 0x12C, 0xf, 0x5, false);
+        return (uint32_t)__builtin_amdgcn_update_dpp(t, (int)x, 0x124, 0xf, 0xA, false);
+    }
+    if constexpr (M == 8) return (uint32_t)__builtin_amdgcn_update_dpp(0, (int)x, 0x128, 0xf, 0xf, false);
+    if constexpr (M == 16) {
+        const auto r = __builtin_amdgcn_permlane16_swap(x, x, false, false);
+        const uint32_t r0 = r[0], r1 = r[1];
+        return (lane & 16) ? r0 : r1;
+    }
+    if constexpr (M == 32) {
+        const auto r = __builtin_amdgcn_permlane32_swap(x, x, false, false);
+        const uint32_t r0 = r[0], r1 = r[1];
+        return (lane & 32) ? r0 : r1;
+    }
+    return x;
+}
+template <int M>
+__device__ __forceinline__ int64_t lane_xor64(int64_t v, int lane) {
+    const uint32_t lo = lane_xor<M>((uint32_t)v, lane), hi = lane_xor<M>((uint32_t)((uint64_t)v >> 32), lane);
+    return (int64_t)(((uint64_t)hi << 32) | lo);
+}
+template <int M>
+__device__ __forceinline__ void fwht64_stage(int64_t& a, int64_t& b, int lane) {
+    const int64_t pa = lane_xor64<M>(a, lane), pb = lane_xor64<M>(b, lane);
+    const bool upper = lane & M;  // this lane holds the second member of each pair
+    a = upper ? pa - a : a + pa;
+    b = upper ? pb - b : b + pb;
+}
+
+// The Walsh-Hadamard transform of the 128 values a wave holds, in place, exact in
+// 64-bit integers: lane l holds two values whose indices differ only in one bit (a: that
+// bit 0, b: 1) and whose other six bits are l's -- values 2l and 2l + 1, or l and l + 64.
+// The transform is one butterfly per index bit in any order, so both layouts work.
+__device__ __forceinline__ void fwht64(int64_t& a, int64_t& b, int lane) {
+    {
+        const int64_t s = a + b, d = a - b;
+        a = s;
+        b = d;
+    }
+    fwht64_stage<1>(a, b, lane);
+    fwht64_stage<2>(a, b, lane);
+    fwht64_stage<4>(a, b, lane);
+    fwht64_stage<8>(a, b, lane);
+    fwht64_stage<16>(a, b, lane);
+    fwht64_stage<32>(a, b, lane);
+}
+
+// The same transform in binary64 (values, not units): every binary16 value and every
+// partial sum (a multiple of 2^-24 below 2^23 in magnitude, 47 significant bits) is
+// exact in binary64, so each butterfly is one exact fused multiply-add by +-1 and the
+// result's conversion to binary32 is RN32 of the exact sum
+template <int M>
+__device__ __forceinline__ double lane_xor_f64(double v, int lane) {
+    const uint64_t u = __builtin_bit_cast(uint64_t, v);
+    const uint64_t lo = lane_xor<M>((uint32_t)u, lane), hi = lane_xor<M>((uint32_t)(u >> 32), lane);
+    return __builtin_bit_cast(double, lo | (hi << 32));
+}
+template <int M>
+__device__ __forceinline__ void fwht64d_stage(double& a, double& b, int lane) {
+    const double pa = lane_xor_f64<M>(a, lane), pb = lane_xor_f64<M>(b, lane);
+    const double sg = (lane & M) ? -1.0 : 1.0;  // the pair's second member takes partner - own
+    a = __builtin_fma(sg, a, pa);
+    b = __builtin_fma(sg, b, pb);
+}
+__device__ __forceinline__ void fwht64d(double& a, double& b, int lane) {
+    {
+        const double s = a + b, d = a - b;
+        a = s;
+        b = d;
+    }
+    fwht64d_stage<1>(a, b, lane);
+    fwht64d_stage<2>(a, b, lane);
+    fwht64d_stage<4>(a, b, lane);
+    fwht64d_stage<8>(a, b, lane);
+    fwht64d_stage<16>(a, b, lane);
+    fwht64d_stage<32>(a, b, lane);
+}
+// the lane's two rotated sums of two binary16 values (signs: nonzero -> negate), RN32
+__device__ __forceinline__ void rotated_pair_f32(uint32_t x0, uint32_t x1, uint32_t sg0, uint32_t sg1, int lane,
+                                                 float& r0, float& r1) {
+    double a = (double)h2f(x0), b = (double)h2f(x1);
+    if (sg0) a = -a;
+    if (sg1) b = -b;
+    fwht64d(a, b, lane);
+    r0 = (float)a;
+    r1 = (float)b;
+}
+
+// RN32 of the exact sum (units of 2^-24): a correctly rounded 64-bit integer
+// conversion, then an exact power-of-two scaling (results are normal)
+__device__ __forceinline__ float units_to_f32(int64_t u) { return __builtin_amdgcn_ldexpf(__ll2float_rn(u), -24); }
+
 // ---- layout ----
 __host__ __device__ inline int64_t k_record_bytes(int k_budget) { return 16 * ((2 * (int64_t)k_budget + 127) / 128); }
 __host__ __device__ inline int64_t tile_bytes(int d, int k_budget, int v_bits) {
@@ -155,6 +269,11 @@ struct AppendArgs {
     const uint16_t* v_new;
     int64_t new_stride_seq;
     int64_t new_stride_head;
+    // the rotated variant's fused step (matrix-core kernel only): queries rotated with
+    // the key signs, the new token rotated and coded as the rotated quantizer codes it
+    // (values too when v_signs != nullptr); nullptr: no rotation
+    const uint8_t* k_signs;
+    const uint8_t* v_signs;
 };
 
 // window token i of sequence s (position len - nw + i; ring row (r0 + i) mod window with

@@ -23,42 +23,6 @@
 
 namespace kvq {
 
-constexpr float kRotSigma = 0.0883883461356163f;  // RN32(1 / sqrt(128)): bits 0x3DB504F3
-static_assert(__builtin_bit_cast(uint32_t, kRotSigma) == 0x3DB504F3u, "rotation scale");
-
-// value of a binary16 pattern in units of 2^-24 (exact)
-__device__ __forceinline__ int64_t h2units(uint32_t h) {
-    const int e = (h >> 10) & 31, m = h & 1023;
-    const int64_t v = e == 0 ? (int64_t)m : ((int64_t)(1024 + m) << (e - 1));
-    return (h & 0x8000u) ? -v : v;
-}
-
-__device__ __forceinline__ int64_t shfl_xor64(int64_t v, int m) {
-    const uint32_t lo = (uint32_t)v, hi = (uint32_t)((uint64_t)v >> 32);
-    const uint32_t plo = (uint32_t)__shfl_xor((int)lo, m), phi = (uint32_t)__shfl_xor((int)hi, m);
-    return (int64_t)(((uint64_t)phi << 32) | plo);
-}
-
-// The Walsh-Hadamard transform of the 128 values a wave holds (lane l: a = value
-// 2l, b = value 2l + 1), in place, exact in 64-bit integers.
-__device__ __forceinline__ void fwht64(int64_t& a, int64_t& b, int lane) {
-    {
-        const int64_t s = a + b, d = a - b;
-        a = s;
-        b = d;
-    }
-#pragma unroll
-    for (int m = 1; m < 64; m <<= 1) {
-        const int64_t pa = shfl_xor64(a, m), pb = shfl_xor64(b, m);
-        const bool upper = lane & m;  // this lane holds the second member of each pair
-        a = upper ? pa - a : a + pa;
-        b = upper ? pb - b : b + pb;
-    }
-}
-
-// RN32 of the exact sum (units of 2^-24): a correctly rounded 64-bit integer
-// conversion, then an exact power-of-two scaling (results are normal)
-__device__ __forceinline__ float units_to_f32(int64_t u) { return __builtin_amdgcn_ldexpf(__ll2float_rn(u), -24); }
 
 // the lane's two rotated sums of a binary16 row (signs: 1 -> -1)
 __device__ __forceinline__ void rotated_pair(uint32_t pair, const uint8_t* __restrict__ sg, int lane, float& s0,

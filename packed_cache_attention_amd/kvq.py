@@ -109,6 +109,9 @@ def lib() -> C.CDLL:
     L.kvq_rot_back.restype = I32
     L.kvq_rot_decode_prepare.argtypes = [G, I32, I32, P, P, P, P, I64, I64, P, P, P, P, P, P, P]
     L.kvq_rot_decode_prepare.restype = I32
+    L.kvq_rot_decode_step_partials.argtypes = [G, I32, P, P, P, I64, I64, P, P, P, I32, I64, P, P, P, P, P, F32, P,
+                                               SZ, I32, P]
+    L.kvq_rot_decode_step_partials.restype = I32
     L.kvq_read_probe.argtypes = [P, I64, P, I32, P]
     L.kvq_read_probe.restype = I32
     if L.kvq_version() != LAYOUT_VERSION:
@@ -124,7 +127,7 @@ EXPORTS = ["kvq_version", "kvq_status_string", "kvq_tile_bytes", "kvq_cache_byte
            "kvq_decode_step_partials", "kvq_decode_step", "kvq_window_decode_attn", "kvq_window_decode_step",
            "kvq_window_workspace_bytes", "kvq_prefill_plan", "kvq_prefill_workspace_bytes",
            "kvq_packed_prefill_attn", "kvq_read_probe", "kvq_rot_quantize_pack", "kvq_rot_queries", "kvq_rot_back",
-           "kvq_rot_decode_prepare"]
+           "kvq_rot_decode_prepare", "kvq_rot_decode_step_partials"]
 
 
 def status_string(st: int) -> str:
@@ -454,6 +457,25 @@ def rot_back(g: Geom, out: torch.Tensor, v_signs: torch.Tensor, stream=None):
     assert out.dtype == torch.float32 and out.is_contiguous()
     _check("kvq_rot_back", lib().kvq_rot_back(C.byref(g), out.shape[1], out.shape[0], _ptr(out), _ptr(v_signs),
                                                _stream(stream)))
+
+
+def rot_decode_step_partials(g: Geom, q: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,
+                             cache: torch.Tensor, seq_byte_off: torch.Tensor, seq_len: torch.Tensor, max_len: int,
+                             k_bits: torch.Tensor, k_sigma: torch.Tensor, v_sigma: torch.Tensor,
+                             k_signs: torch.Tensor, v_signs: torch.Tensor | None, partials: torch.Tensor,
+                             softmax_scale: float | None = None, tiles_per_split: int = 0, stream=None):
+    """The rotated variant's step split phase in one launch: q [n_seq, n_q, 128] (unrotated)
+    rotated inside the attention kernel, the new token [n_seq, n_kv, 128] rotated and packed
+    at slot seq_len-1, partials as kvq_decode_partials writes them."""
+    assert q.dtype == torch.float16 and q.is_contiguous() and partials.dtype == torch.float32
+    ss, sh = _step_rows(k_new, v_new)
+    n_seq, n_q = q.shape[0], q.shape[1]
+    if softmax_scale is None:
+        softmax_scale = g.head_dim ** -0.5
+    _check("kvq_rot_decode_step_partials", lib().kvq_rot_decode_step_partials(
+        C.byref(g), n_q, _ptr(q), _ptr(k_new), _ptr(v_new), ss, sh, _ptr(cache), _ptr(seq_byte_off), _ptr(seq_len),
+        n_seq, max_len, _ptr(k_bits), _ptr(k_sigma), _ptr(v_sigma), _ptr(k_signs), _ptr(v_signs),
+        float(softmax_scale), _ptr(partials), partials.numel() * 4, tiles_per_split, _stream(stream)))
 
 
 def rot_decode_prepare(g: Geom, q: torch.Tensor, q_rot: torch.Tensor, k_new: torch.Tensor, v_new: torch.Tensor,

@@ -193,6 +193,18 @@ def test_host_validation_rejects_before_gpu():
     assert L.kvq_rot_decode_prepare(*rp(good, vsg=None, vsig=None)) == -1
     assert L.kvq_rot_decode_prepare(*rp(good, kn=FAKE + 2)) == -4
     assert L.kvq_rot_decode_prepare(*rp(good, ss=255)) == -4
+    rs = lambda g_, nq=16, q=FAKE, kn=FAKE, ss=256, ksg=FAKE, nb=1 << 30, ml=1024: (
+        C.byref(g_), nq, q, kn, FAKE, ss, 128, FAKE, FAKE, FAKE, 1, ml, FAKE, FAKE, FAKE, ksg, FAKE, 0.088, FAKE, nb,
+        0, None)
+    assert L.kvq_rot_decode_step_partials(*rs(kvq.geom(2, 160, 3, 1024))) == -3   # rotated keys: uniform widths
+    assert L.kvq_rot_decode_step_partials(*rs(kvq.geom(2, 320, 3, 1024))) == -2   # K record past the MFMA kernel's
+    assert L.kvq_rot_decode_step_partials(*rs(good, nq=3)) == -2
+    assert L.kvq_rot_decode_step_partials(*rs(good, q=None)) == -1
+    assert L.kvq_rot_decode_step_partials(*rs(good, ksg=None)) == -1
+    assert L.kvq_rot_decode_step_partials(*rs(good, kn=FAKE + 2)) == -4
+    assert L.kvq_rot_decode_step_partials(*rs(good, ss=255)) == -4
+    assert L.kvq_rot_decode_step_partials(*rs(good, nb=16)) == -6
+    assert L.kvq_rot_decode_step_partials(*rs(good, ml=4096)) == -5
     # read probe (measurement helper): counts, pointers, alignment
     assert L.kvq_read_probe(FAKE, -16, FAKE, 4, None) == -1
     assert L.kvq_read_probe(FAKE, 1024, FAKE, 0, None) == -1

@@ -227,6 +227,104 @@ def test_rotated_decode_prepare(kb, vb, pairing, vrot):
     say("worst rel %.2e" % check_attention(out.cpu().numpy(), ref))
 
 
+@pytest.mark.parametrize("tiles", [0, 1])
+@pytest.mark.parametrize("vrot", [True, False], ids=["vrot", "vplain"])
+@pytest.mark.parametrize("pairing", [kvq.PAIR_HALF, kvq.PAIR_INTERLEAVED], ids=["half", "interleaved"])
+@pytest.mark.parametrize("kb,vb", [(192, 3), (64, 1), (256, 4), (128, 8)], ids=["k3v3", "k1v1", "k4v4", "k2v8"])
+def test_rotated_fused_step(kb, vb, pairing, vrot, tiles):
+    """kvq_rot_decode_step_partials (queries and the new token rotated inside the
+    attention kernel) against kvq_rot_decode_prepare + kvq_decode_partials on the rotated
+    queries: the same cache bytes (and so the oracle's), the same partials bit for bit,
+    then merged (and rotated back) within 2e-3 of the oracle.  Lengths 0, 63, 64, 127 and
+    300 before the step; one tile per chunk or the planner's chunks."""
+    H, grp = 2, 4
+    lens = [0, 63, 64, 127, 300]
+    say("rot fused step: kb %d vb %d pairing %d vrot %d tiles %d" % (kb, vb, pairing, vrot, tiles))
+    seqs = _batch(H, grp, kb, vb, [n + 1 for n in lens], seed=51)
+    ksg = synth.rot_signs(H, seed=51).cuda()
+    vsg = synth.rot_signs(H, seed=52).cuda() if vrot else None
+    vsig = None
+    if not vrot:
+        ev = np.zeros((H, D // 2, 2), np.uint64)
+        for _, V, _ in seqs:
+            oracle.block_energy(V.numpy(), pairing, ev)
+        _, vsig = oracle.allocate(ev, vb * (D // 2), oracle.UNIFORM)
+    cap = 384
+    g = kvq.geom(H, kb, vb, cap, rope_pairing=pairing)
+    ogeom = oracle.Geometry(H, kb, vb, cap, pairing=pairing)
+    region = kvq.cache_bytes(g)
+    S = len(lens)
+    cache = torch.zeros(S * region, dtype=torch.uint8, device="cuda")
+    off = torch.arange(S, dtype=torch.int64, device="cuda") * region
+    head = [(K[:n], V[:n], q) for (K, V, q), n in zip(seqs, lens) if n > 0]
+    rows = torch.cat([x[0] for x in head], 0).cuda()
+    vrows = torch.cat([x[1] for x in head], 0).cuda()
+    row0 = np.concatenate([[0], np.cumsum(lens)[:-1]]).astype(np.int64)
+    vsig_t = None if vsig is None else torch.from_numpy(vsig).cuda()
+    kvq.rot_quantize_pack(g, rows, vrows, torch.zeros(S, dtype=torch.int64, device="cuda"),
+                          torch.tensor(lens, dtype=torch.int32, device="cuda"), torch.tensor(row0, device="cuda"),
+                          max(lens), ksg, vsg, vsig_t, cache, off)
+    kn = torch.stack([K[n] for (K, _, _), n in zip(seqs, lens)]).cuda()
+    vn = torch.stack([V[n] for (_, V, _), n in zip(seqs, lens)]).cuda()
+    q = torch.stack([x[2] for x in seqs]).cuda().contiguous()
+    seq_len = torch.tensor([n + 1 for n in lens], dtype=torch.int32, device="cuda")
+    kbits = torch.full((H, D // 2), kb // (D // 2), dtype=torch.uint8, device="cuda")
+    ksig = torch.full((H, D // 2), float(SIG_ROT), dtype=torch.float32, device="cuda")
+    vs = ksig if vrot else vsig_t
+    plan = kvq.decode_plan(g, H * grp, S, cap, kvq.DECODE_MFMA, tiles)
+    part_a = torch.full((plan["workspace"] // 4,), float("nan"), dtype=torch.float32, device="cuda")
+    part_b = part_a.clone()
+    cache_b = cache.clone()
+    # two launches: the step's preparation, then the split phase on the rotated queries
+    q_rot = torch.empty_like(q)
+    kvq.rot_decode_prepare(g, q, q_rot, kn, vn, cache, off, seq_len, ksg, vsg, vsig_t)
+    kvq.decode_partials(g, q_rot, cache, off, seq_len, cap, kbits, ksig, vs, part_a, kernel=kvq.DECODE_MFMA,
+                        tiles_per_split=tiles)
+    # one launch
+    kvq.rot_decode_step_partials(g, q, kn, vn, cache_b, off, seq_len, cap, kbits, ksig, vs, ksg, vsg, part_b,
+                                 tiles_per_split=tiles)
+    np.testing.assert_array_equal(cache_b.cpu().numpy(), cache.cpu().numpy())
+    oc = np.zeros(S * region, np.uint8)
+    for i, (K, V, _) in enumerate(seqs):
+        oracle.quantize_pack_rot(ogeom, oc[i * region:(i + 1) * region], K.numpy(), V.numpy(), 0, ksg.cpu().numpy(),
+                                 None if vsg is None else vsg.cpu().numpy(), vsig)
+    _check_bytes(cache_b, oc, "fused step")
+    ns = plan["n_split"]
+    pa = part_a[:S * H * grp * ns * 130].view(S * H * grp, ns, 130).cpu().numpy()
+    pb = part_b[:S * H * grp * ns * 130].view(S * H * grp, ns, 130).cpu().numpy()
+    np.testing.assert_array_equal(pb.view(np.uint32), pa.view(np.uint32))
+    out = torch.empty(S, H * grp, D, dtype=torch.float32, device="cuda")
+    kvq.merge_partials(S, H * grp, ns, part_b, out)
+    if vrot:
+        kvq.rot_back(g, out, vsg)
+    ref = np.stack([oracle.decode_attention_rot(ogeom, oc[i * region:(i + 1) * region], q.cpu().numpy()[i],
+                                                lens[i] + 1, ksg.cpu().numpy(),
+                                                None if vsg is None else vsg.cpu().numpy(), vsig)
+                    for i in range(S)])
+    say("worst rel %.2e" % check_attention(out.cpu().numpy(), ref))
+
+
+def test_rotated_fused_step_rejects_wide_keys():
+    """Rotated keys wider than 4 bits (K records over 64 bytes) have no matrix-core step:
+    the fused call reports KVQ_ERR_SHAPE and writes nothing."""
+    H, grp, kb, vb, cap = 2, 4, 320, 3, 128
+    g = kvq.geom(H, kb, vb, cap)
+    cache = torch.zeros(kvq.cache_bytes(g), dtype=torch.uint8, device="cuda")
+    z = torch.zeros(1, dtype=torch.int64, device="cuda")
+    x = torch.zeros(1, H, D, dtype=torch.float16, device="cuda")
+    q = torch.zeros(1, H * grp, D, dtype=torch.float16, device="cuda")
+    sg = torch.zeros(H, D, dtype=torch.uint8, device="cuda")
+    kbits = torch.full((H, D // 2), kb // (D // 2), dtype=torch.uint8, device="cuda")
+    sig = torch.full((H, D // 2), float(SIG_ROT), dtype=torch.float32, device="cuda")
+    part = torch.zeros(1 << 16, dtype=torch.float32, device="cuda")
+    with pytest.raises(kvq.KvqError) as err:
+        kvq.rot_decode_step_partials(g, q, x, x, cache, z, torch.ones(1, dtype=torch.int32, device="cuda"), cap,
+                                     kbits, sig, sig, sg, sg, part)
+    assert err.value.status == -2
+    torch.cuda.synchronize()
+    assert int(cache.count_nonzero()) == 0
+
+
 @pytest.mark.parametrize("align", ["4byte", "16byte-oddstride"])
 @pytest.mark.parametrize("vrot", [True, False], ids=["vrot", "vplain"])
 def test_rotated_pack_from_strided_unaligned_rows(align, vrot):
