@@ -304,6 +304,44 @@ def test_rotated_fused_step(kb, vb, pairing, vrot, tiles):
     say("worst rel %.2e" % check_attention(out.cpu().numpy(), ref))
 
 
+def test_rotated_fused_step_full_size():
+    """The rotated step as the bench times it, at its size: one 128K-token Qwen2.5-3B-shaped
+    layer (K3V3, values rotated), the 131073rd token appended by kvq_rot_decode_step_partials
+    in the automatic plan with max_len = capacity; the cache bytes against the oracle's
+    rotated packing of all tokens, the merged and back-rotated output within 2e-3 of the
+    oracle's attention over them."""
+    wl = synth.WORKLOADS["c3"]
+    H, grp, kb, vb = wl.n_kv_heads, wl.group, wl.k_budget, wl.v_bits
+    n = wl.seq_lens[0]
+    say("rot fused step full size: %d tokens" % n)
+    (K, V, q), = _batch(H, grp, kb, vb, [n + 1], seed=13)
+    ksg, vsg = synth.rot_signs(H, seed=13), synth.rot_signs(H, seed=14)
+    cap = synth.ceil_to(n + 64, 64)
+    g = kvq.geom(H, kb, vb, cap)
+    ogeom = oracle.Geometry(H, kb, vb, cap)
+    cache = torch.zeros(kvq.cache_bytes(g), dtype=torch.uint8, device="cuda")
+    off = torch.zeros(1, dtype=torch.int64, device="cuda")
+    _gpu_pack(g, [(K[:n], V[:n], q)], [0], ksg, vsg, None, cache, off)
+    kbits = torch.full((H, D // 2), kb // (D // 2), dtype=torch.uint8, device="cuda")
+    sig = torch.full((H, D // 2), float(SIG_ROT), dtype=torch.float32, device="cuda")
+    plan = kvq.decode_plan(g, H * grp, 1, cap)
+    say("plan %s" % plan)
+    assert plan["kernel"] == kvq.DECODE_MFMA
+    part = torch.empty(plan["workspace"] // 4 + 4, dtype=torch.float32, device="cuda")
+    seq_len = torch.tensor([n + 1], dtype=torch.int32, device="cuda")
+    kvq.rot_decode_step_partials(g, q[None].cuda().contiguous(), K[n:n + 1].cuda().contiguous(),
+                                 V[n:n + 1].cuda().contiguous(), cache, off, seq_len, cap, kbits, sig, sig,
+                                 ksg.cuda(), vsg.cuda(), part)
+    out = torch.empty(1, H * grp, D, dtype=torch.float32, device="cuda")
+    kvq.merge_partials(1, H * grp, plan["n_split"], part, out)
+    kvq.rot_back(g, out, vsg.cuda())
+    oc = np.zeros(kvq.cache_bytes(g), np.uint8)
+    _oracle_pack(ogeom, oc, [(K, V, q)], [0], ksg, vsg, None)
+    _check_bytes(cache, oc, "fused step, full size")
+    ref = oracle.decode_attention_rot(ogeom, oc, q.numpy(), n + 1, ksg.numpy(), vsg.numpy(), None)
+    say("worst rel %.2e" % check_attention(out.cpu().numpy()[0], ref))
+
+
 def test_rotated_fused_step_rejects_wide_keys():
     """Rotated keys wider than 4 bits (K records over 64 bytes) have no matrix-core step:
     the fused call reports KVQ_ERR_SHAPE and writes nothing."""
