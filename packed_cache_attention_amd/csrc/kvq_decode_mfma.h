@@ -613,7 +613,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         rec[RD + 1] = 0;
         kb ^= 1;
         // 16-bit values: the next K section (into the buffer the previous tile's records
-        // left), then the first half of this tile's value operands, both in flight
+        // left), then the first batch of this tile's value operands, both in flight
         // during QK; loads complete in issue order, so the operands' own waits never
         // wait for the DMA
         u32x4 vr[16];
@@ -636,8 +636,8 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         for (int i = 0; i < 16; ++i) acc[i] = acc0[i] + acc1[i];
         // ---- V section landed (scales, runs); the next K section then goes out (into
         // the K buffer this tile's records left), behind this tile's V in the queue.
-        // 16-bit values: the scales landed (the next K section and the 16 operand loads
-        // went out after them)
+        // 16-bit values: the scales landed (the next K section and the first operand
+        // batch went out after them), then the second batch goes out
         if constexpr (V16) {
             if (more) __builtin_amdgcn_s_waitcnt(wait_vm(2 * kPre + KI));
             else __builtin_amdgcn_s_waitcnt(wait_vm(2 * kPre));
