@@ -174,16 +174,11 @@ hipError_t launch_decode_partials(const kvq_geom& g, const DecodePlan& plan, int
                                   const AppendArgs& app) {
     const float scale_log2 = softmax_scale * kLog2e;
     const int grp = n_q_heads / g.n_kv_heads;
-    // the matrix-core kernel appends inside (the tail tile's wave); the generic one
-    // gets the append as a kernel of its own first
+    // the matrix-core kernel appends inside (the tail tile's wave); the generic one in
+    // the launch that builds its query table (one wave per (sequence, KV head))
     if (plan.kernel == KVQ_DECODE_MFMA)
         return launch_decode_mfma(g, plan, n_q_heads, q, cache, seq_byte_off, seq_len, n_seq, max_len, k_bits,
                                   k_sigma, v_sigma, scale_log2, partials, st, app);
-    if (app.k) {
-        const hipError_t e = launch_append_step(g, n_seq, app, seq_len, k_bits, k_sigma, v_sigma, cache,
-                                                seq_byte_off, st);
-        if (e != hipSuccess) return e;
-    }
     const int n_chunks = plan.n_split + (app.window > 0 ? window_chunks(app.window) : 0);  // + the window's
     return launch_decode_generic(g, plan.tiles_per_split, n_chunks, n_q_heads, q, cache, seq_byte_off, seq_len,
                                  n_seq, max_len, k_bits, k_sigma, v_sigma, scale_log2, partials, st, app);

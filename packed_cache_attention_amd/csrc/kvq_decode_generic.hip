@@ -21,6 +21,7 @@
 //     weight x level into its outputs for the G heads, the weights read as broadcasts.
 // The value block scale multiplies the combined output once.
 #include "kvq_internal.h"
+#include "kvq_append.h"
 
 namespace kvq {
 
@@ -33,12 +34,18 @@ constexpr int kGenericQMax = 16;  // query heads per KV head
 // 256 threads per (KV head, sequence): every load is issued first (the group's queries
 // as 8-byte pieces, the widths and scales), the K-order rank of each block comes from
 // ballots over the widths, then thread t writes head j's entries for coordinates t, t + 128.
-__global__ __launch_bounds__(256) void generic_qtable_kernel(const uint16_t* __restrict__ q,
-                                                              const uint8_t* __restrict__ k_bits,
-                                                              const float* __restrict__ k_sigma, int n_q, int g,
-                                                              int G, int pairing, int k16, float scale_log2,
-                                                              float* __restrict__ table) {
+__global__ __launch_bounds__(256) void generic_qtable_kernel(
+    const uint16_t* __restrict__ q, const uint8_t* __restrict__ k_bits, const float* __restrict__ k_sigma, int n_q,
+    int g, int G, int pairing, int k16, float scale_log2, float* __restrict__ table, AppendArgs app,
+    const float* __restrict__ v_sigma, uint8_t* __restrict__ cache, const int64_t* __restrict__ seq_byte_off,
+    const int32_t* __restrict__ seq_len, int64_t capacity, int k_budget, int v_bits) {
     const int kvh = blockIdx.x, s = blockIdx.y, tid = threadIdx.x;
+    // the decode step's new token (or the token leaving the fp16 window) for this
+    // (sequence, KV head): the last wave packs it, as the append kernel would
+    if (app.k != nullptr && tid >= 192)
+        append_token(app.k, app.v, app.stride_seq, app.stride_head, nullptr, nullptr, nullptr, 1, capacity, k_bits,
+                     k_sigma, v_sigma, cache, seq_byte_off, pairing, k_budget, v_bits, seq_len, app, s, kvh, 0,
+                     tid & 63);
     __shared__ float s_q[kGenericQMax][kHeadDim];
     __shared__ int s_pos[kHeadDim];  // coordinate -> field position in the K order (-1: width 0)
     __shared__ float s_sig[kHeadDim];
@@ -369,7 +376,7 @@ int generic_blocks_per_cu(const kvq_geom& g, int n_q_heads) {
 }
 
 hipError_t launch_decode_generic(const kvq_geom& g, int tiles_per_split, int n_chunks, int n_q_heads,
-                                 const uint16_t* q, const uint8_t* cache, const int64_t* seq_byte_off,
+                                 const uint16_t* q, uint8_t* cache, const int64_t* seq_byte_off,
                                  const int32_t* seq_len, int n_seq, int64_t max_len, const uint8_t* k_bits,
                                  const float* k_sigma, const float* v_sigma, float scale_log2, float* partials,
                                  hipStream_t st, const AppendArgs& app) {
@@ -378,7 +385,8 @@ hipError_t launch_decode_generic(const kvq_geom& g, int tiles_per_split, int n_c
     // the query table sits after the partials of every chunk
     float* table = partials + (int64_t)n_seq * n_q_heads * n_chunks * (kHeadDim + 2);
     hipLaunchKernelGGL(generic_qtable_kernel, dim3(g.n_kv_heads, n_seq), dim3(256), 0, st, q, k_bits, k_sigma,
-                       n_q_heads, grp, G, g.rope_pairing, g.k_budget == 16 * kMaxBlocks ? 1 : 0, scale_log2, table);
+                       n_q_heads, grp, G, g.rope_pairing, g.k_budget == 16 * kMaxBlocks ? 1 : 0, scale_log2, table, app,
+                       v_sigma, cache, seq_byte_off, seq_len, g.capacity_tokens, g.k_budget, g.v_bits);
     hipError_t e = hipGetLastError();
     if (e != hipSuccess) return e;
     const int lds = generic_lds_bytes(G, (int)(k_record_bytes(g.k_budget) / 4), app.window > 0);

@@ -429,15 +429,12 @@ hipError_t launch_decode_partials(const kvq_geom& g, const DecodePlan& plan, int
 // the vector-ALU kernel (kvq_decode_generic.hip): a query-table launch, then the
 // chunks; the table lives after the partials of all n_chunks chunks
 hipError_t launch_decode_generic(const kvq_geom& g, int tiles_per_split, int n_chunks, int n_q_heads,
-                                 const uint16_t* q, const uint8_t* cache, const int64_t* seq_byte_off,
+                                 const uint16_t* q, uint8_t* cache, const int64_t* seq_byte_off,
                                  const int32_t* seq_len, int n_seq, int64_t max_len, const uint8_t* k_bits,
                                  const float* k_sigma, const float* v_sigma, float scale_log2, float* partials,
                                  hipStream_t st, const AppendArgs& app);
 int64_t generic_table_bytes(const kvq_geom& g, int n_q_heads, int n_seq);
 int generic_blocks_per_cu(const kvq_geom& g, int n_q_heads);
-hipError_t launch_append_step(const kvq_geom& g, int n_seq, const AppendArgs& app, const int32_t* seq_len,
-                              const uint8_t* k_bits, const float* k_sigma, const float* v_sigma, uint8_t* cache,
-                              const int64_t* seq_byte_off, hipStream_t st);
 hipError_t launch_merge(int n_rows, int n_split, const float* partials, float* out, hipStream_t st);
 
 // plain streaming read of `bytes` (a multiple of 16) by n_blocks workgroups; one word per
