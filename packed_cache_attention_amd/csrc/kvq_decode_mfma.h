@@ -102,6 +102,7 @@ struct MfmaSmem {
     // 8-position units (its last unit zero-padded), classes in descending width
     alignas(16) uint16_t qsplit[2][8][8 * kMaxUnits + 8];  // rows 400 B apart: the 16 rows read by one
                                                           // b128 load fall in distinct LDS banks
+    alignas(16) uint16_t qzero[8 * kMaxUnits + 8];         // a zero row as long: the off-diagonal B rows
     float vsig[kHeadDim];
     alignas(16) float alpha[kWaves][8];
     alignas(16) float wm[8][kWaves];  // per head: each wave's reference R (log2 units)
@@ -175,26 +176,24 @@ __device__ __forceinline__ void qk_unit(const MfmaSmem& sm, const uint32_t (&rec
 }
 
 // QK over the units of one width class, two units per step into two accumulators
-// (independent MFMA chains, both units' lookups in flight together).  qb / qs: the
-// lane's q split row and its stride per unit (0 off the diagonal).
+// (independent MFMA chains, both units' lookups in flight together).  qb: the lane's
+// q split row (the zero row off the diagonal); unit u's 8 positions sit 16 bytes after
+// unit u - 1's.
 template <int W, int RD>
 __device__ __forceinline__ void qk_class(const MfmaSmem& sm, const uint32_t (&rec)[RD + 2], int start, int units,
-                                         int ubase, const uint16_t* qb, uint32_t qmask, floatx16& acc0,
-                                         floatx16& acc1) {
-    // unit u's q split sits 8 positions (16 bytes) after unit u - 1's on the diagonal
+                                         int ubase, const uint16_t* qb, floatx16& acc0, floatx16& acc1) {
     const char* qc = (const char*)qb;
     int j = 0;
     for (; j + 1 < units; j += 2) {
         H8 a0, b0, a1, b1;
-        qk_unit<W, RD>(sm, rec, start + j * 8 * W, (const uint16_t*)(qc + ((16u * (ubase + j)) & qmask)), a0, b0);
-        qk_unit<W, RD>(sm, rec, start + (j + 1) * 8 * W, (const uint16_t*)(qc + ((16u * (ubase + j + 1)) & qmask)),
-                       a1, b1);
+        qk_unit<W, RD>(sm, rec, start + j * 8 * W, (const uint16_t*)(qc + 16u * (ubase + j)), a0, b0);
+        qk_unit<W, RD>(sm, rec, start + (j + 1) * 8 * W, (const uint16_t*)(qc + 16u * (ubase + j + 1)), a1, b1);
         acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0.h, b0.h, acc0, 0, 0, 0);
         acc1 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a1.h, b1.h, acc1, 0, 0, 0);
     }
     if (j < units) {
         H8 a0, b0;
-        qk_unit<W, RD>(sm, rec, start + j * 8 * W, (const uint16_t*)(qc + ((16u * (ubase + j)) & qmask)), a0, b0);
+        qk_unit<W, RD>(sm, rec, start + j * 8 * W, (const uint16_t*)(qc + 16u * (ubase + j)), a0, b0);
         acc0 = __builtin_amdgcn_mfma_f32_32x32x16_f16(a0.h, b0.h, acc0, 0, 0, 0);
     }
 }
@@ -437,6 +436,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     {
         uint4* qz = (uint4*)&sm.qsplit[0][0][0];
         for (int i = tid; i < (int)(sizeof(sm.qsplit) / 16); i += 256) qz[i] = uint4{0, 0, 0, 0};
+        if (tid < (int)(sizeof(sm.qzero) / 16)) ((uint4*)sm.qzero)[tid] = uint4{0, 0, 0, 0};
         if (tid < kHeadDim) sm.vsig[tid] = my_vsig;
     }
     // width classes (descending): every wave ranks the blocks; a block's two fields sit
@@ -494,10 +494,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     // LDS only, so each wave starts on its tile as soon as its own K section lands.
     if (tau < t1 && (kStageInK1 || !appender)) dma_k(tau, 0);
     lds_barrier();
-    // B operand rows: the lane's column (hi|lo, head) on the diagonal, else a row that
-    // stays zero (the last unit of hi row 0: at most 22 units are ever filled)
-    const uint16_t* qb = bdiag ? &sm.qsplit[(col >> 3) & 1][col & 7][0] : &sm.qsplit[0][0][8 * (kMaxUnits - 1)];
-    const uint32_t qmask = bdiag ? ~0u : 0u;
+    // B operand rows: the lane's column (hi|lo, head) on the diagonal, else the zero row
+    // (as long as a q split row, so every lane's unit address is one add)
+    const uint16_t* qb = bdiag ? &sm.qsplit[(col >> 3) & 1][col & 7][0] : &sm.qzero[0];
 
     // ---- the step's append (one wave): quantize and pack the new token for slot
     // len-1 exactly as the quantize path does.  The bytes go into the LDS copy of
@@ -623,14 +622,14 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         }
         // ---- QK: this lane's token, 8 fields of one width class per instruction
         floatx16 acc0 = {}, acc1 = {};
-        qk_class<8, RD>(sm, rec, cstart[8], cunits[8], cubase[8], qb, qmask, acc0, acc1);
-        qk_class<7, RD>(sm, rec, cstart[7], cunits[7], cubase[7], qb, qmask, acc0, acc1);
-        qk_class<6, RD>(sm, rec, cstart[6], cunits[6], cubase[6], qb, qmask, acc0, acc1);
-        qk_class<5, RD>(sm, rec, cstart[5], cunits[5], cubase[5], qb, qmask, acc0, acc1);
-        qk_class<4, RD>(sm, rec, cstart[4], cunits[4], cubase[4], qb, qmask, acc0, acc1);
-        qk_class<3, RD>(sm, rec, cstart[3], cunits[3], cubase[3], qb, qmask, acc0, acc1);
-        qk_class<2, RD>(sm, rec, cstart[2], cunits[2], cubase[2], qb, qmask, acc0, acc1);
-        qk_class<1, RD>(sm, rec, cstart[1], cunits[1], cubase[1], qb, qmask, acc0, acc1);
+        qk_class<8, RD>(sm, rec, cstart[8], cunits[8], cubase[8], qb, acc0, acc1);
+        qk_class<7, RD>(sm, rec, cstart[7], cunits[7], cubase[7], qb, acc0, acc1);
+        qk_class<6, RD>(sm, rec, cstart[6], cunits[6], cubase[6], qb, acc0, acc1);
+        qk_class<5, RD>(sm, rec, cstart[5], cunits[5], cubase[5], qb, acc0, acc1);
+        qk_class<4, RD>(sm, rec, cstart[4], cunits[4], cubase[4], qb, acc0, acc1);
+        qk_class<3, RD>(sm, rec, cstart[3], cunits[3], cubase[3], qb, acc0, acc1);
+        qk_class<2, RD>(sm, rec, cstart[2], cunits[2], cubase[2], qb, acc0, acc1);
+        qk_class<1, RD>(sm, rec, cstart[1], cunits[1], cubase[1], qb, acc0, acc1);
         floatx16 acc;
 #pragma unroll
         for (int i = 0; i < 16; ++i) acc[i] = acc0[i] + acc1[i];
