@@ -103,7 +103,6 @@ struct MfmaSmem {
     alignas(16) uint16_t qsplit[2][8][8 * kMaxUnits + 8];  // rows 400 B apart: the 16 rows read by one
                                                           // b128 load fall in distinct LDS banks
     alignas(16) uint16_t qzero[8 * kMaxUnits + 8];         // a zero row as long: the off-diagonal B rows
-    float vsig[kHeadDim];
     alignas(16) float alpha[kWaves][8];
     alignas(16) float wm[8][kWaves];  // per head: each wave's reference R (log2 units)
     alignas(16) float wl[8][kWaves];  // ... and its sum of weights
@@ -308,7 +307,9 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
     const int my_w = k_bits[kvh * kMaxBlocks + lane];
     const float my_ksig = k_sigma[kvh * kMaxBlocks + lane];
     const int vs_blk = pairing == KVQ_PAIR_HALF ? (tid & (kMaxBlocks - 1)) : ((tid >> 1) & (kMaxBlocks - 1));
-    const float my_vsig = v_sigma[kvh * kMaxBlocks + vs_blk];  // used by threads < 128
+    // the value block scale of coordinate tid % 128: the combine's thread (half, c) scales
+    // coordinate c by it (both halves map c to the same block)
+    const float my_vsig = v_sigma[kvh * kMaxBlocks + vs_blk];
     const int qp = pairing == KVQ_PAIR_HALF ? lane : 2 * lane;
     const int qq = pairing == KVQ_PAIR_HALF ? lane + kMaxBlocks : 2 * lane + 1;
     uint32_t qv[2][2];  // heads wave and wave + 4 (clamped; unused past the group): coordinates qp, qq
@@ -437,7 +438,6 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
         uint4* qz = (uint4*)&sm.qsplit[0][0][0];
         for (int i = tid; i < (int)(sizeof(sm.qsplit) / 16); i += 256) qz[i] = uint4{0, 0, 0, 0};
         if (tid < (int)(sizeof(sm.qzero) / 16)) ((uint4*)sm.qzero)[tid] = uint4{0, 0, 0, 0};
-        if (tid < kHeadDim) sm.vsig[tid] = my_vsig;
     }
     // width classes (descending): every wave ranks the blocks; a block's two fields sit
     // at its rank within its class.  Wave w fills the q split of heads w, w+4.
@@ -837,7 +837,7 @@ __global__ __launch_bounds__(256) __attribute__((amdgpu_waves_per_eu(3))) void d
             mwj[j] = *(const float4*)sm.wm[h0 + j];
             lwj[j] = *(const float4*)sm.wl[h0 + j];
         }
-        const float vs = V16 ? 1.f : sm.vsig[c];
+        const float vs = V16 ? 1.f : my_vsig;
         float* const part0 = ws + (((int64_t)s * n_q + kvh * g + h0) * n_split + split) * D2;
 #pragma unroll
         for (int j = 0; j < 4; ++j) {
