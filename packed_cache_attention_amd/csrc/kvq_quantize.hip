@@ -39,7 +39,7 @@ __device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(
 // One step of binary lifting on threshold addresses: `at` is the LDS byte address of
 // the threshold of the code found so far (the table start for code 0), `c` the
 // candidate's (at + 4 << open bit position).  The step moves to the candidate when the
-// value reaches its product RN(s * RN(sig * t)); a NaN threshold never does.
+// value reaches its product RN(s * RN(sig * t)).
 __device__ __forceinline__ uint32_t lift(uint32_t at, uint32_t c, float x, float sig, float s) {
     const float a = *(lds_cf32*)(uintptr_t)c;
     const float b = s * (sig * a);
@@ -50,6 +50,30 @@ __device__ __forceinline__ uint32_t lift(uint32_t at, uint32_t c, float x, float
 // (the levels are symmetric), and s * (sig * 0) = +0 for the non-negative finite s and
 // sig, so the first lifting step is the test x >= 0 (false for NaN, as the step is).
 __device__ __forceinline__ uint32_t top_bit(float x, int w) { return x >= 0.f ? 4u << (w - 1) : 0u; }
+
+// G fields of one width w (1..8) for the lane's token: x >= RN(s * RN(sig * t)) decides
+// each bit, from the top one down; the codes overwrite the fields' fp16 values in the
+// lane's staged row.
+template <int G>
+__device__ __forceinline__ void k_group(const uint32_t* fx, const float* fsig, uint16_t* krow, int w, uint32_t thr0,
+                                        float sk) {
+    const uint32_t tb = thr0 + 4u * KVQ_CB_OFF(w);
+    uint32_t at[G], c[G];
+    float x[G], sg[G];
+#pragma unroll
+    for (int i = 0; i < G; ++i) {
+        c[i] = __builtin_amdgcn_readfirstlane(fx[i]) & 127u;
+        sg[i] = fsig[i];
+        x[i] = h2f(krow[c[i]]);
+        at[i] = tb + top_bit(x[i], w);
+    }
+    for (int sh = w - 2; sh >= 0; --sh) {
+#pragma unroll
+        for (int i = 0; i < G; ++i) at[i] = lift(at[i], at[i] + (4u << sh), x[i], sg[i], sk);
+    }
+#pragma unroll
+    for (int i = 0; i < G; ++i) krow[c[i]] = (uint16_t)((at[i] - tb) >> 2);
+}
 
 __global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(
     const uint16_t* __restrict__ kx, const uint16_t* __restrict__ vx, int64_t stride_tok, int64_t stride_head,
@@ -74,7 +98,7 @@ __global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(
     uint8_t* tile = cache + seq_byte_off[s] + ((int64_t)h * (capacity / kTile) + tau) * TB;
 
     __shared__ uint32_t s_k[kTile * kRowDw], s_v[kTile * kRowDw];
-    __shared__ float s_thr[512];  // the codebook thresholds, then a NaN
+    __shared__ float s_thr[512];  // the codebook thresholds
     __shared__ float s_quarter[kQWaves][kTile];
     __shared__ float s_ks[kTile], s_vs[kTile];
     // K order, field f: coordinate | width << 7 | bit offset << 12, and the block's
@@ -84,6 +108,7 @@ __global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(
     __shared__ float s_vsig[kHeadDim];
     __shared__ int s_range[kQWaves + 1];  // wave w encodes fields [s_range[w], s_range[w+1])
     __shared__ uint8_t s_wfirst[64];      // the field holding bit 32k of the record (nf: none)
+    __shared__ uint8_t s_cend[kHeadDim];  // field f -> the end of its width class in the K order
 
     const int tid = threadIdx.x, lane = tid & 63;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);  // uniform in the wave
@@ -114,7 +139,6 @@ __global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(
         }
     }
     for (int i = tid; i < 510; i += kQThreads) s_thr[i] = c_thresholds[i];
-    if (tid == 0) s_thr[510] = __builtin_nanf("");
     if (tid < kHeadDim) {
         const int blk = pairing == KVQ_PAIR_HALF ? (tid & (kMaxBlocks - 1)) : (tid >> 1);
         s_vsig[tid] = v_sigma[h * kMaxBlocks + blk];
@@ -126,17 +150,19 @@ __global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(
         const int w = k_bits[h * kMaxBlocks + i];
         const float sig = k_sigma[h * kMaxBlocks + i];
         const unsigned long long below = (1ull << i) - 1ull;
-        int rank = 0, off = 0;
+        int rank = 0, off = 0, ge = 0;  // ge: blocks at least as wide
         for (int wc = 16; wc >= 1; --wc) {
             const unsigned long long mk = __ballot(w == wc);
             if (wc > w) { rank += __popcll(mk); off += 2 * wc * __popcll(mk); }
             if (wc == w) { rank += __popcll(mk & below); off += 2 * wc * __popcll(mk & below); }
+            if (wc >= w) ge += __popcll(mk);
         }
         const int nf = 2 * __popcll(__ballot(w > 0));
         s_wfirst[i] = (uint8_t)nf;
         if (w > 0) {
             const int pc = pairing == KVQ_PAIR_HALF ? i : 2 * i;
             const int qc = pairing == KVQ_PAIR_HALF ? i + kMaxBlocks : 2 * i + 1;
+            s_cend[2 * rank] = s_cend[2 * rank + 1] = (uint8_t)(2 * ge);
             s_fx[2 * rank] = pc | w << 7 | off << 12;
             s_fx[2 * rank + 1] = qc | w << 7 | (off + w) << 12;
             s_fsig[2 * rank] = s_fsig[2 * rank + 1] = sig;
@@ -196,42 +222,27 @@ __global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(
     // ---- phase 2: codes (lane = token), written over the lane's own fp16 values
     const bool valid = lane >= lo_p && lane < hi_p;
     {
-        // K: groups of kGroup consecutive fields.  Widths fall along the K order, so
-        // the group's first searched field is its widest (w0); a field of width w joins
-        // the lifting for its last w steps, where the open bit position is the same for
-        // every field of the group.  Width-16 fields keep the raw fp16 bits.
+        // K: groups of up to kGroup consecutive fields of one width class (widths fall
+        // along the K order), searched side by side, every field through all of its w
+        // bits.  Width-16 fields keep the raw fp16 bits.
         const float sk = s_ks[lane];
         uint16_t* krow = (uint16_t*)(s_k + lane * kRowDw);
         const int f0 = __builtin_amdgcn_readfirstlane(s_range[wave]);
         const int f1 = __builtin_amdgcn_readfirstlane(s_range[wave + 1]);
-        const uint32_t thr0 = lds_addr(s_thr), nan_at = thr0 + 4u * 510u;
-        for (int f = f0; f < f1; f += kGroup) {
-            const int gn = min(kGroup, f1 - f);
-            uint32_t fx[kGroup], at[kGroup], tb[kGroup];
-            int ws[kGroup];  // search width (0: no search)
-            int w0 = 0;
-            float x[kGroup], sg[kGroup];
-#pragma unroll
-            for (int i = 0; i < kGroup; ++i) {
-                fx[i] = __builtin_amdgcn_readfirstlane(s_fx[f + i]);
-                sg[i] = s_fsig[f + i];
-                const int w = (fx[i] >> 7) & 31;
-                ws[i] = i < gn && w != 16 ? w : 0;
-                w0 = max(w0, ws[i]);
-                x[i] = h2f(krow[fx[i] & 127]);
-                tb[i] = thr0 + 4u * KVQ_CB_OFF(ws[i]);
-                at[i] = ws[i] > 0 ? tb[i] + top_bit(x[i], ws[i]) : tb[i];
+        const uint32_t thr0 = lds_addr(s_thr);
+        for (int f = f0; f < f1;) {
+            const uint32_t fx0 = __builtin_amdgcn_readfirstlane(s_fx[f]);
+            const int w = (fx0 >> 7) & 31;
+            const int gn = min(min(kGroup, f1 - f), (int)__builtin_amdgcn_readfirstlane(s_cend[f]) - f);
+            if (w != 16) {
+                switch (gn) {
+                    case 1: k_group<1>(s_fx + f, s_fsig + f, krow, w, thr0, sk); break;
+                    case 2: k_group<2>(s_fx + f, s_fsig + f, krow, w, thr0, sk); break;
+                    case 3: k_group<3>(s_fx + f, s_fsig + f, krow, w, thr0, sk); break;
+                    default: k_group<kGroup>(s_fx + f, s_fsig + f, krow, w, thr0, sk); break;
+                }
             }
-            // the remaining bits; a field with fewer than w0 bits compares with the NaN
-            // (and stays put) until its own next bit comes up
-            for (int sh = w0 - 2; sh >= 0; --sh) {
-#pragma unroll
-                for (int i = 0; i < kGroup; ++i)
-                    at[i] = lift(at[i], sh < ws[i] - 1 ? at[i] + (4u << sh) : nan_at, x[i], sg[i], sk);
-            }
-#pragma unroll
-            for (int i = 0; i < kGroup; ++i)
-                if (ws[i] > 0) krow[fx[i] & 127] = (uint16_t)((at[i] - tb[i]) >> 2);
+            f += gn;
         }
 
         // V: kVGroup coordinates at a time; slots outside the call get code 0 (16-bit
