@@ -32,47 +32,80 @@ constexpr int kQThreads = 64 * kQWaves;
 constexpr int kGroup = 4;   // K fields searched side by side
 constexpr int kVGroup = 8;  // V coordinates searched side by side
 
-// LDS byte address of a shared-memory object
-typedef __attribute__((address_space(3))) const float lds_cf32;
-__device__ __forceinline__ uint32_t lds_addr(const void* p) { return (uint32_t)(uintptr_t)(lds_cf32*)p; }
-
-// One step of binary lifting on threshold addresses: `at` is the LDS byte address of
-// the threshold of the code found so far (the table start for code 0), `c` the
-// candidate's (at + 4 << open bit position).  The step moves to the candidate when the
-// value reaches its product RN(s * RN(sig * t)).
-__device__ __forceinline__ uint32_t lift(uint32_t at, uint32_t c, float x, float sig, float s) {
-    const float a = *(lds_cf32*)(uintptr_t)c;
-    const float b = s * (sig * a);
-    return x >= b ? c : at;
-}
 
 // The top bit of a width-w code: the middle threshold of every codebook is exactly +0
 // (the levels are symmetric), and s * (sig * 0) = +0 for the non-negative finite s and
 // sig, so the first lifting step is the test x >= 0 (false for NaN, as the step is).
 __device__ __forceinline__ uint32_t top_bit(float x, int w) { return x >= 0.f ? 4u << (w - 1) : 0u; }
 
-// G fields of one width w (1..8) for the lane's token: x >= RN(s * RN(sig * t)) decides
-// each bit, from the top one down; the codes overwrite the fields' fp16 values in the
-// lane's staged row.
-template <int G>
-__device__ __forceinline__ void k_group(const uint32_t* fx, const float* fsig, uint16_t* krow, int w, uint32_t thr0,
+// Binary lifting at a compile-time width W over G values side by side: c4 = 4 * (code so
+// far); each step tries the next lower bit against the threshold product
+// RN(s * RN(sig * t)), the threshold read at tw + c4 (tw: the width's LDS table, a
+// constant that folds into the read's offset).  The top bit is the sign test.
+template <int W, int G>
+__device__ __forceinline__ void lift_codes(const float* tw, const float (&x)[G], const float (&sg)[G], float s,
+                                           uint32_t (&c4)[G]) {
+#pragma unroll
+    for (int i = 0; i < G; ++i) c4[i] = top_bit(x[i], W);
+#pragma unroll
+    for (int sh = W - 2; sh >= 0; --sh) {
+#pragma unroll
+        for (int i = 0; i < G; ++i) {
+            const uint32_t cand = c4[i] | (4u << sh);
+            const float a = *(const float*)((const char*)tw + cand);
+            const float b = s * (sg[i] * a);
+            if (x[i] >= b) c4[i] = cand;
+        }
+    }
+}
+
+// G key fields of width W for the lane's token; the codes overwrite the fields' fp16
+// values in the lane's staged row.
+template <int W, int G>
+__device__ __forceinline__ void k_group(const uint32_t* fx, const float* fsig, uint16_t* krow, const float* thr,
                                         float sk) {
-    const uint32_t tb = thr0 + 4u * KVQ_CB_OFF(w);
-    uint32_t at[G], c[G];
+    uint32_t c[G], c4[G];
     float x[G], sg[G];
 #pragma unroll
     for (int i = 0; i < G; ++i) {
         c[i] = __builtin_amdgcn_readfirstlane(fx[i]) & 127u;
         sg[i] = fsig[i];
         x[i] = h2f(krow[c[i]]);
-        at[i] = tb + top_bit(x[i], w);
     }
-    for (int sh = w - 2; sh >= 0; --sh) {
+    lift_codes<W, G>(thr + KVQ_CB_OFF(W), x, sg, sk, c4);
 #pragma unroll
-        for (int i = 0; i < G; ++i) at[i] = lift(at[i], at[i] + (4u << sh), x[i], sg[i], sk);
+    for (int i = 0; i < G; ++i) krow[c[i]] = (uint16_t)(c4[i] >> 2);
+}
+
+template <int W>
+__device__ __forceinline__ void k_group_w(int gn, const uint32_t* fx, const float* fsig, uint16_t* krow,
+                                          const float* thr, float sk) {
+    switch (gn) {
+        case 1: k_group<W, 1>(fx, fsig, krow, thr, sk); break;
+        case 2: k_group<W, 2>(fx, fsig, krow, thr, sk); break;
+        case 3: k_group<W, 3>(fx, fsig, krow, thr, sk); break;
+        default: k_group<W, kGroup>(fx, fsig, krow, thr, sk); break;
     }
+}
+
+// The wave's 16 value coordinates c0 .. c0 + 15 at the uniform width VB, eight side by
+// side; slots outside the call get code 0.
+template <int VB>
+__device__ __forceinline__ void v_codes(uint16_t* vrow, const float* s_vsig, int c0, const float* thr, float sv,
+                                        bool valid) {
 #pragma unroll
-    for (int i = 0; i < G; ++i) krow[c[i]] = (uint16_t)((at[i] - tb) >> 2);
+    for (int g0 = 0; g0 < kHeadDim / kQWaves; g0 += kVGroup) {
+        uint32_t c4[kVGroup];
+        float x[kVGroup], sg[kVGroup];
+#pragma unroll
+        for (int i = 0; i < kVGroup; ++i) {
+            x[i] = h2f(vrow[c0 + g0 + i]);
+            sg[i] = s_vsig[c0 + g0 + i];
+        }
+        lift_codes<VB, kVGroup>(thr + KVQ_CB_OFF(VB), x, sg, sv, c4);
+#pragma unroll
+        for (int i = 0; i < kVGroup; ++i) vrow[c0 + g0 + i] = valid ? (uint16_t)(c4[i] >> 2) : (uint16_t)0;
+    }
 }
 
 __global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(
@@ -229,45 +262,39 @@ __global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(
         uint16_t* krow = (uint16_t*)(s_k + lane * kRowDw);
         const int f0 = __builtin_amdgcn_readfirstlane(s_range[wave]);
         const int f1 = __builtin_amdgcn_readfirstlane(s_range[wave + 1]);
-        const uint32_t thr0 = lds_addr(s_thr);
         for (int f = f0; f < f1;) {
             const uint32_t fx0 = __builtin_amdgcn_readfirstlane(s_fx[f]);
             const int w = (fx0 >> 7) & 31;
             const int gn = min(min(kGroup, f1 - f), (int)__builtin_amdgcn_readfirstlane(s_cend[f]) - f);
-            if (w != 16) {
-                switch (gn) {
-                    case 1: k_group<1>(s_fx + f, s_fsig + f, krow, w, thr0, sk); break;
-                    case 2: k_group<2>(s_fx + f, s_fsig + f, krow, w, thr0, sk); break;
-                    case 3: k_group<3>(s_fx + f, s_fsig + f, krow, w, thr0, sk); break;
-                    default: k_group<kGroup>(s_fx + f, s_fsig + f, krow, w, thr0, sk); break;
-                }
+            switch (w) {  // width 16 keeps the raw bits
+                case 1: k_group_w<1>(gn, s_fx + f, s_fsig + f, krow, s_thr, sk); break;
+                case 2: k_group_w<2>(gn, s_fx + f, s_fsig + f, krow, s_thr, sk); break;
+                case 3: k_group_w<3>(gn, s_fx + f, s_fsig + f, krow, s_thr, sk); break;
+                case 4: k_group_w<4>(gn, s_fx + f, s_fsig + f, krow, s_thr, sk); break;
+                case 5: k_group_w<5>(gn, s_fx + f, s_fsig + f, krow, s_thr, sk); break;
+                case 6: k_group_w<6>(gn, s_fx + f, s_fsig + f, krow, s_thr, sk); break;
+                case 7: k_group_w<7>(gn, s_fx + f, s_fsig + f, krow, s_thr, sk); break;
+                case 8: k_group_w<8>(gn, s_fx + f, s_fsig + f, krow, s_thr, sk); break;
+                default: break;
             }
             f += gn;
         }
 
         // V: kVGroup coordinates at a time; slots outside the call get code 0 (16-bit
         // V keeps the raw rows, whose invalid slots the run builder skips)
-        if (v_bits != 16) {
-            const float sv = s_vs[lane];
-            uint16_t* vrow = (uint16_t*)(s_v + lane * kRowDw);
-            const uint32_t vthr = thr0 + 4u * KVQ_CB_OFF(v_bits);
-            constexpr int kVPer = kHeadDim / kQWaves;
-            for (int c0 = kVPer * wave; c0 < kVPer * wave + kVPer; c0 += kVGroup) {
-                uint32_t at[kVGroup];
-                float x[kVGroup], sg[kVGroup];
-#pragma unroll
-                for (int i = 0; i < kVGroup; ++i) {
-                    x[i] = h2f(vrow[c0 + i]);
-                    sg[i] = s_vsig[c0 + i];
-                    at[i] = vthr + top_bit(x[i], v_bits);
-                }
-                for (int sh = v_bits - 2; sh >= 0; --sh) {
-#pragma unroll
-                    for (int i = 0; i < kVGroup; ++i) at[i] = lift(at[i], at[i] + (4u << sh), x[i], sg[i], sv);
-                }
-#pragma unroll
-                for (int i = 0; i < kVGroup; ++i) vrow[c0 + i] = valid ? (uint16_t)((at[i] - vthr) >> 2) : (uint16_t)0;
-            }
+        const float sv = s_vs[lane];
+        uint16_t* vrow = (uint16_t*)(s_v + lane * kRowDw);
+        const int c0 = (kHeadDim / kQWaves) * wave;
+        switch (v_bits) {  // 16-bit values keep the raw rows (the run builder skips invalid slots)
+            case 1: v_codes<1>(vrow, s_vsig, c0, s_thr, sv, valid); break;
+            case 2: v_codes<2>(vrow, s_vsig, c0, s_thr, sv, valid); break;
+            case 3: v_codes<3>(vrow, s_vsig, c0, s_thr, sv, valid); break;
+            case 4: v_codes<4>(vrow, s_vsig, c0, s_thr, sv, valid); break;
+            case 5: v_codes<5>(vrow, s_vsig, c0, s_thr, sv, valid); break;
+            case 6: v_codes<6>(vrow, s_vsig, c0, s_thr, sv, valid); break;
+            case 7: v_codes<7>(vrow, s_vsig, c0, s_thr, sv, valid); break;
+            case 8: v_codes<8>(vrow, s_vsig, c0, s_thr, sv, valid); break;
+            default: break;
         }
     }
     __syncthreads();
