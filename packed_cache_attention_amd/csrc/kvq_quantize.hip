@@ -140,7 +140,7 @@ __global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(
     __shared__ float s_fsig[kHeadDim + kGroup];
     __shared__ float s_vsig[kHeadDim];
     __shared__ int s_range[kQWaves + 1];  // wave w encodes fields [s_range[w], s_range[w+1])
-    __shared__ uint8_t s_wfirst[64];      // the field holding bit 32k of the record (nf: none)
+    __shared__ uint8_t s_wfirst[65];      // the field holding bit 32k of the record (nf: none)
     __shared__ uint8_t s_cend[kHeadDim];  // field f -> the end of its width class in the K order
 
     const int tid = threadIdx.x, lane = tid & 63;
@@ -192,6 +192,7 @@ __global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(
         }
         const int nf = 2 * __popcll(__ballot(w > 0));
         s_wfirst[i] = (uint8_t)nf;
+        if (i == 0) s_wfirst[64] = (uint8_t)nf;  // one past the longest record (64 words)
         if (w > 0) {
             const int pc = pairing == KVQ_PAIR_HALF ? i : 2 * i;
             const int qc = pairing == KVQ_PAIR_HALF ? i + kMaxBlocks : 2 * i + 1;
@@ -235,7 +236,9 @@ __global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(
         for (int k = 0; k < 16; ++k) {
             const uint32_t pr = r[k];
             const float a = h2f(pr & 0xffffu), b = h2f(pr >> 16);
-            t[k] = a * a + b * b;
+            // both squares are exact in binary32, so the fused form rounds a^2 + b^2 once,
+            // exactly as the separate products and sum do
+            t[k] = __builtin_fmaf(a, a, b * b);
         }
 #pragma unroll
         for (int m = 1; m < 16; m <<= 1)
@@ -300,8 +303,9 @@ __global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(
     __syncthreads();
 
     // ---- phase 3: the tile's records (valid slots), runs and scales
-    // K record word k of slot `lane`: the fields from s_wfirst[k] on that start
-    // before bit 32k + 32, each field's code shifted to its offset
+    // K record word k of slot `lane`: the field holding bit 32k (s_wfirst[k]) and every
+    // later one that starts before bit 32k + 32 -- up to the field holding bit 32k + 32
+    // when it starts inside the word -- each field's code shifted to its offset
     uint32_t* krec = (uint32_t*)tile;
     {
         const uint16_t* krow = (const uint16_t*)(s_k + lane * kRowDw);
@@ -309,24 +313,25 @@ __global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(
         for (int k = wave; k < RW; k += kQWaves) {
             const int lo = 32 * k;
             uint32_t val = 0u;
-            int f = __builtin_amdgcn_readfirstlane(s_wfirst[k]);
-            if (f < nf) {
-                // the field holding bit 32k starts at or before it; the rest start inside
-                const uint32_t fx0 = __builtin_amdgcn_readfirstlane(s_fx[f]);
+            const int fa = __builtin_amdgcn_readfirstlane(s_wfirst[k]);
+            int fb = __builtin_amdgcn_readfirstlane(s_wfirst[k + 1]);
+            if (fb < nf && (int)((__builtin_amdgcn_readfirstlane(s_fx[fb]) >> 12) & 2047) < lo + 32) ++fb;
+            if (fa < nf) {
+                const uint32_t fx0 = __builtin_amdgcn_readfirstlane(s_fx[fa]);
                 val = (uint32_t)krow[fx0 & 127] >> (lo - (int)((fx0 >> 12) & 2047));
-                bool done = false;
-                for (++f; f < nf && !done; f += kGroup) {
+                int f = fa + 1;
+                for (; f + kGroup <= fb; f += kGroup) {
                     uint32_t fx[kGroup], code[kGroup];
 #pragma unroll
                     for (int i = 0; i < kGroup; ++i) fx[i] = __builtin_amdgcn_readfirstlane(s_fx[f + i]);
 #pragma unroll
                     for (int i = 0; i < kGroup; ++i) code[i] = krow[fx[i] & 127];
 #pragma unroll
-                    for (int i = 0; i < kGroup; ++i) {
-                        const int of = (fx[i] >> 12) & 2047;
-                        if (f + i >= nf || of >= lo + 32) done = true;
-                        if (!done) val |= code[i] << (of - lo);
-                    }
+                    for (int i = 0; i < kGroup; ++i) val |= code[i] << ((int)((fx[i] >> 12) & 2047) - lo);
+                }
+                for (; f < fb; ++f) {
+                    const uint32_t fx1 = __builtin_amdgcn_readfirstlane(s_fx[f]);
+                    val |= (uint32_t)krow[fx1 & 127] << ((int)((fx1 >> 12) & 2047) - lo);
                 }
             }
             if (valid) krec[lane * RW + k] = val;
