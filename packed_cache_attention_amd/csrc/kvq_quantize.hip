@@ -108,6 +108,23 @@ __device__ __forceinline__ void v_codes(uint16_t* vrow, const float* s_vsig, int
     }
 }
 
+// Word k of coordinate c's run at width VB: bits [32k, 32k + 32) hold slots plo..phi,
+// slot p's code at bit p*VB - 32k (the first one possibly cut at the word's start, the
+// last at its end).  The slots' codes sit one staged row (2*kRowDw halves) apart, so
+// every read after the first is at a constant offset from it.
+template <int VB>
+__device__ __forceinline__ uint32_t run_word(const uint32_t* s_v, int c, int k) {
+    constexpr int kMaxSlots = 32 / VB + 2;  // slots a word can touch
+    const int plo = 32 * k / VB, phi = min(kTile - 1, (32 * k + 31) / VB);
+    const uint16_t* col = (const uint16_t*)s_v + c + plo * 2 * kRowDw;
+    const int sh0 = plo * VB - 32 * k;  // in (-VB, 0]
+    uint32_t val = (uint32_t)col[0] >> -sh0;
+#pragma unroll
+    for (int i = 1; i < kMaxSlots; ++i)
+        if (plo + i <= phi) val |= (uint32_t)col[i * 2 * kRowDw] << (sh0 + i * VB);
+    return val;
+}
+
 __global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(
     const uint16_t* __restrict__ kx, const uint16_t* __restrict__ vx, int64_t stride_tok, int64_t stride_head,
     const int64_t* __restrict__ first_slot, const int32_t* __restrict__ n_new, const int64_t* __restrict__ src_row0,
@@ -353,12 +370,16 @@ __global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(
                 if (p >= lo_p && p < hi_p) val |= (uint32_t)col[p * 2 * kRowDw] << (16 * e);
             }
         } else {
-            // word k holds bits [32k, 32k + 32): slots plo..phi, slot p at bit p*v_bits - 32k
-            const int plo = 32 * k / v_bits, phi = min(kTile - 1, (32 * k + 31) / v_bits);
-            const uint16_t* col = (const uint16_t*)s_v + c;
-            const int sh0 = plo * v_bits - 32 * k;  // in (-v_bits, 0]
-            val = (uint32_t)col[plo * 2 * kRowDw] >> -sh0;
-            for (int p = plo + 1; p <= phi; ++p) val |= (uint32_t)col[p * 2 * kRowDw] << (p * v_bits - 32 * k);
+            switch (v_bits) {
+                case 1: val = run_word<1>(s_v, c, k); break;
+                case 2: val = run_word<2>(s_v, c, k); break;
+                case 3: val = run_word<3>(s_v, c, k); break;
+                case 4: val = run_word<4>(s_v, c, k); break;
+                case 5: val = run_word<5>(s_v, c, k); break;
+                case 6: val = run_word<6>(s_v, c, k); break;
+                case 7: val = run_word<7>(s_v, c, k); break;
+                default: val = run_word<8>(s_v, c, k); break;
+            }
         }
         uint32_t* dst = vrun + c * VW + k;
         if (whole) *dst = val;
