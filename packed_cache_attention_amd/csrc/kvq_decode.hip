@@ -173,7 +173,6 @@ hipError_t launch_decode_partials(const kvq_geom& g, const DecodePlan& plan, int
                                   const float* v_sigma, float softmax_scale, float* partials, hipStream_t st,
                                   const AppendArgs& app) {
     const float scale_log2 = softmax_scale * kLog2e;
-    const int grp = n_q_heads / g.n_kv_heads;
     // the matrix-core kernel appends inside (the tail tile's wave); the generic one in
     // the launch that builds its query table (one wave per (sequence, KV head))
     if (plan.kernel == KVQ_DECODE_MFMA)

@@ -147,22 +147,26 @@ __device__ __forceinline__ double u128_to_f64(uint64_t lo, uint64_t hi) {
     return ldexp((double)keep, drop);
 }
 
-// One workgroup per unit.  Wave 0 (lane i = block i) forms E_i, E_tot and sigma.
-// Greedy: step after step the block with the largest marginal gain E_i * dD[b_i]
-// (lowest index on ties) gains one bit.  A block's gains fall strictly with its
-// width (dD strictly decreasing; all zero when E_i = 0), so the candidate (i, w) is
-// always taken after (i, w - 1), and the greedy order is the order of all 8 nb
-// candidates (i, w) by gain descending, then block, then width ascending: the first
-// `budget` of them are taken, and b_i counts block i's.  Thread t holds candidate
-// (t / 8, t % 8) and finds its rank in that order by comparing against every other.
+// Workgroups (unit, part): wave 0 (lane i = block i) of every part forms E_i and E_tot,
+// part 0 writes sigma (and the widths of the uniform mode).  Greedy: step after step
+// the block with the largest marginal gain E_i * dD[b_i] (lowest index on ties) gains
+// one bit.  A block's gains fall strictly with its width (dD strictly decreasing; all
+// zero when E_i = 0), so the candidate (i, w) is always taken after (i, w - 1), and
+// the greedy order is the order of all 8 nb candidates (i, w) by gain descending, then
+// block, then width ascending: the first `budget` of them are taken, and b_i counts
+// block i's.  Part p ranks the candidates of blocks 8p .. 8p+7, wave w block 8p + w:
+// eight threads per candidate each count the candidates that precede it among 64 of
+// the 512 (rank = #{j : key_j > key, or key_j == key and j < own index}), and the
+// eight counts are summed across the lanes.
 constexpr int kAllocThreads = 8 * 64;
+constexpr int kAllocBlocksPerPart = kAllocThreads / 64;
 
 __global__ __launch_bounds__(kAllocThreads) void allocate_kernel(const uint64_t* __restrict__ energy, int nb,
                                                                 int budget, int mode, uint8_t* __restrict__ bits,
                                                                 float* __restrict__ sigma) {
     __shared__ double s_E[64];
     __shared__ uint64_t s_key[kAllocThreads];
-    const int u = blockIdx.x, tid = threadIdx.x;
+    const int u = blockIdx.x, part = blockIdx.y, tid = threadIdx.x;
     const int wave = __builtin_amdgcn_readfirstlane(tid >> 6);
     if (wave == 0) {
         const int i = tid;
@@ -170,54 +174,54 @@ __global__ __launch_bounds__(kAllocThreads) void allocate_kernel(const uint64_t*
         const uint64_t lo = act ? energy[((int64_t)u * nb + i) * 2] : 0ull;
         const uint64_t hi = act ? energy[((int64_t)u * nb + i) * 2 + 1] : 0ull;
         const double E = ldexp(u128_to_f64(lo, hi), -48);
-        uint64_t tlo = lo, thi = hi;
-        for (int off = 32; off >= 1; off >>= 1) {
-            const uint64_t olo = __shfl_xor(tlo, off), ohi = __shfl_xor(thi, off);
-            tlo += olo;
-            thi += ohi + (tlo < olo ? 1ull : 0ull);
-        }
-        const double Etot = ldexp(u128_to_f64(tlo, thi), -48);
         s_E[i] = E;
-        if (act) {
-            sigma[(int64_t)u * nb + i] = Etot > 0.0 ? (float)sqrt(E / (2.0 * Etot)) : 0.0f;
-            if (budget == 16 * nb) bits[(int64_t)u * nb + i] = 16;
-            else if (mode == KVQ_UNIFORM) bits[(int64_t)u * nb + i] = (uint8_t)(budget / nb);
+        if (part == 0) {
+            uint64_t tlo = lo, thi = hi;
+            for (int off = 32; off >= 1; off >>= 1) {
+                const uint64_t olo = __shfl_xor(tlo, off), ohi = __shfl_xor(thi, off);
+                tlo += olo;
+                thi += ohi + (tlo < olo ? 1ull : 0ull);
+            }
+            const double Etot = ldexp(u128_to_f64(tlo, thi), -48);
+            if (act) {
+                sigma[(int64_t)u * nb + i] = Etot > 0.0 ? (float)sqrt(E / (2.0 * Etot)) : 0.0f;
+                if (budget == 16 * nb) bits[(int64_t)u * nb + i] = 16;
+                else if (mode == KVQ_UNIFORM) bits[(int64_t)u * nb + i] = (uint8_t)(budget / nb);
+            }
         }
     }
     if (budget == 16 * nb || mode == KVQ_UNIFORM) return;  // uniform over the workgroup
     __syncthreads();
-    const int i = tid >> 3, w = tid & 7;
-    const bool act = i < nb;
-    // gains are >= 0, so their bit patterns order like the values; candidates of
-    // absent blocks get gain 0 and the largest indices, so they precede nobody
-    const double gain = act ? s_E[i] * (double)c_gain_dd[w] : 0.0;
-    const uint64_t key = __double_as_longlong(gain);
-    s_key[tid] = key;
+    {
+        // gains are >= 0, so their bit patterns order like the values; candidates of
+        // absent blocks get gain 0 and the largest indices, so they precede nobody
+        const int i = tid >> 3, w = tid & 7;
+        const double gain = i < nb ? s_E[i] * (double)c_gain_dd[w] : 0.0;
+        s_key[tid] = __double_as_longlong(gain);
+    }
     __syncthreads();
-    // rank = #{j : key_j > key, or key_j == key and j < tid}; indices j of other waves
-    // are all below or all above this wave's, only its own 64 need the index test
+    const int cand = 64 * part + (tid >> 3), sub = tid & 7;
+    const uint64_t key = s_key[cand];
     int rank = 0;
-    const int lo_j = 64 * wave;
-    for (int j = 0; j < lo_j; j += 2) {
+    for (int j = 64 * sub; j < 64 * sub + 64; j += 2) {
         const uint64_t a = s_key[j], b2 = s_key[j + 1];
-        rank += (a >= key) + (b2 >= key);
+        rank += (a > key || (a == key && j < cand)) ? 1 : 0;
+        rank += (b2 > key || (b2 == key && j + 1 < cand)) ? 1 : 0;
     }
-    for (int j = lo_j; j < lo_j + 64; ++j) {
-        const uint64_t a = s_key[j];
-        rank += (a > key || (a == key && j < tid)) ? 1 : 0;
-    }
-    for (int j = lo_j + 64; j < kAllocThreads; j += 2) {
-        const uint64_t a = s_key[j], b2 = s_key[j + 1];
-        rank += (a > key) + (b2 > key);
-    }
-    const unsigned long long taken = __ballot(rank < budget);
-    if (act && w == 0) bits[(int64_t)u * nb + i] = (uint8_t)__popcll((taken >> (tid & 56)) & 0xffull);
+    rank += __shfl_xor(rank, 1);
+    rank += __shfl_xor(rank, 2);
+    rank += __shfl_xor(rank, 4);
+    const unsigned long long taken = __ballot(sub == 0 && rank < budget);
+    const int blk = kAllocBlocksPerPart * part + wave;
+    if ((tid & 63) == 0 && blk < nb) bits[(int64_t)u * nb + blk] = (uint8_t)__popcll(taken);
 }
 
 hipError_t launch_allocate(const uint64_t* energy, int n_units, int nb, int budget, int mode, uint8_t* bits,
                            float* sigma, hipStream_t st) {
-    hipLaunchKernelGGL(allocate_kernel, dim3(n_units), dim3(kAllocThreads), 0, st, energy, nb, budget, mode, bits,
-                       sigma);
+    const bool greedy = !(budget == 16 * nb || mode == KVQ_UNIFORM);
+    const int parts = greedy ? (nb + kAllocBlocksPerPart - 1) / kAllocBlocksPerPart : 1;
+    hipLaunchKernelGGL(allocate_kernel, dim3(n_units, parts), dim3(kAllocThreads), 0, st, energy, nb, budget, mode,
+                       bits, sigma);
     return hipGetLastError();
 }
 
