@@ -3,13 +3,14 @@
 // Allocation for KV-Cache Quantization" (abstract: TQ-MSE codes at the widths the
 // Block-GTQ allocator assigns, kept in a packed cache).
 //
-// One workgroup owns one (sequence, KV head, tile): it is the only writer of that
-// tile during the call, so partially filled tiles are updated with plain
-// read-modify-write.  Phase 1: each wave takes tokens; lane l holds coordinates
-// 2l, 2l+1, forms the squared-norm tree with xor-butterflies (level 1 is the
-// lane's own pair, level k the butterfly with mask 2^(k-2)), and finds each code
-// by binary search over the monotone threshold products.  Phase 2: the tile's K
-// records, V runs and scales are assembled dword by dword from the codes in LDS.
+// Two kernels write the same bytes.  The bulk kernel: one workgroup owns one
+// (sequence, KV head, tile) -- the only writer of that tile during the call, so
+// partially filled tiles are updated with plain read-modify-write -- with lane =
+// token; norms, codes by binary search over the monotone threshold products, then
+// the tile's K records, V runs and scales assembled dword by dword from the codes
+// in LDS.  The append kernel (a few new tokens per sequence): one wave per (token,
+// head), lane l holding coordinates 2l, 2l+1, the squared-norm tree by
+// xor-butterflies (kvq_append.h).
 #include "kvq_internal.h"
 #include "kvq_append.h"
 
@@ -23,7 +24,7 @@ namespace kvq {
 // quarters of each K row, waves 4-7 those of V.  Codes: each wave takes a run of
 // K-order fields (about an eighth of the work) and 16 of the V coordinates.  A
 // field's width is the same for every lane, so the binary lifting runs without
-// divergence, several fields side by side.  Each coordinate is read by one wave
+// divergence, several fields of one width side by side, at a compile-time width.  Each coordinate is read by one wave
 // only, which overwrites its fp16 value with the code; the store phase then builds
 // every K record word and V run word in one thread from those code rows.
 constexpr int kRowDw = kHeadDim / 2 + 1;
@@ -33,9 +34,10 @@ constexpr int kGroup = 4;   // K fields searched side by side
 constexpr int kVGroup = 8;  // V coordinates searched side by side
 
 
-// The top bit of a width-w code: the middle threshold of every codebook is exactly +0
-// (the levels are symmetric), and s * (sig * 0) = +0 for the non-negative finite s and
-// sig, so the first lifting step is the test x >= 0 (false for NaN, as the step is).
+// The top bit of a width-w code, as a byte offset into the width's threshold table: the
+// middle threshold of every codebook is exactly +0 (the levels are symmetric), and
+// s * (sig * 0) = +0 for the non-negative finite s and sig, so the first lifting step
+// is the test x >= 0 (false for NaN, as the step is).
 __device__ __forceinline__ uint32_t top_bit(float x, int w) { return x >= 0.f ? 4u << (w - 1) : 0u; }
 
 // Binary lifting at a compile-time width W over G values side by side: c4 = 4 * (code so
