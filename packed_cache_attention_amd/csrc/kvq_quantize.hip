@@ -329,7 +329,8 @@ __global__ __launch_bounds__(kQThreads) void quantize_pack_kernel(
     {
         const uint16_t* krow = (const uint16_t*)(s_k + lane * kRowDw);
         const int nf = __builtin_amdgcn_readfirstlane(s_range[kQWaves]);
-        for (int k = wave; k < RW; k += kQWaves) {
+        // waves 4-7 take the first words: waves 0-3 take the second round of run words below
+        for (int k = (wave + kQWaves / 2) % kQWaves; k < RW; k += kQWaves) {
             const int lo = 32 * k;
             uint32_t val = 0u;
             const int fa = __builtin_amdgcn_readfirstlane(s_wfirst[k]);
